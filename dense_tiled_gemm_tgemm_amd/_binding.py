@@ -1,0 +1,160 @@
+"""ctypes binding of libtgemm.so (argument marshalling only).
+
+Every function here forwards to the C ABI declared in include/tgemm.h; all
+arithmetic runs in the HIP kernels. If the library has not been built the
+first call raises: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libtgemm.so")
+
+TGEMM_B_KxN = 0
+TGEMM_B_NxK = 1
+TGEMM_OK = 0
+TGEMM_ERR_INVALID = -1
+TGEMM_ERR_UNSUPPORTED = -2
+TGEMM_ERR_HIP = -3
+
+_LAYOUT = {"KxN": TGEMM_B_KxN, "NxK": TGEMM_B_NxK, TGEMM_B_KxN: TGEMM_B_KxN, TGEMM_B_NxK: TGEMM_B_NxK}
+
+_lib = None
+_I64 = ctypes.c_int64
+_P = ctypes.c_void_p
+_INT = ctypes.c_int
+
+
+class TgemmError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        msg = f"tgemm failed: {status_string(status)} ({status})"
+        if status == TGEMM_ERR_HIP:
+            msg += f", hipError_t {last_hip_error()}"
+        if what:
+            msg += f" [{what}]"
+        super().__init__(msg)
+
+
+def load():
+    """Load libtgemm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build the HIP library first "
+            "(python -m dense_tiled_gemm_tgemm_amd.build, or __graft_entry__.build())")
+    lib = ctypes.CDLL(LIB_PATH)
+    gemm_args = [_I64, _I64, _I64, _P, _I64, _P, _I64, _INT, _P, _I64, _P]
+    lib.tgemm_f16.restype = _INT
+    lib.tgemm_f16.argtypes = gemm_args
+    lib.tgemm_f16_config.restype = _INT
+    lib.tgemm_f16_config.argtypes = gemm_args + [_INT, _INT, _INT]
+    lib.tgemm_status_string.restype = ctypes.c_char_p
+    lib.tgemm_status_string.argtypes = [_INT]
+    lib.tgemm_last_hip_error.restype = _INT
+    lib.tgemm_last_hip_error.argtypes = []
+    lib.tgemm_plan_f16.restype = _INT
+    lib.tgemm_plan_f16.argtypes = [_I64, _I64, _I64, _P, _I64, _P, _I64, _INT, _P, _I64,
+                                   _INT, _INT, _INT, ctypes.POINTER(_I64)]
+    lib.tgemm_tile_of.restype = _INT
+    lib.tgemm_tile_of.argtypes = [_I64, _I64, _INT, _INT, _I64, ctypes.POINTER(_I64), ctypes.POINTER(_I64)]
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().tgemm_status_string(int(status)).decode()
+
+
+def last_hip_error() -> int:
+    return int(load().tgemm_last_hip_error())
+
+
+def tgemm_f16(M, N, K, A, lda, B, ldb, b_layout, C, ldc, stream=None) -> int:
+    """Raw C call: pointers are integers (device addresses); returns the status."""
+    return int(load().tgemm_f16(M, N, K, A, lda, B, ldb, _LAYOUT[b_layout], C, ldc, stream))
+
+
+def tgemm_f16_config(M, N, K, A, lda, B, ldb, b_layout, C, ldc, stream=None,
+                     force_generic=0, group_m=0, num_xcd=0) -> int:
+    return int(load().tgemm_f16_config(M, N, K, A, lda, B, ldb, _LAYOUT[b_layout], C, ldc, stream,
+                                       int(force_generic), int(group_m), int(num_xcd)))
+
+
+def tgemm_plan_f16(M, N, K, A, lda, B, ldb, b_layout, C, ldc, force_generic=0, group_m=0, num_xcd=0):
+    """Host-only plan query: (status, info dict or None)."""
+    info = (_I64 * 8)()
+    rc = int(load().tgemm_plan_f16(M, N, K, A, lda, B, ldb, _LAYOUT[b_layout], C, ldc,
+                                   int(force_generic), int(group_m), int(num_xcd), info))
+    if rc != TGEMM_OK:
+        return rc, None
+    keys = ("variant", "bm", "bn", "bk", "workgroups", "group_m", "num_xcd", "threads")
+    return rc, dict(zip(keys, (int(v) for v in info)))
+
+
+def tgemm_tile_of(grid_m, grid_n, group_m, num_xcd, wid):
+    tm, tn = _I64(), _I64()
+    rc = int(load().tgemm_tile_of(grid_m, grid_n, group_m, num_xcd, wid, ctypes.byref(tm), ctypes.byref(tn)))
+    if rc != TGEMM_OK:
+        raise TgemmError(rc, "tile_of")
+    return tm.value, tn.value
+
+
+# ----------------------------------------------------------- torch tensors --
+
+def _row_major(t, name):
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must have unit column stride (row-major)")
+    ld = t.stride(0) if t.shape[0] > 1 else max(t.shape[1], 1)
+    return max(ld, 1)
+
+
+def _check_tensor(t, name):
+    import torch
+    if t.dtype != torch.float16:
+        raise TypeError(f"{name} must be torch.float16, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+
+
+def mm(A, B, b_layout: str = "KxN", out=None, stream=None, force_generic: int = 0,
+       group_m: int = 0, num_xcd: int = 0):
+    """C = A @ B for fp16 device tensors (fp32 accumulation in the kernel).
+
+    A: (M, K). B: (K, N) when b_layout == "KxN", (N, K) when "NxK".
+    out: optional (M, N) fp16 tensor with unit column stride; allocated with
+    torch.empty when None. Runs on `stream` (default: torch's current stream).
+    """
+    import torch
+    _check_tensor(A, "A")
+    _check_tensor(B, "B")
+    lay = _LAYOUT[b_layout]
+    M, K = A.shape
+    if lay == TGEMM_B_KxN:
+        Kb, N = B.shape
+    else:
+        N, Kb = B.shape
+    if Kb != K:
+        raise ValueError(f"inner dimensions differ: A is {tuple(A.shape)}, B is {tuple(B.shape)} ({b_layout})")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=A.device)
+    else:
+        _check_tensor(out, "out")
+        if tuple(out.shape) != (M, N):
+            raise ValueError(f"out must be ({M}, {N})")
+    lda, ldb, ldc = _row_major(A, "A"), _row_major(B, "B"), _row_major(out, "out")
+    if stream is None:
+        stream = torch.cuda.current_stream(A.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    rc = tgemm_f16_config(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, lay, out.data_ptr(), ldc,
+                          stream, force_generic, group_m, num_xcd)
+    if rc != TGEMM_OK:
+        raise TgemmError(rc, f"M={M} N={N} K={K} layout={b_layout}")
+    return out

@@ -1,0 +1,43 @@
+"""Compile the HIP library for gfx950 in-tree.
+
+``python -m dense_tiled_gemm_tgemm_amd.build`` writes
+``dense_tiled_gemm_tgemm_amd/libtgemm.so``. All device code is built with
+packed-fp32 instructions disabled (``-packed-fp32-ops``).
+"""
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+SRC = os.path.join(PKG, "csrc", "tgemm.hip")
+LIB = os.path.join(PKG, "libtgemm.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+FLAGS = [
+    "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC", "-shared",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-function",
+    "-I", os.path.join(ROOT, "include"),
+    "-I", os.path.join(PKG, "csrc"),
+]
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, *FLAGS, *extra, SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed to build libtgemm.so")
+    if verbose and res.stderr:
+        # hipcc's host pass does not know the packed-fp32 feature; that warning is harmless
+        sys.stderr.write("\n".join(l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l))
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,400 @@
+// fp16 dense tiled GEMM for MI355X (gfx950): C = A * B, binary16 in, fp32
+// accumulate, binary16 out.
+//
+// One workgroup owns one BM x BN output tile and walks K in BK steps (page 1,
+// "Using NVIDIA CUDA Tile to write a high-performance matrix multiply",
+// sections 1-6; page 4, CUDA programming guide 13.4.2, section 2.4.9.1).
+// Per K step the tile's A (BM x BK) and B (BK x BN) blocks are staged from
+// HBM/L2 into LDS with coalesced 128-bit loads, double-buffered so the next
+// step's loads are in flight while the current step runs on the matrix cores
+// (the load / barrier / compute / overlap / write-back lifecycle of page 3,
+// "Why GEMM", section 2.2). Partial K tiles are padded with zeros and C
+// elements outside M x N are never written (page 4, section 2.4.6.1.3).
+//
+// gfx950 mapping:
+//  * 256 threads = 4 waves of 64 lanes in a 2 x 2 grid; each wave owns a
+//    128 x 128 sub-tile held as 4 x 4 blocks of 32 x 32 fp32 accumulators
+//    (256 accumulator registers per lane).
+//  * Inner product: v_mfma_f32_32x32x16_f16. For a 32x32x16 product each lane
+//    supplies 8 consecutive-k binary16 values of one row of each operand
+//    (row = lane mod 32, k half = lane / 32), read from LDS as one 128-bit
+//    word. The B fragment is passed as the instruction's first operand and
+//    the A fragment as its second, so the 32 x 32 result block is C
+//    transposed: lane l holds C row (l mod 32), and its accumulator registers
+//    4q..4q+3 hold four consecutive C columns 8q + 4*(l/32) + 0..3. The
+//    epilogue therefore writes 64-bit runs of four binary16 values.
+//  * LDS: both operands are kept K-contiguous, [row][64 halves], as 16-byte
+//    chunks; chunk c of row r lives at slot c ^ ((r & 7) ^ ((r >> 3) & 1)).
+//    Eight consecutive rows, and sixteen consecutive rows split by parity,
+//    map one logical chunk to distinct 16-byte bank groups, so the 128-bit
+//    fragment reads (32 rows x one chunk per half-wave) and the 128-bit
+//    staging writes are free of bank conflicts (page 3, sections 3.1 and
+//    5.3; page 5, "Why swizzle matters").
+//  * B stored K x N is transposed in registers while staging: each thread
+//    loads an 8 (k) x 8 (n) block with eight 128-bit row loads and writes it
+//    as eight 128-bit K-contiguous chunks, so both B layouts share one
+//    compute loop.
+//  * Workgroup -> tile: die-aware renumbering, then the grouped order of
+//    page 1, section "Swizzle" (tile_of in tgemm_plan.h).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tgemm.h"
+#include "tgemm_plan.h"
+
+namespace tg {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float acc16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kChunks = BK / 8;                 // 16-byte chunks per LDS row
+constexpr int kTileChunks = 256 * kChunks;      // chunks per staged operand block
+static_assert(BM == 256 && BN == 256 && BK == 64 && NTHREADS == 256,
+              "the staging maps below assume a 256 x 256 x 64 tile and 256 threads");
+
+struct Args {
+    const uint16_t* A;
+    const uint16_t* B;
+    uint16_t* C;
+    int64_t lda, ldb, ldc;
+    int M, N, K;
+    int grid_m, grid_n, W, group_m, num_xcd;
+};
+
+__device__ __forceinline__ int lds_slot(int row, int chunk) {
+    return row * kChunks + (chunk ^ ((row & 7) ^ ((row >> 3) & 1)));
+}
+
+// Eight binary16 values from p[0..nv-1]; lanes at or past nv read as zero.
+__device__ __forceinline__ u32x4 load8_elems(const uint16_t* __restrict__ p, int nv) {
+    unsigned w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const unsigned lo = (2 * q < nv) ? (unsigned)p[2 * q] : 0u;
+        const unsigned hi = (2 * q + 1 < nv) ? (unsigned)p[2 * q + 1] : 0u;
+        w[q] = lo | (hi << 16);
+    }
+    return u32x4{w[0], w[1], w[2], w[3]};
+}
+
+// Stage one BK-wide block of a K-contiguous operand (A, or B stored N x K):
+// rows row0 .. row0+255, k = k0 .. k0+63. Thread t loads chunk (t & 7) of
+// rows (t >> 3) + 32p: eight threads cover one 128-byte row segment.
+// MASK: rows >= nrows and k >= K read as zero (page 4, section 2.4.6.1.3).
+template <bool VEC, bool MASK>
+__device__ __forceinline__ void load_kcontig(u32x4 (&r)[8], const uint16_t* __restrict__ X,
+                                             int64_t ld, int nrows, int K, int row0, int k0,
+                                             int tid) {
+    const int gk = k0 + (tid & 7) * 8;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const int gr = row0 + (tid >> 3) + 32 * p;
+        if (!MASK) {
+            const uint16_t* src = X + (int64_t)gr * ld + gk;
+            r[p] = VEC ? *(const u32x4*)src : load8_elems(src, 8);
+        } else {
+            const int rem = K - gk;
+            const int nv = (gr < nrows) ? (rem < 0 ? 0 : (rem > 8 ? 8 : rem)) : 0;
+            const int grc = gr < nrows ? gr : nrows - 1;
+            const uint16_t* src = X + (int64_t)grc * ld + (nv > 0 ? gk : 0);
+            if (VEC && nv == 8)
+                r[p] = *(const u32x4*)src;
+            else
+                r[p] = load8_elems(src, nv);
+        }
+    }
+}
+
+__device__ __forceinline__ void store_kcontig(u32x4* __restrict__ s, const u32x4 (&r)[8], int tid) {
+    const int c = tid & 7;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) s[lds_slot((tid >> 3) + 32 * p, c)] = r[p];
+}
+
+// Stage one BK-deep block of B stored K x N: k = k0 .. k0+63, n = n0 .. n0+255.
+// Thread t owns the 8 x 8 block k = k0 + 8*(t & 7) + 0..7, n = n0 + 8*(t >> 3) + 0..7
+// and loads it as eight 128-bit row pieces.
+template <bool VEC, bool MASK>
+__device__ __forceinline__ void load_kxn(u32x4 (&r)[8], const uint16_t* __restrict__ B, int64_t ldb,
+                                         int N, int K, int n0, int k0, int tid) {
+    const int gn = n0 + (tid >> 3) * 8;
+    const int gk0 = k0 + (tid & 7) * 8;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+        const int gk = gk0 + kk;
+        if (!MASK) {
+            const uint16_t* src = B + (int64_t)gk * ldb + gn;
+            r[kk] = VEC ? *(const u32x4*)src : load8_elems(src, 8);
+        } else {
+            const int rem = N - gn;
+            const int nv = (gk < K) ? (rem < 0 ? 0 : (rem > 8 ? 8 : rem)) : 0;
+            const int gkc = gk < K ? gk : K - 1;
+            const uint16_t* src = B + (int64_t)gkc * ldb + (nv > 0 ? gn : 0);
+            if (VEC && nv == 8)
+                r[kk] = *(const u32x4*)src;
+            else
+                r[kk] = load8_elems(src, nv);
+        }
+    }
+}
+
+// Transpose the 8 x 8 block in registers and write it K-contiguous: LDS row
+// n0' + nn receives k = 8*(t & 7) + 0..7 as logical chunk (t & 7). Threads
+// with odd column-block index write their rows in swapped pair order so that
+// the 16 lanes of a bank-group pass touch rows of both parities.
+__device__ __forceinline__ void store_kxn(u32x4* __restrict__ s, const u32x4 (&r)[8], int tid) {
+    const int kb = tid & 7;
+    const int nb = tid >> 3;
+    u32x4 t[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {       // word q of a row holds columns 2q (low) and 2q+1 (high)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {   // word p of a column holds rows 2p (low) and 2p+1 (high)
+            const unsigned lo = r[2 * p][q], hi = r[2 * p + 1][q];
+            t[2 * q][p] = (lo & 0xffffu) | (hi << 16);
+            t[2 * q + 1][p] = (lo >> 16) | (hi & 0xffff0000u);
+        }
+    }
+    const int odd = nb & 1;
+#pragma unroll
+    for (int sidx = 0; sidx < 8; ++sidx) {
+        const u32x4 v = odd ? t[sidx ^ 1] : t[sidx];
+        s[lds_slot(nb * 8 + (sidx ^ odd), kb)] = v;
+    }
+}
+
+// One BK step of the wave's 128 x 128 sub-tile: 4 k16 slices x 4 x 4 MFMAs.
+__device__ __forceinline__ void mma_step(acc16 (&acc)[4][4], const u32x4* __restrict__ sA,
+                                         const u32x4* __restrict__ sB, int wm, int wn, int lane) {
+    const int r32 = lane & 31, khalf = lane >> 5;
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+        half8 af[4], bf[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            af[i] = __builtin_bit_cast(half8, sA[lds_slot(wm * 128 + i * 32 + r32, kk * 2 + khalf)]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            bf[j] = __builtin_bit_cast(half8, sB[lds_slot(wn * 128 + j * 32 + r32, kk * 2 + khalf)]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[j], af[i], acc[i][j], 0, 0, 0);
+    }
+}
+
+__device__ __forceinline__ unsigned pack_half2(float a, float b) {
+    // fp32 -> binary16, round to nearest even (page 1, section 6: the fp32
+    // accumulator is converted to C's type when it is stored)
+    const _Float16 ha = (_Float16)a, hb = (_Float16)b;
+    return (unsigned)__builtin_bit_cast(uint16_t, ha) | ((unsigned)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+
+template <bool VEC_C>
+__device__ __forceinline__ void store_c(const acc16 (&acc)[4][4], const Args& a, int m0, int n0, int wm,
+                                        int wn, int lane) {
+    const int r32 = lane & 31, khalf = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int m = m0 + wm * 128 + i * 32 + r32;
+        if (m >= a.M) continue;
+        uint16_t* crow = a.C + (int64_t)m * a.ldc;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int n = n0 + wn * 128 + j * 32 + q * 8 + khalf * 4;
+                const unsigned w0 = pack_half2(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]);
+                const unsigned w1 = pack_half2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+                if (VEC_C && n + 4 <= a.N) {
+                    *(u32x2*)(crow + n) = u32x2{w0, w1};
+                } else {
+                    if (n + 0 < a.N) crow[n + 0] = (uint16_t)(w0 & 0xffffu);
+                    if (n + 1 < a.N) crow[n + 1] = (uint16_t)(w0 >> 16);
+                    if (n + 2 < a.N) crow[n + 2] = (uint16_t)(w1 & 0xffffu);
+                    if (n + 3 < a.N) crow[n + 3] = (uint16_t)(w1 >> 16);
+                }
+            }
+        }
+    }
+}
+
+template <int NXK, bool VEC, bool MASK>
+__device__ __forceinline__ void load_stage(u32x4 (&ra)[8], u32x4 (&rb)[8], const Args& a, int m0, int n0,
+                                           int k0, int tid) {
+    load_kcontig<VEC, MASK>(ra, a.A, a.lda, a.M, a.K, m0, k0, tid);
+    if (NXK)
+        load_kcontig<VEC, MASK>(rb, a.B, a.ldb, a.N, a.K, n0, k0, tid);
+    else
+        load_kxn<VEC, MASK>(rb, a.B, a.ldb, a.N, a.K, n0, k0, tid);
+}
+
+template <int NXK>
+__device__ __forceinline__ void store_stage(u32x4* __restrict__ sA, u32x4* __restrict__ sB,
+                                            const u32x4 (&ra)[8], const u32x4 (&rb)[8], int tid) {
+    store_kcontig(sA, ra, tid);
+    if (NXK)
+        store_kcontig(sB, rb, tid);
+    else
+        store_kxn(sB, rb, tid);
+}
+
+template <int NXK, bool VEC, bool VEC_C>
+__global__ void __launch_bounds__(NTHREADS)
+__attribute__((amdgpu_waves_per_eu(1, 1)))
+tgemm_f16_kernel(Args a) {
+    __shared__ u32x4 smem[2][2][kTileChunks];   // [stage][A | B], 128 KiB
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    int tm, tn;
+    tile_of((int)blockIdx.x, a.W, a.grid_m, a.grid_n, a.group_m, a.num_xcd, &tm, &tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const bool interior = (m0 + BM <= a.M) && (n0 + BN <= a.N);
+    const int nk = (a.K + BK - 1) / BK;
+
+    acc16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = acc16{};
+
+    u32x4 ra[8], rb[8];
+    if (nk > 0) {
+        if (interior && BK <= a.K)
+            load_stage<NXK, VEC, false>(ra, rb, a, m0, n0, 0, tid);
+        else
+            load_stage<NXK, VEC, true>(ra, rb, a, m0, n0, 0, tid);
+        store_stage<NXK>(smem[0][0], smem[0][1], ra, rb, tid);
+        __syncthreads();
+    }
+    for (int t = 0; t < nk; ++t) {
+        const int cur = t & 1;
+        const bool more = t + 1 < nk;
+        if (more) {
+            const int k0 = (t + 1) * BK;
+            if (interior && k0 + BK <= a.K)
+                load_stage<NXK, VEC, false>(ra, rb, a, m0, n0, k0, tid);
+            else
+                load_stage<NXK, VEC, true>(ra, rb, a, m0, n0, k0, tid);
+        }
+        mma_step(acc, smem[cur][0], smem[cur][1], wm, wn, lane);
+        if (more) store_stage<NXK>(smem[cur ^ 1][0], smem[cur ^ 1][1], ra, rb, tid);
+        __syncthreads();
+    }
+    store_c<VEC_C>(acc, a, m0, n0, wm, wn, lane);
+}
+
+typedef void (*KernelFn)(Args);
+
+template <int NXK, bool VEC, bool VEC_C>
+static const void* kernel_ptr() {
+    return reinterpret_cast<const void*>(&tgemm_f16_kernel<NXK, VEC, VEC_C>);
+}
+
+static const void* pick_kernel(int variant) {
+    switch (variant & 7) {
+        case 0: return kernel_ptr<0, false, false>();
+        case 1: return kernel_ptr<0, true, false>();
+        case 2: return kernel_ptr<0, false, true>();
+        case 3: return kernel_ptr<0, true, true>();
+        case 4: return kernel_ptr<1, false, false>();
+        case 5: return kernel_ptr<1, true, false>();
+        case 6: return kernel_ptr<1, false, true>();
+        default: return kernel_ptr<1, true, true>();
+    }
+}
+
+static thread_local int g_last_hip_error = 0;
+
+}  // namespace tg
+
+extern "C" int tgemm_f16_config(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                                const void* B, int64_t ldb, int b_layout, void* C, int64_t ldc,
+                                void* stream, int force_generic, int group_m, int num_xcd) {
+    tg::Plan pl;
+    const int rc = tg::make_plan(M, N, K, A, lda, B, ldb, b_layout, C, ldc, force_generic, group_m,
+                                 num_xcd, &pl);
+    if (rc != TGEMM_OK) return rc;
+    if (pl.M == 0 || pl.N == 0) return TGEMM_OK;
+    tg::Args args;
+    args.A = static_cast<const uint16_t*>(A);
+    args.B = static_cast<const uint16_t*>(B);
+    args.C = static_cast<uint16_t*>(C);
+    args.lda = pl.lda;
+    args.ldb = pl.ldb;
+    args.ldc = pl.ldc;
+    args.M = pl.M;
+    args.N = pl.N;
+    args.K = pl.K;
+    args.grid_m = pl.grid_m;
+    args.grid_n = pl.grid_n;
+    args.W = pl.W;
+    args.group_m = pl.group_m;
+    args.num_xcd = pl.num_xcd;
+    void* kargs[] = {&args};
+    const hipError_t e = hipLaunchKernel(tg::pick_kernel(pl.variant), dim3((unsigned)pl.W),
+                                         dim3(tg::NTHREADS), kargs, 0, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) {
+        tg::g_last_hip_error = (int)e;
+        return TGEMM_ERR_HIP;
+    }
+    return TGEMM_OK;
+}
+
+extern "C" int tgemm_f16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                         int64_t ldb, int b_layout, void* C, int64_t ldc, void* stream) {
+    return tgemm_f16_config(M, N, K, A, lda, B, ldb, b_layout, C, ldc, stream, 0, 0, 0);
+}
+
+extern "C" const char* tgemm_status_string(int status) {
+    switch (status) {
+        case TGEMM_OK: return "ok";
+        case TGEMM_ERR_INVALID: return "invalid argument";
+        case TGEMM_ERR_UNSUPPORTED: return "unsupported problem size";
+        case TGEMM_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+extern "C" int tgemm_last_hip_error(void) { return tg::g_last_hip_error; }
+
+extern "C" int tgemm_plan_f16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                              int64_t ldb, int b_layout, void* C, int64_t ldc, int force_generic,
+                              int group_m, int num_xcd, int64_t* info) {
+    if (!info) return TGEMM_ERR_INVALID;
+    tg::Plan pl;
+    const int rc = tg::make_plan(M, N, K, A, lda, B, ldb, b_layout, C, ldc, force_generic, group_m,
+                                 num_xcd, &pl);
+    if (rc != TGEMM_OK) return rc;
+    info[0] = pl.variant;
+    info[1] = tg::BM;
+    info[2] = tg::BN;
+    info[3] = tg::BK;
+    info[4] = (pl.M == 0 || pl.N == 0) ? 0 : pl.W;
+    info[5] = pl.group_m;
+    info[6] = pl.num_xcd;
+    info[7] = tg::NTHREADS;
+    return TGEMM_OK;
+}
+
+extern "C" int tgemm_tile_of(int64_t grid_m, int64_t grid_n, int group_m, int num_xcd, int64_t wid,
+                             int64_t* tile_m, int64_t* tile_n) {
+    if (!tile_m || !tile_n || grid_m <= 0 || grid_n <= 0 || group_m <= 0 || num_xcd <= 0)
+        return TGEMM_ERR_INVALID;
+    if (grid_m > 2147483647 || grid_n > 2147483647 || grid_m * grid_n > 2147483647 || wid < 0 ||
+        wid >= grid_m * grid_n)
+        return TGEMM_ERR_INVALID;
+    const int g = group_m > grid_m ? (int)grid_m : group_m;
+    int tm, tn;
+    tg::tile_of((int)wid, (int)(grid_m * grid_n), (int)grid_m, (int)grid_n, g, num_xcd, &tm, &tn);
+    *tile_m = tm;
+    *tile_n = tn;
+    return TGEMM_OK;
+}

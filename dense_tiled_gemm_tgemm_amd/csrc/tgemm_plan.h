@@ -1,0 +1,136 @@
+// Host-side planning for the fp16 tiled GEMM: argument checks, variant
+// choice, grid size, and the workgroup -> output-tile map shared with the
+// kernels. Plain C++ apart from the host/device qualifiers on tile_of().
+#pragma once
+
+#include <stdint.h>
+
+#include "tgemm.h"
+
+#if defined(__HIPCC__)
+#define TG_HD __host__ __device__
+#else
+#define TG_HD
+#endif
+
+namespace tg {
+
+// Workgroup tile: BM x BN outputs, K walked BK at a time (page 1, section
+// "Step 2: set the tile size": each block owns one tm x tn output tile).
+constexpr int BM = 256;
+constexpr int BN = 256;
+constexpr int BK = 64;
+constexpr int NTHREADS = 256;            // 4 waves of 64 lanes, 2 x 2 over the tile
+
+constexpr int kDefaultGroupM = 8;        // page 1, section "Swizzle": GROUP_SIZE_M = 8
+constexpr int kDefaultNumXcd = 8;        // MI355X: 8 accelerator dies of 32 CUs
+
+enum : int { kVecAB = 1, kVecC = 2, kLayoutNxK = 4 };
+
+// Output tile computed by workgroup `wid` of W = grid_m * grid_n.
+// Step 1 (die-aware renumbering): the dispatcher hands workgroup w to die
+// w mod X. Renumber so die x receives one contiguous range of logical ids,
+// in its own dispatch order, so neighbouring tiles share that die's L2.
+// Step 2 (grouped order, page 1, section "Swizzle"): logical ids walk down
+// group_m tile-rows before moving one tile-column right, so a die's
+// concurrently running tiles reuse a few A row-panels and B column-panels.
+// group_m must be <= grid_m (the host clamps it; larger values map the same).
+TG_HD inline void tile_of(int wid, int W, int grid_m, int grid_n, int group_m, int num_xcd,
+                          int* tile_m, int* tile_n) {
+    int p = wid;
+    if (num_xcd > 1) {
+        const int q = W / num_xcd, r = W % num_xcd;
+        const int x = wid % num_xcd, s = wid / num_xcd;
+        p = (x < r) ? x * (q + 1) + s : r * (q + 1) + (x - r) * q + s;
+    }
+    const int in_group = group_m * grid_n;
+    const int g = p / in_group;
+    const int first = g * group_m;
+    const int rows = (grid_m - first < group_m) ? grid_m - first : group_m;
+    *tile_m = first + p % rows;
+    *tile_n = (p - g * in_group) / rows;
+}
+
+struct Plan {
+    int M, N, K;
+    int64_t lda, ldb, ldc;
+    int layout;        // 0 = KxN, 1 = NxK
+    int variant;       // kVecAB | kVecC | kLayoutNxK bits
+    int grid_m, grid_n, W;
+    int group_m, num_xcd;
+};
+
+inline bool span_bytes(int64_t rows, int64_t cols, int64_t ld, uint64_t* bytes) {
+    // bytes covered by a row-major rows x cols array of 2-byte elements
+    if (rows <= 0 || cols <= 0) {
+        *bytes = 0;
+        return true;
+    }
+    int64_t last;
+    if (__builtin_mul_overflow(rows - 1, ld, &last)) return false;
+    if (__builtin_add_overflow(last, cols, &last)) return false;
+    if (last > INT64_MAX / 2) return false;
+    *bytes = (uint64_t)last * 2u;
+    return true;
+}
+
+inline bool overlaps(const void* p, uint64_t pn, const void* q, uint64_t qn) {
+    if (pn == 0 || qn == 0) return false;
+    const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
+    return a < b + qn && b < a + pn;
+}
+
+inline int make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                     int64_t ldb, int b_layout, void* C, int64_t ldc, int force_generic,
+                     int group_m, int num_xcd, Plan* pl) {
+    const int64_t kMaxDim = 2147483647;
+    if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
+        return TGEMM_ERR_INVALID;
+    if (b_layout != TGEMM_B_KxN && b_layout != TGEMM_B_NxK) return TGEMM_ERR_INVALID;
+    if (force_generic != 0 && force_generic != 1) return TGEMM_ERR_INVALID;
+    if (group_m < 0 || group_m > 1024 || num_xcd < 0 || num_xcd > 64) return TGEMM_ERR_INVALID;
+    const int64_t one = 1;
+    if (lda < (K > one ? K : one)) return TGEMM_ERR_INVALID;
+    const int64_t bmin = (b_layout == TGEMM_B_KxN) ? N : K;
+    if (ldb < (bmin > one ? bmin : one)) return TGEMM_ERR_INVALID;
+    if (ldc < (N > one ? N : one)) return TGEMM_ERR_INVALID;
+
+    uint64_t na, nb, nc;
+    if (!span_bytes(M, K, lda, &na)) return TGEMM_ERR_INVALID;
+    if (b_layout == TGEMM_B_KxN) {
+        if (!span_bytes(K, N, ldb, &nb)) return TGEMM_ERR_INVALID;
+    } else {
+        if (!span_bytes(N, K, ldb, &nb)) return TGEMM_ERR_INVALID;
+    }
+    if (!span_bytes(M, N, ldc, &nc)) return TGEMM_ERR_INVALID;
+    if ((na && !A) || (nb && !B) || (nc && !C)) return TGEMM_ERR_INVALID;
+    if (((uintptr_t)A & 1) || ((uintptr_t)B & 1) || ((uintptr_t)C & 1)) return TGEMM_ERR_INVALID;
+    if (overlaps(C, nc, A, na) || overlaps(C, nc, B, nb)) return TGEMM_ERR_INVALID;
+
+    const int64_t gm = (M + BM - 1) / BM, gn = (N + BN - 1) / BN;
+    if (gm * gn > kMaxDim) return TGEMM_ERR_UNSUPPORTED;
+
+    pl->M = (int)M;
+    pl->N = (int)N;
+    pl->K = (int)K;
+    pl->lda = lda;
+    pl->ldb = ldb;
+    pl->ldc = ldc;
+    pl->layout = b_layout;
+    pl->grid_m = (int)gm;
+    pl->grid_n = (int)gn;
+    pl->W = (int)(gm * gn);
+    int g = group_m ? group_m : kDefaultGroupM;
+    if (gm > 0 && g > gm) g = (int)gm;
+    pl->group_m = g > 0 ? g : 1;
+    pl->num_xcd = num_xcd ? num_xcd : kDefaultNumXcd;
+
+    const bool vec_ab = !force_generic && ((uintptr_t)A % 16 == 0) && (lda % 8 == 0) &&
+                        ((uintptr_t)B % 16 == 0) && (ldb % 8 == 0);
+    const bool vec_c = ((uintptr_t)C % 8 == 0) && (ldc % 4 == 0);
+    pl->variant = (vec_ab ? kVecAB : 0) | (vec_c ? kVecC : 0) |
+                  (b_layout == TGEMM_B_NxK ? kLayoutNxK : 0);
+    return TGEMM_OK;
+}
+
+}  // namespace tg

@@ -1,0 +1,134 @@
+/*
+ * tgemm: fp16 dense tiled matrix product C = A * B on AMD Instinct MI355X
+ * (gfx950). C ABI: plain pointers and sizes, no HIP or framework types.
+ *
+ * The operation (page 1, "Using NVIDIA CUDA Tile to write a high-performance
+ * matrix multiply", section "What is matrix multiplication?"): for A of M x K
+ * and B of K x N, C[i][j] = sum over k of A[i][k] * B[k][j].
+ * Numerics follow the pages' tile kernels (page 1, sections 4-6; page 4,
+ * CUDA programming guide 13.4.2, chapter "Writing tile kernels", section
+ * 2.4.9.1 "Matrix multiplication"): binary16 inputs, fp32 accumulation,
+ * conversion to binary16 (round to nearest even) only when C is stored,
+ * partial K tiles padded with zeros, out-of-range C elements never written.
+ * Each workgroup owns one output tile and walks K tile by tile.
+ *
+ * Storage (all row-major, element strides in units of 16-bit elements):
+ *   A: M x K,  element (i, k) at A[i*lda + k]
+ *   B: b_layout TGEMM_B_KxN: K x N, element (k, j) at B[k*ldb + j]
+ *      b_layout TGEMM_B_NxK: N x K, element (k, j) at B[j*ldb + k]
+ *         (C = A * B^T when B is viewed as the N x K array it is stored as)
+ *   C: M x N,  element (i, j) at C[i*ldc + j]
+ * A, B, C point to device memory holding IEEE 754 binary16 bit patterns.
+ *
+ * Ownership: the caller owns all three buffers. The library allocates no
+ * device memory and keeps no pointer after a call returns.
+ *
+ * Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL means the
+ * default stream) and the call returns without waiting. C is valid once the
+ * stream has been synchronized. A and B are only read.
+ *
+ * Errors: nothing is printed and nothing is thrown across the ABI. A call
+ * that returns TGEMM_ERR_INVALID or TGEMM_ERR_UNSUPPORTED has enqueued no
+ * work. TGEMM_ERR_HIP means the HIP runtime refused the launch; its
+ * hipError_t value is available from tgemm_last_hip_error() on the calling
+ * thread.
+ */
+#ifndef TGEMM_H_
+#define TGEMM_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { TGEMM_B_KxN = 0, TGEMM_B_NxK = 1 } tgemm_b_layout;
+
+enum {
+    TGEMM_OK = 0,
+    TGEMM_ERR_INVALID = -1,     /* argument check failed; nothing enqueued */
+    TGEMM_ERR_UNSUPPORTED = -2, /* valid but outside what this build runs  */
+    TGEMM_ERR_HIP = -3          /* the HIP runtime reported an error       */
+};
+
+/*
+ * C = A * B (binary16 in, fp32 accumulate, binary16 out) on `stream`.
+ *
+ * Argument checks (TGEMM_ERR_INVALID, nothing enqueued) - the call fails if:
+ *   M, N or K is negative or above 2^31 - 1;
+ *   lda < max(1, K); ldb < max(1, N) for KxN or < max(1, K) for NxK;
+ *   ldc < max(1, N); b_layout is neither TGEMM_B_KxN nor TGEMM_B_NxK;
+ *   a pointer is NULL while its operand holds at least one element;
+ *   a pointer is not 2-byte aligned;
+ *   the memory spanned by C overlaps the memory spanned by A or B.
+ * Degenerate shapes: M == 0 or N == 0 is a successful no-op. K == 0 writes
+ * zeros to the M x N region of C (the accumulator starts at zero and the K
+ * walk runs zero times).
+ * Alignment: any 2-byte-aligned operand works. Operands whose base is
+ * 16-byte aligned with a row stride that is a multiple of 8 elements are
+ * read with 128-bit loads; C with an 8-byte-aligned base and ldc a multiple
+ * of 4 is written with 64-bit stores; other operands take element-wise paths.
+ * C must not alias A or B (page 4, section 2.4.12.1: restrict-qualified
+ * operands must not overlap).
+ */
+int tgemm_f16(int64_t M, int64_t N, int64_t K,
+              const void* A, int64_t lda,
+              const void* B, int64_t ldb, int b_layout,
+              void* C, int64_t ldc,
+              void* stream);
+
+/*
+ * Same as tgemm_f16 with explicit launch choices, for tests and tuning.
+ *   force_generic: 1 = use element-wise operand loads even where 128-bit
+ *                  loads are possible (same results); 0 = automatic.
+ *   group_m:       tile-rows per raster group (page 1, section "Swizzle",
+ *                  GROUP_SIZE_M); 0 = default (8); 1..1024 otherwise.
+ *   num_xcd:       number of dies the workgroups are spread over for the
+ *                  die-aware renumbering; 0 = default (8 on MI355X);
+ *                  1 disables the renumbering; 1..64 otherwise.
+ * Out-of-range choices return TGEMM_ERR_INVALID.
+ */
+int tgemm_f16_config(int64_t M, int64_t N, int64_t K,
+                     const void* A, int64_t lda,
+                     const void* B, int64_t ldb, int b_layout,
+                     void* C, int64_t ldc,
+                     void* stream,
+                     int force_generic, int group_m, int num_xcd);
+
+/* Human-readable text of a TGEMM_* status code (static storage). */
+const char* tgemm_status_string(int status);
+
+/* hipError_t of the most recent TGEMM_ERR_HIP on the calling thread (0 if none). */
+int tgemm_last_hip_error(void);
+
+/*
+ * Host-only planning query (no GPU call): the launch tgemm_f16_config would
+ * make for these arguments. Returns TGEMM_OK and fills info[0..7]:
+ *   info[0] variant bits: bit0 128-bit A/B loads, bit1 64-bit C stores,
+ *           bit2 B layout is NxK
+ *   info[1] tile rows (BM)   info[2] tile columns (BN)   info[3] K step (BK)
+ *   info[4] workgroups launched  info[5] group_m  info[6] num_xcd
+ *   info[7] threads per workgroup
+ * or the same error tgemm_f16_config would return. `info` must hold 8 values.
+ */
+int tgemm_plan_f16(int64_t M, int64_t N, int64_t K,
+                   const void* A, int64_t lda,
+                   const void* B, int64_t ldb, int b_layout,
+                   void* C, int64_t ldc,
+                   int force_generic, int group_m, int num_xcd,
+                   int64_t* info);
+
+/*
+ * Host-only: the output tile that workgroup `wid` of a grid_m x grid_n tile
+ * grid computes, exactly as the kernels compute it (die-aware renumbering,
+ * then the grouped order of page 1, section "Swizzle"). Returns TGEMM_OK, or
+ * TGEMM_ERR_INVALID for non-positive sizes or wid outside the grid.
+ */
+int tgemm_tile_of(int64_t grid_m, int64_t grid_n, int group_m, int num_xcd,
+                  int64_t wid, int64_t* tile_m, int64_t* tile_n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TGEMM_H_ */

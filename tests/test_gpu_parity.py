@@ -1,0 +1,229 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Every case draws seeded inputs, runs tgemm on cuda:0, and compares element by
+element with the oracle: bit-exact where the answer is exactly representable
+(integer-valued products, identities, all-ones), otherwise within
+|g - ref| <= 1e-3 * sum_k |a*b| + ulp16(ref).
+"""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import dense_tiled_gemm_tgemm_amd as tg  # noqa: E402
+from dense_tiled_gemm_tgemm_amd import inputs  # noqa: E402
+
+DEV = "cuda:0"
+NAN16 = 0x7E01          # a quiet-NaN binary16 pattern used as a sentinel
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    tg.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def _dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+
+
+def _host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def _run(A, B, lay, **kw):
+    C = tg.mm(_dev(A), _dev(B), lay, **kw)
+    return _host(C)
+
+
+def _full_check(oracle_mod, A, B, lay, got, what):
+    ref, ab = oracle_mod.gemm(A, B, lay)
+    res = oracle_mod.check(got, ref, ab)
+    assert res["nfail"] == 0, f"{what}: {res}"
+    return res
+
+
+SMALL = [(1, 1, 1), (1, 300, 7), (31, 17, 65), (64, 64, 64), (255, 257, 63), (256, 256, 64),
+         (257, 255, 129), (300, 520, 200), (513, 300, 8), (96, 1100, 1000), (512, 512, 512)]
+
+
+@pytest.mark.parametrize("generic", [0, 1])
+@pytest.mark.parametrize("lay", ["KxN", "NxK"])
+@pytest.mark.parametrize("M,N,K", SMALL)
+def test_small_shapes_full_parity(oracle_mod, M, N, K, lay, generic):
+    print(f"case small M={M} N={N} K={K} {lay} generic={generic}", flush=True)
+    seed = (M * 7 + N * 13 + K * 17) % 100003
+    A = inputs.random_f16((M, K), seed)
+    B = inputs.random_f16((K, N) if lay == "KxN" else (N, K), seed + 1)
+    got = _run(A, B, lay, force_generic=generic)
+    _full_check(oracle_mod, A, B, lay, got, f"{M}x{N}x{K} {lay} generic={generic}")
+
+
+@pytest.mark.parametrize("lay", ["KxN", "NxK"])
+@pytest.mark.parametrize("offset", [0, 1])
+def test_strided_offset_operands_and_guard_band(oracle_mod, lay, offset):
+    """Operands inside larger buffers (ld > row length, optional 1-element offset
+    that leaves them only 2-byte aligned); C inside a NaN-filled buffer with a
+    column guard band and a guard row: every element outside M x N stays intact."""
+    print(f"case strided {lay} offset={offset}", flush=True)
+    M, N, K = 300, 270, 130
+    lda, ldb, ldc = K + 13, (N if lay == "KxN" else K) + 9, N + 11
+    rows_b = K if lay == "KxN" else N
+    Abuf = inputs.random_f16((M * lda + offset,), 71)
+    Bbuf = inputs.random_f16((rows_b * ldb + offset,), 72)
+    A = np.lib.stride_tricks.as_strided(Abuf[offset:], (M, K), (2 * lda, 2))
+    B = np.lib.stride_tricks.as_strided(Bbuf[offset:], (rows_b, K if lay == "NxK" else N), (2 * ldb, 2))
+    Ad, Bd = _dev(Abuf), _dev(Bbuf)
+    Cd = torch.full(((M + 1) * ldc + 5,), NAN16, dtype=torch.int32).to(torch.int16).view(torch.float16).to(DEV)
+    rc = tg.tgemm_f16(M, N, K, Ad.data_ptr() + 2 * offset, lda, Bd.data_ptr() + 2 * offset, ldb, lay,
+                      Cd.data_ptr() + 2 * offset, ldc, torch.cuda.current_stream().cuda_stream)
+    assert rc == tg.TGEMM_OK
+    Cbits = _host(Cd).view(np.uint16)
+    inside = np.zeros(Cbits.shape, dtype=bool)
+    idx = offset + (np.arange(M)[:, None] * ldc + np.arange(N)[None, :])
+    inside[idx.ravel()] = True
+    assert np.all(Cbits[~inside] == NAN16), "write outside M x N"
+    got = Cbits[idx]
+    _full_check(oracle_mod, np.ascontiguousarray(A), np.ascontiguousarray(B), lay, got, "strided")
+    # inputs were not modified
+    assert np.array_equal(_host(Ad).view(np.uint16), Abuf.view(np.uint16))
+    assert np.array_equal(_host(Bd).view(np.uint16), Bbuf.view(np.uint16))
+
+
+@pytest.mark.parametrize("K", [1, 64, 65, 4096, 4099, 8192])
+def test_all_ones_closed_form(K):
+    """All-ones operands: every C element is binary16(K) (4099 -> 4100)."""
+    print(f"case ones K={K}", flush=True)
+    M, N = 300, 260
+    for lay in ("KxN", "NxK"):
+        A = torch.ones((M, K), dtype=torch.float16, device=DEV)
+        B = torch.ones((K, N) if lay == "KxN" else (N, K), dtype=torch.float16, device=DEV)
+        C = tg.mm(A, B, lay)
+        want = float(np.float16(K))
+        assert bool((C == want).all()), f"K={K} {lay}: values {torch.unique(C)[:5]}"
+
+
+@pytest.mark.parametrize("lay", ["KxN", "NxK"])
+def test_identity_closed_form(lay):
+    """B = I gives C = A bit for bit; A = I gives C = B."""
+    print(f"case identity {lay}", flush=True)
+    M, K = 517, 384
+    A = _dev(inputs.random_f16((M, K), 81))
+    I = torch.eye(K, dtype=torch.float16, device=DEV)
+    C = tg.mm(A, I, lay)
+    assert torch.equal(C.view(torch.int16), A.view(torch.int16))
+    Bk = _dev(inputs.random_f16((K, 333), 82))
+    C2 = tg.mm(I, Bk if lay == "KxN" else Bk.t().contiguous(), lay)
+    assert torch.equal(C2.view(torch.int16), Bk.view(torch.int16))
+
+
+def _ternary_case(oracle_mod, M, N, K, lay, seed, npts=None):
+    A = inputs.ternary_f16((M, K), seed)
+    B = inputs.ternary_f16((K, N) if lay == "KxN" else (N, K), seed + 1)
+    C = tg.mm(_dev(A), _dev(B), lay)
+    got = _host(C)
+    if npts is None:
+        ref, _ = oracle_mod.gemm(A, B, lay)
+        sel = got
+    else:
+        I, J = inputs.sample_points(M, N, npts, seed + 2)
+        ref, _ = oracle_mod.gemm_points(A, B, lay, I, J)
+        sel = got[I, J]
+    assert np.abs(ref).max() <= 2048, "ternary sums must stay exactly representable"
+    # every partial sum is an integer below 2^24: the result is exact in any order
+    assert np.array_equal(sel.astype(np.float64), ref), f"ternary {M}x{N}x{K} {lay} not bit-exact"
+    g = got.astype(np.float64)
+    assert np.all(g == np.round(g)) and np.abs(g).max() <= K
+
+
+@pytest.mark.parametrize("name", ["sq256", "sq4096", "ragged", "sq8192_nt", "qkv_proj"])
+def test_ternary_bit_exact_at_workload_shapes(oracle_mod, name):
+    w = inputs.WORKLOADS[name]
+    print(f"case ternary {name}", flush=True)
+    full = w.M * w.N * w.K <= 2 ** 37
+    _ternary_case(oracle_mod, w.M, w.N, w.K, w.b_layout, 100 + w.seed, None if full else 8192)
+
+
+@pytest.mark.parametrize("name", ["sq256", "sq4096", "ragged", "sq8192_nt", "qkv_proj"])
+def test_workload_parity(oracle_mod, name):
+    """The five workloads, launched exactly as the benchmark launches them."""
+    w = inputs.WORKLOADS[name]
+    print(f"case workload {name}", flush=True)
+    A, B = inputs.make_inputs(w)
+    Ad, Bd = _dev(A), _dev(B)
+    C = torch.empty((w.M, w.N), dtype=torch.float16, device=DEV)
+    rc = tg.tgemm_f16(w.M, w.N, w.K, Ad.data_ptr(), w.K, Bd.data_ptr(), B.shape[1], w.b_layout,
+                      C.data_ptr(), w.N, torch.cuda.current_stream().cuda_stream)
+    assert rc == tg.TGEMM_OK
+    got = _host(C)
+    assert np.isfinite(got.astype(np.float32)).all()
+    if w.M * w.N * w.K <= 2 ** 37:
+        ref, ab = oracle_mod.gemm(A, B, w.b_layout)
+        res = oracle_mod.check(got, ref, ab)
+    else:
+        I, J = inputs.sample_points(w.M, w.N, 8192, w.seed + 1000)
+        ref, ab = oracle_mod.gemm_points(A, B, w.b_layout, I, J)
+        res = oracle_mod.check(got[I, J], ref, ab)
+    print(f"  {name}: {res['n']} checked, {res['nfail']} fail, worst {res['worst']:.4f}", flush=True)
+    assert res["nfail"] == 0, res
+
+
+def test_deterministic_and_inputs_unchanged():
+    print("case determinism", flush=True)
+    w = inputs.WORKLOADS["ragged"]
+    A, B = inputs.make_inputs(w)
+    Ad, Bd = _dev(A), _dev(B)
+    C1 = tg.mm(Ad, Bd, w.b_layout)
+    C2 = tg.mm(Ad, Bd, w.b_layout)
+    torch.cuda.synchronize()
+    assert torch.equal(C1.view(torch.int16), C2.view(torch.int16))
+    assert np.array_equal(_host(Ad).view(np.uint16), A.view(np.uint16))
+    assert np.array_equal(_host(Bd).view(np.uint16), B.view(np.uint16))
+
+
+@pytest.mark.parametrize("group_m,num_xcd", [(1, 1), (3, 1), (8, 8), (64, 5), (2, 8)])
+def test_raster_choice_does_not_change_result(group_m, num_xcd):
+    print(f"case raster g={group_m} x={num_xcd}", flush=True)
+    A = _dev(inputs.random_f16((1300, 700), 91))
+    B = _dev(inputs.random_f16((1500, 700), 92))
+    base = tg.mm(A, B, "NxK")
+    other = tg.mm(A, B, "NxK", group_m=group_m, num_xcd=num_xcd)
+    torch.cuda.synchronize()
+    assert torch.equal(base.view(torch.int16), other.view(torch.int16))
+
+
+def test_degenerate_shapes():
+    print("case degenerate", flush=True)
+    # K == 0 writes zeros
+    A = torch.empty((300, 0), dtype=torch.float16, device=DEV)
+    B = torch.empty((0, 270), dtype=torch.float16, device=DEV)
+    C = torch.full((300, 270), 7.0, dtype=torch.float16, device=DEV)
+    tg.mm(A, B, "KxN", out=C)
+    torch.cuda.synchronize()
+    assert bool((C == 0).all())
+    # M == 0 / N == 0 leave C untouched
+    C = torch.full((4, 4), 3.0, dtype=torch.float16, device=DEV)
+    st = torch.cuda.current_stream().cuda_stream
+    assert tg.tgemm_f16(0, 4, 4, A.data_ptr(), 4, B.data_ptr(), 4, "KxN", C.data_ptr(), 4, st) == 0
+    assert tg.tgemm_f16(4, 0, 4, A.data_ptr(), 4, B.data_ptr(), 1, "KxN", C.data_ptr(), 4, st) == 0
+    torch.cuda.synchronize()
+    assert bool((C == 3.0).all())
+
+
+def test_runs_on_a_side_stream(oracle_mod):
+    print("case side stream", flush=True)
+    A = inputs.random_f16((400, 300), 95)
+    B = inputs.random_f16((300, 500), 96)
+    Ad, Bd = _dev(A), _dev(B)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        C = tg.mm(Ad, Bd, "KxN")
+    s.synchronize()
+    _full_check(oracle_mod, A, B, "KxN", C.cpu().numpy(), "side stream")
