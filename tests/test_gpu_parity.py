@@ -209,9 +209,14 @@ def test_degenerate_shapes():
     assert bool((C == 0).all())
     # M == 0 / N == 0 leave C untouched
     C = torch.full((4, 4), 3.0, dtype=torch.float16, device=DEV)
+    A4 = torch.ones((4, 4), dtype=torch.float16, device=DEV)
+    B4 = torch.ones((4, 4), dtype=torch.float16, device=DEV)
     st = torch.cuda.current_stream().cuda_stream
-    assert tg.tgemm_f16(0, 4, 4, A.data_ptr(), 4, B.data_ptr(), 4, "KxN", C.data_ptr(), 4, st) == 0
-    assert tg.tgemm_f16(4, 0, 4, A.data_ptr(), 4, B.data_ptr(), 1, "KxN", C.data_ptr(), 4, st) == 0
+    # M == 0: A may be NULL (no elements), B still holds K x N elements
+    assert tg.tgemm_f16(0, 4, 4, 0, 4, B4.data_ptr(), 4, "KxN", C.data_ptr(), 4, st) == 0
+    # N == 0: B and C hold no elements
+    assert tg.tgemm_f16(4, 0, 4, A4.data_ptr(), 4, 0, 1, "KxN", 0, 1, st) == 0
+    assert tg.tgemm_f16(4, 0, 4, A4.data_ptr(), 4, B4.data_ptr(), 1, "KxN", C.data_ptr(), 4, st) == 0
     torch.cuda.synchronize()
     assert bool((C == 3.0).all())
 
