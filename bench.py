@@ -88,6 +88,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of the GEMM, run device-to-device copies of MIB MiB; used to "
+                         "scale the HBM byte counters (FETCH_SIZE / WRITE_SIZE) of a profiler run")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -97,6 +100,16 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20)
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {args.warmup + args.steps} copies of {n} bytes")
+        return
 
     import dense_tiled_gemm_tgemm_amd as tg
     from dense_tiled_gemm_tgemm_amd import inputs

@@ -52,14 +52,14 @@ def load():
     lib.tgemm_f16.restype = _INT
     lib.tgemm_f16.argtypes = gemm_args
     lib.tgemm_f16_config.restype = _INT
-    lib.tgemm_f16_config.argtypes = gemm_args + [_INT, _INT, _INT]
+    lib.tgemm_f16_config.argtypes = gemm_args + [_INT, _INT, _INT, _INT, _INT]
     lib.tgemm_status_string.restype = ctypes.c_char_p
     lib.tgemm_status_string.argtypes = [_INT]
     lib.tgemm_last_hip_error.restype = _INT
     lib.tgemm_last_hip_error.argtypes = []
     lib.tgemm_plan_f16.restype = _INT
     lib.tgemm_plan_f16.argtypes = [_I64, _I64, _I64, _P, _I64, _P, _I64, _INT, _P, _I64,
-                                   _INT, _INT, _INT, ctypes.POINTER(_I64)]
+                                   _INT, _INT, _INT, _INT, _INT, ctypes.POINTER(_I64)]
     lib.tgemm_tile_of.restype = _INT
     lib.tgemm_tile_of.argtypes = [_I64, _I64, _INT, _INT, _I64, ctypes.POINTER(_I64), ctypes.POINTER(_I64)]
     _lib = lib
@@ -80,19 +80,23 @@ def tgemm_f16(M, N, K, A, lda, B, ldb, b_layout, C, ldc, stream=None) -> int:
 
 
 def tgemm_f16_config(M, N, K, A, lda, B, ldb, b_layout, C, ldc, stream=None,
-                     force_generic=0, group_m=0, num_xcd=0) -> int:
+                     force_generic=0, group_m=0, num_xcd=0, k_step=0, stages=0) -> int:
     return int(load().tgemm_f16_config(M, N, K, A, lda, B, ldb, _LAYOUT[b_layout], C, ldc, stream,
-                                       int(force_generic), int(group_m), int(num_xcd)))
+                                       int(force_generic), int(group_m), int(num_xcd), int(k_step),
+                                       int(stages)))
 
 
-def tgemm_plan_f16(M, N, K, A, lda, B, ldb, b_layout, C, ldc, force_generic=0, group_m=0, num_xcd=0):
+def tgemm_plan_f16(M, N, K, A, lda, B, ldb, b_layout, C, ldc, force_generic=0, group_m=0, num_xcd=0,
+                   k_step=0, stages=0):
     """Host-only plan query: (status, info dict or None)."""
-    info = (_I64 * 8)()
+    info = (_I64 * 10)()
     rc = int(load().tgemm_plan_f16(M, N, K, A, lda, B, ldb, _LAYOUT[b_layout], C, ldc,
-                                   int(force_generic), int(group_m), int(num_xcd), info))
+                                   int(force_generic), int(group_m), int(num_xcd), int(k_step),
+                                   int(stages), info))
     if rc != TGEMM_OK:
         return rc, None
-    keys = ("variant", "bm", "bn", "bk", "workgroups", "group_m", "num_xcd", "threads")
+    keys = ("variant", "bm", "bn", "bk", "workgroups", "group_m", "num_xcd", "threads", "stages",
+            "lds_bytes")
     return rc, dict(zip(keys, (int(v) for v in info)))
 
 
@@ -124,7 +128,7 @@ def _check_tensor(t, name):
 
 
 def mm(A, B, b_layout: str = "KxN", out=None, stream=None, force_generic: int = 0,
-       group_m: int = 0, num_xcd: int = 0):
+       group_m: int = 0, num_xcd: int = 0, k_step: int = 0, stages: int = 0):
     """C = A @ B for fp16 device tensors (fp32 accumulation in the kernel).
 
     A: (M, K). B: (K, N) when b_layout == "KxN", (N, K) when "NxK".
@@ -154,7 +158,7 @@ def mm(A, B, b_layout: str = "KxN", out=None, stream=None, force_generic: int = 
     elif hasattr(stream, "cuda_stream"):
         stream = stream.cuda_stream
     rc = tgemm_f16_config(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, lay, out.data_ptr(), ldc,
-                          stream, force_generic, group_m, num_xcd)
+                          stream, force_generic, group_m, num_xcd, k_step, stages)
     if rc != TGEMM_OK:
         raise TgemmError(rc, f"M={M} N={N} K={K} layout={b_layout}")
     return out

@@ -242,6 +242,255 @@ __device__ __forceinline__ void store_stage(u32x4* __restrict__ sA, u32x4* __res
         store_kxn(sB, rb, tid);
 }
 
+
+// ---------------------------------------------------------------------------
+// Direct HBM/L2 -> LDS staging, used when both operands are K-contiguous
+// (A, and B stored N x K), 16-byte aligned, K a multiple of 8.
+//
+// buffer_load_dwordx4 ... lds writes lane L of a wave instruction to LDS
+// bytes [base + 16L, base + 16L + 16): the destination slot is fixed by the
+// lane, so the XOR swizzle is applied on the source side instead. Wave w's
+// instruction j fills slots (4j + w) * 64 + L, i.e. row r = 32j + (tid >> 3)
+// and physical chunk L & 7, which must hold logical chunk
+// (L & 7) ^ ((r & 7) ^ ((r >> 3) & 1)) - the same for every j.
+//
+// Zero padding (page 4, section 2.4.6.1.3): a lane whose row lies past the
+// operand or whose chunk lies past K gets the byte offset kOob, which is at
+// or beyond the buffer's record count, so the hardware range check returns
+// zeros for it. On such steps each lane also clears its own LDS slots first.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+constexpr unsigned kOob = 0x80000000u;       // record counts are capped below this
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    // s_waitcnt fields: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt_hi[15:14]
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+__device__ __forceinline__ void wait_lgkmcnt0() {
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+}
+
+// Compiler-level fence: no memory access is moved across it. The hardware
+// ordering comes from the explicit s_waitcnt and s_barrier around it.
+#define TG_COMPILER_FENCE() __asm__ __volatile__("" ::: "memory")
+
+__device__ __forceinline__ void block_barrier() {
+    TG_COMPILER_FENCE();
+    __builtin_amdgcn_s_barrier();
+    TG_COMPILER_FENCE();
+}
+
+// Buffer resource over the operand rows row0 .. nrows-1 (row stride ld): the
+// record count is the byte span from the first of these rows to the
+// operand's last element (below 2^31 by the host's stride limit).
+struct Rsrc {
+    const uint16_t* base;
+    int nrec;
+};
+
+__device__ __forceinline__ Rsrc operand_rsrc(const uint16_t* X, int64_t ld, int nrows, int ncols, int row0) {
+    int64_t span = ((int64_t)(nrows - row0 - 1) * ld + ncols) * 2;
+    if (span > (int64_t)kOob - 1) span = (int64_t)kOob - 1;
+    return Rsrc{X + (int64_t)row0 * ld, (int)span};
+}
+
+// LDS layout of one staged operand block (256 rows x KS halves) as 16-byte
+// chunks, CPR = KS / 8 per row, chunk c of row r at slot r*CPR + (c ^ f(r)):
+//   KS = 64: f(r) = (r & 7) ^ ((r >> 3) & 1)
+//   KS = 32: f(r) = ((r >> 1) ^ (r >> 3)) & 3
+// For the 128-bit fragment reads (32 consecutive rows at one chunk per
+// half-wave) both keep every 8-lane and every 16-lane group on distinct
+// 16-byte bank groups, whether LDS is served 128 or 256 bytes per pass.
+template <int KS>
+struct Lds {
+    static constexpr int kCpr = KS / 8;
+    static constexpr int kBlock = 256 * kCpr;          // chunks per operand block
+    static constexpr int kStage = 2 * kBlock;          // A block then B block
+    __device__ static __forceinline__ int swz(int r) {
+        return KS == 64 ? ((r & 7) ^ ((r >> 3) & 1)) : (((r >> 1) ^ (r >> 3)) & 3);
+    }
+    __device__ static __forceinline__ int slot(int r, int c) { return r * kCpr + (c ^ swz(r)); }
+};
+
+template <int KS>
+__device__ __forceinline__ void read_frags(half8 (&fa)[4], half8 (&fb)[4], const u32x4* __restrict__ sA,
+                                           const u32x4* __restrict__ sB, int wm, int wn, int lane, int kk) {
+    const int r32 = lane & 31, khalf = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        fa[i] = __builtin_bit_cast(half8, sA[Lds<KS>::slot(wm * 128 + i * 32 + r32, kk * 2 + khalf)]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        fb[j] = __builtin_bit_cast(half8, sB[Lds<KS>::slot(wn * 128 + j * 32 + r32, kk * 2 + khalf)]);
+}
+
+__device__ __forceinline__ void mma_slice(acc16 (&acc)[4][4], const half8 (&fa)[4], const half8 (&fb)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+}
+
+// Per-lane source offsets of one operand's 256-row panel. A wave instruction
+// j fills LDS slots (4j + w) * 64 + L, i.e. row (256 / CPR) * j + tid / CPR at
+// physical chunk tid % CPR, which must hold logical chunk
+// (tid % CPR) ^ f(row); f(row) does not depend on j. voff[j] is that row's
+// byte offset plus the chunk's, or kOob when the row is past the operand.
+template <int KS>
+struct PanelOffsets {
+    static constexpr int kCpr = KS / 8;
+    unsigned voff[kCpr];
+    unsigned kchunk;      // k offset (elements) of this lane's chunk inside a K step
+};
+
+template <int KS>
+__device__ __forceinline__ PanelOffsets<KS> panel_offsets(int64_t ld, int nrows, int row0, int tid) {
+    constexpr int kCpr = KS / 8;
+    PanelOffsets<KS> p;
+    const int r = tid / kCpr;
+    const unsigned chunk = (unsigned)((tid % kCpr) ^ Lds<KS>::swz(r));
+    p.kchunk = chunk * 8u;
+#pragma unroll
+    for (int j = 0; j < kCpr; ++j) {
+        const int row = r + (256 / kCpr) * j;
+        p.voff[j] = (row0 + row < nrows) ? (unsigned)row * (unsigned)ld * 2u + chunk * 16u : kOob;
+    }
+    return p;
+}
+
+// Issue one K step of one operand into `dst` (this operand's block of a
+// stage): CPR instructions per wave. masked: some lane may lie past the
+// operand or past K, and reads zeros (see above).
+template <int KS>
+__device__ __forceinline__ void dma_step(const Rsrc& rs, const PanelOffsets<KS>& p, int k0, int K,
+                                         bool masked, u32x4* __restrict__ dst, int wave, int lane) {
+#if defined(__HIP_DEVICE_COMPILE__)   // the host pass cannot instantiate these target builtins
+    constexpr int kCpr = KS / 8;
+    // word 3 = 0x00020000: raw (untyped) access, 32-bit data format
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)rs.base, 0, rs.nrec, 0x00020000);
+    if (!masked) {
+#pragma unroll
+        for (int j = 0; j < kCpr; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(dst + (j * 4 + wave) * 64), 16, p.voff[j],
+                                                     (unsigned)k0 * 2u, 0, 0);
+    } else {
+#pragma unroll
+        for (int j = 0; j < kCpr; ++j) dst[(j * 4 + wave) * 64 + lane] = u32x4{0u, 0u, 0u, 0u};
+        TG_COMPILER_FENCE();
+        wait_lgkmcnt0();
+        TG_COMPILER_FENCE();
+        const bool kin = (unsigned)k0 + p.kchunk < (unsigned)K;
+#pragma unroll
+        for (int j = 0; j < kCpr; ++j) {
+            const unsigned v = (kin && p.voff[j] != kOob) ? p.voff[j] + (unsigned)k0 * 2u : kOob;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(dst + (j * 4 + wave) * 64), 16, v, 0u, 0,
+                                                     0);
+        }
+    }
+#endif
+}
+
+// Wait until at most n K steps of this wave's loads are still in flight
+// (each step is LPS load instructions); n is uniform and below 4.
+template <int LPS>
+__device__ __forceinline__ void wait_steps_in_flight(int n) {
+    switch (n) {
+        case 0: wait_vmcnt<0>(); break;
+        case 1: wait_vmcnt<LPS>(); break;
+        case 2: wait_vmcnt<2 * LPS>(); break;
+        default: wait_vmcnt<3 * LPS>(); break;
+    }
+}
+
+// Tile kernel for operands both stored K-contiguous (A, and B as N x K),
+// streamed straight into an S-stage LDS ring of KS-deep K steps. The loads
+// of step t + S go into step t's stage right after the barrier that ends
+// every wave's reads of it, so each step's loads have S - 1 steps of compute
+// to land. That barrier sits before the last k16 slice of step t: the next
+// step's first fragment reads overlap the last slice's MFMAs.
+template <bool VEC_C, int KS, int S>
+__global__ void __launch_bounds__(NTHREADS)
+__attribute__((amdgpu_waves_per_eu(1, 1)))
+tgemm_f16_dma_kernel(Args a) {
+    using L = Lds<KS>;
+    static_assert(KS == 64 || KS == 32, "K step");
+    static_assert(S >= 2 && S <= 5 && S * L::kStage * 16 <= 160 * 1024, "LDS ring must fit 160 KiB");
+    constexpr int kSlices = KS / 16;                 // k16 slices per step (even)
+    constexpr int kLps = 2 * (KS / 8);               // load instructions per step per wave
+    __shared__ u32x4 smem[S * L::kStage];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+
+    int tm, tn;
+    tile_of((int)blockIdx.x, a.W, a.grid_m, a.grid_n, a.group_m, a.num_xcd, &tm, &tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const bool edge = (m0 + BM > a.M) || (n0 + BN > a.N);
+    const int nk = (a.K + KS - 1) / KS;
+    const bool ktail = (a.K % KS) != 0;
+
+    acc16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = acc16{};
+
+    if (nk > 0) {
+        const Rsrc ra = operand_rsrc(a.A, a.lda, a.M, a.K, m0);
+        const Rsrc rb = operand_rsrc(a.B, a.ldb, a.N, a.K, n0);
+        const PanelOffsets<KS> pa = panel_offsets<KS>(a.lda, a.M, m0, tid);
+        const PanelOffsets<KS> pb = panel_offsets<KS>(a.ldb, a.N, n0, tid);
+        // loads of K step t (both operands) into stage `stage`
+#define TG_ISSUE(t, stage)                                                                   \
+    do {                                                                                     \
+        const bool masked_ = edge || (ktail && (t) == nk - 1);                               \
+        u32x4* dst_ = smem + (stage) * L::kStage;                                            \
+        dma_step<KS>(ra, pa, (t) * KS, a.K, masked_, dst_, wave, lane);                      \
+        dma_step<KS>(rb, pb, (t) * KS, a.K, masked_, dst_ + L::kBlock, wave, lane);          \
+    } while (0)
+
+        const int pro = nk < S ? nk : S;
+        for (int t = 0; t < pro; ++t) TG_ISSUE(t, t);
+        wait_steps_in_flight<kLps>(pro - 1);          // step 0 landed
+        block_barrier();
+
+        half8 fa[2][4], fb[2][4];
+        read_frags<KS>(fa[0], fb[0], smem, smem + L::kBlock, wm, wn, lane, 0);
+        int st = 0;                                   // stage of step t
+        for (int t = 0; t < nk; ++t) {
+            const u32x4* sA = smem + st * L::kStage;
+            const u32x4* sB = sA + L::kBlock;
+#pragma unroll
+            for (int kk = 0; kk + 1 < kSlices; ++kk) {
+                read_frags<KS>(fa[(kk + 1) & 1], fb[(kk + 1) & 1], sA, sB, wm, wn, lane, kk + 1);
+                mma_slice(acc, fa[kk & 1], fb[kk & 1]);
+            }
+            TG_COMPILER_FENCE();
+            wait_lgkmcnt0();                          // this wave's reads of stage st returned
+            const int nst = (st + 1 == S) ? 0 : st + 1;
+            if (t + 1 < nk) {
+                const int last = (t + S - 1 < nk - 1) ? t + S - 1 : nk - 1;
+                wait_steps_in_flight<kLps>(last - (t + 1));   // step t + 1 landed
+                block_barrier();
+                if (t + S < nk) TG_ISSUE(t + S, st);
+                const u32x4* nA = smem + nst * L::kStage;
+                read_frags<KS>(fa[0], fb[0], nA, nA + L::kBlock, wm, wn, lane, 0);
+            }
+            mma_slice(acc, fa[(kSlices - 1) & 1], fb[(kSlices - 1) & 1]);
+            st = nst;
+        }
+#undef TG_ISSUE
+    }
+    store_c<VEC_C>(acc, a, m0, n0, wm, wn, lane);
+}
+
 template <int NXK, bool VEC, bool VEC_C>
 __global__ void __launch_bounds__(NTHREADS)
 __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -291,14 +540,27 @@ tgemm_f16_kernel(Args a) {
     store_c<VEC_C>(acc, a, m0, n0, wm, wn, lane);
 }
 
-typedef void (*KernelFn)(Args);
-
 template <int NXK, bool VEC, bool VEC_C>
 static const void* kernel_ptr() {
     return reinterpret_cast<const void*>(&tgemm_f16_kernel<NXK, VEC, VEC_C>);
 }
 
-static const void* pick_kernel(int variant) {
+template <bool VEC_C>
+static const void* dma_kernel_ptr(int k_step, int stages) {
+    if (k_step == 64) return reinterpret_cast<const void*>(&tgemm_f16_dma_kernel<VEC_C, 64, 2>);
+    switch (stages) {
+        case 2: return reinterpret_cast<const void*>(&tgemm_f16_dma_kernel<VEC_C, 32, 2>);
+        case 3: return reinterpret_cast<const void*>(&tgemm_f16_dma_kernel<VEC_C, 32, 3>);
+        case 4: return reinterpret_cast<const void*>(&tgemm_f16_dma_kernel<VEC_C, 32, 4>);
+        default: return reinterpret_cast<const void*>(&tgemm_f16_dma_kernel<VEC_C, 32, 5>);
+    }
+}
+
+static const void* pick_kernel(const Plan& pl) {
+    const int variant = pl.variant;
+    if (variant & kDma)
+        return (variant & kVecC) ? dma_kernel_ptr<true>(pl.k_step, pl.stages)
+                                 : dma_kernel_ptr<false>(pl.k_step, pl.stages);
     switch (variant & 7) {
         case 0: return kernel_ptr<0, false, false>();
         case 1: return kernel_ptr<0, true, false>();
@@ -317,10 +579,11 @@ static thread_local int g_last_hip_error = 0;
 
 extern "C" int tgemm_f16_config(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                                 const void* B, int64_t ldb, int b_layout, void* C, int64_t ldc,
-                                void* stream, int force_generic, int group_m, int num_xcd) {
+                                void* stream, int force_generic, int group_m, int num_xcd, int k_step,
+                                int stages) {
     tg::Plan pl;
     const int rc = tg::make_plan(M, N, K, A, lda, B, ldb, b_layout, C, ldc, force_generic, group_m,
-                                 num_xcd, &pl);
+                                 num_xcd, k_step, stages, &pl);
     if (rc != TGEMM_OK) return rc;
     if (pl.M == 0 || pl.N == 0) return TGEMM_OK;
     tg::Args args;
@@ -338,8 +601,10 @@ extern "C" int tgemm_f16_config(int64_t M, int64_t N, int64_t K, const void* A, 
     args.W = pl.W;
     args.group_m = pl.group_m;
     args.num_xcd = pl.num_xcd;
+    const void* fn = tg::pick_kernel(pl);
+    if (!fn) return TGEMM_ERR_UNSUPPORTED;
     void* kargs[] = {&args};
-    const hipError_t e = hipLaunchKernel(tg::pick_kernel(pl.variant), dim3((unsigned)pl.W),
+    const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)pl.W),
                                          dim3(tg::NTHREADS), kargs, 0, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) {
         tg::g_last_hip_error = (int)e;
@@ -350,7 +615,7 @@ extern "C" int tgemm_f16_config(int64_t M, int64_t N, int64_t K, const void* A, 
 
 extern "C" int tgemm_f16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
                          int64_t ldb, int b_layout, void* C, int64_t ldc, void* stream) {
-    return tgemm_f16_config(M, N, K, A, lda, B, ldb, b_layout, C, ldc, stream, 0, 0, 0);
+    return tgemm_f16_config(M, N, K, A, lda, B, ldb, b_layout, C, ldc, stream, 0, 0, 0, 0, 0);
 }
 
 extern "C" const char* tgemm_status_string(int status) {
@@ -367,20 +632,22 @@ extern "C" int tgemm_last_hip_error(void) { return tg::g_last_hip_error; }
 
 extern "C" int tgemm_plan_f16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
                               int64_t ldb, int b_layout, void* C, int64_t ldc, int force_generic,
-                              int group_m, int num_xcd, int64_t* info) {
+                              int group_m, int num_xcd, int k_step, int stages, int64_t* info) {
     if (!info) return TGEMM_ERR_INVALID;
     tg::Plan pl;
     const int rc = tg::make_plan(M, N, K, A, lda, B, ldb, b_layout, C, ldc, force_generic, group_m,
-                                 num_xcd, &pl);
+                                 num_xcd, k_step, stages, &pl);
     if (rc != TGEMM_OK) return rc;
     info[0] = pl.variant;
     info[1] = tg::BM;
     info[2] = tg::BN;
-    info[3] = tg::BK;
+    info[3] = pl.k_step;
     info[4] = (pl.M == 0 || pl.N == 0) ? 0 : pl.W;
     info[5] = pl.group_m;
     info[6] = pl.num_xcd;
     info[7] = tg::NTHREADS;
+    info[8] = pl.stages;
+    info[9] = (int64_t)pl.stages * 2 * 256 * pl.k_step * 2;   // LDS bytes per workgroup
     return TGEMM_OK;
 }
 

@@ -24,8 +24,16 @@ constexpr int NTHREADS = 256;            // 4 waves of 64 lanes, 2 x 2 over the 
 
 constexpr int kDefaultGroupM = 8;        // page 1, section "Swizzle": GROUP_SIZE_M = 8
 constexpr int kDefaultNumXcd = 8;        // MI355X: 8 accelerator dies of 32 CUs
+// Direct-to-LDS pipeline: K step and LDS ring depth (stages * 32 KiB at K step 32).
+constexpr int kDefaultDmaKStep = 32;
+constexpr int kDefaultDmaStages = 4;
 
-enum : int { kVecAB = 1, kVecC = 2, kLayoutNxK = 4 };
+enum : int { kVecAB = 1, kVecC = 2, kLayoutNxK = 4, kDma = 8 };
+
+// Largest row stride (elements) for the direct-to-LDS path: every in-range
+// byte offset inside a 256-row panel, (255 * ld + K) * 2 with K <= ld, stays
+// below 2^31, under the out-of-range offset the kernel uses for zero padding.
+constexpr int64_t kMaxDmaLd = 4000000;
 
 // Output tile computed by workgroup `wid` of W = grid_m * grid_n.
 // Step 1 (die-aware renumbering): the dispatcher hands workgroup w to die
@@ -58,6 +66,7 @@ struct Plan {
     int variant;       // kVecAB | kVecC | kLayoutNxK bits
     int grid_m, grid_n, W;
     int group_m, num_xcd;
+    int k_step, stages;   // K step per LDS stage and ring depth of the launched kernel
 };
 
 inline bool span_bytes(int64_t rows, int64_t cols, int64_t ld, uint64_t* bytes) {
@@ -82,13 +91,16 @@ inline bool overlaps(const void* p, uint64_t pn, const void* q, uint64_t qn) {
 
 inline int make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
                      int64_t ldb, int b_layout, void* C, int64_t ldc, int force_generic,
-                     int group_m, int num_xcd, Plan* pl) {
+                     int group_m, int num_xcd, int k_step, int stages, Plan* pl) {
     const int64_t kMaxDim = 2147483647;
     if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
         return TGEMM_ERR_INVALID;
     if (b_layout != TGEMM_B_KxN && b_layout != TGEMM_B_NxK) return TGEMM_ERR_INVALID;
     if (force_generic != 0 && force_generic != 1) return TGEMM_ERR_INVALID;
     if (group_m < 0 || group_m > 1024 || num_xcd < 0 || num_xcd > 64) return TGEMM_ERR_INVALID;
+    if (k_step != 0 && k_step != 32 && k_step != 64) return TGEMM_ERR_INVALID;
+    if (stages != 0 && (stages < 2 || stages > 5)) return TGEMM_ERR_INVALID;
+    if (k_step == 64 && stages != 0 && stages != 2) return TGEMM_ERR_INVALID;  // 2 x 64 KiB fills LDS
     const int64_t one = 1;
     if (lda < (K > one ? K : one)) return TGEMM_ERR_INVALID;
     const int64_t bmin = (b_layout == TGEMM_B_KxN) ? N : K;
@@ -128,8 +140,17 @@ inline int make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
     const bool vec_ab = !force_generic && ((uintptr_t)A % 16 == 0) && (lda % 8 == 0) &&
                         ((uintptr_t)B % 16 == 0) && (ldb % 8 == 0);
     const bool vec_c = ((uintptr_t)C % 8 == 0) && (ldc % 4 == 0);
+    const bool dma = vec_ab && b_layout == TGEMM_B_NxK && (K % 8 == 0) && lda <= kMaxDmaLd &&
+                     ldb <= kMaxDmaLd;
     pl->variant = (vec_ab ? kVecAB : 0) | (vec_c ? kVecC : 0) |
-                  (b_layout == TGEMM_B_NxK ? kLayoutNxK : 0);
+                  (b_layout == TGEMM_B_NxK ? kLayoutNxK : 0) | (dma ? kDma : 0);
+    if (dma) {
+        pl->k_step = k_step ? k_step : kDefaultDmaKStep;
+        pl->stages = pl->k_step == 64 ? 2 : (stages ? stages : kDefaultDmaStages);
+    } else {
+        pl->k_step = BK;
+        pl->stages = 2;
+    }
     return TGEMM_OK;
 }
 

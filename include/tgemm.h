@@ -86,14 +86,21 @@ int tgemm_f16(int64_t M, int64_t N, int64_t K,
  *   num_xcd:       number of dies the workgroups are spread over for the
  *                  die-aware renumbering; 0 = default (8 on MI355X);
  *                  1 disables the renumbering; 1..64 otherwise.
- * Out-of-range choices return TGEMM_ERR_INVALID.
+ *   k_step:        K depth of one LDS stage of the direct-to-LDS path
+ *                  (operands K-contiguous, 16-byte aligned, K % 8 == 0):
+ *                  0 = default, 32 or 64.
+ *   stages:        LDS ring depth of that path: 0 = default, 2..5 (k_step 64
+ *                  allows only 2). Other paths ignore k_step and stages.
+ * Out-of-range choices return TGEMM_ERR_INVALID. Every choice computes the
+ * same C bit for bit (each output's k order is fixed by its tile position).
  */
 int tgemm_f16_config(int64_t M, int64_t N, int64_t K,
                      const void* A, int64_t lda,
                      const void* B, int64_t ldb, int b_layout,
                      void* C, int64_t ldc,
                      void* stream,
-                     int force_generic, int group_m, int num_xcd);
+                     int force_generic, int group_m, int num_xcd,
+                     int k_step, int stages);
 
 /* Human-readable text of a TGEMM_* status code (static storage). */
 const char* tgemm_status_string(int status);
@@ -103,19 +110,20 @@ int tgemm_last_hip_error(void);
 
 /*
  * Host-only planning query (no GPU call): the launch tgemm_f16_config would
- * make for these arguments. Returns TGEMM_OK and fills info[0..7]:
+ * make for these arguments. Returns TGEMM_OK and fills info[0..9]:
  *   info[0] variant bits: bit0 128-bit A/B loads, bit1 64-bit C stores,
- *           bit2 B layout is NxK
- *   info[1] tile rows (BM)   info[2] tile columns (BN)   info[3] K step (BK)
+ *           bit2 B layout is NxK, bit3 operands streamed directly into LDS
+ *   info[1] tile rows (BM)   info[2] tile columns (BN)   info[3] K step
  *   info[4] workgroups launched  info[5] group_m  info[6] num_xcd
- *   info[7] threads per workgroup
- * or the same error tgemm_f16_config would return. `info` must hold 8 values.
+ *   info[7] threads per workgroup  info[8] LDS stages  info[9] LDS bytes
+ * or the same error tgemm_f16_config would return. `info` must hold 10 values.
  */
 int tgemm_plan_f16(int64_t M, int64_t N, int64_t K,
                    const void* A, int64_t lda,
                    const void* B, int64_t ldb, int b_layout,
                    void* C, int64_t ldc,
                    int force_generic, int group_m, int num_xcd,
+                   int k_step, int stages,
                    int64_t* info);
 
 /*

@@ -65,13 +65,17 @@ def _plan(M, N, K, A=PA, lda=None, B=PB, ldb=None, lay="KxN", C=PC, ldc=None, **
     dict(M=4, N=4, K=4, group_m=-1),
     dict(M=4, N=4, K=4, group_m=1025),
     dict(M=4, N=4, K=4, num_xcd=65),
+    dict(M=4, N=4, K=4, k_step=16),
+    dict(M=4, N=4, K=4, stages=1),
+    dict(M=4, N=4, K=4, stages=6),
+    dict(M=4, N=4, K=4, k_step=64, stages=3),
 ])
 def test_invalid_arguments_rejected(args):
     rc, info = _plan(**args)
     assert rc == tg.TGEMM_ERR_INVALID and info is None
     # the launching entry point returns the same code without touching the GPU
     a = dict(args)
-    kw = {k: a.pop(k) for k in ("force_generic", "group_m", "num_xcd") if k in a}
+    kw = {k: a.pop(k) for k in ("force_generic", "group_m", "num_xcd", "k_step", "stages") if k in a}
     M, N, K = a["M"], a["N"], a["K"]
     lay = a.get("lay", "KxN")
     lda = a.get("lda", K)
@@ -85,8 +89,8 @@ def test_invalid_arguments_rejected(args):
 def test_bad_layout_rejected():
     lib = tg.load()
     assert lib.tgemm_f16(4, 4, 4, PA, 4, PB, 4, 2, PC, 4, None) == tg.TGEMM_ERR_INVALID
-    info = (ctypes.c_int64 * 8)()
-    assert lib.tgemm_plan_f16(4, 4, 4, PA, 4, PB, 4, -1, PC, 4, 0, 0, 0, info) == tg.TGEMM_ERR_INVALID
+    info = (ctypes.c_int64 * 10)()
+    assert lib.tgemm_plan_f16(4, 4, 4, PA, 4, PB, 4, -1, PC, 4, 0, 0, 0, 0, 0, info) == tg.TGEMM_ERR_INVALID
 
 
 def test_empty_outputs_are_noops_without_gpu():
@@ -101,9 +105,17 @@ def test_empty_outputs_are_noops_without_gpu():
 def test_plan_variants_and_grid():
     rc, info = _plan(8192, 8192, 8192, lay="NxK")
     assert rc == 0
-    assert info["variant"] == 1 | 2 | 4
-    assert (info["bm"], info["bn"], info["bk"], info["threads"]) == (256, 256, 64, 256)
+    assert info["variant"] == 1 | 2 | 4 | 8
     assert info["workgroups"] == 32 * 32 and info["group_m"] == 8 and info["num_xcd"] == 8
+    assert (info["bm"], info["bn"], info["threads"]) == (256, 256, 256)
+    assert (info["bk"], info["stages"], info["lds_bytes"]) == (32, 4, 4 * 32 * 1024)
+    rc, info = _plan(8192, 8192, 8192, lay="NxK", k_step=64)
+    assert (info["bk"], info["stages"], info["lds_bytes"]) == (64, 2, 128 * 1024)
+    rc, info = _plan(8192, 8192, 8192, lay="NxK", k_step=32, stages=5)
+    assert (info["bk"], info["stages"], info["lds_bytes"]) == (32, 5, 160 * 1024)
+    # K not a multiple of 8: no direct-to-LDS
+    rc, info = _plan(512, 512, 516, lay="NxK", lda=520, ldb=520)
+    assert info["variant"] == 1 | 2 | 4 and info["bk"] == 64
     # ragged: odd strides -> element-wise loads and stores
     rc, info = _plan(3001, 5003, 4099)
     assert rc == 0 and info["variant"] == 0 and info["workgroups"] == 12 * 20
@@ -115,6 +127,11 @@ def test_plan_variants_and_grid():
     assert info["variant"] == 2
     rc, info = _plan(256, 256, 256, C=PC + 2)
     assert info["variant"] == 1
+    # direct-to-LDS needs both operands K-contiguous, aligned, and ld within 32-bit panel offsets
+    rc, info = _plan(512, 512, 512, lay="NxK", force_generic=1)
+    assert info["variant"] == 2 | 4
+    rc, info = _plan(512, 512, 512, lay="NxK", lda=4_000_008)
+    assert info["variant"] == 1 | 2 | 4
     # group_m larger than the tile rows is clamped (same map)
     rc, info = _plan(512, 4096, 64, group_m=100)
     assert info["group_m"] == 2

@@ -65,15 +65,22 @@ def test_small_shapes_full_parity(oracle_mod, M, N, K, lay, generic):
     _full_check(oracle_mod, A, B, lay, got, f"{M}x{N}x{K} {lay} generic={generic}")
 
 
-@pytest.mark.parametrize("lay", ["KxN", "NxK"])
-@pytest.mark.parametrize("offset", [0, 1])
-def test_strided_offset_operands_and_guard_band(oracle_mod, lay, offset):
-    """Operands inside larger buffers (ld > row length, optional 1-element offset
-    that leaves them only 2-byte aligned); C inside a NaN-filled buffer with a
+@pytest.mark.parametrize("lay,offset,M,N,K,pad", [
+    ("KxN", 0, 300, 270, 130, (13, 9, 11)),
+    ("KxN", 1, 300, 270, 130, (13, 9, 11)),
+    ("NxK", 0, 300, 270, 130, (13, 9, 11)),
+    ("NxK", 1, 300, 270, 130, (13, 9, 11)),
+    # 16-byte-aligned strides: the direct-to-LDS path, with edge tiles and a K tail
+    ("NxK", 0, 700, 600, 264, (8, 16, 8)),
+    ("NxK", 8, 520, 777, 72, (24, 8, 4)),
+    ("KxN", 0, 700, 600, 264, (8, 16, 8)),
+])
+def test_strided_offset_operands_and_guard_band(oracle_mod, lay, offset, M, N, K, pad):
+    """Operands inside larger buffers (ld > row length, optional element offset
+    that may leave them only 2-byte aligned); C inside a NaN-filled buffer with a
     column guard band and a guard row: every element outside M x N stays intact."""
-    print(f"case strided {lay} offset={offset}", flush=True)
-    M, N, K = 300, 270, 130
-    lda, ldb, ldc = K + 13, (N if lay == "KxN" else K) + 9, N + 11
+    print(f"case strided {lay} offset={offset} {M}x{N}x{K} pad={pad}", flush=True)
+    lda, ldb, ldc = K + pad[0], (N if lay == "KxN" else K) + pad[1], N + pad[2]
     rows_b = K if lay == "KxN" else N
     Abuf = inputs.random_f16((M * lda + offset,), 71)
     Bbuf = inputs.random_f16((rows_b * ldb + offset,), 72)
@@ -232,3 +239,23 @@ def test_runs_on_a_side_stream(oracle_mod):
         C = tg.mm(Ad, Bd, "KxN")
     s.synchronize()
     _full_check(oracle_mod, A, B, "KxN", C.cpu().numpy(), "side stream")
+
+
+PIPES = [(64, 2), (32, 2), (32, 3), (32, 4), (32, 5)]
+
+
+@pytest.mark.parametrize("M,N,K", [(512, 512, 512), (700, 600, 264), (1000, 1300, 8), (256, 256, 4096 + 32)])
+def test_pipeline_choices_are_bit_identical(oracle_mod, M, N, K):
+    """Every direct-to-LDS pipeline (K step x ring depth) and the register-staged
+    path produce the same bits: each output's k16 slices are summed in the same order."""
+    print(f"case pipelines {M}x{N}x{K}", flush=True)
+    A = inputs.random_f16((M, K), M + K)
+    B = inputs.random_f16((N, K), N + K)
+    Ad, Bd = _dev(A), _dev(B)
+    base = tg.mm(Ad, Bd, "NxK", force_generic=1)
+    got = _host(base)
+    _full_check(oracle_mod, A, B, "NxK", got, f"pipelines {M}x{N}x{K}")
+    for ks, st in PIPES:
+        C = tg.mm(Ad, Bd, "NxK", k_step=ks, stages=st)
+        torch.cuda.synchronize()
+        assert torch.equal(C.view(torch.int16), base.view(torch.int16)), (ks, st)
