@@ -249,19 +249,19 @@ __device__ __forceinline__ void store_stage(u32x4* __restrict__ sA, u32x4* __res
 //
 // buffer_load_dwordx4 ... lds writes lane L of a wave instruction to LDS
 // bytes [base + 16L, base + 16L + 16): the destination slot is fixed by the
-// lane, so the XOR swizzle is applied on the source side instead. Wave w's
-// instruction j fills slots (4j + w) * 64 + L, i.e. row r = 32j + (tid >> 3)
-// and physical chunk L & 7, which must hold logical chunk
-// (L & 7) ^ ((r & 7) ^ ((r >> 3) & 1)) - the same for every j.
+// lane, so the XOR swizzle is applied on the source side instead.
 //
-// Zero padding (page 4, section 2.4.6.1.3): a lane whose row lies past the
-// operand or whose chunk lies past K gets the byte offset kOob, which is at
-// or beyond the buffer's record count, so the hardware range check returns
-// zeros for it. On such steps each lane also clears its own LDS slots first.
+// Zero padding (page 4, section 2.4.6.1.3) comes from the buffer range
+// check: a lane whose byte offset (vector + scalar part) reaches the
+// resource's record count reads zeros, and the zeros are what it writes into
+// its LDS slot. Rows past the operand carry the offset bit kOob; on the last,
+// partial K step so do chunks past K; and steps past the end of K use a
+// scalar offset of kOob, so they touch no memory at all. The main loop is
+// therefore the same for edge and interior tiles, and branch-free.
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-constexpr unsigned kOob = 0x80000000u;       // record counts are capped below this
+constexpr unsigned kOob = 0x80000000u;       // record counts stay below this
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -284,9 +284,9 @@ __device__ __forceinline__ void block_barrier() {
     TG_COMPILER_FENCE();
 }
 
-// Buffer resource over the operand rows row0 .. nrows-1 (row stride ld): the
-// record count is the byte span from the first of these rows to the
-// operand's last element (below 2^31 by the host's stride limit).
+// Base pointer and record count of the buffer resource over operand rows
+// row0 .. nrows-1 (row stride ld): the byte span from the first of these rows
+// to the operand's last element (below 2^31 by the host's stride limit).
 struct Rsrc {
     const uint16_t* base;
     int nrec;
@@ -328,91 +328,99 @@ __device__ __forceinline__ void read_frags(half8 (&fa)[4], half8 (&fb)[4], const
         fb[j] = __builtin_bit_cast(half8, sB[Lds<KS>::slot(wn * 128 + j * 32 + r32, kk * 2 + khalf)]);
 }
 
-__device__ __forceinline__ void mma_slice(acc16 (&acc)[4][4], const half8 (&fa)[4], const half8 (&fb)[4]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
-}
-
-// Per-lane source offsets of one operand's 256-row panel. A wave instruction
-// j fills LDS slots (4j + w) * 64 + L, i.e. row (256 / CPR) * j + tid / CPR at
-// physical chunk tid % CPR, which must hold logical chunk
-// (tid % CPR) ^ f(row); f(row) does not depend on j. voff[j] is that row's
-// byte offset plus the chunk's, or kOob when the row is past the operand.
+// Per-lane source offsets of the 2 * CPR load instructions of a K step (A's
+// CPR rows, then B's). A wave instruction j fills LDS slots (4j + w) * 64 + L,
+// i.e. row (256 / CPR) * j + tid / CPR at physical chunk tid % CPR, which
+// must hold logical chunk (tid % CPR) ^ f(row); f(row) does not depend on j.
+// voff[idx] is that row's byte offset plus the chunk's, with kOob set when
+// the row lies past its operand. tail_oob is kOob when this lane's chunk lies
+// past K on the last, partial K step (0 otherwise).
 template <int KS>
-struct PanelOffsets {
+struct LaneLoads {
     static constexpr int kCpr = KS / 8;
-    unsigned voff[kCpr];
-    unsigned kchunk;      // k offset (elements) of this lane's chunk inside a K step
+    unsigned voff[2 * kCpr];
+    unsigned tail_oob;
 };
 
 template <int KS>
-__device__ __forceinline__ PanelOffsets<KS> panel_offsets(int64_t ld, int nrows, int row0, int tid) {
+__device__ __forceinline__ LaneLoads<KS> lane_loads(const Args& a, int m0, int n0, int tid) {
     constexpr int kCpr = KS / 8;
-    PanelOffsets<KS> p;
+    LaneLoads<KS> p;
     const int r = tid / kCpr;
     const unsigned chunk = (unsigned)((tid % kCpr) ^ Lds<KS>::swz(r));
-    p.kchunk = chunk * 8u;
 #pragma unroll
     for (int j = 0; j < kCpr; ++j) {
         const int row = r + (256 / kCpr) * j;
-        p.voff[j] = (row0 + row < nrows) ? (unsigned)row * (unsigned)ld * 2u + chunk * 16u : kOob;
+        p.voff[j] = ((unsigned)row * (unsigned)a.lda * 2u + chunk * 16u) | (m0 + row < a.M ? 0u : kOob);
+        p.voff[kCpr + j] = ((unsigned)row * (unsigned)a.ldb * 2u + chunk * 16u) | (n0 + row < a.N ? 0u : kOob);
     }
+    const int krem = a.K % KS;             // valid k of the last step (0: the last step is full)
+    p.tail_oob = (krem != 0 && (int)chunk * 8 >= krem) ? kOob : 0u;
     return p;
 }
 
-// Issue one K step of one operand into `dst` (this operand's block of a
-// stage): CPR instructions per wave. masked: some lane may lie past the
-// operand or past K, and reads zeros (see above).
+// Load instruction `idx` (0 .. 2*CPR-1) of a K step into `stage`, with the
+// step's scalar offset and this lane's extra out-of-range bit `oob`.
 template <int KS>
-__device__ __forceinline__ void dma_step(const Rsrc& rs, const PanelOffsets<KS>& p, int k0, int K,
-                                         bool masked, u32x4* __restrict__ dst, int wave, int lane) {
+__device__ __forceinline__ void issue_load(const Rsrc& ra, const Rsrc& rb, const LaneLoads<KS>& p, int idx,
+                                           unsigned soff, unsigned oob, u32x4* __restrict__ stage, int wave) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the host pass cannot instantiate these target builtins
     constexpr int kCpr = KS / 8;
+    const bool isb = idx >= kCpr;
+    const int j = isb ? idx - kCpr : idx;
+    const Rsrc& rs = isb ? rb : ra;
     // word 3 = 0x00020000: raw (untyped) access, 32-bit data format
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)rs.base, 0, rs.nrec, 0x00020000);
-    if (!masked) {
-#pragma unroll
-        for (int j = 0; j < kCpr; ++j)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(dst + (j * 4 + wave) * 64), 16, p.voff[j],
-                                                     (unsigned)k0 * 2u, 0, 0);
-    } else {
-#pragma unroll
-        for (int j = 0; j < kCpr; ++j) dst[(j * 4 + wave) * 64 + lane] = u32x4{0u, 0u, 0u, 0u};
-        TG_COMPILER_FENCE();
-        wait_lgkmcnt0();
-        TG_COMPILER_FENCE();
-        const bool kin = (unsigned)k0 + p.kchunk < (unsigned)K;
-#pragma unroll
-        for (int j = 0; j < kCpr; ++j) {
-            const unsigned v = (kin && p.voff[j] != kOob) ? p.voff[j] + (unsigned)k0 * 2u : kOob;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(dst + (j * 4 + wave) * 64), 16, v, 0u, 0,
-                                                     0);
-        }
-    }
+    u32x4* dst = stage + (isb ? Lds<KS>::kBlock : 0) + (j * 4 + wave) * 64;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)dst, 16, p.voff[idx] | oob, soff, 0, 0);
 #endif
 }
 
-// Wait until at most n K steps of this wave's loads are still in flight
-// (each step is LPS load instructions); n is uniform and below 4.
-template <int LPS>
-__device__ __forceinline__ void wait_steps_in_flight(int n) {
-    switch (n) {
-        case 0: wait_vmcnt<0>(); break;
-        case 1: wait_vmcnt<LPS>(); break;
-        case 2: wait_vmcnt<2 * LPS>(); break;
-        default: wait_vmcnt<3 * LPS>(); break;
+// One k16 slice: 16 MFMAs on the current fragments. The next slice's eight
+// fragment reads follow MFMAs 0..7, in the order the next slice consumes
+// them (A0, B0..B3, A1..A3); when LOADS, the load instructions
+// [ld_first, ld_first + CPR) follow MFMAs 8..15, so the newest read is eight
+// MFMAs old when the slice ends. With one wave per SIMD every other
+// instruction competes with MFMA issue, so the order is pinned at both the
+// IR and the machine level.
+template <int KS, bool LOADS>
+__device__ __forceinline__ void slice(acc16 (&acc)[4][4], const half8 (&fa)[4], const half8 (&fb)[4],
+                                      half8 (&na)[4], half8 (&nb)[4], const u32x4* __restrict__ rA,
+                                      const u32x4* __restrict__ rB, int wm, int wn, int lane, int next_kk,
+                                      const Rsrc& ra, const Rsrc& rb, const LaneLoads<KS>& p, int ld_first,
+                                      unsigned soff, unsigned oob, u32x4* __restrict__ ld_stage, int wave) {
+    constexpr int kHalf = KS / 8;
+    const int r32 = lane & 31, khalf = lane >> 5;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        const int i = q >> 2, j = q & 3;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+        if (q < 8) {
+            if (q >= 1 && q <= 4)
+                nb[q - 1] = __builtin_bit_cast(
+                    half8, rB[Lds<KS>::slot(wn * 128 + (q - 1) * 32 + r32, next_kk * 2 + khalf)]);
+            else {
+                const int ai = q == 0 ? 0 : q - 4;
+                na[ai] = __builtin_bit_cast(half8, rA[Lds<KS>::slot(wm * 128 + ai * 32 + r32, next_kk * 2 + khalf)]);
+            }
+        } else if (LOADS && q - 8 < kHalf) {
+            issue_load<KS>(ra, rb, p, ld_first + (q - 8), soff, oob, ld_stage, wave);
+        }
+        TG_COMPILER_FENCE();
+        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
 // Tile kernel for operands both stored K-contiguous (A, and B as N x K),
-// streamed straight into an S-stage LDS ring of KS-deep K steps. The loads
-// of step t + S go into step t's stage right after the barrier that ends
-// every wave's reads of it, so each step's loads have S - 1 steps of compute
-// to land. That barrier sits before the last k16 slice of step t: the next
-// step's first fragment reads overlap the last slice's MFMAs.
+// streamed straight into an S-stage LDS ring of KS-deep K steps. Step t's
+// loads go into stage t mod S in two halves: the first right after the
+// barrier that ends every wave's reads of that stage (during the last k16
+// slice of step t - S), the second during the first slice of step t - S + 1.
+// Each step's loads thus have about S - 1 steps of compute to land. The
+// barrier sits before the last slice of a step: the next step's first
+// fragment reads overlap that slice's MFMAs. Every step issues the same
+// number of loads (steps past K read nothing and write zeros into stages
+// that are never read), so all wait counts are constants.
 template <bool VEC_C, int KS, int S>
 __global__ void __launch_bounds__(NTHREADS)
 __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -421,7 +429,8 @@ tgemm_f16_dma_kernel(Args a) {
     static_assert(KS == 64 || KS == 32, "K step");
     static_assert(S >= 2 && S <= 5 && S * L::kStage * 16 <= 160 * 1024, "LDS ring must fit 160 KiB");
     constexpr int kSlices = KS / 16;                 // k16 slices per step (even)
-    constexpr int kLps = 2 * (KS / 8);               // load instructions per step per wave
+    constexpr int kCpr = KS / 8;
+    constexpr int kLps = 2 * kCpr;                   // load instructions per step per wave
     __shared__ u32x4 smem[S * L::kStage];
 
     const int tid = threadIdx.x;
@@ -432,9 +441,7 @@ tgemm_f16_dma_kernel(Args a) {
     int tm, tn;
     tile_of((int)blockIdx.x, a.W, a.grid_m, a.grid_n, a.group_m, a.num_xcd, &tm, &tn);
     const int m0 = tm * BM, n0 = tn * BN;
-    const bool edge = (m0 + BM > a.M) || (n0 + BN > a.N);
     const int nk = (a.K + KS - 1) / KS;
-    const bool ktail = (a.K % KS) != 0;
 
     acc16 acc[4][4];
 #pragma unroll
@@ -445,20 +452,18 @@ tgemm_f16_dma_kernel(Args a) {
     if (nk > 0) {
         const Rsrc ra = operand_rsrc(a.A, a.lda, a.M, a.K, m0);
         const Rsrc rb = operand_rsrc(a.B, a.ldb, a.N, a.K, n0);
-        const PanelOffsets<KS> pa = panel_offsets<KS>(a.lda, a.M, m0, tid);
-        const PanelOffsets<KS> pb = panel_offsets<KS>(a.ldb, a.N, n0, tid);
-        // loads of K step t (both operands) into stage `stage`
-#define TG_ISSUE(t, stage)                                                                   \
-    do {                                                                                     \
-        const bool masked_ = edge || (ktail && (t) == nk - 1);                               \
-        u32x4* dst_ = smem + (stage) * L::kStage;                                            \
-        dma_step<KS>(ra, pa, (t) * KS, a.K, masked_, dst_, wave, lane);                      \
-        dma_step<KS>(rb, pb, (t) * KS, a.K, masked_, dst_ + L::kBlock, wave, lane);          \
-    } while (0)
+        const LaneLoads<KS> p = lane_loads<KS>(a, m0, n0, tid);
+        // scalar offset and extra out-of-range bits of K step t
+#define TG_SOFF(t) ((t) < nk ? (unsigned)(t) * (unsigned)(KS * 2) : kOob)
+#define TG_OOB(t) ((t) == nk - 1 ? p.tail_oob : 0u)
 
-        const int pro = nk < S ? nk : S;
-        for (int t = 0; t < pro; ++t) TG_ISSUE(t, t);
-        wait_steps_in_flight<kLps>(pro - 1);          // step 0 landed
+        // prologue: steps 0 .. S-2 and the first half of step S-1
+        for (int t = 0; t < S; ++t) {
+            u32x4* stage = smem + t * L::kStage;
+            const int n = (t + 1 < S) ? kLps : kCpr;
+            for (int idx = 0; idx < n; ++idx) issue_load<KS>(ra, rb, p, idx, TG_SOFF(t), TG_OOB(t), stage, wave);
+        }
+        wait_vmcnt<(S - 2) * kLps + kCpr>();          // step 0 landed
         block_barrier();
 
         half8 fa[2][4], fb[2][4];
@@ -467,26 +472,30 @@ tgemm_f16_dma_kernel(Args a) {
         for (int t = 0; t < nk; ++t) {
             const u32x4* sA = smem + st * L::kStage;
             const u32x4* sB = sA + L::kBlock;
+            const int pst = (st == 0) ? S - 1 : st - 1;   // stage of step t + S - 1
+            const int nst = (st + 1 == S) ? 0 : st + 1;
+            // slice 0 carries the second half of step t + S - 1's loads
+            slice<KS, true>(acc, fa[0], fb[0], fa[1], fb[1], sA, sB, wm, wn, lane, 1, ra, rb, p, kCpr,
+                            TG_SOFF(t + S - 1), TG_OOB(t + S - 1), smem + pst * L::kStage, wave);
 #pragma unroll
-            for (int kk = 0; kk + 1 < kSlices; ++kk) {
-                read_frags<KS>(fa[(kk + 1) & 1], fb[(kk + 1) & 1], sA, sB, wm, wn, lane, kk + 1);
-                mma_slice(acc, fa[kk & 1], fb[kk & 1]);
-            }
+            for (int kk = 1; kk + 1 < kSlices; ++kk)
+                slice<KS, false>(acc, fa[kk & 1], fb[kk & 1], fa[(kk + 1) & 1], fb[(kk + 1) & 1], sA, sB, wm, wn,
+                                 lane, kk + 1, ra, rb, p, 0, 0u, 0u, smem, wave);
             TG_COMPILER_FENCE();
             wait_lgkmcnt0();                          // this wave's reads of stage st returned
-            const int nst = (st + 1 == S) ? 0 : st + 1;
-            if (t + 1 < nk) {
-                const int last = (t + S - 1 < nk - 1) ? t + S - 1 : nk - 1;
-                wait_steps_in_flight<kLps>(last - (t + 1));   // step t + 1 landed
-                block_barrier();
-                if (t + S < nk) TG_ISSUE(t + S, st);
-                const u32x4* nA = smem + nst * L::kStage;
-                read_frags<KS>(fa[0], fb[0], nA, nA + L::kBlock, wm, wn, lane, 0);
-            }
-            mma_slice(acc, fa[(kSlices - 1) & 1], fb[(kSlices - 1) & 1]);
+            wait_vmcnt<(S - 2) * kLps>();             // step t + 1 landed
+            block_barrier();
+            // the first half of step t + S's loads goes into the stage just released
+            const u32x4* nA = smem + nst * L::kStage;
+            slice<KS, true>(acc, fa[(kSlices - 1) & 1], fb[(kSlices - 1) & 1], fa[0], fb[0], nA, nA + L::kBlock,
+                            wm, wn, lane, 0, ra, rb, p, 0, TG_SOFF(t + S), TG_OOB(t + S), smem + st * L::kStage,
+                            wave);
             st = nst;
         }
-#undef TG_ISSUE
+        // no load may still be writing this workgroup's LDS when it exits
+        wait_vmcnt<0>();
+#undef TG_SOFF
+#undef TG_OOB
     }
     store_c<VEC_C>(acc, a, m0, n0, wm, wn, lane);
 }

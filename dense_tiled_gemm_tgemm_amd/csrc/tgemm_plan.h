@@ -26,7 +26,7 @@ constexpr int kDefaultGroupM = 8;        // page 1, section "Swizzle": GROUP_SIZ
 constexpr int kDefaultNumXcd = 8;        // MI355X: 8 accelerator dies of 32 CUs
 // Direct-to-LDS pipeline: K step and LDS ring depth (stages * 32 KiB at K step 32).
 constexpr int kDefaultDmaKStep = 32;
-constexpr int kDefaultDmaStages = 4;
+constexpr int kDefaultDmaStages = 3;
 
 enum : int { kVecAB = 1, kVecC = 2, kLayoutNxK = 4, kDma = 8 };
 

@@ -108,7 +108,7 @@ def test_plan_variants_and_grid():
     assert info["variant"] == 1 | 2 | 4 | 8
     assert info["workgroups"] == 32 * 32 and info["group_m"] == 8 and info["num_xcd"] == 8
     assert (info["bm"], info["bn"], info["threads"]) == (256, 256, 256)
-    assert (info["bk"], info["stages"], info["lds_bytes"]) == (32, 4, 4 * 32 * 1024)
+    assert (info["bk"], info["stages"], info["lds_bytes"]) == (32, 3, 3 * 32 * 1024)
     rc, info = _plan(8192, 8192, 8192, lay="NxK", k_step=64)
     assert (info["bk"], info["stages"], info["lds_bytes"]) == (64, 2, 128 * 1024)
     rc, info = _plan(8192, 8192, 8192, lay="NxK", k_step=32, stages=5)
