@@ -329,11 +329,17 @@ __device__ __forceinline__ void read_frags(half8 (&fa)[4], half8 (&fb)[4], const
 }
 
 // Per-lane source offsets of the 2 * CPR load instructions of a K step (A's
-// CPR rows, then B's). A wave instruction j fills LDS slots (4j + w) * 64 + L,
-// i.e. row (256 / CPR) * j + tid / CPR at physical chunk tid % CPR, which
-// must hold logical chunk (tid % CPR) ^ f(row); f(row) does not depend on j.
-// voff[idx] is that row's byte offset plus the chunk's, with kOob set when
-// the row lies past its operand. tail_oob is kOob when this lane's chunk lies
+// CPR, then B's). A wave instruction j fills LDS slots (4j + w) * 64 + L.
+//  * K-contiguous operand (A; B stored N x K): slot -> row (256 / CPR) * j +
+//    tid / CPR, physical chunk tid % CPR, which must hold logical chunk
+//    (tid % CPR) ^ f(row); f(row) does not depend on j. The K step advances
+//    the scalar offset by KS * 2 bytes.
+//  * B stored K x N, kept N-contiguous ([k][n], 32 chunks of 8 n per k row):
+//    slot -> k row 8j + (tid >> 5), physical chunk tid & 31, holding logical
+//    chunk g^-1 of it (see KnLds). The K step advances the scalar offset by
+//    KS * ldb * 2 bytes; k rows past K lie past the buffer and read zeros.
+// voff[idx] is the row's byte offset plus the chunk's, with kOob set when the
+// row lies past its operand. tail_oob is kOob when this lane's A chunk lies
 // past K on the last, partial K step (0 otherwise).
 template <int KS>
 struct LaneLoads {
@@ -342,7 +348,18 @@ struct LaneLoads {
     unsigned tail_oob;
 };
 
-template <int KS>
+// B stored K x N in LDS as [k][n]: 16-byte chunk c (n = 8c .. 8c+7) of k row
+// k sits at physical chunk c ^ 2(k & 3) ^ 8((c >> 1) & 1). For the
+// transposing fragment reads (16 lanes: 4 k rows x 32 contiguous bytes) this
+// keeps every 16- and 32-lane group on distinct banks.
+struct KnLds {
+    __device__ static __forceinline__ int phys(int c, int k) { return c ^ (2 * (k & 3)) ^ (8 * ((c >> 1) & 1)); }
+    __device__ static __forceinline__ int logical(int p, int k) {
+        return p ^ (2 * (k & 3)) ^ (8 * (((p >> 1) & 1) ^ (k & 1)));
+    }
+};
+
+template <int KS, int NXK>
 __device__ __forceinline__ LaneLoads<KS> lane_loads(const Args& a, int m0, int n0, int tid) {
     constexpr int kCpr = KS / 8;
     LaneLoads<KS> p;
@@ -352,7 +369,13 @@ __device__ __forceinline__ LaneLoads<KS> lane_loads(const Args& a, int m0, int n
     for (int j = 0; j < kCpr; ++j) {
         const int row = r + (256 / kCpr) * j;
         p.voff[j] = ((unsigned)row * (unsigned)a.lda * 2u + chunk * 16u) | (m0 + row < a.M ? 0u : kOob);
-        p.voff[kCpr + j] = ((unsigned)row * (unsigned)a.ldb * 2u + chunk * 16u) | (n0 + row < a.N ? 0u : kOob);
+        if (NXK) {
+            p.voff[kCpr + j] = ((unsigned)row * (unsigned)a.ldb * 2u + chunk * 16u) | (n0 + row < a.N ? 0u : kOob);
+        } else {
+            const int krow = 8 * j + (tid >> 5);
+            const unsigned c = (unsigned)KnLds::logical(tid & 31, krow);
+            p.voff[kCpr + j] = (unsigned)krow * (unsigned)a.ldb * 2u + c * 16u;
+        }
     }
     const int krem = a.K % KS;             // valid k of the last step (0: the last step is full)
     p.tail_oob = (krem != 0 && (int)chunk * 8 >= krem) ? kOob : 0u;
@@ -360,10 +383,12 @@ __device__ __forceinline__ LaneLoads<KS> lane_loads(const Args& a, int m0, int n
 }
 
 // Load instruction `idx` (0 .. 2*CPR-1) of a K step into `stage`, with the
-// step's scalar offset and this lane's extra out-of-range bit `oob`.
+// step's scalar offsets (soa for A, sob for B) and this lane's extra
+// out-of-range bit `oob` for A.
 template <int KS>
 __device__ __forceinline__ void issue_load(const Rsrc& ra, const Rsrc& rb, const LaneLoads<KS>& p, int idx,
-                                           unsigned soff, unsigned oob, u32x4* __restrict__ stage, int wave) {
+                                           unsigned soa, unsigned sob, unsigned oob, u32x4* __restrict__ stage,
+                                           int wave) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the host pass cannot instantiate these target builtins
     constexpr int kCpr = KS / 8;
     const bool isb = idx >= kCpr;
@@ -372,61 +397,103 @@ __device__ __forceinline__ void issue_load(const Rsrc& ra, const Rsrc& rb, const
     // word 3 = 0x00020000: raw (untyped) access, 32-bit data format
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)rs.base, 0, rs.nrec, 0x00020000);
     u32x4* dst = stage + (isb ? Lds<KS>::kBlock : 0) + (j * 4 + wave) * 64;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)dst, 16, p.voff[idx] | oob, soff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)dst, 16, isb ? p.voff[idx] : (p.voff[idx] | oob),
+                                             isb ? sob : soa, 0, 0);
 #endif
 }
 
-// One k16 slice: 16 MFMAs on the current fragments. The next slice's eight
-// fragment reads follow MFMAs 0..7, in the order the next slice consumes
-// them (A0, B0..B3, A1..A3); when LOADS, the load instructions
-// [ld_first, ld_first + CPR) follow MFMAs 8..15, so the newest read is eight
-// MFMAs old when the slice ends. With one wave per SIMD every other
-// instruction competes with MFMA issue, so the order is pinned at both the
-// IR and the machine level.
-template <int KS, bool LOADS>
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Four k values (k0 .. k0+3, from 4 k rows) of one n column of B stored
+// [k][n] in LDS, by the transposing read: in each 16-lane group, lane i
+// points at k row k0 + i/4, columns n0 + 4(i % 4) .. +3, and lane j receives
+// column n0 + j.
+__device__ __forceinline__ s16x4 read_tr(const u32x4* __restrict__ sB, int krow, int ncol) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const int c = ncol >> 3;
+    const int byte = krow * 512 + KnLds::phys(c, krow) * 16 + (ncol & 7) * 2;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)((__attribute__((address_space(3))) char*)(sB) + byte));
+#else
+    return s16x4{};
+#endif
+}
+
+// One k16 slice: 16 MFMAs on the current fragments, with the next slice's
+// fragment reads and (when LOADS) kHalf = CPR load instructions placed
+// between them, reads first, in the order the next slice consumes them:
+// A0, B0..B3, A1..A3. A K-contiguous B fragment is one 128-bit read; a
+// [k][n] B fragment is two transposing 64-bit reads (k +0..3, k +4..7), so
+// that layout has 12 reads per slice and CPR must be 4. The newest read is
+// at least four MFMAs old when the slice ends. With one wave per SIMD every
+// other instruction competes with MFMA issue, so the order is pinned at both
+// the IR and the machine level.
+template <int KS, int NXK, bool LOADS>
 __device__ __forceinline__ void slice(acc16 (&acc)[4][4], const half8 (&fa)[4], const half8 (&fb)[4],
                                       half8 (&na)[4], half8 (&nb)[4], const u32x4* __restrict__ rA,
                                       const u32x4* __restrict__ rB, int wm, int wn, int lane, int next_kk,
                                       const Rsrc& ra, const Rsrc& rb, const LaneLoads<KS>& p, int ld_first,
-                                      unsigned soff, unsigned oob, u32x4* __restrict__ ld_stage, int wave) {
+                                      unsigned soa, unsigned sob, unsigned oob, u32x4* __restrict__ ld_stage,
+                                      int wave) {
     constexpr int kHalf = KS / 8;
+    constexpr int kReads = NXK ? 8 : 12;
+    static_assert(kReads + kHalf <= 16, "reads and loads must fit the 16 MFMA slots");
     const int r32 = lane & 31, khalf = lane >> 5;
+    s16x4 lo[4];
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
         const int i = q >> 2, j = q & 3;
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
-        if (q < 8) {
-            if (q >= 1 && q <= 4)
-                nb[q - 1] = __builtin_bit_cast(
-                    half8, rB[Lds<KS>::slot(wn * 128 + (q - 1) * 32 + r32, next_kk * 2 + khalf)]);
-            else {
-                const int ai = q == 0 ? 0 : q - 4;
+        if (q < kReads) {
+            // read slot q -> fragment: NxK: A0,B0,B1,B2,B3,A1,A2,A3; KxN: A0,B0h0,B0h1,...,B3h1,A1,A2,A3
+            const int nbr = NXK ? 4 : 8;
+            if (q >= 1 && q <= nbr) {
+                if (NXK) {
+                    nb[q - 1] = __builtin_bit_cast(
+                        half8, rB[Lds<KS>::slot(wn * 128 + (q - 1) * 32 + r32, next_kk * 2 + khalf)]);
+                } else {
+                    const int fbi = (q - 1) >> 1, h = (q - 1) & 1;
+                    const int g = lane >> 4, jl = lane & 15;
+                    const int ncol = wn * 128 + fbi * 32 + 16 * (g & 1) + 4 * (jl & 3);
+                    const int krow = next_kk * 16 + 8 * (g >> 1) + 4 * h + (jl >> 2);
+                    const s16x4 v = read_tr(rB, krow, ncol);
+                    if (h == 0) {
+                        lo[fbi] = v;
+                    } else {
+                        nb[fbi] = __builtin_bit_cast(half8, __builtin_shufflevector(lo[fbi], v, 0, 1, 2, 3, 4, 5, 6, 7));
+                    }
+                }
+            } else {
+                const int ai = q == 0 ? 0 : q - nbr;
                 na[ai] = __builtin_bit_cast(half8, rA[Lds<KS>::slot(wm * 128 + ai * 32 + r32, next_kk * 2 + khalf)]);
             }
-        } else if (LOADS && q - 8 < kHalf) {
-            issue_load<KS>(ra, rb, p, ld_first + (q - 8), soff, oob, ld_stage, wave);
+        } else if (LOADS && q - kReads < kHalf) {
+            issue_load<KS>(ra, rb, p, ld_first + (q - kReads), soa, sob, oob, ld_stage, wave);
         }
         TG_COMPILER_FENCE();
         __builtin_amdgcn_sched_barrier(0);
     }
 }
 
-// Tile kernel for operands both stored K-contiguous (A, and B as N x K),
-// streamed straight into an S-stage LDS ring of KS-deep K steps. Step t's
-// loads go into stage t mod S in two halves: the first right after the
-// barrier that ends every wave's reads of that stage (during the last k16
-// slice of step t - S), the second during the first slice of step t - S + 1.
-// Each step's loads thus have about S - 1 steps of compute to land. The
-// barrier sits before the last slice of a step: the next step's first
-// fragment reads overlap that slice's MFMAs. Every step issues the same
-// number of loads (steps past K read nothing and write zeros into stages
-// that are never read), so all wait counts are constants.
-template <bool VEC_C, int KS, int S>
+// Tile kernel with both operands streamed straight into an S-stage LDS
+// ring of KS-deep K steps: A K-contiguous, B either K-contiguous (stored
+// N x K, NXK = 1) or kept [k][n] and transposed on read (stored K x N).
+// Step t's loads go into stage t mod S in two halves: the first right after
+// the barrier that ends every wave's reads of that stage (during the last
+// k16 slice of step t - S), the second during the first slice of step
+// t - S + 1. Each step's loads thus have about S - 1 steps of compute to
+// land. The barrier sits before the last slice of a step: the next step's
+// first fragment reads overlap that slice's MFMAs. Every step issues the
+// same number of loads (steps past K read nothing and write zeros into
+// stages that are never read), so all wait counts are constants.
+template <int NXK, bool VEC_C, int KS, int S>
 __global__ void __launch_bounds__(NTHREADS)
 __attribute__((amdgpu_waves_per_eu(1, 1)))
 tgemm_f16_dma_kernel(Args a) {
     using L = Lds<KS>;
     static_assert(KS == 64 || KS == 32, "K step");
+    static_assert(NXK || KS == 32, "B stored K x N streams 32-deep K steps");
     static_assert(S >= 2 && S <= 5 && S * L::kStage * 16 <= 160 * 1024, "LDS ring must fit 160 KiB");
     constexpr int kSlices = KS / 16;                 // k16 slices per step (even)
     constexpr int kCpr = KS / 8;
@@ -451,23 +518,38 @@ tgemm_f16_dma_kernel(Args a) {
 
     if (nk > 0) {
         const Rsrc ra = operand_rsrc(a.A, a.lda, a.M, a.K, m0);
-        const Rsrc rb = operand_rsrc(a.B, a.ldb, a.N, a.K, n0);
-        const LaneLoads<KS> p = lane_loads<KS>(a, m0, n0, tid);
-        // scalar offset and extra out-of-range bits of K step t
-#define TG_SOFF(t) ((t) < nk ? (unsigned)(t) * (unsigned)(KS * 2) : kOob)
+        // B: N x K rows n0.. ; K x N columns n0.. of all K rows
+        const Rsrc rb = NXK ? operand_rsrc(a.B, a.ldb, a.N, a.K, n0) : operand_rsrc(a.B + n0, a.ldb, a.K, a.N - n0, 0);
+        const LaneLoads<KS> p = lane_loads<KS, NXK>(a, m0, n0, tid);
+        const unsigned bstep = NXK ? (unsigned)(KS * 2) : (unsigned)KS * (unsigned)a.ldb * 2u;
+        // scalar offsets and A's extra out-of-range bits of K step t
+#define TG_SOA(t) ((t) < nk ? (unsigned)(t) * (unsigned)(KS * 2) : kOob)
+#define TG_SOB(t) ((t) < nk ? (unsigned)(t) * bstep : kOob)
 #define TG_OOB(t) ((t) == nk - 1 ? p.tail_oob : 0u)
 
         // prologue: steps 0 .. S-2 and the first half of step S-1
         for (int t = 0; t < S; ++t) {
             u32x4* stage = smem + t * L::kStage;
             const int n = (t + 1 < S) ? kLps : kCpr;
-            for (int idx = 0; idx < n; ++idx) issue_load<KS>(ra, rb, p, idx, TG_SOFF(t), TG_OOB(t), stage, wave);
+            for (int idx = 0; idx < n; ++idx)
+                issue_load<KS>(ra, rb, p, idx, TG_SOA(t), TG_SOB(t), TG_OOB(t), stage, wave);
         }
         wait_vmcnt<(S - 2) * kLps + kCpr>();          // step 0 landed
         block_barrier();
 
         half8 fa[2][4], fb[2][4];
         read_frags<KS>(fa[0], fb[0], smem, smem + L::kBlock, wm, wn, lane, 0);
+        if (!NXK) {
+            const int g = lane >> 4, jl = lane & 15;
+#pragma unroll
+            for (int f = 0; f < 4; ++f) {
+                const int ncol = wn * 128 + f * 32 + 16 * (g & 1) + 4 * (jl & 3);
+                const int krow = 8 * (g >> 1) + (jl >> 2);
+                const s16x4 v0 = read_tr(smem + L::kBlock, krow, ncol);
+                const s16x4 v1 = read_tr(smem + L::kBlock, krow + 4, ncol);
+                fb[0][f] = __builtin_bit_cast(half8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+            }
+        }
         int st = 0;                                   // stage of step t
         for (int t = 0; t < nk; ++t) {
             const u32x4* sA = smem + st * L::kStage;
@@ -475,26 +557,28 @@ tgemm_f16_dma_kernel(Args a) {
             const int pst = (st == 0) ? S - 1 : st - 1;   // stage of step t + S - 1
             const int nst = (st + 1 == S) ? 0 : st + 1;
             // slice 0 carries the second half of step t + S - 1's loads
-            slice<KS, true>(acc, fa[0], fb[0], fa[1], fb[1], sA, sB, wm, wn, lane, 1, ra, rb, p, kCpr,
-                            TG_SOFF(t + S - 1), TG_OOB(t + S - 1), smem + pst * L::kStage, wave);
+            slice<KS, NXK, true>(acc, fa[0], fb[0], fa[1], fb[1], sA, sB, wm, wn, lane, 1, ra, rb, p, kCpr,
+                                 TG_SOA(t + S - 1), TG_SOB(t + S - 1), TG_OOB(t + S - 1), smem + pst * L::kStage,
+                                 wave);
 #pragma unroll
             for (int kk = 1; kk + 1 < kSlices; ++kk)
-                slice<KS, false>(acc, fa[kk & 1], fb[kk & 1], fa[(kk + 1) & 1], fb[(kk + 1) & 1], sA, sB, wm, wn,
-                                 lane, kk + 1, ra, rb, p, 0, 0u, 0u, smem, wave);
+                slice<KS, NXK, false>(acc, fa[kk & 1], fb[kk & 1], fa[(kk + 1) & 1], fb[(kk + 1) & 1], sA, sB, wm,
+                                      wn, lane, kk + 1, ra, rb, p, 0, 0u, 0u, 0u, smem, wave);
             TG_COMPILER_FENCE();
             wait_lgkmcnt0();                          // this wave's reads of stage st returned
             wait_vmcnt<(S - 2) * kLps>();             // step t + 1 landed
             block_barrier();
             // the first half of step t + S's loads goes into the stage just released
             const u32x4* nA = smem + nst * L::kStage;
-            slice<KS, true>(acc, fa[(kSlices - 1) & 1], fb[(kSlices - 1) & 1], fa[0], fb[0], nA, nA + L::kBlock,
-                            wm, wn, lane, 0, ra, rb, p, 0, TG_SOFF(t + S), TG_OOB(t + S), smem + st * L::kStage,
-                            wave);
+            slice<KS, NXK, true>(acc, fa[(kSlices - 1) & 1], fb[(kSlices - 1) & 1], fa[0], fb[0], nA,
+                                 nA + L::kBlock, wm, wn, lane, 0, ra, rb, p, 0, TG_SOA(t + S), TG_SOB(t + S),
+                                 TG_OOB(t + S), smem + st * L::kStage, wave);
             st = nst;
         }
         // no load may still be writing this workgroup's LDS when it exits
         wait_vmcnt<0>();
-#undef TG_SOFF
+#undef TG_SOA
+#undef TG_SOB
 #undef TG_OOB
     }
     store_c<VEC_C>(acc, a, m0, n0, wm, wn, lane);
@@ -555,21 +639,29 @@ static const void* kernel_ptr() {
 }
 
 template <bool VEC_C>
-static const void* dma_kernel_ptr(int k_step, int stages) {
-    if (k_step == 64) return reinterpret_cast<const void*>(&tgemm_f16_dma_kernel<VEC_C, 64, 2>);
+static const void* dma_kernel_ptr(int nxk, int k_step, int stages) {
+    if (!nxk) {
+        switch (stages) {
+            case 2: return reinterpret_cast<const void*>(&tgemm_f16_dma_kernel<0, VEC_C, 32, 2>);
+            case 3: return reinterpret_cast<const void*>(&tgemm_f16_dma_kernel<0, VEC_C, 32, 3>);
+            case 4: return reinterpret_cast<const void*>(&tgemm_f16_dma_kernel<0, VEC_C, 32, 4>);
+            default: return reinterpret_cast<const void*>(&tgemm_f16_dma_kernel<0, VEC_C, 32, 5>);
+        }
+    }
+    if (k_step == 64) return reinterpret_cast<const void*>(&tgemm_f16_dma_kernel<1, VEC_C, 64, 2>);
     switch (stages) {
-        case 2: return reinterpret_cast<const void*>(&tgemm_f16_dma_kernel<VEC_C, 32, 2>);
-        case 3: return reinterpret_cast<const void*>(&tgemm_f16_dma_kernel<VEC_C, 32, 3>);
-        case 4: return reinterpret_cast<const void*>(&tgemm_f16_dma_kernel<VEC_C, 32, 4>);
-        default: return reinterpret_cast<const void*>(&tgemm_f16_dma_kernel<VEC_C, 32, 5>);
+        case 2: return reinterpret_cast<const void*>(&tgemm_f16_dma_kernel<1, VEC_C, 32, 2>);
+        case 3: return reinterpret_cast<const void*>(&tgemm_f16_dma_kernel<1, VEC_C, 32, 3>);
+        case 4: return reinterpret_cast<const void*>(&tgemm_f16_dma_kernel<1, VEC_C, 32, 4>);
+        default: return reinterpret_cast<const void*>(&tgemm_f16_dma_kernel<1, VEC_C, 32, 5>);
     }
 }
 
 static const void* pick_kernel(const Plan& pl) {
     const int variant = pl.variant;
     if (variant & kDma)
-        return (variant & kVecC) ? dma_kernel_ptr<true>(pl.k_step, pl.stages)
-                                 : dma_kernel_ptr<false>(pl.k_step, pl.stages);
+        return (variant & kVecC) ? dma_kernel_ptr<true>(pl.layout, pl.k_step, pl.stages)
+                                 : dma_kernel_ptr<false>(pl.layout, pl.k_step, pl.stages);
     switch (variant & 7) {
         case 0: return kernel_ptr<0, false, false>();
         case 1: return kernel_ptr<0, true, false>();

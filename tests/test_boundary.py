@@ -126,7 +126,13 @@ def test_plan_variants_and_grid():
     rc, info = _plan(256, 256, 256, A=PA + 8)
     assert info["variant"] == 2
     rc, info = _plan(256, 256, 256, C=PC + 2)
-    assert info["variant"] == 1
+    assert info["variant"] == 1 | 8          # K x N, aligned: direct-to-LDS with transposing reads
+    rc, info = _plan(4096, 4096, 4096)
+    assert info["variant"] == 1 | 2 | 8 and (info["bk"], info["stages"]) == (32, 3)
+    rc, info = _plan(4096, 4096, 4096, k_step=64)
+    assert rc == tg.TGEMM_ERR_INVALID         # K x N streams 32-deep steps only
+    rc, info = _plan(4096, 4096, 4099, lda=4104)
+    assert info["variant"] == 1 | 2          # K % 8 != 0: register-staged path
     # direct-to-LDS needs both operands K-contiguous, aligned, and ld within 32-bit panel offsets
     rc, info = _plan(512, 512, 512, lay="NxK", force_generic=1)
     assert info["variant"] == 2 | 4
