@@ -346,6 +346,7 @@ struct LaneLoads {
     static constexpr int kCpr = KS / 8;
     unsigned voff[2 * kCpr];
     unsigned tail_oob;
+    unsigned kchunk;      // k offset (elements) of this lane's K-contiguous chunk inside a K step
 };
 
 // B stored K x N in LDS as [k][n]: 16-byte chunk c (n = 8c .. 8c+7) of k row
@@ -379,13 +380,14 @@ __device__ __forceinline__ LaneLoads<KS> lane_loads(const Args& a, int m0, int n
     }
     const int krem = a.K % KS;             // valid k of the last step (0: the last step is full)
     p.tail_oob = (krem != 0 && (int)chunk * 8 >= krem) ? kOob : 0u;
+    p.kchunk = chunk * 8u;
     return p;
 }
 
 // Load instruction `idx` (0 .. 2*CPR-1) of a K step into `stage`, with the
 // step's scalar offsets (soa for A, sob for B) and this lane's extra
-// out-of-range bit `oob` for A.
-template <int KS>
+// out-of-range bit `oob` for its K-contiguous chunks.
+template <int KS, int NXK>
 __device__ __forceinline__ void issue_load(const Rsrc& ra, const Rsrc& rb, const LaneLoads<KS>& p, int idx,
                                            unsigned soa, unsigned sob, unsigned oob, u32x4* __restrict__ stage,
                                            int wave) {
@@ -397,9 +399,67 @@ __device__ __forceinline__ void issue_load(const Rsrc& ra, const Rsrc& rb, const
     // word 3 = 0x00020000: raw (untyped) access, 32-bit data format
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)rs.base, 0, rs.nrec, 0x00020000);
     u32x4* dst = stage + (isb ? Lds<KS>::kBlock : 0) + (j * 4 + wave) * 64;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)dst, 16, isb ? p.voff[idx] : (p.voff[idx] | oob),
-                                             isb ? sob : soa, 0, 0);
+    // chunks past K: A, and B when it is K-contiguous (a K x N B's rows past K lie past its buffer)
+    const unsigned v = (isb && !NXK) ? p.voff[idx] : (p.voff[idx] | oob);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)dst, 16, v, isb ? sob : soa, 0, 0);
 #endif
+}
+
+// Eight binary16 values, p[e] for e < nv and zero past nv, as one 16-byte
+// LDS chunk.
+__device__ __forceinline__ u32x4 chunk_from(const uint16_t* __restrict__ p, int nv) {
+    unsigned w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const unsigned lo = (2 * q < nv) ? (unsigned)p[2 * q] : 0u;
+        const unsigned hi = (2 * q + 1 < nv) ? (unsigned)p[2 * q + 1] : 0u;
+        w[q] = lo | (hi << 16);
+    }
+    return u32x4{w[0], w[1], w[2], w[3]};
+}
+
+// Last K step (k0 = its first k): the 16-byte chunks that straddle the end
+// of valid data. A chunk straddling K (A, and B stored N x K) was loaded
+// whole, so past K it holds the next row's elements; and in an operand's
+// final row the range check zeroes a straddling access entirely. Each lane
+// rebuilds such chunks of its own slots from element loads - the valid part,
+// zeros after it - once its loads have landed and before the barrier that
+// publishes the stage. B stored K x N straddles only at column N, and only
+// its final row K - 1 loses data (other rows read the next row past N,
+// which lands in output columns that are never stored).
+template <int KS, int NXK>
+__device__ __forceinline__ void fix_last_step(u32x4* __restrict__ stage, const LaneLoads<KS>& p, const Args& a,
+                                              int m0, int n0, int k0, int tid, int wave, int lane) {
+    constexpr int kCpr = KS / 8;
+    const int r = tid / kCpr;
+    const int kc = k0 + (int)p.kchunk;
+    const int nv = a.K - kc;                          // valid elements of this lane's K chunk
+    if (nv > 0 && nv < 8) {
+#pragma unroll
+        for (int j = 0; j < kCpr; ++j) {
+            const int row = r + (256 / kCpr) * j;
+            const int slot = (j * 4 + wave) * 64 + lane;
+            if (m0 + row < a.M) stage[slot] = chunk_from(a.A + (int64_t)(m0 + row) * a.lda + kc, nv);
+            if (NXK && n0 + row < a.N)
+                stage[Lds<KS>::kBlock + slot] = chunk_from(a.B + (int64_t)(n0 + row) * a.ldb + kc, nv);
+        }
+    }
+    if (!NXK) {
+#pragma unroll
+        for (int j = 0; j < kCpr; ++j) {
+            const int krow = 8 * j + (tid >> 5);
+            const int c = KnLds::logical(tid & 31, krow);
+            const int nc = n0 + 8 * c;
+            const int nvn = a.N - nc;
+            if (k0 + krow == a.K - 1 && nvn > 0 && nvn < 8)
+                stage[Lds<KS>::kBlock + (j * 4 + wave) * 64 + lane] =
+                    chunk_from(a.B + (int64_t)(a.K - 1) * a.ldb + nc, nvn);
+        }
+    }
+    TG_COMPILER_FENCE();
+    wait_lgkmcnt0();
+    __builtin_amdgcn_s_waitcnt(0);                    // element loads returned and written
+    TG_COMPILER_FENCE();
 }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -469,7 +529,7 @@ __device__ __forceinline__ void slice(acc16 (&acc)[4][4], const half8 (&fa)[4], 
                 na[ai] = __builtin_bit_cast(half8, rA[Lds<KS>::slot(wm * 128 + ai * 32 + r32, next_kk * 2 + khalf)]);
             }
         } else if (LOADS && q - kReads < kHalf) {
-            issue_load<KS>(ra, rb, p, ld_first + (q - kReads), soa, sob, oob, ld_stage, wave);
+            issue_load<KS, NXK>(ra, rb, p, ld_first + (q - kReads), soa, sob, oob, ld_stage, wave);
         }
         TG_COMPILER_FENCE();
         __builtin_amdgcn_sched_barrier(0);
@@ -532,9 +592,13 @@ tgemm_f16_dma_kernel(Args a) {
             u32x4* stage = smem + t * L::kStage;
             const int n = (t + 1 < S) ? kLps : kCpr;
             for (int idx = 0; idx < n; ++idx)
-                issue_load<KS>(ra, rb, p, idx, TG_SOA(t), TG_SOB(t), TG_OOB(t), stage, wave);
+                issue_load<KS, NXK>(ra, rb, p, idx, TG_SOA(t), TG_SOB(t), TG_OOB(t), stage, wave);
         }
+        // the last step has chunks straddling the end of valid data
+        const bool straddle = (a.K % 8) != 0 || (!NXK && (a.N % 8) != 0);
+        const int klast = (nk - 1) * KS;
         wait_vmcnt<(S - 2) * kLps + kCpr>();          // step 0 landed
+        if (straddle && nk == 1) fix_last_step<KS, NXK>(smem, p, a, m0, n0, klast, tid, wave, lane);
         block_barrier();
 
         half8 fa[2][4], fb[2][4];
@@ -567,6 +631,8 @@ tgemm_f16_dma_kernel(Args a) {
             TG_COMPILER_FENCE();
             wait_lgkmcnt0();                          // this wave's reads of stage st returned
             wait_vmcnt<(S - 2) * kLps>();             // step t + 1 landed
+            if (straddle && t + 2 == nk)
+                fix_last_step<KS, NXK>(smem + nst * L::kStage, p, a, m0, n0, klast, tid, wave, lane);
             block_barrier();
             // the first half of step t + S's loads goes into the stage just released
             const u32x4* nA = smem + nst * L::kStage;

@@ -140,10 +140,11 @@ inline int make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
     const bool vec_ab = !force_generic && ((uintptr_t)A % 16 == 0) && (lda % 8 == 0) &&
                         ((uintptr_t)B % 16 == 0) && (ldb % 8 == 0);
     const bool vec_c = ((uintptr_t)C % 8 == 0) && (ldc % 4 == 0);
-    // direct-to-LDS: 16-byte aligned K-contiguous A with K % 8 == 0 (whole
-    // 16-byte chunks), row strides small enough for 32-bit panel offsets; a
-    // K x N B additionally needs every byte offset (K + 32) * ldb * 2 < 2^31.
-    const bool dma = vec_ab && (K % 8 == 0) && lda <= kMaxDmaLd &&
+    // direct-to-LDS (any 2-byte alignment: gfx950 buffer loads accept
+    // unaligned addresses): row strides small enough for 32-bit panel
+    // offsets; a K x N B additionally needs every byte offset
+    // (K + 32) * ldb * 2 below 2^31.
+    const bool dma = !force_generic && lda <= kMaxDmaLd &&
                      (b_layout == TGEMM_B_NxK ? ldb <= kMaxDmaLd : (K + 32) * ldb < (int64_t(1) << 30));
     if (dma && b_layout == TGEMM_B_KxN && k_step == 64) return TGEMM_ERR_INVALID;  // K x N streams 32-deep steps
     pl->variant = (vec_ab ? kVecAB : 0) | (vec_c ? kVecC : 0) |

@@ -103,9 +103,10 @@ def test_empty_outputs_are_noops_without_gpu():
 
 
 def test_plan_variants_and_grid():
+    V, C8, NXK, DMA = 1, 2, 4, 8
     rc, info = _plan(8192, 8192, 8192, lay="NxK")
     assert rc == 0
-    assert info["variant"] == 1 | 2 | 4 | 8
+    assert info["variant"] == V | C8 | NXK | DMA
     assert info["workgroups"] == 32 * 32 and info["group_m"] == 8 and info["num_xcd"] == 8
     assert (info["bm"], info["bn"], info["threads"]) == (256, 256, 256)
     assert (info["bk"], info["stages"], info["lds_bytes"]) == (32, 3, 3 * 32 * 1024)
@@ -113,31 +114,30 @@ def test_plan_variants_and_grid():
     assert (info["bk"], info["stages"], info["lds_bytes"]) == (64, 2, 128 * 1024)
     rc, info = _plan(8192, 8192, 8192, lay="NxK", k_step=32, stages=5)
     assert (info["bk"], info["stages"], info["lds_bytes"]) == (32, 5, 160 * 1024)
-    # K not a multiple of 8: no direct-to-LDS
-    rc, info = _plan(512, 512, 516, lay="NxK", lda=520, ldb=520)
-    assert info["variant"] == 1 | 2 | 4 and info["bk"] == 64
-    # ragged: odd strides -> element-wise loads and stores
+    # ragged, odd strides (2-byte aligned rows): still streamed into LDS; element-wise C stores
     rc, info = _plan(3001, 5003, 4099)
-    assert rc == 0 and info["variant"] == 0 and info["workgroups"] == 12 * 20
-    # 16-byte-aligned, ld % 8 == 0 but forced generic
+    assert rc == 0 and info["variant"] == DMA and info["workgroups"] == 12 * 20
+    # forced register-staged path with element-wise loads
     rc, info = _plan(256, 256, 256, force_generic=1)
-    assert info["variant"] == 2
-    # base misaligned to 8 bytes -> no vector loads; C 8-byte aligned keeps 64-bit stores
+    assert info["variant"] == C8
+    rc, info = _plan(512, 512, 512, lay="NxK", force_generic=1)
+    assert info["variant"] == C8 | NXK
+    # base not 16-byte aligned: no 128-bit flag, still direct-to-LDS; C 8-byte aligned keeps 64-bit stores
     rc, info = _plan(256, 256, 256, A=PA + 8)
-    assert info["variant"] == 2
+    assert info["variant"] == C8 | DMA
     rc, info = _plan(256, 256, 256, C=PC + 2)
-    assert info["variant"] == 1 | 8          # K x N, aligned: direct-to-LDS with transposing reads
+    assert info["variant"] == V | DMA
     rc, info = _plan(4096, 4096, 4096)
-    assert info["variant"] == 1 | 2 | 8 and (info["bk"], info["stages"]) == (32, 3)
+    assert info["variant"] == V | C8 | DMA and (info["bk"], info["stages"]) == (32, 3)
     rc, info = _plan(4096, 4096, 4096, k_step=64)
     assert rc == tg.TGEMM_ERR_INVALID         # K x N streams 32-deep steps only
     rc, info = _plan(4096, 4096, 4099, lda=4104)
-    assert info["variant"] == 1 | 2          # K % 8 != 0: register-staged path
-    # direct-to-LDS needs both operands K-contiguous, aligned, and ld within 32-bit panel offsets
-    rc, info = _plan(512, 512, 512, lay="NxK", force_generic=1)
-    assert info["variant"] == 2 | 4
+    assert info["variant"] == V | C8 | DMA    # K % 8 != 0 is fine: the straddling chunk is cleared
+    # strides past the 32-bit panel-offset limit: register-staged path
     rc, info = _plan(512, 512, 512, lay="NxK", lda=4_000_008)
-    assert info["variant"] == 1 | 2 | 4
+    assert info["variant"] == V | C8 | NXK
+    rc, info = _plan(512, 512, 512, ldb=(1 << 30) // (512 + 32) + 8)
+    assert not info["variant"] & DMA
     # group_m larger than the tile rows is clamped (same map)
     rc, info = _plan(512, 4096, 64, group_m=100)
     assert info["group_m"] == 2

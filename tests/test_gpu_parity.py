@@ -262,3 +262,56 @@ def test_pipeline_choices_are_bit_identical(oracle_mod, M, N, K, lay):
         C = tg.mm(Ad, Bd, lay, k_step=ks, stages=st)
         torch.cuda.synchronize()
         assert torch.equal(C.view(torch.int16), base.view(torch.int16)), (ks, st)
+
+
+def _nan_padded(rows, cols, ld, seed, offset):
+    """A rows x cols matrix at `offset` elements into a buffer with row stride ld,
+    every element outside the matrix (row padding and trailing space) a NaN."""
+    buf = np.full(offset + rows * ld + 64, np.float16(np.nan), dtype=np.float16)
+    view = np.lib.stride_tricks.as_strided(buf[offset:], (rows, cols), (2 * ld, 2))
+    view[...] = inputs.random_f16((rows, cols), seed)
+    return buf, np.ascontiguousarray(view)
+
+
+@pytest.mark.parametrize("generic", [0, 1])
+@pytest.mark.parametrize("lay", ["NxK", "KxN"])
+@pytest.mark.parametrize("K", [5, 37, 261, 264, 512 + 24, 1000])
+def test_nan_beyond_k_and_edges_never_leaks(oracle_mod, lay, K, generic):
+    """Padding past K, past N (row stride slack) and after the last element is NaN;
+    odd strides and an odd element offset leave the rows only 2-byte aligned. Every
+    output must still match the oracle, so no padded element reaches the sums."""
+    print(f"case nan-padding {lay} K={K} generic={generic}", flush=True)
+    M, N, off = 300, 270, 3
+    lda = K + 5
+    Abuf, A = _nan_padded(M, K, lda, K, off)
+    if lay == "NxK":
+        ldb = K + 3
+        Bbuf, B = _nan_padded(N, K, ldb, K + 1, off)
+    else:
+        ldb = N + 7
+        Bbuf, B = _nan_padded(K, N, ldb, K + 1, off)
+    Ad, Bd = _dev(Abuf), _dev(Bbuf)
+    C = torch.empty((M, N), dtype=torch.float16, device=DEV)
+    rc = tg.tgemm_f16_config(M, N, K, Ad.data_ptr() + 2 * off, lda, Bd.data_ptr() + 2 * off, ldb, lay,
+                             C.data_ptr(), N, torch.cuda.current_stream().cuda_stream, generic)
+    assert rc == tg.TGEMM_OK
+    got = _host(C)
+    assert np.isfinite(got.astype(np.float32)).all(), "a padded NaN reached an output"
+    _full_check(oracle_mod, A, B, lay, got, f"nan padding {lay} K={K}")
+
+
+@pytest.mark.parametrize("lay", ["NxK", "KxN"])
+def test_inf_in_neighbouring_row_stays_local(lay):
+    """Compact operands (ld = row length): an Inf in one row of B must not turn the
+    neighbouring output column into NaN (elements past K belong to the next row)."""
+    print(f"case inf neighbour {lay}", flush=True)
+    M, N, K = 300, 270, 264 + 4
+    A = inputs.random_f16((M, K), 7)
+    B = inputs.random_f16((N, K) if lay == "NxK" else (K, N), 8)
+    if lay == "NxK":
+        B[6, 0] = np.float16(np.inf)          # B[:, 6] holds the Inf; k = K of row 5 would be this element
+    else:
+        B[0, 6] = np.float16(np.inf)
+    C = _run(A, B, lay)
+    cols = np.isfinite(C.astype(np.float32)).all(axis=0)
+    assert not cols[6] and cols[5] and cols[7] and cols[:6].all() and cols[7:].all()
