@@ -63,9 +63,12 @@ def cpu_baseline(A, B, w, got, target_s: float = 12.0):
         ref, ab = oracle.gemm(A[:rows], B, w.b_layout)
         return time.perf_counter() - t0, ref, ab
 
-    dt, _, _ = run(8)                                  # calibration (includes decoding B)
-    per_row = max(dt / 8, 1e-6)
-    rows = int(min(w.M, max(16, target_s / per_row)))
+    # two-point calibration: the fixed cost (decoding all of B) drops out
+    t_a, _, _ = run(16)
+    t_b, _, _ = run(64)
+    per_row = max((t_b - t_a) / 48, 1e-6)
+    fixed = max(t_a - 16 * per_row, 0.0)
+    rows = int(min(w.M, max(16, (target_s - fixed) / per_row)))
     dt, ref, ab = run(rows)
     res = oracle.check(got[:rows], ref, ab)
     flops = 2.0 * rows * w.N * w.K
@@ -88,6 +91,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="instead of the GEMM, time the matrix-core issue probe (the GEMM's "
+                         "MFMA stream without memory traffic) and print its TFLOP/s")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the GEMM, run device-to-device copies of MIB MiB; used to "
                          "scale the HBM byte counters (FETCH_SIZE / WRITE_SIZE) of a profiler run")
@@ -113,6 +119,25 @@ def main():
 
     import dense_tiled_gemm_tgemm_amd as tg
     from dense_tiled_gemm_tgemm_amd import inputs
+
+    if args.mfma_ceiling:
+        tg.load()
+        stream = torch.cuda.current_stream()
+        wg, iters = 1024, 512
+        out = torch.empty(wg * 256, dtype=torch.float32, device="cuda:0")
+        for _ in range(args.warmup):
+            tg.mfma_issue_probe(wg, iters, out.data_ptr(), stream.cuda_stream)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(args.steps):
+            tg.mfma_issue_probe(wg, iters, out.data_ptr(), stream.cuda_stream)
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / args.steps
+        flops = wg * 4 * iters * 16 * 2.0 * 32 * 32 * 16
+        print(json.dumps({"probe": "mfma_issue", "workgroups": wg, "iters": iters, "ms": round(ms, 5),
+                          "tflops": round(flops / ms / 1e9, 1), "peak": PEAK_F16_TFLOPS}), flush=True)
+        return
 
     name = args.workload or inputs.HEADLINE
     w = inputs.WORKLOADS[name]

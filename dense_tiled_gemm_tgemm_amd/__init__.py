@@ -15,6 +15,7 @@ from ._binding import (  # noqa: F401
     TgemmError,
     last_hip_error,
     load,
+    mfma_issue_probe,
     mm,
     status_string,
     tgemm_f16,

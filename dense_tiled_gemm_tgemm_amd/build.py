@@ -10,7 +10,7 @@ import sys
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "tgemm.hip")
+SRCS = [os.path.join(PKG, "csrc", "tgemm.hip"), os.path.join(PKG, "csrc", "mfma_probe.hip")]
 LIB = os.path.join(PKG, "libtgemm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -25,7 +25,7 @@ FLAGS = [
 
 def build(verbose: bool = False, extra=()) -> str:
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *extra, SRC, "-o", tmp]
+    cmd = [HIPCC, *FLAGS, *extra, *SRCS, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

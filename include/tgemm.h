@@ -135,6 +135,18 @@ int tgemm_plan_f16(int64_t M, int64_t N, int64_t K,
 int tgemm_tile_of(int64_t grid_m, int64_t grid_n, int group_m, int num_xcd,
                   int64_t wid, int64_t* tile_m, int64_t* tile_n);
 
+/*
+ * Measurement aid (not part of the product operation): launches `workgroups`
+ * workgroups of 256 threads that run the GEMM kernel's matrix-core stream
+ * (iters rounds of 16 independent 32x32x16 fp16 MFMAs per wave) on
+ * register-resident pseudo-random binary16 data, with no memory traffic.
+ * Its TFLOP/s is the ceiling the matrix cores of the board sustain for such
+ * data (clock and power limits included). `out` must hold workgroups * 256
+ * floats of device memory. Returns TGEMM_OK, TGEMM_ERR_INVALID (bad sizes,
+ * NULL out) or TGEMM_ERR_HIP.
+ */
+int tgemm_mfma_issue_probe(int64_t workgroups, int iters, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

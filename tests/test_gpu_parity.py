@@ -315,3 +315,13 @@ def test_inf_in_neighbouring_row_stays_local(lay):
     C = _run(A, B, lay)
     cols = np.isfinite(C.astype(np.float32)).all(axis=0)
     assert not cols[6] and cols[5] and cols[7] and cols[:6].all() and cols[7:].all()
+
+
+def test_mfma_issue_probe_runs():
+    """The matrix-core issue probe (measurement aid) launches and produces finite sums."""
+    out = torch.empty(8 * 256, dtype=torch.float32, device=DEV)
+    tg.mfma_issue_probe(8, 4, out.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all())
+    with pytest.raises(tg.TgemmError):
+        tg.mfma_issue_probe(0, 4, out.data_ptr())
