@@ -1,39 +1,32 @@
 // fp16 dense tiled GEMM for MI355X (gfx950): C = A * B, binary16 in, fp32
 // accumulate, binary16 out.
 //
-// One workgroup owns one BM x BN output tile and walks K in BK steps (page 1,
+// One workgroup owns one BM x BN output tile and walks K in steps (page 1,
 // "Using NVIDIA CUDA Tile to write a high-performance matrix multiply",
 // sections 1-6; page 4, CUDA programming guide 13.4.2, section 2.4.9.1).
-// Per K step the tile's A (BM x BK) and B (BK x BN) blocks are staged from
-// HBM/L2 into LDS with coalesced 128-bit loads, double-buffered so the next
-// step's loads are in flight while the current step runs on the matrix cores
-// (the load / barrier / compute / overlap / write-back lifecycle of page 3,
-// "Why GEMM", section 2.2). Partial K tiles are padded with zeros and C
-// elements outside M x N are never written (page 4, section 2.4.6.1.3).
+// Per K step the tile's A and B blocks are staged from HBM/L2 into LDS while
+// earlier steps run on the matrix cores (the load / barrier / compute /
+// overlap / write-back lifecycle of page 3, "Why GEMM", section 2.2).
+// Partial K tiles are padded with zeros and C elements outside M x N are
+// never written (page 4, section 2.4.6.1.3).
 //
 // gfx950 mapping:
 //  * 256 threads = 4 waves of 64 lanes in a 2 x 2 grid; each wave owns a
-//    128 x 128 sub-tile held as 4 x 4 blocks of 32 x 32 fp32 accumulators
+//    128 x 128 sub-tile held as 8 x 8 blocks of 16 x 16 fp32 accumulators
 //    (256 accumulator registers per lane).
-//  * Inner product: v_mfma_f32_32x32x16_f16. For a 32x32x16 product each lane
-//    supplies 8 consecutive-k binary16 values of one row of each operand
-//    (row = lane mod 32, k half = lane / 32), read from LDS as one 128-bit
-//    word. The B fragment is passed as the instruction's first operand and
-//    the A fragment as its second, so the 32 x 32 result block is C
-//    transposed: lane l holds C row (l mod 32), and its accumulator registers
-//    4q..4q+3 hold four consecutive C columns 8q + 4*(l/32) + 0..3. The
-//    epilogue therefore writes 64-bit runs of four binary16 values.
-//  * LDS: both operands are kept K-contiguous, [row][64 halves], as 16-byte
-//    chunks; chunk c of row r lives at slot c ^ ((r & 7) ^ ((r >> 3) & 1)).
-//    Eight consecutive rows, and sixteen consecutive rows split by parity,
-//    map one logical chunk to distinct 16-byte bank groups, so the 128-bit
-//    fragment reads (32 rows x one chunk per half-wave) and the 128-bit
-//    staging writes are free of bank conflicts (page 3, sections 3.1 and
-//    5.3; page 5, "Why swizzle matters").
-//  * B stored K x N is transposed in registers while staging: each thread
-//    loads an 8 (k) x 8 (n) block with eight 128-bit row loads and writes it
-//    as eight 128-bit K-contiguous chunks, so both B layouts share one
-//    compute loop.
+//  * Inner product: v_mfma_f32_16x16x32_f16, one per 16 x 16 block and
+//    32-deep K slice. Each lane supplies 8 consecutive-k binary16 values of
+//    one row of each operand (row = lane mod 16, k = 8 * (lane / 16) + 0..7),
+//    read from LDS as one 128-bit word. The B fragment is passed as the
+//    instruction's first operand and the A fragment as its second, so the
+//    16 x 16 result block is C transposed: lane l holds C row (l mod 16) and
+//    its four accumulator registers hold the four consecutive C columns
+//    4 * (l / 16) + 0..3. The epilogue writes 64-bit runs of four binary16.
+//    (This shape keeps the matrix cores busier between the interleaved LDS
+//    and load instructions than the 32 x 32 x 16 one, which needs twice the
+//    cycles per instruction but issues less evenly.)
+//  * Every path multiplies the same operand values in the same 32-deep K
+//    slices in ascending order, so all of them produce the same bits.
 //  * Workgroup -> tile: die-aware renumbering, then the grouped order of
 //    page 1, section "Swizzle" (tile_of in tgemm_plan.h).
 #include <hip/hip_runtime.h>
@@ -45,14 +38,13 @@
 namespace tg {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef float acc16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kChunks = BK / 8;                 // 16-byte chunks per LDS row
-constexpr int kTileChunks = 256 * kChunks;      // chunks per staged operand block
 static_assert(BM == 256 && BN == 256 && BK == 64 && NTHREADS == 256,
-              "the staging maps below assume a 256 x 256 x 64 tile and 256 threads");
+              "the staging maps below assume a 256 x 256 tile, 64-deep register staging and 256 threads");
 
 struct Args {
     const uint16_t* A;
@@ -63,8 +55,35 @@ struct Args {
     int grid_m, grid_n, W, group_m, num_xcd;
 };
 
-__device__ __forceinline__ int lds_slot(int row, int chunk) {
-    return row * kChunks + (chunk ^ ((row & 7) ^ ((row >> 3) & 1)));
+// LDS layout of one staged K-contiguous operand block (256 rows x KS halves)
+// as 16-byte chunks, CPR = KS / 8 per row, chunk c of row r at slot
+// r * CPR + (c ^ f(r)):
+//   KS = 64: f(r) = (r & 7) ^ ((r >> 3) & 1)
+//   KS = 32: f(r) = (r ^ (r >> 2)) & 3
+// A fragment read takes 16 consecutive rows at one chunk per 16-lane group
+// (4 groups = 4 consecutive chunks); both maps keep every 8- and 16-lane
+// group of such a read on distinct 16-byte bank groups, and the chunks of
+// any row distinct, so reads and 128-bit writes are free of bank conflicts
+// (page 3, sections 3.1 and 5.3; page 5, "Why swizzle matters"). Both depend
+// on r mod 16 only, so the fragment of 16-row block i sits 16 * CPR slots
+// after that of block 0.
+template <int KS>
+struct Lds {
+    static constexpr int kCpr = KS / 8;
+    static constexpr int kBlock = 256 * kCpr;          // chunks per operand block
+    static constexpr int kStage = 2 * kBlock;          // A block then B block
+    __device__ static __forceinline__ int swz(int r) {
+        return KS == 64 ? ((r & 7) ^ ((r >> 3) & 1)) : ((r ^ (r >> 2)) & 3);
+    }
+    __device__ static __forceinline__ int slot(int r, int c) { return r * kCpr + (c ^ swz(r)); }
+};
+
+// Fragment of the 16-row block `blk` of a K-contiguous LDS block for the
+// 32-deep slice `s`: lane l gets row 16 * blk + (l mod 16) of the wave's
+// 128-row half `half`, k = 32 s + 8 (l / 16) + 0..7.
+template <int KS>
+__device__ __forceinline__ half8 read_kc(const u32x4* __restrict__ s_blk, int half, int blk, int lane, int s) {
+    return __builtin_bit_cast(half8, s_blk[Lds<KS>::slot(half * 128 + blk * 16 + (lane & 15), s * 4 + (lane >> 4))]);
 }
 
 // Eight binary16 values from p[0..nv-1]; lanes at or past nv read as zero.
@@ -78,6 +97,59 @@ __device__ __forceinline__ u32x4 load8_elems(const uint16_t* __restrict__ p, int
     }
     return u32x4{w[0], w[1], w[2], w[3]};
 }
+
+__device__ __forceinline__ f32x4 mfma16(const half8& b, const half8& a, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(b, a, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ unsigned pack_half2(float a, float b) {
+    // fp32 -> binary16, round to nearest even (page 1, section 6: the fp32
+    // accumulator is converted to C's type when it is stored)
+    const _Float16 ha = (_Float16)a, hb = (_Float16)b;
+    return (unsigned)__builtin_bit_cast(uint16_t, ha) | ((unsigned)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+
+// Lane l of wave (wm, wn) holds, in acc[i][j], C row m0 + 128 wm + 16 i + (l mod 16)
+// at columns n0 + 128 wn + 16 j + 4 (l / 16) + 0..3.
+template <bool VEC_C>
+__device__ __forceinline__ void store_c(const f32x4 (&acc)[8][8], const Args& a, int m0, int n0, int wm,
+                                        int wn, int lane) {
+    const int r16 = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int m = m0 + wm * 128 + i * 16 + r16;
+        if (m >= a.M) continue;
+        uint16_t* crow = a.C + (int64_t)m * a.ldc;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int n = n0 + wn * 128 + j * 16 + g * 4;
+            const unsigned w0 = pack_half2(acc[i][j][0], acc[i][j][1]);
+            const unsigned w1 = pack_half2(acc[i][j][2], acc[i][j][3]);
+            if (VEC_C && n + 4 <= a.N) {
+                *(u32x2*)(crow + n) = u32x2{w0, w1};
+            } else {
+                if (n + 0 < a.N) crow[n + 0] = (uint16_t)(w0 & 0xffffu);
+                if (n + 1 < a.N) crow[n + 1] = (uint16_t)(w0 >> 16);
+                if (n + 2 < a.N) crow[n + 2] = (uint16_t)(w1 & 0xffffu);
+                if (n + 3 < a.N) crow[n + 3] = (uint16_t)(w1 >> 16);
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ void zero_acc(f32x4 (&acc)[8][8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{};
+}
+
+// ---------------------------------------------------------------------------
+// Register-staged path (any stride, element-wise or 128-bit global loads):
+// both operands are written K-contiguous into a BK = 64 deep LDS block with
+// the KS = 64 map above, double-buffered.
+// ---------------------------------------------------------------------------
+using LdsR = Lds<BK>;
 
 // Stage one BK-wide block of a K-contiguous operand (A, or B stored N x K):
 // rows row0 .. row0+255, k = k0 .. k0+63. Thread t loads chunk (t & 7) of
@@ -110,7 +182,7 @@ __device__ __forceinline__ void load_kcontig(u32x4 (&r)[8], const uint16_t* __re
 __device__ __forceinline__ void store_kcontig(u32x4* __restrict__ s, const u32x4 (&r)[8], int tid) {
     const int c = tid & 7;
 #pragma unroll
-    for (int p = 0; p < 8; ++p) s[lds_slot((tid >> 3) + 32 * p, c)] = r[p];
+    for (int p = 0; p < 8; ++p) s[LdsR::slot((tid >> 3) + 32 * p, c)] = r[p];
 }
 
 // Stage one BK-deep block of B stored K x N: k = k0 .. k0+63, n = n0 .. n0+255.
@@ -161,64 +233,24 @@ __device__ __forceinline__ void store_kxn(u32x4* __restrict__ s, const u32x4 (&r
 #pragma unroll
     for (int sidx = 0; sidx < 8; ++sidx) {
         const u32x4 v = odd ? t[sidx ^ 1] : t[sidx];
-        s[lds_slot(nb * 8 + (sidx ^ odd), kb)] = v;
+        s[LdsR::slot(nb * 8 + (sidx ^ odd), kb)] = v;
     }
 }
 
-// One BK step of the wave's 128 x 128 sub-tile: 4 k16 slices x 4 x 4 MFMAs.
-__device__ __forceinline__ void mma_step(acc16 (&acc)[4][4], const u32x4* __restrict__ sA,
+// One BK step of the wave's 128 x 128 sub-tile: 2 k32 slices x 8 x 8 MFMAs.
+__device__ __forceinline__ void mma_step(f32x4 (&acc)[8][8], const u32x4* __restrict__ sA,
                                          const u32x4* __restrict__ sB, int wm, int wn, int lane) {
-    const int r32 = lane & 31, khalf = lane >> 5;
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-        half8 af[4], bf[4];
+    for (int s = 0; s < BK / 32; ++s) {
+        half8 af[8], bf[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            af[i] = __builtin_bit_cast(half8, sA[lds_slot(wm * 128 + i * 32 + r32, kk * 2 + khalf)]);
+        for (int i = 0; i < 8; ++i) af[i] = read_kc<BK>(sA, wm, i, lane, s);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            bf[j] = __builtin_bit_cast(half8, sB[lds_slot(wn * 128 + j * 32 + r32, kk * 2 + khalf)]);
+        for (int j = 0; j < 8; ++j) bf[j] = read_kc<BK>(sB, wn, j, lane, s);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[j], af[i], acc[i][j], 0, 0, 0);
-    }
-}
-
-__device__ __forceinline__ unsigned pack_half2(float a, float b) {
-    // fp32 -> binary16, round to nearest even (page 1, section 6: the fp32
-    // accumulator is converted to C's type when it is stored)
-    const _Float16 ha = (_Float16)a, hb = (_Float16)b;
-    return (unsigned)__builtin_bit_cast(uint16_t, ha) | ((unsigned)__builtin_bit_cast(uint16_t, hb) << 16);
-}
-
-template <bool VEC_C>
-__device__ __forceinline__ void store_c(const acc16 (&acc)[4][4], const Args& a, int m0, int n0, int wm,
-                                        int wn, int lane) {
-    const int r32 = lane & 31, khalf = lane >> 5;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int m = m0 + wm * 128 + i * 32 + r32;
-        if (m >= a.M) continue;
-        uint16_t* crow = a.C + (int64_t)m * a.ldc;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int n = n0 + wn * 128 + j * 32 + q * 8 + khalf * 4;
-                const unsigned w0 = pack_half2(acc[i][j][4 * q + 0], acc[i][j][4 * q + 1]);
-                const unsigned w1 = pack_half2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-                if (VEC_C && n + 4 <= a.N) {
-                    *(u32x2*)(crow + n) = u32x2{w0, w1};
-                } else {
-                    if (n + 0 < a.N) crow[n + 0] = (uint16_t)(w0 & 0xffffu);
-                    if (n + 1 < a.N) crow[n + 1] = (uint16_t)(w0 >> 16);
-                    if (n + 2 < a.N) crow[n + 2] = (uint16_t)(w1 & 0xffffu);
-                    if (n + 3 < a.N) crow[n + 3] = (uint16_t)(w1 >> 16);
-                }
-            }
-        }
+            for (int j = 0; j < 8; ++j) acc[i][j] = mfma16(bf[j], af[i], acc[i][j]);
     }
 }
 
@@ -242,24 +274,73 @@ __device__ __forceinline__ void store_stage(u32x4* __restrict__ sA, u32x4* __res
         store_kxn(sB, rb, tid);
 }
 
+template <int NXK, bool VEC, bool VEC_C>
+__global__ void __launch_bounds__(NTHREADS)
+__attribute__((amdgpu_waves_per_eu(1, 1)))
+tgemm_f16_kernel(Args a) {
+    __shared__ u32x4 smem[2][2][LdsR::kBlock];   // [stage][A | B], 128 KiB
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    int tm, tn;
+    tile_of((int)blockIdx.x, a.W, a.grid_m, a.grid_n, a.group_m, a.num_xcd, &tm, &tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const bool interior = (m0 + BM <= a.M) && (n0 + BN <= a.N);
+    const int nk = (a.K + BK - 1) / BK;
+
+    f32x4 acc[8][8];
+    zero_acc(acc);
+
+    u32x4 ra[8], rb[8];
+    if (nk > 0) {
+        if (interior && BK <= a.K)
+            load_stage<NXK, VEC, false>(ra, rb, a, m0, n0, 0, tid);
+        else
+            load_stage<NXK, VEC, true>(ra, rb, a, m0, n0, 0, tid);
+        store_stage<NXK>(smem[0][0], smem[0][1], ra, rb, tid);
+        __syncthreads();
+    }
+    for (int t = 0; t < nk; ++t) {
+        const int cur = t & 1;
+        const bool more = t + 1 < nk;
+        if (more) {
+            const int k0 = (t + 1) * BK;
+            if (interior && k0 + BK <= a.K)
+                load_stage<NXK, VEC, false>(ra, rb, a, m0, n0, k0, tid);
+            else
+                load_stage<NXK, VEC, true>(ra, rb, a, m0, n0, k0, tid);
+        }
+        mma_step(acc, smem[cur][0], smem[cur][1], wm, wn, lane);
+        if (more) store_stage<NXK>(smem[cur ^ 1][0], smem[cur ^ 1][1], ra, rb, tid);
+        __syncthreads();
+    }
+    store_c<VEC_C>(acc, a, m0, n0, wm, wn, lane);
+}
 
 // ---------------------------------------------------------------------------
-// Direct HBM/L2 -> LDS staging, used when both operands are K-contiguous
-// (A, and B stored N x K), 16-byte aligned, K a multiple of 8.
+// Direct HBM/L2 -> LDS staging (any 2-byte alignment; row strides below the
+// limits the host checks).
 //
 // buffer_load_dwordx4 ... lds writes lane L of a wave instruction to LDS
 // bytes [base + 16L, base + 16L + 16): the destination slot is fixed by the
 // lane, so the XOR swizzle is applied on the source side instead.
 //
-// Zero padding (page 4, section 2.4.6.1.3) comes from the buffer range
-// check: a lane whose byte offset (vector + scalar part) reaches the
-// resource's record count reads zeros, and the zeros are what it writes into
-// its LDS slot. Rows past the operand carry the offset bit kOob; on the last,
-// partial K step so do chunks past K; and steps past the end of K use a
-// scalar offset of kOob, so they touch no memory at all. The main loop is
-// therefore the same for edge and interior tiles, and branch-free.
+// Zero padding (page 4, section 2.4.6.1.3): a lane whose byte offset (vector
+// + scalar part) reaches the buffer resource's record count reads zeros, and
+// the zeros are what it writes into its LDS slot. Rows past the operand
+// carry the offset bit kOob, steps past the end of K use a scalar offset of
+// kOob (they touch no memory at all), and B stored K x N has its rows past K
+// beyond its buffer. The one remaining case, chunks at or past K on the
+// last, partial K step, is rewritten in LDS before that step is published.
+// Each lane's load offsets are computed once: with one wave per SIMD, a
+// vector ALU write into a register a matrix instruction has just read stalls
+// the matrix cores, so the main loop carries no per-load arithmetic.
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) const char lds_cchar;
 
 constexpr unsigned kOob = 0x80000000u;       // record counts stay below this
 
@@ -298,34 +379,104 @@ __device__ __forceinline__ Rsrc operand_rsrc(const uint16_t* X, int64_t ld, int 
     return Rsrc{X + (int64_t)row0 * ld, (int)span};
 }
 
-// LDS layout of one staged operand block (256 rows x KS halves) as 16-byte
-// chunks, CPR = KS / 8 per row, chunk c of row r at slot r*CPR + (c ^ f(r)):
-//   KS = 64: f(r) = (r & 7) ^ ((r >> 3) & 1)
-//   KS = 32: f(r) = ((r >> 1) ^ (r >> 3)) & 3
-// For the 128-bit fragment reads (32 consecutive rows at one chunk per
-// half-wave) both keep every 8-lane and every 16-lane group on distinct
-// 16-byte bank groups, whether LDS is served 128 or 256 bytes per pass.
-template <int KS>
-struct Lds {
-    static constexpr int kCpr = KS / 8;
-    static constexpr int kBlock = 256 * kCpr;          // chunks per operand block
-    static constexpr int kStage = 2 * kBlock;          // A block then B block
-    __device__ static __forceinline__ int swz(int r) {
-        return KS == 64 ? ((r & 7) ^ ((r >> 3) & 1)) : (((r >> 1) ^ (r >> 3)) & 3);
-    }
-    __device__ static __forceinline__ int slot(int r, int c) { return r * kCpr + (c ^ swz(r)); }
+// B stored K x N is kept N-contiguous in LDS, [k][n] (512 bytes per k row):
+// 16-byte chunk c (n = 8c .. 8c+7) of k row k sits at physical chunk
+// c ^ h(k), h(k) = 2 (k & 3) ^ 8 ((k >> 3) & 1) ^ 16 ((k >> 4) & 1). A
+// transposing fragment read has each 16-lane group read 4 consecutive k rows
+// x 32 contiguous bytes, the four groups 8 rows apart; h spreads every 16-
+// and 32-lane part of such a read over distinct banks. h ignores k bits 2
+// and 5, so the second half of a fragment (k + 4) and the next 32-deep slice
+// (k + 32) sit at fixed byte distances from the first.
+struct KnLds {
+    __device__ static __forceinline__ int h(int k) { return (2 * (k & 3)) ^ (8 * ((k >> 3) & 1)) ^ (16 * ((k >> 4) & 1)); }
+    __device__ static __forceinline__ int phys(int c, int k) { return c ^ h(k); }
+    __device__ static __forceinline__ int logical(int p, int k) { return p ^ h(k); }
 };
 
-template <int KS>
-__device__ __forceinline__ void read_frags(half8 (&fa)[4], half8 (&fb)[4], const u32x4* __restrict__ sA,
-                                           const u32x4* __restrict__ sB, int wm, int wn, int lane, int kk) {
-    const int r32 = lane & 31, khalf = lane >> 5;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Four k values (4 consecutive k rows) of one n column of B stored [k][n],
+// by the transposing read ds_read_b64_tr_b16: in each 16-lane group, lane i
+// points at k row k0 + i/4, columns n0 + 4(i % 4) .. +3, and lane j receives
+// column n0 + j.
+__device__ __forceinline__ s16x4 read_tr(lds_cchar* __restrict__ p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+#else
+    (void)p;
+    return s16x4{};
+#endif
+}
+
+__device__ __forceinline__ half8 join_halves(const s16x4& lo, const s16x4& hi) {
+    return __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// This lane's LDS read positions in stage 0 (stage st's A and B blocks sit
+// st * CPR * 256 slots after stage 0's, within 64 KiB, so a read is one base
+// register plus an immediate offset):
+//  a[s], b[s]: the A and (K-contiguous) B fragments of 16-row block 0 for
+//              slice s; block i lies 16 * CPR slots further.
+//  tr[blk]:    for B stored [k][n], the transposing read of 16-column block
+//              blk, slice 0, k rows +0..3 of the lane's 8 (lane l needs
+//              column 128 wn + 16 blk + (l mod 16), k = 8 (l / 16) + 0..7);
+//              k + 4 adds 2 KiB and slice s adds 16 KiB * s.
+template <int KS, int NXK>
+struct FragPtrs {
+    const u32x4* a[KS / 32];
+    const u32x4* b[KS / 32];
+    lds_cchar* tr[8];
+};
+
+template <int KS, int NXK>
+__device__ __forceinline__ FragPtrs<KS, NXK> frag_ptrs(const u32x4* a_blk, const u32x4* b_blk, int wm, int wn,
+                                                        int lane) {
+    using L = Lds<KS>;
+    FragPtrs<KS, NXK> f;
+    const int r16 = lane & 15, g = lane >> 4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        fa[i] = __builtin_bit_cast(half8, sA[Lds<KS>::slot(wm * 128 + i * 32 + r32, kk * 2 + khalf)]);
+    for (int s = 0; s < KS / 32; ++s) {
+        f.a[s] = a_blk + L::slot(wm * 128 + r16, s * 4 + g);
+        f.b[s] = b_blk + L::slot(wn * 128 + r16, s * 4 + g);
+    }
+    const int krow = 8 * g + (r16 >> 2);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-        fb[j] = __builtin_bit_cast(half8, sB[Lds<KS>::slot(wn * 128 + j * 32 + r32, kk * 2 + khalf)]);
+    for (int blk = 0; blk < 8; ++blk) {
+        const int ncol = wn * 128 + blk * 16 + 4 * (r16 & 3);
+        const int byte = krow * 512 + KnLds::phys(ncol >> 3, krow) * 16 + (ncol & 7) * 2;
+        f.tr[blk] = NXK ? nullptr : (lds_cchar*)b_blk + byte;
+    }
+    return f;
+}
+
+// The read positions `so` slots further (those of another stage).
+template <int KS, int NXK>
+__device__ __forceinline__ FragPtrs<KS, NXK> shifted(const FragPtrs<KS, NXK>& f, int so) {
+    FragPtrs<KS, NXK> g;
+#pragma unroll
+    for (int s = 0; s < KS / 32; ++s) {
+        g.a[s] = f.a[s] + so;
+        g.b[s] = f.b[s] + so;
+    }
+#pragma unroll
+    for (int blk = 0; blk < 8; ++blk) g.tr[blk] = NXK ? nullptr : f.tr[blk] + so * 16;
+    return g;
+}
+
+// Fragment reads; `so` is the stage's offset in slots from stage 0.
+template <int KS, int NXK>
+__device__ __forceinline__ half8 frag_a(const FragPtrs<KS, NXK>& f, int so, int s, int i) {
+    return __builtin_bit_cast(half8, f.a[s][so + i * 16 * (KS / 8)]);
+}
+
+template <int KS, int NXK>
+__device__ __forceinline__ half8 frag_b_kc(const FragPtrs<KS, NXK>& f, int so, int s, int j) {
+    return __builtin_bit_cast(half8, f.b[s][so + j * 16 * (KS / 8)]);
+}
+
+template <int KS, int NXK>
+__device__ __forceinline__ s16x4 frag_b_tr(const FragPtrs<KS, NXK>& f, int so, int s, int blk, int hh) {
+    return read_tr(f.tr[blk] + so * 16 + s * 16384 + hh * 2048);
 }
 
 // Per-lane source offsets of the 2 * CPR load instructions of a K step (A's
@@ -334,30 +485,17 @@ __device__ __forceinline__ void read_frags(half8 (&fa)[4], half8 (&fb)[4], const
 //    tid / CPR, physical chunk tid % CPR, which must hold logical chunk
 //    (tid % CPR) ^ f(row); f(row) does not depend on j. The K step advances
 //    the scalar offset by KS * 2 bytes.
-//  * B stored K x N, kept N-contiguous ([k][n], 32 chunks of 8 n per k row):
-//    slot -> k row 8j + (tid >> 5), physical chunk tid & 31, holding logical
-//    chunk g^-1 of it (see KnLds). The K step advances the scalar offset by
-//    KS * ldb * 2 bytes; k rows past K lie past the buffer and read zeros.
+//  * B stored K x N ([k][n], 32 chunks per k row): slot -> k row 8j +
+//    (tid >> 5), physical chunk tid & 31, holding logical chunk
+//    (tid & 31) ^ h(k row). The K step advances the scalar offset by
+//    KS * ldb * 2 bytes.
 // voff[idx] is the row's byte offset plus the chunk's, with kOob set when the
-// row lies past its operand. tail_oob is kOob when this lane's A chunk lies
-// past K on the last, partial K step (0 otherwise).
+// row lies past its operand.
 template <int KS>
 struct LaneLoads {
     static constexpr int kCpr = KS / 8;
     unsigned voff[2 * kCpr];
-    unsigned tail_oob;
     unsigned kchunk;      // k offset (elements) of this lane's K-contiguous chunk inside a K step
-};
-
-// B stored K x N in LDS as [k][n]: 16-byte chunk c (n = 8c .. 8c+7) of k row
-// k sits at physical chunk c ^ 2(k & 3) ^ 8((c >> 1) & 1). For the
-// transposing fragment reads (16 lanes: 4 k rows x 32 contiguous bytes) this
-// keeps every 16- and 32-lane group on distinct banks.
-struct KnLds {
-    __device__ static __forceinline__ int phys(int c, int k) { return c ^ (2 * (k & 3)) ^ (8 * ((c >> 1) & 1)); }
-    __device__ static __forceinline__ int logical(int p, int k) {
-        return p ^ (2 * (k & 3)) ^ (8 * (((p >> 1) & 1) ^ (k & 1)));
-    }
 };
 
 template <int KS, int NXK>
@@ -378,19 +516,17 @@ __device__ __forceinline__ LaneLoads<KS> lane_loads(const Args& a, int m0, int n
             p.voff[kCpr + j] = (unsigned)krow * (unsigned)a.ldb * 2u + c * 16u;
         }
     }
-    const int krem = a.K % KS;             // valid k of the last step (0: the last step is full)
-    p.tail_oob = (krem != 0 && (int)chunk * 8 >= krem) ? kOob : 0u;
     p.kchunk = chunk * 8u;
     return p;
 }
 
-// Load instruction `idx` (0 .. 2*CPR-1) of a K step into `stage`, with the
-// step's scalar offsets (soa for A, sob for B) and this lane's extra
-// out-of-range bit `oob` for its K-contiguous chunks.
+// Load instruction `idx` (0 .. 2*CPR-1) of a K step into the stage whose A
+// and B blocks are a_blk and b_blk, with the step's scalar offsets (soa for
+// A, sob for B).
 template <int KS, int NXK>
 __device__ __forceinline__ void issue_load(const Rsrc& ra, const Rsrc& rb, const LaneLoads<KS>& p, int idx,
-                                           unsigned soa, unsigned sob, unsigned oob, u32x4* __restrict__ stage,
-                                           int wave) {
+                                           unsigned soa, unsigned sob, u32x4* __restrict__ a_blk,
+                                           u32x4* __restrict__ b_blk, int wave) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the host pass cannot instantiate these target builtins
     constexpr int kCpr = KS / 8;
     const bool isb = idx >= kCpr;
@@ -398,62 +534,48 @@ __device__ __forceinline__ void issue_load(const Rsrc& ra, const Rsrc& rb, const
     const Rsrc& rs = isb ? rb : ra;
     // word 3 = 0x00020000: raw (untyped) access, 32-bit data format
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)rs.base, 0, rs.nrec, 0x00020000);
-    u32x4* dst = stage + (isb ? Lds<KS>::kBlock : 0) + (j * 4 + wave) * 64;
-    // chunks past K: A, and B when it is K-contiguous (a K x N B's rows past K lie past its buffer)
-    const unsigned v = (isb && !NXK) ? p.voff[idx] : (p.voff[idx] | oob);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)dst, 16, v, isb ? sob : soa, 0, 0);
+    u32x4* dst = (isb ? b_blk : a_blk) + (j * 4 + wave) * 64;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)dst, 16, p.voff[idx], isb ? sob : soa, 0, 0);
 #endif
 }
 
-// Eight binary16 values, p[e] for e < nv and zero past nv, as one 16-byte
-// LDS chunk.
-__device__ __forceinline__ u32x4 chunk_from(const uint16_t* __restrict__ p, int nv) {
-    unsigned w[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const unsigned lo = (2 * q < nv) ? (unsigned)p[2 * q] : 0u;
-        const unsigned hi = (2 * q + 1 < nv) ? (unsigned)p[2 * q + 1] : 0u;
-        w[q] = lo | (hi << 16);
-    }
-    return u32x4{w[0], w[1], w[2], w[3]};
-}
-
-// Last K step (k0 = its first k): the 16-byte chunks that straddle the end
-// of valid data. A chunk straddling K (A, and B stored N x K) was loaded
-// whole, so past K it holds the next row's elements; and in an operand's
-// final row the range check zeroes a straddling access entirely. Each lane
-// rebuilds such chunks of its own slots from element loads - the valid part,
-// zeros after it - once its loads have landed and before the barrier that
-// publishes the stage. B stored K x N straddles only at column N, and only
-// its final row K - 1 loses data (other rows read the next row past N,
-// which lands in output columns that are never stored).
+// Last K step when it is partial (k0 = its first k). Its K-contiguous chunks
+// at or past K were loaded as whatever lies there (the next row, or zeros past
+// the operand's end), so each lane rewrites those of its own slots: the
+// valid part of a chunk straddling K from element loads, zeros after it, and
+// whole zeros past K. B stored K x N straddles only at column N, and only
+// its final row K - 1 loses data (the range check zeroes the whole 16-byte
+// access; other rows read the next row past N, which lands in output
+// columns that are never stored). This runs after the lane's loads of the
+// stage have landed and before the barrier that publishes it.
 template <int KS, int NXK>
-__device__ __forceinline__ void fix_last_step(u32x4* __restrict__ stage, const LaneLoads<KS>& p, const Args& a,
-                                              int m0, int n0, int k0, int tid, int wave, int lane) {
+__device__ __forceinline__ void fix_last_step(u32x4* __restrict__ a_blk, u32x4* __restrict__ b_blk,
+                                              const LaneLoads<KS>& p, const Args& a, int m0, int n0, int k0,
+                                              int tid, int wave, int lane) {
     constexpr int kCpr = KS / 8;
     const int r = tid / kCpr;
     const int kc = k0 + (int)p.kchunk;
-    const int nv = a.K - kc;                          // valid elements of this lane's K chunk
-    if (nv > 0 && nv < 8) {
-#pragma unroll
+    const int nv = a.K - kc;                          // valid elements of this lane's K chunks (may be <= 0)
+    // one chunk at a time (not unrolled): this runs once per tile, inside a
+    // loop whose fragments hold most of the registers
+    if (nv < 8) {
+#pragma unroll 1
         for (int j = 0; j < kCpr; ++j) {
             const int row = r + (256 / kCpr) * j;
             const int slot = (j * 4 + wave) * 64 + lane;
-            if (m0 + row < a.M) stage[slot] = chunk_from(a.A + (int64_t)(m0 + row) * a.lda + kc, nv);
-            if (NXK && n0 + row < a.N)
-                stage[Lds<KS>::kBlock + slot] = chunk_from(a.B + (int64_t)(n0 + row) * a.ldb + kc, nv);
+            if (m0 + row < a.M) a_blk[slot] = load8_elems(a.A + (int64_t)(m0 + row) * a.lda + kc, nv);
+            if (NXK && n0 + row < a.N) b_blk[slot] = load8_elems(a.B + (int64_t)(n0 + row) * a.ldb + kc, nv);
         }
     }
     if (!NXK) {
-#pragma unroll
+#pragma unroll 1
         for (int j = 0; j < kCpr; ++j) {
             const int krow = 8 * j + (tid >> 5);
             const int c = KnLds::logical(tid & 31, krow);
             const int nc = n0 + 8 * c;
             const int nvn = a.N - nc;
             if (k0 + krow == a.K - 1 && nvn > 0 && nvn < 8)
-                stage[Lds<KS>::kBlock + (j * 4 + wave) * 64 + lane] =
-                    chunk_from(a.B + (int64_t)(a.K - 1) * a.ldb + nc, nvn);
+                b_blk[(j * 4 + wave) * 64 + lane] = load8_elems(a.B + (int64_t)(a.K - 1) * a.ldb + nc, nvn);
         }
     }
     TG_COMPILER_FENCE();
@@ -462,103 +584,161 @@ __device__ __forceinline__ void fix_last_step(u32x4* __restrict__ stage, const L
     TG_COMPILER_FENCE();
 }
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-// Four k values (k0 .. k0+3, from 4 k rows) of one n column of B stored
-// [k][n] in LDS, by the transposing read: in each 16-lane group, lane i
-// points at k row k0 + i/4, columns n0 + 4(i % 4) .. +3, and lane j receives
-// column n0 + j.
-__device__ __forceinline__ s16x4 read_tr(const u32x4* __restrict__ sB, int krow, int ncol) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    const int c = ncol >> 3;
-    const int byte = krow * 512 + KnLds::phys(c, krow) * 16 + (ncol & 7) * 2;
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_s16x4*)((__attribute__((address_space(3))) char*)(sB) + byte));
-#else
-    return s16x4{};
-#endif
+// All fragments of slice `s` of stage 0 (used once, before the main loop).
+template <int KS, int NXK>
+__device__ __forceinline__ void read_frags(half8 (&fa)[8], half8 (&fb)[8], const FragPtrs<KS, NXK>& f, int s) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) fa[i] = frag_a(f, 0, s, i);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        fb[j] = NXK ? frag_b_kc(f, 0, s, j) : join_halves(frag_b_tr(f, 0, s, j, 0), frag_b_tr(f, 0, s, j, 1));
 }
 
-// One k16 slice: 16 MFMAs on the current fragments, with the next slice's
-// fragment reads and (when LOADS) kHalf = CPR load instructions placed
-// between them, reads first, in the order the next slice consumes them:
-// A0, B0..B3, A1..A3. A K-contiguous B fragment is one 128-bit read; a
-// [k][n] B fragment is two transposing 64-bit reads (k +0..3, k +4..7), so
-// that layout has 12 reads per slice and CPR must be 4. The newest read is
-// at least four MFMAs old when the slice ends. With one wave per SIMD every
-// other instruction competes with MFMA issue, so the order is pinned at both
-// the IR and the machine level.
+// One k32 slice: 64 MFMAs (8 x 8 blocks, row-block-major) on the current
+// fragments, with the next slice's fragment reads (slice next_s of the
+// stage `so` slots from stage 0) and, when LOADS, the 2 * CPR load
+// instructions of one K step placed between them: reads after every
+// even-numbered MFMA, in the order the next slice consumes them (A0, B0..B7,
+// A1..A7; a [k][n] B fragment is two transposing reads), loads spread evenly
+// over the odd-numbered ones. One instruction per MFMA keeps the matrix core
+// fed; with one wave per SIMD every other instruction competes with MFMA
+// issue, so the order is pinned at both the IR and the machine level.
 template <int KS, int NXK, bool LOADS>
-__device__ __forceinline__ void slice(acc16 (&acc)[4][4], const half8 (&fa)[4], const half8 (&fb)[4],
-                                      half8 (&na)[4], half8 (&nb)[4], const u32x4* __restrict__ rA,
-                                      const u32x4* __restrict__ rB, int wm, int wn, int lane, int next_kk,
-                                      const Rsrc& ra, const Rsrc& rb, const LaneLoads<KS>& p, int ld_first,
-                                      unsigned soa, unsigned sob, unsigned oob, u32x4* __restrict__ ld_stage,
+__device__ __forceinline__ void slice(f32x4 (&acc)[8][8], const half8 (&fa)[8], const half8 (&fb)[8],
+                                      half8 (&na)[8], half8 (&nb)[8], const FragPtrs<KS, NXK>& f, int so,
+                                      int next_s, const Rsrc& ra, const Rsrc& rb, const LaneLoads<KS>& p,
+                                      unsigned soa, unsigned sob, u32x4* __restrict__ ld_a, u32x4* __restrict__ ld_b,
                                       int wave) {
-    constexpr int kHalf = KS / 8;
-    constexpr int kReads = NXK ? 8 : 12;
-    static_assert(kReads + kHalf <= 16, "reads and loads must fit the 16 MFMA slots");
-    const int r32 = lane & 31, khalf = lane >> 5;
-    s16x4 lo[4];
+    constexpr int kLps = KS / 4;
+    constexpr int kNb = NXK ? 8 : 16;              // B read instructions
+    constexpr int kReads = 8 + kNb;
+    constexpr int kGap = 64 / kLps;                // MFMAs per load
+    static_assert(2 * kReads <= 64, "reads must fit the even MFMA slots");
+    s16x4 lo[8];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-        const int i = q >> 2, j = q & 3;
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[j], fa[i], acc[i][j], 0, 0, 0);
-        if (q < kReads) {
-            // read slot q -> fragment: NxK: A0,B0,B1,B2,B3,A1,A2,A3; KxN: A0,B0h0,B0h1,...,B3h1,A1,A2,A3
-            const int nbr = NXK ? 4 : 8;
-            if (q >= 1 && q <= nbr) {
+    for (int q = 0; q < 64; ++q) {
+        const int i = q >> 3, j = q & 7;
+        acc[i][j] = mfma16(fb[j], fa[i], acc[i][j]);
+        if ((q & 1) == 0 && q / 2 < kReads) {
+            const int rq = q / 2;
+            if (rq >= 1 && rq <= kNb) {
                 if (NXK) {
-                    nb[q - 1] = __builtin_bit_cast(
-                        half8, rB[Lds<KS>::slot(wn * 128 + (q - 1) * 32 + r32, next_kk * 2 + khalf)]);
+                    nb[rq - 1] = frag_b_kc(f, so, next_s, rq - 1);
                 } else {
-                    const int fbi = (q - 1) >> 1, h = (q - 1) & 1;
-                    const int g = lane >> 4, jl = lane & 15;
-                    const int ncol = wn * 128 + fbi * 32 + 16 * (g & 1) + 4 * (jl & 3);
-                    const int krow = next_kk * 16 + 8 * (g >> 1) + 4 * h + (jl >> 2);
-                    const s16x4 v = read_tr(rB, krow, ncol);
-                    if (h == 0) {
-                        lo[fbi] = v;
-                    } else {
-                        nb[fbi] = __builtin_bit_cast(half8, __builtin_shufflevector(lo[fbi], v, 0, 1, 2, 3, 4, 5, 6, 7));
-                    }
+                    const int blk = (rq - 1) >> 1, hh = (rq - 1) & 1;
+                    const s16x4 v = frag_b_tr(f, so, next_s, blk, hh);
+                    if (hh == 0)
+                        lo[blk] = v;
+                    else
+                        nb[blk] = join_halves(lo[blk], v);
                 }
             } else {
-                const int ai = q == 0 ? 0 : q - nbr;
-                na[ai] = __builtin_bit_cast(half8, rA[Lds<KS>::slot(wm * 128 + ai * 32 + r32, next_kk * 2 + khalf)]);
+                const int ai = rq == 0 ? 0 : rq - kNb;
+                na[ai] = frag_a(f, so, next_s, ai);
             }
-        } else if (LOADS && q - kReads < kHalf) {
-            issue_load<KS, NXK>(ra, rb, p, ld_first + (q - kReads), soa, sob, oob, ld_stage, wave);
+        } else if (LOADS && q % kGap == kGap - 1) {
+            issue_load<KS, NXK>(ra, rb, p, q / kGap, soa, sob, ld_a, ld_b, wave);
         }
         TG_COMPILER_FENCE();
         __builtin_amdgcn_sched_barrier(0);
     }
 }
 
-// Tile kernel with both operands streamed straight into an S-stage LDS
-// ring of KS-deep K steps: A K-contiguous, B either K-contiguous (stored
-// N x K, NXK = 1) or kept [k][n] and transposed on read (stored K x N).
-// Step t's loads go into stage t mod S in two halves: the first right after
-// the barrier that ends every wave's reads of that stage (during the last
-// k16 slice of step t - S), the second during the first slice of step
-// t - S + 1. Each step's loads thus have about S - 1 steps of compute to
-// land. The barrier sits before the last slice of a step: the next step's
-// first fragment reads overlap that slice's MFMAs. Every step issues the
-// same number of loads (steps past K read nothing and write zeros into
-// stages that are never read), so all wait counts are constants.
+// Per-workgroup state of the direct-to-LDS kernel. LDS holds the S stages'
+// A blocks, then their B blocks.
+template <int KS, int NXK, int S>
+struct DmaCtx {
+    Rsrc ra, rb;
+    LaneLoads<KS> p;
+    unsigned bstep;       // scalar-offset advance of B per K step
+    int nk, klast;        // K steps; first k of the last step
+    bool fixup;           // the last step needs fix_last_step
+    int m0, n0, tid, wave, lane;
+    u32x4* smem;
+    FragPtrs<KS, NXK> fp; // read positions in stage 0
+    __device__ __forceinline__ u32x4* a_blk(int st) const { return smem + st * Lds<KS>::kBlock; }
+    __device__ __forceinline__ u32x4* b_blk(int st) const { return smem + (S + st) * Lds<KS>::kBlock; }
+    // scalar offsets of K step t
+    __device__ __forceinline__ unsigned soa(int t) const { return t < nk ? (unsigned)t * (unsigned)(KS * 2) : kOob; }
+    __device__ __forceinline__ unsigned sob(int t) const { return t < nk ? (unsigned)t * bstep : kOob; }
+};
+
+// K step t of the direct-to-LDS kernel, in stage st. Its first slice's
+// fragments are in buffer F0 of fa/fb; the next step's first fragments end
+// up in buffer F0 ^ (KS / 32 odd). ST >= 0: st == ST, known at compile time
+// (2-stage ring), so every fragment read is a fixed offset from the stage-0
+// positions. ST < 0: `cur` holds the read positions of stage st on entry and
+// those of the next stage on return; they are derived once per step, before
+// the barrier wait, into registers no matrix instruction reads (a vector ALU
+// write into a just-read MFMA operand register stalls the matrix cores).
+template <int NXK, int KS, int S, int F0, int ST>
+__device__ __forceinline__ void dma_step(f32x4 (&acc)[8][8], half8 (&fa)[2][8], half8 (&fb)[2][8], int st, int t,
+                                         const Args& a, const DmaCtx<KS, NXK, S>& c, FragPtrs<KS, NXK>& cur) {
+    using L = Lds<KS>;
+    constexpr int kSlices = KS / 32;
+    constexpr int kLps = KS / 4;
+    constexpr int FL = (F0 + kSlices - 1) & 1;       // buffer of the last slice
+    static_assert(ST < 0 || S == 2, "compile-time stages need the 2-stage ring");
+    if (ST >= 0) st = ST;
+    const int nst = (st + 1 == S) ? 0 : st + 1;
+    const FragPtrs<KS, NXK>& fc = ST >= 0 ? c.fp : cur;
+    const int so_c = ST >= 0 ? ST * L::kBlock : 0;
+#pragma unroll
+    for (int s = 0; s + 1 < kSlices; ++s)
+        slice<KS, NXK, false>(acc, fa[(F0 + s) & 1], fb[(F0 + s) & 1], fa[(F0 + s + 1) & 1], fb[(F0 + s + 1) & 1],
+                              fc, so_c, s + 1, c.ra, c.rb, c.p, 0u, 0u, c.smem, c.smem, c.wave);
+    if (ST < 0) cur = shifted(c.fp, nst * L::kBlock);
+    TG_COMPILER_FENCE();
+    __builtin_amdgcn_sched_barrier(0);
+    wait_lgkmcnt0();                                  // this wave's reads of stage st returned
+    wait_vmcnt<(S - 2) * kLps>();                     // step t + 1 landed
+    if (c.fixup && t + 2 == c.nk)
+        fix_last_step<KS, NXK>(c.a_blk(nst), c.b_blk(nst), c.p, a, c.m0, c.n0, c.klast, c.tid, c.wave, c.lane);
+    block_barrier();
+    // step t + S's loads go into the stage just released
+    slice<KS, NXK, true>(acc, fa[FL], fb[FL], fa[FL ^ 1], fb[FL ^ 1], ST >= 0 ? c.fp : cur,
+                         ST >= 0 ? ((ST + 1) & 1) * L::kBlock : 0, 0, c.ra, c.rb, c.p, c.soa(t + S), c.sob(t + S),
+                         c.a_blk(st), c.b_blk(st), c.wave);
+}
+
+// Steps t0 .. nk-1 (an even count) in pairs, step t0 in stage st0 with
+// parity P: one-slice steps alternate fragment buffers, and a 2-stage ring
+// alternates stages, so the pair's two steps are two fixed variants.
+template <int NXK, int KS, int S, int P>
+__device__ __forceinline__ void step_pairs(f32x4 (&acc)[8][8], half8 (&fa)[2][8], half8 (&fb)[2][8], int t0,
+                                           int st0, const Args& a, const DmaCtx<KS, NXK, S>& c,
+                                           FragPtrs<KS, NXK>& cur) {
+    constexpr int F1 = KS == 32 ? P : 0, F2 = KS == 32 ? (P ^ 1) : 0;
+    constexpr int S1 = S == 2 ? P : -1, S2 = S == 2 ? (P ^ 1) : -1;
+    int st = st0;
+    for (int t = t0; t < c.nk; t += 2) {
+        dma_step<NXK, KS, S, F1, S1>(acc, fa, fb, st, t, a, c, cur);
+        st = (st + 1 == S) ? 0 : st + 1;
+        dma_step<NXK, KS, S, F2, S2>(acc, fa, fb, st, t + 1, a, c, cur);
+        st = (st + 1 == S) ? 0 : st + 1;
+    }
+}
+
+// Tile kernel with both operands streamed straight into an S-stage LDS ring
+// of KS-deep K steps (KS / 32 slices each): A K-contiguous, B either
+// K-contiguous (stored N x K, NXK = 1) or kept [k][n] and transposed on read
+// (stored K x N). Step t lives in stage t mod S. The barrier of step t sits
+// before its last slice: it follows every wave's last fragment read of stage
+// t (so step t + S's loads go into that stage during the last slice) and
+// every wave's loads of step t + 1 (whose first fragments that slice reads).
+// A step's loads thus have S - 1 steps less one slice to land. Every step
+// issues the same number of loads (steps past K read nothing and write zeros
+// into stages that are never read), so all wait counts are constants.
 template <int NXK, bool VEC_C, int KS, int S>
 __global__ void __launch_bounds__(NTHREADS)
 __attribute__((amdgpu_waves_per_eu(1, 1)))
 tgemm_f16_dma_kernel(Args a) {
     using L = Lds<KS>;
     static_assert(KS == 64 || KS == 32, "K step");
-    static_assert(NXK || KS == 32, "B stored K x N streams 32-deep K steps");
-    static_assert(S >= 2 && S <= 5 && S * L::kStage * 16 <= 160 * 1024, "LDS ring must fit 160 KiB");
-    constexpr int kSlices = KS / 16;                 // k16 slices per step (even)
-    constexpr int kCpr = KS / 8;
-    constexpr int kLps = 2 * kCpr;                   // load instructions per step per wave
-    __shared__ u32x4 smem[S * L::kStage];
+    static_assert(KS == 32 || S == 2, "64-deep steps use a 2-stage ring");
+    static_assert(S >= 2 && S <= 5 && 2 * S * L::kBlock * 16 <= 160 * 1024, "LDS ring must fit 160 KiB");
+    constexpr int kLps = KS / 4;                      // load instructions per step per wave
+    __shared__ u32x4 smem[2 * S * L::kBlock];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -570,131 +750,54 @@ tgemm_f16_dma_kernel(Args a) {
     const int m0 = tm * BM, n0 = tn * BN;
     const int nk = (a.K + KS - 1) / KS;
 
-    acc16 acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = acc16{};
+    f32x4 acc[8][8];
+    zero_acc(acc);
 
     if (nk > 0) {
-        const Rsrc ra = operand_rsrc(a.A, a.lda, a.M, a.K, m0);
+        DmaCtx<KS, NXK, S> c;
+        c.ra = operand_rsrc(a.A, a.lda, a.M, a.K, m0);
         // B: N x K rows n0.. ; K x N columns n0.. of all K rows
-        const Rsrc rb = NXK ? operand_rsrc(a.B, a.ldb, a.N, a.K, n0) : operand_rsrc(a.B + n0, a.ldb, a.K, a.N - n0, 0);
-        const LaneLoads<KS> p = lane_loads<KS, NXK>(a, m0, n0, tid);
-        const unsigned bstep = NXK ? (unsigned)(KS * 2) : (unsigned)KS * (unsigned)a.ldb * 2u;
-        // scalar offsets and A's extra out-of-range bits of K step t
-#define TG_SOA(t) ((t) < nk ? (unsigned)(t) * (unsigned)(KS * 2) : kOob)
-#define TG_SOB(t) ((t) < nk ? (unsigned)(t) * bstep : kOob)
-#define TG_OOB(t) ((t) == nk - 1 ? p.tail_oob : 0u)
+        c.rb = NXK ? operand_rsrc(a.B, a.ldb, a.N, a.K, n0) : operand_rsrc(a.B + n0, a.ldb, a.K, a.N - n0, 0);
+        c.p = lane_loads<KS, NXK>(a, m0, n0, tid);
+        c.bstep = NXK ? (unsigned)(KS * 2) : (unsigned)KS * (unsigned)a.ldb * 2u;
+        c.nk = nk;
+        c.klast = (nk - 1) * KS;
+        c.fixup = (a.K % KS) != 0 || (!NXK && (a.N % 8) != 0);
+        c.m0 = m0;
+        c.n0 = n0;
+        c.tid = tid;
+        c.wave = wave;
+        c.lane = lane;
+        c.smem = smem;
+        c.fp = frag_ptrs<KS, NXK>(c.a_blk(0), c.b_blk(0), wm, wn, lane);
 
-        // prologue: steps 0 .. S-2 and the first half of step S-1
-        for (int t = 0; t < S; ++t) {
-            u32x4* stage = smem + t * L::kStage;
-            const int n = (t + 1 < S) ? kLps : kCpr;
-            for (int idx = 0; idx < n; ++idx)
-                issue_load<KS, NXK>(ra, rb, p, idx, TG_SOA(t), TG_SOB(t), TG_OOB(t), stage, wave);
-        }
-        // the last step has chunks straddling the end of valid data
-        const bool straddle = (a.K % 8) != 0 || (!NXK && (a.N % 8) != 0);
-        const int klast = (nk - 1) * KS;
-        wait_vmcnt<(S - 2) * kLps + kCpr>();          // step 0 landed
-        if (straddle && nk == 1) fix_last_step<KS, NXK>(smem, p, a, m0, n0, klast, tid, wave, lane);
+        // prologue: steps 0 .. S-1
+        for (int t = 0; t < S; ++t)
+            for (int idx = 0; idx < kLps; ++idx)
+                issue_load<KS, NXK>(c.ra, c.rb, c.p, idx, c.soa(t), c.sob(t), c.a_blk(t), c.b_blk(t), wave);
+        wait_vmcnt<(S - 1) * kLps>();                 // step 0 landed
+        if (c.fixup && nk == 1) fix_last_step<KS, NXK>(c.a_blk(0), c.b_blk(0), c.p, a, m0, n0, c.klast, tid, wave, lane);
         block_barrier();
 
-        half8 fa[2][4], fb[2][4];
-        read_frags<KS>(fa[0], fb[0], smem, smem + L::kBlock, wm, wn, lane, 0);
-        if (!NXK) {
-            const int g = lane >> 4, jl = lane & 15;
-#pragma unroll
-            for (int f = 0; f < 4; ++f) {
-                const int ncol = wn * 128 + f * 32 + 16 * (g & 1) + 4 * (jl & 3);
-                const int krow = 8 * (g >> 1) + (jl >> 2);
-                const s16x4 v0 = read_tr(smem + L::kBlock, krow, ncol);
-                const s16x4 v1 = read_tr(smem + L::kBlock, krow + 4, ncol);
-                fb[0][f] = __builtin_bit_cast(half8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+        half8 fa[2][8], fb[2][8];
+        read_frags<KS, NXK>(fa[0], fb[0], c.fp, 0);
+        FragPtrs<KS, NXK> cur = c.fp;                 // read positions of the current stage
+        if constexpr (KS == 64) {
+            // two slices per step: every step starts on fragment buffer 0
+            int st = 0;
+            for (int t = 0; t < nk; ++t) {
+                dma_step<NXK, KS, S, 0, -1>(acc, fa, fb, st, t, a, c, cur);
+                st ^= 1;
             }
-        }
-        int st = 0;                                   // stage of step t
-        for (int t = 0; t < nk; ++t) {
-            const u32x4* sA = smem + st * L::kStage;
-            const u32x4* sB = sA + L::kBlock;
-            const int pst = (st == 0) ? S - 1 : st - 1;   // stage of step t + S - 1
-            const int nst = (st + 1 == S) ? 0 : st + 1;
-            // slice 0 carries the second half of step t + S - 1's loads
-            slice<KS, NXK, true>(acc, fa[0], fb[0], fa[1], fb[1], sA, sB, wm, wn, lane, 1, ra, rb, p, kCpr,
-                                 TG_SOA(t + S - 1), TG_SOB(t + S - 1), TG_OOB(t + S - 1), smem + pst * L::kStage,
-                                 wave);
-#pragma unroll
-            for (int kk = 1; kk + 1 < kSlices; ++kk)
-                slice<KS, NXK, false>(acc, fa[kk & 1], fb[kk & 1], fa[(kk + 1) & 1], fb[(kk + 1) & 1], sA, sB, wm,
-                                      wn, lane, kk + 1, ra, rb, p, 0, 0u, 0u, 0u, smem, wave);
-            TG_COMPILER_FENCE();
-            wait_lgkmcnt0();                          // this wave's reads of stage st returned
-            wait_vmcnt<(S - 2) * kLps>();             // step t + 1 landed
-            if (straddle && t + 2 == nk)
-                fix_last_step<KS, NXK>(smem + nst * L::kStage, p, a, m0, n0, klast, tid, wave, lane);
-            block_barrier();
-            // the first half of step t + S's loads goes into the stage just released
-            const u32x4* nA = smem + nst * L::kStage;
-            slice<KS, NXK, true>(acc, fa[(kSlices - 1) & 1], fb[(kSlices - 1) & 1], fa[0], fb[0], nA,
-                                 nA + L::kBlock, wm, wn, lane, 0, ra, rb, p, 0, TG_SOA(t + S), TG_SOB(t + S),
-                                 TG_OOB(t + S), smem + st * L::kStage, wave);
-            st = nst;
+        } else if (nk & 1) {
+            // an odd step count starts with one step; the rest go in pairs
+            dma_step<NXK, KS, S, 0, S == 2 ? 0 : -1>(acc, fa, fb, 0, 0, a, c, cur);
+            step_pairs<NXK, KS, S, 1>(acc, fa, fb, 1, 1 % S, a, c, cur);
+        } else {
+            step_pairs<NXK, KS, S, 0>(acc, fa, fb, 0, 0, a, c, cur);
         }
         // no load may still be writing this workgroup's LDS when it exits
         wait_vmcnt<0>();
-#undef TG_SOA
-#undef TG_SOB
-#undef TG_OOB
-    }
-    store_c<VEC_C>(acc, a, m0, n0, wm, wn, lane);
-}
-
-template <int NXK, bool VEC, bool VEC_C>
-__global__ void __launch_bounds__(NTHREADS)
-__attribute__((amdgpu_waves_per_eu(1, 1)))
-tgemm_f16_kernel(Args a) {
-    __shared__ u32x4 smem[2][2][kTileChunks];   // [stage][A | B], 128 KiB
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-
-    int tm, tn;
-    tile_of((int)blockIdx.x, a.W, a.grid_m, a.grid_n, a.group_m, a.num_xcd, &tm, &tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-    const bool interior = (m0 + BM <= a.M) && (n0 + BN <= a.N);
-    const int nk = (a.K + BK - 1) / BK;
-
-    acc16 acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = acc16{};
-
-    u32x4 ra[8], rb[8];
-    if (nk > 0) {
-        if (interior && BK <= a.K)
-            load_stage<NXK, VEC, false>(ra, rb, a, m0, n0, 0, tid);
-        else
-            load_stage<NXK, VEC, true>(ra, rb, a, m0, n0, 0, tid);
-        store_stage<NXK>(smem[0][0], smem[0][1], ra, rb, tid);
-        __syncthreads();
-    }
-    for (int t = 0; t < nk; ++t) {
-        const int cur = t & 1;
-        const bool more = t + 1 < nk;
-        if (more) {
-            const int k0 = (t + 1) * BK;
-            if (interior && k0 + BK <= a.K)
-                load_stage<NXK, VEC, false>(ra, rb, a, m0, n0, k0, tid);
-            else
-                load_stage<NXK, VEC, true>(ra, rb, a, m0, n0, k0, tid);
-        }
-        mma_step(acc, smem[cur][0], smem[cur][1], wm, wn, lane);
-        if (more) store_stage<NXK>(smem[cur ^ 1][0], smem[cur ^ 1][1], ra, rb, tid);
-        __syncthreads();
     }
     store_c<VEC_C>(acc, a, m0, n0, wm, wn, lane);
 }
@@ -704,30 +807,25 @@ static const void* kernel_ptr() {
     return reinterpret_cast<const void*>(&tgemm_f16_kernel<NXK, VEC, VEC_C>);
 }
 
-template <bool VEC_C>
-static const void* dma_kernel_ptr(int nxk, int k_step, int stages) {
-    if (!nxk) {
-        switch (stages) {
-            case 2: return reinterpret_cast<const void*>(&tgemm_f16_dma_kernel<0, VEC_C, 32, 2>);
-            case 3: return reinterpret_cast<const void*>(&tgemm_f16_dma_kernel<0, VEC_C, 32, 3>);
-            case 4: return reinterpret_cast<const void*>(&tgemm_f16_dma_kernel<0, VEC_C, 32, 4>);
-            default: return reinterpret_cast<const void*>(&tgemm_f16_dma_kernel<0, VEC_C, 32, 5>);
-        }
-    }
-    if (k_step == 64) return reinterpret_cast<const void*>(&tgemm_f16_dma_kernel<1, VEC_C, 64, 2>);
+template <int NXK, bool VEC_C>
+static const void* dma_kernel_ptr(int k_step, int stages) {
+    if (k_step == 64) return reinterpret_cast<const void*>(&tgemm_f16_dma_kernel<NXK, VEC_C, 64, 2>);
     switch (stages) {
-        case 2: return reinterpret_cast<const void*>(&tgemm_f16_dma_kernel<1, VEC_C, 32, 2>);
-        case 3: return reinterpret_cast<const void*>(&tgemm_f16_dma_kernel<1, VEC_C, 32, 3>);
-        case 4: return reinterpret_cast<const void*>(&tgemm_f16_dma_kernel<1, VEC_C, 32, 4>);
-        default: return reinterpret_cast<const void*>(&tgemm_f16_dma_kernel<1, VEC_C, 32, 5>);
+        case 2: return reinterpret_cast<const void*>(&tgemm_f16_dma_kernel<NXK, VEC_C, 32, 2>);
+        case 3: return reinterpret_cast<const void*>(&tgemm_f16_dma_kernel<NXK, VEC_C, 32, 3>);
+        case 4: return reinterpret_cast<const void*>(&tgemm_f16_dma_kernel<NXK, VEC_C, 32, 4>);
+        default: return reinterpret_cast<const void*>(&tgemm_f16_dma_kernel<NXK, VEC_C, 32, 5>);
     }
 }
 
 static const void* pick_kernel(const Plan& pl) {
     const int variant = pl.variant;
-    if (variant & kDma)
-        return (variant & kVecC) ? dma_kernel_ptr<true>(pl.layout, pl.k_step, pl.stages)
-                                 : dma_kernel_ptr<false>(pl.layout, pl.k_step, pl.stages);
+    if (variant & kDma) {
+        const bool nxk = variant & kLayoutNxK, vc = variant & kVecC;
+        if (nxk)
+            return vc ? dma_kernel_ptr<1, true>(pl.k_step, pl.stages) : dma_kernel_ptr<1, false>(pl.k_step, pl.stages);
+        return vc ? dma_kernel_ptr<0, true>(pl.k_step, pl.stages) : dma_kernel_ptr<0, false>(pl.k_step, pl.stages);
+    }
     switch (variant & 7) {
         case 0: return kernel_ptr<0, false, false>();
         case 1: return kernel_ptr<0, true, false>();

@@ -24,9 +24,10 @@ constexpr int NTHREADS = 256;            // 4 waves of 64 lanes, 2 x 2 over the 
 
 constexpr int kDefaultGroupM = 8;        // page 1, section "Swizzle": GROUP_SIZE_M = 8
 constexpr int kDefaultNumXcd = 8;        // MI355X: 8 accelerator dies of 32 CUs
-// Direct-to-LDS pipeline: K step and LDS ring depth (stages * 32 KiB at K step 32).
-constexpr int kDefaultDmaKStep = 32;
-constexpr int kDefaultDmaStages = 3;
+// Direct-to-LDS pipeline: K step and LDS ring depth (a stage holds 64 KiB at
+// K step 64, 32 KiB at K step 32). 64-deep steps take a 2-stage ring.
+constexpr int kDefaultDmaKStep = 64;
+constexpr int kDefaultDmaStages32 = 4;     // ring depth when the K step is 32
 
 enum : int { kVecAB = 1, kVecC = 2, kLayoutNxK = 4, kDma = 8 };
 
@@ -142,16 +143,17 @@ inline int make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
     const bool vec_c = ((uintptr_t)C % 8 == 0) && (ldc % 4 == 0);
     // direct-to-LDS (any 2-byte alignment: gfx950 buffer loads accept
     // unaligned addresses): row strides small enough for 32-bit panel
-    // offsets; a K x N B additionally needs every byte offset
-    // (K + 32) * ldb * 2 below 2^31.
+    // offsets; a K x N B additionally needs every byte offset it forms,
+    // below (K + 64) * ldb * 2 + 512, to stay below 2^31.
     const bool dma = !force_generic && lda <= kMaxDmaLd &&
-                     (b_layout == TGEMM_B_NxK ? ldb <= kMaxDmaLd : (K + 32) * ldb < (int64_t(1) << 30));
-    if (dma && b_layout == TGEMM_B_KxN && k_step == 64) return TGEMM_ERR_INVALID;  // K x N streams 32-deep steps
+                     (b_layout == TGEMM_B_NxK ? ldb <= kMaxDmaLd
+                                              : ldb < (int64_t(1) << 30) && (K + 64) * ldb < (int64_t(1) << 30) - 512);
     pl->variant = (vec_ab ? kVecAB : 0) | (vec_c ? kVecC : 0) |
                   (b_layout == TGEMM_B_NxK ? kLayoutNxK : 0) | (dma ? kDma : 0);
     if (dma) {
-        pl->k_step = k_step ? k_step : kDefaultDmaKStep;
-        pl->stages = pl->k_step == 64 ? 2 : (stages ? stages : kDefaultDmaStages);
+        // a ring deeper than 2 stages implies 32-deep steps
+        pl->k_step = k_step ? k_step : (stages > 2 ? 32 : kDefaultDmaKStep);
+        pl->stages = pl->k_step == 64 ? 2 : (stages ? stages : kDefaultDmaStages32);
     } else {
         pl->k_step = BK;
         pl->stages = 2;

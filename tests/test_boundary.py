@@ -109,9 +109,11 @@ def test_plan_variants_and_grid():
     assert info["variant"] == V | C8 | NXK | DMA
     assert info["workgroups"] == 32 * 32 and info["group_m"] == 8 and info["num_xcd"] == 8
     assert (info["bm"], info["bn"], info["threads"]) == (256, 256, 256)
-    assert (info["bk"], info["stages"], info["lds_bytes"]) == (32, 3, 3 * 32 * 1024)
-    rc, info = _plan(8192, 8192, 8192, lay="NxK", k_step=64)
     assert (info["bk"], info["stages"], info["lds_bytes"]) == (64, 2, 128 * 1024)
+    rc, info = _plan(8192, 8192, 8192, lay="NxK", k_step=32)
+    assert (info["bk"], info["stages"], info["lds_bytes"]) == (32, 4, 128 * 1024)
+    rc, info = _plan(8192, 8192, 8192, lay="NxK", stages=3)
+    assert (info["bk"], info["stages"], info["lds_bytes"]) == (32, 3, 96 * 1024)
     rc, info = _plan(8192, 8192, 8192, lay="NxK", k_step=32, stages=5)
     assert (info["bk"], info["stages"], info["lds_bytes"]) == (32, 5, 160 * 1024)
     # ragged, odd strides (2-byte aligned rows): still streamed into LDS; element-wise C stores
@@ -128,16 +130,18 @@ def test_plan_variants_and_grid():
     rc, info = _plan(256, 256, 256, C=PC + 2)
     assert info["variant"] == V | DMA
     rc, info = _plan(4096, 4096, 4096)
-    assert info["variant"] == V | C8 | DMA and (info["bk"], info["stages"]) == (32, 3)
+    assert info["variant"] == V | C8 | DMA and (info["bk"], info["stages"]) == (64, 2)
     rc, info = _plan(4096, 4096, 4096, k_step=64)
-    assert rc == tg.TGEMM_ERR_INVALID         # K x N streams 32-deep steps only
+    assert rc == 0 and (info["bk"], info["stages"], info["lds_bytes"]) == (64, 2, 128 * 1024)
     rc, info = _plan(4096, 4096, 4099, lda=4104)
     assert info["variant"] == V | C8 | DMA    # K % 8 != 0 is fine: the straddling chunk is cleared
     # strides past the 32-bit panel-offset limit: register-staged path
     rc, info = _plan(512, 512, 512, lay="NxK", lda=4_000_008)
     assert info["variant"] == V | C8 | NXK
-    rc, info = _plan(512, 512, 512, ldb=(1 << 30) // (512 + 32) + 8)
+    rc, info = _plan(512, 512, 512, ldb=(1 << 30) // (512 + 64))
     assert not info["variant"] & DMA
+    rc, info = _plan(512, 512, 512, ldb=((1 << 30) - 512) // (512 + 64) - 1)
+    assert info["variant"] & DMA
     # group_m larger than the tile rows is clamped (same map)
     rc, info = _plan(512, 4096, 64, group_m=100)
     assert info["group_m"] == 2
