@@ -32,6 +32,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "tgemm.h"
 #include "tgemm_plan.h"
 
@@ -53,6 +55,8 @@ struct Args {
     int64_t lda, ldb, ldc;
     int M, N, K;
     int grid_m, grid_n, W, group_m, num_xcd;
+    int grid;             // workgroups launched; workgroup b computes tiles b, b + grid, ...
+    int c16;              // C is 16-byte aligned and ldc a multiple of 8
 };
 
 // LDS layout of one staged K-contiguous operand block (256 rows x KS halves)
@@ -102,36 +106,58 @@ __device__ __forceinline__ f32x4 mfma16(const half8& b, const half8& a, const f3
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(b, a, c, 0, 0, 0);
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 half2 __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ unsigned pack_half2(float a, float b) {
     // fp32 -> binary16, round to nearest even (page 1, section 6: the fp32
-    // accumulator is converted to C's type when it is stored)
-    const _Float16 ha = (_Float16)a, hb = (_Float16)b;
-    return (unsigned)__builtin_bit_cast(uint16_t, ha) | ((unsigned)__builtin_bit_cast(uint16_t, hb) << 16);
+    // accumulator is converted to C's type when it is stored); one packed
+    // conversion instruction
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{a, b}, half2));
 }
 
 // Lane l of wave (wm, wn) holds, in acc[i][j], C row m0 + 128 wm + 16 i + (l mod 16)
-// at columns n0 + 128 wn + 16 j + 4 (l / 16) + 0..3.
+// at columns n0 + 128 wn + 16 j + 4 (l / 16) + 0..3. For each pair of 16-column
+// blocks (j, j+1), v_permlane16_swap exchanges the converted words between
+// 16-lane rows so that a lane in row g then holds the 8 consecutive columns
+// 16 (j + (g & 1)) + 8 (g >> 1) .. +7 of its C row: one 16-byte store when C
+// is 16-byte aligned with ldc % 8 == 0 (each store instruction writes 16 rows
+// x 64 bytes), two 8-byte stores when it is 8-byte aligned with ldc % 4 == 0,
+// element stores otherwise and where the 8 columns straddle N. All lanes run
+// the exchange; only the stores are predicated. One 16-row block at a time
+// (pinned), so the temporaries stay few when this runs between two tiles
+// with the next tile's fragments already in registers.
 template <bool VEC_C>
 __device__ __forceinline__ void store_c(const f32x4 (&acc)[8][8], const Args& a, int m0, int n0, int wm,
                                         int wn, int lane) {
     const int r16 = lane & 15, g = lane >> 4;
+    const int col0 = n0 + wn * 128 + (g & 1) * 16 + (g >> 1) * 8;
+    uint16_t* base = a.C + (int64_t)(m0 + wm * 128 + r16) * a.ldc + col0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const int m = m0 + wm * 128 + i * 16 + r16;
-        if (m >= a.M) continue;
-        uint16_t* crow = a.C + (int64_t)m * a.ldc;
+        __builtin_amdgcn_sched_barrier(0);
+        const bool row_ok = m0 + wm * 128 + i * 16 + r16 < a.M;
+        uint16_t* row = base + (int64_t)i * 16 * a.ldc;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int n = n0 + wn * 128 + j * 16 + g * 4;
-            const unsigned w0 = pack_half2(acc[i][j][0], acc[i][j][1]);
-            const unsigned w1 = pack_half2(acc[i][j][2], acc[i][j][3]);
-            if (VEC_C && n + 4 <= a.N) {
-                *(u32x2*)(crow + n) = u32x2{w0, w1};
-            } else {
-                if (n + 0 < a.N) crow[n + 0] = (uint16_t)(w0 & 0xffffu);
-                if (n + 1 < a.N) crow[n + 1] = (uint16_t)(w0 >> 16);
-                if (n + 2 < a.N) crow[n + 2] = (uint16_t)(w1 & 0xffffu);
-                if (n + 3 < a.N) crow[n + 3] = (uint16_t)(w1 >> 16);
+        for (int pr = 0; pr < 4; ++pr) {
+            const f32x4& x = acc[i][2 * pr];
+            const f32x4& y = acc[i][2 * pr + 1];
+            const auto s0 = __builtin_amdgcn_permlane16_swap(pack_half2(x[0], x[1]), pack_half2(y[0], y[1]),
+                                                             false, false);
+            const auto s1 = __builtin_amdgcn_permlane16_swap(pack_half2(x[2], x[3]), pack_half2(y[2], y[3]),
+                                                             false, false);
+            const u32x4 v = u32x4{s0[0], s1[0], s0[1], s1[1]};
+            const int col = col0 + 32 * pr;
+            uint16_t* dst = row + 32 * pr;
+            if (row_ok && col + 8 <= a.N && a.c16) {
+                *(u32x4*)dst = v;
+            } else if (row_ok && col + 8 <= a.N && VEC_C) {
+                *(u32x2*)dst = u32x2{v[0], v[1]};
+                *(u32x2*)(dst + 4) = u32x2{v[2], v[3]};
+            } else if (row_ok && col < a.N) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (col + e < a.N) dst[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
             }
         }
     }
@@ -330,14 +356,15 @@ tgemm_f16_kernel(Args a) {
 //
 // Zero padding (page 4, section 2.4.6.1.3): a lane whose byte offset (vector
 // + scalar part) reaches the buffer resource's record count reads zeros, and
-// the zeros are what it writes into its LDS slot. Rows past the operand
-// carry the offset bit kOob, steps past the end of K use a scalar offset of
-// kOob (they touch no memory at all), and B stored K x N has its rows past K
-// beyond its buffer. The one remaining case, chunks at or past K on the
-// last, partial K step, is rewritten in LDS before that step is published.
-// Each lane's load offsets are computed once: with one wave per SIMD, a
-// vector ALU write into a register a matrix instruction has just read stalls
-// the matrix cores, so the main loop carries no per-load arithmetic.
+// the zeros are what it writes into its LDS slot. A tile's resource ends at
+// its operand's last element, so rows past the operand (and, for B stored
+// K x N, rows past K) read zeros; steps past the last tile use a scalar
+// offset of kOob and touch no memory at all. The one remaining case, chunks
+// at or past K on the last, partial K step, is rewritten in LDS before that
+// step is published. Each lane's load offsets are computed once and do not
+// depend on the tile: with one wave per SIMD, a vector ALU write into a
+// register a matrix instruction has just read stalls the matrix cores, so
+// the main loop carries no per-load arithmetic.
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) const char lds_cchar;
@@ -367,7 +394,9 @@ __device__ __forceinline__ void block_barrier() {
 
 // Base pointer and record count of the buffer resource over operand rows
 // row0 .. nrows-1 (row stride ld): the byte span from the first of these rows
-// to the operand's last element (below 2^31 by the host's stride limit).
+// to the operand's last element. Every offset a tile forms inside its 256
+// rows stays below 2^31 (host stride limit); the span is capped below kOob,
+// which only shortens it for tiles far from the operand's end.
 struct Rsrc {
     const uint16_t* base;
     int nrec;
@@ -489,8 +518,8 @@ __device__ __forceinline__ s16x4 frag_b_tr(const FragPtrs<KS, NXK>& f, int so, i
 //    (tid >> 5), physical chunk tid & 31, holding logical chunk
 //    (tid & 31) ^ h(k row). The K step advances the scalar offset by
 //    KS * ldb * 2 bytes.
-// voff[idx] is the row's byte offset plus the chunk's, with kOob set when the
-// row lies past its operand.
+// voff[idx] is the row's byte offset plus the chunk's, relative to the
+// tile's resource base; it is the same for every tile.
 template <int KS>
 struct LaneLoads {
     static constexpr int kCpr = KS / 8;
@@ -499,7 +528,7 @@ struct LaneLoads {
 };
 
 template <int KS, int NXK>
-__device__ __forceinline__ LaneLoads<KS> lane_loads(const Args& a, int m0, int n0, int tid) {
+__device__ __forceinline__ LaneLoads<KS> lane_loads(const Args& a, int tid) {
     constexpr int kCpr = KS / 8;
     LaneLoads<KS> p;
     const int r = tid / kCpr;
@@ -507,9 +536,9 @@ __device__ __forceinline__ LaneLoads<KS> lane_loads(const Args& a, int m0, int n
 #pragma unroll
     for (int j = 0; j < kCpr; ++j) {
         const int row = r + (256 / kCpr) * j;
-        p.voff[j] = ((unsigned)row * (unsigned)a.lda * 2u + chunk * 16u) | (m0 + row < a.M ? 0u : kOob);
+        p.voff[j] = (unsigned)row * (unsigned)a.lda * 2u + chunk * 16u;
         if (NXK) {
-            p.voff[kCpr + j] = ((unsigned)row * (unsigned)a.ldb * 2u + chunk * 16u) | (n0 + row < a.N ? 0u : kOob);
+            p.voff[kCpr + j] = (unsigned)row * (unsigned)a.ldb * 2u + chunk * 16u;
         } else {
             const int krow = 8 * j + (tid >> 5);
             const unsigned c = (unsigned)KnLds::logical(tid & 31, krow);
@@ -603,7 +632,7 @@ __device__ __forceinline__ void read_frags(half8 (&fa)[8], half8 (&fb)[8], const
 // over the odd-numbered ones. One instruction per MFMA keeps the matrix core
 // fed; with one wave per SIMD every other instruction competes with MFMA
 // issue, so the order is pinned at both the IR and the machine level.
-template <int KS, int NXK, bool LOADS>
+template <int KS, int NXK, bool LOADS, bool ZC = false, bool READS = true>
 __device__ __forceinline__ void slice(f32x4 (&acc)[8][8], const half8 (&fa)[8], const half8 (&fb)[8],
                                       half8 (&na)[8], half8 (&nb)[8], const FragPtrs<KS, NXK>& f, int so,
                                       int next_s, const Rsrc& ra, const Rsrc& rb, const LaneLoads<KS>& p,
@@ -618,8 +647,9 @@ __device__ __forceinline__ void slice(f32x4 (&acc)[8][8], const half8 (&fa)[8], 
 #pragma unroll
     for (int q = 0; q < 64; ++q) {
         const int i = q >> 3, j = q & 7;
-        acc[i][j] = mfma16(fb[j], fa[i], acc[i][j]);
-        if ((q & 1) == 0 && q / 2 < kReads) {
+        // ZC: a tile's first slice starts the sums from zero (inline constant C)
+        acc[i][j] = mfma16(fb[j], fa[i], ZC ? f32x4{} : acc[i][j]);
+        if (READS && (q & 1) == 0 && q / 2 < kReads) {
             const int rq = q / 2;
             if (rq >= 1 && rq <= kNb) {
                 if (NXK) {
@@ -644,36 +674,59 @@ __device__ __forceinline__ void slice(f32x4 (&acc)[8][8], const half8 (&fa)[8], 
     }
 }
 
-// Per-workgroup state of the direct-to-LDS kernel. LDS holds the S stages'
-// A blocks, then their B blocks.
+// One output tile: its origin and its operands' buffer resources.
+struct Tile {
+    Rsrc ra, rb;
+    int m0, n0;
+};
+
+template <int NXK>
+__device__ __forceinline__ Tile make_tile(const Args& a, int wid) {
+    int tm, tn;
+    tile_of(wid, a.W, a.grid_m, a.grid_n, a.group_m, a.num_xcd, &tm, &tn);
+    Tile t;
+    t.m0 = tm * BM;
+    t.n0 = tn * BN;
+    t.ra = operand_rsrc(a.A, a.lda, a.M, a.K, t.m0);
+    // B: N x K rows n0.. ; K x N columns n0.. of all K rows
+    t.rb = NXK ? operand_rsrc(a.B, a.ldb, a.N, a.K, t.n0) : operand_rsrc(a.B + t.n0, a.ldb, a.K, a.N - t.n0, 0);
+    return t;
+}
+
+// Per-workgroup constants of the direct-to-LDS kernel. LDS holds the S
+// stages' A blocks, then their B blocks.
 template <int KS, int NXK, int S>
 struct DmaCtx {
-    Rsrc ra, rb;
     LaneLoads<KS> p;
     unsigned bstep;       // scalar-offset advance of B per K step
-    int nk, klast;        // K steps; first k of the last step
-    bool fixup;           // the last step needs fix_last_step
-    int m0, n0, tid, wave, lane;
+    int nk, klast;        // K steps per tile; first k of a tile's last step
+    bool fixup;           // a tile's last step needs fix_last_step
+    int tid, wave, lane;
     u32x4* smem;
     FragPtrs<KS, NXK> fp; // read positions in stage 0
     __device__ __forceinline__ u32x4* a_blk(int st) const { return smem + st * Lds<KS>::kBlock; }
     __device__ __forceinline__ u32x4* b_blk(int st) const { return smem + (S + st) * Lds<KS>::kBlock; }
-    // scalar offsets of K step t
-    __device__ __forceinline__ unsigned soa(int t) const { return t < nk ? (unsigned)t * (unsigned)(KS * 2) : kOob; }
-    __device__ __forceinline__ unsigned sob(int t) const { return t < nk ? (unsigned)t * bstep : kOob; }
 };
 
-// K step t of the direct-to-LDS kernel, in stage st. Its first slice's
-// fragments are in buffer F0 of fa/fb; the next step's first fragments end
-// up in buffer F0 ^ (KS / 32 odd). ST >= 0: st == ST, known at compile time
-// (2-stage ring), so every fragment read is a fixed offset from the stage-0
-// positions. ST < 0: `cur` holds the read positions of stage st on entry and
-// those of the next stage on return; they are derived once per step, before
-// the barrier wait, into registers no matrix instruction reads (a vector ALU
-// write into a just-read MFMA operand register stalls the matrix cores).
-template <int NXK, int KS, int S, int F0, int ST>
+// K step t of tile tc, in stage st (FIRST: the tile's first step, whose
+// first slice starts the sums from zero; LAST: its last step, which leaves
+// the next step's first fragments unread so that they are not held in
+// registers while the tile's C is stored). The steps a workgroup walks form one
+// stream over its tiles: the loads issued here are for the step S further on,
+// which is step t + S of tc or, near the end of tc, a first step of the
+// workgroup's next tile tn (none when !has_next: those loads read nothing
+// and write zeros). Its first slice's fragments are in buffer F0 of fa/fb;
+// the next step's first fragments end up in buffer F0 ^ (KS / 32 odd).
+// ST >= 0: st == ST, known at compile time (2-stage ring), so every fragment
+// read is a fixed offset from the stage-0 positions. ST < 0: `cur` holds the
+// read positions of stage st on entry and those of the next stage on return;
+// they are derived once per step, before the barrier wait, into registers no
+// matrix instruction reads (a vector ALU write into a just-read MFMA operand
+// register stalls the matrix cores).
+template <int NXK, int KS, int S, int F0, int ST, bool FIRST = false, bool LAST = false>
 __device__ __forceinline__ void dma_step(f32x4 (&acc)[8][8], half8 (&fa)[2][8], half8 (&fb)[2][8], int st, int t,
-                                         const Args& a, const DmaCtx<KS, NXK, S>& c, FragPtrs<KS, NXK>& cur) {
+                                         const Args& a, const DmaCtx<KS, NXK, S>& c, FragPtrs<KS, NXK>& cur,
+                                         const Tile& tc, const Tile& tn, bool has_next) {
     using L = Lds<KS>;
     constexpr int kSlices = KS / 32;
     constexpr int kLps = KS / 4;
@@ -683,38 +736,54 @@ __device__ __forceinline__ void dma_step(f32x4 (&acc)[8][8], half8 (&fa)[2][8], 
     const int nst = (st + 1 == S) ? 0 : st + 1;
     const FragPtrs<KS, NXK>& fc = ST >= 0 ? c.fp : cur;
     const int so_c = ST >= 0 ? ST * L::kBlock : 0;
+    static_assert(!FIRST || kSlices > 1, "the zero-start slice is the first of a 2-slice step");
 #pragma unroll
-    for (int s = 0; s + 1 < kSlices; ++s)
-        slice<KS, NXK, false>(acc, fa[(F0 + s) & 1], fb[(F0 + s) & 1], fa[(F0 + s + 1) & 1], fb[(F0 + s + 1) & 1],
-                              fc, so_c, s + 1, c.ra, c.rb, c.p, 0u, 0u, c.smem, c.smem, c.wave);
+    for (int s = 0; s + 1 < kSlices; ++s) {
+        if (FIRST && s == 0)
+            slice<KS, NXK, false, true>(acc, fa[F0 & 1], fb[F0 & 1], fa[(F0 + 1) & 1], fb[(F0 + 1) & 1], fc, so_c,
+                                        1, tc.ra, tc.rb, c.p, 0u, 0u, c.smem, c.smem, c.wave);
+        else
+            slice<KS, NXK, false>(acc, fa[(F0 + s) & 1], fb[(F0 + s) & 1], fa[(F0 + s + 1) & 1],
+                                  fb[(F0 + s + 1) & 1], fc, so_c, s + 1, tc.ra, tc.rb, c.p, 0u, 0u, c.smem, c.smem,
+                                  c.wave);
+    }
     if (ST < 0) cur = shifted(c.fp, nst * L::kBlock);
+    // the step these loads are for (uniform: scalar selects)
+    const int tl = t + S;
+    const bool in_next = tl >= c.nk;
+    const int ls = in_next ? tl - c.nk : tl;
+    const bool live = !in_next || has_next;
+    const unsigned soa = live ? (unsigned)ls * (unsigned)(KS * 2) : kOob;
+    const unsigned sob = live ? (unsigned)ls * c.bstep : kOob;
+    const Rsrc lra = in_next ? tn.ra : tc.ra;
+    const Rsrc lrb = in_next ? tn.rb : tc.rb;
     TG_COMPILER_FENCE();
     __builtin_amdgcn_sched_barrier(0);
     wait_lgkmcnt0();                                  // this wave's reads of stage st returned
     wait_vmcnt<(S - 2) * kLps>();                     // step t + 1 landed
     if (c.fixup && t + 2 == c.nk)
-        fix_last_step<KS, NXK>(c.a_blk(nst), c.b_blk(nst), c.p, a, c.m0, c.n0, c.klast, c.tid, c.wave, c.lane);
+        fix_last_step<KS, NXK>(c.a_blk(nst), c.b_blk(nst), c.p, a, tc.m0, tc.n0, c.klast, c.tid, c.wave, c.lane);
     block_barrier();
-    // step t + S's loads go into the stage just released
-    slice<KS, NXK, true>(acc, fa[FL], fb[FL], fa[FL ^ 1], fb[FL ^ 1], ST >= 0 ? c.fp : cur,
-                         ST >= 0 ? ((ST + 1) & 1) * L::kBlock : 0, 0, c.ra, c.rb, c.p, c.soa(t + S), c.sob(t + S),
-                         c.a_blk(st), c.b_blk(st), c.wave);
+    // the loads go into the stage just released
+    slice<KS, NXK, true, false, !LAST>(acc, fa[FL], fb[FL], fa[FL ^ 1], fb[FL ^ 1], ST >= 0 ? c.fp : cur,
+                                       ST >= 0 ? ((ST + 1) & 1) * L::kBlock : 0, 0, lra, lrb, c.p, soa, sob,
+                                       c.a_blk(st), c.b_blk(st), c.wave);
 }
 
-// Steps t0 .. nk-1 (an even count) in pairs, step t0 in stage st0 with
-// parity P: one-slice steps alternate fragment buffers, and a 2-stage ring
-// alternates stages, so the pair's two steps are two fixed variants.
+// Steps t0 .. nk-1 (an even count) of tile tc in pairs, step t0 in stage st0
+// with parity P: one-slice steps alternate fragment buffers, and a 2-stage
+// ring alternates stages, so the pair's two steps are two fixed variants.
 template <int NXK, int KS, int S, int P>
 __device__ __forceinline__ void step_pairs(f32x4 (&acc)[8][8], half8 (&fa)[2][8], half8 (&fb)[2][8], int t0,
                                            int st0, const Args& a, const DmaCtx<KS, NXK, S>& c,
-                                           FragPtrs<KS, NXK>& cur) {
+                                           FragPtrs<KS, NXK>& cur, const Tile& tc, const Tile& tn, bool has_next) {
     constexpr int F1 = KS == 32 ? P : 0, F2 = KS == 32 ? (P ^ 1) : 0;
     constexpr int S1 = S == 2 ? P : -1, S2 = S == 2 ? (P ^ 1) : -1;
     int st = st0;
     for (int t = t0; t < c.nk; t += 2) {
-        dma_step<NXK, KS, S, F1, S1>(acc, fa, fb, st, t, a, c, cur);
+        dma_step<NXK, KS, S, F1, S1>(acc, fa, fb, st, t, a, c, cur, tc, tn, has_next);
         st = (st + 1 == S) ? 0 : st + 1;
-        dma_step<NXK, KS, S, F2, S2>(acc, fa, fb, st, t + 1, a, c, cur);
+        dma_step<NXK, KS, S, F2, S2>(acc, fa, fb, st, t + 1, a, c, cur, tc, tn, has_next);
         st = (st + 1 == S) ? 0 : st + 1;
     }
 }
@@ -722,13 +791,18 @@ __device__ __forceinline__ void step_pairs(f32x4 (&acc)[8][8], half8 (&fa)[2][8]
 // Tile kernel with both operands streamed straight into an S-stage LDS ring
 // of KS-deep K steps (KS / 32 slices each): A K-contiguous, B either
 // K-contiguous (stored N x K, NXK = 1) or kept [k][n] and transposed on read
-// (stored K x N). Step t lives in stage t mod S. The barrier of step t sits
-// before its last slice: it follows every wave's last fragment read of stage
-// t (so step t + S's loads go into that stage during the last slice) and
-// every wave's loads of step t + 1 (whose first fragments that slice reads).
-// A step's loads thus have S - 1 steps less one slice to land. Every step
-// issues the same number of loads (steps past K read nothing and write zeros
-// into stages that are never read), so all wait counts are constants.
+// (stored K x N). Workgroup b computes tiles b, b + grid, ... (grid = the
+// workgroups launched: one per compute unit for 64-deep steps, else one per
+// tile). Its K steps form one stream across those tiles; step g lives in
+// stage g mod S. The barrier of a step sits before its last slice: it
+// follows every wave's last fragment read of the step's stage (so the loads
+// for the step S further on go into that stage during the last slice) and
+// every wave's loads of the next step (whose first fragments that slice
+// reads). A step's loads thus have S - 1 steps less one slice to land, and
+// the next tile's first steps load while the current tile finishes, so a
+// tile's C stores drain while the next tile computes. Every step issues the
+// same number of loads (steps past the last tile read nothing and write
+// zeros into stages that are never read), so all wait counts are constants.
 template <int NXK, bool VEC_C, int KS, int S>
 __global__ void __launch_bounds__(NTHREADS)
 __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -744,62 +818,79 @@ tgemm_f16_dma_kernel(Args a) {
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
-
-    int tm, tn;
-    tile_of((int)blockIdx.x, a.W, a.grid_m, a.grid_n, a.group_m, a.num_xcd, &tm, &tn);
-    const int m0 = tm * BM, n0 = tn * BN;
     const int nk = (a.K + KS - 1) / KS;
 
+    int wid = (int)blockIdx.x;
+    Tile tc = make_tile<NXK>(a, wid);
+    bool has_next = wid + a.grid < a.W;              // K == 0: one tile per workgroup
+    Tile tn = has_next ? make_tile<NXK>(a, wid + a.grid) : tc;
     f32x4 acc[8][8];
-    zero_acc(acc);
+    if (KS == 32) zero_acc(acc);
 
+    DmaCtx<KS, NXK, S> c;
+    c.p = lane_loads<KS, NXK>(a, tid);
+    c.bstep = NXK ? (unsigned)(KS * 2) : (unsigned)KS * (unsigned)a.ldb * 2u;
+    c.nk = nk;
+    c.klast = (nk - 1) * KS;
+    c.fixup = (a.K % KS) != 0 || (!NXK && (a.N % 8) != 0);
+    c.tid = tid;
+    c.wave = wave;
+    c.lane = lane;
+    c.smem = smem;
+    c.fp = frag_ptrs<KS, NXK>(c.a_blk(0), c.b_blk(0), wm, wn, lane);
+    half8 fa[2][8], fb[2][8];
     if (nk > 0) {
-        DmaCtx<KS, NXK, S> c;
-        c.ra = operand_rsrc(a.A, a.lda, a.M, a.K, m0);
-        // B: N x K rows n0.. ; K x N columns n0.. of all K rows
-        c.rb = NXK ? operand_rsrc(a.B, a.ldb, a.N, a.K, n0) : operand_rsrc(a.B + n0, a.ldb, a.K, a.N - n0, 0);
-        c.p = lane_loads<KS, NXK>(a, m0, n0, tid);
-        c.bstep = NXK ? (unsigned)(KS * 2) : (unsigned)KS * (unsigned)a.ldb * 2u;
-        c.nk = nk;
-        c.klast = (nk - 1) * KS;
-        c.fixup = (a.K % KS) != 0 || (!NXK && (a.N % 8) != 0);
-        c.m0 = m0;
-        c.n0 = n0;
-        c.tid = tid;
-        c.wave = wave;
-        c.lane = lane;
-        c.smem = smem;
-        c.fp = frag_ptrs<KS, NXK>(c.a_blk(0), c.b_blk(0), wm, wn, lane);
-
-        // prologue: steps 0 .. S-1
+        // prologue: steps 0 .. S-1 of the first tile (a workgroup with more
+        // than one tile has nk >= S)
         for (int t = 0; t < S; ++t)
             for (int idx = 0; idx < kLps; ++idx)
-                issue_load<KS, NXK>(c.ra, c.rb, c.p, idx, c.soa(t), c.sob(t), c.a_blk(t), c.b_blk(t), wave);
+                issue_load<KS, NXK>(tc.ra, tc.rb, c.p, idx, t < nk ? (unsigned)t * (unsigned)(KS * 2) : kOob,
+                                    t < nk ? (unsigned)t * c.bstep : kOob, c.a_blk(t), c.b_blk(t), wave);
         wait_vmcnt<(S - 1) * kLps>();                 // step 0 landed
-        if (c.fixup && nk == 1) fix_last_step<KS, NXK>(c.a_blk(0), c.b_blk(0), c.p, a, m0, n0, c.klast, tid, wave, lane);
+        if (c.fixup && nk == 1)
+            fix_last_step<KS, NXK>(c.a_blk(0), c.b_blk(0), c.p, a, tc.m0, tc.n0, c.klast, tid, wave, lane);
         block_barrier();
-
-        half8 fa[2][8], fb[2][8];
         read_frags<KS, NXK>(fa[0], fb[0], c.fp, 0);
-        FragPtrs<KS, NXK> cur = c.fp;                 // read positions of the current stage
-        if constexpr (KS == 64) {
-            // two slices per step: every step starts on fragment buffer 0
-            int st = 0;
-            for (int t = 0; t < nk; ++t) {
-                dma_step<NXK, KS, S, 0, -1>(acc, fa, fb, st, t, a, c, cur);
+    }
+    FragPtrs<KS, NXK> cur = c.fp;                     // read positions of the current stage
+    if constexpr (KS == 64) {
+        // tile after tile (two slices per step: every step starts on
+        // fragment buffer 0). A tile's first slice starts its sums from zero
+        // and its C is stored after the last step, so the accumulators carry
+        // nothing from one tile to the next; only the next tile's first
+        // fragments and the load stream do.
+        // (64-deep steps are used with nk >= 2)
+        int st = 0;
+        for (;;) {
+            dma_step<NXK, KS, S, 0, -1, true>(acc, fa, fb, st, 0, a, c, cur, tc, tn, has_next);
+            st ^= 1;
+            for (int t = 1; t + 1 < nk; ++t) {
+                dma_step<NXK, KS, S, 0, -1>(acc, fa, fb, st, t, a, c, cur, tc, tn, has_next);
                 st ^= 1;
             }
-        } else if (nk & 1) {
-            // an odd step count starts with one step; the rest go in pairs
-            dma_step<NXK, KS, S, 0, S == 2 ? 0 : -1>(acc, fa, fb, 0, 0, a, c, cur);
-            step_pairs<NXK, KS, S, 1>(acc, fa, fb, 1, 1 % S, a, c, cur);
-        } else {
-            step_pairs<NXK, KS, S, 0>(acc, fa, fb, 0, 0, a, c, cur);
+            dma_step<NXK, KS, S, 0, -1, false, true>(acc, fa, fb, st, nk - 1, a, c, cur, tc, tn, has_next);
+            st ^= 1;
+            store_c<VEC_C>(acc, a, tc.m0, tc.n0, wm, wn, lane);
+            if (!has_next) break;
+            read_frags<KS, NXK>(fa[0], fb[0], cur, 0);   // the next tile's first fragments
+            wid += a.grid;
+            tc = tn;
+            has_next = wid + a.grid < a.W;
+            if (has_next) tn = make_tile<NXK>(a, wid + a.grid);
         }
-        // no load may still be writing this workgroup's LDS when it exits
-        wait_vmcnt<0>();
+    } else {
+        // one tile per workgroup; an odd step count starts with one step,
+        // the rest go in pairs
+        if (nk & 1) {
+            dma_step<NXK, KS, S, 0, S == 2 ? 0 : -1>(acc, fa, fb, 0, 0, a, c, cur, tc, tn, has_next);
+            step_pairs<NXK, KS, S, 1>(acc, fa, fb, 1, 1 % S, a, c, cur, tc, tn, has_next);
+        } else {
+            step_pairs<NXK, KS, S, 0>(acc, fa, fb, 0, 0, a, c, cur, tc, tn, has_next);
+        }
+        store_c<VEC_C>(acc, a, tc.m0, tc.n0, wm, wn, lane);
     }
-    store_c<VEC_C>(acc, a, m0, n0, wm, wn, lane);
+    // no load may still be writing this workgroup's LDS when it exits
+    wait_vmcnt<0>();
 }
 
 template <int NXK, bool VEC, bool VEC_C>
@@ -840,6 +931,30 @@ static const void* pick_kernel(const Plan& pl) {
 
 static thread_local int g_last_hip_error = 0;
 
+// The direct-to-LDS kernel with 64-deep steps runs one workgroup per compute
+// unit when a workgroup has at least two steps per tile (the cross-tile load
+// stream reaches at most one tile ahead).
+static bool persistent(const Plan& pl) {
+    return (pl.variant & kDma) && pl.k_step == 64 && pl.K >= 2 * 64;
+}
+
+// Compute units of the current device (cached per device), or -hipError_t.
+static int compute_units() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return -(int)e;
+    if (dev >= 0 && dev < 64) {
+        const int v = cache[dev].load(std::memory_order_relaxed);
+        if (v > 0) return v;
+    }
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return -(int)e;
+    if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
 }  // namespace tg
 
 extern "C" int tgemm_f16_config(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
@@ -866,10 +981,21 @@ extern "C" int tgemm_f16_config(int64_t M, int64_t N, int64_t K, const void* A, 
     args.W = pl.W;
     args.group_m = pl.group_m;
     args.num_xcd = pl.num_xcd;
+    args.grid = pl.W;
+    args.c16 = ((uintptr_t)C % 16 == 0) && (pl.ldc % 8 == 0);
+    if (tg::persistent(pl)) {
+        // one workgroup per compute unit, each walking several tiles
+        const int ncu = tg::compute_units();
+        if (ncu < 0) {
+            tg::g_last_hip_error = -ncu;
+            return TGEMM_ERR_HIP;
+        }
+        if (ncu > 0 && ncu < pl.W) args.grid = ncu;
+    }
     const void* fn = tg::pick_kernel(pl);
     if (!fn) return TGEMM_ERR_UNSUPPORTED;
     void* kargs[] = {&args};
-    const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)pl.W),
+    const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)args.grid),
                                          dim3(tg::NTHREADS), kargs, 0, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) {
         tg::g_last_hip_error = (int)e;

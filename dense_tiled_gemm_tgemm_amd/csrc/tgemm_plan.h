@@ -145,14 +145,17 @@ inline int make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
     // unaligned addresses): row strides small enough for 32-bit panel
     // offsets; a K x N B additionally needs every byte offset it forms,
     // below (K + 64) * ldb * 2 + 512, to stay below 2^31.
-    const bool dma = !force_generic && lda <= kMaxDmaLd &&
+    // (K == 0 only writes zeros: the register-staged kernel does that)
+    const bool dma = !force_generic && K > 0 && lda <= kMaxDmaLd &&
                      (b_layout == TGEMM_B_NxK ? ldb <= kMaxDmaLd
                                               : ldb < (int64_t(1) << 30) && (K + 64) * ldb < (int64_t(1) << 30) - 512);
     pl->variant = (vec_ab ? kVecAB : 0) | (vec_c ? kVecC : 0) |
                   (b_layout == TGEMM_B_NxK ? kLayoutNxK : 0) | (dma ? kDma : 0);
     if (dma) {
-        // a ring deeper than 2 stages implies 32-deep steps
-        pl->k_step = k_step ? k_step : (stages > 2 ? 32 : kDefaultDmaKStep);
+        // a ring deeper than 2 stages implies 32-deep steps; 64-deep steps
+        // need at least two steps
+        pl->k_step = k_step ? k_step : ((stages > 2 || K <= 64) ? 32 : kDefaultDmaKStep);
+        if (pl->k_step == 64 && K <= 64) return TGEMM_ERR_INVALID;
         pl->stages = pl->k_step == 64 ? 2 : (stages ? stages : kDefaultDmaStages32);
     } else {
         pl->k_step = BK;

@@ -87,9 +87,9 @@ int tgemm_f16(int64_t M, int64_t N, int64_t K,
  *                  die-aware renumbering; 0 = default (8 on MI355X);
  *                  1 disables the renumbering; 1..64 otherwise.
  *   k_step:        K depth of one LDS stage of the direct-to-LDS path
- *                  (used whenever both row strides are small enough for
- *                  32-bit offsets): 0 = default (64, or 32 when stages > 2),
- *                  32 or 64.
+ *                  (used whenever K > 0 and both row strides are small
+ *                  enough for 32-bit offsets): 0 = default (64, or 32 when
+ *                  stages > 2 or K <= 64), 32 or 64 (64 needs K > 64).
  *   stages:        LDS ring depth of that path: 0 = default (2 at k_step 64,
  *                  4 at k_step 32), 2..5 (k_step 64 allows only 2). Other
  *                  paths ignore k_step and stages.

@@ -69,6 +69,7 @@ def _plan(M, N, K, A=PA, lda=None, B=PB, ldb=None, lay="KxN", C=PC, ldc=None, **
     dict(M=4, N=4, K=4, stages=1),
     dict(M=4, N=4, K=4, stages=6),
     dict(M=4, N=4, K=4, k_step=64, stages=3),
+    dict(M=4, N=4, K=64, k_step=64),             # 64-deep steps need K > 64
 ])
 def test_invalid_arguments_rejected(args):
     rc, info = _plan(**args)
@@ -142,6 +143,11 @@ def test_plan_variants_and_grid():
     assert not info["variant"] & DMA
     rc, info = _plan(512, 512, 512, ldb=((1 << 30) - 512) // (512 + 64) - 1)
     assert info["variant"] & DMA
+    # K <= 64 streams 32-deep steps; K == 0 (zeros only) takes the register-staged kernel
+    rc, info = _plan(512, 512, 64, lay="NxK")
+    assert info["variant"] & DMA and (info["bk"], info["stages"]) == (32, 4)
+    rc, info = _plan(512, 512, 0, lay="NxK", lda=1, ldb=1)
+    assert rc == 0 and not info["variant"] & DMA
     # group_m larger than the tile rows is clamped (same map)
     rc, info = _plan(512, 4096, 64, group_m=100)
     assert info["group_m"] == 2

@@ -259,9 +259,40 @@ def test_pipeline_choices_are_bit_identical(oracle_mod, M, N, K, lay):
     got = _host(base)
     _full_check(oracle_mod, A, B, lay, got, f"pipelines {M}x{N}x{K} {lay}")
     for ks, st in PIPES:
+        if ks == 64 and K <= 64:                     # 64-deep steps need two steps or more
+            with pytest.raises(tg.TgemmError, match="invalid"):
+                tg.mm(Ad, Bd, lay, k_step=ks, stages=st)
+            continue
         C = tg.mm(Ad, Bd, lay, k_step=ks, stages=st)
         torch.cuda.synchronize()
         assert torch.equal(C.view(torch.int16), base.view(torch.int16)), (ks, st)
+
+
+@pytest.mark.parametrize("lay", ["NxK", "KxN"])
+@pytest.mark.parametrize("M,N,K", [(4300, 4300, 1000), (4608, 3840, 200), (4352, 4096, 128)])
+def test_persistent_grid_matches_register_staged(oracle_mod, M, N, K, lay):
+    """More output tiles (270 .. 289) than compute units: the direct-to-LDS kernel
+    runs one workgroup per compute unit, each walking one or two tiles with the
+    next tile's first K steps streamed in while the current one finishes. Edge
+    tiles, partial last K steps (K % 64 = 40, 8) and the shortest persistent K
+    (two steps) included. Bit-identical to the register-staged kernel (one
+    workgroup per tile), also under another raster, and within tolerance of the
+    oracle on sampled outputs."""
+    print(f"case persistent {M}x{N}x{K} {lay}", flush=True)
+    A = inputs.random_f16((M, K), M + 7 * K)
+    B = inputs.random_f16((N, K) if lay == "NxK" else (K, N), N + 5 * K)
+    Ad, Bd = _dev(A), _dev(B)
+    base = tg.mm(Ad, Bd, lay, force_generic=1)
+    C = tg.mm(Ad, Bd, lay)
+    C2 = tg.mm(Ad, Bd, lay, group_m=3, num_xcd=1)
+    torch.cuda.synchronize()
+    assert torch.equal(C.view(torch.int16), base.view(torch.int16))
+    assert torch.equal(C2.view(torch.int16), base.view(torch.int16))
+    got = _host(C)
+    I, J = inputs.sample_points(M, N, 4096, M + N + K)
+    ref, ab = oracle_mod.gemm_points(A, B, lay, I, J)
+    res = oracle_mod.check(got[I, J], ref, ab)
+    assert res["nfail"] == 0, res
 
 
 def _nan_padded(rows, cols, ld, seed, offset):
