@@ -11,7 +11,7 @@ Prints ONE JSON line (rank 0):
   cpu_baseline  the CPU oracle (fp64, all OpenMP threads) timed on a bounded
              block of whole output rows of the same workload
 
-Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload NAME]
+Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 100] [--workload NAME]
 """
 import argparse
 import hashlib
@@ -87,13 +87,19 @@ def cpu_baseline(A, B, w, got, target_s: float = 12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the board's clock settles under sustained MFMA load over ~40 launches of
+    # this size: 100 warmup launches (~80 ms) reach the steady state
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mfma-ceiling", action="store_true",
-                    help="instead of the GEMM, time the matrix-core issue probe (the GEMM's "
-                         "MFMA stream without memory traffic) and print its TFLOP/s")
+                    help="instead of the GEMM, time the matrix-core ceiling probe (the GEMM's "
+                         "instruction stream on the workload's values, without synchronization, "
+                         "tile changes or C stores) and print its TFLOP/s")
+    ap.add_argument("--torch-matmul", action="store_true",
+                    help="instead of this library's GEMM, time torch.matmul (the vendor BLAS) on "
+                         "the same inputs and print its TFLOP/s (context, not the headline)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the GEMM, run device-to-device copies of MIB MiB; used to "
                          "scale the HBM byte counters (FETCH_SIZE / WRITE_SIZE) of a profiler run")
@@ -121,22 +127,38 @@ def main():
     from dense_tiled_gemm_tgemm_amd import inputs
 
     if args.mfma_ceiling:
+        # the GEMM's instruction stream without synchronization, tile changes or
+        # C stores, on the workload's own A values (the operands' switching
+        # activity sets the power-limited clock)
         tg.load()
+        name = args.workload or inputs.HEADLINE
+        w = inputs.WORKLOADS[name]
+        A, _ = inputs.make_inputs(w)
+        nbytes = 1 << min(26, int(A.nbytes).bit_length() - 1)
+        data = torch.from_numpy(A.reshape(-1)[: nbytes // 2].copy()).to("cuda:0")
         stream = torch.cuda.current_stream()
-        wg, iters = 1024, 512
+        wg, iters = 256, 400
         out = torch.empty(wg * 256, dtype=torch.float32, device="cuda:0")
-        for _ in range(args.warmup):
-            tg.mfma_issue_probe(wg, iters, out.data_ptr(), stream.cuda_stream)
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        ev[0].record(stream)
-        for _ in range(args.steps):
-            tg.mfma_issue_probe(wg, iters, out.data_ptr(), stream.cuda_stream)
-        ev[1].record(stream)
-        torch.cuda.synchronize()
-        ms = ev[0].elapsed_time(ev[1]) / args.steps
-        flops = wg * 4 * iters * 16 * 2.0 * 32 * 32 * 16
-        print(json.dumps({"probe": "mfma_issue", "workgroups": wg, "iters": iters, "ms": round(ms, 5),
-                          "tflops": round(flops / ms / 1e9, 1), "peak": PEAK_F16_TFLOPS}), flush=True)
+        flops = wg * 4 * iters * 128 * 2.0 * 16 * 16 * 32
+
+        def probe_ms(buf):
+            for _ in range(args.warmup):
+                tg.mfma_issue_probe(wg, iters, buf.data_ptr(), nbytes, out.data_ptr(), stream.cuda_stream)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record(stream)
+            for _ in range(args.steps):
+                tg.mfma_issue_probe(wg, iters, buf.data_ptr(), nbytes, out.data_ptr(), stream.cuda_stream)
+            ev[1].record(stream)
+            torch.cuda.synchronize()
+            return ev[0].elapsed_time(ev[1]) / args.steps
+
+        ms = probe_ms(data)
+        ms0 = probe_ms(torch.zeros_like(data))      # same instructions, operands that never toggle
+        print(json.dumps({"probe": "mfma_ceiling", "data": f"{name} A, first {nbytes >> 20} MiB",
+                          "workgroups": wg, "iters": iters, "ms": round(ms, 5),
+                          "tflops": round(flops / ms / 1e9, 1),
+                          "tflops_zero_operands": round(flops / ms0 / 1e9, 1),
+                          "peak": PEAK_F16_TFLOPS}), flush=True)
         return
 
     name = args.workload or inputs.HEADLINE
@@ -151,6 +173,26 @@ def main():
     stream = torch.cuda.current_stream(dev)
     sptr = stream.cuda_stream
     lda, ldb, ldc = w.K, B.shape[1], w.N
+
+    if args.torch_matmul:
+        Bt = Bd.t() if w.b_layout == "NxK" else Bd
+
+        def vendor():
+            torch.matmul(Ad, Bt, out=Cd)
+
+        for _ in range(args.warmup):
+            vendor()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for _ in range(args.steps):
+            vendor()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / args.steps
+        print(json.dumps({"vendor": "torch.matmul", "workload": name, "ms": round(ms, 5),
+                          "tflops": round(float(w.flops) / ms / 1e9, 1)}), flush=True)
+        return
 
     def step():
         rc = tg.tgemm_f16(w.M, w.N, w.K, Ad.data_ptr(), lda, Bd.data_ptr(), ldb, w.b_layout,

@@ -61,7 +61,7 @@ def load():
     lib.tgemm_plan_f16.argtypes = [_I64, _I64, _I64, _P, _I64, _P, _I64, _INT, _P, _I64,
                                    _INT, _INT, _INT, _INT, _INT, ctypes.POINTER(_I64)]
     lib.tgemm_mfma_issue_probe.restype = _INT
-    lib.tgemm_mfma_issue_probe.argtypes = [_I64, _INT, _P, _P]
+    lib.tgemm_mfma_issue_probe.argtypes = [_I64, _INT, _P, _I64, _P, _P]
     lib.tgemm_tile_of.restype = _INT
     lib.tgemm_tile_of.argtypes = [_I64, _I64, _INT, _INT, _I64, ctypes.POINTER(_I64), ctypes.POINTER(_I64)]
     _lib = lib
@@ -110,9 +110,11 @@ def tgemm_tile_of(grid_m, grid_n, group_m, num_xcd, wid):
     return tm.value, tn.value
 
 
-def mfma_issue_probe(workgroups: int, iters: int, out_ptr: int, stream=None) -> None:
-    """Launch the matrix-core issue probe (measurement aid; see include/tgemm.h)."""
-    rc = int(load().tgemm_mfma_issue_probe(int(workgroups), int(iters), out_ptr, stream))
+def mfma_issue_probe(workgroups: int, iters: int, data_ptr: int, data_bytes: int, out_ptr: int,
+                     stream=None) -> None:
+    """Launch the matrix-core ceiling probe (measurement aid; see include/tgemm.h)."""
+    rc = int(load().tgemm_mfma_issue_probe(int(workgroups), int(iters), data_ptr, int(data_bytes), out_ptr,
+                                           stream))
     if rc != TGEMM_OK:
         raise TgemmError(rc, "mfma_issue_probe")
 

@@ -623,7 +623,7 @@ __device__ __forceinline__ void read_frags(half8 (&fa)[8], half8 (&fb)[8], const
         fb[j] = NXK ? frag_b_kc(f, 0, s, j) : join_halves(frag_b_tr(f, 0, s, j, 0), frag_b_tr(f, 0, s, j, 1));
 }
 
-// One k32 slice: 64 MFMAs (8 x 8 blocks, row-block-major) on the current
+// One k32 slice: 64 MFMAs (8 x 8 blocks, serpentine by row) on the current
 // fragments, with the next slice's fragment reads (slice next_s of the
 // stage `so` slots from stage 0) and, when LOADS, the 2 * CPR load
 // instructions of one K step placed between them: reads after every
@@ -646,7 +646,9 @@ __device__ __forceinline__ void slice(f32x4 (&acc)[8][8], const half8 (&fa)[8], 
     s16x4 lo[8];
 #pragma unroll
     for (int q = 0; q < 64; ++q) {
-        const int i = q >> 3, j = q & 7;
+        // serpentine over the 8 x 8 blocks: a row change keeps the B fragment,
+        // so one operand changes per MFMA throughout (less switching power)
+        const int i = q >> 3, j = (i & 1) ? 7 - (q & 7) : (q & 7);
         // ZC: a tile's first slice starts the sums from zero (inline constant C)
         acc[i][j] = mfma16(fb[j], fa[i], ZC ? f32x4{} : acc[i][j]);
         if (READS && (q & 1) == 0 && q / 2 < kReads) {

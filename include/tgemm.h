@@ -139,15 +139,20 @@ int tgemm_tile_of(int64_t grid_m, int64_t grid_n, int group_m, int num_xcd,
 
 /*
  * Measurement aid (not part of the product operation): launches `workgroups`
- * workgroups of 256 threads that run the GEMM kernel's matrix-core stream
- * (iters rounds of 16 independent 32x32x16 fp16 MFMAs per wave) on
- * register-resident pseudo-random binary16 data, with no memory traffic.
- * Its TFLOP/s is the ceiling the matrix cores of the board sustain for such
- * data (clock and power limits included). `out` must hold workgroups * 256
- * floats of device memory. Returns TGEMM_OK, TGEMM_ERR_INVALID (bad sizes,
- * NULL out) or TGEMM_ERR_HIP.
+ * workgroups of 256 threads that run the GEMM kernel's instruction stream
+ * without its synchronization, tile changes or C stores: per wave, `iters`
+ * rounds of two slices of 64 independent 16x16x32 fp16 MFMAs, with 16
+ * 128-bit LDS fragment reads and 8 direct-to-LDS 16-byte loads per slice
+ * (operands drawn from `data`). MI355X is power-limited under MFMA load and
+ * the operands' switching activity sets the clock, so with the benchmark's
+ * inputs as `data` its TFLOP/s is the ceiling the GEMM's instruction mix
+ * reaches on this board. `data`: device memory, 16-byte aligned, data_bytes
+ * a power of two in [1 MiB, 1 GiB]; `out` must hold workgroups * 256 floats
+ * of device memory. Returns TGEMM_OK, TGEMM_ERR_INVALID (bad sizes or
+ * pointers) or TGEMM_ERR_HIP.
  */
-int tgemm_mfma_issue_probe(int64_t workgroups, int iters, float* out, void* stream);
+int tgemm_mfma_issue_probe(int64_t workgroups, int iters, const void* data, int64_t data_bytes,
+                           float* out, void* stream);
 
 #ifdef __cplusplus
 }

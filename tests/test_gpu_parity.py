@@ -349,10 +349,15 @@ def test_inf_in_neighbouring_row_stays_local(lay):
 
 
 def test_mfma_issue_probe_runs():
-    """The matrix-core issue probe (measurement aid) launches and produces finite sums."""
+    """The matrix-core ceiling probe (measurement aid) launches on binary16 data and
+    produces finite sums; bad sizes are rejected before any launch."""
+    print("case mfma ceiling probe", flush=True)
+    data = _dev(inputs.random_f16((1 << 19,), 7) * np.float16(0.1))     # 1 MiB
     out = torch.empty(8 * 256, dtype=torch.float32, device=DEV)
-    tg.mfma_issue_probe(8, 4, out.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    st = torch.cuda.current_stream().cuda_stream
+    tg.mfma_issue_probe(8, 4, data.data_ptr(), 1 << 20, out.data_ptr(), st)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(out).all())
-    with pytest.raises(tg.TgemmError):
-        tg.mfma_issue_probe(0, 4, out.data_ptr())
+    for wg, nb in ((0, 1 << 20), (8, (1 << 20) + 2), (8, 1 << 19)):
+        with pytest.raises(tg.TgemmError):
+            tg.mfma_issue_probe(wg, 4, data.data_ptr(), nb, out.data_ptr(), st)
