@@ -64,23 +64,52 @@ WORKLOADS = {
 HEADLINE = "sq8192_nt"
 
 
-def _draw(rng: np.random.Generator, dist: tuple, shape) -> np.ndarray:
+def _draw64(rng: np.random.Generator, dist: tuple, shape) -> np.ndarray:
     kind = dist[0]
     if kind == "uniform":
-        x = rng.uniform(dist[1], dist[2], shape)
-    elif kind == "normal":
-        x = rng.standard_normal(shape) * dist[1]
-    else:
-        raise ValueError(f"unknown distribution {dist!r}")
-    return x.astype(np.float16)
+        return rng.uniform(dist[1], dist[2], shape)
+    if kind == "normal":
+        return rng.standard_normal(shape) * dist[1]
+    raise ValueError(f"unknown distribution {dist!r}")
 
 
-def make_inputs(w: Workload):
-    """(A, B) as C-contiguous float16 arrays: A is (M, K), B is ``w.b_shape``."""
+def _draw(rng: np.random.Generator, dist: tuple, shape) -> np.ndarray:
+    return _draw64(rng, dist, shape).astype(np.float16)
+
+
+def to_bf16_bits(x) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) of finite values: round to binary32 with
+    numpy, then keep the upper 16 bits rounded to nearest even (add 0x7fff plus
+    the lowest kept bit, then shift). Used to draw inputs only."""
+    u = np.ascontiguousarray(np.asarray(x, dtype=np.float64).astype(np.float32)).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+def make_inputs(w: Workload, ab_type: str = "f16"):
+    """(A, B) as C-contiguous arrays: A is (M, K), B is ``w.b_shape``.
+    ab_type "f16": float16 arrays; "bf16": uint16 bfloat16 bit patterns drawn
+    from the same seeded values."""
     rng = np.random.default_rng(w.seed)
-    A = _draw(rng, w.a_dist, (w.M, w.K))
-    B = _draw(rng, w.b_dist, w.b_shape)
+    if ab_type == "f16":
+        A = _draw(rng, w.a_dist, (w.M, w.K))
+        B = _draw(rng, w.b_dist, w.b_shape)
+    elif ab_type == "bf16":
+        A = to_bf16_bits(_draw64(rng, w.a_dist, (w.M, w.K)))
+        B = to_bf16_bits(_draw64(rng, w.b_dist, w.b_shape))
+    else:
+        raise ValueError(f"unknown input type {ab_type!r}")
     return A, B
+
+
+def random_bf16(shape, seed: int, dist=("uniform", -1.0, 1.0)) -> np.ndarray:
+    """Seeded bfloat16 bit patterns (uint16) for small ad-hoc shapes."""
+    return to_bf16_bits(_draw64(np.random.default_rng(seed), dist, shape))
+
+
+def random_bias(n: int, seed: int, scale: float = 1.0) -> np.ndarray:
+    """Seeded float32 bias vector, uniform in [-scale, scale]."""
+    return (np.random.default_rng(seed).uniform(-scale, scale, n)).astype(np.float32)
 
 
 def random_f16(shape, seed: int, dist=("uniform", -1.0, 1.0)) -> np.ndarray:

@@ -15,6 +15,14 @@ gemm_points(A, B, b_layout, I, J)   the same for selected (i, j)
 check(got, ref, absum)    the per-element tolerance test
 raster                    submodule: the pages' block-id -> tile maps
 
+Extended operation (other element types, scale / bias / rectifier on store):
+bf16_to_double(bits), f32_to_double(bits)   exact decoders (uint16 / uint32 in)
+ulp_type(x, c_type)       spacing of binary16 / bfloat16 / binary32 at |x|
+gemm_ex(A, B, b_layout, ab_type, alpha, bias, act[, I, J])
+                          fp64 reference of act(alpha*sum + bias[j]) and its
+                          tolerance magnitude |alpha|*sum|a*b| + |bias[j]|
+check_ex(got, c_type, ref, tol_mag)   the tolerance test for any output type
+
 ``A`` is a 2-D numpy float16/uint16 array (M x K, row stride = its first
 stride). ``B`` is K x N for ``b_layout="KxN"`` and N x K for ``"NxK"``.
 """
@@ -56,6 +64,21 @@ def _load():
                                  _I64, _P, _P, _P, _P]
     lib.ref_check_f16.restype = _I64
     lib.ref_check_f16.argtypes = [_I64, _P, _P, _P, ctypes.c_double, _P, _P, _I64]
+    lib.ref_bf16_to_double.restype = ctypes.c_double
+    lib.ref_bf16_to_double.argtypes = [ctypes.c_uint16]
+    lib.ref_f32_to_double.restype = ctypes.c_double
+    lib.ref_f32_to_double.argtypes = [ctypes.c_uint32]
+    lib.ref_decode_bf16.restype = None
+    lib.ref_decode_bf16.argtypes = [_I64, _P, _P]
+    lib.ref_decode_f32.restype = None
+    lib.ref_decode_f32.argtypes = [_I64, _P, _P]
+    lib.ref_ulp_type.restype = ctypes.c_double
+    lib.ref_ulp_type.argtypes = [ctypes.c_double, ctypes.c_int]
+    lib.ref_gemm_ex.restype = ctypes.c_int
+    lib.ref_gemm_ex.argtypes = [_I64, _I64, _I64, _P, _I64, _P, _I64, ctypes.c_int, ctypes.c_int,
+                                ctypes.c_double, _P, ctypes.c_int, _I64, _P, _P, _P, _P]
+    lib.ref_check_ex.restype = _I64
+    lib.ref_check_ex.argtypes = [_I64, ctypes.c_int, _P, _P, _P, _P, ctypes.c_double, _P, _P, _I64]
     _lib = lib
     return lib
 
@@ -156,5 +179,109 @@ def check(got, ref, absum, rel: float = 1e-3, max_report: int = 10) -> dict:
     first = np.full(max(max_report, 1), -1, dtype=np.int64)
     nfail = int(_load().ref_check_f16(g.size, _ptr(g), _ptr(r), _ptr(s), float(rel),
                                       _ptr(worst), _ptr(first), max_report))
+    return {"n": int(g.size), "nfail": nfail, "worst": float(worst[0]),
+            "first_fail": [int(x) for x in first[:min(nfail, max_report)]]}
+
+
+# ------------------------------------------------- extended operation --
+
+# element type codes: 0 binary16, 1 bfloat16, 2 binary32
+_TYPES = {"f16": 0, "bf16": 1, "f32": 2, 0: 0, 1: 1, 2: 2}
+_ACTS = {"none": 0, "relu": 1, 0: 0, 1: 1}
+
+
+def bf16_to_double(bits: np.ndarray) -> np.ndarray:
+    src = np.ascontiguousarray(np.asarray(bits, dtype=np.uint16))
+    out = np.empty(src.shape, dtype=np.float64)
+    _load().ref_decode_bf16(src.size, _ptr(src), _ptr(out))
+    return out
+
+
+def f32_to_double(bits: np.ndarray) -> np.ndarray:
+    b = np.asarray(bits)
+    if b.dtype == np.float32:
+        b = b.view(np.uint32)
+    src = np.ascontiguousarray(b, dtype=np.uint32)
+    out = np.empty(src.shape, dtype=np.float64)
+    _load().ref_decode_f32(src.size, _ptr(src), _ptr(out))
+    return out
+
+
+def ulp_type(x: float, c_type) -> float:
+    return float(_load().ref_ulp_type(float(x), _TYPES[c_type]))
+
+
+def _u16(x) -> np.ndarray:
+    """binary16 or bfloat16 operand as uint16 bit patterns (float16 arrays are viewed)."""
+    x = np.asarray(x)
+    if x.dtype == np.float16:
+        return x.view(np.uint16)
+    if x.dtype == np.uint16:
+        return x
+    raise TypeError(f"expected float16 or uint16 bit patterns, got {x.dtype}")
+
+
+def gemm_ex(A, B, b_layout, ab_type="f16", alpha=1.0, bias=None, act="none", I=None, J=None):
+    """fp64 reference of act(alpha * sum_k A[i,k] B[k,j] + bias[j]) and its
+    tolerance magnitude |alpha| * sum_k |A[i,k] B[k,j]| + |bias[j]|.
+
+    A, B: uint16 bit patterns of ``ab_type`` (float16 arrays accepted for
+    binary16). bias: None or N float32 values. I, J: None for the full M x N
+    output (returned as 2-D arrays), else the selected elements (1-D)."""
+    A = _u16(A)
+    B = _u16(B)
+    lay = _LAYOUTS[b_layout]
+    M, K, lda = _rows(A)
+    if lay == 0:
+        Kb, N, ldb = _rows(B)
+    else:
+        N, Kb, ldb = _rows(B)
+    if Kb != K:
+        raise ValueError(f"inner dimensions differ: A has K={K}, B has K={Kb}")
+    bptr = None
+    if bias is not None:
+        bias = np.ascontiguousarray(bias, dtype=np.float32)
+        if bias.shape != (N,):
+            raise ValueError(f"bias must hold N={N} values")
+        bptr = _ptr(bias)
+    if I is None:
+        ref = np.empty((M, N), dtype=np.float64)
+        tol = np.empty((M, N), dtype=np.float64)
+        npts, ip, jp = -1, None, None
+    else:
+        I = np.ascontiguousarray(I, dtype=np.int64)
+        J = np.ascontiguousarray(J, dtype=np.int64)
+        if I.shape != J.shape:
+            raise ValueError("I and J differ in shape")
+        ref = np.empty(I.size, dtype=np.float64)
+        tol = np.empty(I.size, dtype=np.float64)
+        npts, ip, jp = I.size, _ptr(I), _ptr(J)
+    rc = _load().ref_gemm_ex(M, N, K, _ptr(A), lda, _ptr(B), ldb, lay, _TYPES[ab_type], float(alpha), bptr,
+                             _ACTS[act], npts, ip, jp, _ptr(ref), _ptr(tol))
+    if rc != 0:
+        raise ValueError("oracle rejected its arguments")
+    return ref, tol
+
+
+def check_ex(got, c_type, ref, tol_mag, rel: float = 1e-3, max_report: int = 10) -> dict:
+    """Tolerance test for outputs of type c_type ("f16", "bf16": uint16 bit
+    patterns or float16; "f32": float32 or uint32 bit patterns):
+    |g - ref| <= rel * tol_mag + ulp_type(ref) per element."""
+    t = _TYPES[c_type]
+    g = np.asarray(got)
+    if t == 2:
+        g = np.ascontiguousarray(g.view(np.uint32) if g.dtype == np.float32 else g, dtype=np.uint32).ravel()
+        g16, g32 = None, _ptr(g)
+    else:
+        g = np.ascontiguousarray(_u16(g)).ravel()
+        g16, g32 = _ptr(g), None
+    r = np.ascontiguousarray(ref, dtype=np.float64).ravel()
+    s = np.ascontiguousarray(tol_mag, dtype=np.float64).ravel()
+    if not (g.size == r.size == s.size):
+        raise ValueError("got/ref/tol_mag sizes differ")
+    worst = np.zeros(1, dtype=np.float64)
+    first = np.full(max(max_report, 1), -1, dtype=np.int64)
+    nfail = int(_load().ref_check_ex(g.size, t, g16, g32, _ptr(r), _ptr(s), float(rel), _ptr(worst), _ptr(first),
+                                     max_report))
     return {"n": int(g.size), "nfail": nfail, "worst": float(worst[0]),
             "first_fail": [int(x) for x in first[:min(nfail, max_report)]]}
