@@ -12,6 +12,12 @@ Prints ONE JSON line (rank 0):
              block of whole output rows of the same workload
 
 Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 100] [--workload NAME]
+                       [--ab f16|bf16] [--out f16|bf16|f32] [--epilogue]
+
+The defaults time the headline line (binary16 in and out, tgemm_f16). --ab,
+--out and --epilogue time the typed entry point (tgemm_gemm) on the same
+workload: bfloat16 operands drawn from the same seeded values, a bfloat16 or
+fp32 C, and the epilogue alpha = 0.5, a seeded fp32 bias, rectifier.
 """
 import argparse
 import hashlib
@@ -25,7 +31,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "fp16 GEMM TFLOPS (2MNK/s) at 8192³ on 1 MI355X; % of MFMA peak"
 PEAK_F16_TFLOPS = 2516.6      # 256 CUs x 2.4 GHz x 4096 dense fp16 flop/clk/CU
-KERNEL_SOURCES = ("dense_tiled_gemm_tgemm_amd/csrc/tgemm.hip", "dense_tiled_gemm_tgemm_amd/csrc/tgemm_plan.h")
+KERNEL_SOURCES = ("dense_tiled_gemm_tgemm_amd/csrc/tgemm_kernels.h", "dense_tiled_gemm_tgemm_amd/csrc/tgemm_inst.hip",
+                  "dense_tiled_gemm_tgemm_amd/csrc/tgemm.hip", "dense_tiled_gemm_tgemm_amd/csrc/tgemm_plan.h")
+EPI_ALPHA = 0.5
 
 
 def log(*a):
@@ -40,10 +48,17 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(workload: str):
+def variant_tag(ab: str, out: str, epilogue: bool) -> str:
+    """"" for the headline variant, else e.g. "_bf16_f32_epi"."""
+    if ab == "f16" and out == "f16" and not epilogue:
+        return ""
+    return f"_{ab}_{out}" + ("_epi" if epilogue else "")
+
+
+def traffic_from_profiles(workload: str, tag: str = ""):
     """Per-launch HBM bytes from committed rocprofv3 counter summaries, when they
     were taken on the current kernel source (else None)."""
-    path = os.path.join(ROOT, "profiles", f"tgemm_{workload}_hbm_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"tgemm_{workload}{tag}_hbm_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -53,15 +68,19 @@ def traffic_from_profiles(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(A, B, w, got, target_s: float = 12.0):
+def cpu_baseline(A, B, w, got, target_s: float = 12.0, ab="f16", out="f16", alpha=1.0, bias=None, act="none"):
     """Time the oracle on whole output rows 0..R-1 (all N columns, full K)."""
-    import numpy as np
     import oracle
+
+    plain = ab == "f16" and out == "f16" and bias is None and alpha == 1.0 and act == "none"
 
     def run(rows):
         t0 = time.perf_counter()
-        ref, ab = oracle.gemm(A[:rows], B, w.b_layout)
-        return time.perf_counter() - t0, ref, ab
+        if plain:
+            ref, tol = oracle.gemm(A[:rows], B, w.b_layout)
+        else:
+            ref, tol = oracle.gemm_ex(A[:rows], B, w.b_layout, ab, alpha, bias, act)
+        return time.perf_counter() - t0, ref, tol
 
     # two-point calibration: the fixed cost (decoding all of B) drops out
     t_a, _, _ = run(16)
@@ -69,8 +88,8 @@ def cpu_baseline(A, B, w, got, target_s: float = 12.0):
     per_row = max((t_b - t_a) / 48, 1e-6)
     fixed = max(t_a - 16 * per_row, 0.0)
     rows = int(min(w.M, max(16, (target_s - fixed) / per_row)))
-    dt, ref, ab = run(rows)
-    res = oracle.check(got[:rows], ref, ab)
+    dt, ref, tol = run(rows)
+    res = oracle.check(got[:rows], ref, tol) if plain else oracle.check_ex(got[:rows], out, ref, tol)
     flops = 2.0 * rows * w.N * w.K
     return {
         "value": flops / dt / 1e12,
@@ -92,6 +111,9 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default=None)
+    ap.add_argument("--ab", choices=("f16", "bf16"), default="f16", help="operand type")
+    ap.add_argument("--out", choices=("f16", "bf16", "f32"), default="f16", help="output type")
+    ap.add_argument("--epilogue", action="store_true", help="alpha = 0.5, seeded fp32 bias, rectifier")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mfma-ceiling", action="store_true",
                     help="instead of the GEMM, time the matrix-core ceiling probe (the GEMM's "
@@ -163,13 +185,23 @@ def main():
 
     name = args.workload or inputs.HEADLINE
     w = inputs.WORKLOADS[name]
-    log(f"bench: workload {name} M={w.M} N={w.N} K={w.K} B {w.b_layout}")
+    tag = variant_tag(args.ab, args.out, args.epilogue)
+    log(f"bench: workload {name} M={w.M} N={w.N} K={w.K} B {w.b_layout} {args.ab}->{args.out}"
+        f"{' epilogue' if args.epilogue else ''}")
     tg.load()
     dev = torch.device("cuda:0")
-    A, B = inputs.make_inputs(w)
-    Ad = torch.from_numpy(A).to(dev)
-    Bd = torch.from_numpy(B).to(dev)
-    Cd = torch.empty((w.M, w.N), dtype=torch.float16, device=dev)
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
+    A, B = inputs.make_inputs(w, args.ab)
+    A = A.view(np.uint16)
+    B = B.view(np.uint16)
+    Ad = torch.from_numpy(A.view(np.int16)).to(dev).view(tdt[args.ab])
+    Bd = torch.from_numpy(B.view(np.int16)).to(dev).view(tdt[args.ab])
+    Cd = torch.empty((w.M, w.N), dtype=tdt[args.out], device=dev)
+    alpha, bias_np, act = 1.0, None, "none"
+    if args.epilogue:
+        alpha, act = EPI_ALPHA, "relu"
+        bias_np = inputs.random_bias(w.N, w.seed + 77)
+    bias_d = torch.from_numpy(bias_np).to(dev) if bias_np is not None else None
     stream = torch.cuda.current_stream(dev)
     sptr = stream.cuda_stream
     lda, ldb, ldc = w.K, B.shape[1], w.N
@@ -194,11 +226,20 @@ def main():
                           "tflops": round(float(w.flops) / ms / 1e9, 1)}), flush=True)
         return
 
-    def step():
-        rc = tg.tgemm_f16(w.M, w.N, w.K, Ad.data_ptr(), lda, Bd.data_ptr(), ldb, w.b_layout,
-                          Cd.data_ptr(), ldc, sptr)
-        if rc != tg.TGEMM_OK:
-            raise tg.TgemmError(rc)
+    if tag == "":
+        def step():
+            rc = tg.tgemm_f16(w.M, w.N, w.K, Ad.data_ptr(), lda, Bd.data_ptr(), ldb, w.b_layout,
+                              Cd.data_ptr(), ldc, sptr)
+            if rc != tg.TGEMM_OK:
+                raise tg.TgemmError(rc)
+    else:
+        bptr = bias_d.data_ptr() if bias_d is not None else None
+
+        def step():
+            rc = tg.tgemm_gemm(w.M, w.N, w.K, args.ab, Ad.data_ptr(), lda, Bd.data_ptr(), ldb, w.b_layout,
+                               args.out, Cd.data_ptr(), ldc, alpha, bptr, act, sptr)
+            if rc != tg.TGEMM_OK:
+                raise tg.TgemmError(rc)
 
     for _ in range(args.warmup):
         step()
@@ -224,8 +265,11 @@ def main():
     log(f"bench: {args.steps} steps, region {region_ms:.3f} ms (host wall {wall * 1e3:.3f} ms), "
         f"per launch mean {mean_ms:.4f} min {min(per_launch_ms):.4f} max {max(per_launch_ms):.4f} ms")
 
+    metric = METRIC if tag == "" else (
+        f"GEMM TFLOPS (2MNK/s) at {w.M}x{w.N}x{w.K}, {args.ab} in, {args.out} out"
+        f"{', alpha/bias/relu epilogue' if args.epilogue else ''} on 1 MI355X")
     rec = {
-        "metric": METRIC,
+        "metric": metric,
         "value": round(value, 2),
         "unit": "TFLOPS",
         "n_gpus": 1,
@@ -235,23 +279,25 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": args.ab,
         "data": "synthetic",
         "config": {"workload": name, "M": w.M, "N": w.N, "K": w.K, "b_layout": w.b_layout,
-                   "seed": w.seed, "accumulate": "f32", "output": "f16"},
+                   "seed": w.seed, "accumulate": "f32", "output": args.out,
+                   "epilogue": (f"alpha={EPI_ALPHA}, bias, relu" if args.epilogue else "none")},
         "roofline": {
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": PEAK_F16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_F16_TFLOPS, 4),
-            "traffic": traffic_from_profiles(name),
+            "traffic": traffic_from_profiles(name, tag),
         },
     }
     if not args.no_cpu_baseline:
         torch.cuda.synchronize()
-        got = Cd.cpu().numpy()
-        rec["cpu_baseline"] = cpu_baseline(A, B, w, got)
+        got = Cd.cpu().numpy() if args.out == "f32" else Cd.view(torch.int16).cpu().numpy().view(np.uint16)
+        rec["cpu_baseline"] = cpu_baseline(A, B, w, got, ab=args.ab, out=args.out, alpha=alpha, bias=bias_np,
+                                           act=act)
     print(json.dumps(rec), flush=True)
 
 

@@ -18,8 +18,24 @@ TGEMM_OK = 0
 TGEMM_ERR_INVALID = -1
 TGEMM_ERR_UNSUPPORTED = -2
 TGEMM_ERR_HIP = -3
+TGEMM_F16 = 0
+TGEMM_BF16 = 1
+TGEMM_F32 = 2
+TGEMM_ACT_NONE = 0
+TGEMM_ACT_RELU = 1
 
 _LAYOUT = {"KxN": TGEMM_B_KxN, "NxK": TGEMM_B_NxK, TGEMM_B_KxN: TGEMM_B_KxN, TGEMM_B_NxK: TGEMM_B_NxK}
+_DTYPE = {"f16": TGEMM_F16, "bf16": TGEMM_BF16, "f32": TGEMM_F32,
+          TGEMM_F16: TGEMM_F16, TGEMM_BF16: TGEMM_BF16, TGEMM_F32: TGEMM_F32}
+_ACT = {"none": TGEMM_ACT_NONE, "relu": TGEMM_ACT_RELU, TGEMM_ACT_NONE: TGEMM_ACT_NONE,
+        TGEMM_ACT_RELU: TGEMM_ACT_RELU}
+
+
+
+def _code(table, v):
+    """Name -> C enum value; plain integers pass through unchanged (the C side checks them)."""
+    return int(v) if isinstance(v, int) else table[v]
+
 
 _lib = None
 _I64 = ctypes.c_int64
@@ -53,6 +69,13 @@ def load():
     lib.tgemm_f16.argtypes = gemm_args
     lib.tgemm_f16_config.restype = _INT
     lib.tgemm_f16_config.argtypes = gemm_args + [_INT, _INT, _INT, _INT, _INT]
+    ex_args = [_I64, _I64, _I64, _INT, _P, _I64, _P, _I64, _INT, _INT, _P, _I64, ctypes.c_float, _P, _INT]
+    lib.tgemm_gemm.restype = _INT
+    lib.tgemm_gemm.argtypes = ex_args + [_P]
+    lib.tgemm_gemm_config.restype = _INT
+    lib.tgemm_gemm_config.argtypes = ex_args + [_P, _INT, _INT, _INT, _INT, _INT]
+    lib.tgemm_plan_gemm.restype = _INT
+    lib.tgemm_plan_gemm.argtypes = ex_args + [_INT, _INT, _INT, _INT, _INT, ctypes.POINTER(_I64)]
     lib.tgemm_status_string.restype = ctypes.c_char_p
     lib.tgemm_status_string.argtypes = [_INT]
     lib.tgemm_last_hip_error.restype = _INT
@@ -100,6 +123,35 @@ def tgemm_plan_f16(M, N, K, A, lda, B, ldb, b_layout, C, ldc, force_generic=0, g
     keys = ("variant", "bm", "bn", "bk", "workgroups", "group_m", "num_xcd", "threads", "stages",
             "lds_bytes")
     return rc, dict(zip(keys, (int(v) for v in info)))
+
+
+def tgemm_gemm(M, N, K, ab_type, A, lda, B, ldb, b_layout, c_type, C, ldc, alpha=1.0, bias=None, act="none",
+               stream=None) -> int:
+    """Raw C call of the typed GEMM with epilogue; returns the status."""
+    return int(load().tgemm_gemm(M, N, K, _code(_DTYPE, ab_type), A, lda, B, ldb, _LAYOUT[b_layout], _code(_DTYPE, c_type), C,
+                                 ldc, float(alpha), bias, _code(_ACT, act), stream))
+
+
+def tgemm_gemm_config(M, N, K, ab_type, A, lda, B, ldb, b_layout, c_type, C, ldc, alpha=1.0, bias=None,
+                      act="none", stream=None, force_generic=0, group_m=0, num_xcd=0, k_step=0, stages=0) -> int:
+    return int(load().tgemm_gemm_config(M, N, K, _code(_DTYPE, ab_type), A, lda, B, ldb, _LAYOUT[b_layout],
+                                        _code(_DTYPE, c_type), C, ldc, float(alpha), bias, _code(_ACT, act), stream,
+                                        int(force_generic), int(group_m), int(num_xcd), int(k_step), int(stages)))
+
+
+_PLAN_KEYS = ("variant", "bm", "bn", "bk", "workgroups", "group_m", "num_xcd", "threads", "stages", "lds_bytes")
+
+
+def tgemm_plan_gemm(M, N, K, ab_type, A, lda, B, ldb, b_layout, c_type, C, ldc, alpha=1.0, bias=None,
+                    act="none", force_generic=0, group_m=0, num_xcd=0, k_step=0, stages=0):
+    """Host-only plan query of the typed GEMM: (status, info dict or None)."""
+    info = (_I64 * 10)()
+    rc = int(load().tgemm_plan_gemm(M, N, K, _code(_DTYPE, ab_type), A, lda, B, ldb, _LAYOUT[b_layout], _code(_DTYPE, c_type),
+                                    C, ldc, float(alpha), bias, _code(_ACT, act), int(force_generic), int(group_m),
+                                    int(num_xcd), int(k_step), int(stages), info))
+    if rc != TGEMM_OK:
+        return rc, None
+    return rc, dict(zip(_PLAN_KEYS, (int(v) for v in info)))
 
 
 def tgemm_tile_of(grid_m, grid_n, group_m, num_xcd, wid):
@@ -172,4 +224,60 @@ def mm(A, B, b_layout: str = "KxN", out=None, stream=None, force_generic: int = 
                           stream, force_generic, group_m, num_xcd, k_step, stages)
     if rc != TGEMM_OK:
         raise TgemmError(rc, f"M={M} N={N} K={K} layout={b_layout}")
+    return out
+
+
+def _torch_code(dtype):
+    import torch
+    codes = {torch.float16: TGEMM_F16, torch.bfloat16: TGEMM_BF16, torch.float32: TGEMM_F32}
+    if dtype not in codes:
+        raise TypeError(f"unsupported dtype {dtype}")
+    return codes[dtype]
+
+
+def gemm(A, B, b_layout: str = "KxN", out=None, out_dtype=None, alpha: float = 1.0, bias=None, act: str = "none",
+         stream=None, force_generic: int = 0, group_m: int = 0, num_xcd: int = 0, k_step: int = 0,
+         stages: int = 0):
+    """C = act(alpha * A @ B + bias) for float16 or bfloat16 device tensors
+    (fp32 accumulation and epilogue in the kernel).
+
+    A: (M, K), B: (K, N) for "KxN" or (N, K) for "NxK", both of one dtype
+    (float16 or bfloat16). out: optional (M, N) float16 / bfloat16 / float32
+    tensor with unit column stride; allocated with torch.empty as `out_dtype`
+    (default: A's dtype) when None. bias: None or an (N,) float32 device
+    tensor with unit stride. act: "none" or "relu".
+    """
+    import torch
+    for t, name in ((A, "A"), (B, "B")):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+    if A.dtype != B.dtype or A.dtype not in (torch.float16, torch.bfloat16):
+        raise TypeError(f"A and B must both be float16 or both bfloat16, got {A.dtype} and {B.dtype}")
+    lay = _LAYOUT[b_layout]
+    M, K = A.shape
+    if lay == TGEMM_B_KxN:
+        Kb, N = B.shape
+    else:
+        N, Kb = B.shape
+    if Kb != K:
+        raise ValueError(f"inner dimensions differ: A is {tuple(A.shape)}, B is {tuple(B.shape)} ({b_layout})")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype or A.dtype, device=A.device)
+    elif tuple(out.shape) != (M, N) or not out.is_cuda:
+        raise ValueError(f"out must be a ({M}, {N}) device tensor")
+    bias_ptr = None
+    if bias is not None:
+        if bias.dtype != torch.float32 or not bias.is_cuda or tuple(bias.shape) != (N,) or (N > 1 and bias.stride(0) != 1):
+            raise ValueError(f"bias must be a contiguous ({N},) float32 device tensor")
+        bias_ptr = bias.data_ptr()
+    lda, ldb, ldc = _row_major(A, "A"), _row_major(B, "B"), _row_major(out, "out")
+    if stream is None:
+        stream = torch.cuda.current_stream(A.device).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    rc = tgemm_gemm_config(M, N, K, _torch_code(A.dtype), A.data_ptr(), lda, B.data_ptr(), ldb, lay,
+                           _torch_code(out.dtype), out.data_ptr(), ldc, alpha, bias_ptr, act, stream,
+                           force_generic, group_m, num_xcd, k_step, stages)
+    if rc != TGEMM_OK:
+        raise TgemmError(rc, f"M={M} N={N} K={K} layout={b_layout} {A.dtype}->{out.dtype}")
     return out

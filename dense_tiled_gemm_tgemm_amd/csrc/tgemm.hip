@@ -1,934 +1,31 @@
-// fp16 dense tiled GEMM for MI355X (gfx950): C = A * B, binary16 in, fp32
-// accumulate, binary16 out.
-//
-// One workgroup owns one BM x BN output tile and walks K in steps (page 1,
-// "Using NVIDIA CUDA Tile to write a high-performance matrix multiply",
-// sections 1-6; page 4, CUDA programming guide 13.4.2, section 2.4.9.1).
-// Per K step the tile's A and B blocks are staged from HBM/L2 into LDS while
-// earlier steps run on the matrix cores (the load / barrier / compute /
-// overlap / write-back lifecycle of page 3, "Why GEMM", section 2.2).
-// Partial K tiles are padded with zeros and C elements outside M x N are
-// never written (page 4, section 2.4.6.1.3).
-//
-// gfx950 mapping:
-//  * 256 threads = 4 waves of 64 lanes in a 2 x 2 grid; each wave owns a
-//    128 x 128 sub-tile held as 8 x 8 blocks of 16 x 16 fp32 accumulators
-//    (256 accumulator registers per lane).
-//  * Inner product: v_mfma_f32_16x16x32_f16, one per 16 x 16 block and
-//    32-deep K slice. Each lane supplies 8 consecutive-k binary16 values of
-//    one row of each operand (row = lane mod 16, k = 8 * (lane / 16) + 0..7),
-//    read from LDS as one 128-bit word. The B fragment is passed as the
-//    instruction's first operand and the A fragment as its second, so the
-//    16 x 16 result block is C transposed: lane l holds C row (l mod 16) and
-//    its four accumulator registers hold the four consecutive C columns
-//    4 * (l / 16) + 0..3. The epilogue writes 64-bit runs of four binary16.
-//    (This shape keeps the matrix cores busier between the interleaved LDS
-//    and load instructions than the 32 x 32 x 16 one, which needs twice the
-//    cycles per instruction but issues less evenly.)
-//  * Every path multiplies the same operand values in the same 32-deep K
-//    slices in ascending order, so all of them produce the same bits.
-//  * Workgroup -> tile: die-aware renumbering, then the grouped order of
-//    page 1, section "Swizzle" (tile_of in tgemm_plan.h).
+// Host entry points of the dense tiled GEMM for MI355X (gfx950): argument
+// checks and planning (tgemm_plan.h), kernel choice among the instantiated
+// combinations of element types and epilogue, and the launch. The kernels and
+// their design are in tgemm_kernels.h.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 #include <atomic>
 
 #include "tgemm.h"
+#include "tgemm_kernels.h"
 #include "tgemm_plan.h"
 
 namespace tg {
 
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-static_assert(BM == 256 && BN == 256 && BK == 64 && NTHREADS == 256,
-              "the staging maps below assume a 256 x 256 tile, 64-deep register staging and 256 threads");
-
-struct Args {
-    const uint16_t* A;
-    const uint16_t* B;
-    uint16_t* C;
-    int64_t lda, ldb, ldc;
-    int M, N, K;
-    int grid_m, grid_n, W, group_m, num_xcd;
-    int grid;             // workgroups launched; workgroup b computes tiles b, b + grid, ...
-    int c16;              // C is 16-byte aligned and ldc a multiple of 8
-};
-
-// LDS layout of one staged K-contiguous operand block (256 rows x KS halves)
-// as 16-byte chunks, CPR = KS / 8 per row, chunk c of row r at slot
-// r * CPR + (c ^ f(r)):
-//   KS = 64: f(r) = (r & 7) ^ ((r >> 3) & 1)
-//   KS = 32: f(r) = (r ^ (r >> 2)) & 3
-// A fragment read takes 16 consecutive rows at one chunk per 16-lane group
-// (4 groups = 4 consecutive chunks); both maps keep every 8- and 16-lane
-// group of such a read on distinct 16-byte bank groups, and the chunks of
-// any row distinct, so reads and 128-bit writes are free of bank conflicts
-// (page 3, sections 3.1 and 5.3; page 5, "Why swizzle matters"). Both depend
-// on r mod 16 only, so the fragment of 16-row block i sits 16 * CPR slots
-// after that of block 0.
-template <int KS>
-struct Lds {
-    static constexpr int kCpr = KS / 8;
-    static constexpr int kBlock = 256 * kCpr;          // chunks per operand block
-    static constexpr int kStage = 2 * kBlock;          // A block then B block
-    __device__ static __forceinline__ int swz(int r) {
-        return KS == 64 ? ((r & 7) ^ ((r >> 3) & 1)) : ((r ^ (r >> 2)) & 3);
-    }
-    __device__ static __forceinline__ int slot(int r, int c) { return r * kCpr + (c ^ swz(r)); }
-};
-
-// Fragment of the 16-row block `blk` of a K-contiguous LDS block for the
-// 32-deep slice `s`: lane l gets row 16 * blk + (l mod 16) of the wave's
-// 128-row half `half`, k = 32 s + 8 (l / 16) + 0..7.
-template <int KS>
-__device__ __forceinline__ half8 read_kc(const u32x4* __restrict__ s_blk, int half, int blk, int lane, int s) {
-    return __builtin_bit_cast(half8, s_blk[Lds<KS>::slot(half * 128 + blk * 16 + (lane & 15), s * 4 + (lane >> 4))]);
-}
-
-// Eight binary16 values from p[0..nv-1]; lanes at or past nv read as zero.
-__device__ __forceinline__ u32x4 load8_elems(const uint16_t* __restrict__ p, int nv) {
-    unsigned w[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const unsigned lo = (2 * q < nv) ? (unsigned)p[2 * q] : 0u;
-        const unsigned hi = (2 * q + 1 < nv) ? (unsigned)p[2 * q + 1] : 0u;
-        w[q] = lo | (hi << 16);
-    }
-    return u32x4{w[0], w[1], w[2], w[3]};
-}
-
-__device__ __forceinline__ f32x4 mfma16(const half8& b, const half8& a, const f32x4& c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(b, a, c, 0, 0, 0);
-}
-
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 half2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ unsigned pack_half2(float a, float b) {
-    // fp32 -> binary16, round to nearest even (page 1, section 6: the fp32
-    // accumulator is converted to C's type when it is stored); one packed
-    // conversion instruction
-    return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{a, b}, half2));
-}
-
-// Lane l of wave (wm, wn) holds, in acc[i][j], C row m0 + 128 wm + 16 i + (l mod 16)
-// at columns n0 + 128 wn + 16 j + 4 (l / 16) + 0..3. For each pair of 16-column
-// blocks (j, j+1), v_permlane16_swap exchanges the converted words between
-// 16-lane rows so that a lane in row g then holds the 8 consecutive columns
-// 16 (j + (g & 1)) + 8 (g >> 1) .. +7 of its C row: one 16-byte store when C
-// is 16-byte aligned with ldc % 8 == 0 (each store instruction writes 16 rows
-// x 64 bytes), two 8-byte stores when it is 8-byte aligned with ldc % 4 == 0,
-// element stores otherwise and where the 8 columns straddle N. All lanes run
-// the exchange; only the stores are predicated. One 16-row block at a time
-// (pinned), so the temporaries stay few when this runs between two tiles
-// with the next tile's fragments already in registers.
-template <bool VEC_C>
-__device__ __forceinline__ void store_c(const f32x4 (&acc)[8][8], const Args& a, int m0, int n0, int wm,
-                                        int wn, int lane) {
-    const int r16 = lane & 15, g = lane >> 4;
-    const int col0 = n0 + wn * 128 + (g & 1) * 16 + (g >> 1) * 8;
-    uint16_t* base = a.C + (int64_t)(m0 + wm * 128 + r16) * a.ldc + col0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        __builtin_amdgcn_sched_barrier(0);
-        const bool row_ok = m0 + wm * 128 + i * 16 + r16 < a.M;
-        uint16_t* row = base + (int64_t)i * 16 * a.ldc;
-#pragma unroll
-        for (int pr = 0; pr < 4; ++pr) {
-            const f32x4& x = acc[i][2 * pr];
-            const f32x4& y = acc[i][2 * pr + 1];
-            const auto s0 = __builtin_amdgcn_permlane16_swap(pack_half2(x[0], x[1]), pack_half2(y[0], y[1]),
-                                                             false, false);
-            const auto s1 = __builtin_amdgcn_permlane16_swap(pack_half2(x[2], x[3]), pack_half2(y[2], y[3]),
-                                                             false, false);
-            const u32x4 v = u32x4{s0[0], s1[0], s0[1], s1[1]};
-            const int col = col0 + 32 * pr;
-            uint16_t* dst = row + 32 * pr;
-            if (row_ok && col + 8 <= a.N && a.c16) {
-                *(u32x4*)dst = v;
-            } else if (row_ok && col + 8 <= a.N && VEC_C) {
-                *(u32x2*)dst = u32x2{v[0], v[1]};
-                *(u32x2*)(dst + 4) = u32x2{v[2], v[3]};
-            } else if (row_ok && col < a.N) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    if (col + e < a.N) dst[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
-            }
-        }
-    }
-}
-
-__device__ __forceinline__ void zero_acc(f32x4 (&acc)[8][8]) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{};
-}
-
-// ---------------------------------------------------------------------------
-// Register-staged path (any stride, element-wise or 128-bit global loads):
-// both operands are written K-contiguous into a BK = 64 deep LDS block with
-// the KS = 64 map above, double-buffered.
-// ---------------------------------------------------------------------------
-using LdsR = Lds<BK>;
-
-// Stage one BK-wide block of a K-contiguous operand (A, or B stored N x K):
-// rows row0 .. row0+255, k = k0 .. k0+63. Thread t loads chunk (t & 7) of
-// rows (t >> 3) + 32p: eight threads cover one 128-byte row segment.
-// MASK: rows >= nrows and k >= K read as zero (page 4, section 2.4.6.1.3).
-template <bool VEC, bool MASK>
-__device__ __forceinline__ void load_kcontig(u32x4 (&r)[8], const uint16_t* __restrict__ X,
-                                             int64_t ld, int nrows, int K, int row0, int k0,
-                                             int tid) {
-    const int gk = k0 + (tid & 7) * 8;
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-        const int gr = row0 + (tid >> 3) + 32 * p;
-        if (!MASK) {
-            const uint16_t* src = X + (int64_t)gr * ld + gk;
-            r[p] = VEC ? *(const u32x4*)src : load8_elems(src, 8);
-        } else {
-            const int rem = K - gk;
-            const int nv = (gr < nrows) ? (rem < 0 ? 0 : (rem > 8 ? 8 : rem)) : 0;
-            const int grc = gr < nrows ? gr : nrows - 1;
-            const uint16_t* src = X + (int64_t)grc * ld + (nv > 0 ? gk : 0);
-            if (VEC && nv == 8)
-                r[p] = *(const u32x4*)src;
-            else
-                r[p] = load8_elems(src, nv);
-        }
-    }
-}
-
-__device__ __forceinline__ void store_kcontig(u32x4* __restrict__ s, const u32x4 (&r)[8], int tid) {
-    const int c = tid & 7;
-#pragma unroll
-    for (int p = 0; p < 8; ++p) s[LdsR::slot((tid >> 3) + 32 * p, c)] = r[p];
-}
-
-// Stage one BK-deep block of B stored K x N: k = k0 .. k0+63, n = n0 .. n0+255.
-// Thread t owns the 8 x 8 block k = k0 + 8*(t & 7) + 0..7, n = n0 + 8*(t >> 3) + 0..7
-// and loads it as eight 128-bit row pieces.
-template <bool VEC, bool MASK>
-__device__ __forceinline__ void load_kxn(u32x4 (&r)[8], const uint16_t* __restrict__ B, int64_t ldb,
-                                         int N, int K, int n0, int k0, int tid) {
-    const int gn = n0 + (tid >> 3) * 8;
-    const int gk0 = k0 + (tid & 7) * 8;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-        const int gk = gk0 + kk;
-        if (!MASK) {
-            const uint16_t* src = B + (int64_t)gk * ldb + gn;
-            r[kk] = VEC ? *(const u32x4*)src : load8_elems(src, 8);
-        } else {
-            const int rem = N - gn;
-            const int nv = (gk < K) ? (rem < 0 ? 0 : (rem > 8 ? 8 : rem)) : 0;
-            const int gkc = gk < K ? gk : K - 1;
-            const uint16_t* src = B + (int64_t)gkc * ldb + (nv > 0 ? gn : 0);
-            if (VEC && nv == 8)
-                r[kk] = *(const u32x4*)src;
-            else
-                r[kk] = load8_elems(src, nv);
-        }
-    }
-}
-
-// Transpose the 8 x 8 block in registers and write it K-contiguous: LDS row
-// n0' + nn receives k = 8*(t & 7) + 0..7 as logical chunk (t & 7). Threads
-// with odd column-block index write their rows in swapped pair order so that
-// the 16 lanes of a bank-group pass touch rows of both parities.
-__device__ __forceinline__ void store_kxn(u32x4* __restrict__ s, const u32x4 (&r)[8], int tid) {
-    const int kb = tid & 7;
-    const int nb = tid >> 3;
-    u32x4 t[8];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {       // word q of a row holds columns 2q (low) and 2q+1 (high)
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {   // word p of a column holds rows 2p (low) and 2p+1 (high)
-            const unsigned lo = r[2 * p][q], hi = r[2 * p + 1][q];
-            t[2 * q][p] = (lo & 0xffffu) | (hi << 16);
-            t[2 * q + 1][p] = (lo >> 16) | (hi & 0xffff0000u);
-        }
-    }
-    const int odd = nb & 1;
-#pragma unroll
-    for (int sidx = 0; sidx < 8; ++sidx) {
-        const u32x4 v = odd ? t[sidx ^ 1] : t[sidx];
-        s[LdsR::slot(nb * 8 + (sidx ^ odd), kb)] = v;
-    }
-}
-
-// One BK step of the wave's 128 x 128 sub-tile: 2 k32 slices x 8 x 8 MFMAs.
-__device__ __forceinline__ void mma_step(f32x4 (&acc)[8][8], const u32x4* __restrict__ sA,
-                                         const u32x4* __restrict__ sB, int wm, int wn, int lane) {
-#pragma unroll
-    for (int s = 0; s < BK / 32; ++s) {
-        half8 af[8], bf[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) af[i] = read_kc<BK>(sA, wm, i, lane, s);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) bf[j] = read_kc<BK>(sB, wn, j, lane, s);
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) acc[i][j] = mfma16(bf[j], af[i], acc[i][j]);
-    }
-}
-
-template <int NXK, bool VEC, bool MASK>
-__device__ __forceinline__ void load_stage(u32x4 (&ra)[8], u32x4 (&rb)[8], const Args& a, int m0, int n0,
-                                           int k0, int tid) {
-    load_kcontig<VEC, MASK>(ra, a.A, a.lda, a.M, a.K, m0, k0, tid);
-    if (NXK)
-        load_kcontig<VEC, MASK>(rb, a.B, a.ldb, a.N, a.K, n0, k0, tid);
-    else
-        load_kxn<VEC, MASK>(rb, a.B, a.ldb, a.N, a.K, n0, k0, tid);
-}
-
-template <int NXK>
-__device__ __forceinline__ void store_stage(u32x4* __restrict__ sA, u32x4* __restrict__ sB,
-                                            const u32x4 (&ra)[8], const u32x4 (&rb)[8], int tid) {
-    store_kcontig(sA, ra, tid);
-    if (NXK)
-        store_kcontig(sB, rb, tid);
-    else
-        store_kxn(sB, rb, tid);
-}
-
-template <int NXK, bool VEC, bool VEC_C>
-__global__ void __launch_bounds__(NTHREADS)
-__attribute__((amdgpu_waves_per_eu(1, 1)))
-tgemm_f16_kernel(Args a) {
-    __shared__ u32x4 smem[2][2][LdsR::kBlock];   // [stage][A | B], 128 KiB
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-
-    int tm, tn;
-    tile_of((int)blockIdx.x, a.W, a.grid_m, a.grid_n, a.group_m, a.num_xcd, &tm, &tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-    const bool interior = (m0 + BM <= a.M) && (n0 + BN <= a.N);
-    const int nk = (a.K + BK - 1) / BK;
-
-    f32x4 acc[8][8];
-    zero_acc(acc);
-
-    u32x4 ra[8], rb[8];
-    if (nk > 0) {
-        if (interior && BK <= a.K)
-            load_stage<NXK, VEC, false>(ra, rb, a, m0, n0, 0, tid);
-        else
-            load_stage<NXK, VEC, true>(ra, rb, a, m0, n0, 0, tid);
-        store_stage<NXK>(smem[0][0], smem[0][1], ra, rb, tid);
-        __syncthreads();
-    }
-    for (int t = 0; t < nk; ++t) {
-        const int cur = t & 1;
-        const bool more = t + 1 < nk;
-        if (more) {
-            const int k0 = (t + 1) * BK;
-            if (interior && k0 + BK <= a.K)
-                load_stage<NXK, VEC, false>(ra, rb, a, m0, n0, k0, tid);
-            else
-                load_stage<NXK, VEC, true>(ra, rb, a, m0, n0, k0, tid);
-        }
-        mma_step(acc, smem[cur][0], smem[cur][1], wm, wn, lane);
-        if (more) store_stage<NXK>(smem[cur ^ 1][0], smem[cur ^ 1][1], ra, rb, tid);
-        __syncthreads();
-    }
-    store_c<VEC_C>(acc, a, m0, n0, wm, wn, lane);
-}
-
-// ---------------------------------------------------------------------------
-// Direct HBM/L2 -> LDS staging (any 2-byte alignment; row strides below the
-// limits the host checks).
-//
-// buffer_load_dwordx4 ... lds writes lane L of a wave instruction to LDS
-// bytes [base + 16L, base + 16L + 16): the destination slot is fixed by the
-// lane, so the XOR swizzle is applied on the source side instead.
-//
-// Zero padding (page 4, section 2.4.6.1.3): a lane whose byte offset (vector
-// + scalar part) reaches the buffer resource's record count reads zeros, and
-// the zeros are what it writes into its LDS slot. A tile's resource ends at
-// its operand's last element, so rows past the operand (and, for B stored
-// K x N, rows past K) read zeros; steps past the last tile use a scalar
-// offset of kOob and touch no memory at all. The one remaining case, chunks
-// at or past K on the last, partial K step, is rewritten in LDS before that
-// step is published. Each lane's load offsets are computed once and do not
-// depend on the tile: with one wave per SIMD, a vector ALU write into a
-// register a matrix instruction has just read stalls the matrix cores, so
-// the main loop carries no per-load arithmetic.
-// ---------------------------------------------------------------------------
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(3))) const char lds_cchar;
-
-constexpr unsigned kOob = 0x80000000u;       // record counts stay below this
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-    // s_waitcnt fields: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt_hi[15:14]
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-__device__ __forceinline__ void wait_lgkmcnt0() {
-    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
-}
-
-// Compiler-level fence: no memory access is moved across it. The hardware
-// ordering comes from the explicit s_waitcnt and s_barrier around it.
-#define TG_COMPILER_FENCE() __asm__ __volatile__("" ::: "memory")
-
-__device__ __forceinline__ void block_barrier() {
-    TG_COMPILER_FENCE();
-    __builtin_amdgcn_s_barrier();
-    TG_COMPILER_FENCE();
-}
-
-// Base pointer and record count of the buffer resource over operand rows
-// row0 .. nrows-1 (row stride ld): the byte span from the first of these rows
-// to the operand's last element. Every offset a tile forms inside its 256
-// rows stays below 2^31 (host stride limit); the span is capped below kOob,
-// which only shortens it for tiles far from the operand's end.
-struct Rsrc {
-    const uint16_t* base;
-    int nrec;
-};
-
-__device__ __forceinline__ Rsrc operand_rsrc(const uint16_t* X, int64_t ld, int nrows, int ncols, int row0) {
-    int64_t span = ((int64_t)(nrows - row0 - 1) * ld + ncols) * 2;
-    if (span > (int64_t)kOob - 1) span = (int64_t)kOob - 1;
-    return Rsrc{X + (int64_t)row0 * ld, (int)span};
-}
-
-// B stored K x N is kept N-contiguous in LDS, [k][n] (512 bytes per k row):
-// 16-byte chunk c (n = 8c .. 8c+7) of k row k sits at physical chunk
-// c ^ h(k), h(k) = 2 (k & 3) ^ 8 ((k >> 3) & 1) ^ 16 ((k >> 4) & 1). A
-// transposing fragment read has each 16-lane group read 4 consecutive k rows
-// x 32 contiguous bytes, the four groups 8 rows apart; h spreads every 16-
-// and 32-lane part of such a read over distinct banks. h ignores k bits 2
-// and 5, so the second half of a fragment (k + 4) and the next 32-deep slice
-// (k + 32) sit at fixed byte distances from the first.
-struct KnLds {
-    __device__ static __forceinline__ int h(int k) { return (2 * (k & 3)) ^ (8 * ((k >> 3) & 1)) ^ (16 * ((k >> 4) & 1)); }
-    __device__ static __forceinline__ int phys(int c, int k) { return c ^ h(k); }
-    __device__ static __forceinline__ int logical(int p, int k) { return p ^ h(k); }
-};
-
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-// Four k values (4 consecutive k rows) of one n column of B stored [k][n],
-// by the transposing read ds_read_b64_tr_b16: in each 16-lane group, lane i
-// points at k row k0 + i/4, columns n0 + 4(i % 4) .. +3, and lane j receives
-// column n0 + j.
-__device__ __forceinline__ s16x4 read_tr(lds_cchar* __restrict__ p) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
-#else
-    (void)p;
-    return s16x4{};
-#endif
-}
-
-__device__ __forceinline__ half8 join_halves(const s16x4& lo, const s16x4& hi) {
-    return __builtin_bit_cast(half8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
-// This lane's LDS read positions in stage 0 (stage st's A and B blocks sit
-// st * CPR * 256 slots after stage 0's, within 64 KiB, so a read is one base
-// register plus an immediate offset):
-//  a[s], b[s]: the A and (K-contiguous) B fragments of 16-row block 0 for
-//              slice s; block i lies 16 * CPR slots further.
-//  tr[blk]:    for B stored [k][n], the transposing read of 16-column block
-//              blk, slice 0, k rows +0..3 of the lane's 8 (lane l needs
-//              column 128 wn + 16 blk + (l mod 16), k = 8 (l / 16) + 0..7);
-//              k + 4 adds 2 KiB and slice s adds 16 KiB * s.
-template <int KS, int NXK>
-struct FragPtrs {
-    const u32x4* a[KS / 32];
-    const u32x4* b[KS / 32];
-    lds_cchar* tr[8];
-};
-
-template <int KS, int NXK>
-__device__ __forceinline__ FragPtrs<KS, NXK> frag_ptrs(const u32x4* a_blk, const u32x4* b_blk, int wm, int wn,
-                                                        int lane) {
-    using L = Lds<KS>;
-    FragPtrs<KS, NXK> f;
-    const int r16 = lane & 15, g = lane >> 4;
-#pragma unroll
-    for (int s = 0; s < KS / 32; ++s) {
-        f.a[s] = a_blk + L::slot(wm * 128 + r16, s * 4 + g);
-        f.b[s] = b_blk + L::slot(wn * 128 + r16, s * 4 + g);
-    }
-    const int krow = 8 * g + (r16 >> 2);
-#pragma unroll
-    for (int blk = 0; blk < 8; ++blk) {
-        const int ncol = wn * 128 + blk * 16 + 4 * (r16 & 3);
-        const int byte = krow * 512 + KnLds::phys(ncol >> 3, krow) * 16 + (ncol & 7) * 2;
-        f.tr[blk] = NXK ? nullptr : (lds_cchar*)b_blk + byte;
-    }
-    return f;
-}
-
-// The read positions `so` slots further (those of another stage).
-template <int KS, int NXK>
-__device__ __forceinline__ FragPtrs<KS, NXK> shifted(const FragPtrs<KS, NXK>& f, int so) {
-    FragPtrs<KS, NXK> g;
-#pragma unroll
-    for (int s = 0; s < KS / 32; ++s) {
-        g.a[s] = f.a[s] + so;
-        g.b[s] = f.b[s] + so;
-    }
-#pragma unroll
-    for (int blk = 0; blk < 8; ++blk) g.tr[blk] = NXK ? nullptr : f.tr[blk] + so * 16;
-    return g;
-}
-
-// Fragment reads; `so` is the stage's offset in slots from stage 0.
-template <int KS, int NXK>
-__device__ __forceinline__ half8 frag_a(const FragPtrs<KS, NXK>& f, int so, int s, int i) {
-    return __builtin_bit_cast(half8, f.a[s][so + i * 16 * (KS / 8)]);
-}
-
-template <int KS, int NXK>
-__device__ __forceinline__ half8 frag_b_kc(const FragPtrs<KS, NXK>& f, int so, int s, int j) {
-    return __builtin_bit_cast(half8, f.b[s][so + j * 16 * (KS / 8)]);
-}
-
-template <int KS, int NXK>
-__device__ __forceinline__ s16x4 frag_b_tr(const FragPtrs<KS, NXK>& f, int so, int s, int blk, int hh) {
-    return read_tr(f.tr[blk] + so * 16 + s * 16384 + hh * 2048);
-}
-
-// Per-lane source offsets of the 2 * CPR load instructions of a K step (A's
-// CPR, then B's). A wave instruction j fills LDS slots (4j + w) * 64 + L.
-//  * K-contiguous operand (A; B stored N x K): slot -> row (256 / CPR) * j +
-//    tid / CPR, physical chunk tid % CPR, which must hold logical chunk
-//    (tid % CPR) ^ f(row); f(row) does not depend on j. The K step advances
-//    the scalar offset by KS * 2 bytes.
-//  * B stored K x N ([k][n], 32 chunks per k row): slot -> k row 8j +
-//    (tid >> 5), physical chunk tid & 31, holding logical chunk
-//    (tid & 31) ^ h(k row). The K step advances the scalar offset by
-//    KS * ldb * 2 bytes.
-// voff[idx] is the row's byte offset plus the chunk's, relative to the
-// tile's resource base; it is the same for every tile.
-template <int KS>
-struct LaneLoads {
-    static constexpr int kCpr = KS / 8;
-    unsigned voff[2 * kCpr];
-    unsigned kchunk;      // k offset (elements) of this lane's K-contiguous chunk inside a K step
-};
-
-template <int KS, int NXK>
-__device__ __forceinline__ LaneLoads<KS> lane_loads(const Args& a, int tid) {
-    constexpr int kCpr = KS / 8;
-    LaneLoads<KS> p;
-    const int r = tid / kCpr;
-    const unsigned chunk = (unsigned)((tid % kCpr) ^ Lds<KS>::swz(r));
-#pragma unroll
-    for (int j = 0; j < kCpr; ++j) {
-        const int row = r + (256 / kCpr) * j;
-        p.voff[j] = (unsigned)row * (unsigned)a.lda * 2u + chunk * 16u;
-        if (NXK) {
-            p.voff[kCpr + j] = (unsigned)row * (unsigned)a.ldb * 2u + chunk * 16u;
-        } else {
-            const int krow = 8 * j + (tid >> 5);
-            const unsigned c = (unsigned)KnLds::logical(tid & 31, krow);
-            p.voff[kCpr + j] = (unsigned)krow * (unsigned)a.ldb * 2u + c * 16u;
-        }
-    }
-    p.kchunk = chunk * 8u;
-    return p;
-}
-
-// Load instruction `idx` (0 .. 2*CPR-1) of a K step into the stage whose A
-// and B blocks are a_blk and b_blk, with the step's scalar offsets (soa for
-// A, sob for B).
-template <int KS, int NXK>
-__device__ __forceinline__ void issue_load(const Rsrc& ra, const Rsrc& rb, const LaneLoads<KS>& p, int idx,
-                                           unsigned soa, unsigned sob, u32x4* __restrict__ a_blk,
-                                           u32x4* __restrict__ b_blk, int wave) {
-#if defined(__HIP_DEVICE_COMPILE__)   // the host pass cannot instantiate these target builtins
-    constexpr int kCpr = KS / 8;
-    const bool isb = idx >= kCpr;
-    const int j = isb ? idx - kCpr : idx;
-    const Rsrc& rs = isb ? rb : ra;
-    // word 3 = 0x00020000: raw (untyped) access, 32-bit data format
-    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)rs.base, 0, rs.nrec, 0x00020000);
-    u32x4* dst = (isb ? b_blk : a_blk) + (j * 4 + wave) * 64;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)dst, 16, p.voff[idx], isb ? sob : soa, 0, 0);
-#endif
-}
-
-// Last K step when it is partial (k0 = its first k). Its K-contiguous chunks
-// at or past K were loaded as whatever lies there (the next row, or zeros past
-// the operand's end), so each lane rewrites those of its own slots: the
-// valid part of a chunk straddling K from element loads, zeros after it, and
-// whole zeros past K. B stored K x N straddles only at column N, and only
-// its final row K - 1 loses data (the range check zeroes the whole 16-byte
-// access; other rows read the next row past N, which lands in output
-// columns that are never stored). This runs after the lane's loads of the
-// stage have landed and before the barrier that publishes it.
-template <int KS, int NXK>
-__device__ __forceinline__ void fix_last_step(u32x4* __restrict__ a_blk, u32x4* __restrict__ b_blk,
-                                              const LaneLoads<KS>& p, const Args& a, int m0, int n0, int k0,
-                                              int tid, int wave, int lane) {
-    constexpr int kCpr = KS / 8;
-    const int r = tid / kCpr;
-    const int kc = k0 + (int)p.kchunk;
-    const int nv = a.K - kc;                          // valid elements of this lane's K chunks (may be <= 0)
-    // one chunk at a time (not unrolled): this runs once per tile, inside a
-    // loop whose fragments hold most of the registers
-    if (nv < 8) {
-#pragma unroll 1
-        for (int j = 0; j < kCpr; ++j) {
-            const int row = r + (256 / kCpr) * j;
-            const int slot = (j * 4 + wave) * 64 + lane;
-            if (m0 + row < a.M) a_blk[slot] = load8_elems(a.A + (int64_t)(m0 + row) * a.lda + kc, nv);
-            if (NXK && n0 + row < a.N) b_blk[slot] = load8_elems(a.B + (int64_t)(n0 + row) * a.ldb + kc, nv);
-        }
-    }
-    if (!NXK) {
-#pragma unroll 1
-        for (int j = 0; j < kCpr; ++j) {
-            const int krow = 8 * j + (tid >> 5);
-            const int c = KnLds::logical(tid & 31, krow);
-            const int nc = n0 + 8 * c;
-            const int nvn = a.N - nc;
-            if (k0 + krow == a.K - 1 && nvn > 0 && nvn < 8)
-                b_blk[(j * 4 + wave) * 64 + lane] = load8_elems(a.B + (int64_t)(a.K - 1) * a.ldb + nc, nvn);
-        }
-    }
-    TG_COMPILER_FENCE();
-    wait_lgkmcnt0();
-    __builtin_amdgcn_s_waitcnt(0);                    // element loads returned and written
-    TG_COMPILER_FENCE();
-}
-
-// All fragments of slice `s` of stage 0 (used once, before the main loop).
-template <int KS, int NXK>
-__device__ __forceinline__ void read_frags(half8 (&fa)[8], half8 (&fb)[8], const FragPtrs<KS, NXK>& f, int s) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) fa[i] = frag_a(f, 0, s, i);
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-        fb[j] = NXK ? frag_b_kc(f, 0, s, j) : join_halves(frag_b_tr(f, 0, s, j, 0), frag_b_tr(f, 0, s, j, 1));
-}
-
-// One k32 slice: 64 MFMAs (8 x 8 blocks, serpentine by row) on the current
-// fragments, with the next slice's fragment reads (slice next_s of the
-// stage `so` slots from stage 0) and, when LOADS, the 2 * CPR load
-// instructions of one K step placed between them: reads after every
-// even-numbered MFMA, in the order the next slice consumes them (A0, B0..B7,
-// A1..A7; a [k][n] B fragment is two transposing reads), loads spread evenly
-// over the odd-numbered ones. One instruction per MFMA keeps the matrix core
-// fed; with one wave per SIMD every other instruction competes with MFMA
-// issue, so the order is pinned at both the IR and the machine level.
-template <int KS, int NXK, bool LOADS, bool ZC = false, bool READS = true>
-__device__ __forceinline__ void slice(f32x4 (&acc)[8][8], const half8 (&fa)[8], const half8 (&fb)[8],
-                                      half8 (&na)[8], half8 (&nb)[8], const FragPtrs<KS, NXK>& f, int so,
-                                      int next_s, const Rsrc& ra, const Rsrc& rb, const LaneLoads<KS>& p,
-                                      unsigned soa, unsigned sob, u32x4* __restrict__ ld_a, u32x4* __restrict__ ld_b,
-                                      int wave) {
-    constexpr int kLps = KS / 4;
-    constexpr int kNb = NXK ? 8 : 16;              // B read instructions
-    constexpr int kReads = 8 + kNb;
-    constexpr int kGap = 64 / kLps;                // MFMAs per load
-    static_assert(2 * kReads <= 64, "reads must fit the even MFMA slots");
-    s16x4 lo[8];
-#pragma unroll
-    for (int q = 0; q < 64; ++q) {
-        // serpentine over the 8 x 8 blocks: a row change keeps the B fragment,
-        // so one operand changes per MFMA throughout (less switching power)
-        const int i = q >> 3, j = (i & 1) ? 7 - (q & 7) : (q & 7);
-        // ZC: a tile's first slice starts the sums from zero (inline constant C)
-        acc[i][j] = mfma16(fb[j], fa[i], ZC ? f32x4{} : acc[i][j]);
-        if (READS && (q & 1) == 0 && q / 2 < kReads) {
-            const int rq = q / 2;
-            if (rq >= 1 && rq <= kNb) {
-                if (NXK) {
-                    nb[rq - 1] = frag_b_kc(f, so, next_s, rq - 1);
-                } else {
-                    const int blk = (rq - 1) >> 1, hh = (rq - 1) & 1;
-                    const s16x4 v = frag_b_tr(f, so, next_s, blk, hh);
-                    if (hh == 0)
-                        lo[blk] = v;
-                    else
-                        nb[blk] = join_halves(lo[blk], v);
-                }
-            } else {
-                const int ai = rq == 0 ? 0 : rq - kNb;
-                na[ai] = frag_a(f, so, next_s, ai);
-            }
-        } else if (LOADS && q % kGap == kGap - 1) {
-            issue_load<KS, NXK>(ra, rb, p, q / kGap, soa, sob, ld_a, ld_b, wave);
-        }
-        TG_COMPILER_FENCE();
-        __builtin_amdgcn_sched_barrier(0);
-    }
-}
-
-// One output tile: its origin and its operands' buffer resources.
-struct Tile {
-    Rsrc ra, rb;
-    int m0, n0;
-};
-
-template <int NXK>
-__device__ __forceinline__ Tile make_tile(const Args& a, int wid) {
-    int tm, tn;
-    tile_of(wid, a.W, a.grid_m, a.grid_n, a.group_m, a.num_xcd, &tm, &tn);
-    Tile t;
-    t.m0 = tm * BM;
-    t.n0 = tn * BN;
-    t.ra = operand_rsrc(a.A, a.lda, a.M, a.K, t.m0);
-    // B: N x K rows n0.. ; K x N columns n0.. of all K rows
-    t.rb = NXK ? operand_rsrc(a.B, a.ldb, a.N, a.K, t.n0) : operand_rsrc(a.B + t.n0, a.ldb, a.K, a.N - t.n0, 0);
-    return t;
-}
-
-// Per-workgroup constants of the direct-to-LDS kernel. LDS holds the S
-// stages' A blocks, then their B blocks.
-template <int KS, int NXK, int S>
-struct DmaCtx {
-    LaneLoads<KS> p;
-    unsigned bstep;       // scalar-offset advance of B per K step
-    int nk, klast;        // K steps per tile; first k of a tile's last step
-    bool fixup;           // a tile's last step needs fix_last_step
-    int tid, wave, lane;
-    u32x4* smem;
-    FragPtrs<KS, NXK> fp; // read positions in stage 0
-    __device__ __forceinline__ u32x4* a_blk(int st) const { return smem + st * Lds<KS>::kBlock; }
-    __device__ __forceinline__ u32x4* b_blk(int st) const { return smem + (S + st) * Lds<KS>::kBlock; }
-};
-
-// K step t of tile tc, in stage st (FIRST: the tile's first step, whose
-// first slice starts the sums from zero; LAST: its last step, which leaves
-// the next step's first fragments unread so that they are not held in
-// registers while the tile's C is stored). The steps a workgroup walks form one
-// stream over its tiles: the loads issued here are for the step S further on,
-// which is step t + S of tc or, near the end of tc, a first step of the
-// workgroup's next tile tn (none when !has_next: those loads read nothing
-// and write zeros). Its first slice's fragments are in buffer F0 of fa/fb;
-// the next step's first fragments end up in buffer F0 ^ (KS / 32 odd).
-// ST >= 0: st == ST, known at compile time (2-stage ring), so every fragment
-// read is a fixed offset from the stage-0 positions. ST < 0: `cur` holds the
-// read positions of stage st on entry and those of the next stage on return;
-// they are derived once per step, before the barrier wait, into registers no
-// matrix instruction reads (a vector ALU write into a just-read MFMA operand
-// register stalls the matrix cores).
-template <int NXK, int KS, int S, int F0, int ST, bool FIRST = false, bool LAST = false>
-__device__ __forceinline__ void dma_step(f32x4 (&acc)[8][8], half8 (&fa)[2][8], half8 (&fb)[2][8], int st, int t,
-                                         const Args& a, const DmaCtx<KS, NXK, S>& c, FragPtrs<KS, NXK>& cur,
-                                         const Tile& tc, const Tile& tn, bool has_next) {
-    using L = Lds<KS>;
-    constexpr int kSlices = KS / 32;
-    constexpr int kLps = KS / 4;
-    constexpr int FL = (F0 + kSlices - 1) & 1;       // buffer of the last slice
-    static_assert(ST < 0 || S == 2, "compile-time stages need the 2-stage ring");
-    if (ST >= 0) st = ST;
-    const int nst = (st + 1 == S) ? 0 : st + 1;
-    const FragPtrs<KS, NXK>& fc = ST >= 0 ? c.fp : cur;
-    const int so_c = ST >= 0 ? ST * L::kBlock : 0;
-    static_assert(!FIRST || kSlices > 1, "the zero-start slice is the first of a 2-slice step");
-#pragma unroll
-    for (int s = 0; s + 1 < kSlices; ++s) {
-        if (FIRST && s == 0)
-            slice<KS, NXK, false, true>(acc, fa[F0 & 1], fb[F0 & 1], fa[(F0 + 1) & 1], fb[(F0 + 1) & 1], fc, so_c,
-                                        1, tc.ra, tc.rb, c.p, 0u, 0u, c.smem, c.smem, c.wave);
-        else
-            slice<KS, NXK, false>(acc, fa[(F0 + s) & 1], fb[(F0 + s) & 1], fa[(F0 + s + 1) & 1],
-                                  fb[(F0 + s + 1) & 1], fc, so_c, s + 1, tc.ra, tc.rb, c.p, 0u, 0u, c.smem, c.smem,
-                                  c.wave);
-    }
-    if (ST < 0) cur = shifted(c.fp, nst * L::kBlock);
-    // the step these loads are for (uniform: scalar selects)
-    const int tl = t + S;
-    const bool in_next = tl >= c.nk;
-    const int ls = in_next ? tl - c.nk : tl;
-    const bool live = !in_next || has_next;
-    const unsigned soa = live ? (unsigned)ls * (unsigned)(KS * 2) : kOob;
-    const unsigned sob = live ? (unsigned)ls * c.bstep : kOob;
-    const Rsrc lra = in_next ? tn.ra : tc.ra;
-    const Rsrc lrb = in_next ? tn.rb : tc.rb;
-    TG_COMPILER_FENCE();
-    __builtin_amdgcn_sched_barrier(0);
-    wait_lgkmcnt0();                                  // this wave's reads of stage st returned
-    wait_vmcnt<(S - 2) * kLps>();                     // step t + 1 landed
-    if (c.fixup && t + 2 == c.nk)
-        fix_last_step<KS, NXK>(c.a_blk(nst), c.b_blk(nst), c.p, a, tc.m0, tc.n0, c.klast, c.tid, c.wave, c.lane);
-    block_barrier();
-    // the loads go into the stage just released
-    slice<KS, NXK, true, false, !LAST>(acc, fa[FL], fb[FL], fa[FL ^ 1], fb[FL ^ 1], ST >= 0 ? c.fp : cur,
-                                       ST >= 0 ? ((ST + 1) & 1) * L::kBlock : 0, 0, lra, lrb, c.p, soa, sob,
-                                       c.a_blk(st), c.b_blk(st), c.wave);
-}
-
-// Steps t0 .. nk-1 (an even count) of tile tc in pairs, step t0 in stage st0
-// with parity P: one-slice steps alternate fragment buffers, and a 2-stage
-// ring alternates stages, so the pair's two steps are two fixed variants.
-template <int NXK, int KS, int S, int P>
-__device__ __forceinline__ void step_pairs(f32x4 (&acc)[8][8], half8 (&fa)[2][8], half8 (&fb)[2][8], int t0,
-                                           int st0, const Args& a, const DmaCtx<KS, NXK, S>& c,
-                                           FragPtrs<KS, NXK>& cur, const Tile& tc, const Tile& tn, bool has_next) {
-    constexpr int F1 = KS == 32 ? P : 0, F2 = KS == 32 ? (P ^ 1) : 0;
-    constexpr int S1 = S == 2 ? P : -1, S2 = S == 2 ? (P ^ 1) : -1;
-    int st = st0;
-    for (int t = t0; t < c.nk; t += 2) {
-        dma_step<NXK, KS, S, F1, S1>(acc, fa, fb, st, t, a, c, cur, tc, tn, has_next);
-        st = (st + 1 == S) ? 0 : st + 1;
-        dma_step<NXK, KS, S, F2, S2>(acc, fa, fb, st, t + 1, a, c, cur, tc, tn, has_next);
-        st = (st + 1 == S) ? 0 : st + 1;
-    }
-}
-
-// Tile kernel with both operands streamed straight into an S-stage LDS ring
-// of KS-deep K steps (KS / 32 slices each): A K-contiguous, B either
-// K-contiguous (stored N x K, NXK = 1) or kept [k][n] and transposed on read
-// (stored K x N). Workgroup b computes tiles b, b + grid, ... (grid = the
-// workgroups launched: one per compute unit for 64-deep steps, else one per
-// tile). Its K steps form one stream across those tiles; step g lives in
-// stage g mod S. The barrier of a step sits before its last slice: it
-// follows every wave's last fragment read of the step's stage (so the loads
-// for the step S further on go into that stage during the last slice) and
-// every wave's loads of the next step (whose first fragments that slice
-// reads). A step's loads thus have S - 1 steps less one slice to land, and
-// the next tile's first steps load while the current tile finishes, so a
-// tile's C stores drain while the next tile computes. Every step issues the
-// same number of loads (steps past the last tile read nothing and write
-// zeros into stages that are never read), so all wait counts are constants.
-template <int NXK, bool VEC_C, int KS, int S>
-__global__ void __launch_bounds__(NTHREADS)
-__attribute__((amdgpu_waves_per_eu(1, 1)))
-tgemm_f16_dma_kernel(Args a) {
-    using L = Lds<KS>;
-    static_assert(KS == 64 || KS == 32, "K step");
-    static_assert(KS == 32 || S == 2, "64-deep steps use a 2-stage ring");
-    static_assert(S >= 2 && S <= 5 && 2 * S * L::kBlock * 16 <= 160 * 1024, "LDS ring must fit 160 KiB");
-    constexpr int kLps = KS / 4;                      // load instructions per step per wave
-    __shared__ u32x4 smem[2 * S * L::kBlock];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
-    const int nk = (a.K + KS - 1) / KS;
-
-    int wid = (int)blockIdx.x;
-    Tile tc = make_tile<NXK>(a, wid);
-    bool has_next = wid + a.grid < a.W;              // K == 0: one tile per workgroup
-    Tile tn = has_next ? make_tile<NXK>(a, wid + a.grid) : tc;
-    f32x4 acc[8][8];
-    if (KS == 32) zero_acc(acc);
-
-    DmaCtx<KS, NXK, S> c;
-    c.p = lane_loads<KS, NXK>(a, tid);
-    c.bstep = NXK ? (unsigned)(KS * 2) : (unsigned)KS * (unsigned)a.ldb * 2u;
-    c.nk = nk;
-    c.klast = (nk - 1) * KS;
-    c.fixup = (a.K % KS) != 0 || (!NXK && (a.N % 8) != 0);
-    c.tid = tid;
-    c.wave = wave;
-    c.lane = lane;
-    c.smem = smem;
-    c.fp = frag_ptrs<KS, NXK>(c.a_blk(0), c.b_blk(0), wm, wn, lane);
-    half8 fa[2][8], fb[2][8];
-    if (nk > 0) {
-        // prologue: steps 0 .. S-1 of the first tile (a workgroup with more
-        // than one tile has nk >= S)
-        for (int t = 0; t < S; ++t)
-            for (int idx = 0; idx < kLps; ++idx)
-                issue_load<KS, NXK>(tc.ra, tc.rb, c.p, idx, t < nk ? (unsigned)t * (unsigned)(KS * 2) : kOob,
-                                    t < nk ? (unsigned)t * c.bstep : kOob, c.a_blk(t), c.b_blk(t), wave);
-        wait_vmcnt<(S - 1) * kLps>();                 // step 0 landed
-        if (c.fixup && nk == 1)
-            fix_last_step<KS, NXK>(c.a_blk(0), c.b_blk(0), c.p, a, tc.m0, tc.n0, c.klast, tid, wave, lane);
-        block_barrier();
-        read_frags<KS, NXK>(fa[0], fb[0], c.fp, 0);
-    }
-    FragPtrs<KS, NXK> cur = c.fp;                     // read positions of the current stage
-    if constexpr (KS == 64) {
-        // tile after tile (two slices per step: every step starts on
-        // fragment buffer 0). A tile's first slice starts its sums from zero
-        // and its C is stored after the last step, so the accumulators carry
-        // nothing from one tile to the next; only the next tile's first
-        // fragments and the load stream do.
-        // (64-deep steps are used with nk >= 2)
-        int st = 0;
-        for (;;) {
-            dma_step<NXK, KS, S, 0, -1, true>(acc, fa, fb, st, 0, a, c, cur, tc, tn, has_next);
-            st ^= 1;
-            for (int t = 1; t + 1 < nk; ++t) {
-                dma_step<NXK, KS, S, 0, -1>(acc, fa, fb, st, t, a, c, cur, tc, tn, has_next);
-                st ^= 1;
-            }
-            dma_step<NXK, KS, S, 0, -1, false, true>(acc, fa, fb, st, nk - 1, a, c, cur, tc, tn, has_next);
-            st ^= 1;
-            store_c<VEC_C>(acc, a, tc.m0, tc.n0, wm, wn, lane);
-            if (!has_next) break;
-            read_frags<KS, NXK>(fa[0], fb[0], cur, 0);   // the next tile's first fragments
-            wid += a.grid;
-            tc = tn;
-            has_next = wid + a.grid < a.W;
-            if (has_next) tn = make_tile<NXK>(a, wid + a.grid);
-        }
-    } else {
-        // one tile per workgroup; an odd step count starts with one step,
-        // the rest go in pairs
-        if (nk & 1) {
-            dma_step<NXK, KS, S, 0, S == 2 ? 0 : -1>(acc, fa, fb, 0, 0, a, c, cur, tc, tn, has_next);
-            step_pairs<NXK, KS, S, 1>(acc, fa, fb, 1, 1 % S, a, c, cur, tc, tn, has_next);
-        } else {
-            step_pairs<NXK, KS, S, 0>(acc, fa, fb, 0, 0, a, c, cur, tc, tn, has_next);
-        }
-        store_c<VEC_C>(acc, a, tc.m0, tc.n0, wm, wn, lane);
-    }
-    // no load may still be writing this workgroup's LDS when it exits
-    wait_vmcnt<0>();
-}
-
-template <int NXK, bool VEC, bool VEC_C>
-static const void* kernel_ptr() {
-    return reinterpret_cast<const void*>(&tgemm_f16_kernel<NXK, VEC, VEC_C>);
-}
-
-template <int NXK, bool VEC_C>
-static const void* dma_kernel_ptr(int k_step, int stages) {
-    if (k_step == 64) return reinterpret_cast<const void*>(&tgemm_f16_dma_kernel<NXK, VEC_C, 64, 2>);
-    switch (stages) {
-        case 2: return reinterpret_cast<const void*>(&tgemm_f16_dma_kernel<NXK, VEC_C, 32, 2>);
-        case 3: return reinterpret_cast<const void*>(&tgemm_f16_dma_kernel<NXK, VEC_C, 32, 3>);
-        case 4: return reinterpret_cast<const void*>(&tgemm_f16_dma_kernel<NXK, VEC_C, 32, 4>);
-        default: return reinterpret_cast<const void*>(&tgemm_f16_dma_kernel<NXK, VEC_C, 32, 5>);
-    }
-}
-
 static const void* pick_kernel(const Plan& pl) {
-    const int variant = pl.variant;
-    if (variant & kDma) {
-        const bool nxk = variant & kLayoutNxK, vc = variant & kVecC;
-        if (nxk)
-            return vc ? dma_kernel_ptr<1, true>(pl.k_step, pl.stages) : dma_kernel_ptr<1, false>(pl.k_step, pl.stages);
-        return vc ? dma_kernel_ptr<0, true>(pl.k_step, pl.stages) : dma_kernel_ptr<0, false>(pl.k_step, pl.stages);
-    }
-    switch (variant & 7) {
-        case 0: return kernel_ptr<0, false, false>();
-        case 1: return kernel_ptr<0, true, false>();
-        case 2: return kernel_ptr<0, false, true>();
-        case 3: return kernel_ptr<0, true, true>();
-        case 4: return kernel_ptr<1, false, false>();
-        case 5: return kernel_ptr<1, true, false>();
-        case 6: return kernel_ptr<1, false, true>();
-        default: return kernel_ptr<1, true, true>();
-    }
+    const int ab = pl.ab_type, ct = pl.c_type;
+    const bool e = pl.epi;
+#define TG_PICK(a, c) \
+    if (ab == a && ct == c) return e ? kernel_for<a, c, true>(pl) : kernel_for<a, c, false>(pl);
+    TG_PICK(0, 0)
+    TG_PICK(0, 1)
+    TG_PICK(0, 2)
+    TG_PICK(1, 0)
+    TG_PICK(1, 1)
+    TG_PICK(1, 2)
+#undef TG_PICK
+    return nullptr;
 }
 
 static thread_local int g_last_hip_error = 0;
@@ -957,21 +54,42 @@ static int compute_units() {
     return n;
 }
 
+static bool epilogue_requested(float alpha, const float* bias, int act) {
+    return !(alpha == 1.0f) || bias != nullptr || act != TGEMM_ACT_NONE;
+}
+
+static int plan_gemm(int64_t M, int64_t N, int64_t K, int ab_type, const void* A, int64_t lda, const void* B,
+                     int64_t ldb, int b_layout, int c_type, void* C, int64_t ldc, float alpha, const float* bias,
+                     int act, int force_generic, int group_m, int num_xcd, int k_step, int stages, Plan* pl,
+                     const void** fn) {
+    if (act != TGEMM_ACT_NONE && act != TGEMM_ACT_RELU) return TGEMM_ERR_INVALID;
+    const int rc = make_plan(M, N, K, A, lda, B, ldb, b_layout, C, ldc, force_generic, group_m, num_xcd, k_step,
+                             stages, pl, ab_type, c_type, bias, epilogue_requested(alpha, bias, act));
+    if (rc != TGEMM_OK) return rc;
+    *fn = pick_kernel(*pl);
+    return *fn ? TGEMM_OK : TGEMM_ERR_UNSUPPORTED;
+}
+
 }  // namespace tg
 
-extern "C" int tgemm_f16_config(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
-                                const void* B, int64_t ldb, int b_layout, void* C, int64_t ldc,
-                                void* stream, int force_generic, int group_m, int num_xcd, int k_step,
-                                int stages) {
+extern "C" int tgemm_gemm_config(int64_t M, int64_t N, int64_t K, int ab_type, const void* A, int64_t lda,
+                                 const void* B, int64_t ldb, int b_layout, int c_type, void* C, int64_t ldc,
+                                 float alpha, const float* bias, int act, void* stream, int force_generic,
+                                 int group_m, int num_xcd, int k_step, int stages) {
     tg::Plan pl;
-    const int rc = tg::make_plan(M, N, K, A, lda, B, ldb, b_layout, C, ldc, force_generic, group_m,
-                                 num_xcd, k_step, stages, &pl);
+    const void* fn = nullptr;
+    const int rc = tg::plan_gemm(M, N, K, ab_type, A, lda, B, ldb, b_layout, c_type, C, ldc, alpha, bias, act,
+                                 force_generic, group_m, num_xcd, k_step, stages, &pl, &fn);
     if (rc != TGEMM_OK) return rc;
     if (pl.M == 0 || pl.N == 0) return TGEMM_OK;
+    const int c_size = c_type == TGEMM_F32 ? 4 : 2;
     tg::Args args;
     args.A = static_cast<const uint16_t*>(A);
     args.B = static_cast<const uint16_t*>(B);
-    args.C = static_cast<uint16_t*>(C);
+    args.C = C;
+    args.bias = bias;
+    args.alpha = alpha;
+    args.relu = act == TGEMM_ACT_RELU;
     args.lda = pl.lda;
     args.ldb = pl.ldb;
     args.ldc = pl.ldc;
@@ -984,7 +102,8 @@ extern "C" int tgemm_f16_config(int64_t M, int64_t N, int64_t K, const void* A, 
     args.group_m = pl.group_m;
     args.num_xcd = pl.num_xcd;
     args.grid = pl.W;
-    args.c16 = ((uintptr_t)C % 16 == 0) && (pl.ldc % 8 == 0);
+    args.c16 = ((uintptr_t)C % 16 == 0) && ((pl.ldc * c_size) % 16 == 0);
+    args.c8 = (pl.variant & tg::kVecC) != 0;
     if (tg::persistent(pl)) {
         // one workgroup per compute unit, each walking several tiles
         const int ncu = tg::compute_units();
@@ -994,16 +113,29 @@ extern "C" int tgemm_f16_config(int64_t M, int64_t N, int64_t K, const void* A, 
         }
         if (ncu > 0 && ncu < pl.W) args.grid = ncu;
     }
-    const void* fn = tg::pick_kernel(pl);
-    if (!fn) return TGEMM_ERR_UNSUPPORTED;
     void* kargs[] = {&args};
-    const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)args.grid),
-                                         dim3(tg::NTHREADS), kargs, 0, static_cast<hipStream_t>(stream));
+    const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)args.grid), dim3(tg::NTHREADS), kargs, 0,
+                                         static_cast<hipStream_t>(stream));
     if (e != hipSuccess) {
         tg::g_last_hip_error = (int)e;
         return TGEMM_ERR_HIP;
     }
     return TGEMM_OK;
+}
+
+extern "C" int tgemm_gemm(int64_t M, int64_t N, int64_t K, int ab_type, const void* A, int64_t lda, const void* B,
+                          int64_t ldb, int b_layout, int c_type, void* C, int64_t ldc, float alpha,
+                          const float* bias, int act, void* stream) {
+    return tgemm_gemm_config(M, N, K, ab_type, A, lda, B, ldb, b_layout, c_type, C, ldc, alpha, bias, act, stream,
+                             0, 0, 0, 0, 0);
+}
+
+extern "C" int tgemm_f16_config(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                                const void* B, int64_t ldb, int b_layout, void* C, int64_t ldc,
+                                void* stream, int force_generic, int group_m, int num_xcd, int k_step,
+                                int stages) {
+    return tgemm_gemm_config(M, N, K, TGEMM_F16, A, lda, B, ldb, b_layout, TGEMM_F16, C, ldc, 1.0f, nullptr,
+                             TGEMM_ACT_NONE, stream, force_generic, group_m, num_xcd, k_step, stages);
 }
 
 extern "C" int tgemm_f16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
@@ -1023,14 +155,7 @@ extern "C" const char* tgemm_status_string(int status) {
 
 extern "C" int tgemm_last_hip_error(void) { return tg::g_last_hip_error; }
 
-extern "C" int tgemm_plan_f16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
-                              int64_t ldb, int b_layout, void* C, int64_t ldc, int force_generic,
-                              int group_m, int num_xcd, int k_step, int stages, int64_t* info) {
-    if (!info) return TGEMM_ERR_INVALID;
-    tg::Plan pl;
-    const int rc = tg::make_plan(M, N, K, A, lda, B, ldb, b_layout, C, ldc, force_generic, group_m,
-                                 num_xcd, k_step, stages, &pl);
-    if (rc != TGEMM_OK) return rc;
+static void fill_info(const tg::Plan& pl, int64_t* info) {
     info[0] = pl.variant;
     info[1] = tg::BM;
     info[2] = tg::BN;
@@ -1041,7 +166,27 @@ extern "C" int tgemm_plan_f16(int64_t M, int64_t N, int64_t K, const void* A, in
     info[7] = tg::NTHREADS;
     info[8] = pl.stages;
     info[9] = (int64_t)pl.stages * 2 * 256 * pl.k_step * 2;   // LDS bytes per workgroup
+}
+
+extern "C" int tgemm_plan_gemm(int64_t M, int64_t N, int64_t K, int ab_type, const void* A, int64_t lda,
+                               const void* B, int64_t ldb, int b_layout, int c_type, void* C, int64_t ldc,
+                               float alpha, const float* bias, int act, int force_generic, int group_m,
+                               int num_xcd, int k_step, int stages, int64_t* info) {
+    if (!info) return TGEMM_ERR_INVALID;
+    tg::Plan pl;
+    const void* fn = nullptr;
+    const int rc = tg::plan_gemm(M, N, K, ab_type, A, lda, B, ldb, b_layout, c_type, C, ldc, alpha, bias, act,
+                                 force_generic, group_m, num_xcd, k_step, stages, &pl, &fn);
+    if (rc != TGEMM_OK) return rc;
+    fill_info(pl, info);
     return TGEMM_OK;
+}
+
+extern "C" int tgemm_plan_f16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+                              int64_t ldb, int b_layout, void* C, int64_t ldc, int force_generic,
+                              int group_m, int num_xcd, int k_step, int stages, int64_t* info) {
+    return tgemm_plan_gemm(M, N, K, TGEMM_F16, A, lda, B, ldb, b_layout, TGEMM_F16, C, ldc, 1.0f, nullptr,
+                           TGEMM_ACT_NONE, force_generic, group_m, num_xcd, k_step, stages, info);
 }
 
 extern "C" int tgemm_tile_of(int64_t grid_m, int64_t grid_n, int group_m, int num_xcd, int64_t wid,

@@ -1,6 +1,6 @@
-// Host-side planning for the fp16 tiled GEMM: argument checks, variant
-// choice, grid size, and the workgroup -> output-tile map shared with the
-// kernels. Plain C++ apart from the host/device qualifiers on tile_of().
+// Host-side planning for the tiled GEMM: argument checks, variant choice,
+// grid size, and the workgroup -> output-tile map shared with the kernels.
+// Plain C++ apart from the host/device qualifiers on tile_of().
 #pragma once
 
 #include <stdint.h>
@@ -64,14 +64,17 @@ struct Plan {
     int M, N, K;
     int64_t lda, ldb, ldc;
     int layout;        // 0 = KxN, 1 = NxK
-    int variant;       // kVecAB | kVecC | kLayoutNxK bits
+    int ab_type;       // TGEMM_F16 or TGEMM_BF16 (both operands)
+    int c_type;        // TGEMM_F16, TGEMM_BF16 or TGEMM_F32
+    bool epi;          // scale, bias or activation requested (else C = A * B as it is)
+    int variant;       // kVecAB | kVecC | kLayoutNxK | kDma bits
     int grid_m, grid_n, W;
     int group_m, num_xcd;
     int k_step, stages;   // K step per LDS stage and ring depth of the launched kernel
 };
 
-inline bool span_bytes(int64_t rows, int64_t cols, int64_t ld, uint64_t* bytes) {
-    // bytes covered by a row-major rows x cols array of 2-byte elements
+inline bool span_bytes(int64_t rows, int64_t cols, int64_t ld, uint64_t* bytes, int esize = 2) {
+    // bytes covered by a row-major rows x cols array of esize-byte elements
     if (rows <= 0 || cols <= 0) {
         *bytes = 0;
         return true;
@@ -79,8 +82,8 @@ inline bool span_bytes(int64_t rows, int64_t cols, int64_t ld, uint64_t* bytes) 
     int64_t last;
     if (__builtin_mul_overflow(rows - 1, ld, &last)) return false;
     if (__builtin_add_overflow(last, cols, &last)) return false;
-    if (last > INT64_MAX / 2) return false;
-    *bytes = (uint64_t)last * 2u;
+    if (last > INT64_MAX / 4) return false;
+    *bytes = (uint64_t)last * (uint64_t)esize;
     return true;
 }
 
@@ -90,13 +93,20 @@ inline bool overlaps(const void* p, uint64_t pn, const void* q, uint64_t qn) {
     return a < b + qn && b < a + pn;
 }
 
+// ab_type / c_type: element types; bias: N floats or null; alpha and act as
+// in tgemm_gemm (epi: alpha != 1, a bias or an activation).
 inline int make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
                      int64_t ldb, int b_layout, void* C, int64_t ldc, int force_generic,
-                     int group_m, int num_xcd, int k_step, int stages, Plan* pl) {
+                     int group_m, int num_xcd, int k_step, int stages, Plan* pl,
+                     int ab_type = TGEMM_F16, int c_type = TGEMM_F16, const void* bias = nullptr,
+                     bool epi = false) {
     const int64_t kMaxDim = 2147483647;
     if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
         return TGEMM_ERR_INVALID;
     if (b_layout != TGEMM_B_KxN && b_layout != TGEMM_B_NxK) return TGEMM_ERR_INVALID;
+    if (ab_type != TGEMM_F16 && ab_type != TGEMM_BF16) return TGEMM_ERR_INVALID;
+    if (c_type != TGEMM_F16 && c_type != TGEMM_BF16 && c_type != TGEMM_F32) return TGEMM_ERR_INVALID;
+    const int c_size = c_type == TGEMM_F32 ? 4 : 2;
     if (force_generic != 0 && force_generic != 1) return TGEMM_ERR_INVALID;
     if (group_m < 0 || group_m > 1024 || num_xcd < 0 || num_xcd > 64) return TGEMM_ERR_INVALID;
     if (k_step != 0 && k_step != 32 && k_step != 64) return TGEMM_ERR_INVALID;
@@ -115,10 +125,14 @@ inline int make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
     } else {
         if (!span_bytes(N, K, ldb, &nb)) return TGEMM_ERR_INVALID;
     }
-    if (!span_bytes(M, N, ldc, &nc)) return TGEMM_ERR_INVALID;
+    if (!span_bytes(M, N, ldc, &nc, c_size)) return TGEMM_ERR_INVALID;
     if ((na && !A) || (nb && !B) || (nc && !C)) return TGEMM_ERR_INVALID;
-    if (((uintptr_t)A & 1) || ((uintptr_t)B & 1) || ((uintptr_t)C & 1)) return TGEMM_ERR_INVALID;
+    if (((uintptr_t)A & 1) || ((uintptr_t)B & 1) || ((uintptr_t)C % c_size)) return TGEMM_ERR_INVALID;
     if (overlaps(C, nc, A, na) || overlaps(C, nc, B, nb)) return TGEMM_ERR_INVALID;
+    // the bias is read while C is written: 4-byte aligned, apart from C
+    const uint64_t nbias = bias ? (uint64_t)N * 4u : 0u;
+    if (bias && ((uintptr_t)bias & 3)) return TGEMM_ERR_INVALID;
+    if (overlaps(C, nc, bias, nbias)) return TGEMM_ERR_INVALID;
 
     const int64_t gm = (M + BM - 1) / BM, gn = (N + BN - 1) / BN;
     if (gm * gn > kMaxDim) return TGEMM_ERR_UNSUPPORTED;
@@ -130,6 +144,9 @@ inline int make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
     pl->ldb = ldb;
     pl->ldc = ldc;
     pl->layout = b_layout;
+    pl->ab_type = ab_type;
+    pl->c_type = c_type;
+    pl->epi = epi;
     pl->grid_m = (int)gm;
     pl->grid_n = (int)gn;
     pl->W = (int)(gm * gn);
@@ -140,7 +157,7 @@ inline int make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
 
     const bool vec_ab = !force_generic && ((uintptr_t)A % 16 == 0) && (lda % 8 == 0) &&
                         ((uintptr_t)B % 16 == 0) && (ldb % 8 == 0);
-    const bool vec_c = ((uintptr_t)C % 8 == 0) && (ldc % 4 == 0);
+    const bool vec_c = ((uintptr_t)C % 8 == 0) && ((ldc * c_size) % 8 == 0);
     // direct-to-LDS (any 2-byte alignment: gfx950 buffer loads accept
     // unaligned addresses): row strides small enough for 32-bit panel
     // offsets; a K x N B additionally needs every byte offset it forms,

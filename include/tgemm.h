@@ -1,6 +1,8 @@
 /*
- * tgemm: fp16 dense tiled matrix product C = A * B on AMD Instinct MI355X
- * (gfx950). C ABI: plain pointers and sizes, no HIP or framework types.
+ * tgemm: dense tiled matrix product C = A * B on AMD Instinct MI355X
+ * (gfx950), binary16 in and out (tgemm_f16), with bfloat16 inputs, bfloat16
+ * or fp32 output and a scale / bias / activation epilogue (tgemm_gemm).
+ * C ABI: plain pointers and sizes, no HIP or framework types.
  *
  * The operation (page 1, "Using NVIDIA CUDA Tile to write a high-performance
  * matrix multiply", section "What is matrix multiplication?"): for A of M x K
@@ -43,6 +45,13 @@ extern "C" {
 #endif
 
 typedef enum { TGEMM_B_KxN = 0, TGEMM_B_NxK = 1 } tgemm_b_layout;
+
+/* Element types: IEEE 754 binary16, bfloat16 (the upper 16 bits of a
+ * binary32), IEEE 754 binary32. */
+typedef enum { TGEMM_F16 = 0, TGEMM_BF16 = 1, TGEMM_F32 = 2 } tgemm_dtype;
+
+/* Activation applied by the epilogue of tgemm_gemm. */
+typedef enum { TGEMM_ACT_NONE = 0, TGEMM_ACT_RELU = 1 } tgemm_act;
 
 enum {
     TGEMM_OK = 0,
@@ -104,6 +113,57 @@ int tgemm_f16_config(int64_t M, int64_t N, int64_t K,
                      int force_generic, int group_m, int num_xcd,
                      int k_step, int stages);
 
+/*
+ * C = act(alpha * A * B + bias) with a choice of element types, on `stream`.
+ *
+ * The pages' tile kernels take their element types as parameters: inputs
+ * of two bytes (binary16 or bfloat16) share one tile configuration (page 1,
+ * section "Step 2: set the tile size"), and the guide's example accumulates
+ * binary16 products in fp32 and stores an fp32 C (page 4, section 2.4.9.1);
+ * production GEMMs fuse work on the output into the store (page 5, Croqtile
+ * tutorial "dense GEMM fp16 from naive", section "SOTA comparison": epilogue
+ * fusion).
+ * For every output element, in fp32 after the fp32 accumulation:
+ *   v = alpha * sum_k A[i][k] * B[k][j] + bias[j]   (one fused multiply-add)
+ *   v = max(v, 0) if act == TGEMM_ACT_RELU (a NaN stays NaN)
+ * then v is converted to c_type with round to nearest even (an fp32 C gets
+ * v itself). alpha == 1, bias == NULL and act == TGEMM_ACT_NONE store the
+ * sums exactly as tgemm_f16 does (for binary16 in and out: the same bits).
+ *
+ *   ab_type: TGEMM_F16 or TGEMM_BF16, the type of both A and B.
+ *   c_type:  TGEMM_F16, TGEMM_BF16 or TGEMM_F32; ldc counts elements of
+ *            that type (C[i*ldc + j]).
+ *   bias:    NULL, or N fp32 values in device memory (4-byte aligned),
+ *            added to every row; only read.
+ * Storage, ownership, asynchrony and the remaining argument checks are those
+ * of tgemm_f16, with these in addition (TGEMM_ERR_INVALID, nothing enqueued):
+ * ab_type or c_type or act out of range; C not aligned to its element size;
+ * bias not 4-byte aligned; the bias overlapping C.
+ * K == 0 stores act(bias[j]) (zero sums, scaled, plus the bias).
+ */
+int tgemm_gemm(int64_t M, int64_t N, int64_t K,
+               int ab_type, const void* A, int64_t lda,
+               const void* B, int64_t ldb, int b_layout,
+               int c_type, void* C, int64_t ldc,
+               float alpha, const float* bias, int act,
+               void* stream);
+
+/*
+ * tgemm_gemm with the launch choices of tgemm_f16_config (same meaning and
+ * ranges). The binary16-in, binary16-out product without epilogue is built
+ * for every K step and ring depth; every other combination for the default
+ * ring depth of each K step (2 stages at 64, 4 at 32): other depths return
+ * TGEMM_ERR_UNSUPPORTED for it, with nothing enqueued.
+ */
+int tgemm_gemm_config(int64_t M, int64_t N, int64_t K,
+                      int ab_type, const void* A, int64_t lda,
+                      const void* B, int64_t ldb, int b_layout,
+                      int c_type, void* C, int64_t ldc,
+                      float alpha, const float* bias, int act,
+                      void* stream,
+                      int force_generic, int group_m, int num_xcd,
+                      int k_step, int stages);
+
 /* Human-readable text of a TGEMM_* status code (static storage). */
 const char* tgemm_status_string(int status);
 
@@ -127,6 +187,20 @@ int tgemm_plan_f16(int64_t M, int64_t N, int64_t K,
                    int force_generic, int group_m, int num_xcd,
                    int k_step, int stages,
                    int64_t* info);
+
+/*
+ * Host-only planning query for tgemm_gemm_config: the same info[0..9] as
+ * tgemm_plan_f16, or the error tgemm_gemm_config would return (including
+ * TGEMM_ERR_UNSUPPORTED for a ring depth that is not built for the types).
+ */
+int tgemm_plan_gemm(int64_t M, int64_t N, int64_t K,
+                    int ab_type, const void* A, int64_t lda,
+                    const void* B, int64_t ldb, int b_layout,
+                    int c_type, void* C, int64_t ldc,
+                    float alpha, const float* bias, int act,
+                    int force_generic, int group_m, int num_xcd,
+                    int k_step, int stages,
+                    int64_t* info);
 
 /*
  * Host-only: the output tile that workgroup `wid` of a grid_m x grid_n tile

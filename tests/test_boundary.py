@@ -196,3 +196,102 @@ def test_binding_raises_when_library_missing(monkeypatch, tmp_path):
     monkeypatch.setattr(_binding, "LIB_PATH", str(tmp_path / "libtgemm.so"))
     with pytest.raises(RuntimeError, match="missing"):
         _binding.load()
+
+
+# ------------------------------------------------ typed GEMM with epilogue --
+
+def _plan_ex(M, N, K, ab="f16", ct="f16", A=PA, lda=None, B=PB, ldb=None, lay="KxN", C=PC, ldc=None,
+             alpha=1.0, bias=None, act="none", **kw):
+    lda = K if lda is None else lda
+    ldb = (N if lay == "KxN" else K) if ldb is None else ldb
+    ldc = N if ldc is None else ldc
+    return tg.tgemm_plan_gemm(M, N, K, ab, A, lda, B, ldb, lay, ct, C, ldc, alpha, bias, act, **kw)
+
+
+PBIAS = 4 << 40
+
+
+@pytest.mark.parametrize("args", [
+    dict(M=4, N=4, K=4, ab=2),                        # fp32 inputs are not a binary16/bfloat16 pair
+    dict(M=4, N=4, K=4, ab=-1),
+    dict(M=4, N=4, K=4, ct=3),
+    dict(M=4, N=4, K=4, act=2),
+    dict(M=4, N=4, K=4, ct="f32", C=PC + 2),          # fp32 C must be 4-byte aligned
+    dict(M=4, N=4, K=4, bias=PBIAS + 2),              # bias must be 4-byte aligned
+    dict(M=4, N=4, K=4, bias=PC + 4),                 # bias overlaps C
+    dict(M=4, N=4, K=4, ct="f32", C=PA + 16),         # fp32 C spans 4-byte elements: overlaps A
+    dict(M=4, N=9, K=8, ct="f32", ldc=8),
+])
+def test_typed_invalid_arguments_rejected(args):
+    rc, info = _plan_ex(**args)
+    assert rc == tg.TGEMM_ERR_INVALID and info is None
+    # the launching entry point returns the same code without touching the GPU
+    a = dict(args)
+    M, N, K = a.pop("M"), a.pop("N"), a.pop("K")
+    rc2 = tg.tgemm_gemm(M, N, K, a.get("ab", "f16"), a.get("A", PA), K, a.get("B", PB), N, "KxN",
+                        a.get("ct", "f16"), a.get("C", PC), a.get("ldc", N), 1.0, a.get("bias"),
+                        a.get("act", "none"))
+    assert rc2 == tg.TGEMM_ERR_INVALID
+
+
+def test_fp32_output_overlap_uses_four_byte_elements():
+    # 4 x 4 fp32 C ends 64 bytes after its base; A 40 bytes after C's base overlaps only as fp32
+    assert _plan_ex(4, 4, 4, ct="f16", C=PA - 40)[0] == tg.TGEMM_OK
+    assert _plan_ex(4, 4, 4, ct="f32", C=PA - 40)[0] == tg.TGEMM_ERR_INVALID
+
+
+def test_typed_plans_match_f16_plans():
+    for ab in ("f16", "bf16"):
+        for ct in ("f16", "bf16", "f32"):
+            for kw in (dict(), dict(alpha=0.5), dict(bias=PBIAS), dict(act="relu")):
+                rc, info = _plan_ex(8192, 8192, 8192, ab=ab, ct=ct, lay="NxK", **kw)
+                rc0, info0 = _plan(8192, 8192, 8192, lay="NxK")
+                assert rc == rc0 == 0 and info == info0, (ab, ct, kw)
+                rc, info = _plan_ex(512, 512, 64, ab=ab, ct=ct, **kw)
+                assert rc == 0 and (info["bk"], info["stages"]) == (32, 4)
+                rc, info = _plan_ex(300, 200, 100, ab=ab, ct=ct, force_generic=1, **kw)
+                assert rc == 0 and not info["variant"] & 8
+
+
+def test_typed_ring_depths_other_than_default_are_unsupported():
+    # every depth for the plain binary16 product
+    for st in (2, 3, 4, 5):
+        assert _plan_ex(1024, 1024, 1024, stages=st)[0] == tg.TGEMM_OK
+    # the default depth of each K step for every other combination
+    for ab, ct, kw in (("bf16", "bf16", {}), ("f16", "f32", {}), ("f16", "f16", dict(alpha=2.0))):
+        assert _plan_ex(1024, 1024, 1024, ab=ab, ct=ct, k_step=32, stages=4, **kw)[0] == tg.TGEMM_OK
+        assert _plan_ex(1024, 1024, 1024, ab=ab, ct=ct, k_step=64, **kw)[0] == tg.TGEMM_OK
+        for st in (2, 3, 5):
+            assert _plan_ex(1024, 1024, 1024, ab=ab, ct=ct, k_step=32, stages=st, **kw)[0] == \
+                tg.TGEMM_ERR_UNSUPPORTED
+            # the launching entry point refuses the same way, before any GPU call
+            lib = tg.load()
+            rc = lib.tgemm_gemm_config(1024, 1024, 1024, tg._binding._DTYPE[ab], PA, 1024, PB, 1024, 0,
+                                       tg._binding._DTYPE[ct], PC, 1024, kw.get("alpha", 1.0), None, 0, None,
+                                       0, 0, 0, 32, st)
+            assert rc == tg.TGEMM_ERR_UNSUPPORTED
+
+
+def test_fp32_output_store_width_flags():
+    V, C8, DMA = 1, 2, 8
+    # fp32 C: 8-byte aligned with an even ldc gives 64-bit stores
+    rc, info = _plan_ex(256, 256, 256, ct="f32")
+    assert info["variant"] == V | C8 | DMA
+    rc, info = _plan_ex(256, 255, 256, ct="f32", ldb=256, ldc=255)
+    assert info["variant"] == V | DMA
+    rc, info = _plan_ex(256, 256, 256, ct="f32", C=PC + 4)
+    assert info["variant"] == V | DMA
+
+
+def test_typed_empty_outputs_are_noops_without_gpu():
+    lib = tg.load()
+    assert lib.tgemm_gemm(0, 5, 7, 1, PA, 7, PB, 5, 0, 2, PC, 5, 1.0, None, 0, None) == tg.TGEMM_OK
+    assert lib.tgemm_gemm(5, 0, 7, 1, PA, 7, PB, 1, 0, 2, PC, 1, 2.0, PBIAS, 1, None) == tg.TGEMM_OK
+
+
+def test_header_declares_type_and_activation_values():
+    src = open(os.path.join(ROOT, "include", "tgemm.h")).read()
+    for name, val in (("TGEMM_F16", 0), ("TGEMM_BF16", 1), ("TGEMM_F32", 2), ("TGEMM_ACT_NONE", 0),
+                      ("TGEMM_ACT_RELU", 1)):
+        assert re.search(rf"{name}\s*=\s*{val}\b", src)
+        assert getattr(tg, name) == val

@@ -1,0 +1,321 @@
+"""GPU parity of the typed GEMM (binary16 / bfloat16 inputs; binary16,
+bfloat16 or fp32 output; scale, bias and rectifier on store) through the C
+ABI, against the extended CPU oracle:
+
+  |g - ref| <= 1e-3 * (|alpha| * sum_k |a*b| + |bias[j]|) + ulp_out(ref)
+
+element by element, and bit-exact where the answer is exactly representable
+(integer sums stored in fp32) or where two outputs of the library must agree
+(one accumulation rounded to two output types; every pipeline and raster).
+"""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import dense_tiled_gemm_tgemm_amd as tg  # noqa: E402
+from dense_tiled_gemm_tgemm_amd import inputs  # noqa: E402
+
+DEV = "cuda:0"
+TORCH_DT = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
+COMBOS = [(ab, ct) for ab in ("f16", "bf16") for ct in ("f16", "bf16", "f32")]
+EPI = {"plain": dict(alpha=1.0, bias=False, act="none"),
+       "epi": dict(alpha=-0.625, bias=True, act="relu")}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    tg.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def _bits(shape, seed, ab, dist=("uniform", -1.0, 1.0)):
+    """Seeded operand as uint16 bit patterns of its type."""
+    if ab == "f16":
+        return inputs.random_f16(shape, seed, dist).view(np.uint16)
+    return inputs.random_bf16(shape, seed, dist)
+
+
+def _dev(bits, ab):
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV)
+    return t.view(TORCH_DT[ab])
+
+
+def _out_np(t):
+    torch.cuda.synchronize()
+    if t.dtype == torch.float32:
+        return t.cpu().numpy()
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _bias(N, seed, on):
+    if not on:
+        return None, None
+    b = inputs.random_bias(N, seed, scale=2.0)
+    return b, torch.from_numpy(b).to(DEV)
+
+
+def _check(oracle_mod, A, B, lay, ab, ct, got, alpha, bias_np, act, what, I=None, J=None):
+    ref, tol = oracle_mod.gemm_ex(A, B, lay, ab, alpha, bias_np, act, I=I, J=J)
+    sel = got if I is None else got[I, J]
+    res = oracle_mod.check_ex(sel, ct, ref, tol)
+    assert res["nfail"] == 0, f"{what}: {res}"
+    return res
+
+
+SMALL = [(1, 1, 1), (31, 17, 65), (255, 257, 63), (300, 520, 200), (513, 300, 8), (512, 512, 512)]
+
+
+@pytest.mark.parametrize("epi", ["plain", "epi"])
+@pytest.mark.parametrize("lay", ["KxN", "NxK"])
+@pytest.mark.parametrize("ab,ct", COMBOS)
+@pytest.mark.parametrize("M,N,K", SMALL)
+def test_small_shapes_full_parity(oracle_mod, M, N, K, ab, ct, lay, epi):
+    print(f"case typed {M}x{N}x{K} {ab}->{ct} {lay} {epi}", flush=True)
+    seed = (M * 7 + N * 13 + K * 17) % 100003
+    A = _bits((M, K), seed, ab)
+    B = _bits((K, N) if lay == "KxN" else (N, K), seed + 1, ab)
+    e = EPI[epi]
+    b_np, b_dev = _bias(N, seed + 2, e["bias"])
+    C = tg.gemm(_dev(A, ab), _dev(B, ab), lay, out_dtype=TORCH_DT[ct], alpha=e["alpha"], bias=b_dev, act=e["act"])
+    _check(oracle_mod, A, B, lay, ab, ct, _out_np(C), e["alpha"], b_np, e["act"], f"{M}x{N}x{K} {ab}->{ct} {lay}")
+
+
+@pytest.mark.parametrize("lay", ["KxN", "NxK"])
+@pytest.mark.parametrize("ab,ct", [("bf16", "bf16"), ("f16", "f32"), ("bf16", "f32")])
+@pytest.mark.parametrize("M,N,K", [(300, 520, 200), (257, 255, 129)])
+def test_register_staged_path_full_parity(oracle_mod, M, N, K, ab, ct, lay):
+    print(f"case typed generic {M}x{N}x{K} {ab}->{ct} {lay}", flush=True)
+    A = _bits((M, K), M + 3 * K, ab)
+    B = _bits((K, N) if lay == "KxN" else (N, K), N + 5 * K, ab)
+    b_np, b_dev = _bias(N, 11, True)
+    Ad, Bd = _dev(A, ab), _dev(B, ab)
+    C = tg.gemm(Ad, Bd, lay, out_dtype=TORCH_DT[ct], alpha=0.5, bias=b_dev, act="relu", force_generic=1)
+    _check(oracle_mod, A, B, lay, ab, ct, _out_np(C), 0.5, b_np, "relu", "generic")
+    C2 = tg.gemm(Ad, Bd, lay, out_dtype=TORCH_DT[ct], alpha=0.5, bias=b_dev, act="relu")
+    torch.cuda.synchronize()
+    assert torch.equal(C.view(torch.int16) if ct != "f32" else C, C2.view(torch.int16) if ct != "f32" else C2)
+
+
+def test_plain_f16_equals_tgemm_f16_bitwise():
+    """The typed entry point without epilogue is the binary16 product, bit for bit."""
+    print("case typed plain = f16", flush=True)
+    A = _dev(_bits((700, 300), 1, "f16"), "f16")
+    B = _dev(_bits((600, 300), 2, "f16"), "f16")
+    C1 = tg.mm(A, B, "NxK")
+    C2 = tg.gemm(A, B, "NxK")
+    torch.cuda.synchronize()
+    assert torch.equal(C1.view(torch.int16), C2.view(torch.int16))
+
+
+@pytest.mark.parametrize("ab", ["f16", "bf16"])
+@pytest.mark.parametrize("lay,M,N,K", [("NxK", 700, 600, 264), ("KxN", 1300, 1000, 4099), ("NxK", 520, 777, 72)])
+def test_one_accumulation_rounded_to_each_output_type(ab, lay, M, N, K):
+    """The fp32 output holds the accumulator itself; the binary16 and bfloat16
+    outputs are that value rounded to nearest even (torch's CPU conversions),
+    bit for bit. The same holds with the epilogue applied."""
+    print(f"case typed rounding {ab} {lay} {M}x{N}x{K}", flush=True)
+    A = _dev(_bits((M, K), M + K, ab), ab)
+    B = _dev(_bits((N, K) if lay == "NxK" else (K, N), N + K, ab), ab)
+    _, b_dev = _bias(N, 5, True)
+    for kw in (dict(), dict(alpha=-1.75, bias=b_dev, act="relu")):
+        c32 = tg.gemm(A, B, lay, out_dtype=torch.float32, **kw)
+        c16 = tg.gemm(A, B, lay, out_dtype=torch.float16, **kw)
+        cbf = tg.gemm(A, B, lay, out_dtype=torch.bfloat16, **kw)
+        torch.cuda.synchronize()
+        h32 = c32.cpu()
+        assert torch.equal(h32.to(torch.float16).view(torch.int16), c16.cpu().view(torch.int16))
+        assert torch.equal(h32.to(torch.bfloat16).view(torch.int16), cbf.cpu().view(torch.int16))
+
+
+@pytest.mark.parametrize("ab", ["f16", "bf16"])
+def test_epilogue_is_one_fused_multiply_add_then_rectifier(ab):
+    """fp32 output with the epilogue equals rn32(alpha * s + b) clipped at zero,
+    s the plain fp32 output (the fused multiply-add rounds once: computed here
+    in fp64 from the exact product alpha * s, within one fp32 ulp)."""
+    print(f"case typed epilogue closed form {ab}", flush=True)
+    M, N, K = 640, 900, 333
+    A = _dev(_bits((M, K), 21, ab), ab)
+    B = _dev(_bits((K, N), 22, ab), ab)
+    b_np, b_dev = _bias(N, 23, True)
+    s = _out_np(tg.gemm(A, B, "KxN", out_dtype=torch.float32)).astype(np.float64)
+    alpha = np.float32(0.3)
+    got = _out_np(tg.gemm(A, B, "KxN", out_dtype=torch.float32, alpha=float(alpha), bias=b_dev,
+                          act="relu")).astype(np.float64)
+    want = np.maximum((float(alpha) * s + b_np.astype(np.float64)).astype(np.float32), 0).astype(np.float64)
+    ulp = np.spacing(np.abs(want).astype(np.float32)).astype(np.float64)
+    assert np.all(np.abs(got - want) <= ulp)
+    assert (got == 0).sum() > 0 and (got > 0).sum() > 0
+    # scale only, no bias: the product alpha * s rounded once
+    got2 = _out_np(tg.gemm(A, B, "KxN", out_dtype=torch.float32, alpha=-2.0)).astype(np.float64)
+    assert np.array_equal(got2, -2.0 * s)
+
+
+@pytest.mark.parametrize("name", ["sq256", "sq4096", "ragged", "sq8192_nt", "qkv_proj"])
+def test_bf16_ternary_bit_exact_fp32_output(oracle_mod, name):
+    """Entries in {-1, 0, 1} are exact in bfloat16 and every partial sum is an
+    integer below 2^24: the fp32 output is exact at the workload shapes."""
+    w = inputs.WORKLOADS[name]
+    print(f"case typed ternary {name}", flush=True)
+    A = inputs.to_bf16_bits(inputs.ternary_f16((w.M, w.K), 200 + w.seed).astype(np.float64))
+    B = inputs.to_bf16_bits(inputs.ternary_f16(w.b_shape, 201 + w.seed).astype(np.float64))
+    C = tg.gemm(_dev(A, "bf16"), _dev(B, "bf16"), w.b_layout, out_dtype=torch.float32)
+    got = _out_np(C)
+    I, J = inputs.sample_points(w.M, w.N, 8192, 202 + w.seed)
+    ref, _ = oracle_mod.gemm_ex(A, B, w.b_layout, "bf16", I=I, J=J)
+    assert np.array_equal(got[I, J].astype(np.float64), ref)
+    g = got.astype(np.float64)
+    assert np.all(g == np.round(g)) and np.abs(g).max() <= w.K
+
+
+@pytest.mark.parametrize("ct", ["bf16", "f32"])
+@pytest.mark.parametrize("name", ["sq4096", "ragged", "sq8192_nt", "qkv_proj"])
+def test_bf16_workload_parity(oracle_mod, name, ct):
+    """The workloads with bfloat16 operands drawn from the same seeded values,
+    launched as the benchmark launches them (raw C call on torch's stream)."""
+    w = inputs.WORKLOADS[name]
+    print(f"case typed workload {name} bf16->{ct}", flush=True)
+    A, B = inputs.make_inputs(w, "bf16")
+    Ad, Bd = _dev(A, "bf16"), _dev(B, "bf16")
+    C = torch.empty((w.M, w.N), dtype=TORCH_DT[ct], device=DEV)
+    rc = tg.tgemm_gemm(w.M, w.N, w.K, "bf16", Ad.data_ptr(), w.K, Bd.data_ptr(), B.shape[1], w.b_layout, ct,
+                       C.data_ptr(), w.N, 1.0, None, "none", torch.cuda.current_stream().cuda_stream)
+    assert rc == tg.TGEMM_OK
+    got = _out_np(C)
+    I, J = inputs.sample_points(w.M, w.N, 8192, w.seed + 3000)
+    res = _check(oracle_mod, A, B, w.b_layout, "bf16", ct, got, 1.0, None, "none", name, I, J)
+    print(f"  {name}: {res['n']} checked, worst {res['worst']:.4f}", flush=True)
+
+
+@pytest.mark.parametrize("ab,ct", [("f16", "f32"), ("f16", "f16"), ("bf16", "bf16")])
+def test_epilogue_workload_parity(oracle_mod, ab, ct):
+    """Scale, bias and rectifier on the projection workload (fused QKV width)."""
+    w = inputs.WORKLOADS["qkv_proj"]
+    print(f"case typed epilogue workload {ab}->{ct}", flush=True)
+    A, B = inputs.make_inputs(w, ab)
+    if ab == "f16":
+        A, B = A.view(np.uint16), B.view(np.uint16)
+    b_np, b_dev = _bias(w.N, 31, True)
+    C = tg.gemm(_dev(A, ab), _dev(B, ab), w.b_layout, out_dtype=TORCH_DT[ct], alpha=0.125, bias=b_dev,
+                act="relu")
+    got = _out_np(C)
+    I, J = inputs.sample_points(w.M, w.N, 8192, 32)
+    _check(oracle_mod, A, B, w.b_layout, ab, ct, got, 0.125, b_np, "relu", "qkv epilogue", I, J)
+
+
+@pytest.mark.parametrize("ab,ct", COMBOS)
+@pytest.mark.parametrize("lay", ["NxK", "KxN"])
+def test_persistent_grid_and_pipelines_agree(oracle_mod, ab, ct, lay):
+    """More tiles than compute units (the persistent kernel), with the
+    epilogue: bit-identical to the register-staged kernel, to 32-deep steps,
+    and under another raster; sampled outputs within tolerance."""
+    M, N, K = 4300, 4300, 1000
+    print(f"case typed persistent {ab}->{ct} {lay}", flush=True)
+    A = _bits((M, K), 41, ab)
+    B = _bits((N, K) if lay == "NxK" else (K, N), 42, ab)
+    b_np, b_dev = _bias(N, 43, True)
+    Ad, Bd = _dev(A, ab), _dev(B, ab)
+    kw = dict(out_dtype=TORCH_DT[ct], alpha=-0.75, bias=b_dev, act="relu")
+    outs = [tg.gemm(Ad, Bd, lay, **kw), tg.gemm(Ad, Bd, lay, force_generic=1, **kw),
+            tg.gemm(Ad, Bd, lay, k_step=32, **kw), tg.gemm(Ad, Bd, lay, group_m=3, num_xcd=1, **kw)]
+    torch.cuda.synchronize()
+    base = outs[0] if ct == "f32" else outs[0].view(torch.int16)
+    for o in outs[1:]:
+        assert torch.equal(base, o if ct == "f32" else o.view(torch.int16))
+    I, J = inputs.sample_points(M, N, 4096, 44)
+    _check(oracle_mod, A, B, lay, ab, ct, _out_np(outs[0]), -0.75, b_np, "relu", "persistent", I, J)
+
+
+@pytest.mark.parametrize("ct", ["f16", "bf16", "f32"])
+def test_k_zero_stores_rectified_bias(ct):
+    print(f"case typed K=0 {ct}", flush=True)
+    A = torch.empty((300, 0), dtype=torch.bfloat16, device=DEV)
+    B = torch.empty((0, 270), dtype=torch.bfloat16, device=DEV)
+    b_np, b_dev = _bias(270, 51, True)
+    C = torch.full((300, 270), 7.0, dtype=TORCH_DT[ct], device=DEV)
+    tg.gemm(A, B, "KxN", out=C, alpha=2.0, bias=b_dev, act="relu")
+    want = torch.from_numpy(np.maximum(b_np, 0)).to(TORCH_DT[ct])
+    assert torch.equal(C.cpu(), want.expand(300, 270))
+
+
+@pytest.mark.parametrize("ct,offset,pad", [
+    ("f32", 0, 2),      # rows start 16-byte aligned: 16-byte stores
+    ("f32", 2, 6),      # 8-byte aligned rows: 8-byte stores
+    ("f32", 1, 3),      # element stores
+    ("bf16", 0, 2),     # 16-byte stores
+    ("f16", 4, 2),      # 8-byte stores
+    ("bf16", 1, 3),     # element stores
+])
+def test_output_alignment_paths_and_guard_band(oracle_mod, ct, offset, pad):
+    """C inside a larger NaN-filled buffer (row stride N + pad, start `offset`
+    elements in): 16-byte, 8-byte and element stores, edge tiles; nothing
+    outside the M x N window changes."""
+    M, N, K = 300, 270, 130
+    print(f"case typed guard {ct} offset={offset} pad={pad}", flush=True)
+    A = _bits((M, K), 61, "bf16")
+    B = _bits((K, N), 62, "bf16")
+    b_np, b_dev = _bias(N, 63, True)
+    ldc = N + pad
+    total = offset + M * ldc + 64
+    if ct == "f32":
+        buf = torch.full((total,), float("nan"), dtype=torch.float32, device=DEV)
+    else:
+        buf = torch.full((total,), 0x7FC1 if ct == "bf16" else 0x7E01, dtype=torch.int16, device=DEV)
+        buf = buf.view(TORCH_DT[ct])
+    Ad, Bd = _dev(A, "bf16"), _dev(B, "bf16")
+    rc = tg.tgemm_gemm(M, N, K, "bf16", Ad.data_ptr(), K, Bd.data_ptr(), N, "KxN", ct,
+                       buf.data_ptr() + offset * buf.element_size(), ldc, 1.5, b_dev.data_ptr(), "none",
+                       torch.cuda.current_stream().cuda_stream)
+    assert rc == tg.TGEMM_OK
+    host = _out_np(buf)
+    win = host[offset:offset + M * ldc].reshape(M, ldc)
+    _check(oracle_mod, A, B, "KxN", "bf16", ct, np.ascontiguousarray(win[:, :N]), 1.5, b_np, "none", "guard")
+    outside = np.concatenate([host[:offset], win[:, N:].ravel(), host[offset + M * ldc:]])
+    if ct == "f32":
+        assert np.isnan(outside).all()
+    else:
+        assert (outside == (0x7FC1 if ct == "bf16" else 0x7E01)).all()
+
+
+def test_bias_nan_and_inf_propagate(oracle_mod):
+    """A NaN bias makes its column NaN (the rectifier keeps NaN); an infinite
+    bias its column infinite (or zero after the rectifier for -inf)."""
+    print("case typed bias specials", flush=True)
+    M, N, K = 64, 40, 32
+    A = _bits((M, K), 71, "f16")
+    B = _bits((K, N), 72, "f16")
+    b = inputs.random_bias(N, 73)
+    b[3], b[10], b[20] = np.nan, np.inf, -np.inf
+    for act in ("none", "relu"):
+        C = tg.gemm(_dev(A, "f16"), _dev(B, "f16"), "KxN", out_dtype=torch.float32, bias=torch.from_numpy(b).to(DEV),
+                    act=act)
+        got = _out_np(C)
+        assert np.isnan(got[:, 3]).all()
+        assert (got[:, 10] == np.inf).all()
+        assert (got[:, 20] == (-np.inf if act == "none" else 0)).all()
+        keep = [j for j in range(N) if j not in (3, 10, 20)]
+        ref, tol = oracle_mod.gemm_ex(A, B, "KxN", "f16", 1.0, b, act)
+        res = oracle_mod.check_ex(np.ascontiguousarray(got[:, keep]), "f32", np.ascontiguousarray(ref[:, keep]),
+                                  np.ascontiguousarray(tol[:, keep]))
+        assert res["nfail"] == 0, res
+
+
+def test_binary16_output_overflow_is_infinity(oracle_mod):
+    """Sums past binary16's range are stored as infinities of their sign."""
+    print("case typed overflow", flush=True)
+    K = 64
+    A = np.full((32, K), 60.0, dtype=np.float16).view(np.uint16)
+    B = np.full((K, 48), 30.0, dtype=np.float16)
+    B[:, 1::2] *= -1
+    B = B.view(np.uint16)
+    C = tg.gemm(_dev(A, "f16"), _dev(B, "f16"), "KxN")        # sums are +-115200
+    got = _out_np(C)
+    ref, tol = oracle_mod.gemm_ex(A, B, "KxN", "f16")
+    assert oracle_mod.check_ex(got, "f16", ref, tol)["nfail"] == 0
+    f = got.view(np.float16)
+    assert np.isposinf(f[:, 0::2]).all() and np.isneginf(f[:, 1::2]).all()
