@@ -12,7 +12,7 @@ Prints ONE JSON line (rank 0):
              block of whole output rows of the same workload
 
 Usage: python bench.py [--gpus 1] [--steps 200] [--warmup 100] [--workload NAME]
-                       [--ab f16|bf16] [--out f16|bf16|f32] [--epilogue]
+                       [--ab f16|bf16] [--out f16|bf16|f32] [--epilogue] [--tune]
 
 The defaults time the headline line (binary16 in and out, tgemm_f16). --ab,
 --out and --epilogue time the typed entry point (tgemm_gemm) on the same
@@ -114,6 +114,8 @@ def main():
     ap.add_argument("--ab", choices=("f16", "bf16"), default="f16", help="operand type")
     ap.add_argument("--out", choices=("f16", "bf16", "f32"), default="f16", help="output type")
     ap.add_argument("--epilogue", action="store_true", help="alpha = 0.5, seeded fp32 bias, rectifier")
+    ap.add_argument("--tune", action="store_true",
+                    help="run the runtime tuner on the workload first; the timed launches use its choice")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mfma-ceiling", action="store_true",
                     help="instead of the GEMM, time the matrix-core ceiling probe (the GEMM's "
@@ -241,6 +243,15 @@ def main():
             if rc != tg.TGEMM_OK:
                 raise tg.TgemmError(rc)
 
+    tuned = None
+    if args.tune:
+        rc, tuned = tg.tgemm_tune_gemm(w.M, w.N, w.K, args.ab, Ad.data_ptr(), lda, Bd.data_ptr(), ldb, w.b_layout,
+                                       args.out, Cd.data_ptr(), ldc, alpha,
+                                       bias_d.data_ptr() if bias_d is not None else None, act, sptr, 5)
+        if rc != tg.TGEMM_OK:
+            raise tg.TgemmError(rc, "tune")
+        log(f"bench: tuned choice {tuned}")
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -283,7 +294,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": name, "M": w.M, "N": w.N, "K": w.K, "b_layout": w.b_layout,
                    "seed": w.seed, "accumulate": "f32", "output": args.out,
-                   "epilogue": (f"alpha={EPI_ALPHA}, bias, relu" if args.epilogue else "none")},
+                   "epilogue": (f"alpha={EPI_ALPHA}, bias, relu" if args.epilogue else "none"),
+                   "launch": ({k: tuned[k] for k in ("k_step", "stages", "group_m", "num_xcd")} if tuned
+                              else "default")},
         "roofline": {
             "bound": "mfma",
             "achieved": round(achieved, 2),

@@ -33,4 +33,8 @@ from ._binding import (  # noqa: F401
     tgemm_plan_f16,
     tgemm_plan_gemm,
     tgemm_tile_of,
+    tgemm_tune_gemm,
+    tune,
+    tuning_clear,
+    tuning_entries,
 )

@@ -76,6 +76,12 @@ def load():
     lib.tgemm_gemm_config.argtypes = ex_args + [_P, _INT, _INT, _INT, _INT, _INT]
     lib.tgemm_plan_gemm.restype = _INT
     lib.tgemm_plan_gemm.argtypes = ex_args + [_INT, _INT, _INT, _INT, _INT, ctypes.POINTER(_I64)]
+    lib.tgemm_tune_gemm.restype = _INT
+    lib.tgemm_tune_gemm.argtypes = ex_args + [_P, _INT, ctypes.POINTER(_I64)]
+    lib.tgemm_tuning_entries.restype = _INT
+    lib.tgemm_tuning_entries.argtypes = []
+    lib.tgemm_tuning_clear.restype = None
+    lib.tgemm_tuning_clear.argtypes = []
     lib.tgemm_status_string.restype = ctypes.c_char_p
     lib.tgemm_status_string.argtypes = [_INT]
     lib.tgemm_last_hip_error.restype = _INT
@@ -152,6 +158,29 @@ def tgemm_plan_gemm(M, N, K, ab_type, A, lda, B, ldb, b_layout, c_type, C, ldc, 
     if rc != TGEMM_OK:
         return rc, None
     return rc, dict(zip(_PLAN_KEYS, (int(v) for v in info)))
+
+
+_TUNE_KEYS = ("k_step", "stages", "group_m", "num_xcd", "median_ns", "candidates")
+
+
+def tgemm_tune_gemm(M, N, K, ab_type, A, lda, B, ldb, b_layout, c_type, C, ldc, alpha=1.0, bias=None, act="none",
+                    stream=None, rounds=5):
+    """Raw C call of the runtime tuner: (status, chosen launch dict or None)."""
+    info = (_I64 * 6)()
+    rc = int(load().tgemm_tune_gemm(M, N, K, _code(_DTYPE, ab_type), A, lda, B, ldb, _LAYOUT[b_layout],
+                                    _code(_DTYPE, c_type), C, ldc, float(alpha), bias, _code(_ACT, act), stream,
+                                    int(rounds), info))
+    if rc != TGEMM_OK:
+        return rc, None
+    return rc, dict(zip(_TUNE_KEYS, (int(v) for v in info)))
+
+
+def tuning_entries() -> int:
+    return int(load().tgemm_tuning_entries())
+
+
+def tuning_clear() -> None:
+    load().tgemm_tuning_clear()
 
 
 def tgemm_tile_of(grid_m, grid_n, group_m, num_xcd, wid):
@@ -235,9 +264,17 @@ def _torch_code(dtype):
     return codes[dtype]
 
 
+def tune(A, B, b_layout: str = "KxN", out=None, out_dtype=None, alpha: float = 1.0, bias=None, act: str = "none",
+         stream=None, rounds: int = 5):
+    """Time every launch choice of this problem on these tensors and record
+    the fastest for its shape (later gemm / mm calls with automatic choices
+    use it). Returns (C, chosen launch dict). Synchronizes the stream."""
+    return gemm(A, B, b_layout, out, out_dtype, alpha, bias, act, stream, _tune_rounds=rounds)
+
+
 def gemm(A, B, b_layout: str = "KxN", out=None, out_dtype=None, alpha: float = 1.0, bias=None, act: str = "none",
          stream=None, force_generic: int = 0, group_m: int = 0, num_xcd: int = 0, k_step: int = 0,
-         stages: int = 0):
+         stages: int = 0, _tune_rounds: int = 0):
     """C = act(alpha * A @ B + bias) for float16 or bfloat16 device tensors
     (fp32 accumulation and epilogue in the kernel).
 
@@ -275,6 +312,13 @@ def gemm(A, B, b_layout: str = "KxN", out=None, out_dtype=None, alpha: float = 1
         stream = torch.cuda.current_stream(A.device).cuda_stream
     elif hasattr(stream, "cuda_stream"):
         stream = stream.cuda_stream
+    if _tune_rounds:
+        rc, chosen = tgemm_tune_gemm(M, N, K, _torch_code(A.dtype), A.data_ptr(), lda, B.data_ptr(), ldb, lay,
+                                     _torch_code(out.dtype), out.data_ptr(), ldc, alpha, bias_ptr, act, stream,
+                                     _tune_rounds)
+        if rc != TGEMM_OK:
+            raise TgemmError(rc, f"tune M={M} N={N} K={K} layout={b_layout} {A.dtype}->{out.dtype}")
+        return out, chosen
     rc = tgemm_gemm_config(M, N, K, _torch_code(A.dtype), A.data_ptr(), lda, B.data_ptr(), ldb, lay,
                            _torch_code(out.dtype), out.data_ptr(), ldc, alpha, bias_ptr, act, stream,
                            force_generic, group_m, num_xcd, k_step, stages)

@@ -5,7 +5,11 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <atomic>
+#include <mutex>
+#include <unordered_map>
+#include <vector>
 
 #include "tgemm.h"
 #include "tgemm_kernels.h"
@@ -58,32 +62,89 @@ static bool epilogue_requested(float alpha, const float* bias, int act) {
     return !(alpha == 1.0f) || bias != nullptr || act != TGEMM_ACT_NONE;
 }
 
+// ---------------------------------------------------------------------------
+// Runtime tuning (page 2, "CUDA 13.1 new feature: the Tile programming model",
+// section 7.4: several tile configurations are tried and the fastest is kept
+// per problem shape, so later calls pay nothing). Here the choices are the
+// launch parameters that leave the result unchanged bit for bit: K step and
+// LDS ring depth of the direct-to-LDS pipeline, and the raster group height.
+// The table is per device, keyed by everything that selects a kernel: sizes,
+// strides, layout, types, epilogue on/off and the variant bits (alignment
+// classes, load path).
+// ---------------------------------------------------------------------------
+struct TuneKey {
+    int dev;
+    int64_t M, N, K, lda, ldb, ldc;
+    int layout, ab, ct, epi, variant;
+    bool operator==(const TuneKey& o) const {
+        return dev == o.dev && M == o.M && N == o.N && K == o.K && lda == o.lda && ldb == o.ldb && ldc == o.ldc &&
+               layout == o.layout && ab == o.ab && ct == o.ct && epi == o.epi && variant == o.variant;
+    }
+};
+
+struct TuneKeyHash {
+    size_t operator()(const TuneKey& k) const {
+        uint64_t h = 1469598103934665603ull;
+        const int64_t v[] = {k.dev, k.M, k.N, k.K, k.lda, k.ldb, k.ldc, k.layout, k.ab, k.ct, k.epi, k.variant};
+        for (int64_t x : v) h = (h ^ (uint64_t)x) * 1099511628211ull;    // FNV-1a over the fields
+        return (size_t)h;
+    }
+};
+
+struct TuneChoice {
+    int k_step, stages, group_m, num_xcd;
+};
+
+static std::mutex g_tune_mu;
+static std::unordered_map<TuneKey, TuneChoice, TuneKeyHash> g_tuned;
+static std::atomic<int> g_tuned_count{0};
+
+static bool tune_key(const Plan& pl, TuneKey* k) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return false;
+    *k = TuneKey{dev, pl.M, pl.N, pl.K, pl.lda, pl.ldb, pl.ldc, pl.layout, pl.ab_type, pl.c_type, pl.epi ? 1 : 0,
+                 pl.variant};
+    return true;
+}
+
+static bool tuned_choice(const Plan& pl, TuneChoice* c) {
+    if (g_tuned_count.load(std::memory_order_acquire) == 0) return false;   // nothing tuned: no runtime query
+    TuneKey k;
+    if (!tune_key(pl, &k)) return false;
+    std::lock_guard<std::mutex> lock(g_tune_mu);
+    const auto it = g_tuned.find(k);
+    if (it == g_tuned.end()) return false;
+    *c = it->second;
+    return true;
+}
+
+// Plan and kernel for a call. With every launch choice automatic (all zero)
+// the choice recorded by tgemm_tune_gemm for this problem, if any, is used.
 static int plan_gemm(int64_t M, int64_t N, int64_t K, int ab_type, const void* A, int64_t lda, const void* B,
                      int64_t ldb, int b_layout, int c_type, void* C, int64_t ldc, float alpha, const float* bias,
                      int act, int force_generic, int group_m, int num_xcd, int k_step, int stages, Plan* pl,
-                     const void** fn) {
+                     const void** fn, bool use_tuned = true) {
     if (act != TGEMM_ACT_NONE && act != TGEMM_ACT_RELU) return TGEMM_ERR_INVALID;
-    const int rc = make_plan(M, N, K, A, lda, B, ldb, b_layout, C, ldc, force_generic, group_m, num_xcd, k_step,
-                             stages, pl, ab_type, c_type, bias, epilogue_requested(alpha, bias, act));
+    const bool epi = epilogue_requested(alpha, bias, act);
+    int rc = make_plan(M, N, K, A, lda, B, ldb, b_layout, C, ldc, force_generic, group_m, num_xcd, k_step, stages,
+                       pl, ab_type, c_type, bias, epi);
     if (rc != TGEMM_OK) return rc;
+    TuneChoice t;
+    if (use_tuned && !force_generic && !group_m && !num_xcd && !k_step && !stages && tuned_choice(*pl, &t)) {
+        Plan tp;
+        rc = make_plan(M, N, K, A, lda, B, ldb, b_layout, C, ldc, 0, t.group_m, t.num_xcd, t.k_step, t.stages,
+                       &tp, ab_type, c_type, bias, epi);
+        if (rc == TGEMM_OK) *pl = tp;
+    }
     *fn = pick_kernel(*pl);
     return *fn ? TGEMM_OK : TGEMM_ERR_UNSUPPORTED;
 }
 
-}  // namespace tg
-
-extern "C" int tgemm_gemm_config(int64_t M, int64_t N, int64_t K, int ab_type, const void* A, int64_t lda,
-                                 const void* B, int64_t ldb, int b_layout, int c_type, void* C, int64_t ldc,
-                                 float alpha, const float* bias, int act, void* stream, int force_generic,
-                                 int group_m, int num_xcd, int k_step, int stages) {
-    tg::Plan pl;
-    const void* fn = nullptr;
-    const int rc = tg::plan_gemm(M, N, K, ab_type, A, lda, B, ldb, b_layout, c_type, C, ldc, alpha, bias, act,
-                                 force_generic, group_m, num_xcd, k_step, stages, &pl, &fn);
-    if (rc != TGEMM_OK) return rc;
-    if (pl.M == 0 || pl.N == 0) return TGEMM_OK;
+// Enqueue the planned kernel.
+static int launch(const Plan& pl, const void* fn, const void* A, const void* B, void* C, int c_type, float alpha,
+                  const float* bias, int act, void* stream) {
     const int c_size = c_type == TGEMM_F32 ? 4 : 2;
-    tg::Args args;
+    Args args;
     args.A = static_cast<const uint16_t*>(A);
     args.B = static_cast<const uint16_t*>(B);
     args.C = C;
@@ -103,24 +164,39 @@ extern "C" int tgemm_gemm_config(int64_t M, int64_t N, int64_t K, int ab_type, c
     args.num_xcd = pl.num_xcd;
     args.grid = pl.W;
     args.c16 = ((uintptr_t)C % 16 == 0) && ((pl.ldc * c_size) % 16 == 0);
-    args.c8 = (pl.variant & tg::kVecC) != 0;
-    if (tg::persistent(pl)) {
+    args.c8 = (pl.variant & kVecC) != 0;
+    if (persistent(pl)) {
         // one workgroup per compute unit, each walking several tiles
-        const int ncu = tg::compute_units();
+        const int ncu = compute_units();
         if (ncu < 0) {
-            tg::g_last_hip_error = -ncu;
+            g_last_hip_error = -ncu;
             return TGEMM_ERR_HIP;
         }
         if (ncu > 0 && ncu < pl.W) args.grid = ncu;
     }
     void* kargs[] = {&args};
-    const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)args.grid), dim3(tg::NTHREADS), kargs, 0,
+    const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)args.grid), dim3(NTHREADS), kargs, 0,
                                          static_cast<hipStream_t>(stream));
     if (e != hipSuccess) {
-        tg::g_last_hip_error = (int)e;
+        g_last_hip_error = (int)e;
         return TGEMM_ERR_HIP;
     }
     return TGEMM_OK;
+}
+
+}  // namespace tg
+
+extern "C" int tgemm_gemm_config(int64_t M, int64_t N, int64_t K, int ab_type, const void* A, int64_t lda,
+                                 const void* B, int64_t ldb, int b_layout, int c_type, void* C, int64_t ldc,
+                                 float alpha, const float* bias, int act, void* stream, int force_generic,
+                                 int group_m, int num_xcd, int k_step, int stages) {
+    tg::Plan pl;
+    const void* fn = nullptr;
+    const int rc = tg::plan_gemm(M, N, K, ab_type, A, lda, B, ldb, b_layout, c_type, C, ldc, alpha, bias, act,
+                                 force_generic, group_m, num_xcd, k_step, stages, &pl, &fn);
+    if (rc != TGEMM_OK) return rc;
+    if (pl.M == 0 || pl.N == 0) return TGEMM_OK;
+    return tg::launch(pl, fn, A, B, C, c_type, alpha, bias, act, stream);
 }
 
 extern "C" int tgemm_gemm(int64_t M, int64_t N, int64_t K, int ab_type, const void* A, int64_t lda, const void* B,
@@ -141,6 +217,110 @@ extern "C" int tgemm_f16_config(int64_t M, int64_t N, int64_t K, const void* A, 
 extern "C" int tgemm_f16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
                          int64_t ldb, int b_layout, void* C, int64_t ldc, void* stream) {
     return tgemm_f16_config(M, N, K, A, lda, B, ldb, b_layout, C, ldc, stream, 0, 0, 0, 0, 0);
+}
+
+extern "C" int tgemm_tune_gemm(int64_t M, int64_t N, int64_t K, int ab_type, const void* A, int64_t lda,
+                               const void* B, int64_t ldb, int b_layout, int c_type, void* C, int64_t ldc,
+                               float alpha, const float* bias, int act, void* stream, int rounds, int64_t* info) {
+    if (rounds < 1 || rounds > 100) return TGEMM_ERR_INVALID;
+    tg::Plan base;
+    const void* fn = nullptr;
+    int rc = tg::plan_gemm(M, N, K, ab_type, A, lda, B, ldb, b_layout, c_type, C, ldc, alpha, bias, act, 0, 0, 0, 0,
+                           0, &base, &fn, false);
+    if (rc != TGEMM_OK) return rc;
+    if (info)
+        for (int i = 0; i < 6; ++i) info[i] = 0;
+    if (base.M == 0 || base.N == 0) return TGEMM_OK;
+
+    // candidates: K step x ring depth (direct-to-LDS path only) x raster group height
+    struct Cand {
+        tg::TuneChoice c;
+        tg::Plan pl;
+        const void* fn;
+    };
+    std::vector<Cand> cands;
+    const int pipes[][2] = {{64, 2}, {32, 4}, {32, 2}, {32, 3}, {32, 5}};
+    const int npipes = (base.variant & tg::kDma) ? 5 : 1;
+    const int groups[] = {4, 8, 16};
+    for (int ip = 0; ip < npipes; ++ip) {
+        for (int g : groups) {
+            const int ks = (base.variant & tg::kDma) ? pipes[ip][0] : 0;
+            const int st = (base.variant & tg::kDma) ? pipes[ip][1] : 0;
+            Cand cd;
+            cd.c = tg::TuneChoice{ks, st, g, tg::kDefaultNumXcd};
+            if (tg::plan_gemm(M, N, K, ab_type, A, lda, B, ldb, b_layout, c_type, C, ldc, alpha, bias, act, 0, g,
+                              tg::kDefaultNumXcd, ks, st, &cd.pl, &cd.fn, false) != TGEMM_OK)
+                continue;                                   // not built for these types, or invalid for this K
+            bool dup = false;                               // group heights clamp to the tile rows
+            for (const Cand& o : cands)
+                dup = dup || (o.pl.k_step == cd.pl.k_step && o.pl.stages == cd.pl.stages &&
+                              o.pl.group_m == cd.pl.group_m);
+            if (!dup) cands.push_back(cd);
+        }
+    }
+    if (cands.empty()) return TGEMM_ERR_UNSUPPORTED;
+    const int nc = (int)cands.size();
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    // one event between consecutive launches; every round runs every candidate
+    // once (interleaved, so clock drift under load spreads over all of them)
+    std::vector<hipEvent_t> ev((size_t)nc * rounds + 1, nullptr);
+    hipError_t e = hipSuccess;
+    for (auto& x : ev)
+        if (e == hipSuccess) e = hipEventCreate(&x);
+    for (int i = 0; i < nc && e == hipSuccess && rc == TGEMM_OK; ++i)       // warm-up launch of each
+        rc = tg::launch(cands[i].pl, cands[i].fn, A, B, C, c_type, alpha, bias, act, stream);
+    if (e == hipSuccess && rc == TGEMM_OK) e = hipEventRecord(ev[0], st);
+    for (int r = 0; r < rounds && e == hipSuccess && rc == TGEMM_OK; ++r)
+        for (int i = 0; i < nc && e == hipSuccess && rc == TGEMM_OK; ++i) {
+            rc = tg::launch(cands[i].pl, cands[i].fn, A, B, C, c_type, alpha, bias, act, stream);
+            if (rc == TGEMM_OK) e = hipEventRecord(ev[(size_t)r * nc + i + 1], st);
+        }
+    if (e == hipSuccess && rc == TGEMM_OK) e = hipEventSynchronize(ev.back());
+    std::vector<float> med(nc, 0.f);
+    for (int i = 0; i < nc && e == hipSuccess && rc == TGEMM_OK; ++i) {
+        std::vector<float> t(rounds);
+        for (int r = 0; r < rounds && e == hipSuccess; ++r) {
+            const size_t j = (size_t)r * nc + i;
+            e = hipEventElapsedTime(&t[r], ev[j], ev[j + 1]);
+        }
+        std::sort(t.begin(), t.end());
+        med[i] = t[rounds / 2];
+    }
+    for (auto& x : ev)
+        if (x) (void)hipEventDestroy(x);
+    if (rc != TGEMM_OK) return rc;
+    if (e != hipSuccess) {
+        tg::g_last_hip_error = (int)e;
+        return TGEMM_ERR_HIP;
+    }
+    int best = 0;
+    for (int i = 1; i < nc; ++i)
+        if (med[i] < med[best]) best = i;
+    tg::TuneKey key;
+    if (!tg::tune_key(base, &key)) return TGEMM_ERR_HIP;
+    const tg::Plan& bp = cands[best].pl;
+    {
+        std::lock_guard<std::mutex> lock(tg::g_tune_mu);
+        tg::g_tuned[key] = tg::TuneChoice{bp.k_step, bp.stages, bp.group_m, bp.num_xcd};
+        tg::g_tuned_count.store((int)tg::g_tuned.size(), std::memory_order_release);
+    }
+    if (info) {
+        info[0] = bp.k_step;
+        info[1] = bp.stages;
+        info[2] = bp.group_m;
+        info[3] = bp.num_xcd;
+        info[4] = (int64_t)(med[best] * 1e6f);   // median launch time, ns
+        info[5] = nc;
+    }
+    return TGEMM_OK;
+}
+
+extern "C" int tgemm_tuning_entries(void) { return tg::g_tuned_count.load(std::memory_order_acquire); }
+
+extern "C" void tgemm_tuning_clear(void) {
+    std::lock_guard<std::mutex> lock(tg::g_tune_mu);
+    tg::g_tuned.clear();
+    tg::g_tuned_count.store(0, std::memory_order_release);
 }
 
 extern "C" const char* tgemm_status_string(int status) {

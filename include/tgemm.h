@@ -164,6 +164,47 @@ int tgemm_gemm_config(int64_t M, int64_t N, int64_t K,
                       int force_generic, int group_m, int num_xcd,
                       int k_step, int stages);
 
+/*
+ * Runtime tuning, per problem shape (page 2, "CUDA 13.1 new feature: the Tile
+ * programming model", section 7.4 "Autotuning": several tile configurations
+ * are tried, the fastest is kept per problem shape, and later calls reuse it
+ * at no cost).
+ *
+ * tgemm_tune_gemm takes the arguments of tgemm_gemm and runs the problem on
+ * the caller's buffers under each launch choice that leaves the result
+ * unchanged bit for bit: the K step and LDS ring depth of the direct-to-LDS
+ * pipeline (those built for the types) and a raster group height of 4, 8 or
+ * 16 tile rows. Each choice runs once to warm up, then `rounds` times (1..100),
+ * interleaved with the others, timed with HIP events on `stream`; the choice
+ * with the smallest median time is recorded for the problem's key on the
+ * current device. The key is everything that selects a kernel: M, N, K, the
+ * three strides, b_layout, both types, whether an epilogue is requested, and
+ * the alignment classes of A, B and C. From then on, tgemm_gemm, tgemm_f16,
+ * the *_config calls with all five launch choices 0, and the plan queries use
+ * the recorded choice for that key.
+ *
+ * Synchronizes `stream` (not for use under graph capture). C holds the
+ * product on return, as after tgemm_gemm (every choice computes the same
+ * bits). Creates and destroys HIP events; allocates no device memory.
+ * info: NULL or 6 values: the chosen k_step, stages, group_m, num_xcd, its
+ * median launch time in ns, and the number of choices tried.
+ * Returns the argument errors of tgemm_gemm (nothing run), TGEMM_ERR_INVALID
+ * for rounds outside 1..100, or TGEMM_ERR_HIP. M == 0 or N == 0: nothing is
+ * run or recorded (info all 0). The table is shared by all threads.
+ */
+int tgemm_tune_gemm(int64_t M, int64_t N, int64_t K,
+                    int ab_type, const void* A, int64_t lda,
+                    const void* B, int64_t ldb, int b_layout,
+                    int c_type, void* C, int64_t ldc,
+                    float alpha, const float* bias, int act,
+                    void* stream, int rounds, int64_t* info);
+
+/* Number of problem keys with a recorded choice (all devices). */
+int tgemm_tuning_entries(void);
+
+/* Forget every recorded choice; later calls use the default launch choices. */
+void tgemm_tuning_clear(void);
+
 /* Human-readable text of a TGEMM_* status code (static storage). */
 const char* tgemm_status_string(int status);
 

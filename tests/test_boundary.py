@@ -295,3 +295,24 @@ def test_header_declares_type_and_activation_values():
                       ("TGEMM_ACT_RELU", 1)):
         assert re.search(rf"{name}\s*=\s*{val}\b", src)
         assert getattr(tg, name) == val
+
+
+# ------------------------------------------------------------ runtime tuning --
+
+def test_tuning_rejects_bad_arguments_without_gpu():
+    lib = tg.load()
+    assert tg.tuning_entries() == 0
+    # argument errors of tgemm_gemm, and rounds outside 1..100: nothing runs
+    assert tg.tgemm_tune_gemm(4, 4, 4, "f16", PA, 3, PB, 4, "KxN", "f16", PC, 4)[0] == tg.TGEMM_ERR_INVALID
+    assert tg.tgemm_tune_gemm(4, 4, 4, "f16", PA, 4, PB, 4, "KxN", "f32", PC + 2, 4)[0] == tg.TGEMM_ERR_INVALID
+    assert tg.tgemm_tune_gemm(4, 4, 4, "f16", PA, 4, PB, 4, "KxN", "f16", PC, 4, rounds=0)[0] == \
+        tg.TGEMM_ERR_INVALID
+    assert tg.tgemm_tune_gemm(4, 4, 4, "f16", PA, 4, PB, 4, "KxN", "f16", PC, 4, rounds=101)[0] == \
+        tg.TGEMM_ERR_INVALID
+    # empty output: nothing to tune, nothing recorded
+    rc, info = tg.tgemm_tune_gemm(0, 4, 4, "bf16", PA, 4, PB, 4, "KxN", "f32", PC, 4)
+    assert rc == tg.TGEMM_OK and all(v == 0 for v in info.values())
+    assert tg.tuning_entries() == 0
+    tg.tuning_clear()
+    assert tg.tuning_entries() == 0
+    assert lib.tgemm_tune_gemm(0, 4, 4, 0, PA, 4, PB, 4, 0, 0, PC, 4, 1.0, None, 0, None, 5, None) == tg.TGEMM_OK

@@ -1,0 +1,91 @@
+"""GPU tests of runtime tuning: the tuner records a launch choice per problem
+key, later automatic calls use it (visible in the plan query), and the result
+is the same bits as without tuning and within the oracle's tolerance."""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import dense_tiled_gemm_tgemm_amd as tg  # noqa: E402
+from dense_tiled_gemm_tgemm_amd import inputs  # noqa: E402
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(autouse=True)
+def _clean_table():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    tg.tuning_clear()
+    yield
+    torch.cuda.synchronize()
+    tg.tuning_clear()
+
+
+def _dev16(bits, dt):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(DEV).view(dt)
+
+
+def _plan(A, B, C, lay, ab, ct, **kw):
+    M, K = A.shape
+    N = C.shape[1]
+    return tg.tgemm_plan_gemm(M, N, K, ab, A.data_ptr(), A.stride(0), B.data_ptr(), B.stride(0), lay, ct,
+                              C.data_ptr(), C.stride(0), **kw)
+
+
+def test_tuned_choice_is_recorded_used_and_changes_no_bits():
+    print("case tuning f16 NxK", flush=True)
+    M, N, K = 2304, 2560, 1000
+    A = _dev16(inputs.random_f16((M, K), 1).view(np.uint16), torch.float16)
+    B = _dev16(inputs.random_f16((N, K), 2).view(np.uint16), torch.float16)
+    base = tg.mm(A, B, "NxK")
+    C = torch.empty_like(base)
+    rc0, plan0 = _plan(A, B, C, "NxK", "f16", "f16")
+    assert rc0 == 0 and (plan0["bk"], plan0["stages"], plan0["group_m"]) == (64, 2, 8)
+    C, chosen = tg.tune(A, B, "NxK", out=C, rounds=3)
+    torch.cuda.synchronize()
+    print(f"  chosen {chosen}", flush=True)
+    assert torch.equal(C.view(torch.int16), base.view(torch.int16))
+    assert tg.tuning_entries() == 1
+    assert chosen["candidates"] == 15 and chosen["median_ns"] > 0
+    assert (chosen["k_step"], chosen["stages"]) in {(64, 2), (32, 2), (32, 3), (32, 4), (32, 5)}
+    assert chosen["group_m"] in (4, 8, 16) and chosen["num_xcd"] == 8
+    rc, plan = _plan(A, B, C, "NxK", "f16", "f16")
+    assert (plan["bk"], plan["stages"], plan["group_m"], plan["num_xcd"]) == \
+        (chosen["k_step"], chosen["stages"], chosen["group_m"], chosen["num_xcd"])
+    # another key (other types) is not affected
+    C32 = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    rc, plan32 = _plan(A, B, C32, "NxK", "f16", "f32")
+    assert (plan32["bk"], plan32["stages"], plan32["group_m"]) == (64, 2, 8)
+    # the tuned automatic call gives the same bits
+    again = tg.mm(A, B, "NxK")
+    torch.cuda.synchronize()
+    assert torch.equal(again.view(torch.int16), base.view(torch.int16))
+    tg.tuning_clear()
+    rc, plan = _plan(A, B, C, "NxK", "f16", "f16")
+    assert plan == plan0
+
+
+def test_tuning_with_epilogue_and_bf16(oracle_mod):
+    print("case tuning bf16 -> f32 epilogue", flush=True)
+    M, N, K = 2600, 1300, 4099          # 11 tile rows: group heights 4, 8 and 11
+    A = inputs.random_bf16((M, K), 3)
+    B = inputs.random_bf16((K, N), 4)
+    bias = inputs.random_bias(N, 5)
+    Ad, Bd = _dev16(A, torch.bfloat16), _dev16(B, torch.bfloat16)
+    bd = torch.from_numpy(bias).to(DEV)
+    base = tg.gemm(Ad, Bd, "KxN", out_dtype=torch.float32, alpha=0.25, bias=bd, act="relu")
+    C, chosen = tg.tune(Ad, Bd, "KxN", out_dtype=torch.float32, alpha=0.25, bias=bd, act="relu", rounds=3)
+    torch.cuda.synchronize()
+    print(f"  chosen {chosen}", flush=True)
+    # bfloat16 -> fp32 with an epilogue builds the default ring depth of each K step
+    assert chosen["candidates"] == 6 and (chosen["k_step"], chosen["stages"]) in {(64, 2), (32, 4)}
+    assert torch.equal(C, base)
+    got = tg.gemm(Ad, Bd, "KxN", out_dtype=torch.float32, alpha=0.25, bias=bd, act="relu").cpu().numpy()
+    I, J = inputs.sample_points(M, N, 4096, 6)
+    ref, tol = oracle_mod.gemm_ex(A, B, "KxN", "bf16", 0.25, bias, "relu", I=I, J=J)
+    res = oracle_mod.check_ex(got[I, J], "f32", ref, tol)
+    assert res["nfail"] == 0, res
+    assert np.array_equal(got, base.cpu().numpy())
