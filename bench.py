@@ -276,7 +276,7 @@ def main():
     log(f"bench: {args.steps} steps, region {region_ms:.3f} ms (host wall {wall * 1e3:.3f} ms), "
         f"per launch mean {mean_ms:.4f} min {min(per_launch_ms):.4f} max {max(per_launch_ms):.4f} ms")
 
-    metric = METRIC if tag == "" else (
+    metric = METRIC if (tag == "" and name == inputs.HEADLINE) else (
         f"GEMM TFLOPS (2MNK/s) at {w.M}x{w.N}x{w.K}, {args.ab} in, {args.out} out"
         f"{', alpha/bias/relu epilogue' if args.epilogue else ''} on 1 MI355X")
     rec = {
