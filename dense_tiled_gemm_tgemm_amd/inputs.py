@@ -89,7 +89,7 @@ def to_bf16_bits(x) -> np.ndarray:
 def make_inputs(w: Workload, ab_type: str = "f16"):
     """(A, B) as C-contiguous arrays: A is (M, K), B is ``w.b_shape``.
     ab_type "f16": float16 arrays; "bf16": uint16 bfloat16 bit patterns drawn
-    from the same seeded values."""
+    from the same seeded values; "f32": float32 arrays of the same values."""
     rng = np.random.default_rng(w.seed)
     if ab_type == "f16":
         A = _draw(rng, w.a_dist, (w.M, w.K))
@@ -97,6 +97,9 @@ def make_inputs(w: Workload, ab_type: str = "f16"):
     elif ab_type == "bf16":
         A = to_bf16_bits(_draw64(rng, w.a_dist, (w.M, w.K)))
         B = to_bf16_bits(_draw64(rng, w.b_dist, w.b_shape))
+    elif ab_type == "f32":
+        A = _draw64(rng, w.a_dist, (w.M, w.K)).astype(np.float32)
+        B = _draw64(rng, w.b_dist, w.b_shape).astype(np.float32)
     else:
         raise ValueError(f"unknown input type {ab_type!r}")
     return A, B
@@ -105,6 +108,11 @@ def make_inputs(w: Workload, ab_type: str = "f16"):
 def random_bf16(shape, seed: int, dist=("uniform", -1.0, 1.0)) -> np.ndarray:
     """Seeded bfloat16 bit patterns (uint16) for small ad-hoc shapes."""
     return to_bf16_bits(_draw64(np.random.default_rng(seed), dist, shape))
+
+
+def random_f32(shape, seed: int, dist=("uniform", -1.0, 1.0)) -> np.ndarray:
+    """Seeded binary32 array for small ad-hoc shapes."""
+    return _draw64(np.random.default_rng(seed), dist, shape).astype(np.float32)
 
 
 def random_bias(n: int, seed: int, scale: float = 1.0) -> np.ndarray:

@@ -221,15 +221,28 @@ def _u16(x) -> np.ndarray:
     raise TypeError(f"expected float16 or uint16 bit patterns, got {x.dtype}")
 
 
+def _operand(x, ab: int) -> np.ndarray:
+    """Operand bit patterns of type code ab: uint16 for 0/1, uint32 for 2 (float32 arrays are viewed)."""
+    if ab != 2:
+        return _u16(x)
+    x = np.asarray(x)
+    if x.dtype == np.float32:
+        return x.view(np.uint32)
+    if x.dtype == np.uint32:
+        return x
+    raise TypeError(f"expected float32 or uint32 bit patterns, got {x.dtype}")
+
+
 def gemm_ex(A, B, b_layout, ab_type="f16", alpha=1.0, bias=None, act="none", I=None, J=None):
     """fp64 reference of act(alpha * sum_k A[i,k] B[k,j] + bias[j]) and its
     tolerance magnitude |alpha| * sum_k |A[i,k] B[k,j]| + |bias[j]|.
 
-    A, B: uint16 bit patterns of ``ab_type`` (float16 arrays accepted for
-    binary16). bias: None or N float32 values. I, J: None for the full M x N
-    output (returned as 2-D arrays), else the selected elements (1-D)."""
-    A = _u16(A)
-    B = _u16(B)
+    A, B: bit patterns of ``ab_type`` (uint16 for "f16" / "bf16", float16
+    arrays accepted for binary16; float32 or uint32 for "f32"). bias: None or
+    N float32 values. I, J: None for the full M x N output (returned as 2-D
+    arrays), else the selected elements (1-D)."""
+    A = _operand(A, _TYPES[ab_type])
+    B = _operand(B, _TYPES[ab_type])
     lay = _LAYOUTS[b_layout]
     M, K, lda = _rows(A)
     if lay == 0:

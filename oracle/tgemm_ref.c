@@ -212,16 +212,18 @@ int64_t ref_check_f16(int64_t n, const uint16_t* got, const double* ref, const d
  * Extended operation: other element types and a fused epilogue.
  *
  * Element types (the pages' tile kernels take the element type as a
- * parameter: page 1, section 6 and its launcher; page 2, section 7; page 4,
- * section 2.4.9.1 accumulates in fp32 and stores an fp32 C):
+ * parameter: page 1, section 6 and its launcher, which picks tiles for 2-byte
+ * and 4-byte inputs; page 2, section 7; page 4, section 2.4.9.1 accumulates in
+ * fp32 and stores an fp32 C):
  *   type 0: IEEE 754 binary16 (decoded by ref_half_to_double above);
  *   type 1: bfloat16, the upper half of a binary32: sign (1 bit), biased
  *           exponent e (8 bits), fraction f (7 bits). e == 0: f * 2^-133;
  *           0 < e < 255: (128 + f) * 2^(e - 134); e == 255: inf / NaN;
  *   type 2: IEEE 754 binary32: sign, e (8 bits), f (23 bits). e == 0:
  *           f * 2^-149; 0 < e < 255: (2^23 + f) * 2^(e - 150); e == 255:
- *           inf / NaN (output only).
- * Products of two binary16 or two bfloat16 values are exact in fp64.
+ *           inf / NaN.
+ * Products of two values of any one of these types are exact in fp64 (at
+ * most 24 + 24 significant bits).
  *
  * Epilogue (the reading of "scale, bias and activation on store"):
  *   C[i][j] = act(alpha * sum_k A[i][k] B[k][j] + bias[j]),
@@ -287,40 +289,45 @@ static double overflow_threshold(int type) {
     return ldexp(2.0 - ldexp(1.0, -24), 127);                    /* max f32 + half ulp */
 }
 
-static double* decode_a_t(int64_t M, int64_t K, const uint16_t* A, int64_t lda, int type) {
+/* Element p of an operand of the given type (16-bit patterns for types 0
+ * and 1, 32-bit patterns for type 2). */
+static double elem_at(const void* X, int64_t p, int type) {
+    return type == 2 ? ref_f32_to_double(((const uint32_t*)X)[p]) : decode_elem(((const uint16_t*)X)[p], type);
+}
+
+static double* decode_a_t(int64_t M, int64_t K, const void* A, int64_t lda, int type) {
     double* a = (double*)malloc((size_t)(M * K > 0 ? M * K : 1) * sizeof(double));
     if (!a) return NULL;
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < M; ++i)
-        for (int64_t k = 0; k < K; ++k) a[i * K + k] = decode_elem(A[i * lda + k], type);
+        for (int64_t k = 0; k < K; ++k) a[i * K + k] = elem_at(A, i * lda + k, type);
     return a;
 }
 
-static double* decode_bt_t(int64_t N, int64_t K, const uint16_t* B, int64_t ldb, int b_layout, int type) {
+static double* decode_bt_t(int64_t N, int64_t K, const void* B, int64_t ldb, int b_layout, int type) {
     double* bt = (double*)malloc((size_t)(N * K > 0 ? N * K : 1) * sizeof(double));
     if (!bt) return NULL;
 #pragma omp parallel for schedule(static)
     for (int64_t j = 0; j < N; ++j)
-        for (int64_t k = 0; k < K; ++k) {
-            const uint16_t h = (b_layout == 0) ? B[k * ldb + j] : B[j * ldb + k];
-            bt[j * K + k] = decode_elem(h, type);
-        }
+        for (int64_t k = 0; k < K; ++k)
+            bt[j * K + k] = elem_at(B, (b_layout == 0) ? k * ldb + j : j * ldb + k, type);
     return bt;
 }
 
 /*
  * Reference values of the extended operation at a set of output elements
  * (npts < 0: all, row-major; else (I[p], J[p])). ab_type: 0 binary16,
- * 1 bfloat16 for both operands. bias: N floats or NULL. act: 0 none,
+ * 1 bfloat16, 2 binary32 for both operands (strides in elements of that
+ * type). bias: N floats or NULL. act: 0 none,
  * 1 rectifier. ref[p] and tol_mag[p] as described above. Returns 0, or -1
  * on bad arguments or allocation failure.
  */
 int ref_gemm_ex(int64_t M, int64_t N, int64_t K,
-                const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int b_layout, int ab_type,
+                const void* A, int64_t lda, const void* B, int64_t ldb, int b_layout, int ab_type,
                 double alpha, const float* bias, int act,
                 int64_t npts, const int64_t* I, const int64_t* J, double* ref, double* tol_mag) {
     if (M < 0 || N < 0 || K < 0 || (b_layout != 0 && b_layout != 1)) return -1;
-    if ((ab_type != 0 && ab_type != 1) || (act != 0 && act != 1)) return -1;
+    if (ab_type < 0 || ab_type > 2 || (act != 0 && act != 1)) return -1;
     if (npts > 0 && (!I || !J)) return -1;
     double* a = decode_a_t(M, K, A, lda, ab_type);
     double* bt = decode_bt_t(N, K, B, ldb, b_layout, ab_type);

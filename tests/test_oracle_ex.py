@@ -262,3 +262,33 @@ def test_bf16_input_rounding_is_nearest_even():
     pattern, values between round to the nearer one."""
     x = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -8 + 2.0 ** -20, -2.0 - 2.0 ** -7])
     assert [int(v) for v in inputs.to_bf16_bits(x)] == [0x3F80, 0x3F82, 0x3F81, 0xC000]
+
+
+# ------------------------------------------------------------ binary32 inputs --
+
+@pytest.mark.parametrize("b_layout", ["KxN", "NxK"])
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (3, 5, 7), (6, 4, 9)])
+def test_f32_inputs_brute_force_with_epilogue(oracle_mod, M, N, K, b_layout):
+    """binary32 operands over a wide exponent range: exact rational answer."""
+    seed = 2000 + M * 100 + N * 10 + K
+    rng = np.random.default_rng(seed)
+    A = (rng.uniform(-2, 2, (M, K)) * 2.0 ** rng.integers(-40, 40, (M, K))).astype(np.float32)
+    Bshape = (K, N) if b_layout == "KxN" else (N, K)
+    B = (rng.uniform(-2, 2, Bshape) * 2.0 ** rng.integers(-40, 40, Bshape)).astype(np.float32)
+    bias = inputs.random_bias(N, seed, scale=4.0)
+    ref, mag = oracle_mod.gemm_ex(A, B, b_layout, "f32", 1.25, bias, "relu")
+    eref, emag = _exact_ex(A.view(np.uint32), B.view(np.uint32), b_layout, oracle_mod.f32_to_double, 1.25, bias,
+                           "relu")
+    for i in range(M):
+        for j in range(N):
+            bound = Fraction((K + 2) * 2.0 ** -52) * emag[i][j]
+            assert abs(Fraction(ref[i, j]) - eref[i][j]) <= bound, (i, j)
+
+
+def test_f32_inputs_reduce_to_f16_product(oracle_mod):
+    """binary16 values widened to binary32 give the binary16 product exactly."""
+    A = inputs.random_f16((13, 50), 81)
+    B = inputs.random_f16((19, 50), 82)
+    r16, a16 = oracle_mod.gemm(A, B, "NxK")
+    r32, a32 = oracle_mod.gemm_ex(A.astype(np.float32), B.astype(np.float32), "NxK", "f32")
+    assert np.array_equal(r16, r32) and np.array_equal(a16, a32)
