@@ -30,7 +30,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "fp16 GEMM TFLOPS (2MNK/s) at 8192³ on 1 MI355X; % of MFMA peak"
-PEAK_F16_TFLOPS = 2516.6      # 256 CUs x 2.4 GHz x 4096 dense fp16 flop/clk/CU
+PEAK_F16_TFLOPS = 2516.6      # 256 CUs x 2.4 GHz x 4096 dense fp16 flop/clk/CU (bfloat16 the same)
+PEAK_F32_TFLOPS = 157.3       # dense fp32 matrix rate (256 flop/clk/CU)
 KERNEL_SOURCES = ("dense_tiled_gemm_tgemm_amd/csrc/tgemm_kernels.h", "dense_tiled_gemm_tgemm_amd/csrc/tgemm_inst.hip",
                   "dense_tiled_gemm_tgemm_amd/csrc/tgemm.hip", "dense_tiled_gemm_tgemm_amd/csrc/tgemm_plan.h")
 EPI_ALPHA = 0.5
@@ -111,7 +112,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default=None)
-    ap.add_argument("--ab", choices=("f16", "bf16"), default="f16", help="operand type")
+    ap.add_argument("--ab", choices=("f16", "bf16", "f32"), default="f16", help="operand type")
     ap.add_argument("--out", choices=("f16", "bf16", "f32"), default="f16", help="output type")
     ap.add_argument("--epilogue", action="store_true", help="alpha = 0.5, seeded fp32 bias, rectifier")
     ap.add_argument("--tune", action="store_true",
@@ -194,10 +195,14 @@ def main():
     dev = torch.device("cuda:0")
     tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}
     A, B = inputs.make_inputs(w, args.ab)
-    A = A.view(np.uint16)
-    B = B.view(np.uint16)
-    Ad = torch.from_numpy(A.view(np.int16)).to(dev).view(tdt[args.ab])
-    Bd = torch.from_numpy(B.view(np.int16)).to(dev).view(tdt[args.ab])
+    if args.ab == "f32":
+        Ad = torch.from_numpy(A).to(dev)
+        Bd = torch.from_numpy(B).to(dev)
+    else:
+        A = A.view(np.uint16)
+        B = B.view(np.uint16)
+        Ad = torch.from_numpy(A.view(np.int16)).to(dev).view(tdt[args.ab])
+        Bd = torch.from_numpy(B.view(np.int16)).to(dev).view(tdt[args.ab])
     Cd = torch.empty((w.M, w.N), dtype=tdt[args.out], device=dev)
     alpha, bias_np, act = 1.0, None, "none"
     if args.epilogue:
@@ -273,6 +278,7 @@ def main():
     value = flops * args.steps / (region_ms / 1e3) / 1e12
     mean_ms = float(np.mean(per_launch_ms))
     achieved = flops / (mean_ms / 1e3) / 1e12
+    peak = PEAK_F32_TFLOPS if args.ab == "f32" else PEAK_F16_TFLOPS
     log(f"bench: {args.steps} steps, region {region_ms:.3f} ms (host wall {wall * 1e3:.3f} ms), "
         f"per launch mean {mean_ms:.4f} min {min(per_launch_ms):.4f} max {max(per_launch_ms):.4f} ms")
 
@@ -300,9 +306,9 @@ def main():
         "roofline": {
             "bound": "mfma",
             "achieved": round(achieved, 2),
-            "peak": PEAK_F16_TFLOPS,
+            "peak": peak,
             "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_F16_TFLOPS, 4),
+            "frac": round(achieved / peak, 4),
             "traffic": traffic_from_profiles(name, tag),
         },
     }

@@ -275,11 +275,11 @@ def tune(A, B, b_layout: str = "KxN", out=None, out_dtype=None, alpha: float = 1
 def gemm(A, B, b_layout: str = "KxN", out=None, out_dtype=None, alpha: float = 1.0, bias=None, act: str = "none",
          stream=None, force_generic: int = 0, group_m: int = 0, num_xcd: int = 0, k_step: int = 0,
          stages: int = 0, _tune_rounds: int = 0):
-    """C = act(alpha * A @ B + bias) for float16 or bfloat16 device tensors
-    (fp32 accumulation and epilogue in the kernel).
+    """C = act(alpha * A @ B + bias) for float16, bfloat16 or float32 device
+    tensors (fp32 accumulation and epilogue in the kernel).
 
     A: (M, K), B: (K, N) for "KxN" or (N, K) for "NxK", both of one dtype
-    (float16 or bfloat16). out: optional (M, N) float16 / bfloat16 / float32
+    (float16, bfloat16 or float32). out: optional (M, N) float16 / bfloat16 / float32
     tensor with unit column stride; allocated with torch.empty as `out_dtype`
     (default: A's dtype) when None. bias: None or an (N,) float32 device
     tensor with unit stride. act: "none" or "relu".
@@ -288,8 +288,8 @@ def gemm(A, B, b_layout: str = "KxN", out=None, out_dtype=None, alpha: float = 1
     for t, name in ((A, "A"), (B, "B")):
         if not t.is_cuda:
             raise ValueError(f"{name} must be a device tensor")
-    if A.dtype != B.dtype or A.dtype not in (torch.float16, torch.bfloat16):
-        raise TypeError(f"A and B must both be float16 or both bfloat16, got {A.dtype} and {B.dtype}")
+    if A.dtype != B.dtype or A.dtype not in (torch.float16, torch.bfloat16, torch.float32):
+        raise TypeError(f"A and B must be of one dtype among float16, bfloat16, float32; got {A.dtype} and {B.dtype}")
     lay = _LAYOUT[b_layout]
     M, K = A.shape
     if lay == TGEMM_B_KxN:

@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libtgemm.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # (input type, output type, epilogue) combinations: 0 binary16, 1 bfloat16, 2 fp32
-COMBOS = [(ab, ct, epi) for ab in (0, 1) for ct in (0, 1, 2) for epi in (0, 1)]
+COMBOS = [(ab, ct, epi) for ab in (0, 1, 2) for ct in (0, 1, 2) for epi in (0, 1)]
 
 FLAGS = [
     "-O3", "-std=c++17", "--offload-arch=gfx950", "-fPIC",

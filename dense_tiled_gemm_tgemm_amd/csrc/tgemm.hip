@@ -28,6 +28,9 @@ static const void* pick_kernel(const Plan& pl) {
     TG_PICK(1, 0)
     TG_PICK(1, 1)
     TG_PICK(1, 2)
+    TG_PICK(2, 0)
+    TG_PICK(2, 1)
+    TG_PICK(2, 2)
 #undef TG_PICK
     return nullptr;
 }
@@ -345,7 +348,8 @@ static void fill_info(const tg::Plan& pl, int64_t* info) {
     info[6] = pl.num_xcd;
     info[7] = tg::NTHREADS;
     info[8] = pl.stages;
-    info[9] = (int64_t)pl.stages * 2 * 256 * pl.k_step * 2;   // LDS bytes per workgroup
+    // LDS bytes per workgroup: stages x (A block + B block) x 256 rows x K step
+    info[9] = (int64_t)pl.stages * 2 * 256 * pl.k_step * (pl.ab_type == TGEMM_F32 ? 4 : 2);
 }
 
 extern "C" int tgemm_plan_gemm(int64_t M, int64_t N, int64_t K, int ab_type, const void* A, int64_t lda,

@@ -1,7 +1,7 @@
 // Kernel instantiations for one (input type, output type, epilogue), chosen
-// when this file is compiled: TG_AB (0 binary16, 1 bfloat16 inputs), TG_CT
-// (0 binary16, 1 bfloat16, 2 fp32 output), TG_EPI (0 sums stored as they are,
-// 1 scale, bias and activation applied). The library links one object per
+// when this file is compiled: TG_AB (0 binary16, 1 bfloat16, 2 binary32
+// inputs), TG_CT (0 binary16, 1 bfloat16, 2 fp32 output), TG_EPI (0 sums
+// stored as they are, 1 scale, bias and activation applied). The library links one object per
 // combination, so the combinations compile in parallel.
 #include "tgemm_kernels.h"
 
@@ -39,14 +39,25 @@ const void* rs_ptr(bool vec) {
                : reinterpret_cast<const void*>(&tgemm_rs_kernel<kTy, NXK, false>);
 }
 
+template <int NXK>
+const void* f32in_ptr(bool vec) {
+    return vec ? reinterpret_cast<const void*>(&tgemm_f32in_kernel<kTy, NXK, true>)
+               : reinterpret_cast<const void*>(&tgemm_f32in_kernel<kTy, NXK, false>);
+}
+
 }  // namespace
 
 template <>
 const void* kernel_for<TG_AB, TG_CT, (TG_EPI != 0)>(const Plan& pl) {
     const bool nxk = (pl.variant & kLayoutNxK) != 0;
-    if (pl.variant & kDma) return nxk ? dma_ptr<1>(pl.k_step, pl.stages) : dma_ptr<0>(pl.k_step, pl.stages);
     const bool vec = (pl.variant & kVecAB) != 0;
-    return nxk ? rs_ptr<1>(vec) : rs_ptr<0>(vec);
+    if constexpr (TG_AB == 2) {
+        // binary32 operands: one kernel family, staged through registers
+        return nxk ? f32in_ptr<1>(vec) : f32in_ptr<0>(vec);
+    } else {
+        if (pl.variant & kDma) return nxk ? dma_ptr<1>(pl.k_step, pl.stages) : dma_ptr<0>(pl.k_step, pl.stages);
+        return nxk ? rs_ptr<1>(vec) : rs_ptr<0>(vec);
+    }
 }
 
 }  // namespace tg

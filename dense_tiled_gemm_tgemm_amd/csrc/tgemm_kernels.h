@@ -50,11 +50,14 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-// Kernel type code TY: input type (bit 0: 0 binary16, 1 bfloat16), output
-// type (bits 1-2: 0 binary16, 1 bfloat16, 2 fp32), epilogue (bit 3: scale,
-// bias and activation applied; clear: the sums are stored as they are).
-constexpr int ty_code(int ab, int ct, bool epi) { return ab | (ct << 1) | (epi ? 8 : 0); }
-constexpr int ab_of(int ty) { return ty & 1; }
+// Kernel type code TY: input type (bit 0: bfloat16, bit 4: binary32, neither:
+// binary16), output type (bits 1-2: 0 binary16, 1 bfloat16, 2 fp32),
+// epilogue (bit 3: scale, bias and activation applied; clear: the sums are
+// stored as they are).
+constexpr int ty_code(int ab, int ct, bool epi) {
+    return (ab == 1 ? 1 : 0) | (ct << 1) | (epi ? 8 : 0) | (ab == 2 ? 16 : 0);
+}
+constexpr int ab_of(int ty) { return (ty & 16) ? 2 : (ty & 1); }
 constexpr int ct_of(int ty) { return (ty >> 1) & 3; }
 constexpr bool epi_of(int ty) { return (ty & 8) != 0; }
 
@@ -1003,6 +1006,190 @@ tgemm_dma_kernel(Args a) {
     wait_vmcnt<0>();
 }
 
+// ---------------------------------------------------------------------------
+// binary32 operands. Page 1's launcher gives 4-byte inputs a tile
+// configuration of their own; here the output tile and the wave grid stay
+// those of the 16-bit kernels (256 x 256, 2 x 2 waves of 128 x 128 as 8 x 8
+// blocks of 16 x 16 fp32 accumulators, so store_c is shared) and the K step
+// is 16 floats. The inner product is v_mfma_f32_16x16x4_f32 (one float of
+// each operand per lane, 32 cycles): at 1/16 of the 16-bit rate per
+// instruction, the operand traffic per MFMA is small, so operands are staged
+// through registers (any stride and alignment of 4 bytes) into a 2-stage LDS
+// ring.
+//
+// LDS: per stage an A block and a B block of 256 rows x 4 chunks of 4 floats
+// (k 4c .. 4c+3 in chunk c), chunk c of row r at slot r * 4 + (c ^ f(r)),
+// f(r) = (r ^ (r >> 2)) & 3 (the 64-byte-row map of Lds<32>: conflict-free
+// fragment reads and chunk writes).
+//
+// Fragments: lane l (row l mod 16 of a 16-row block, group g = l / 16) reads
+// chunk g, i.e. k = k0 + 4g + 0..3. MFMA e (0..3) takes element e of the A
+// and B chunks: its four lane groups cover k0 + e, k0 + 4 + e, k0 + 8 + e,
+// k0 + 12 + e, so the four MFMAs together sum the 16 k of the step.
+// ---------------------------------------------------------------------------
+constexpr int kF32Ks = kF32KStep;               // K step (floats)
+using LdsF = Lds<32>;                           // 4 chunks of 16 bytes per row
+static_assert(LdsF::kCpr == 4 && LdsF::kBlock == 1024, "fp32 LDS blocks: 256 rows x 4 chunks");
+
+// Four floats at p[0..nv-1]; the rest read as zero.
+__device__ __forceinline__ u32x4 load4_f32(const uint32_t* __restrict__ p, int nv) {
+    unsigned w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) w[q] = (q < nv) ? p[q] : 0u;
+    return u32x4{w[0], w[1], w[2], w[3]};
+}
+
+// K-contiguous operand (A, or B stored N x K): thread t loads chunk (t & 3) of
+// rows (t >> 2) + 64 p, p = 0..3, for k = k0 .. k0 + 15. MASK: rows >= nrows
+// and k >= K read as zero (page 4, section 2.4.6.1.3).
+template <bool VEC, bool MASK>
+__device__ __forceinline__ void f32_load_kc(u32x4 (&r)[4], const uint32_t* __restrict__ X, int64_t ld, int nrows,
+                                            int K, int row0, int k0, int tid) {
+    const int gk = k0 + (tid & 3) * 4;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int gr = row0 + (tid >> 2) + 64 * p;
+        if (!MASK) {
+            const uint32_t* src = X + (int64_t)gr * ld + gk;
+            r[p] = VEC ? *(const u32x4*)src : load4_f32(src, 4);
+        } else {
+            const int rem = K - gk;
+            const int nv = (gr < nrows) ? (rem < 0 ? 0 : (rem > 4 ? 4 : rem)) : 0;
+            const int grc = gr < nrows ? gr : nrows - 1;
+            const uint32_t* src = X + (int64_t)grc * ld + (nv > 0 ? gk : 0);
+            r[p] = (VEC && nv == 4) ? *(const u32x4*)src : load4_f32(src, nv);
+        }
+    }
+}
+
+__device__ __forceinline__ void f32_store_kc(u32x4* __restrict__ s, const u32x4 (&r)[4], int tid) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) s[LdsF::slot((tid >> 2) + 64 * p, tid & 3)] = r[p];
+}
+
+// B stored K x N: thread t owns the 4 x 4 block k = k0 + 4 (t >> 6) + 0..3,
+// n = n0 + 4 (t & 63) + 0..3, loaded as four 16-byte row pieces.
+template <bool VEC, bool MASK>
+__device__ __forceinline__ void f32_load_kxn(u32x4 (&r)[4], const uint32_t* __restrict__ B, int64_t ldb, int N,
+                                             int K, int n0, int k0, int tid) {
+    const int gn = n0 + (tid & 63) * 4;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int gk = k0 + (tid >> 6) * 4 + q;
+        if (!MASK) {
+            const uint32_t* src = B + (int64_t)gk * ldb + gn;
+            r[q] = VEC ? *(const u32x4*)src : load4_f32(src, 4);
+        } else {
+            const int rem = N - gn;
+            const int nv = (gk < K) ? (rem < 0 ? 0 : (rem > 4 ? 4 : rem)) : 0;
+            const int gkc = gk < K ? gk : K - 1;
+            const uint32_t* src = B + (int64_t)gkc * ldb + (nv > 0 ? gn : 0);
+            r[q] = (VEC && nv == 4) ? *(const u32x4*)src : load4_f32(src, nv);
+        }
+    }
+}
+
+// Transpose the 4 x 4 block: LDS row n0' + v receives k = 4 (t >> 6) + 0..3
+// as chunk (t >> 6).
+__device__ __forceinline__ void f32_store_kxn(u32x4* __restrict__ s, const u32x4 (&r)[4], int tid) {
+    const int kc = tid >> 6, nb = tid & 63;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) s[LdsF::slot(nb * 4 + v, kc)] = u32x4{r[0][v], r[1][v], r[2][v], r[3][v]};
+}
+
+__device__ __forceinline__ f32x4 read_f32_frag(const u32x4* __restrict__ s_blk, int half, int blk, int lane) {
+    return __builtin_bit_cast(f32x4, s_blk[LdsF::slot(half * 128 + blk * 16 + (lane & 15), lane >> 4)]);
+}
+
+// One 16-deep K step of the wave's 128 x 128 sub-tile: 4 x 8 x 8 MFMAs.
+__device__ __forceinline__ void f32_mma_step(f32x4 (&acc)[8][8], const u32x4* __restrict__ sA,
+                                             const u32x4* __restrict__ sB, int wm, int wn, int lane) {
+    f32x4 af[8], bf[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) af[i] = read_f32_frag(sA, wm, i, lane);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) bf[j] = read_f32_frag(sB, wn, j, lane);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(bf[j][e], af[i][e], acc[i][j], 0, 0, 0);
+}
+
+template <int NXK, bool VEC, bool MASK>
+__device__ __forceinline__ void f32_load_stage(u32x4 (&ra)[4], u32x4 (&rb)[4], const Args& a, int m0, int n0,
+                                               int k0, int tid) {
+    const uint32_t* A = reinterpret_cast<const uint32_t*>(a.A);
+    const uint32_t* B = reinterpret_cast<const uint32_t*>(a.B);
+    f32_load_kc<VEC, MASK>(ra, A, a.lda, a.M, a.K, m0, k0, tid);
+    if (NXK)
+        f32_load_kc<VEC, MASK>(rb, B, a.ldb, a.N, a.K, n0, k0, tid);
+    else
+        f32_load_kxn<VEC, MASK>(rb, B, a.ldb, a.N, a.K, n0, k0, tid);
+}
+
+template <int NXK>
+__device__ __forceinline__ void f32_store_stage(u32x4* __restrict__ sA, u32x4* __restrict__ sB,
+                                                const u32x4 (&ra)[4], const u32x4 (&rb)[4], int tid) {
+    f32_store_kc(sA, ra, tid);
+    if (NXK)
+        f32_store_kc(sB, rb, tid);
+    else
+        f32_store_kxn(sB, rb, tid);
+}
+
+// One workgroup per output tile; the next step's operands are loaded into
+// registers while the current step runs on the matrix cores, then written to
+// the other LDS stage (one barrier per step).
+template <int TY, int NXK, bool VEC>
+__global__ void __launch_bounds__(NTHREADS)
+__attribute__((amdgpu_waves_per_eu(1, 1)))
+tgemm_f32in_kernel(Args a) {
+    static_assert(ab_of(TY) == 2, "binary32 operands");
+    __shared__ u32x4 smem[2][2][LdsF::kBlock];   // [stage][A | B], 64 KiB
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    int tm, tn;
+    tile_of((int)blockIdx.x, a.W, a.grid_m, a.grid_n, a.group_m, a.num_xcd, &tm, &tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const bool interior = (m0 + BM <= a.M) && (n0 + BN <= a.N);
+    const int nk = (a.K + kF32Ks - 1) / kF32Ks;
+
+    f32x4 acc[8][8];
+    zero_acc(acc);
+
+    u32x4 ra[4], rb[4];
+    if (nk > 0) {
+        if (interior && kF32Ks <= a.K)
+            f32_load_stage<NXK, VEC, false>(ra, rb, a, m0, n0, 0, tid);
+        else
+            f32_load_stage<NXK, VEC, true>(ra, rb, a, m0, n0, 0, tid);
+        f32_store_stage<NXK>(smem[0][0], smem[0][1], ra, rb, tid);
+        __syncthreads();
+    }
+    for (int t = 0; t < nk; ++t) {
+        const int cur = t & 1;
+        const bool more = t + 1 < nk;
+        if (more) {
+            const int k0 = (t + 1) * kF32Ks;
+            if (interior && k0 + kF32Ks <= a.K)
+                f32_load_stage<NXK, VEC, false>(ra, rb, a, m0, n0, k0, tid);
+            else
+                f32_load_stage<NXK, VEC, true>(ra, rb, a, m0, n0, k0, tid);
+        }
+        f32_mma_step(acc, smem[cur][0], smem[cur][1], wm, wn, lane);
+        if (more) f32_store_stage<NXK>(smem[cur ^ 1][0], smem[cur ^ 1][1], ra, rb, tid);
+        __syncthreads();
+    }
+    store_c<TY>(acc, a, m0, n0, wm, wn, lane);
+}
+
 // Kernel for a plan, per (input type, output type, epilogue): each is
 // instantiated in a translation unit of its own. Returns null for a K step /
 // ring depth that combination does not instantiate.
@@ -1017,6 +1204,9 @@ TG_DECLARE_KERNEL_FOR(0, 2)
 TG_DECLARE_KERNEL_FOR(1, 0)
 TG_DECLARE_KERNEL_FOR(1, 1)
 TG_DECLARE_KERNEL_FOR(1, 2)
+TG_DECLARE_KERNEL_FOR(2, 0)
+TG_DECLARE_KERNEL_FOR(2, 1)
+TG_DECLARE_KERNEL_FOR(2, 2)
 #undef TG_DECLARE_KERNEL_FOR
 
 }  // namespace tg

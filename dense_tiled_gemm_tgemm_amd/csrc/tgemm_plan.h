@@ -28,6 +28,7 @@ constexpr int kDefaultNumXcd = 8;        // MI355X: 8 accelerator dies of 32 CUs
 // K step 64, 32 KiB at K step 32). 64-deep steps take a 2-stage ring.
 constexpr int kDefaultDmaKStep = 64;
 constexpr int kDefaultDmaStages32 = 4;     // ring depth when the K step is 32
+constexpr int kF32KStep = 16;              // K step (floats) of the binary32-operand kernel
 
 enum : int { kVecAB = 1, kVecC = 2, kLayoutNxK = 4, kDma = 8 };
 
@@ -64,7 +65,7 @@ struct Plan {
     int M, N, K;
     int64_t lda, ldb, ldc;
     int layout;        // 0 = KxN, 1 = NxK
-    int ab_type;       // TGEMM_F16 or TGEMM_BF16 (both operands)
+    int ab_type;       // TGEMM_F16, TGEMM_BF16 or TGEMM_F32 (both operands)
     int c_type;        // TGEMM_F16, TGEMM_BF16 or TGEMM_F32
     bool epi;          // scale, bias or activation requested (else C = A * B as it is)
     int variant;       // kVecAB | kVecC | kLayoutNxK | kDma bits
@@ -104,8 +105,9 @@ inline int make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
     if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
         return TGEMM_ERR_INVALID;
     if (b_layout != TGEMM_B_KxN && b_layout != TGEMM_B_NxK) return TGEMM_ERR_INVALID;
-    if (ab_type != TGEMM_F16 && ab_type != TGEMM_BF16) return TGEMM_ERR_INVALID;
+    if (ab_type != TGEMM_F16 && ab_type != TGEMM_BF16 && ab_type != TGEMM_F32) return TGEMM_ERR_INVALID;
     if (c_type != TGEMM_F16 && c_type != TGEMM_BF16 && c_type != TGEMM_F32) return TGEMM_ERR_INVALID;
+    const int ab_size = ab_type == TGEMM_F32 ? 4 : 2;
     const int c_size = c_type == TGEMM_F32 ? 4 : 2;
     if (force_generic != 0 && force_generic != 1) return TGEMM_ERR_INVALID;
     if (group_m < 0 || group_m > 1024 || num_xcd < 0 || num_xcd > 64) return TGEMM_ERR_INVALID;
@@ -119,15 +121,15 @@ inline int make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
     if (ldc < (N > one ? N : one)) return TGEMM_ERR_INVALID;
 
     uint64_t na, nb, nc;
-    if (!span_bytes(M, K, lda, &na)) return TGEMM_ERR_INVALID;
+    if (!span_bytes(M, K, lda, &na, ab_size)) return TGEMM_ERR_INVALID;
     if (b_layout == TGEMM_B_KxN) {
-        if (!span_bytes(K, N, ldb, &nb)) return TGEMM_ERR_INVALID;
+        if (!span_bytes(K, N, ldb, &nb, ab_size)) return TGEMM_ERR_INVALID;
     } else {
-        if (!span_bytes(N, K, ldb, &nb)) return TGEMM_ERR_INVALID;
+        if (!span_bytes(N, K, ldb, &nb, ab_size)) return TGEMM_ERR_INVALID;
     }
     if (!span_bytes(M, N, ldc, &nc, c_size)) return TGEMM_ERR_INVALID;
     if ((na && !A) || (nb && !B) || (nc && !C)) return TGEMM_ERR_INVALID;
-    if (((uintptr_t)A & 1) || ((uintptr_t)B & 1) || ((uintptr_t)C % c_size)) return TGEMM_ERR_INVALID;
+    if (((uintptr_t)A % ab_size) || ((uintptr_t)B % ab_size) || ((uintptr_t)C % c_size)) return TGEMM_ERR_INVALID;
     if (overlaps(C, nc, A, na) || overlaps(C, nc, B, nb)) return TGEMM_ERR_INVALID;
     // the bias is read while C is written: 4-byte aligned, apart from C
     const uint64_t nbias = bias ? (uint64_t)N * 4u : 0u;
@@ -155,15 +157,16 @@ inline int make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
     pl->group_m = g > 0 ? g : 1;
     pl->num_xcd = num_xcd ? num_xcd : kDefaultNumXcd;
 
-    const bool vec_ab = !force_generic && ((uintptr_t)A % 16 == 0) && (lda % 8 == 0) &&
-                        ((uintptr_t)B % 16 == 0) && (ldb % 8 == 0);
+    const bool vec_ab = !force_generic && ((uintptr_t)A % 16 == 0) && ((lda * ab_size) % 16 == 0) &&
+                        ((uintptr_t)B % 16 == 0) && ((ldb * ab_size) % 16 == 0);
     const bool vec_c = ((uintptr_t)C % 8 == 0) && ((ldc * c_size) % 8 == 0);
     // direct-to-LDS (any 2-byte alignment: gfx950 buffer loads accept
     // unaligned addresses): row strides small enough for 32-bit panel
     // offsets; a K x N B additionally needs every byte offset it forms,
     // below (K + 64) * ldb * 2 + 512, to stay below 2^31.
     // (K == 0 only writes zeros: the register-staged kernel does that)
-    const bool dma = !force_generic && K > 0 && lda <= kMaxDmaLd &&
+    // (binary32 operands have a kernel of their own, staged through registers)
+    const bool dma = !force_generic && ab_type != TGEMM_F32 && K > 0 && lda <= kMaxDmaLd &&
                      (b_layout == TGEMM_B_NxK ? ldb <= kMaxDmaLd
                                               : ldb < (int64_t(1) << 30) && (K + 64) * ldb < (int64_t(1) << 30) - 512);
     pl->variant = (vec_ab ? kVecAB : 0) | (vec_c ? kVecC : 0) |
@@ -174,6 +177,9 @@ inline int make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
         pl->k_step = k_step ? k_step : ((stages > 2 || K <= 64) ? 32 : kDefaultDmaKStep);
         if (pl->k_step == 64 && K <= 64) return TGEMM_ERR_INVALID;
         pl->stages = pl->k_step == 64 ? 2 : (stages ? stages : kDefaultDmaStages32);
+    } else if (ab_type == TGEMM_F32) {
+        pl->k_step = kF32KStep;
+        pl->stages = 2;
     } else {
         pl->k_step = BK;
         pl->stages = 2;

@@ -1,7 +1,8 @@
 /*
  * tgemm: dense tiled matrix product C = A * B on AMD Instinct MI355X
- * (gfx950), binary16 in and out (tgemm_f16), with bfloat16 inputs, bfloat16
- * or fp32 output and a scale / bias / activation epilogue (tgemm_gemm).
+ * (gfx950), binary16 in and out (tgemm_f16), with bfloat16 or binary32
+ * inputs, bfloat16 or fp32 output and a scale / bias / activation epilogue
+ * (tgemm_gemm).
  * C ABI: plain pointers and sizes, no HIP or framework types.
  *
  * The operation (page 1, "Using NVIDIA CUDA Tile to write a high-performance
@@ -117,8 +118,9 @@ int tgemm_f16_config(int64_t M, int64_t N, int64_t K,
  * C = act(alpha * A * B + bias) with a choice of element types, on `stream`.
  *
  * The pages' tile kernels take their element types as parameters: inputs
- * of two bytes (binary16 or bfloat16) share one tile configuration (page 1,
- * section "Step 2: set the tile size"), and the guide's example accumulates
+ * of two bytes (binary16 or bfloat16) share one tile configuration and
+ * binary32 inputs get another (page 1, section "Step 2: set the tile size"),
+ * and the guide's example accumulates
  * binary16 products in fp32 and stores an fp32 C (page 4, section 2.4.9.1);
  * production GEMMs fuse work on the output into the store (page 5, Croqtile
  * tutorial "dense GEMM fp16 from naive", section "SOTA comparison": epilogue
@@ -130,14 +132,21 @@ int tgemm_f16_config(int64_t M, int64_t N, int64_t K,
  * v itself). alpha == 1, bias == NULL and act == TGEMM_ACT_NONE store the
  * sums exactly as tgemm_f16 does (for binary16 in and out: the same bits).
  *
- *   ab_type: TGEMM_F16 or TGEMM_BF16, the type of both A and B.
+ *   ab_type: TGEMM_F16, TGEMM_BF16 or TGEMM_F32, the type of both A and B
+ *            (lda and ldb count elements of that type; binary32 operands
+ *            must be 4-byte aligned). Binary32 operands run on
+ *            v_mfma_f32_16x16x4_f32 with fp32 accumulation, one kernel
+ *            family staged through registers (16-deep K steps, 2 LDS stages:
+ *            the k_step and stages choices of tgemm_gemm_config do not apply
+ *            to it).
  *   c_type:  TGEMM_F16, TGEMM_BF16 or TGEMM_F32; ldc counts elements of
  *            that type (C[i*ldc + j]).
  *   bias:    NULL, or N fp32 values in device memory (4-byte aligned),
  *            added to every row; only read.
  * Storage, ownership, asynchrony and the remaining argument checks are those
  * of tgemm_f16, with these in addition (TGEMM_ERR_INVALID, nothing enqueued):
- * ab_type or c_type or act out of range; C not aligned to its element size;
+ * ab_type or c_type or act out of range; A, B or C not aligned to its
+ * element size;
  * bias not 4-byte aligned; the bias overlapping C.
  * K == 0 stores act(bias[j]) (zero sums, scaled, plus the bias).
  */

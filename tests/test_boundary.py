@@ -212,8 +212,11 @@ PBIAS = 4 << 40
 
 
 @pytest.mark.parametrize("args", [
-    dict(M=4, N=4, K=4, ab=2),                        # fp32 inputs are not a binary16/bfloat16 pair
+    dict(M=4, N=4, K=4, ab=3),
     dict(M=4, N=4, K=4, ab=-1),
+    dict(M=4, N=4, K=4, ab="f32", A=PA + 2),          # binary32 operands must be 4-byte aligned
+    dict(M=4, N=4, K=4, ab="f32", B=PB + 6),
+    dict(M=4, N=4, K=4, ab="f32", C=PA + 40),         # A spans 4-byte elements: C overlaps it
     dict(M=4, N=4, K=4, ct=3),
     dict(M=4, N=4, K=4, act=2),
     dict(M=4, N=4, K=4, ct="f32", C=PC + 2),          # fp32 C must be 4-byte aligned
@@ -316,3 +319,21 @@ def test_tuning_rejects_bad_arguments_without_gpu():
     tg.tuning_clear()
     assert tg.tuning_entries() == 0
     assert lib.tgemm_tune_gemm(0, 4, 4, 0, PA, 4, PB, 4, 0, 0, PC, 4, 1.0, None, 0, None, 5, None) == tg.TGEMM_OK
+
+
+def test_fp32_operand_plans():
+    V, C8, NXK, DMA = 1, 2, 4, 8
+    # binary32 operands: register-staged kernel, 16-deep steps, 2 stages of 2 x 256 x 16 floats
+    rc, info = _plan_ex(8192, 8192, 8192, ab="f32", ct="f32", lay="NxK")
+    assert rc == 0 and info["variant"] == V | C8 | NXK
+    assert (info["bk"], info["stages"], info["lds_bytes"], info["workgroups"]) == (16, 2, 64 * 1024, 1024)
+    # launch choices for the direct-to-LDS pipeline do not apply
+    rc2, info2 = _plan_ex(8192, 8192, 8192, ab="f32", ct="f32", lay="NxK", k_step=32, stages=5)
+    assert rc2 == 0 and info2 == info
+    # 16-byte loads need 16-byte rows: lda a multiple of 4 floats
+    rc, info = _plan_ex(300, 200, 101, ab="f32", ct="f16", lda=101)
+    assert rc == 0 and info["variant"] == C8
+    rc, info = _plan_ex(300, 200, 100, ab="f32", ct="f16", lda=100, ldb=200)
+    assert rc == 0 and info["variant"] == V | C8
+    rc, info = _plan_ex(300, 200, 100, ab="f32", ct="bf16", A=PA + 4)
+    assert rc == 0 and info["variant"] == C8

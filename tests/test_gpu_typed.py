@@ -319,3 +319,124 @@ def test_binary16_output_overflow_is_infinity(oracle_mod):
     assert oracle_mod.check_ex(got, "f16", ref, tol)["nfail"] == 0
     f = got.view(np.float16)
     assert np.isposinf(f[:, 0::2]).all() and np.isneginf(f[:, 1::2]).all()
+
+
+# ------------------------------------------------------------ binary32 operands --
+
+def _f32(shape, seed, dist=("uniform", -1.0, 1.0)):
+    return inputs.random_f32(shape, seed, dist)
+
+
+def _d32(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(DEV)
+
+
+@pytest.mark.parametrize("epi", ["plain", "epi"])
+@pytest.mark.parametrize("lay", ["KxN", "NxK"])
+@pytest.mark.parametrize("ct", ["f16", "bf16", "f32"])
+@pytest.mark.parametrize("M,N,K", SMALL + [(257, 255, 129)])
+def test_f32_operands_small_shapes_full_parity(oracle_mod, M, N, K, ct, lay, epi):
+    print(f"case f32-in {M}x{N}x{K} ->{ct} {lay} {epi}", flush=True)
+    seed = (M * 11 + N * 5 + K * 3) % 100003
+    A = _f32((M, K), seed)
+    B = _f32((K, N) if lay == "KxN" else (N, K), seed + 1)
+    e = EPI[epi]
+    b_np, b_dev = _bias(N, seed + 2, e["bias"])
+    Ad, Bd = _d32(A), _d32(B)
+    C = tg.gemm(Ad, Bd, lay, out_dtype=TORCH_DT[ct], alpha=e["alpha"], bias=b_dev, act=e["act"])
+    _check(oracle_mod, A, B, lay, "f32", ct, _out_np(C), e["alpha"], b_np, e["act"], f"f32 {M}x{N}x{K} {lay}")
+    # element-wise operand loads (force_generic) give the same bits
+    C2 = tg.gemm(Ad, Bd, lay, out_dtype=TORCH_DT[ct], alpha=e["alpha"], bias=b_dev, act=e["act"], force_generic=1)
+    torch.cuda.synchronize()
+    if ct == "f32":
+        assert torch.equal(C, C2)
+    else:
+        assert torch.equal(C.view(torch.int16), C2.view(torch.int16))
+
+
+@pytest.mark.parametrize("lay,offset,pad", [("KxN", 1, 3), ("NxK", 1, 5), ("NxK", 0, 3), ("KxN", 2, 2)])
+def test_f32_operands_strided_and_offset(oracle_mod, lay, offset, pad):
+    """Operands inside larger buffers: row strides of K + pad (N + pad) floats,
+    bases `offset` floats in (4-byte-aligned only when offset is odd)."""
+    M, N, K = 300, 270, 133
+    print(f"case f32-in strided {lay} offset={offset} pad={pad}", flush=True)
+    A = _f32((M, K), 91)
+    B = _f32((K, N) if lay == "KxN" else (N, K), 92)
+    bufA = np.full(offset + M * (K + pad), np.nan, dtype=np.float32)
+    va = bufA[offset:offset + M * (K + pad)].reshape(M, K + pad)
+    va[:, :K] = A
+    rows_b, cols_b = B.shape
+    bufB = np.full(offset + rows_b * (cols_b + pad), np.nan, dtype=np.float32)
+    vb = bufB[offset:offset + rows_b * (cols_b + pad)].reshape(rows_b, cols_b + pad)
+    vb[:, :cols_b] = B
+    dA, dB = _d32(bufA), _d32(bufB)
+    C = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    rc = tg.tgemm_gemm(M, N, K, "f32", dA.data_ptr() + 4 * offset, K + pad, dB.data_ptr() + 4 * offset,
+                       cols_b + pad, lay, "f32", C.data_ptr(), N, 1.0, None, "none",
+                       torch.cuda.current_stream().cuda_stream)
+    assert rc == tg.TGEMM_OK
+    _check(oracle_mod, A, B, lay, "f32", "f32", _out_np(C), 1.0, None, "none", "f32 strided")
+
+
+@pytest.mark.parametrize("name", ["sq256", "sq4096", "ragged", "sq8192_nt", "qkv_proj"])
+def test_f32_operands_ternary_bit_exact(oracle_mod, name):
+    """Entries in {-1, 0, 1}: every product and partial sum is an integer below
+    2^24, so the fp32 output is exact at the workload shapes."""
+    w = inputs.WORKLOADS[name]
+    print(f"case f32-in ternary {name}", flush=True)
+    A = inputs.ternary_f16((w.M, w.K), 300 + w.seed).astype(np.float32)
+    B = inputs.ternary_f16(w.b_shape, 301 + w.seed).astype(np.float32)
+    C = tg.gemm(_d32(A), _d32(B), w.b_layout, out_dtype=torch.float32)
+    got = _out_np(C)
+    I, J = inputs.sample_points(w.M, w.N, 8192, 302 + w.seed)
+    ref, _ = oracle_mod.gemm_ex(A, B, w.b_layout, "f32", I=I, J=J)
+    assert np.array_equal(got[I, J].astype(np.float64), ref)
+    g = got.astype(np.float64)
+    assert np.all(g == np.round(g)) and np.abs(g).max() <= w.K
+
+
+@pytest.mark.parametrize("name", ["sq4096", "ragged", "sq8192_nt", "qkv_proj"])
+def test_f32_operands_workload_parity(oracle_mod, name):
+    w = inputs.WORKLOADS[name]
+    print(f"case f32-in workload {name}", flush=True)
+    A, B = inputs.make_inputs(w, "f32")
+    C = torch.empty((w.M, w.N), dtype=torch.float32, device=DEV)
+    Ad, Bd = _d32(A), _d32(B)
+    rc = tg.tgemm_gemm(w.M, w.N, w.K, "f32", Ad.data_ptr(), w.K, Bd.data_ptr(), B.shape[1], w.b_layout, "f32",
+                       C.data_ptr(), w.N, 1.0, None, "none", torch.cuda.current_stream().cuda_stream)
+    assert rc == tg.TGEMM_OK
+    got = _out_np(C)
+    I, J = inputs.sample_points(w.M, w.N, 8192, w.seed + 4000)
+    res = _check(oracle_mod, A, B, w.b_layout, "f32", "f32", got, 1.0, None, "none", name, I, J)
+    print(f"  {name}: {res['n']} checked, worst {res['worst']:.4f}", flush=True)
+
+
+def test_f32_operands_one_accumulation_rounded_to_each_output_type():
+    print("case f32-in rounding", flush=True)
+    M, N, K = 700, 600, 264
+    A, B = _d32(_f32((M, K), 93)), _d32(_f32((N, K), 94))
+    _, b_dev = _bias(N, 95, True)
+    for kw in (dict(), dict(alpha=-1.75, bias=b_dev, act="relu")):
+        c32 = tg.gemm(A, B, "NxK", out_dtype=torch.float32, **kw)
+        c16 = tg.gemm(A, B, "NxK", out_dtype=torch.float16, **kw)
+        cbf = tg.gemm(A, B, "NxK", out_dtype=torch.bfloat16, **kw)
+        torch.cuda.synchronize()
+        h32 = c32.cpu()
+        assert torch.equal(h32.to(torch.float16).view(torch.int16), c16.cpu().view(torch.int16))
+        assert torch.equal(h32.to(torch.bfloat16).view(torch.int16), cbf.cpu().view(torch.int16))
+
+
+def test_f32_operands_k_zero_and_raster():
+    print("case f32-in K=0 and raster", flush=True)
+    A = torch.empty((300, 0), dtype=torch.float32, device=DEV)
+    B = torch.empty((0, 270), dtype=torch.float32, device=DEV)
+    C = torch.full((300, 270), 7.0, dtype=torch.float32, device=DEV)
+    tg.gemm(A, B, "KxN", out=C)
+    torch.cuda.synchronize()
+    assert bool((C == 0).all())
+    A = _d32(_f32((1300, 700), 96))
+    B = _d32(_f32((1500, 700), 97))
+    base = tg.gemm(A, B, "NxK", out_dtype=torch.float32)
+    other = tg.gemm(A, B, "NxK", out_dtype=torch.float32, group_m=3, num_xcd=1)
+    torch.cuda.synchronize()
+    assert torch.equal(base, other)
