@@ -40,9 +40,10 @@ const void* rs_ptr(bool vec) {
 }
 
 template <int NXK>
-const void* f32in_ptr(bool vec) {
-    return vec ? reinterpret_cast<const void*>(&tgemm_f32in_kernel<kTy, NXK, true>)
-               : reinterpret_cast<const void*>(&tgemm_f32in_kernel<kTy, NXK, false>);
+const void* f32in_ptr(bool pipelined, bool vec) {
+    if (pipelined) return reinterpret_cast<const void*>(&tgemm_f32in_kernel<kTy, NXK>);
+    return vec ? reinterpret_cast<const void*>(&tgemm_f32in_rs_kernel<kTy, NXK, true>)
+               : reinterpret_cast<const void*>(&tgemm_f32in_rs_kernel<kTy, NXK, false>);
 }
 
 }  // namespace
@@ -52,8 +53,9 @@ const void* kernel_for<TG_AB, TG_CT, (TG_EPI != 0)>(const Plan& pl) {
     const bool nxk = (pl.variant & kLayoutNxK) != 0;
     const bool vec = (pl.variant & kVecAB) != 0;
     if constexpr (TG_AB == 2) {
-        // binary32 operands: one kernel family, staged through registers
-        return nxk ? f32in_ptr<1>(vec) : f32in_ptr<0>(vec);
+        // binary32 operands: the pipelined kernel, or the general one
+        const bool pipelined = (pl.variant & kDma) != 0;
+        return nxk ? f32in_ptr<1>(pipelined, vec) : f32in_ptr<0>(pipelined, vec);
     } else {
         if (pl.variant & kDma) return nxk ? dma_ptr<1>(pl.k_step, pl.stages) : dma_ptr<0>(pl.k_step, pl.stages);
         return nxk ? rs_ptr<1>(vec) : rs_ptr<0>(vec);

@@ -184,7 +184,10 @@ __device__ __forceinline__ void load_bias(float (&bv)[8][4], const Args& a, int 
 //    x 64 bytes), two 8-byte stores when 8-byte aligned, element stores
 //    otherwise and where the 8 columns straddle N.
 //  * fp32 output: each block's four columns are 16 contiguous bytes of the
-//    lane's row, stored as they are (16 rows x 64 bytes per instruction).
+//    lane's row, stored as they are (16 rows x 64 bytes per instruction) when
+//    every C row starts 16-byte aligned, element stores otherwise (an 8-byte
+//    path here made the register allocator move the accumulators around in
+//    the main loop of the binary32-operand kernel).
 // All lanes run the exchange; only the stores are predicated. One 16-row block
 // at a time (pinned), so the temporaries stay few when this runs between two
 // tiles with the next tile's fragments already in registers.
@@ -220,9 +223,6 @@ __device__ __forceinline__ void store_c(const f32x4 (&acc)[8][8], const Args& a,
                 float* dst = row + 16 * j;
                 if (row_ok && col + 4 <= a.N && a.c16) {
                     *(f32x4*)dst = v;
-                } else if (row_ok && col + 4 <= a.N && a.c8) {
-                    *(f32x2*)dst = f32x2{v[0], v[1]};
-                    *(f32x2*)(dst + 2) = f32x2{v[2], v[3]};
                 } else if (row_ok && col < a.N) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
@@ -1015,7 +1015,8 @@ tgemm_dma_kernel(Args a) {
 // each operand per lane, 32 cycles): at 1/16 of the 16-bit rate per
 // instruction, the operand traffic per MFMA is small, so operands are staged
 // through registers (any stride and alignment of 4 bytes) into a 2-stage LDS
-// ring.
+// ring; fragments are read one step ahead so that the matrix cores do not
+// wait for LDS after each barrier.
 //
 // LDS: per stage an A block and a B block of 256 rows x 4 chunks of 4 floats
 // (k 4c .. 4c+3 in chunk c), chunk c of row r at slot r * 4 + (c ^ f(r)),
@@ -1097,11 +1098,246 @@ __device__ __forceinline__ void f32_store_kxn(u32x4* __restrict__ s, const u32x4
     for (int v = 0; v < 4; ++v) s[LdsF::slot(nb * 4 + v, kc)] = u32x4{r[0][v], r[1][v], r[2][v], r[3][v]};
 }
 
+template <int NXK, bool VEC, bool MASK>
+__device__ __forceinline__ void f32_load_stage(u32x4 (&ra)[4], u32x4 (&rb)[4], const Args& a, int m0, int n0,
+                                               int k0, int tid) {
+    const uint32_t* A = reinterpret_cast<const uint32_t*>(a.A);
+    const uint32_t* B = reinterpret_cast<const uint32_t*>(a.B);
+    f32_load_kc<VEC, MASK>(ra, A, a.lda, a.M, a.K, m0, k0, tid);
+    if (NXK)
+        f32_load_kc<VEC, MASK>(rb, B, a.ldb, a.N, a.K, n0, k0, tid);
+    else
+        f32_load_kxn<VEC, MASK>(rb, B, a.ldb, a.N, a.K, n0, k0, tid);
+}
+
+// Operands of step t into registers (whole chunks inside the operands take
+// the unmasked loads).
+template <int NXK, bool VEC>
+__device__ __forceinline__ void f32_load_step(u32x4 (&ra)[4], u32x4 (&rb)[4], const Args& a, int m0, int n0, int t,
+                                              bool interior, int tid) {
+    const int k0 = t * kF32Ks;
+    if (interior && k0 + kF32Ks <= a.K)
+        f32_load_stage<NXK, VEC, false>(ra, rb, a, m0, n0, k0, tid);
+    else
+        f32_load_stage<NXK, VEC, true>(ra, rb, a, m0, n0, k0, tid);
+}
+
+template <int NXK>
+__device__ __forceinline__ void f32_store_stage(u32x4* __restrict__ sA, u32x4* __restrict__ sB,
+                                                const u32x4 (&ra)[4], const u32x4 (&rb)[4], int tid) {
+    f32_store_kc(sA, ra, tid);
+    if (NXK)
+        f32_store_kc(sB, rb, tid);
+    else
+        f32_store_kxn(sB, rb, tid);
+}
+
 __device__ __forceinline__ f32x4 read_f32_frag(const u32x4* __restrict__ s_blk, int half, int blk, int lane) {
     return __builtin_bit_cast(f32x4, s_blk[LdsF::slot(half * 128 + blk * 16 + (lane & 15), lane >> 4)]);
 }
 
-// One 16-deep K step of the wave's 128 x 128 sub-tile: 4 x 8 x 8 MFMAs.
+// Staging of the pipelined kernel (K a multiple of 4, and N too for B stored
+// K x N, so that no 4-float chunk straddles the end of a row): 16-byte buffer
+// loads through per-tile resources that return zeros past each operand's last
+// element (rows past M or N, and for B stored K x N rows past K); chunks at
+// or past K (columns at or past N) are cleared with selects. No branches, so
+// the accumulators stay in place across the step.
+__device__ __forceinline__ Rsrc f32_rsrc(const uint16_t* X, int64_t ld, int nrows, int ncols, int row0) {
+    int64_t span = ((int64_t)(nrows - row0 - 1) * ld + ncols) * 4;
+    if (span > (int64_t)kOob - 1) span = (int64_t)kOob - 1;
+    return Rsrc{X + (int64_t)row0 * ld * 2, (int)span};
+}
+
+struct F32Lanes {
+    unsigned va[4], vb[4];   // byte offsets of this lane's loads from the tile's resource bases
+    int kc;                  // k offset (floats) of this lane's K-contiguous chunk within a step
+    int nc;                  // column offset (floats) of this lane's K x N chunk within the tile
+};
+
+template <int NXK>
+__device__ __forceinline__ F32Lanes f32_lanes(const Args& a, int tid) {
+    F32Lanes L;
+    const unsigned c = (unsigned)(tid & 3);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const unsigned row = (unsigned)((tid >> 2) + 64 * p);
+        L.va[p] = (row * (unsigned)a.lda + 4u * c) * 4u;
+        if (NXK) L.vb[p] = (row * (unsigned)a.ldb + 4u * c) * 4u;
+    }
+    if (!NXK) {
+        const unsigned kr = (unsigned)(4 * (tid >> 6)), nb = (unsigned)(tid & 63);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) L.vb[q] = ((kr + (unsigned)q) * (unsigned)a.ldb + 4u * nb) * 4u;
+    }
+    L.kc = 4 * (tid & 3);
+    L.nc = 4 * (tid & 63);
+    return L;
+}
+
+template <int NXK>
+__device__ __forceinline__ void f32_buf_load(u32x4 (&ra)[4], u32x4 (&rb)[4], const Rsrc& rsa, const Rsrc& rsb,
+                                             const F32Lanes& L, const Args& a, int n0, int t) {
+#if defined(__HIP_DEVICE_COMPILE__)   // the host pass cannot instantiate these target builtins
+    const int k0 = t * kF32Ks;
+    const __amdgpu_buffer_rsrc_t xa = __builtin_amdgcn_make_buffer_rsrc((void*)rsa.base, 0, rsa.nrec, 0x00020000);
+    const __amdgpu_buffer_rsrc_t xb = __builtin_amdgcn_make_buffer_rsrc((void*)rsb.base, 0, rsb.nrec, 0x00020000);
+    const unsigned soa = (unsigned)k0 * 4u;
+    const unsigned sob = NXK ? (unsigned)k0 * 4u : (unsigned)k0 * (unsigned)a.ldb * 4u;
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+        ra[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xa, (int)L.va[p], (int)soa, 0));
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+        rb[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xb, (int)L.vb[p], (int)sob, 0));
+#else
+    (void)ra; (void)rb; (void)rsa; (void)rsb; (void)L; (void)a; (void)n0; (void)t;
+#endif
+}
+
+// Write step t's staged operands into an LDS stage, clearing chunks at or past
+// K (columns at or past N for B stored K x N). The selects sit here, a half
+// step after the loads were issued, so they never wait on memory inside the
+// matrix-instruction stream.
+template <int NXK>
+__device__ __forceinline__ void f32_store_step(u32x4* __restrict__ sA, u32x4* __restrict__ sB, u32x4 (&ra)[4],
+                                               u32x4 (&rb)[4], const F32Lanes& L, const Args& a, int n0, int t,
+                                               int tid) {
+    const bool k_ok = t * kF32Ks + L.kc < a.K;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) ra[p] = k_ok ? ra[p] : u32x4{};
+    if (NXK) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) rb[p] = k_ok ? rb[p] : u32x4{};
+    } else {
+        const bool n_ok = n0 + L.nc < a.N;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) rb[q] = n_ok ? rb[q] : u32x4{};
+    }
+    f32_store_stage<NXK>(sA, sB, ra, rb, tid);
+}
+
+// The wave's fragments as 8-byte halves of its 16-byte chunks: lo = k0 + 4g +
+// 0..1 (MFMAs e = 0, 1), hi = k0 + 4g + 2..3 (e = 2, 3).
+struct F32Frags {
+    f32x2 alo[8], ahi[8], blo[8], bhi[8];
+};
+
+// This lane's 8-byte read position of 16-row block 0 in stage 0 of A (B):
+// block i lies 128 positions further (16 rows x 4 chunks x 2 halves), stage 1
+// kF32Stage positions further, the hi half 1 further.
+constexpr int kF32Stage = 2 * 2 * LdsF::kBlock;   // 8-byte units per stage (A and B blocks)
+
+// Half of a step's MFMAs (EH = 0: e = 0, 1 on the lo halves; EH = 1: e = 2,
+// 3 on the hi halves), 128 MFMAs walking the 8 x 8 blocks in serpentine order
+// twice, with the 16 reads of the other halves placed after every eighth
+// MFMA: EH = 0 reads this step's hi halves, EH = 1 the next step's lo halves
+// (from `pa` / `pb`, in the order the next half consumes them: A0, B0..B7,
+// A1..A7). The compiler schedules the section: pinning it instruction by
+// instruction, as in the 16-bit kernels, makes the register allocator rotate
+// all 256 accumulators at every step here.
+template <int EH, int Q0 = 0, int Q1 = 128>
+__device__ __forceinline__ void f32_half(f32x4 (&acc)[8][8], F32Frags& f, const f32x2* __restrict__ pa,
+                                         const f32x2* __restrict__ pb) {
+    constexpr int kHalf = EH ? 0 : 1;                 // which half the reads fill
+#pragma unroll
+    for (int q = Q0; q < Q1; ++q) {
+        const int e = q >> 6, x = q & 63;
+        const int i = x >> 3, j = (i & 1) ? 7 - (x & 7) : (x & 7);
+        const f32x2& av = EH ? f.ahi[i] : f.alo[i];
+        const f32x2& bv = EH ? f.bhi[j] : f.blo[j];
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(bv[e], av[e], acc[i][j], 0, 0, 0);
+        if ((q & 7) == 7) {
+            const int r = q >> 3;                     // 0 .. 15
+            if (r >= 1 && r <= 8) {
+                f32x2& d = EH ? f.blo[r - 1] : f.bhi[r - 1];
+                d = pb[(r - 1) * 128 + kHalf];
+            } else {
+                const int ai = r == 0 ? 0 : r - 8;
+                f32x2& d = EH ? f.alo[ai] : f.ahi[ai];
+                d = pa[ai * 128 + kHalf];
+            }
+        }
+    }
+}
+
+// One workgroup per output tile. Per 16-deep step t (LDS stage t mod 2): the
+// first half of the MFMAs runs on the lo halves while the hi halves are read;
+// then the step t + 1 operands (in registers since step t - 1) are written to
+// the other stage, the loads for step t + 2 are issued, and one barrier
+// publishes the stage; the second half runs on the hi halves while the next
+// step's lo halves are read. The matrix cores never wait on LDS, only on the
+// barrier.
+template <int TY, int NXK>
+__global__ void __launch_bounds__(NTHREADS)
+__attribute__((amdgpu_waves_per_eu(1, 1)))
+tgemm_f32in_kernel(Args a) {
+    static_assert(ab_of(TY) == 2, "binary32 operands");
+    __shared__ u32x4 smem[2][2][LdsF::kBlock];   // [stage][A | B], 64 KiB
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    int tm, tn;
+    tile_of((int)blockIdx.x, a.W, a.grid_m, a.grid_n, a.group_m, a.num_xcd, &tm, &tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int nk = (a.K + kF32Ks - 1) / kF32Ks;
+    const F32Lanes L = f32_lanes<NXK>(a, tid);
+    const Rsrc rsa = f32_rsrc(a.A, a.lda, a.M, a.K, m0);
+    // B: N x K rows n0.. ; K x N columns n0.. of all K rows
+    const Rsrc rsb = NXK ? f32_rsrc(a.B, a.ldb, a.N, a.K, n0) : f32_rsrc(a.B + 2 * n0, a.ldb, a.K, a.N - n0, 0);
+
+    // stage-0 read positions (8-byte units) of 16-row block 0
+    const int r16 = lane & 15, g = lane >> 4;
+    const f32x2* pa0 = reinterpret_cast<const f32x2*>(smem[0][0]) + 2 * LdsF::slot(wm * 128 + r16, g);
+    const f32x2* pb0 = reinterpret_cast<const f32x2*>(smem[0][1]) + 2 * LdsF::slot(wn * 128 + r16, g);
+
+    f32x4 acc[8][8];
+    zero_acc(acc);
+    F32Frags f;
+    u32x4 ra[4], rb[4];
+    if (nk > 0) {
+        f32_buf_load<NXK>(ra, rb, rsa, rsb, L, a, n0, 0);
+        f32_store_step<NXK>(smem[0][0], smem[0][1], ra, rb, L, a, n0, 0, tid);
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f.alo[i] = pa0[i * 128];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) f.blo[j] = pb0[j * 128];
+        f32_buf_load<NXK>(ra, rb, rsa, rsb, L, a, n0, 1);   // past the last step: zeros
+    }
+    for (int t = 0; t < nk; ++t) {
+        const int st = t & 1;
+        const int so = st * kF32Stage, sn = (st ^ 1) * kF32Stage;
+        f32_half<0, 0, 96>(acc, f, pa0 + so, pb0 + so);
+        // step t + 1 (zeros past the last step) into the other stage, then
+        // the loads of step t + 2 (no branches); the last 32 MFMAs of the half
+        // run while the LDS writes complete, then one barrier publishes the
+        // stage. The section boundaries are pinned (each section is scheduled
+        // freely inside): otherwise the compiler moves matrix instructions
+        // across this block and leaves the next step's reads and the staged
+        // data's selects exposed.
+        TG_COMPILER_FENCE();
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<0>();                              // step t + 1 in the staging registers
+        f32_store_step<NXK>(smem[st ^ 1][0], smem[st ^ 1][1], ra, rb, L, a, n0, t + 1, tid);
+        f32_buf_load<NXK>(ra, rb, rsa, rsb, L, a, n0, t + 2);
+        TG_COMPILER_FENCE();
+        __builtin_amdgcn_sched_barrier(0);
+        f32_half<0, 96, 128>(acc, f, pa0 + so, pb0 + so);
+        TG_COMPILER_FENCE();
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        f32_half<1>(acc, f, pa0 + sn, pb0 + sn);
+        TG_COMPILER_FENCE();
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    store_c<TY>(acc, a, m0, n0, wm, wn, lane);
+}
+
+// One 16-deep K step of the wave's 128 x 128 sub-tile from LDS: 4 x 8 x 8 MFMAs.
 __device__ __forceinline__ void f32_mma_step(f32x4 (&acc)[8][8], const u32x4* __restrict__ sA,
                                              const u32x4* __restrict__ sB, int wm, int wn, int lane) {
     f32x4 af[8], bf[8];
@@ -1118,35 +1354,16 @@ __device__ __forceinline__ void f32_mma_step(f32x4 (&acc)[8][8], const u32x4* __
                 acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(bf[j][e], af[i][e], acc[i][j], 0, 0, 0);
 }
 
-template <int NXK, bool VEC, bool MASK>
-__device__ __forceinline__ void f32_load_stage(u32x4 (&ra)[4], u32x4 (&rb)[4], const Args& a, int m0, int n0,
-                                               int k0, int tid) {
-    const uint32_t* A = reinterpret_cast<const uint32_t*>(a.A);
-    const uint32_t* B = reinterpret_cast<const uint32_t*>(a.B);
-    f32_load_kc<VEC, MASK>(ra, A, a.lda, a.M, a.K, m0, k0, tid);
-    if (NXK)
-        f32_load_kc<VEC, MASK>(rb, B, a.ldb, a.N, a.K, n0, k0, tid);
-    else
-        f32_load_kxn<VEC, MASK>(rb, B, a.ldb, a.N, a.K, n0, k0, tid);
-}
 
-template <int NXK>
-__device__ __forceinline__ void f32_store_stage(u32x4* __restrict__ sA, u32x4* __restrict__ sB,
-                                                const u32x4 (&ra)[4], const u32x4 (&rb)[4], int tid) {
-    f32_store_kc(sA, ra, tid);
-    if (NXK)
-        f32_store_kc(sB, rb, tid);
-    else
-        f32_store_kxn(sB, rb, tid);
-}
 
-// One workgroup per output tile; the next step's operands are loaded into
-// registers while the current step runs on the matrix cores, then written to
+// General kernel (any 4-byte alignment and stride, any K): one workgroup per
+// output tile; the next step's operands are loaded into registers (masked at
+// the edges) while the current step runs on the matrix cores, then written to
 // the other LDS stage (one barrier per step).
 template <int TY, int NXK, bool VEC>
 __global__ void __launch_bounds__(NTHREADS)
 __attribute__((amdgpu_waves_per_eu(1, 1)))
-tgemm_f32in_kernel(Args a) {
+tgemm_f32in_rs_kernel(Args a) {
     static_assert(ab_of(TY) == 2, "binary32 operands");
     __shared__ u32x4 smem[2][2][LdsF::kBlock];   // [stage][A | B], 64 KiB
 

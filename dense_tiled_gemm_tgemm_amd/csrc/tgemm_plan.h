@@ -159,27 +159,37 @@ inline int make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
 
     const bool vec_ab = !force_generic && ((uintptr_t)A % 16 == 0) && ((lda * ab_size) % 16 == 0) &&
                         ((uintptr_t)B % 16 == 0) && ((ldb * ab_size) % 16 == 0);
-    const bool vec_c = ((uintptr_t)C % 8 == 0) && ((ldc * c_size) % 8 == 0);
+    // vector C stores: 8-byte runs of a 16-bit C, 16-byte runs of an fp32 C
+    const int c_vec = c_type == TGEMM_F32 ? 16 : 8;
+    const bool vec_c = ((uintptr_t)C % c_vec == 0) && ((ldc * c_size) % c_vec == 0);
     // direct-to-LDS (any 2-byte alignment: gfx950 buffer loads accept
     // unaligned addresses): row strides small enough for 32-bit panel
     // offsets; a K x N B additionally needs every byte offset it forms,
     // below (K + 64) * ldb * 2 + 512, to stay below 2^31.
     // (K == 0 only writes zeros: the register-staged kernel does that)
-    // (binary32 operands have a kernel of their own, staged through registers)
-    const bool dma = !force_generic && ab_type != TGEMM_F32 && K > 0 && lda <= kMaxDmaLd &&
-                     (b_layout == TGEMM_B_NxK ? ldb <= kMaxDmaLd
-                                              : ldb < (int64_t(1) << 30) && (K + 64) * ldb < (int64_t(1) << 30) - 512);
+    // (binary32 operands have kernels of their own: the kDma bit then marks the
+    // pipelined one, whose buffer loads need K (and, for B stored K x N, N) a
+    // multiple of 4 and every byte offset of a tile below 2^31)
+    const bool dma =
+        ab_type == TGEMM_F32
+            ? (!force_generic && K > 0 && K % 4 == 0 && lda <= kMaxDmaLd / 2 &&
+               (b_layout == TGEMM_B_NxK ? ldb <= kMaxDmaLd / 2
+                                        : N % 4 == 0 && ldb < (int64_t(1) << 29) &&
+                                              (K + 64) * ldb < (int64_t(1) << 29) - 256))
+            : (!force_generic && K > 0 && lda <= kMaxDmaLd &&
+               (b_layout == TGEMM_B_NxK ? ldb <= kMaxDmaLd
+                                        : ldb < (int64_t(1) << 30) && (K + 64) * ldb < (int64_t(1) << 30) - 512));
     pl->variant = (vec_ab ? kVecAB : 0) | (vec_c ? kVecC : 0) |
                   (b_layout == TGEMM_B_NxK ? kLayoutNxK : 0) | (dma ? kDma : 0);
-    if (dma) {
+    if (ab_type == TGEMM_F32) {
+        pl->k_step = kF32KStep;
+        pl->stages = 2;
+    } else if (dma) {
         // a ring deeper than 2 stages implies 32-deep steps; 64-deep steps
         // need at least two steps
         pl->k_step = k_step ? k_step : ((stages > 2 || K <= 64) ? 32 : kDefaultDmaKStep);
         if (pl->k_step == 64 && K <= 64) return TGEMM_ERR_INVALID;
         pl->stages = pl->k_step == 64 ? 2 : (stages ? stages : kDefaultDmaStages32);
-    } else if (ab_type == TGEMM_F32) {
-        pl->k_step = kF32KStep;
-        pl->stages = 2;
     } else {
         pl->k_step = BK;
         pl->stages = 2;

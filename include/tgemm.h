@@ -223,8 +223,10 @@ int tgemm_last_hip_error(void);
 /*
  * Host-only planning query (no GPU call): the launch tgemm_f16_config would
  * make for these arguments. Returns TGEMM_OK and fills info[0..9]:
- *   info[0] variant bits: bit0 128-bit A/B loads, bit1 64-bit C stores,
- *           bit2 B layout is NxK, bit3 operands streamed directly into LDS
+ *   info[0] variant bits: bit0 128-bit A/B loads, bit1 vector C stores
+ *           (64-bit runs of a 16-bit C, 128-bit runs of an fp32 C), bit2 B
+ *           layout is NxK, bit3 the pipelined kernel (16-bit operands:
+ *           streamed directly into LDS; binary32 operands: buffer loads)
  *   info[1] tile rows (BM)   info[2] tile columns (BN)   info[3] K step
  *   info[4] workgroups launched  info[5] group_m  info[6] num_xcd
  *   info[7] threads per workgroup  info[8] LDS stages  info[9] LDS bytes

@@ -276,13 +276,13 @@ def test_typed_ring_depths_other_than_default_are_unsupported():
 
 
 def test_fp32_output_store_width_flags():
-    V, C8, DMA = 1, 2, 8
-    # fp32 C: 8-byte aligned with an even ldc gives 64-bit stores
+    V, CV, DMA = 1, 2, 8
+    # fp32 C: 16-byte-aligned rows (base and 4 * ldc) give 128-bit stores
     rc, info = _plan_ex(256, 256, 256, ct="f32")
-    assert info["variant"] == V | C8 | DMA
-    rc, info = _plan_ex(256, 255, 256, ct="f32", ldb=256, ldc=255)
+    assert info["variant"] == V | CV | DMA
+    rc, info = _plan_ex(256, 254, 256, ct="f32", ldb=256, ldc=254)
     assert info["variant"] == V | DMA
-    rc, info = _plan_ex(256, 256, 256, ct="f32", C=PC + 4)
+    rc, info = _plan_ex(256, 256, 256, ct="f32", C=PC + 8)
     assert info["variant"] == V | DMA
 
 
@@ -322,18 +322,27 @@ def test_tuning_rejects_bad_arguments_without_gpu():
 
 
 def test_fp32_operand_plans():
-    V, C8, NXK, DMA = 1, 2, 4, 8
-    # binary32 operands: register-staged kernel, 16-deep steps, 2 stages of 2 x 256 x 16 floats
+    V, CV, NXK, PIPE = 1, 2, 4, 8
+    # binary32 operands: 16-deep steps, 2 stages of 2 x 256 x 16 floats; the
+    # pipelined kernel when K is a multiple of 4 (and N too for B stored K x N)
     rc, info = _plan_ex(8192, 8192, 8192, ab="f32", ct="f32", lay="NxK")
-    assert rc == 0 and info["variant"] == V | C8 | NXK
+    assert rc == 0 and info["variant"] == V | CV | NXK | PIPE
     assert (info["bk"], info["stages"], info["lds_bytes"], info["workgroups"]) == (16, 2, 64 * 1024, 1024)
-    # launch choices for the direct-to-LDS pipeline do not apply
+    # launch choices for the 16-bit pipelines do not apply
     rc2, info2 = _plan_ex(8192, 8192, 8192, ab="f32", ct="f32", lay="NxK", k_step=32, stages=5)
     assert rc2 == 0 and info2 == info
-    # 16-byte loads need 16-byte rows: lda a multiple of 4 floats
+    # K not a multiple of 4, or N for B stored K x N, or forced: the general kernel
     rc, info = _plan_ex(300, 200, 101, ab="f32", ct="f16", lda=101)
-    assert rc == 0 and info["variant"] == C8
-    rc, info = _plan_ex(300, 200, 100, ab="f32", ct="f16", lda=100, ldb=200)
-    assert rc == 0 and info["variant"] == V | C8
+    assert rc == 0 and info["variant"] == CV
+    rc, info = _plan_ex(300, 202, 100, ab="f32", ct="f16", lda=100, ldb=202, ldc=208)
+    assert rc == 0 and info["variant"] == CV
+    rc, info = _plan_ex(300, 202, 100, ab="f32", ct="f16", lay="NxK", ldc=208)
+    assert rc == 0 and info["variant"] == V | CV | NXK | PIPE
+    rc, info = _plan_ex(300, 200, 100, ab="f32", ct="f16", lda=100, ldb=200, force_generic=1)
+    assert rc == 0 and info["variant"] == CV
+    # 4-byte-aligned bases are fine for the pipelined kernel (buffer loads)
     rc, info = _plan_ex(300, 200, 100, ab="f32", ct="bf16", A=PA + 4)
-    assert rc == 0 and info["variant"] == C8
+    assert rc == 0 and info["variant"] == CV | PIPE
+    # strides past the 32-bit offset limits: the general kernel
+    rc, info = _plan_ex(300, 200, 100, ab="f32", ct="f32", lay="NxK", lda=2_000_004)
+    assert rc == 0 and not info["variant"] & PIPE

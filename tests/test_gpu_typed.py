@@ -354,12 +354,17 @@ def test_f32_operands_small_shapes_full_parity(oracle_mod, M, N, K, ct, lay, epi
         assert torch.equal(C.view(torch.int16), C2.view(torch.int16))
 
 
-@pytest.mark.parametrize("lay,offset,pad", [("KxN", 1, 3), ("NxK", 1, 5), ("NxK", 0, 3), ("KxN", 2, 2)])
-def test_f32_operands_strided_and_offset(oracle_mod, lay, offset, pad):
-    """Operands inside larger buffers: row strides of K + pad (N + pad) floats,
-    bases `offset` floats in (4-byte-aligned only when offset is odd)."""
-    M, N, K = 300, 270, 133
-    print(f"case f32-in strided {lay} offset={offset} pad={pad}", flush=True)
+@pytest.mark.parametrize("lay,offset,pad,N,K", [
+    ("KxN", 1, 3, 270, 133), ("NxK", 1, 5, 270, 133), ("NxK", 0, 3, 270, 133), ("KxN", 2, 2, 270, 133),
+    # K (and N for B stored K x N) multiples of 4: the pipelined kernel (buffer loads)
+    ("KxN", 1, 3, 272, 132), ("NxK", 1, 5, 270, 132), ("NxK", 0, 4, 270, 132), ("KxN", 2, 2, 272, 4100),
+])
+def test_f32_operands_strided_and_offset(oracle_mod, lay, offset, pad, N, K):
+    """Operands inside larger NaN-filled buffers: row strides of K + pad
+    (N + pad) floats, bases `offset` floats in (only 4-byte aligned when offset
+    is odd): NaN past K, past N or after the last row must never reach C."""
+    M = 300
+    print(f"case f32-in strided {lay} offset={offset} pad={pad} N={N} K={K}", flush=True)
     A = _f32((M, K), 91)
     B = _f32((K, N) if lay == "KxN" else (N, K), 92)
     bufA = np.full(offset + M * (K + pad), np.nan, dtype=np.float32)
