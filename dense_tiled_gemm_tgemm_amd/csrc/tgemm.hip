@@ -341,15 +341,15 @@ extern "C" int tgemm_last_hip_error(void) { return tg::g_last_hip_error; }
 static void fill_info(const tg::Plan& pl, int64_t* info) {
     info[0] = pl.variant;
     info[1] = tg::BM;
-    info[2] = tg::BN;
+    info[2] = pl.bn;
     info[3] = pl.k_step;
     info[4] = (pl.M == 0 || pl.N == 0) ? 0 : pl.W;
     info[5] = pl.group_m;
     info[6] = pl.num_xcd;
     info[7] = tg::NTHREADS;
     info[8] = pl.stages;
-    // LDS bytes per workgroup: stages x (A block + B block) x 256 rows x K step
-    info[9] = (int64_t)pl.stages * 2 * 256 * pl.k_step * (pl.ab_type == TGEMM_F32 ? 4 : 2);
+    // LDS bytes per workgroup: stages x (A block + B block rows) x K step x element size
+    info[9] = (int64_t)pl.stages * (tg::BM + pl.bn) * pl.k_step * (pl.ab_type == TGEMM_F32 ? 4 : 2);
 }
 
 extern "C" int tgemm_plan_gemm(int64_t M, int64_t N, int64_t K, int ab_type, const void* A, int64_t lda,

@@ -163,10 +163,11 @@ __device__ __forceinline__ float epi(float x, float alpha, float b, bool relu) {
 
 // Bias values of this lane's 32 columns (column n0 + 128 wn + 16 j + 4 (l / 16)
 // + e in bv[j][e]); zeros past N or without a bias.
-__device__ __forceinline__ void load_bias(float (&bv)[8][4], const Args& a, int n0, int wn, int lane) {
-    const int colb = n0 + wn * 128 + 4 * (lane >> 4);
+template <int NJ>
+__device__ __forceinline__ void load_bias(float (&bv)[NJ][4], const Args& a, int n0, int wn, int lane) {
+    const int colb = n0 + wn * 16 * NJ + 4 * (lane >> 4);
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int col = colb + 16 * j + e;
@@ -175,7 +176,8 @@ __device__ __forceinline__ void load_bias(float (&bv)[8][4], const Args& a, int 
 }
 
 // Lane l of wave (wm, wn) holds, in acc[i][j], C row m0 + 128 wm + 16 i + (l mod 16)
-// at columns n0 + 128 wn + 16 j + 4 (l / 16) + 0..3.
+// at columns n0 + 16 NJ wn + 16 j + 4 (l / 16) + 0..3 (NJ = 8 column blocks per
+// wave, 4 in the two-workgroups-per-unit binary32 kernel).
 //  * 16-bit outputs: for each pair of 16-column blocks (j, j+1),
 //    v_permlane16_swap exchanges the converted words between 16-lane rows so
 //    that a lane in row g then holds the 8 consecutive columns
@@ -191,13 +193,14 @@ __device__ __forceinline__ void load_bias(float (&bv)[8][4], const Args& a, int 
 // All lanes run the exchange; only the stores are predicated. One 16-row block
 // at a time (pinned), so the temporaries stay few when this runs between two
 // tiles with the next tile's fragments already in registers.
-template <int TY>
-__device__ __forceinline__ void store_c(const f32x4 (&acc)[8][8], const Args& a, int m0, int n0, int wm,
+template <int TY, int NJ = 8>
+__device__ __forceinline__ void store_c(const f32x4 (&acc)[8][NJ], const Args& a, int m0, int n0, int wm,
                                         int wn, int lane) {
+    static_assert(NJ == 8 || NJ == 4, "a wave owns 8 or 4 blocks of 16 columns");
     constexpr int CT = ct_of(TY);
     constexpr bool EPI = epi_of(TY);
     const int r16 = lane & 15, g = lane >> 4;
-    float bv[8][4];
+    float bv[NJ][4];
     float alpha = 1.f;
     bool relu = false;
     if constexpr (EPI) {
@@ -206,7 +209,7 @@ __device__ __forceinline__ void store_c(const f32x4 (&acc)[8][8], const Args& a,
         relu = a.relu != 0;
     }
     if constexpr (CT == 2) {
-        const int colb = n0 + wn * 128 + 4 * g;
+        const int colb = n0 + wn * 16 * NJ + 4 * g;
         float* base = static_cast<float*>(a.C) + (int64_t)(m0 + wm * 128 + r16) * a.ldc + colb;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -214,7 +217,7 @@ __device__ __forceinline__ void store_c(const f32x4 (&acc)[8][8], const Args& a,
             const bool row_ok = m0 + wm * 128 + i * 16 + r16 < a.M;
             float* row = base + (int64_t)i * 16 * a.ldc;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+            for (int j = 0; j < NJ; ++j) {
                 const f32x4& x = acc[i][j];
                 f32x4 v;
 #pragma unroll
@@ -231,7 +234,7 @@ __device__ __forceinline__ void store_c(const f32x4 (&acc)[8][8], const Args& a,
             }
         }
     } else {
-        const int col0 = n0 + wn * 128 + (g & 1) * 16 + (g >> 1) * 8;
+        const int col0 = n0 + wn * 16 * NJ + (g & 1) * 16 + (g >> 1) * 8;
         uint16_t* base = static_cast<uint16_t*>(a.C) + (int64_t)(m0 + wm * 128 + r16) * a.ldc + col0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -239,7 +242,7 @@ __device__ __forceinline__ void store_c(const f32x4 (&acc)[8][8], const Args& a,
             const bool row_ok = m0 + wm * 128 + i * 16 + r16 < a.M;
             uint16_t* row = base + (int64_t)i * 16 * a.ldc;
 #pragma unroll
-            for (int pr = 0; pr < 4; ++pr) {
+            for (int pr = 0; pr < NJ / 2; ++pr) {
                 const f32x4& x = acc[i][2 * pr];
                 const f32x4& y = acc[i][2 * pr + 1];
                 const float* bx = bv[2 * pr];
@@ -1110,18 +1113,6 @@ __device__ __forceinline__ void f32_load_stage(u32x4 (&ra)[4], u32x4 (&rb)[4], c
         f32_load_kxn<VEC, MASK>(rb, B, a.ldb, a.N, a.K, n0, k0, tid);
 }
 
-// Operands of step t into registers (whole chunks inside the operands take
-// the unmasked loads).
-template <int NXK, bool VEC>
-__device__ __forceinline__ void f32_load_step(u32x4 (&ra)[4], u32x4 (&rb)[4], const Args& a, int m0, int n0, int t,
-                                              bool interior, int tid) {
-    const int k0 = t * kF32Ks;
-    if (interior && k0 + kF32Ks <= a.K)
-        f32_load_stage<NXK, VEC, false>(ra, rb, a, m0, n0, k0, tid);
-    else
-        f32_load_stage<NXK, VEC, true>(ra, rb, a, m0, n0, k0, tid);
-}
-
 template <int NXK>
 __device__ __forceinline__ void f32_store_stage(u32x4* __restrict__ sA, u32x4* __restrict__ sB,
                                                 const u32x4 (&ra)[4], const u32x4 (&rb)[4], int tid) {
@@ -1136,20 +1127,33 @@ __device__ __forceinline__ f32x4 read_f32_frag(const u32x4* __restrict__ s_blk, 
     return __builtin_bit_cast(f32x4, s_blk[LdsF::slot(half * 128 + blk * 16 + (lane & 15), lane >> 4)]);
 }
 
-// Staging of the pipelined kernel (K a multiple of 4, and N too for B stored
-// K x N, so that no 4-float chunk straddles the end of a row): 16-byte buffer
-// loads through per-tile resources that return zeros past each operand's last
-// element (rows past M or N, and for B stored K x N rows past K); chunks at
-// or past K (columns at or past N) are cleared with selects. No branches, so
-// the accumulators stay in place across the step.
+// Pipelined kernel (K a multiple of 4, and N too for B stored K x N, so that
+// no 4-float chunk straddles the end of a row): tile 256 x 128, 4 waves of
+// 128 x 64 (8 x 4 blocks, 128 accumulators), two workgroups per compute unit
+// (two waves per SIMD from independent workgroups, so one workgroup's barrier
+// and staging gaps are covered by the other's matrix instructions). LDS per
+// workgroup: 2 stages of A (256 rows) and B (128 rows) blocks of 4 chunks,
+// 48 KiB. Staging: 16-byte buffer loads through per-tile resources that
+// return zeros past each operand's last element (rows past M or N, and for B
+// stored K x N rows past K); chunks at or past K (columns at or past N) are
+// cleared with selects when the staged step is written to LDS. No branches,
+// so the accumulators stay in place across a step.
+constexpr int kF32Bn = kF32PipeBn;              // tile columns of the pipelined kernel
+constexpr int kF32ABlk = 256 * 4;               // slots of an A block
+constexpr int kF32BBlk = kF32Bn * 4;            // slots of a B block
+constexpr int kF32StageSlots = kF32ABlk + kF32BBlk;
+
 __device__ __forceinline__ Rsrc f32_rsrc(const uint16_t* X, int64_t ld, int nrows, int ncols, int row0) {
     int64_t span = ((int64_t)(nrows - row0 - 1) * ld + ncols) * 4;
     if (span > (int64_t)kOob - 1) span = (int64_t)kOob - 1;
     return Rsrc{X + (int64_t)row0 * ld * 2, (int)span};
 }
 
+// This lane's loads of a step: A chunks (t & 3) of rows (t >> 2) + 64 p,
+// p = 0..3; B stored N x K chunks (t & 3) of rows (t >> 2) + 64 p, p = 0..1;
+// B stored K x N the 2 x 4 block k = 2 (t >> 5) + 0..1, n = 4 (t & 31) + 0..3.
 struct F32Lanes {
-    unsigned va[4], vb[4];   // byte offsets of this lane's loads from the tile's resource bases
+    unsigned va[4], vb[2];   // byte offsets from the tile's resource bases
     int kc;                  // k offset (floats) of this lane's K-contiguous chunk within a step
     int nc;                  // column offset (floats) of this lane's K x N chunk within the tile
 };
@@ -1162,21 +1166,21 @@ __device__ __forceinline__ F32Lanes f32_lanes(const Args& a, int tid) {
     for (int p = 0; p < 4; ++p) {
         const unsigned row = (unsigned)((tid >> 2) + 64 * p);
         L.va[p] = (row * (unsigned)a.lda + 4u * c) * 4u;
-        if (NXK) L.vb[p] = (row * (unsigned)a.ldb + 4u * c) * 4u;
+        if (NXK && p < 2) L.vb[p] = (row * (unsigned)a.ldb + 4u * c) * 4u;
     }
     if (!NXK) {
-        const unsigned kr = (unsigned)(4 * (tid >> 6)), nb = (unsigned)(tid & 63);
+        const unsigned kr = (unsigned)(2 * (tid >> 5)), nb = (unsigned)(tid & 31);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) L.vb[q] = ((kr + (unsigned)q) * (unsigned)a.ldb + 4u * nb) * 4u;
+        for (int q = 0; q < 2; ++q) L.vb[q] = ((kr + (unsigned)q) * (unsigned)a.ldb + 4u * nb) * 4u;
     }
     L.kc = 4 * (tid & 3);
-    L.nc = 4 * (tid & 63);
+    L.nc = 4 * (tid & 31);
     return L;
 }
 
 template <int NXK>
-__device__ __forceinline__ void f32_buf_load(u32x4 (&ra)[4], u32x4 (&rb)[4], const Rsrc& rsa, const Rsrc& rsb,
-                                             const F32Lanes& L, const Args& a, int n0, int t) {
+__device__ __forceinline__ void f32_buf_load(u32x4 (&ra)[4], u32x4 (&rb)[2], const Rsrc& rsa, const Rsrc& rsb,
+                                             const F32Lanes& L, const Args& a, int t) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the host pass cannot instantiate these target builtins
     const int k0 = t * kF32Ks;
     const __amdgpu_buffer_rsrc_t xa = __builtin_amdgcn_make_buffer_rsrc((void*)rsa.base, 0, rsa.nrec, 0x00020000);
@@ -1187,72 +1191,71 @@ __device__ __forceinline__ void f32_buf_load(u32x4 (&ra)[4], u32x4 (&rb)[4], con
     for (int p = 0; p < 4; ++p)
         ra[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xa, (int)L.va[p], (int)soa, 0));
 #pragma unroll
-    for (int p = 0; p < 4; ++p)
+    for (int p = 0; p < 2; ++p)
         rb[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xb, (int)L.vb[p], (int)sob, 0));
 #else
-    (void)ra; (void)rb; (void)rsa; (void)rsb; (void)L; (void)a; (void)n0; (void)t;
+    (void)ra; (void)rb; (void)rsa; (void)rsb; (void)L; (void)a; (void)t;
 #endif
 }
 
-// Write step t's staged operands into an LDS stage, clearing chunks at or past
-// K (columns at or past N for B stored K x N). The selects sit here, a half
-// step after the loads were issued, so they never wait on memory inside the
-// matrix-instruction stream.
+// Write step t's staged operands into an LDS stage (A block at `s`, B block
+// kF32ABlk slots later), clearing chunks at or past K (columns at or past N
+// for B stored K x N). The selects sit here, a half step after the loads were
+// issued, so they never wait on memory inside the matrix-instruction stream.
 template <int NXK>
-__device__ __forceinline__ void f32_store_step(u32x4* __restrict__ sA, u32x4* __restrict__ sB, u32x4 (&ra)[4],
-                                               u32x4 (&rb)[4], const F32Lanes& L, const Args& a, int n0, int t,
-                                               int tid) {
+__device__ __forceinline__ void f32_store_step(u32x4* __restrict__ s, u32x4 (&ra)[4], u32x4 (&rb)[2],
+                                               const F32Lanes& L, const Args& a, int n0, int t, int tid) {
     const bool k_ok = t * kF32Ks + L.kc < a.K;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) ra[p] = k_ok ? ra[p] : u32x4{};
+    for (int p = 0; p < 4; ++p) s[LdsF::slot((tid >> 2) + 64 * p, tid & 3)] = k_ok ? ra[p] : u32x4{};
+    u32x4* sb = s + kF32ABlk;
     if (NXK) {
 #pragma unroll
-        for (int p = 0; p < 4; ++p) rb[p] = k_ok ? rb[p] : u32x4{};
+        for (int p = 0; p < 2; ++p) sb[LdsF::slot((tid >> 2) + 64 * p, tid & 3)] = k_ok ? rb[p] : u32x4{};
     } else {
+        // 2 x 4 block -> 4 rows (columns n) x 2 floats (k = 2 (t >> 5) + 0..1):
+        // 8-byte half (t >> 5) & 1 of chunk (t >> 6) of row 4 (t & 31) + v
         const bool n_ok = n0 + L.nc < a.N;
+        u32x2* sb2 = reinterpret_cast<u32x2*>(sb);
+        const int kp = tid >> 5, nb = tid & 31;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) rb[q] = n_ok ? rb[q] : u32x4{};
+        for (int v = 0; v < 4; ++v)
+            sb2[2 * LdsF::slot(4 * nb + v, kp >> 1) + (kp & 1)] = n_ok ? u32x2{rb[0][v], rb[1][v]} : u32x2{};
     }
-    f32_store_stage<NXK>(sA, sB, ra, rb, tid);
 }
 
 // The wave's fragments as 8-byte halves of its 16-byte chunks: lo = k0 + 4g +
 // 0..1 (MFMAs e = 0, 1), hi = k0 + 4g + 2..3 (e = 2, 3).
 struct F32Frags {
-    f32x2 alo[8], ahi[8], blo[8], bhi[8];
+    f32x2 alo[8], ahi[8], blo[4], bhi[4];
 };
 
-// This lane's 8-byte read position of 16-row block 0 in stage 0 of A (B):
-// block i lies 128 positions further (16 rows x 4 chunks x 2 halves), stage 1
-// kF32Stage positions further, the hi half 1 further.
-constexpr int kF32Stage = 2 * 2 * LdsF::kBlock;   // 8-byte units per stage (A and B blocks)
-
-// Half of a step's MFMAs (EH = 0: e = 0, 1 on the lo halves; EH = 1: e = 2,
-// 3 on the hi halves), 128 MFMAs walking the 8 x 8 blocks in serpentine order
-// twice, with the 16 reads of the other halves placed after every eighth
+// Half of a step's MFMAs, [Q0, Q1) of 64 (EH = 0: e = 0, 1 on the lo halves;
+// EH = 1: e = 2, 3 on the hi halves), walking the 8 x 4 blocks in serpentine
+// order twice, with the 12 reads of the other halves placed after every fifth
 // MFMA: EH = 0 reads this step's hi halves, EH = 1 the next step's lo halves
-// (from `pa` / `pb`, in the order the next half consumes them: A0, B0..B7,
-// A1..A7). The compiler schedules the section: pinning it instruction by
-// instruction, as in the 16-bit kernels, makes the register allocator rotate
-// all 256 accumulators at every step here.
-template <int EH, int Q0 = 0, int Q1 = 128>
-__device__ __forceinline__ void f32_half(f32x4 (&acc)[8][8], F32Frags& f, const f32x2* __restrict__ pa,
+// (from `pa` / `pb`, in the order the next half consumes them: A0, B0..B3,
+// A1..A7). The compiler schedules inside a section; pinning it instruction
+// by instruction, as in the 16-bit kernels, makes the register allocator
+// rotate the accumulators at every step here.
+template <int EH, int Q0 = 0, int Q1 = 64>
+__device__ __forceinline__ void f32_half(f32x4 (&acc)[8][4], F32Frags& f, const f32x2* __restrict__ pa,
                                          const f32x2* __restrict__ pb) {
     constexpr int kHalf = EH ? 0 : 1;                 // which half the reads fill
 #pragma unroll
     for (int q = Q0; q < Q1; ++q) {
-        const int e = q >> 6, x = q & 63;
-        const int i = x >> 3, j = (i & 1) ? 7 - (x & 7) : (x & 7);
+        const int e = q >> 5, x = q & 31;
+        const int i = x >> 2, j = (i & 1) ? 3 - (x & 3) : (x & 3);
         const f32x2& av = EH ? f.ahi[i] : f.alo[i];
         const f32x2& bv = EH ? f.bhi[j] : f.blo[j];
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(bv[e], av[e], acc[i][j], 0, 0, 0);
-        if ((q & 7) == 7) {
-            const int r = q >> 3;                     // 0 .. 15
-            if (r >= 1 && r <= 8) {
+        if (q % 5 == 4 && q / 5 < 12) {
+            const int r = q / 5;                      // 0 .. 11
+            if (r >= 1 && r <= 4) {
                 f32x2& d = EH ? f.blo[r - 1] : f.bhi[r - 1];
                 d = pb[(r - 1) * 128 + kHalf];
             } else {
-                const int ai = r == 0 ? 0 : r - 8;
+                const int ai = r == 0 ? 0 : r - 4;
                 f32x2& d = EH ? f.alo[ai] : f.ahi[ai];
                 d = pa[ai * 128 + kHalf];
             }
@@ -1260,19 +1263,20 @@ __device__ __forceinline__ void f32_half(f32x4 (&acc)[8][8], F32Frags& f, const 
     }
 }
 
-// One workgroup per output tile. Per 16-deep step t (LDS stage t mod 2): the
-// first half of the MFMAs runs on the lo halves while the hi halves are read;
-// then the step t + 1 operands (in registers since step t - 1) are written to
-// the other stage, the loads for step t + 2 are issued, and one barrier
-// publishes the stage; the second half runs on the hi halves while the next
-// step's lo halves are read. The matrix cores never wait on LDS, only on the
-// barrier.
+// Per 16-deep step t (LDS stage t mod 2): the first 48 MFMAs of the lo half
+// while the hi halves are read; the step t + 1 operands (staged since step
+// t - 1) are written to the other stage and the loads of step t + 2 issued;
+// the last 16 MFMAs of the lo half cover the LDS writes; one barrier
+// publishes the stage; the hi half runs while the next step's lo halves are
+// read. The section boundaries are pinned: otherwise the compiler moves
+// matrix instructions across the staging block and leaves the next step's
+// reads exposed.
 template <int TY, int NXK>
 __global__ void __launch_bounds__(NTHREADS)
-__attribute__((amdgpu_waves_per_eu(1, 1)))
+__attribute__((amdgpu_waves_per_eu(2, 2)))
 tgemm_f32in_kernel(Args a) {
     static_assert(ab_of(TY) == 2, "binary32 operands");
-    __shared__ u32x4 smem[2][2][LdsF::kBlock];   // [stage][A | B], 64 KiB
+    __shared__ u32x4 smem[2 * kF32StageSlots];   // [stage][A block | B block], 48 KiB
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1281,51 +1285,49 @@ tgemm_f32in_kernel(Args a) {
 
     int tm, tn;
     tile_of((int)blockIdx.x, a.W, a.grid_m, a.grid_n, a.group_m, a.num_xcd, &tm, &tn);
-    const int m0 = tm * BM, n0 = tn * BN;
+    const int m0 = tm * BM, n0 = tn * kF32Bn;
     const int nk = (a.K + kF32Ks - 1) / kF32Ks;
     const F32Lanes L = f32_lanes<NXK>(a, tid);
     const Rsrc rsa = f32_rsrc(a.A, a.lda, a.M, a.K, m0);
     // B: N x K rows n0.. ; K x N columns n0.. of all K rows
     const Rsrc rsb = NXK ? f32_rsrc(a.B, a.ldb, a.N, a.K, n0) : f32_rsrc(a.B + 2 * n0, a.ldb, a.K, a.N - n0, 0);
 
-    // stage-0 read positions (8-byte units) of 16-row block 0
+    // stage-0 read positions (8-byte units) of 16-row block 0; block i lies
+    // 128 further, stage 1 2 * kF32StageSlots further, the hi half 1 further
     const int r16 = lane & 15, g = lane >> 4;
-    const f32x2* pa0 = reinterpret_cast<const f32x2*>(smem[0][0]) + 2 * LdsF::slot(wm * 128 + r16, g);
-    const f32x2* pb0 = reinterpret_cast<const f32x2*>(smem[0][1]) + 2 * LdsF::slot(wn * 128 + r16, g);
+    const f32x2* pa0 = reinterpret_cast<const f32x2*>(smem) + 2 * LdsF::slot(wm * 128 + r16, g);
+    const f32x2* pb0 = reinterpret_cast<const f32x2*>(smem + kF32ABlk) + 2 * LdsF::slot(wn * 64 + r16, g);
+    constexpr int kStage2 = 2 * kF32StageSlots;
 
-    f32x4 acc[8][8];
-    zero_acc(acc);
+    f32x4 acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{};
     F32Frags f;
-    u32x4 ra[4], rb[4];
+    u32x4 ra[4], rb[2];
     if (nk > 0) {
-        f32_buf_load<NXK>(ra, rb, rsa, rsb, L, a, n0, 0);
-        f32_store_step<NXK>(smem[0][0], smem[0][1], ra, rb, L, a, n0, 0, tid);
+        f32_buf_load<NXK>(ra, rb, rsa, rsb, L, a, 0);
+        f32_store_step<NXK>(smem, ra, rb, L, a, n0, 0, tid);
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < 8; ++i) f.alo[i] = pa0[i * 128];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) f.blo[j] = pb0[j * 128];
-        f32_buf_load<NXK>(ra, rb, rsa, rsb, L, a, n0, 1);   // past the last step: zeros
+        for (int j = 0; j < 4; ++j) f.blo[j] = pb0[j * 128];
+        f32_buf_load<NXK>(ra, rb, rsa, rsb, L, a, 1);   // past the last step: zeros
     }
     for (int t = 0; t < nk; ++t) {
         const int st = t & 1;
-        const int so = st * kF32Stage, sn = (st ^ 1) * kF32Stage;
-        f32_half<0, 0, 96>(acc, f, pa0 + so, pb0 + so);
-        // step t + 1 (zeros past the last step) into the other stage, then
-        // the loads of step t + 2 (no branches); the last 32 MFMAs of the half
-        // run while the LDS writes complete, then one barrier publishes the
-        // stage. The section boundaries are pinned (each section is scheduled
-        // freely inside): otherwise the compiler moves matrix instructions
-        // across this block and leaves the next step's reads and the staged
-        // data's selects exposed.
+        const int so = st * kStage2, sn = (st ^ 1) * kStage2;
+        f32_half<0, 0, 48>(acc, f, pa0 + so, pb0 + so);
         TG_COMPILER_FENCE();
         __builtin_amdgcn_sched_barrier(0);
         wait_vmcnt<0>();                              // step t + 1 in the staging registers
-        f32_store_step<NXK>(smem[st ^ 1][0], smem[st ^ 1][1], ra, rb, L, a, n0, t + 1, tid);
-        f32_buf_load<NXK>(ra, rb, rsa, rsb, L, a, n0, t + 2);
+        f32_store_step<NXK>(smem + (st ^ 1) * kF32StageSlots, ra, rb, L, a, n0, t + 1, tid);
+        f32_buf_load<NXK>(ra, rb, rsa, rsb, L, a, t + 2);
         TG_COMPILER_FENCE();
         __builtin_amdgcn_sched_barrier(0);
-        f32_half<0, 96, 128>(acc, f, pa0 + so, pb0 + so);
+        f32_half<0, 48, 64>(acc, f, pa0 + so, pb0 + so);
         TG_COMPILER_FENCE();
         __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
@@ -1334,7 +1336,7 @@ tgemm_f32in_kernel(Args a) {
         TG_COMPILER_FENCE();
         __builtin_amdgcn_sched_barrier(0);
     }
-    store_c<TY>(acc, a, m0, n0, wm, wn, lane);
+    store_c<TY, 4>(acc, a, m0, n0, wm, wn, lane);
 }
 
 // One 16-deep K step of the wave's 128 x 128 sub-tile from LDS: 4 x 8 x 8 MFMAs.

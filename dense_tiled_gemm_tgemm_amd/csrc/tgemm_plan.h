@@ -28,7 +28,8 @@ constexpr int kDefaultNumXcd = 8;        // MI355X: 8 accelerator dies of 32 CUs
 // K step 64, 32 KiB at K step 32). 64-deep steps take a 2-stage ring.
 constexpr int kDefaultDmaKStep = 64;
 constexpr int kDefaultDmaStages32 = 4;     // ring depth when the K step is 32
-constexpr int kF32KStep = 16;              // K step (floats) of the binary32-operand kernel
+constexpr int kF32KStep = 16;              // K step (floats) of the binary32-operand kernels
+constexpr int kF32PipeBn = 128;            // tile columns of the pipelined binary32-operand kernel
 
 enum : int { kVecAB = 1, kVecC = 2, kLayoutNxK = 4, kDma = 8 };
 
@@ -69,6 +70,7 @@ struct Plan {
     int c_type;        // TGEMM_F16, TGEMM_BF16 or TGEMM_F32
     bool epi;          // scale, bias or activation requested (else C = A * B as it is)
     int variant;       // kVecAB | kVecC | kLayoutNxK | kDma bits
+    int bn;            // tile columns of the launched kernel (BN, or kF32PipeBn)
     int grid_m, grid_n, W;
     int group_m, num_xcd;
     int k_step, stages;   // K step per LDS stage and ring depth of the launched kernel
@@ -136,8 +138,8 @@ inline int make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
     if (bias && ((uintptr_t)bias & 3)) return TGEMM_ERR_INVALID;
     if (overlaps(C, nc, bias, nbias)) return TGEMM_ERR_INVALID;
 
-    const int64_t gm = (M + BM - 1) / BM, gn = (N + BN - 1) / BN;
-    if (gm * gn > kMaxDim) return TGEMM_ERR_UNSUPPORTED;
+    // tile grid: fixed below once the kernel (and its tile width) is known
+    const int64_t gm = (M + BM - 1) / BM;
 
     pl->M = (int)M;
     pl->N = (int)N;
@@ -149,9 +151,6 @@ inline int make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
     pl->ab_type = ab_type;
     pl->c_type = c_type;
     pl->epi = epi;
-    pl->grid_m = (int)gm;
-    pl->grid_n = (int)gn;
-    pl->W = (int)(gm * gn);
     int g = group_m ? group_m : kDefaultGroupM;
     if (gm > 0 && g > gm) g = (int)gm;
     pl->group_m = g > 0 ? g : 1;
@@ -194,6 +193,12 @@ inline int make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
         pl->k_step = BK;
         pl->stages = 2;
     }
+    pl->bn = (ab_type == TGEMM_F32 && dma) ? kF32PipeBn : BN;
+    const int64_t gn = (N + pl->bn - 1) / pl->bn;
+    if (gm * gn > kMaxDim) return TGEMM_ERR_UNSUPPORTED;
+    pl->grid_m = (int)gm;
+    pl->grid_n = (int)gn;
+    pl->W = (int)(gm * gn);
     return TGEMM_OK;
 }
 

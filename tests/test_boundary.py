@@ -327,7 +327,9 @@ def test_fp32_operand_plans():
     # pipelined kernel when K is a multiple of 4 (and N too for B stored K x N)
     rc, info = _plan_ex(8192, 8192, 8192, ab="f32", ct="f32", lay="NxK")
     assert rc == 0 and info["variant"] == V | CV | NXK | PIPE
-    assert (info["bk"], info["stages"], info["lds_bytes"], info["workgroups"]) == (16, 2, 64 * 1024, 1024)
+    # the pipelined kernel's tile is 256 x 128 (two workgroups per compute unit)
+    assert (info["bm"], info["bn"]) == (256, 128)
+    assert (info["bk"], info["stages"], info["lds_bytes"], info["workgroups"]) == (16, 2, 48 * 1024, 2048)
     # launch choices for the 16-bit pipelines do not apply
     rc2, info2 = _plan_ex(8192, 8192, 8192, ab="f32", ct="f32", lay="NxK", k_step=32, stages=5)
     assert rc2 == 0 and info2 == info
@@ -340,6 +342,7 @@ def test_fp32_operand_plans():
     assert rc == 0 and info["variant"] == V | CV | NXK | PIPE
     rc, info = _plan_ex(300, 200, 100, ab="f32", ct="f16", lda=100, ldb=200, force_generic=1)
     assert rc == 0 and info["variant"] == CV
+    assert (info["bn"], info["lds_bytes"], info["workgroups"]) == (256, 64 * 1024, 2)
     # 4-byte-aligned bases are fine for the pipelined kernel (buffer loads)
     rc, info = _plan_ex(300, 200, 100, ab="f32", ct="bf16", A=PA + 4)
     assert rc == 0 and info["variant"] == CV | PIPE
