@@ -92,7 +92,9 @@ int tgemm_f16(int64_t M, int64_t N, int64_t K,
  *   force_generic: 1 = use element-wise operand loads even where 128-bit
  *                  loads are possible (same results); 0 = automatic.
  *   group_m:       tile-rows per raster group (page 1, section "Swizzle",
- *                  GROUP_SIZE_M); 0 = default (8); 1..1024 otherwise.
+ *                  GROUP_SIZE_M, counted in its 128-row tiles); 0 = default
+ *                  (4 of these 256-row tiles: the same 1024 rows as the
+ *                  page's 8); 1..1024 otherwise.
  *   num_xcd:       number of dies the workgroups are spread over for the
  *                  die-aware renumbering; 0 = default (8 on MI355X);
  *                  1 disables the renumbering; 1..64 otherwise.

@@ -108,7 +108,7 @@ def test_plan_variants_and_grid():
     rc, info = _plan(8192, 8192, 8192, lay="NxK")
     assert rc == 0
     assert info["variant"] == V | C8 | NXK | DMA
-    assert info["workgroups"] == 32 * 32 and info["group_m"] == 8 and info["num_xcd"] == 8
+    assert info["workgroups"] == 32 * 32 and info["group_m"] == 4 and info["num_xcd"] == 8
     assert (info["bm"], info["bn"], info["threads"]) == (256, 256, 256)
     assert (info["bk"], info["stages"], info["lds_bytes"]) == (64, 2, 128 * 1024)
     rc, info = _plan(8192, 8192, 8192, lay="NxK", k_step=32)

@@ -43,7 +43,7 @@ def test_tuned_choice_is_recorded_used_and_changes_no_bits():
     base = tg.mm(A, B, "NxK")
     C = torch.empty_like(base)
     rc0, plan0 = _plan(A, B, C, "NxK", "f16", "f16")
-    assert rc0 == 0 and (plan0["bk"], plan0["stages"], plan0["group_m"]) == (64, 2, 8)
+    assert rc0 == 0 and (plan0["bk"], plan0["stages"], plan0["group_m"]) == (64, 2, 4)
     C, chosen = tg.tune(A, B, "NxK", out=C, rounds=3)
     torch.cuda.synchronize()
     print(f"  chosen {chosen}", flush=True)
@@ -58,7 +58,7 @@ def test_tuned_choice_is_recorded_used_and_changes_no_bits():
     # another key (other types) is not affected
     C32 = torch.empty((M, N), dtype=torch.float32, device=DEV)
     rc, plan32 = _plan(A, B, C32, "NxK", "f16", "f32")
-    assert (plan32["bk"], plan32["stages"], plan32["group_m"]) == (64, 2, 8)
+    assert (plan32["bk"], plan32["stages"], plan32["group_m"]) == (64, 2, 4)
     # the tuned automatic call gives the same bits
     again = tg.mm(A, B, "NxK")
     torch.cuda.synchronize()
