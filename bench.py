@@ -112,6 +112,10 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default=None)
+    ap.add_argument("--warmup-seconds", type=float, default=0.3,
+                    help="after --warmup launches, keep launching until this much time has passed: the board's "
+                         "power-limited clock settles over tens of milliseconds of sustained load, which a fixed "
+                         "launch count does not give small problems")
     ap.add_argument("--ab", choices=("f16", "bf16", "f32"), default="f16", help="operand type")
     ap.add_argument("--out", choices=("f16", "bf16", "f32"), default="f16", help="output type")
     ap.add_argument("--epilogue", action="store_true", help="alpha = 0.5, seeded fp32 bias, rectifier")
@@ -257,9 +261,18 @@ def main():
             raise tg.TgemmError(rc, "tune")
         log(f"bench: tuned choice {tuned}")
 
+    t_w = time.perf_counter()
+    n_warm = 0
     for _ in range(args.warmup):
         step()
+        n_warm += 1
     torch.cuda.synchronize()
+    while time.perf_counter() - t_w < args.warmup_seconds:
+        for _ in range(16):
+            step()
+            n_warm += 1
+        torch.cuda.synchronize()
+    log(f"bench: {n_warm} warm-up launches in {time.perf_counter() - t_w:.3f} s")
 
     # events recorded on the launch stream between consecutive launches
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
@@ -292,6 +305,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_launches": n_warm,
         "ms_per_step": round(region_ms / args.steps, 5),
         "higher_is_better": True,
         "scaling": "weak",

@@ -166,7 +166,10 @@ static int launch(const Plan& pl, const void* fn, const void* A, const void* B, 
     args.group_m = pl.group_m;
     args.num_xcd = pl.num_xcd;
     args.grid = pl.W;
-    args.c16 = ((uintptr_t)C % 16 == 0) && ((pl.ldc * c_size) % 16 == 0);
+    // 16-byte C stores: rows 16-byte aligned, and every byte offset inside a
+    // wave's 128 rows below 2^31 (they go through a 32-bit buffer offset)
+    args.c16 = ((uintptr_t)C % 16 == 0) && ((pl.ldc * c_size) % 16 == 0) &&
+               (127 * pl.ldc + (int64_t)pl.N) * c_size + 16 < (int64_t(1) << 31);
     args.c8 = (pl.variant & kVecC) != 0;
     if (persistent(pl)) {
         // one workgroup per compute unit, each walking several tiles

@@ -175,6 +175,37 @@ __device__ __forceinline__ void load_bias(float (&bv)[NJ][4], const Args& a, int
         }
 }
 
+// 16-byte C stores go through a buffer resource over the wave's 128 C rows
+// (the host keeps this path only where every byte offset in those rows fits
+// in 31 bits) with the streaming policy nt sc1: C is written once and never
+// read back, and every workgroup stores its tile at about the same time, so
+// the burst drains faster when the lines bypass the caches' normal
+// replacement (measured at 8192^3: +2.3% with an fp32 C against nt alone,
+// and 3-4% against plain stores).
+#if defined(__HIP_DEVICE_COMPILE__)
+typedef __amdgpu_buffer_rsrc_t BufRsrc;
+#else
+typedef int BufRsrc;                                  // host pass: never used
+#endif
+constexpr int kCStorePolicy = 2 | 16;                 // nt | sc1
+
+__device__ __forceinline__ BufRsrc c_rows_rsrc(void* C, int64_t byte_offset) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_amdgcn_make_buffer_rsrc(static_cast<char*>(C) + byte_offset, 0, 0x7fffffff, 0x00020000);
+#else
+    (void)C; (void)byte_offset;
+    return 0;
+#endif
+}
+
+__device__ __forceinline__ void store16_stream(const u32x4& v, const BufRsrc& r, int64_t byte_offset) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)byte_offset, 0, kCStorePolicy);
+#else
+    (void)v; (void)r; (void)byte_offset;
+#endif
+}
+
 // Lane l of wave (wm, wn) holds, in acc[i][j], C row m0 + 128 wm + 16 i + (l mod 16)
 // at columns n0 + 16 NJ wn + 16 j + 4 (l / 16) + 0..3 (NJ = 8 column blocks per
 // wave, 4 in the two-workgroups-per-unit binary32 kernel).
@@ -192,11 +223,9 @@ __device__ __forceinline__ void load_bias(float (&bv)[NJ][4], const Args& a, int
 //    the main loop of the binary32-operand kernel).
 // All lanes run the exchange; only the stores are predicated. One 16-row block
 // at a time (pinned), so the temporaries stay few when this runs between two
-// tiles with the next tile's fragments already in registers. The vector stores
-// are non-temporal: C is written once and not read back, and every workgroup
-// stores its tile at about the same time, so keeping the lines out of the
-// caches' normal replacement lets the burst drain faster (measured 1.4% at
-// 8192^3 with a binary16 C, 4.2% with an fp32 C).
+// tiles with the next tile's fragments already in registers. Vector stores
+// use the streaming policies (store16_stream above; the 8-byte path is
+// non-temporal).
 template <int TY, int NJ = 8>
 __device__ __forceinline__ void store_c(const f32x4 (&acc)[8][NJ], const Args& a, int m0, int n0, int wm,
                                         int wn, int lane) {
@@ -204,6 +233,7 @@ __device__ __forceinline__ void store_c(const f32x4 (&acc)[8][NJ], const Args& a
     constexpr int CT = ct_of(TY);
     constexpr bool EPI = epi_of(TY);
     const int r16 = lane & 15, g = lane >> 4;
+    const BufRsrc crs = c_rows_rsrc(a.C, (int64_t)(m0 + wm * 128) * a.ldc * (CT == 2 ? 4 : 2));
     float bv[NJ][4];
     float alpha = 1.f;
     bool relu = false;
@@ -229,7 +259,7 @@ __device__ __forceinline__ void store_c(const f32x4 (&acc)[8][NJ], const Args& a
                 const int col = colb + 16 * j;
                 float* dst = row + 16 * j;
                 if (row_ok && col + 4 <= a.N && a.c16) {
-                    __builtin_nontemporal_store(v, (f32x4*)dst);
+                    store16_stream(__builtin_bit_cast(u32x4, v), crs, ((int64_t)(i * 16 + r16) * a.ldc + colb + 16 * j) * 4);
                 } else if (row_ok && col < a.N) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
@@ -265,7 +295,7 @@ __device__ __forceinline__ void store_c(const f32x4 (&acc)[8][NJ], const Args& a
                 const int col = col0 + 32 * pr;
                 uint16_t* dst = row + 32 * pr;
                 if (row_ok && col + 8 <= a.N && a.c16) {
-                    __builtin_nontemporal_store(v, (u32x4*)dst);
+                    store16_stream(v, crs, ((int64_t)(i * 16 + r16) * a.ldc + col0 + 32 * pr) * 2);
                 } else if (row_ok && col + 8 <= a.N && a.c8) {
                     __builtin_nontemporal_store(u32x2{v[0], v[1]}, (u32x2*)dst);
                     __builtin_nontemporal_store(u32x2{v[2], v[3]}, (u32x2*)(dst + 4));

@@ -24,8 +24,8 @@ constexpr int NTHREADS = 256;            // 4 waves of 64 lanes, 2 x 2 over the 
 
 // Raster group height in tiles. Page 1, section "Swizzle", groups 8 tile-rows
 // of 128 rows (GROUP_SIZE_M = 8 with tm = 128): 1024 rows of A per group. With
-// 256-row tiles the same 1024 rows are 4 tile-rows; measured on MI355X, 4 beat
-// 8 at every square and projection shape tried (1.3-6%).
+// 256-row tiles the same 1024 rows are 4 tile-rows (on MI355X, 4 and 8 measure
+// the same within noise at 8192^3 and on the projection shape).
 constexpr int kDefaultGroupM = 4;
 constexpr int kDefaultNumXcd = 8;        // MI355X: 8 accelerator dies of 32 CUs
 // Direct-to-LDS pipeline: K step and LDS ring depth (a stage holds 64 KiB at
