@@ -445,3 +445,83 @@ def test_f32_operands_k_zero_and_raster():
     other = tg.gemm(A, B, "NxK", out_dtype=torch.float32, group_m=3, num_xcd=1)
     torch.cuda.synchronize()
     assert torch.equal(base, other)
+
+
+@pytest.mark.parametrize("ct,ldc", [("f16", 17_000_000), ("f32", 4_400_000), ("f16", 8_000_000)])
+def test_c_row_stride_beyond_buffer_offsets(oracle_mod, ct, ldc):
+    """16-byte C stores use 32-bit offsets within a wave's 128 rows; a C whose
+    row stride puts those offsets past 2^31 takes the 8-byte stores instead
+    (ldc 17e6 for binary16, 4.4e6 for fp32), one just below keeps them
+    (8e6). Two rows only, so the allocation stays small."""
+    M, N, K = 2, 300, 96
+    print(f"case typed large ldc {ct} {ldc}", flush=True)
+    A = _bits((M, K), 81, "bf16")
+    B = _bits((K, N), 82, "bf16")
+    total = (M - 1) * ldc + N
+    C = torch.full((total,), float("nan"), dtype=TORCH_DT[ct], device=DEV)
+    Ad, Bd = _dev(A, "bf16"), _dev(B, "bf16")          # kept alive until the launch has run
+    rc = tg.tgemm_gemm(M, N, K, "bf16", Ad.data_ptr(), K, Bd.data_ptr(), N, "KxN", ct,
+                       C.data_ptr(), ldc, 1.0, None, "none", torch.cuda.current_stream().cuda_stream)
+    assert rc == tg.TGEMM_OK
+    torch.cuda.synchronize()
+    rows = torch.stack([C[0:N], C[ldc:ldc + N]])
+    got = _out_np(rows.contiguous())
+    _check(oracle_mod, A, B, "KxN", "bf16", ct, got, 1.0, None, "none", f"ldc {ldc}")
+    gap = C[N:ldc]                                      # the padding between the two rows is untouched
+    assert bool(torch.isnan(gap.float()).all())
+
+
+def test_graph_capture_replays_match_eager():
+    """One launch per call, no allocation, no synchronization: the typed entry
+    point can be captured in a HIP graph. Each replay (with new operands copied
+    into the captured buffers, and eager work between replays) equals the eager
+    result bit for bit."""
+    print("case typed graph capture", flush=True)
+    M, N, K = 1000, 900, 700
+    A = torch.empty((M, K), dtype=torch.bfloat16, device=DEV)
+    B = torch.empty((N, K), dtype=torch.bfloat16, device=DEV)
+    bias = torch.from_numpy(inputs.random_bias(N, 90)).to(DEV)
+    C = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    A.copy_(_dev(_bits((M, K), 91, "bf16"), "bf16"))
+    B.copy_(_dev(_bits((N, K), 92, "bf16"), "bf16"))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):                        # warm-up outside the graph
+        tg.gemm(A, B, "NxK", out=C, alpha=0.5, bias=bias, act="relu")
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        tg.gemm(A, B, "NxK", out=C, alpha=0.5, bias=bias, act="relu")
+    for rep in range(4):
+        A.copy_(_dev(_bits((M, K), 100 + rep, "bf16"), "bf16"))
+        B.copy_(_dev(_bits((N, K), 200 + rep, "bf16"), "bf16"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = C.clone()
+        eager = tg.gemm(A, B, "NxK", out_dtype=torch.float32, alpha=0.5, bias=bias, act="relu")
+        torch.cuda.synchronize()
+        assert torch.equal(got, eager), rep
+
+
+def test_concurrent_streams():
+    """Two products in flight on two streams, each equal to its lone result."""
+    print("case typed two streams", flush=True)
+    A1, B1 = _dev(_bits((2048, 1024), 301, "f16"), "f16"), _dev(_bits((3072, 1024), 302, "f16"), "f16")
+    A2, B2 = _dev(_bits((1536, 2048), 303, "bf16"), "bf16"), _dev(_bits((2048, 2560), 304, "bf16"), "bf16")
+    ref1 = tg.gemm(A1, B1, "NxK")
+    ref2 = tg.gemm(A2, B2, "KxN", out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            c1 = tg.gemm(A1, B1, "NxK")
+        with torch.cuda.stream(s2):
+            c2 = tg.gemm(A2, B2, "KxN", out_dtype=torch.float32)
+        outs.append((c1, c2))
+    torch.cuda.synchronize()
+    for c1, c2 in outs:
+        assert torch.equal(c1.view(torch.int16), ref1.view(torch.int16))
+        assert torch.equal(c2, ref2)
