@@ -252,7 +252,13 @@ __device__ __forceinline__ void store_c(const f32x4 (&acc)[8][NJ], const Args& a
             float* row = base + (int64_t)i * 16 * a.ldc;
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
-                const f32x4& x = acc[i][j];
+                // the block's values enter vector registers here and not
+                // earlier: left to itself the compiler copied all 256
+                // accumulators out at the top of the store (ahead of the
+                // per-block branches), ran out of registers, and its spill
+                // code then stored one lane value from the wrong register
+                f32x4 x = acc[i][j];
+                asm volatile("" : "+v"(x));
                 f32x4 v;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] = epi<EPI>(x[e], alpha, EPI ? bv[j][e] : 0.f, relu);
@@ -314,6 +320,20 @@ __device__ __forceinline__ void zero_acc(f32x4 (&acc)[8][8]) {
     for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{};
+}
+
+// Zero accumulators produced by a matrix instruction (0 * 0 + 0 = +0, the
+// same bits as zero_acc). Sums that start from plain zero moves make the
+// register allocator keep some of them in vector registers across the K loop
+// and copy them into the accumulator file at every step; starting from a
+// matrix result keeps all of them in the accumulator file.
+template <int AB>
+__device__ __forceinline__ void zero_acc_mma(f32x4 (&acc)[8][8]) {
+    const half8 z{};
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = mfma16<AB>(z, z, f32x4{});
 }
 
 // ---------------------------------------------------------------------------
@@ -849,6 +869,7 @@ struct DmaCtx {
     LaneLoads<KS> p;
     unsigned bstep;       // scalar-offset advance of B per K step
     int nk, klast;        // K steps per tile; first k of a tile's last step
+    int lead;             // leading empty steps (0 or 1): data step of step t is t - lead
     bool fixup;           // a tile's last step needs fix_last_step
     int tid, wave, lane;
     u32x4* smem;
@@ -866,13 +887,11 @@ struct DmaCtx {
 // workgroup's next tile tn (none when !has_next: those loads read nothing
 // and write zeros). Its first slice's fragments are in buffer F0 of fa/fb;
 // the next step's first fragments end up in buffer F0 ^ (KS / 32 odd).
-// ST >= 0: st == ST, known at compile time (2-stage ring), so every fragment
-// read is a fixed offset from the stage-0 positions. ST < 0: `cur` holds the
-// read positions of stage st on entry and those of the next stage on return;
-// they are derived once per step, before the barrier wait, into registers no
-// matrix instruction reads (a vector ALU write into a just-read MFMA operand
-// register stalls the matrix cores).
-template <int AB, int NXK, int KS, int S, int F0, int ST, bool FIRST = false, bool LAST = false>
+// `cur` holds the read positions of stage st on entry and those of the next
+// stage on return; they are derived once per step, before the barrier wait,
+// into registers no matrix instruction reads (a vector ALU write into a
+// just-read MFMA operand register stalls the matrix cores).
+template <int AB, int NXK, int KS, int S, int F0, bool FIRST = false, bool LAST = false>
 __device__ __forceinline__ void dma_step(f32x4 (&acc)[8][8], half8 (&fa)[2][8], half8 (&fb)[2][8], int st, int t,
                                          const Args& a, const DmaCtx<KS, NXK, S>& c, FragPtrs<KS, NXK>& cur,
                                          const Tile& tc, const Tile& tn, bool has_next) {
@@ -880,30 +899,27 @@ __device__ __forceinline__ void dma_step(f32x4 (&acc)[8][8], half8 (&fa)[2][8], 
     constexpr int kSlices = KS / 32;
     constexpr int kLps = KS / 4;
     constexpr int FL = (F0 + kSlices - 1) & 1;       // buffer of the last slice
-    static_assert(ST < 0 || S == 2, "compile-time stages need the 2-stage ring");
-    if (ST >= 0) st = ST;
     const int nst = (st + 1 == S) ? 0 : st + 1;
-    const FragPtrs<KS, NXK>& fc = ST >= 0 ? c.fp : cur;
-    const int so_c = ST >= 0 ? ST * L::kBlock : 0;
     static_assert(!FIRST || kSlices > 1, "the zero-start slice is the first of a 2-slice step");
 #pragma unroll
     for (int s = 0; s + 1 < kSlices; ++s) {
         if (FIRST && s == 0)
-            slice<AB, KS, NXK, false, true>(acc, fa[F0 & 1], fb[F0 & 1], fa[(F0 + 1) & 1], fb[(F0 + 1) & 1], fc, so_c,
+            slice<AB, KS, NXK, false, true>(acc, fa[F0 & 1], fb[F0 & 1], fa[(F0 + 1) & 1], fb[(F0 + 1) & 1], cur, 0,
                                         1, tc.ra, tc.rb, c.p, 0u, 0u, c.smem, c.smem, c.wave);
         else
             slice<AB, KS, NXK, false>(acc, fa[(F0 + s) & 1], fb[(F0 + s) & 1], fa[(F0 + s + 1) & 1],
-                                  fb[(F0 + s + 1) & 1], fc, so_c, s + 1, tc.ra, tc.rb, c.p, 0u, 0u, c.smem, c.smem,
+                                  fb[(F0 + s + 1) & 1], cur, 0, s + 1, tc.ra, tc.rb, c.p, 0u, 0u, c.smem, c.smem,
                                   c.wave);
     }
-    if (ST < 0) cur = shifted(c.fp, nst * L::kBlock);
+    cur = shifted(c.fp, nst * L::kBlock);
     // the step these loads are for (uniform: scalar selects)
     const int tl = t + S;
     const bool in_next = tl >= c.nk;
     const int ls = in_next ? tl - c.nk : tl;
     const bool live = !in_next || has_next;
-    const unsigned soa = live ? (unsigned)ls * (unsigned)(KS * 2) : kOob;
-    const unsigned sob = live ? (unsigned)ls * c.bstep : kOob;
+    const int ld = KS == 32 ? ls - c.lead : ls;      // >= 0: tl >= S > lead
+    const unsigned soa = live ? (unsigned)ld * (unsigned)(KS * 2) : kOob;
+    const unsigned sob = live ? (unsigned)ld * c.bstep : kOob;
     const Rsrc lra = in_next ? tn.ra : tc.ra;
     const Rsrc lrb = in_next ? tn.rb : tc.rb;
     TG_COMPILER_FENCE();
@@ -914,25 +930,25 @@ __device__ __forceinline__ void dma_step(f32x4 (&acc)[8][8], half8 (&fa)[2][8], 
         fix_last_step<KS, NXK>(c.a_blk(nst), c.b_blk(nst), c.p, a, tc.m0, tc.n0, c.klast, c.tid, c.wave, c.lane);
     block_barrier();
     // the loads go into the stage just released
-    slice<AB, KS, NXK, true, false, !LAST>(acc, fa[FL], fb[FL], fa[FL ^ 1], fb[FL ^ 1], ST >= 0 ? c.fp : cur,
-                                       ST >= 0 ? ((ST + 1) & 1) * L::kBlock : 0, 0, lra, lrb, c.p, soa, sob,
-                                       c.a_blk(st), c.b_blk(st), c.wave);
+    slice<AB, KS, NXK, true, false, !LAST>(acc, fa[FL], fb[FL], fa[FL ^ 1], fb[FL ^ 1], cur, 0, 0, lra, lrb, c.p,
+                                       soa, sob, c.a_blk(st), c.b_blk(st), c.wave);
 }
 
-// Steps t0 .. nk-1 (an even count) of tile tc in pairs, step t0 in stage st0
-// with parity P: one-slice steps alternate fragment buffers, and a 2-stage
-// ring alternates stages, so the pair's two steps are two fixed variants.
-template <int AB, int NXK, int KS, int S, int P>
-__device__ __forceinline__ void step_pairs(f32x4 (&acc)[8][8], half8 (&fa)[2][8], half8 (&fb)[2][8], int t0,
-                                           int st0, const Args& a, const DmaCtx<KS, NXK, S>& c,
-                                           FragPtrs<KS, NXK>& cur, const Tile& tc, const Tile& tn, bool has_next) {
-    constexpr int F1 = KS == 32 ? P : 0, F2 = KS == 32 ? (P ^ 1) : 0;
-    constexpr int S1 = S == 2 ? P : -1, S2 = S == 2 ? (P ^ 1) : -1;
-    int st = st0;
-    for (int t = t0; t < c.nk; t += 2) {
-        dma_step<AB, NXK, KS, S, F1, S1>(acc, fa, fb, st, t, a, c, cur, tc, tn, has_next);
+// The steps 0 .. nk-1 (an even count) of a one-slice ring, in pairs: such
+// steps alternate fragment buffers, so the pair's two steps are two fixed
+// variants. One loop with nothing before or after it in the tile: a second
+// path into store_c (an odd step taken apart from the pairs) made the register
+// allocator split the accumulators between the two register files and move
+// them every step.
+template <int AB, int NXK, int S>
+__device__ __forceinline__ void step_pairs(f32x4 (&acc)[8][8], half8 (&fa)[2][8], half8 (&fb)[2][8],
+                                           const Args& a, const DmaCtx<32, NXK, S>& c, FragPtrs<32, NXK>& cur,
+                                           const Tile& tc) {
+    int st = 0;
+    for (int t = 0; t < c.nk; t += 2) {
+        dma_step<AB, NXK, 32, S, 0>(acc, fa, fb, st, t, a, c, cur, tc, tc, false);
         st = (st + 1 == S) ? 0 : st + 1;
-        dma_step<AB, NXK, KS, S, F2, S2>(acc, fa, fb, st, t + 1, a, c, cur, tc, tn, has_next);
+        dma_step<AB, NXK, 32, S, 1>(acc, fa, fb, st, t + 1, a, c, cur, tc, tc, false);
         st = (st + 1 == S) ? 0 : st + 1;
     }
 }
@@ -968,20 +984,25 @@ tgemm_dma_kernel(Args a) {
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
-    const int nk = (a.K + KS - 1) / KS;
+    const int nkd = (a.K + KS - 1) / KS;              // K steps holding data
+    // 32-deep steps go in pairs: an odd count gets one leading step whose
+    // loads all fall out of range (zeros), so that every tile runs one loop
+    const int lead = KS == 32 ? (nkd & 1) : 0;
+    const int nk = nkd + lead;
 
     int wid = (int)blockIdx.x;
     Tile tc = make_tile<NXK>(a, wid);
     bool has_next = wid + a.grid < a.W;              // K == 0: one tile per workgroup
     Tile tn = has_next ? make_tile<NXK>(a, wid + a.grid) : tc;
     f32x4 acc[8][8];
-    if (KS == 32) zero_acc(acc);
+    if (KS == 32) zero_acc_mma<AB>(acc);
 
     DmaCtx<KS, NXK, S> c;
     c.p = lane_loads<KS, NXK>(a, tid);
     c.bstep = NXK ? (unsigned)(KS * 2) : (unsigned)KS * (unsigned)a.ldb * 2u;
     c.nk = nk;
-    c.klast = (nk - 1) * KS;
+    c.lead = lead;
+    c.klast = (nkd - 1) * KS;
     c.fixup = (a.K % KS) != 0 || (!NXK && (a.N % 8) != 0);
     c.tid = tid;
     c.wave = wave;
@@ -992,10 +1013,13 @@ tgemm_dma_kernel(Args a) {
     if (nk > 0) {
         // prologue: steps 0 .. S-1 of the first tile (a workgroup with more
         // than one tile has nk >= S)
-        for (int t = 0; t < S; ++t)
+        for (int t = 0; t < S; ++t) {
+            const int d = t - lead;                   // data step
+            const bool live = d >= 0 && t < nk;
             for (int idx = 0; idx < kLps; ++idx)
-                issue_load<KS, NXK>(tc.ra, tc.rb, c.p, idx, t < nk ? (unsigned)t * (unsigned)(KS * 2) : kOob,
-                                    t < nk ? (unsigned)t * c.bstep : kOob, c.a_blk(t), c.b_blk(t), wave);
+                issue_load<KS, NXK>(tc.ra, tc.rb, c.p, idx, live ? (unsigned)d * (unsigned)(KS * 2) : kOob,
+                                    live ? (unsigned)d * c.bstep : kOob, c.a_blk(t), c.b_blk(t), wave);
+        }
         wait_vmcnt<(S - 1) * kLps>();                 // step 0 landed
         if (c.fixup && nk == 1)
             fix_last_step<KS, NXK>(c.a_blk(0), c.b_blk(0), c.p, a, tc.m0, tc.n0, c.klast, tid, wave, lane);
@@ -1012,13 +1036,13 @@ tgemm_dma_kernel(Args a) {
         // (64-deep steps are used with nk >= 2)
         int st = 0;
         for (;;) {
-            dma_step<AB, NXK, KS, S, 0, -1, true>(acc, fa, fb, st, 0, a, c, cur, tc, tn, has_next);
+            dma_step<AB, NXK, KS, S, 0, true>(acc, fa, fb, st, 0, a, c, cur, tc, tn, has_next);
             st ^= 1;
             for (int t = 1; t + 1 < nk; ++t) {
-                dma_step<AB, NXK, KS, S, 0, -1>(acc, fa, fb, st, t, a, c, cur, tc, tn, has_next);
+                dma_step<AB, NXK, KS, S, 0>(acc, fa, fb, st, t, a, c, cur, tc, tn, has_next);
                 st ^= 1;
             }
-            dma_step<AB, NXK, KS, S, 0, -1, false, true>(acc, fa, fb, st, nk - 1, a, c, cur, tc, tn, has_next);
+            dma_step<AB, NXK, KS, S, 0, false, true>(acc, fa, fb, st, nk - 1, a, c, cur, tc, tn, has_next);
             st ^= 1;
             store_c<TY>(acc, a, tc.m0, tc.n0, wm, wn, lane);
             if (!has_next) break;
@@ -1029,14 +1053,8 @@ tgemm_dma_kernel(Args a) {
             if (has_next) tn = make_tile<NXK>(a, wid + a.grid);
         }
     } else {
-        // one tile per workgroup; an odd step count starts with one step,
-        // the rest go in pairs
-        if (nk & 1) {
-            dma_step<AB, NXK, KS, S, 0, S == 2 ? 0 : -1>(acc, fa, fb, 0, 0, a, c, cur, tc, tn, has_next);
-            step_pairs<AB, NXK, KS, S, 1>(acc, fa, fb, 1, 1 % S, a, c, cur, tc, tn, has_next);
-        } else {
-            step_pairs<AB, NXK, KS, S, 0>(acc, fa, fb, 0, 0, a, c, cur, tc, tn, has_next);
-        }
+        // one tile per workgroup, its steps (an even count) in pairs
+        step_pairs<AB, NXK, S>(acc, fa, fb, a, c, cur, tc);
         store_c<TY>(acc, a, tc.m0, tc.n0, wm, wn, lane);
     }
     // no load may still be writing this workgroup's LDS when it exits
