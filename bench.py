@@ -155,6 +155,23 @@ def main():
     import dense_tiled_gemm_tgemm_amd as tg
     from dense_tiled_gemm_tgemm_amd import inputs
 
+    def warm_up(fn):
+        """args.warmup launches, then more until args.warmup_seconds have passed
+        (the board's power-limited clock settles over the first fraction of a
+        second of sustained matrix work)."""
+        t_w = time.perf_counter()
+        n = 0
+        for _ in range(args.warmup):
+            fn()
+            n += 1
+        torch.cuda.synchronize()
+        while time.perf_counter() - t_w < args.warmup_seconds:
+            for _ in range(16):
+                fn()
+                n += 1
+            torch.cuda.synchronize()
+        return n, time.perf_counter() - t_w
+
     if args.mfma_ceiling:
         # the GEMM's instruction stream without synchronization, tile changes or
         # C stores, on the workload's own A values (the operands' switching
@@ -171,8 +188,8 @@ def main():
         flops = wg * 4 * iters * 128 * 2.0 * 16 * 16 * 32
 
         def probe_ms(buf):
-            for _ in range(args.warmup):
-                tg.mfma_issue_probe(wg, iters, buf.data_ptr(), nbytes, out.data_ptr(), stream.cuda_stream)
+            warm_up(lambda: tg.mfma_issue_probe(wg, iters, buf.data_ptr(), nbytes, out.data_ptr(),
+                                                stream.cuda_stream))
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
             ev[0].record(stream)
             for _ in range(args.steps):
@@ -223,8 +240,7 @@ def main():
         def vendor():
             torch.matmul(Ad, Bt, out=Cd)
 
-        for _ in range(args.warmup):
-            vendor()
+        warm_up(vendor)
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         torch.cuda.synchronize()
         ev[0].record(stream)
@@ -261,18 +277,8 @@ def main():
             raise tg.TgemmError(rc, "tune")
         log(f"bench: tuned choice {tuned}")
 
-    t_w = time.perf_counter()
-    n_warm = 0
-    for _ in range(args.warmup):
-        step()
-        n_warm += 1
-    torch.cuda.synchronize()
-    while time.perf_counter() - t_w < args.warmup_seconds:
-        for _ in range(16):
-            step()
-            n_warm += 1
-        torch.cuda.synchronize()
-    log(f"bench: {n_warm} warm-up launches in {time.perf_counter() - t_w:.3f} s")
+    n_warm, t_warm = warm_up(step)
+    log(f"bench: {n_warm} warm-up launches in {t_warm:.3f} s")
 
     # events recorded on the launch stream between consecutive launches
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]

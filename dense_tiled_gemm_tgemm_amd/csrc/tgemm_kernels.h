@@ -966,8 +966,9 @@ __device__ __forceinline__ void step_pairs(f32x4 (&acc)[8][8], half8 (&fa)[2][8]
 // reads). A step's loads thus have S - 1 steps less one slice to land, and
 // the next tile's first steps load while the current tile finishes, so a
 // tile's C stores drain while the next tile computes. Every step issues the
-// same number of loads (steps past the last tile read nothing and write
-// zeros into stages that are never read), so all wait counts are constants.
+// same number of loads (steps past the last tile, and the leading step of an
+// odd 32-deep step count, read nothing and write zeros), so all wait counts
+// are constants.
 template <int TY, int NXK, int KS, int S>
 __global__ void __launch_bounds__(NTHREADS)
 __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -1012,7 +1013,7 @@ tgemm_dma_kernel(Args a) {
     half8 fa[2][8], fb[2][8];
     if (nk > 0) {
         // prologue: steps 0 .. S-1 of the first tile (a workgroup with more
-        // than one tile has nk >= S)
+        // than one tile has nk >= S); step t holds data step t - lead
         for (int t = 0; t < S; ++t) {
             const int d = t - lead;                   // data step
             const bool live = d >= 0 && t < nk;

@@ -249,8 +249,8 @@ PIPES = [(64, 2), (32, 2), (32, 3), (32, 4), (32, 5)]
 def test_pipeline_choices_are_bit_identical(oracle_mod, M, N, K, lay):
     """Every direct-to-LDS pipeline (K step x ring depth) and the register-staged
     path produce the same bits: each output's 32-deep K slices are summed in the
-    same order. Odd step counts (K = 8, 264, 4128 at K step 32) cover the zero
-    step that completes the last pair of one-slice steps."""
+    same order. Odd step counts (K = 8, 264, 4128 at K step 32) cover the leading
+    all-zero step that makes a 32-deep ring's step count even."""
     print(f"case pipelines {M}x{N}x{K} {lay}", flush=True)
     A = inputs.random_f16((M, K), M + K)
     B = inputs.random_f16((N, K) if lay == "NxK" else (K, N), N + K)
