@@ -1,0 +1,100 @@
+"""Generated-code checks of the direct-to-LDS kernels (CPU only: hipcc emits
+gfx950 assembly without a GPU).
+
+The K loop of each kernel must keep its accumulators in the accumulator
+register file and touch no scratch memory: accumulator moves or spill
+reloads there cost up to half the kernel's rate (a reload is followed by a
+wait for every outstanding load, which drains the load pipeline). The whole
+kernel must also be free of the spill sequence that reuses an accumulator
+register as a spill slot ("Reload Reuse"): in one instantiation that sequence
+stored a lane value from the wrong register.
+
+The instantiations checked are those whose register allocation has gone wrong
+before: fp32 output, the epilogue, bfloat16 inputs, each with both B layouts
+and every ring depth that is built for them.
+"""
+import os
+import re
+import shutil
+import subprocess
+from concurrent.futures import ThreadPoolExecutor
+
+import pytest
+
+from dense_tiled_gemm_tgemm_amd import build as hip_build
+
+HIPCC = hip_build.HIPCC
+pytestmark = pytest.mark.skipif(not shutil.which(HIPCC) and not os.path.exists(HIPCC), reason="no hipcc")
+
+CASES = [(0, 0, 0), (0, 2, 0), (0, 0, 1), (1, 2, 1)]   # (input type, output type, epilogue)
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    out = tmp_path_factory.mktemp("asm")
+    flags = [f for f in hip_build.FLAGS if f not in ("-fPIC", "-Wall", "-Wno-unused-function")]
+
+    def one(case):
+        ab, ct, epi = case
+        path = os.path.join(out, f"inst_{ab}{ct}{epi}.s")
+        cmd = [HIPCC, *flags, f"-DTG_AB={ab}", f"-DTG_CT={ct}", f"-DTG_EPI={epi}", "--cuda-device-only", "-S",
+               os.path.join(hip_build.CSRC, "tgemm_inst.hip"), "-o", path]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        assert res.returncode == 0, res.stderr[-2000:]
+        with open(path) as f:
+            return case, f.read()
+
+    with ThreadPoolExecutor(len(CASES)) as ex:
+        return dict(ex.map(one, CASES))
+
+
+def _kernels(text):
+    """(name, body lines) of every direct-to-LDS kernel in an assembly file."""
+    for m in re.finditer(r"^(_ZN2tg16tgemm_dma_kernel\w+):", text, re.M):
+        end = text.index(".Lfunc_end", m.end())
+        yield m.group(1), text[m.end():end].splitlines()
+
+
+def _innermost_mfma_loop(body):
+    """Instructions of the blocks at the deepest loop level that holds MFMAs."""
+    blocks, cur = [], ("", [])
+    for line in body:
+        t = line.strip()
+        lab = re.match(r"^\.LBB\w+:(.*)", t)
+        if lab:
+            blocks.append(cur)
+            cur = (lab.group(1), [])
+        elif t and not t.startswith((";", ".")):
+            cur[1].append(t)
+    blocks.append(cur)
+
+    def depth(comment):
+        d = re.search(r"Depth=(\d+)", comment)
+        return int(d.group(1)) if d else 0
+
+    mfma_depths = [depth(c) for c, ins in blocks if sum(i.startswith("v_mfma") for i in ins) >= 64]
+    deepest = max(mfma_depths, default=0)
+    assert deepest > 0, "no K loop found"
+    return [i for c, ins in blocks if depth(c) == deepest for i in ins]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "ab%d_ct%d_epi%d" % c)
+def test_k_loop_keeps_accumulators_in_place(asm, case):
+    names = []
+    for name, body in _kernels(asm[case]):
+        names.append(name)
+        loop = _innermost_mfma_loop(body)
+        moves = [i for i in loop if i.startswith(("v_accvgpr_write", "v_accvgpr_read", "v_accvgpr_mov"))]
+        scratch = [i for i in loop if "scratch_" in i]
+        assert not scratch, (name, scratch[:4])
+        # a few writes for fragment bookkeeping are tolerated; a split
+        # accumulator shows up as one move per accumulator register
+        assert len(moves) <= 24, (name, len(moves), moves[:6])
+    assert len(names) >= 4, names
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "ab%d_ct%d_epi%d" % c)
+def test_no_accumulator_spill_slot_reuse(asm, case):
+    for name, body in _kernels(asm[case]):
+        bad = [l.strip() for l in body if "Reload Reuse" in l]
+        assert not bad, (name, bad[:4])
