@@ -219,6 +219,14 @@ def _check_tensor(t, name):
         raise ValueError(f"{name} must be a device tensor")
 
 
+def _same_device(A, *others):
+    """Every tensor on A's device (the library launches on the current device,
+    which the callers set to A's)."""
+    for t, name in others:
+        if t is not None and t.device != A.device:
+            raise ValueError(f"{name} is on {t.device}, A on {A.device}")
+
+
 def mm(A, B, b_layout: str = "KxN", out=None, stream=None, force_generic: int = 0,
        group_m: int = 0, num_xcd: int = 0, k_step: int = 0, stages: int = 0):
     """C = A @ B for fp16 device tensors (fp32 accumulation in the kernel).
@@ -244,13 +252,15 @@ def mm(A, B, b_layout: str = "KxN", out=None, stream=None, force_generic: int = 
         _check_tensor(out, "out")
         if tuple(out.shape) != (M, N):
             raise ValueError(f"out must be ({M}, {N})")
+    _same_device(A, (B, "B"), (out, "out"))
     lda, ldb, ldc = _row_major(A, "A"), _row_major(B, "B"), _row_major(out, "out")
     if stream is None:
         stream = torch.cuda.current_stream(A.device).cuda_stream
     elif hasattr(stream, "cuda_stream"):
         stream = stream.cuda_stream
-    rc = tgemm_f16_config(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, lay, out.data_ptr(), ldc,
-                          stream, force_generic, group_m, num_xcd, k_step, stages)
+    with torch.cuda.device(A.device):
+        rc = tgemm_f16_config(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, lay, out.data_ptr(), ldc,
+                              stream, force_generic, group_m, num_xcd, k_step, stages)
     if rc != TGEMM_OK:
         raise TgemmError(rc, f"M={M} N={N} K={K} layout={b_layout}")
     return out
@@ -307,21 +317,24 @@ def gemm(A, B, b_layout: str = "KxN", out=None, out_dtype=None, alpha: float = 1
         if bias.dtype != torch.float32 or not bias.is_cuda or tuple(bias.shape) != (N,) or (N > 1 and bias.stride(0) != 1):
             raise ValueError(f"bias must be a contiguous ({N},) float32 device tensor")
         bias_ptr = bias.data_ptr()
+    _same_device(A, (B, "B"), (out, "out"), (bias, "bias"))
     lda, ldb, ldc = _row_major(A, "A"), _row_major(B, "B"), _row_major(out, "out")
     if stream is None:
         stream = torch.cuda.current_stream(A.device).cuda_stream
     elif hasattr(stream, "cuda_stream"):
         stream = stream.cuda_stream
     if _tune_rounds:
-        rc, chosen = tgemm_tune_gemm(M, N, K, _torch_code(A.dtype), A.data_ptr(), lda, B.data_ptr(), ldb, lay,
-                                     _torch_code(out.dtype), out.data_ptr(), ldc, alpha, bias_ptr, act, stream,
-                                     _tune_rounds)
+        with torch.cuda.device(A.device):
+            rc, chosen = tgemm_tune_gemm(M, N, K, _torch_code(A.dtype), A.data_ptr(), lda, B.data_ptr(), ldb, lay,
+                                         _torch_code(out.dtype), out.data_ptr(), ldc, alpha, bias_ptr, act, stream,
+                                         _tune_rounds)
         if rc != TGEMM_OK:
             raise TgemmError(rc, f"tune M={M} N={N} K={K} layout={b_layout} {A.dtype}->{out.dtype}")
         return out, chosen
-    rc = tgemm_gemm_config(M, N, K, _torch_code(A.dtype), A.data_ptr(), lda, B.data_ptr(), ldb, lay,
-                           _torch_code(out.dtype), out.data_ptr(), ldc, alpha, bias_ptr, act, stream,
-                           force_generic, group_m, num_xcd, k_step, stages)
+    with torch.cuda.device(A.device):
+        rc = tgemm_gemm_config(M, N, K, _torch_code(A.dtype), A.data_ptr(), lda, B.data_ptr(), ldb, lay,
+                               _torch_code(out.dtype), out.data_ptr(), ldc, alpha, bias_ptr, act, stream,
+                               force_generic, group_m, num_xcd, k_step, stages)
     if rc != TGEMM_OK:
         raise TgemmError(rc, f"M={M} N={N} K={K} layout={b_layout} {A.dtype}->{out.dtype}")
     return out
