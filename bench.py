@@ -8,6 +8,9 @@ Prints ONE JSON line (rank 0):
   roofline   the GEMM kernel against the dense fp16 matrix-core peak:
              achieved = 2*M*N*K / mean per-launch time (HIP events recorded
              on the launch stream between consecutive launches)
+  launch_ms  mean, median, min and p90 of the per-launch times
+  cold_cache variant B: up to 50 launches, each after a 512 MiB write that
+             evicts the L2s and the Infinity Cache (events around the GEMM only)
   cpu_baseline  the CPU oracle (fp64, all OpenMP threads) timed on a bounded
              block of whole output rows of the same workload
 
@@ -35,6 +38,7 @@ PEAK_F32_TFLOPS = 157.3       # dense fp32 matrix rate (256 flop/clk/CU)
 KERNEL_SOURCES = ("dense_tiled_gemm_tgemm_amd/csrc/tgemm_kernels.h", "dense_tiled_gemm_tgemm_amd/csrc/tgemm_inst.hip",
                   "dense_tiled_gemm_tgemm_amd/csrc/tgemm.hip", "dense_tiled_gemm_tgemm_amd/csrc/tgemm_plan.h")
 EPI_ALPHA = 0.5
+COLD_FLUSH_BYTES = 512 << 20   # written between cold-cache launches (> 8 x 4 MiB L2 + 256 MiB Infinity Cache)
 
 
 def log(*a):
@@ -101,7 +105,20 @@ def cpu_baseline(A, B, w, got, target_s: float = 12.0, ab="f16", out="f16", alph
                   f"{dt:.1f} s for {flops / 1e9:.0f} GFLOP",
         "parity_rows_checked": rows,
         "parity_fail": res["nfail"],
+        "host_cpus": len(os.sched_getaffinity(0)),
+        "cpu_model": cpu_model(),
     }
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():
@@ -122,6 +139,8 @@ def main():
     ap.add_argument("--tune", action="store_true",
                     help="run the runtime tuner on the workload first; the timed launches use its choice")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache launches (512 MiB written before each) reported beside the headline")
     ap.add_argument("--mfma-ceiling", action="store_true",
                     help="instead of the GEMM, time the matrix-core ceiling probe (the GEMM's "
                          "instruction stream on the workload's values, without synchronization, "
@@ -301,6 +320,34 @@ def main():
     log(f"bench: {args.steps} steps, region {region_ms:.3f} ms (host wall {wall * 1e3:.3f} ms), "
         f"per launch mean {mean_ms:.4f} min {min(per_launch_ms):.4f} max {max(per_launch_ms):.4f} ms")
 
+    def stats(ms):
+        q = np.percentile(ms, [50, 90])
+        return {"mean": round(float(np.mean(ms)), 5), "median": round(float(q[0]), 5),
+                "min": round(float(np.min(ms)), 5), "p90": round(float(q[1]), 5)}
+
+    cold = None
+    if not args.no_cold:
+        # variant B: a 512 MiB write between launches evicts every L2 and the
+        # 256 MiB Infinity Cache, so each launch reads its operands from HBM;
+        # events bracket the GEMM launches only
+        flush = torch.empty(COLD_FLUSH_BYTES, dtype=torch.uint8, device=dev)
+        n_cold = min(args.steps, 50)
+        ev_c = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_cold)]
+        torch.cuda.synchronize()
+        for i in range(n_cold):
+            flush.fill_(i & 255)
+            ev_c[2 * i].record(stream)
+            step()
+            ev_c[2 * i + 1].record(stream)
+        torch.cuda.synchronize()
+        cold_ms = [ev_c[2 * i].elapsed_time(ev_c[2 * i + 1]) for i in range(n_cold)]
+        del flush
+        cs = stats(cold_ms)
+        cold = {"flush_bytes": COLD_FLUSH_BYTES, "launches": n_cold, "launch_ms": cs,
+                "tflops_at_median": round(flops / (cs["median"] / 1e3) / 1e12, 2)}
+        log(f"bench: cold-cache launches (512 MiB written before each): median {cs['median']:.4f} ms, "
+            f"{cold['tflops_at_median']:.1f} TFLOP/s")
+
     metric = METRIC if (tag == "" and name == inputs.HEADLINE) else (
         f"GEMM TFLOPS (2MNK/s) at {w.M}x{w.N}x{w.K}, {args.ab} in, {args.out} out"
         f"{', alpha/bias/relu epilogue' if args.epilogue else ''} on 1 MI355X")
@@ -313,6 +360,7 @@ def main():
         "warmup": args.warmup,
         "warmup_launches": n_warm,
         "ms_per_step": round(region_ms / args.steps, 5),
+        "launch_ms": stats(per_launch_ms),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -332,6 +380,8 @@ def main():
             "traffic": traffic_from_profiles(name, tag),
         },
     }
+    if cold is not None:
+        rec["cold_cache"] = cold
     if not args.no_cpu_baseline:
         torch.cuda.synchronize()
         got = Cd.cpu().numpy() if args.out == "f32" else Cd.view(torch.int16).cpu().numpy().view(np.uint16)
