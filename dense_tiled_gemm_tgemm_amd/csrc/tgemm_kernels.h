@@ -735,32 +735,64 @@ __device__ __forceinline__ void issue_load(const Rsrc& ra, const Rsrc& rb, const
 #endif
 }
 
+// Elements at or past nv of an 8-element chunk set to zero (nv in 1..7).
+__device__ __forceinline__ u32x4 keep_first(const u32x4& v, int nv) {
+    u32x4 r;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const unsigned lo = (2 * q < nv) ? 0x0000ffffu : 0u;
+        const unsigned hi = (2 * q + 1 < nv) ? 0xffff0000u : 0u;
+        r[q] = v[q] & (lo | hi);
+    }
+    return r;
+}
+
 // Last K step when it is partial (k0 = its first k). Its K-contiguous chunks
-// at or past K were loaded as whatever lies there (the next row, or zeros past
-// the operand's end), so each lane rewrites those of its own slots: the
-// valid part of a chunk straddling K from element loads, zeros after it, and
-// whole zeros past K. B stored K x N straddles only at column N, and only
-// its final row K - 1 loses data (the range check zeroes the whole 16-byte
-// access; other rows read the next row past N, which lands in output
-// columns that are never stored). This runs after the lane's loads of the
-// stage have landed and before the barrier that publishes it.
+// at or past K were loaded as whatever lies there. Every row stride is at
+// least 8 elements on this path, so in every row but the operand's last the
+// 16-byte access stayed inside the operand's range and read the next bytes of
+// memory (the rest of the row, or the next row): a chunk straddling K holds
+// its valid elements and only the rest is cleared, by a read-modify-write of
+// the lane's own LDS slot; chunks wholly past K are cleared. In the operand's
+// last row the range check zeroed the whole straddling access, so that chunk
+// is loaded element by element (in a branch only the waves holding that row
+// take, so other waves never wait on memory here). B stored K x N straddles
+// only at column N, and only its final row K - 1 loses data the same way
+// (other rows read the next row past N, which lands in output columns that
+// are never stored). This runs after the lane's loads of the stage have
+// landed and before the barrier that publishes it.
 template <int KS, int NXK>
 __device__ __forceinline__ void fix_last_step(u32x4* __restrict__ a_blk, u32x4* __restrict__ b_blk,
                                               const LaneLoads<KS>& p, const Args& a, int m0, int n0, int k0,
                                               int tid, int wave, int lane) {
     constexpr int kCpr = KS / 8;
+    constexpr int kRowStep = 256 / kCpr;              // rows between a lane's chunks
     const int r = tid / kCpr;
     const int kc = k0 + (int)p.kchunk;
     const int nv = a.K - kc;                          // valid elements of this lane's K chunks (may be <= 0)
-    // one chunk at a time (not unrolled): this runs once per tile, inside a
-    // loop whose fragments hold most of the registers
     if (nv < 8) {
+        // one chunk at a time (not unrolled): this runs once per tile, inside a
+        // loop whose fragments hold most of the registers
 #pragma unroll 1
         for (int j = 0; j < kCpr; ++j) {
-            const int row = r + (256 / kCpr) * j;
+            const int row = r + kRowStep * j;
             const int slot = (j * 4 + wave) * 64 + lane;
-            if (m0 + row < a.M) a_blk[slot] = load8_elems(a.A + (int64_t)(m0 + row) * a.lda + kc, nv);
-            if (NXK && n0 + row < a.N) b_blk[slot] = load8_elems(a.B + (int64_t)(n0 + row) * a.ldb + kc, nv);
+            if (m0 + row < a.M) {
+                if (nv <= 0)
+                    a_blk[slot] = u32x4{};
+                else if (m0 + row == a.M - 1)
+                    a_blk[slot] = load8_elems(a.A + (int64_t)(a.M - 1) * a.lda + kc, nv);
+                else
+                    a_blk[slot] = keep_first(a_blk[slot], nv);
+            }
+            if (NXK && n0 + row < a.N) {
+                if (nv <= 0)
+                    b_blk[slot] = u32x4{};
+                else if (n0 + row == a.N - 1)
+                    b_blk[slot] = load8_elems(a.B + (int64_t)(a.N - 1) * a.ldb + kc, nv);
+                else
+                    b_blk[slot] = keep_first(b_blk[slot], nv);
+            }
         }
     }
     if (!NXK) {
@@ -775,8 +807,7 @@ __device__ __forceinline__ void fix_last_step(u32x4* __restrict__ a_blk, u32x4* 
         }
     }
     TG_COMPILER_FENCE();
-    wait_lgkmcnt0();
-    __builtin_amdgcn_s_waitcnt(0);                    // element loads returned and written
+    wait_lgkmcnt0();                                  // this lane's LDS writes done before the barrier
     TG_COMPILER_FENCE();
 }
 

@@ -170,6 +170,9 @@ inline int make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
     // offsets; a K x N B additionally needs every byte offset it forms,
     // below (K + 64) * ldb * 2 + 512, to stay below 2^31.
     // (K == 0 only writes zeros: the register-staged kernel does that)
+    // (row strides of at least 8 elements: then a 16-byte access can run past
+    // the end of an operand only in its last row, which the kernel reloads
+    // element by element; narrower operands take the register-staged kernel)
     // (binary32 operands have kernels of their own: the kDma bit then marks the
     // pipelined one, whose buffer loads need K (and, for B stored K x N, N) a
     // multiple of 4 and every byte offset of a tile below 2^31)
@@ -179,7 +182,7 @@ inline int make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
                (b_layout == TGEMM_B_NxK ? ldb <= kMaxDmaLd / 2
                                         : N % 4 == 0 && ldb < (int64_t(1) << 29) &&
                                               (K + 64) * ldb < (int64_t(1) << 29) - 256))
-            : (!force_generic && K > 0 && lda <= kMaxDmaLd &&
+            : (!force_generic && K > 0 && lda >= 8 && ldb >= 8 && lda <= kMaxDmaLd &&
                (b_layout == TGEMM_B_NxK ? ldb <= kMaxDmaLd
                                         : ldb < (int64_t(1) << 30) && (K + 64) * ldb < (int64_t(1) << 30) - 512));
     pl->variant = (vec_ab ? kVecAB : 0) | (vec_c ? kVecC : 0) |

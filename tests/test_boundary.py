@@ -69,7 +69,7 @@ def _plan(M, N, K, A=PA, lda=None, B=PB, ldb=None, lay="KxN", C=PC, ldc=None, **
     dict(M=4, N=4, K=4, stages=1),
     dict(M=4, N=4, K=4, stages=6),
     dict(M=4, N=4, K=4, k_step=64, stages=3),
-    dict(M=4, N=4, K=64, k_step=64),             # 64-deep steps need K > 64
+    dict(M=4, N=16, K=64, k_step=64),            # 64-deep steps need K > 64
 ])
 def test_invalid_arguments_rejected(args):
     rc, info = _plan(**args)
@@ -349,3 +349,23 @@ def test_fp32_operand_plans():
     # strides past the 32-bit offset limits: the general kernel
     rc, info = _plan_ex(300, 200, 100, ab="f32", ct="f32", lay="NxK", lda=2_000_004)
     assert rc == 0 and not info["variant"] & PIPE
+
+
+@pytest.mark.parametrize("lay,M,N,K,lda,ldb,dma", [
+    ("KxN", 64, 3, 100, 100, 3, False),      # B rows of 3 elements
+    ("KxN", 64, 7, 100, 100, 7, False),
+    ("KxN", 64, 8, 100, 100, 8, True),
+    ("KxN", 64, 3, 100, 100, 8, True),       # padded rows: a stride of 8 is enough
+    ("NxK", 64, 300, 5, 5, 5, False),        # A and B rows of 5 elements
+    ("NxK", 64, 300, 5, 8, 8, True),
+    ("KxN", 64, 300, 7, 7, 300, False),
+])
+def test_narrow_operands_take_register_staged_path(lay, M, N, K, lda, ldb, dma):
+    """The direct-to-LDS path needs row strides of at least 8 elements: then a
+    16-byte access runs past the end of an operand only in its last row, which
+    the kernel reloads element by element. Narrower operands (K or N below 8
+    with tight strides) go to the register-staged kernel, which masks every
+    element load."""
+    rc, info = _plan(M, N, K, lda=lda, ldb=ldb, lay=lay)
+    assert rc == 0
+    assert bool(info["variant"] & 8) == dma, info

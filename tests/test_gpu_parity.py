@@ -331,6 +331,32 @@ def test_nan_beyond_k_and_edges_never_leaks(oracle_mod, lay, K, generic):
     _full_check(oracle_mod, A, B, lay, got, f"nan padding {lay} K={K}")
 
 
+@pytest.mark.parametrize("lay,M,N,K,ldb", [
+    ("KxN", 64, 3, 100, 3), ("KxN", 100, 7, 300, 7), ("KxN", 129, 1, 77, 1), ("KxN", 64, 3, 100, 8),
+    ("NxK", 70, 5, 130, 130), ("NxK", 64, 300, 5, 5), ("KxN", 64, 300, 5, 300), ("NxK", 64, 300, 5, 8),
+])
+def test_narrow_operands(oracle_mod, lay, M, N, K, ldb):
+    """Operands with rows narrower than 8 elements (K or N below 8, tight
+    strides) and the same shapes with strides of 8: full parity with the
+    oracle. In a K x N B of 3-element rows a 16-byte access at row k runs past
+    the end of B for the last rows, not only the last one."""
+    print(f"case narrow {lay} {M}x{N}x{K} ldb={ldb}", flush=True)
+    lda = K if K >= 8 or ldb < 8 else 8
+    A = inputs.random_f16((M, K), M + N + K)
+    B = inputs.random_f16((K, N) if lay == "KxN" else (N, K), 3 * (M + N + K))
+    rows, cols = B.shape
+    Abuf = np.zeros((M, lda), dtype=np.float16)
+    Abuf[:, :K] = A
+    Bbuf = np.zeros((rows, ldb), dtype=np.float16)
+    Bbuf[:, :cols] = B
+    Ad, Bd = _dev(Abuf), _dev(Bbuf)
+    C = torch.empty((M, N), dtype=torch.float16, device=DEV)
+    rc = tg.tgemm_f16_config(M, N, K, Ad.data_ptr(), lda, Bd.data_ptr(), ldb, lay, C.data_ptr(), N,
+                             torch.cuda.current_stream().cuda_stream, 0)
+    assert rc == tg.TGEMM_OK
+    _full_check(oracle_mod, A, B, lay, _host(C), f"narrow {lay} {M}x{N}x{K} ldb={ldb}")
+
+
 @pytest.mark.parametrize("lay", ["NxK", "KxN"])
 def test_inf_in_neighbouring_row_stays_local(lay):
     """Compact operands (ld = row length): an Inf in one row of B must not turn the
