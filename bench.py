@@ -289,6 +289,7 @@ def main():
 
     tuned = None
     if args.tune:
+        warm_up(step)                                 # tune on a settled clock
         rc, tuned = tg.tgemm_tune_gemm(w.M, w.N, w.K, args.ab, Ad.data_ptr(), lda, Bd.data_ptr(), ldb, w.b_layout,
                                        args.out, Cd.data_ptr(), ldc, alpha,
                                        bias_d.data_ptr() if bias_d is not None else None, act, sptr, 5)

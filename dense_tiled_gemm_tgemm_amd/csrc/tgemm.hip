@@ -98,6 +98,10 @@ struct TuneChoice {
     int k_step, stages, group_m, num_xcd;
 };
 
+constexpr float kTuneWarmupMs = 100.f;        // GPU time of the clock-settling launches
+constexpr int kTuneWarmupMaxLaunches = 4096;
+constexpr float kTuneMinGain = 0.99f;         // a choice must be at least 1% faster than the untuned launch
+
 static std::mutex g_tune_mu;
 static std::unordered_map<TuneKey, TuneChoice, TuneKeyHash> g_tuned;
 static std::atomic<int> g_tuned_count{0};
@@ -267,26 +271,52 @@ extern "C" int tgemm_tune_gemm(int64_t M, int64_t N, int64_t K, int ab_type, con
     if (cands.empty()) return TGEMM_ERR_UNSUPPORTED;
     const int nc = (int)cands.size();
     hipStream_t st = static_cast<hipStream_t>(stream);
+    // the launch the problem gets without tuning
+    int def = 0;
+    for (int i = 0; i < nc; ++i)
+        if (cands[i].pl.k_step == base.k_step && cands[i].pl.stages == base.stages &&
+            cands[i].pl.group_m == base.group_m)
+            def = i;
     // one event between consecutive launches; every round runs every candidate
-    // once (interleaved, so clock drift under load spreads over all of them)
+    // once, round r starting at candidate r (so no candidate always runs first
+    // or last in a round while the clock drifts)
     std::vector<hipEvent_t> ev((size_t)nc * rounds + 1, nullptr);
     hipError_t e = hipSuccess;
     for (auto& x : ev)
         if (e == hipSuccess) e = hipEventCreate(&x);
-    for (int i = 0; i < nc && e == hipSuccess && rc == TGEMM_OK; ++i)       // warm-up launch of each
+    for (int i = 0; i < nc && e == hipSuccess && rc == TGEMM_OK; ++i)       // one launch of each
         rc = tg::launch(cands[i].pl, cands[i].fn, A, B, C, c_type, alpha, bias, act, stream);
+    // settle the clock first: the board's power-limited clock takes a fraction
+    // of a second of sustained matrix work to reach its steady state, and
+    // candidates timed before that differ by more than the choices do
+    {
+        float warm_ms = 0.f;
+        int n = 0;
+        while (e == hipSuccess && rc == TGEMM_OK && warm_ms < tg::kTuneWarmupMs && n < tg::kTuneWarmupMaxLaunches) {
+            e = hipEventRecord(ev[0], st);
+            for (int q = 0; q < 16 && e == hipSuccess && rc == TGEMM_OK; ++q, ++n)
+                rc = tg::launch(cands[def].pl, cands[def].fn, A, B, C, c_type, alpha, bias, act, stream);
+            if (e == hipSuccess && rc == TGEMM_OK) e = hipEventRecord(ev[1], st);
+            if (e == hipSuccess && rc == TGEMM_OK) e = hipEventSynchronize(ev[1]);
+            float ms = 0.f;
+            if (e == hipSuccess && rc == TGEMM_OK) e = hipEventElapsedTime(&ms, ev[0], ev[1]);
+            warm_ms += ms;
+        }
+    }
     if (e == hipSuccess && rc == TGEMM_OK) e = hipEventRecord(ev[0], st);
     for (int r = 0; r < rounds && e == hipSuccess && rc == TGEMM_OK; ++r)
-        for (int i = 0; i < nc && e == hipSuccess && rc == TGEMM_OK; ++i) {
+        for (int q = 0; q < nc && e == hipSuccess && rc == TGEMM_OK; ++q) {
+            const int i = (q + r) % nc;
             rc = tg::launch(cands[i].pl, cands[i].fn, A, B, C, c_type, alpha, bias, act, stream);
-            if (rc == TGEMM_OK) e = hipEventRecord(ev[(size_t)r * nc + i + 1], st);
+            if (rc == TGEMM_OK) e = hipEventRecord(ev[(size_t)r * nc + q + 1], st);
         }
     if (e == hipSuccess && rc == TGEMM_OK) e = hipEventSynchronize(ev.back());
     std::vector<float> med(nc, 0.f);
     for (int i = 0; i < nc && e == hipSuccess && rc == TGEMM_OK; ++i) {
         std::vector<float> t(rounds);
         for (int r = 0; r < rounds && e == hipSuccess; ++r) {
-            const size_t j = (size_t)r * nc + i;
+            const int q = ((i - r) % nc + nc) % nc;   // position of candidate i in round r
+            const size_t j = (size_t)r * nc + q;
             e = hipEventElapsedTime(&t[r], ev[j], ev[j + 1]);
         }
         std::sort(t.begin(), t.end());
@@ -299,9 +329,12 @@ extern "C" int tgemm_tune_gemm(int64_t M, int64_t N, int64_t K, int ab_type, con
         tg::g_last_hip_error = (int)e;
         return TGEMM_ERR_HIP;
     }
+    // the fastest median, unless it beats the untuned launch by too little to
+    // tell from run-to-run noise
     int best = 0;
     for (int i = 1; i < nc; ++i)
         if (med[i] < med[best]) best = i;
+    if (med[best] > tg::kTuneMinGain * med[def]) best = def;
     tg::TuneKey key;
     if (!tg::tune_key(base, &key)) return TGEMM_ERR_HIP;
     const tg::Plan& bp = cands[best].pl;

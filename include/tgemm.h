@@ -185,10 +185,13 @@ int tgemm_gemm_config(int64_t M, int64_t N, int64_t K,
  * the caller's buffers under each launch choice that leaves the result
  * unchanged bit for bit: the K step and LDS ring depth of the direct-to-LDS
  * pipeline (those built for the types) and a raster group height of 4, 8 or
- * 16 tile rows. Each choice runs once to warm up, then `rounds` times (1..100),
- * interleaved with the others, timed with HIP events on `stream`; the choice
- * with the smallest median time is recorded for the problem's key on the
- * current device. The key is everything that selects a kernel: M, N, K, the
+ * 16 tile rows. Each choice runs once; then the untuned launch runs for about
+ * 100 ms of GPU time (at most 4096 launches) so that the power-limited clock
+ * settles; then every choice runs `rounds` times (1..100), interleaved with the
+ * others (round r starts at a different choice), timed with HIP events on
+ * `stream`. The choice with the smallest median time is recorded for the
+ * problem's key on the current device, unless it is less than 1% faster than
+ * the untuned launch, which is then recorded instead. The key is everything that selects a kernel: M, N, K, the
  * three strides, b_layout, both types, whether an epilogue is requested, and
  * the alignment classes of A, B and C. From then on, tgemm_gemm, tgemm_f16,
  * the *_config calls with all five launch choices 0, and the plan queries use
