@@ -1,0 +1,102 @@
+"""Seeded random problems through the typed C entry point, each checked in
+full against the oracle: sizes from 1 to several tiles in every dimension,
+both B layouts, all input and output types, row strides with slack, base
+addresses off by a few elements, and the epilogue on or off. Everything
+outside the operands is NaN and a guard band surrounds C, so any read past an
+operand or write past C shows up.
+
+Tolerance per element (the extended oracle's check):
+  |g - ref| <= 1e-3 * (|alpha| * sum_k |a*b| + |bias[j]|) + ulp_out(ref)
+"""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+import dense_tiled_gemm_tgemm_amd as tg  # noqa: E402
+from dense_tiled_gemm_tgemm_amd import inputs  # noqa: E402
+
+DEV = "cuda:0"
+N_CASES = 120
+ESIZE = {"f16": 2, "bf16": 2, "f32": 4}
+NAN_BITS = {"f16": 0x7E00, "bf16": 0x7FC0}
+
+
+def _cases():
+    rng = np.random.default_rng(20261202)
+    out = []
+    for i in range(N_CASES):
+        ab = str(rng.choice(["f16", "bf16", "f32"]))
+        ct = str(rng.choice(["f16", "bf16", "f32"]))
+        lay = str(rng.choice(["KxN", "NxK"]))
+        M, N, K = (int(x) for x in rng.integers(1, [700, 700, 600]))
+        pads = tuple(int(x) for x in rng.integers(0, 10, 3))
+        offs = tuple(int(x) for x in rng.integers(0, 4, 3))
+        epi = bool(rng.integers(0, 2))
+        out.append((i, ab, ct, lay, M, N, K, pads, offs, epi))
+    return out
+
+
+def _operand(shape, seed, ab):
+    """Seeded values as the bit patterns (uint16) or values (float32) of `ab`."""
+    if ab == "f16":
+        return inputs.random_f16(shape, seed).view(np.uint16)
+    if ab == "bf16":
+        return inputs.random_bf16(shape, seed)
+    return inputs.random_f32(shape, seed)
+
+
+def _embed(x, ld, off, nan):
+    """x placed row by row (stride ld) `off` elements into a NaN-filled buffer."""
+    rows, cols = x.shape
+    buf = np.full(off + rows * ld + 8, nan, dtype=x.dtype)
+    view = buf[off:off + rows * ld].reshape(rows, ld)
+    view[:, :cols] = x
+    return buf
+
+
+@pytest.mark.parametrize("case", _cases(), ids=lambda c: "case%02d" % c[0])
+def test_random_case_full_parity(oracle_mod, case):
+    i, ab, ct, lay, M, N, K, (pa, pb, pc), (oa, ob, oc), epi = case
+    print(f"case random {i}: {ab}->{ct} {lay} {M}x{N}x{K} pads {pa},{pb},{pc} offsets {oa},{ob},{oc} "
+          f"epilogue {epi}", flush=True)
+    A = _operand((M, K), 1000 + i, ab)
+    B = _operand((K, N) if lay == "KxN" else (N, K), 2000 + i, ab)
+    lda, ldb, ldc = K + pa, B.shape[1] + pb, N + pc
+    nan_in = np.float32(np.nan) if ab == "f32" else np.uint16(NAN_BITS[ab])
+    bufA = _embed(A, lda, oa, nan_in)
+    bufB = _embed(B, ldb, ob, nan_in)
+    if ct == "f32":
+        bufC = np.full(oc + M * ldc + 8, np.nan, dtype=np.float32)
+    else:
+        bufC = np.full(oc + M * ldc + 8, NAN_BITS[ct], dtype=np.uint16)
+    alpha, bias, act = 1.0, None, "none"
+    if epi:
+        alpha = (-0.75, 0.5, 1.25)[i % 3]
+        bias = inputs.random_bias(N, 3000 + i, scale=2.0)
+        act = "relu" if i % 2 else "none"
+    dev = lambda x: torch.from_numpy(x.view(np.int16) if x.dtype == np.uint16 else x).to(DEV)  # noqa: E731
+    dA, dB, dC = dev(bufA), dev(bufB), dev(bufC)
+    dbias = torch.from_numpy(bias).to(DEV) if bias is not None else None
+    es_in, es_out = ESIZE[ab], ESIZE[ct]
+    rc = tg.tgemm_gemm(M, N, K, ab, dA.data_ptr() + es_in * oa, lda, dB.data_ptr() + es_in * ob, ldb, lay,
+                       ct, dC.data_ptr() + es_out * oc, ldc, alpha,
+                       dbias.data_ptr() if dbias is not None else None, act,
+                       torch.cuda.current_stream().cuda_stream)
+    assert rc == tg.TGEMM_OK, tg.status_string(rc)
+    torch.cuda.synchronize()
+    out = dC.cpu().numpy()
+    out = out.view(np.uint16) if ct != "f32" else out
+    got = out[oc:oc + M * ldc].reshape(M, ldc)[:, :N]
+    # the guard band and the row slack of C are untouched
+    mask = np.ones(out.shape, dtype=bool)
+    mask[oc:oc + M * ldc].reshape(M, ldc)[:, :N] = False
+    if ct == "f32":
+        assert np.isnan(out[mask]).all(), "a store landed outside C"
+    else:
+        assert (out[mask] == NAN_BITS[ct]).all(), "a store landed outside C"
+    ref, tol = oracle_mod.gemm_ex(A, B, lay, ab, alpha, bias, act)
+    res = oracle_mod.check_ex(np.ascontiguousarray(got), ct, ref, tol)
+    assert res["nfail"] == 0, f"case {i}: {res}"
