@@ -57,7 +57,7 @@ typedef enum { TGEMM_ACT_NONE = 0, TGEMM_ACT_RELU = 1 } tgemm_act;
 enum {
     TGEMM_OK = 0,
     TGEMM_ERR_INVALID = -1,     /* argument check failed; nothing enqueued */
-    TGEMM_ERR_UNSUPPORTED = -2, /* valid but outside what this build runs  */
+    TGEMM_ERR_UNSUPPORTED = -2, /* valid, but outside what the kernels cover  */
     TGEMM_ERR_HIP = -3          /* the HIP runtime reported an error       */
 };
 
