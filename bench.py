@@ -26,6 +26,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -45,11 +46,21 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def code_text(src: str) -> str:
+    """C++ source without comments and whitespace: what the compiler sees
+    (the sources hold no string literal with // or /* in it)."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return re.sub(r"\s+", "", src)
+
+
 def kernel_source_hash() -> str:
+    """Hash of the kernel and planning sources' code (comments ignored): the
+    recorded HBM traffic applies while this matches the hash it was taken with."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -916,7 +916,8 @@ struct DmaCtx {
 // stream over its tiles: the loads issued here are for the step S further on,
 // which is step t + S of tc or, near the end of tc, a first step of the
 // workgroup's next tile tn (none when !has_next: those loads read nothing
-// and write zeros). Its first slice's fragments are in buffer F0 of fa/fb;
+// and write zeros); with a leading empty step (c.lead = 1, 32-deep rings)
+// step u holds data step u - 1. Its first slice's fragments are in buffer F0 of fa/fb;
 // the next step's first fragments end up in buffer F0 ^ (KS / 32 odd).
 // `cur` holds the read positions of stage st on entry and those of the next
 // stage on return; they are derived once per step, before the barrier wait,
