@@ -74,10 +74,14 @@ enum {
  * Degenerate shapes: M == 0 or N == 0 is a successful no-op. K == 0 writes
  * zeros to the M x N region of C (the accumulator starts at zero and the K
  * walk runs zero times).
- * Alignment: any 2-byte-aligned operand works. Operands whose base is
- * 16-byte aligned with a row stride that is a multiple of 8 elements are
- * read with 128-bit loads; C with an 8-byte-aligned base and ldc a multiple
- * of 4 is written with 64-bit stores; other operands take element-wise paths.
+ * Alignment: any 2-byte-aligned operand works. When K > 0 and both operand
+ * row strides are at least 8 elements and small enough for 32-bit offsets,
+ * A and B stream into LDS by 16-byte loads at any 2-byte alignment (rows that
+ * start 16-byte aligned run faster, and rows that start 128-byte aligned,
+ * a stride that is a multiple of 64 elements, fastest); otherwise they are
+ * staged through registers with 128-bit or element loads. C is written with
+ * 16-byte stores where every row starts 16-byte aligned, 8-byte stores where
+ * 8-byte aligned, and element stores otherwise and at its right edge.
  * C must not alias A or B (page 4, section 2.4.12.1: restrict-qualified
  * operands must not overlap).
  */
@@ -99,9 +103,10 @@ int tgemm_f16(int64_t M, int64_t N, int64_t K,
  *                  die-aware renumbering; 0 = default (8 on MI355X);
  *                  1 disables the renumbering; 1..64 otherwise.
  *   k_step:        K depth of one LDS stage of the direct-to-LDS path
- *                  (used whenever K > 0 and both row strides are small
- *                  enough for 32-bit offsets): 0 = default (64, or 32 when
- *                  stages > 2 or K <= 64), 32 or 64 (64 needs K > 64).
+ *                  (used whenever K > 0 and both row strides are at least
+ *                  8 elements and small enough for 32-bit offsets):
+ *                  0 = default (64, or 32 when stages > 2 or K <= 64),
+ *                  32 or 64 (64 needs K > 64).
  *   stages:        LDS ring depth of that path: 0 = default (2 at k_step 64,
  *                  4 at k_step 32), 2..5 (k_step 64 allows only 2). Other
  *                  paths ignore k_step and stages.
