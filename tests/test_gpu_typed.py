@@ -231,6 +231,28 @@ def test_persistent_grid_and_pipelines_agree(oracle_mod, ab, ct, lay):
     _check(oracle_mod, A, B, lay, ab, ct, _out_np(outs[0]), -0.75, b_np, "relu", "persistent", I, J)
 
 
+@pytest.mark.parametrize("ab,ct", [c for c in COMBOS if c[1] != "f32"])
+@pytest.mark.parametrize("lay", ["NxK", "KxN"])
+def test_tile_changes_with_epilogue_bit_identical(oracle_mod, ab, ct, lay):
+    """16-bit C with α, bias and the rectifier, four tiles per workgroup of the
+    persistent kernel (the bias loads sit between the next tile's first loads
+    and this tile's C stores): bit-identical to the register-staged kernel; sampled
+    outputs within tolerance."""
+    M, N, K = 8192, 8192, 640
+    print(f"case typed tile changes {ab}->{ct} {lay}", flush=True)
+    A = _bits((M, K), 51, ab)
+    B = _bits((N, K) if lay == "NxK" else (K, N), 52, ab)
+    b_np, b_dev = _bias(N, 53, True)
+    Ad, Bd = _dev(A, ab), _dev(B, ab)
+    kw = dict(out_dtype=TORCH_DT[ct], alpha=1.25, bias=b_dev, act="relu")
+    C = tg.gemm(Ad, Bd, lay, **kw)
+    base = tg.gemm(Ad, Bd, lay, force_generic=1, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(C.view(torch.int16), base.view(torch.int16))
+    I, J = inputs.sample_points(M, N, 2048, 54)
+    _check(oracle_mod, A, B, lay, ab, ct, _out_np(C), 1.25, b_np, "relu", "tile changes", I, J)
+
+
 @pytest.mark.parametrize("ab,ct", COMBOS)
 @pytest.mark.parametrize("lay", ["NxK", "KxN"])
 def test_odd_step_count_32_deep_ring_agrees(oracle_mod, ab, ct, lay):
