@@ -24,6 +24,7 @@ from ._binding import (  # noqa: F401
     gemm,
     load,
     mfma_issue_probe,
+    xcd_probe,
     mm,
     status_string,
     tgemm_f16,

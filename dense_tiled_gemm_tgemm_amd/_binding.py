@@ -91,6 +91,8 @@ def load():
                                    _INT, _INT, _INT, _INT, _INT, ctypes.POINTER(_I64)]
     lib.tgemm_mfma_issue_probe.restype = _INT
     lib.tgemm_mfma_issue_probe.argtypes = [_I64, _INT, _P, _I64, _P, _P]
+    lib.tgemm_xcd_probe.restype = _INT
+    lib.tgemm_xcd_probe.argtypes = [_I64, _P, _P]
     lib.tgemm_tile_of.restype = _INT
     lib.tgemm_tile_of.argtypes = [_I64, _I64, _INT, _INT, _I64, ctypes.POINTER(_I64), ctypes.POINTER(_I64)]
     _lib = lib
@@ -198,6 +200,13 @@ def mfma_issue_probe(workgroups: int, iters: int, data_ptr: int, data_bytes: int
                                            stream))
     if rc != TGEMM_OK:
         raise TgemmError(rc, "mfma_issue_probe")
+
+
+def xcd_probe(workgroups: int, out_ptr: int, stream=None) -> None:
+    """Launch the die probe (measurement aid; see include/tgemm.h): out[w] = die of workgroup w."""
+    rc = int(load().tgemm_xcd_probe(int(workgroups), out_ptr, stream))
+    if rc != TGEMM_OK:
+        raise TgemmError(rc, "xcd_probe")
 
 
 # ----------------------------------------------------------- torch tensors --

@@ -1,3 +1,5 @@
+// Measurement aids (not part of the product operation).
+//
 // Matrix-core ceiling probe: the GEMM kernel's instruction stream without its
 // synchronization, tile changes or C stores. Each wave (one per SIMD, as in
 // the GEMM) runs `iters` rounds of two 64-instruction slices of independent
@@ -92,6 +94,20 @@ mfma_ceiling_kernel(const uint16_t* data, unsigned data_bytes, float* out, int i
     out[blockIdx.x * 256 + tid] = s;
 }
 
+// Die probe: the first thread of each workgroup records the number of the
+// accelerator die (XCD) it runs on, read from the XCC_ID hardware register
+// (bits 3:0). The die-aware raster assumes that the dispatcher hands
+// workgroup w to die w mod 8; this shows what the hardware does.
+__global__ void __launch_bounds__(64) xcd_id_kernel(int* out, int64_t n) {
+    const int64_t w = blockIdx.x;
+    if (threadIdx.x == 0 && w < n) {
+#if defined(__HIP_DEVICE_COMPILE__)
+        // s_getreg_b32 hwreg(HW_REG_XCC_ID, 0, 4): register 20, offset 0, width 4
+        out[w] = (int)__builtin_amdgcn_s_getreg(20 | (0 << 6) | ((4 - 1) << 11));
+#endif
+    }
+}
+
 }  // namespace tg_probe
 
 extern "C" int tgemm_mfma_issue_probe(int64_t workgroups, int iters, const void* data, int64_t data_bytes,
@@ -105,6 +121,16 @@ extern "C" int tgemm_mfma_issue_probe(int64_t workgroups, int iters, const void*
     void* kargs[] = {&d, &nb, &out, &iters};
     const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&tg_probe::mfma_ceiling_kernel),
                                          dim3((unsigned)workgroups), dim3(256), kargs, 0,
+                                         static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? TGEMM_OK : TGEMM_ERR_HIP;
+}
+
+extern "C" int tgemm_xcd_probe(int64_t workgroups, int* out, void* stream) {
+    if (workgroups <= 0 || workgroups > (1 << 20) || !out) return TGEMM_ERR_INVALID;
+    int64_t n = workgroups;
+    void* kargs[] = {&out, &n};
+    const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&tg_probe::xcd_id_kernel),
+                                         dim3((unsigned)workgroups), dim3(64), kargs, 0,
                                          static_cast<hipStream_t>(stream));
     return e == hipSuccess ? TGEMM_OK : TGEMM_ERR_HIP;
 }

@@ -410,3 +410,68 @@ def test_mfma_issue_probe_runs():
     for wg, nb in ((0, 1 << 20), (8, (1 << 20) + 2), (8, 1 << 19)):
         with pytest.raises(tg.TgemmError):
             tg.mfma_issue_probe(wg, 4, data.data_ptr(), nb, out.data_ptr(), st)
+
+
+def test_xcd_probe_dispatch_order():
+    """The die probe (measurement aid for the die-aware raster): over a launch of
+    8192 workgroups every recorded die number lies in [0, 8) and workgroup w ran
+    on die w mod 8, the order the raster's renumbering assumes."""
+    print("case xcd probe", flush=True)
+    n = 8192
+    st = torch.cuda.current_stream().cuda_stream
+    out = torch.full((n,), -1, dtype=torch.int32, device=DEV)
+    tg.xcd_probe(n, out.data_ptr(), st)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    share = float(np.mean(got == np.arange(n) % 8))
+    print(f"  per die {np.bincount(np.clip(got, 0, 15), minlength=8).tolist()}, w mod 8 share {share:.4f}",
+          flush=True)
+    assert got.min() >= 0 and got.max() < 8
+    assert share == 1.0
+    with pytest.raises(tg.TgemmError):
+        tg.xcd_probe(0, out.data_ptr(), st)
+
+
+def _signed(bits, rng):
+    return bits | (rng.integers(0, 2, size=bits.shape).astype(np.uint16) << 15)
+
+
+@pytest.mark.parametrize("generic", [0, 1])
+@pytest.mark.parametrize("lay", ["NxK", "KxN"])
+def test_binary16_subnormals_kept(lay, generic):
+    """Subnormal binary16 values pass through unchanged. As operands: random
+    subnormals times the identity give C = A bit for bit, so the matrix
+    instructions do not flush subnormal inputs. As results: the smallest normals
+    (even significands) times 1/2 are exact subnormals, so the fp32 -> binary16
+    store does not flush them either."""
+    print(f"case subnormals {lay} generic={generic}", flush=True)
+    M = N = K = 256
+    rng = np.random.default_rng(11)
+    A1 = _signed(rng.integers(1, 0x400, size=(M, K)).astype(np.uint16), rng).view(np.float16)
+    eye = np.eye(K, dtype=np.float16)                        # symmetric: either layout
+    C1 = _run(A1, eye, lay, force_generic=generic)
+    lost = int(np.sum(C1.view(np.uint16) != A1.view(np.uint16)))
+    assert lost == 0, f"{lost} of {M * K} subnormal operands changed"
+    A2 = _signed((0x400 | (2 * rng.integers(0, 0x200, size=(M, K)))).astype(np.uint16), rng).view(np.float16)
+    C2 = _run(A2, (0.5 * eye).astype(np.float16), lay, force_generic=generic)
+    want = (A2.astype(np.float64) / 2).astype(np.float16)
+    assert (np.abs(want.astype(np.float64)) < 2.0 ** -14).all() and (want != 0).all()
+    lost = int(np.sum(C2.view(np.uint16) != want.view(np.uint16)))
+    assert lost == 0, f"{lost} of {M * K} subnormal results changed"
+
+
+def test_bfloat16_subnormal_operands_kept():
+    """The same for bfloat16 operands (exponent field 0, significand 1..127),
+    bfloat16 C: A times the identity gives A bit for bit."""
+    print("case bf16 subnormals", flush=True)
+    M = N = K = 256
+    rng = np.random.default_rng(12)
+    A = _signed(rng.integers(1, 0x80, size=(M, K)).astype(np.uint16), rng)
+    eye = np.where(np.eye(K, dtype=bool), np.uint16(0x3F80), np.uint16(0))
+    Ad = torch.from_numpy(A.view(np.int16)).to(DEV).view(torch.bfloat16)
+    Bd = torch.from_numpy(eye.view(np.int16)).to(DEV).view(torch.bfloat16)
+    for generic in (0, 1):
+        C = tg.gemm(Ad, Bd, "KxN", out_dtype=torch.bfloat16, force_generic=generic)
+        got = C.view(torch.int16).cpu().numpy().view(np.uint16)
+        lost = int(np.sum(got != A))
+        assert lost == 0, f"generic={generic}: {lost} of {M * K} subnormal operands changed"
