@@ -96,8 +96,9 @@ mfma_ceiling_kernel(const uint16_t* data, unsigned data_bytes, float* out, int i
 
 // Die probe: the first thread of each workgroup records the number of the
 // accelerator die (XCD) it runs on, read from the XCC_ID hardware register
-// (bits 3:0). The die-aware raster assumes that the dispatcher hands
-// workgroup w to die w mod 8; this shows what the hardware does.
+// (bits 3:0). The die-aware raster assumes that the dispatcher deals
+// workgroups to the dies in turn, so that those sharing a die are the ones
+// with equal w mod 8; this shows what the hardware does.
 __global__ void __launch_bounds__(64) xcd_id_kernel(int* out, int64_t n) {
     const int64_t w = blockIdx.x;
     if (threadIdx.x == 0 && w < n) {

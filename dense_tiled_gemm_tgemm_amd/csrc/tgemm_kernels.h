@@ -206,6 +206,19 @@ __device__ __forceinline__ void store16_stream(const u32x4& v, const BufRsrc& r,
 #endif
 }
 
+// A 16-byte store that only lanes with `ok` perform, without a branch: the
+// other lanes present an offset at or beyond the resource's record count
+// (0x7fffffff), which the hardware drops. The empty asm hands the selected
+// offset to the store as it is, so no constant part of it is moved into the
+// instruction's immediate offset (which would shift the dropped lanes' offset
+// back into range).
+constexpr unsigned kCOob = 0x80000000u;
+__device__ __forceinline__ void store16_lanes(const u32x4& v, const BufRsrc& r, bool ok, int64_t byte_offset) {
+    unsigned o = ok ? (unsigned)byte_offset : kCOob;
+    asm volatile("" : "+v"(o));
+    store16_stream(v, r, (int)o);
+}
+
 // Lane l of wave (wm, wn) holds, in acc[i][j], C row m0 + 128 wm + 16 i + (l mod 16)
 // at columns n0 + 16 NJ wn + 16 j + 4 (l / 16) + 0..3 (NJ = 8 column blocks per
 // wave, 4 in the two-workgroups-per-unit binary32 kernel).
@@ -221,7 +234,12 @@ __device__ __forceinline__ void store16_stream(const u32x4& v, const BufRsrc& r,
 //    every C row starts 16-byte aligned, element stores otherwise (an 8-byte
 //    path here made the register allocator move the accumulators around in
 //    the main loop of the binary32-operand kernel).
-// All lanes run the exchange; only the stores are predicated. One 16-row block
+// All lanes run the exchange; only the stores are predicated: the 16-byte store
+// on its own condition, the 8-byte and element stores behind one uniform test
+// (`whole`: the wave's 128 rows lie inside C and its columns end at or before
+// N, with 16-byte rows), so an interior wave skips them with one scalar branch
+// per store instead of a chain of exec-mask branches, which took longer than
+// the conversions themselves. One 16-row block
 // at a time (pinned), so the temporaries stay few when this runs between two
 // tiles with the next tile's fragments already in registers. Vector stores
 // use the streaming policies (store16_stream above; the 8-byte path is
@@ -242,6 +260,8 @@ __device__ __forceinline__ void store_c(const f32x4 (&acc)[8][NJ], const Args& a
         alpha = a.alpha;
         relu = a.relu != 0;
     }
+    const bool whole = __builtin_amdgcn_readfirstlane(
+        (int)(a.c16 && m0 + wm * 128 + 128 <= a.M && n0 + wn * 16 * NJ + 16 * NJ <= a.N)) != 0;
     if constexpr (CT == 2) {
         const int colb = n0 + wn * 16 * NJ + 4 * g;
         float* base = static_cast<float*>(a.C) + (int64_t)(m0 + wm * 128 + r16) * a.ldc + colb;
@@ -264,12 +284,15 @@ __device__ __forceinline__ void store_c(const f32x4 (&acc)[8][NJ], const Args& a
                 for (int e = 0; e < 4; ++e) v[e] = epi<EPI>(x[e], alpha, EPI ? bv[j][e] : 0.f, relu);
                 const int col = colb + 16 * j;
                 float* dst = row + 16 * j;
-                if (row_ok && col + 4 <= a.N && a.c16) {
-                    store16_stream(__builtin_bit_cast(u32x4, v), crs, ((int64_t)(i * 16 + r16) * a.ldc + colb + 16 * j) * 4);
-                } else if (row_ok && col < a.N) {
+                const bool ok16 = row_ok & (col + 4 <= a.N) & (a.c16 != 0);
+                store16_lanes(__builtin_bit_cast(u32x4, v), crs, ok16, ((int64_t)(i * 16 + r16) * a.ldc + colb + 16 * j) * 4);
+                if (__builtin_expect(!whole, 0)) {
+                    asm volatile("");                 // a scalar branch of its own, not merged into the lane mask
+                    if (!ok16 && row_ok && col < a.N) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (col + e < a.N) dst[e] = v[e];
+                        for (int e = 0; e < 4; ++e)
+                            if (col + e < a.N) dst[e] = v[e];
+                    }
                 }
             }
         }
@@ -281,6 +304,7 @@ __device__ __forceinline__ void store_c(const f32x4 (&acc)[8][NJ], const Args& a
             __builtin_amdgcn_sched_barrier(0);
             const bool row_ok = m0 + wm * 128 + i * 16 + r16 < a.M;
             uint16_t* row = base + (int64_t)i * 16 * a.ldc;
+            u32x4 vs[NJ / 2];
 #pragma unroll
             for (int pr = 0; pr < NJ / 2; ++pr) {
                 const f32x4& x = acc[i][2 * pr];
@@ -299,16 +323,27 @@ __device__ __forceinline__ void store_c(const f32x4 (&acc)[8][NJ], const Args& a
                 const auto s1 = __builtin_amdgcn_permlane16_swap(x23, y23, false, false);
                 const u32x4 v = u32x4{s0[0], s1[0], s0[1], s1[1]};
                 const int col = col0 + 32 * pr;
-                uint16_t* dst = row + 32 * pr;
-                if (row_ok && col + 8 <= a.N && a.c16) {
-                    store16_stream(v, crs, ((int64_t)(i * 16 + r16) * a.ldc + col0 + 32 * pr) * 2);
-                } else if (row_ok && col + 8 <= a.N && a.c8) {
-                    __builtin_nontemporal_store(u32x2{v[0], v[1]}, (u32x2*)dst);
-                    __builtin_nontemporal_store(u32x2{v[2], v[3]}, (u32x2*)(dst + 4));
-                } else if (row_ok && col < a.N) {
+                const bool ok16 = row_ok & (col + 8 <= a.N) & (a.c16 != 0);
+                store16_lanes(v, crs, ok16, ((int64_t)(i * 16 + r16) * a.ldc + col0 + 32 * pr) * 2);
+                vs[pr] = v;
+            }
+            if (__builtin_expect(!whole, 0)) {
+                asm volatile("");                     // a scalar branch of its own, not merged into the lane mask
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        if (col + e < a.N) dst[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+                for (int pr = 0; pr < NJ / 2; ++pr) {
+                    const u32x4& v = vs[pr];
+                    const int col = col0 + 32 * pr;
+                    uint16_t* dst = row + 32 * pr;
+                    const bool ok16 = row_ok & (col + 8 <= a.N) & (a.c16 != 0);
+                    if (ok16 || !row_ok) {
+                    } else if (col + 8 <= a.N && a.c8) {
+                        __builtin_nontemporal_store(u32x2{v[0], v[1]}, (u32x2*)dst);
+                        __builtin_nontemporal_store(u32x2{v[2], v[3]}, (u32x2*)(dst + 4));
+                    } else if (col < a.N) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            if (col + e < a.N) dst[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+                    }
                 }
             }
         }

@@ -294,9 +294,9 @@ int tgemm_mfma_issue_probe(int64_t workgroups, int iters, const void* data, int6
  * Measurement aid (not part of the product operation): launches `workgroups`
  * workgroups of 64 threads; workgroup w writes to out[w] the number (0-15)
  * of the accelerator die (XCD) it ran on, read from the XCC_ID hardware
- * register. The die-aware renumbering in tgemm_tile_of assumes that
- * workgroup w runs on die w mod num_xcd (page 1, section "Swizzle", gives the
- * grouped order this renumbering feeds). `out`: device memory for
+ * register. The die-aware renumbering in tgemm_tile_of assumes that the
+ * workgroups sharing a die are those with equal w mod num_xcd (page 1,
+ * section "Swizzle", gives the grouped order this renumbering feeds). `out`: device memory for
  * `workgroups` ints. Returns TGEMM_OK, TGEMM_ERR_INVALID (workgroups outside
  * [1, 2^20] or a null `out`) or TGEMM_ERR_HIP.
  */

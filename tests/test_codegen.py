@@ -98,3 +98,30 @@ def test_no_accumulator_spill_slot_reuse(asm, case):
     for name, body in _kernels(asm[case]):
         bad = [l.strip() for l in body if "Reload Reuse" in l]
         assert not bad, (name, bad[:4])
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "ab%d_ct%d_epi%d" % c)
+def test_c_store_offsets_drop_masked_lanes(asm, case):
+    """The 16-byte C stores are predicated by offset, not by branch: a lane
+    that must not store presents 0x80000000, beyond the C resource's record
+    count, and the hardware drops the store. Every such store's offset must
+    therefore come straight from a select against that value, with no constant
+    folded into the instruction's immediate offset (which would move a dropped
+    lane's offset back into range)."""
+    n = 0
+    for name, body in _kernels(asm[case]):
+        ins = [l.strip() for l in body if l.strip() and not l.strip().startswith((";", "."))]
+        oob = {m.group(1) for l in ins for m in [re.match(r"v_bfrev_b32_e32 (v\d+), 1$", l)] if m}
+        for i, l in enumerate(ins):
+            if not (l.startswith("buffer_store_dwordx4") and "nt sc1" in l):
+                continue
+            m = re.match(r"buffer_store_dwordx4 v\[\d+:\d+\], (v\d+), s\[\d+:\d+\], 0 offen nt sc1$", l)
+            assert m, (name, l)
+            j = i - 1
+            while j >= 0 and not re.match(r"\S+ %s," % m.group(1), ins[j]):
+                j -= 1
+            d = ins[j]
+            assert d.startswith("v_cndmask_b32") and (any(r in d.split(", ")[1:] for r in oob) or "0x80000000" in d), \
+                (name, l, d)
+            n += 1
+    assert n >= 32, n
