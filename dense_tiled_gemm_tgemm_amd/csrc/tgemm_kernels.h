@@ -82,22 +82,24 @@ struct Args {
 // LDS layout of one staged K-contiguous operand block (256 rows x KS halves)
 // as 16-byte chunks, CPR = KS / 8 per row, chunk c of row r at slot
 // r * CPR + (c ^ f(r)):
-//   KS = 64: f(r) = (r & 7) ^ ((r >> 3) & 1)
+//   KS = 64: f(r) = r & 7
 //   KS = 32: f(r) = (r ^ (r >> 2)) & 3
 // A fragment read takes 16 consecutive rows at one chunk per 16-lane group
-// (4 groups = 4 consecutive chunks); both maps keep every 8- and 16-lane
-// group of such a read on distinct 16-byte bank groups, and the chunks of
-// any row distinct, so reads and 128-bit writes are free of bank conflicts
-// (page 3, sections 3.1 and 5.3; page 5, "Why swizzle matters"). Both depend
-// on r mod 16 only, so the fragment of 16-row block i sits 16 * CPR slots
-// after that of block 0.
+// (4 groups = 4 consecutive chunks). The direct-to-LDS loads write each
+// instruction's 1 KiB linearly, so only the reads can collide. Measured on
+// gfx950 (LDS conflict counters of a read-only probe): the KS = 64 map serves
+// each 16-byte read in 4 LDS cycles, the rate of a plain linear read, while
+// the earlier map (r & 7) ^ ((r >> 3) & 1), conflict-free on paper for
+// 16-lane groups, took 8 (page 3, sections 3.1 and 5.3; page 5, "Why swizzle
+// matters"). Both maps depend on r mod 16 only, so the fragment of 16-row
+// block i sits 16 * CPR slots after that of block 0.
 template <int KS>
 struct Lds {
     static constexpr int kCpr = KS / 8;
     static constexpr int kBlock = 256 * kCpr;          // chunks per operand block
     static constexpr int kStage = 2 * kBlock;          // A block then B block
     __device__ static __forceinline__ int swz(int r) {
-        return KS == 64 ? ((r & 7) ^ ((r >> 3) & 1)) : ((r ^ (r >> 2)) & 3);
+        return KS == 64 ? (r & 7) : ((r ^ (r >> 2)) & 3);
     }
     __device__ static __forceinline__ int slot(int r, int c) { return r * kCpr + (c ^ swz(r)); }
 };
