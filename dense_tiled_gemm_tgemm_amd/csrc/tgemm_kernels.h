@@ -83,23 +83,23 @@ struct Args {
 // as 16-byte chunks, CPR = KS / 8 per row, chunk c of row r at slot
 // r * CPR + (c ^ f(r)):
 //   KS = 64: f(r) = r & 7
-//   KS = 32: f(r) = (r ^ (r >> 2)) & 3
+//   KS = 32: f(r) = (r >> 1) & 3
 // A fragment read takes 16 consecutive rows at one chunk per 16-lane group
 // (4 groups = 4 consecutive chunks). The direct-to-LDS loads write each
 // instruction's 1 KiB linearly, so only the reads can collide. Measured on
-// gfx950 (LDS conflict counters of a read-only probe): the KS = 64 map serves
-// each 16-byte read in 4 LDS cycles, the rate of a plain linear read, while
-// the earlier map (r & 7) ^ ((r >> 3) & 1), conflict-free on paper for
-// 16-lane groups, took 8 (page 3, sections 3.1 and 5.3; page 5, "Why swizzle
-// matters"). Both maps depend on r mod 16 only, so the fragment of 16-row
-// block i sits 16 * CPR slots after that of block 0.
+// gfx950 (LDS conflict counters of a read-only probe): both maps serve each
+// 16-byte read in 4 LDS cycles, the rate of a plain linear read, while the
+// earlier maps (r & 7) ^ ((r >> 3) & 1) and (r ^ (r >> 2)) & 3, conflict-free
+// on paper for 16-lane groups, took 8 (page 3, sections 3.1 and 5.3; page 5,
+// "Why swizzle matters"). Both maps depend on r mod 16 only, so the fragment
+// of 16-row block i sits 16 * CPR slots after that of block 0.
 template <int KS>
 struct Lds {
     static constexpr int kCpr = KS / 8;
     static constexpr int kBlock = 256 * kCpr;          // chunks per operand block
     static constexpr int kStage = 2 * kBlock;          // A block then B block
     __device__ static __forceinline__ int swz(int r) {
-        return KS == 64 ? (r & 7) : ((r ^ (r >> 2)) & 3);
+        return KS == 64 ? (r & 7) : ((r >> 1) & 3);
     }
     __device__ static __forceinline__ int slot(int r, int c) { return r * kCpr + (c ^ swz(r)); }
 };
