@@ -137,11 +137,21 @@ static int plan_gemm(int64_t M, int64_t N, int64_t K, int ab_type, const void* A
                        pl, ab_type, c_type, bias, epi);
     if (rc != TGEMM_OK) return rc;
     TuneChoice t;
-    if (use_tuned && !force_generic && !group_m && !num_xcd && !k_step && !stages && tuned_choice(*pl, &t)) {
+    const bool automatic = !force_generic && !group_m && !num_xcd && !k_step && !stages;
+    if (automatic && use_tuned && tuned_choice(*pl, &t)) {
         Plan tp;
         rc = make_plan(M, N, K, A, lda, B, ldb, b_layout, C, ldc, 0, t.group_m, t.num_xcd, t.k_step, t.stages,
                        &tp, ab_type, c_type, bias, epi);
         if (rc == TGEMM_OK) *pl = tp;
+    } else if (automatic && (pl->variant & kDma) && !(pl->variant & kLayoutNxK) && ab_type != TGEMM_F32 &&
+               K > 64 && K % 64 != 0) {
+        const int ncu = compute_units();
+        if (ncu > 0 && pl->W <= ncu) {
+            Plan rp;
+            rc = make_plan(M, N, K, A, lda, B, ldb, b_layout, C, ldc, 0, 0, 0, kPartialKxNKStep, 0, &rp,
+                           ab_type, c_type, bias, epi);
+            if (rc == TGEMM_OK) *pl = rp;
+        }
     }
     *fn = pick_kernel(*pl);
     return *fn ? TGEMM_OK : TGEMM_ERR_UNSUPPORTED;

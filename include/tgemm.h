@@ -109,7 +109,10 @@ int tgemm_f16(int64_t M, int64_t N, int64_t K,
  *                  32 or 64 (64 needs K > 64).
  *   stages:        LDS ring depth of that path: 0 = default (2 at k_step 64,
  *                  4 at k_step 32), 2..5 (k_step 64 allows only 2). Other
- *                  paths ignore k_step and stages.
+ *                  paths ignore k_step and stages. With every launch choice
+ *                  0 and no tuned choice recorded, 16-bit operands with B
+ *                  stored K x N, K > 64 not a multiple of 64 and at most one
+ *                  tile per compute unit run at k_step 32 (default depth).
  * Out-of-range choices return TGEMM_ERR_INVALID. Every choice computes the
  * same C bit for bit (each output's k order is fixed by its tile position).
  */

@@ -90,3 +90,30 @@ def test_tuning_with_epilogue_and_bf16(oracle_mod):
     res = oracle_mod.check_ex(got[I, J], "f32", ref, tol)
     assert res["nfail"] == 0, res
     assert np.array_equal(got, base.cpu().numpy())
+
+
+@pytest.mark.parametrize("lay,K,tiles_m,ab,want", [
+    ("KxN", 1000, 4, "f16", (32, 4)),     # B K x N, K % 64 != 0, one round: 32-deep default ring
+    ("KxN", 1000, 4, "bf16", (32, 4)),
+    ("KxN", 1024, 4, "f16", (64, 2)),     # K a multiple of 64
+    ("NxK", 1000, 4, "f16", (64, 2)),     # B stored N x K
+    ("KxN", 1000, 40, "f16", (64, 2)),    # more tiles than compute units: persistent 64-deep
+])
+def test_automatic_pipeline_choice(lay, K, tiles_m, ab, want):
+    """With every launch choice automatic, B stored K x N with a partial last
+    64-deep step on a grid of one round or less runs 32-deep steps; the other
+    cases keep the 64-deep ring. Same bits either way."""
+    print(f"case automatic pipeline {lay} K={K} tiles_m={tiles_m} {ab}", flush=True)
+    M, N = 256 * tiles_m, 2048
+    dt = torch.float16 if ab == "f16" else torch.bfloat16
+    gen = inputs.random_f16 if ab == "f16" else inputs.random_bf16
+    A = _dev16(gen((M, K), 7).view(np.uint16), dt)
+    B = _dev16(gen((K, N) if lay == "KxN" else (N, K), 8).view(np.uint16), dt)
+    C = torch.empty((M, N), dtype=dt, device=DEV)
+    tg.tuning_clear()
+    rc, plan = _plan(A, B, C, lay, ab, ab)
+    assert rc == 0 and (plan["bk"], plan["stages"]) == want, plan
+    auto = tg.gemm(A, B, lay)
+    other = tg.gemm(A, B, lay, k_step=64 if want[0] == 32 else 32)
+    torch.cuda.synchronize()
+    assert torch.equal(auto.view(torch.int16), other.view(torch.int16))
