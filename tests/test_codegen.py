@@ -100,6 +100,42 @@ def test_no_accumulator_spill_slot_reuse(asm, case):
         assert not bad, (name, bad[:4])
 
 
+def _unguarded_c_stores(ins):
+    """(count of streaming 16-byte stores, those whose offset does not come
+    straight from a select against 0x80000000) in a list of instructions."""
+    oob = {m.group(1) for l in ins for m in [re.match(r"v_bfrev_b32_e32 (v\d+), 1$", l)] if m}
+    n, bad = 0, []
+    for i, l in enumerate(ins):
+        if not (l.startswith("buffer_store_dwordx4") and "nt sc1" in l):
+            continue
+        n += 1
+        m = re.match(r"buffer_store_dwordx4 v\[\d+:\d+\], (v\d+), s\[\d+:\d+\], 0 offen nt sc1$", l)
+        if not m:
+            bad.append(l)
+            continue
+        j = i - 1
+        while j >= 0 and not re.match(r"\S+ %s," % m.group(1), ins[j]):
+            j -= 1
+        d = ins[j] if j >= 0 else ""
+        if not (d.startswith("v_cndmask_b32") and (any(r in d.split(", ")[1:] for r in oob) or "0x80000000" in d)):
+            bad.append(l)
+    return n, bad
+
+
+def test_unguarded_store_check_catches_planted_mistakes():
+    """The check below on hand-made instruction lists: a guarded store passes;
+    an immediate offset, or an offset register that is not the select's
+    result, is reported."""
+    good = ["v_bfrev_b32_e32 v9, 1", "v_cndmask_b32_e64 v6, v9, v6, s[18:19]",
+            "buffer_store_dwordx4 v[10:13], v6, s[60:63], 0 offen nt sc1"]
+    assert _unguarded_c_stores(good) == (1, [])
+    imm = good[:2] + ["buffer_store_dwordx4 v[10:13], v6, s[60:63], 0 offen offset:64 nt sc1"]
+    assert len(_unguarded_c_stores(imm)[1]) == 1
+    plain = ["v_bfrev_b32_e32 v9, 1", "v_add_u32_e32 v6, 64, v7",
+             "buffer_store_dwordx4 v[10:13], v6, s[60:63], 0 offen nt sc1"]
+    assert len(_unguarded_c_stores(plain)[1]) == 1
+
+
 @pytest.mark.parametrize("case", CASES, ids=lambda c: "ab%d_ct%d_epi%d" % c)
 def test_c_store_offsets_drop_masked_lanes(asm, case):
     """The 16-byte C stores are predicated by offset, not by branch: a lane
@@ -111,17 +147,7 @@ def test_c_store_offsets_drop_masked_lanes(asm, case):
     n = 0
     for name, body in _kernels(asm[case]):
         ins = [l.strip() for l in body if l.strip() and not l.strip().startswith((";", "."))]
-        oob = {m.group(1) for l in ins for m in [re.match(r"v_bfrev_b32_e32 (v\d+), 1$", l)] if m}
-        for i, l in enumerate(ins):
-            if not (l.startswith("buffer_store_dwordx4") and "nt sc1" in l):
-                continue
-            m = re.match(r"buffer_store_dwordx4 v\[\d+:\d+\], (v\d+), s\[\d+:\d+\], 0 offen nt sc1$", l)
-            assert m, (name, l)
-            j = i - 1
-            while j >= 0 and not re.match(r"\S+ %s," % m.group(1), ins[j]):
-                j -= 1
-            d = ins[j]
-            assert d.startswith("v_cndmask_b32") and (any(r in d.split(", ")[1:] for r in oob) or "0x80000000" in d), \
-                (name, l, d)
-            n += 1
+        k, bad = _unguarded_c_stores(ins)
+        assert not bad, (name, bad[:3])
+        n += k
     assert n >= 32, n
