@@ -720,8 +720,9 @@ __device__ __forceinline__ s16x4 frag_b_tr(const FragPtrs<KS, NXK>& f, int so, i
 //    the scalar offset by KS * 2 bytes.
 //  * B stored K x N ([k][n], 32 chunks per k row): slot -> k row 8j +
 //    (tid >> 5), physical chunk tid & 31, holding logical chunk
-//    (tid & 31) ^ h(k row). The K step advances the scalar offset by
-//    KS * ldb * 2 bytes.
+//    (tid & 31) ^ h(k row). Each K step loads through a resource based at
+//    its own first k row (b_step_rsrc), so these offsets stay below
+//    KS * ldb * 2 + 512 bytes for every K.
 // voff[idx] is the row's byte offset plus the chunk's, relative to the
 // tile's resource base; it is the same for every tile.
 template <int KS>
@@ -911,9 +912,13 @@ __device__ __forceinline__ void slice(f32x4 (&acc)[8][8], const half8 (&fa)[8], 
     }
 }
 
-// One output tile: its origin and its operands' buffer resources.
+// One output tile: its origin and its operands' buffer resources. For B
+// stored K x N, rb.base is column n0 of k row 0 and bspan the byte span from
+// there to B's last element; each K step gets a resource of its own
+// (b_step_rsrc), so the offsets a step forms cover only its KS rows of B.
 struct Tile {
     Rsrc ra, rb;
+    int64_t bspan;
     int m0, n0;
 };
 
@@ -926,8 +931,29 @@ __device__ __forceinline__ Tile make_tile(const Args& a, int wid) {
     t.n0 = tn * BN;
     t.ra = operand_rsrc(a.A, a.lda, a.M, a.K, t.m0);
     // B: N x K rows n0.. ; K x N columns n0.. of all K rows
-    t.rb = NXK ? operand_rsrc(a.B, a.ldb, a.N, a.K, t.n0) : operand_rsrc(a.B + t.n0, a.ldb, a.K, a.N - t.n0, 0);
+    if (NXK) {
+        t.rb = operand_rsrc(a.B, a.ldb, a.N, a.K, t.n0);
+        t.bspan = 0;
+    } else {
+        t.rb = Rsrc{a.B + t.n0, 0};
+        t.bspan = ((int64_t)(a.K - 1) * a.ldb + (a.N - t.n0)) * 2;
+    }
     return t;
+}
+
+// B's resource for data step d of tile t (B stored N x K: the tile's own,
+// the step is a scalar offset). B stored K x N: based at k row d * KS, with
+// the record count running to B's last element (rows past K read zeros),
+// capped below kOob; the lane offsets then stay below KS rows of B, so any
+// K works with a row stride up to the K-contiguous limit. Scalar arithmetic
+// only (d is uniform); a step that loads nothing passes d = 0.
+template <int KS, int NXK>
+__device__ __forceinline__ Rsrc b_step_rsrc(const Tile& t, int d, int64_t ldb) {
+    if (NXK) return t.rb;
+    const int64_t rows = (int64_t)d * KS;
+    int64_t span = t.bspan - rows * ldb * 2;
+    span = span < 0 ? 0 : (span > (int64_t)kOob - 1 ? (int64_t)kOob - 1 : span);
+    return Rsrc{t.rb.base + rows * ldb, (int)span};
 }
 
 // Per-workgroup constants of the direct-to-LDS kernel. LDS holds the S
@@ -935,7 +961,7 @@ __device__ __forceinline__ Tile make_tile(const Args& a, int wid) {
 template <int KS, int NXK, int S>
 struct DmaCtx {
     LaneLoads<KS> p;
-    unsigned bstep;       // scalar-offset advance of B per K step
+    unsigned bstep;       // scalar-offset advance of B per K step (B stored N x K; K x N rebases instead)
     int nk, klast;        // K steps per tile; first k of a tile's last step
     int lead;             // leading empty steps (0 or 1): data step of step t is t - lead
     bool fixup;           // a tile's last step needs fix_last_step
@@ -988,9 +1014,9 @@ __device__ __forceinline__ void dma_step(f32x4 (&acc)[8][8], half8 (&fa)[2][8], 
     const bool live = !in_next || has_next;
     const int ld = KS == 32 ? ls - c.lead : ls;      // >= 0: tl >= S > lead
     const unsigned soa = live ? (unsigned)ld * (unsigned)(KS * 2) : kOob;
-    const unsigned sob = live ? (unsigned)ld * c.bstep : kOob;
+    const unsigned sob = live ? (NXK ? (unsigned)ld * c.bstep : 0u) : kOob;
     const Rsrc lra = in_next ? tn.ra : tc.ra;
-    const Rsrc lrb = in_next ? tn.rb : tc.rb;
+    const Rsrc lrb = b_step_rsrc<KS, NXK>(in_next ? tn : tc, live ? ld : 0, a.ldb);
     TG_COMPILER_FENCE();
     __builtin_amdgcn_sched_barrier(0);
     wait_lgkmcnt0();                                  // this wave's reads of stage st returned
@@ -1072,7 +1098,7 @@ tgemm_dma_kernel(Args a) {
 
     DmaCtx<KS, NXK, S> c;
     c.p = lane_loads<KS, NXK>(a, tid);
-    c.bstep = NXK ? (unsigned)(KS * 2) : (unsigned)KS * (unsigned)a.ldb * 2u;
+    c.bstep = (unsigned)(KS * 2);
     c.nk = nk;
     c.lead = lead;
     c.klast = (nkd - 1) * KS;
@@ -1090,8 +1116,10 @@ tgemm_dma_kernel(Args a) {
             const int d = t - lead;                   // data step
             const bool live = d >= 0 && t < nk;
             for (int idx = 0; idx < kLps; ++idx)
-                issue_load<KS, NXK>(tc.ra, tc.rb, c.p, idx, live ? (unsigned)d * (unsigned)(KS * 2) : kOob,
-                                    live ? (unsigned)d * c.bstep : kOob, c.a_blk(t), c.b_blk(t), wave);
+                issue_load<KS, NXK>(tc.ra, b_step_rsrc<KS, NXK>(tc, live ? d : 0, a.ldb), c.p, idx,
+                                    live ? (unsigned)d * (unsigned)(KS * 2) : kOob,
+                                    live ? (NXK ? (unsigned)d * c.bstep : 0u) : kOob, c.a_blk(t), c.b_blk(t),
+                                    wave);
         }
         wait_vmcnt<(S - 1) * kLps>();                 // step 0 landed
         if (c.fixup && nk == 1)

@@ -85,6 +85,7 @@ struct Plan {
     int grid_m, grid_n, W;
     int group_m, num_xcd;
     int k_step, stages;   // K step per LDS stage and ring depth of the launched kernel
+    int grid;             // workgroups launched (W, or the compute units for a persistent launch)
 };
 
 inline bool span_bytes(int64_t rows, int64_t cols, int64_t ld, uint64_t* bytes, int esize = 2) {
@@ -174,8 +175,8 @@ inline int make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
     const bool vec_c = ((uintptr_t)C % c_vec == 0) && ((ldc * c_size) % c_vec == 0);
     // direct-to-LDS (any 2-byte alignment: gfx950 buffer loads accept
     // unaligned addresses): row strides small enough for 32-bit panel
-    // offsets; a K x N B additionally needs every byte offset it forms,
-    // below (K + 64) * ldb * 2 + 512, to stay below 2^31.
+    // offsets (a K x N B is rebased at every K step, so its offsets stay
+    // below 64 * ldb * 2 + 512 bytes whatever K is: the same stride limit).
     // (K == 0 only writes zeros: the register-staged kernel does that)
     // (row strides of at least 8 elements: then a 16-byte access can run past
     // the end of an operand only in its last row, which the kernel reloads
@@ -189,9 +190,7 @@ inline int make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
                (b_layout == TGEMM_B_NxK ? ldb <= kMaxDmaLd / 2
                                         : N % 4 == 0 && ldb < (int64_t(1) << 29) &&
                                               (K + 64) * ldb < (int64_t(1) << 29) - 256))
-            : (!force_generic && K > 0 && lda >= 8 && ldb >= 8 && lda <= kMaxDmaLd &&
-               (b_layout == TGEMM_B_NxK ? ldb <= kMaxDmaLd
-                                        : ldb < (int64_t(1) << 30) && (K + 64) * ldb < (int64_t(1) << 30) - 512));
+            : (!force_generic && K > 0 && lda >= 8 && ldb >= 8 && lda <= kMaxDmaLd && ldb <= kMaxDmaLd);
     pl->variant = (vec_ab ? kVecAB : 0) | (vec_c ? kVecC : 0) |
                   (b_layout == TGEMM_B_NxK ? kLayoutNxK : 0) | (dma ? kDma : 0);
     if (ab_type == TGEMM_F32) {
@@ -213,6 +212,7 @@ inline int make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
     pl->grid_m = (int)gm;
     pl->grid_n = (int)gn;
     pl->W = (int)(gm * gn);
+    pl->grid = pl->W;
     return TGEMM_OK;
 }
 
