@@ -75,7 +75,7 @@ def load():
     lib.tgemm_gemm_config.restype = _INT
     lib.tgemm_gemm_config.argtypes = ex_args + [_P, _INT, _INT, _INT, _INT, _INT]
     lib.tgemm_plan_gemm.restype = _INT
-    lib.tgemm_plan_gemm.argtypes = ex_args + [_INT, _INT, _INT, _INT, _INT, ctypes.POINTER(_I64)]
+    lib.tgemm_plan_gemm.argtypes = ex_args + [_INT, _INT, _INT, _INT, _INT, _INT, ctypes.POINTER(_I64)]
     lib.tgemm_tune_gemm.restype = _INT
     lib.tgemm_tune_gemm.argtypes = ex_args + [_P, _INT, ctypes.POINTER(_I64)]
     lib.tgemm_tuning_entries.restype = _INT
@@ -88,11 +88,7 @@ def load():
     lib.tgemm_last_hip_error.argtypes = []
     lib.tgemm_plan_f16.restype = _INT
     lib.tgemm_plan_f16.argtypes = [_I64, _I64, _I64, _P, _I64, _P, _I64, _INT, _P, _I64,
-                                   _INT, _INT, _INT, _INT, _INT, ctypes.POINTER(_I64)]
-    lib.tgemm_mfma_issue_probe.restype = _INT
-    lib.tgemm_mfma_issue_probe.argtypes = [_I64, _INT, _P, _I64, _P, _P]
-    lib.tgemm_xcd_probe.restype = _INT
-    lib.tgemm_xcd_probe.argtypes = [_I64, _P, _P]
+                                   _INT, _INT, _INT, _INT, _INT, _INT, ctypes.POINTER(_I64)]
     lib.tgemm_tile_of.restype = _INT
     lib.tgemm_tile_of.argtypes = [_I64, _I64, _INT, _INT, _I64, ctypes.POINTER(_I64), ctypes.POINTER(_I64)]
     _lib = lib
@@ -120,12 +116,12 @@ def tgemm_f16_config(M, N, K, A, lda, B, ldb, b_layout, C, ldc, stream=None,
 
 
 def tgemm_plan_f16(M, N, K, A, lda, B, ldb, b_layout, C, ldc, force_generic=0, group_m=0, num_xcd=0,
-                   k_step=0, stages=0):
-    """Host-only plan query: (status, info dict or None)."""
+                   k_step=0, stages=0, compute_units=0):
+    """Plan query: (status, info dict or None). compute_units=0 asks the current device."""
     info = (_I64 * 10)()
     rc = int(load().tgemm_plan_f16(M, N, K, A, lda, B, ldb, _LAYOUT[b_layout], C, ldc,
                                    int(force_generic), int(group_m), int(num_xcd), int(k_step),
-                                   int(stages), info))
+                                   int(stages), int(compute_units), info))
     if rc != TGEMM_OK:
         return rc, None
     keys = ("variant", "bm", "bn", "bk", "workgroups", "group_m", "num_xcd", "threads", "stages",
@@ -151,12 +147,12 @@ _PLAN_KEYS = ("variant", "bm", "bn", "bk", "workgroups", "group_m", "num_xcd", "
 
 
 def tgemm_plan_gemm(M, N, K, ab_type, A, lda, B, ldb, b_layout, c_type, C, ldc, alpha=1.0, bias=None,
-                    act="none", force_generic=0, group_m=0, num_xcd=0, k_step=0, stages=0):
-    """Host-only plan query of the typed GEMM: (status, info dict or None)."""
+                    act="none", force_generic=0, group_m=0, num_xcd=0, k_step=0, stages=0, compute_units=0):
+    """Plan query of the typed GEMM: (status, info dict or None). compute_units=0 asks the current device."""
     info = (_I64 * 10)()
     rc = int(load().tgemm_plan_gemm(M, N, K, _code(_DTYPE, ab_type), A, lda, B, ldb, _LAYOUT[b_layout], _code(_DTYPE, c_type),
                                     C, ldc, float(alpha), bias, _code(_ACT, act), int(force_generic), int(group_m),
-                                    int(num_xcd), int(k_step), int(stages), info))
+                                    int(num_xcd), int(k_step), int(stages), int(compute_units), info))
     if rc != TGEMM_OK:
         return rc, None
     return rc, dict(zip(_PLAN_KEYS, (int(v) for v in info)))
@@ -191,22 +187,6 @@ def tgemm_tile_of(grid_m, grid_n, group_m, num_xcd, wid):
     if rc != TGEMM_OK:
         raise TgemmError(rc, "tile_of")
     return tm.value, tn.value
-
-
-def mfma_issue_probe(workgroups: int, iters: int, data_ptr: int, data_bytes: int, out_ptr: int,
-                     stream=None) -> None:
-    """Launch the matrix-core ceiling probe (measurement aid; see include/tgemm.h)."""
-    rc = int(load().tgemm_mfma_issue_probe(int(workgroups), int(iters), data_ptr, int(data_bytes), out_ptr,
-                                           stream))
-    if rc != TGEMM_OK:
-        raise TgemmError(rc, "mfma_issue_probe")
-
-
-def xcd_probe(workgroups: int, out_ptr: int, stream=None) -> None:
-    """Launch the die probe (measurement aid; see include/tgemm.h): out[w] = die of workgroup w."""
-    rc = int(load().tgemm_xcd_probe(int(workgroups), out_ptr, stream))
-    if rc != TGEMM_OK:
-        raise TgemmError(rc, "xcd_probe")
 
 
 # ----------------------------------------------------------- torch tensors --

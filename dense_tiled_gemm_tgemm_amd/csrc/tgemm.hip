@@ -61,6 +61,18 @@ static int compute_units() {
     return n;
 }
 
+// The current device's compute units into *ncu: TGEMM_OK, or TGEMM_ERR_HIP
+// (hipError_t kept for tgemm_last_hip_error) when there is no usable device.
+static int device_compute_units(int* ncu) {
+    const int n = compute_units();
+    if (n <= 0) {
+        g_last_hip_error = n < 0 ? -n : (int)hipErrorInvalidDevice;
+        return TGEMM_ERR_HIP;
+    }
+    *ncu = n;
+    return TGEMM_OK;
+}
+
 static bool epilogue_requested(float alpha, const float* bias, int act) {
     return !(alpha == 1.0f) || bias != nullptr || act != TGEMM_ACT_NONE;
 }
@@ -125,17 +137,29 @@ static bool tuned_choice(const Plan& pl, TuneChoice* c) {
     return true;
 }
 
-// Plan and kernel for a call. With every launch choice automatic (all zero)
-// the choice recorded by tgemm_tune_gemm for this problem, if any, is used.
+// Plan and kernel for a call on a device with `ncu` compute units (0: the
+// current device's, queried only once the arguments have passed and there is
+// work to plan). With every launch choice automatic (all zero) the choice
+// recorded by tgemm_tune_gemm for this problem, if any, is used.
 static int plan_gemm(int64_t M, int64_t N, int64_t K, int ab_type, const void* A, int64_t lda, const void* B,
                      int64_t ldb, int b_layout, int c_type, void* C, int64_t ldc, float alpha, const float* bias,
-                     int act, int force_generic, int group_m, int num_xcd, int k_step, int stages, Plan* pl,
-                     const void** fn, bool use_tuned = true) {
+                     int act, int force_generic, int group_m, int num_xcd, int k_step, int stages, int ncu,
+                     Plan* pl, const void** fn, bool use_tuned = true) {
     if (act != TGEMM_ACT_NONE && act != TGEMM_ACT_RELU) return TGEMM_ERR_INVALID;
     const bool epi = epilogue_requested(alpha, bias, act);
     int rc = make_plan(M, N, K, A, lda, B, ldb, b_layout, C, ldc, force_generic, group_m, num_xcd, k_step, stages,
                        pl, ab_type, c_type, bias, epi);
     if (rc != TGEMM_OK) return rc;
+    if (pl->M == 0 || pl->N == 0) {              // nothing to launch
+        *fn = nullptr;
+        pl->grid = 0;
+        return TGEMM_OK;
+    }
+    if (!pick_kernel(*pl)) return TGEMM_ERR_UNSUPPORTED;   // before any device query
+    if (ncu == 0) {
+        rc = device_compute_units(&ncu);
+        if (rc != TGEMM_OK) return rc;
+    }
     TuneChoice t;
     const bool automatic = !force_generic && !group_m && !num_xcd && !k_step && !stages;
     if (automatic && use_tuned && tuned_choice(*pl, &t)) {
@@ -144,15 +168,14 @@ static int plan_gemm(int64_t M, int64_t N, int64_t K, int ab_type, const void* A
                        &tp, ab_type, c_type, bias, epi);
         if (rc == TGEMM_OK) *pl = tp;
     } else if (automatic && (pl->variant & kDma) && !(pl->variant & kLayoutNxK) && ab_type != TGEMM_F32 &&
-               K > 64 && K % 64 != 0) {
-        const int ncu = compute_units();
-        if (ncu > 0 && pl->W <= ncu) {
-            Plan rp;
-            rc = make_plan(M, N, K, A, lda, B, ldb, b_layout, C, ldc, 0, 0, 0, kPartialKxNKStep, 0, &rp,
-                           ab_type, c_type, bias, epi);
-            if (rc == TGEMM_OK) *pl = rp;
-        }
+               K > 64 && K % 64 != 0 && pl->W <= ncu) {
+        Plan rp;
+        rc = make_plan(M, N, K, A, lda, B, ldb, b_layout, C, ldc, 0, 0, 0, kPartialKxNKStep, 0, &rp, ab_type,
+                       c_type, bias, epi);
+        if (rc == TGEMM_OK) *pl = rp;
     }
+    // one workgroup per compute unit, each walking several tiles
+    if (persistent(*pl) && ncu < pl->W) pl->grid = ncu;
     *fn = pick_kernel(*pl);
     return *fn ? TGEMM_OK : TGEMM_ERR_UNSUPPORTED;
 }
@@ -179,21 +202,12 @@ static int launch(const Plan& pl, const void* fn, const void* A, const void* B, 
     args.W = pl.W;
     args.group_m = pl.group_m;
     args.num_xcd = pl.num_xcd;
-    args.grid = pl.W;
+    args.grid = pl.grid;
     // 16-byte C stores: rows 16-byte aligned, and every byte offset inside a
     // wave's 128 rows below 2^31 (they go through a 32-bit buffer offset)
     args.c16 = ((uintptr_t)C % 16 == 0) && ((pl.ldc * c_size) % 16 == 0) &&
                (127 * pl.ldc + (int64_t)pl.N) * c_size + 16 < (int64_t(1) << 31);
     args.c8 = (pl.variant & kVecC) != 0;
-    if (persistent(pl)) {
-        // one workgroup per compute unit, each walking several tiles
-        const int ncu = compute_units();
-        if (ncu < 0) {
-            g_last_hip_error = -ncu;
-            return TGEMM_ERR_HIP;
-        }
-        if (ncu > 0 && ncu < pl.W) args.grid = ncu;
-    }
     void* kargs[] = {&args};
     const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)args.grid), dim3(NTHREADS), kargs, 0,
                                          static_cast<hipStream_t>(stream));
@@ -213,7 +227,7 @@ extern "C" int tgemm_gemm_config(int64_t M, int64_t N, int64_t K, int ab_type, c
     tg::Plan pl;
     const void* fn = nullptr;
     const int rc = tg::plan_gemm(M, N, K, ab_type, A, lda, B, ldb, b_layout, c_type, C, ldc, alpha, bias, act,
-                                 force_generic, group_m, num_xcd, k_step, stages, &pl, &fn);
+                                 force_generic, group_m, num_xcd, k_step, stages, 0, &pl, &fn);
     if (rc != TGEMM_OK) return rc;
     if (pl.M == 0 || pl.N == 0) return TGEMM_OK;
     return tg::launch(pl, fn, A, B, C, c_type, alpha, bias, act, stream);
@@ -246,11 +260,14 @@ extern "C" int tgemm_tune_gemm(int64_t M, int64_t N, int64_t K, int ab_type, con
     tg::Plan base;
     const void* fn = nullptr;
     int rc = tg::plan_gemm(M, N, K, ab_type, A, lda, B, ldb, b_layout, c_type, C, ldc, alpha, bias, act, 0, 0, 0, 0,
-                           0, &base, &fn, false);
+                           0, 0, &base, &fn, false);
     if (rc != TGEMM_OK) return rc;
     if (info)
         for (int i = 0; i < 6; ++i) info[i] = 0;
     if (base.M == 0 || base.N == 0) return TGEMM_OK;
+    int ncu = 0;
+    rc = tg::device_compute_units(&ncu);
+    if (rc != TGEMM_OK) return rc;
 
     // candidates: K step x ring depth (direct-to-LDS path only) x raster group height
     struct Cand {
@@ -269,7 +286,7 @@ extern "C" int tgemm_tune_gemm(int64_t M, int64_t N, int64_t K, int ab_type, con
             Cand cd;
             cd.c = tg::TuneChoice{ks, st, g, tg::kDefaultNumXcd};
             if (tg::plan_gemm(M, N, K, ab_type, A, lda, B, ldb, b_layout, c_type, C, ldc, alpha, bias, act, 0, g,
-                              tg::kDefaultNumXcd, ks, st, &cd.pl, &cd.fn, false) != TGEMM_OK)
+                              tg::kDefaultNumXcd, ks, st, ncu, &cd.pl, &cd.fn, false) != TGEMM_OK)
                 continue;                                   // not built for these types, or invalid for this K
             bool dup = false;                               // group heights clamp to the tile rows
             for (const Cand& o : cands)
@@ -389,7 +406,7 @@ static void fill_info(const tg::Plan& pl, int64_t* info) {
     info[1] = tg::BM;
     info[2] = pl.bn;
     info[3] = pl.k_step;
-    info[4] = (pl.M == 0 || pl.N == 0) ? 0 : pl.W;
+    info[4] = (pl.M == 0 || pl.N == 0) ? 0 : pl.grid;
     info[5] = pl.group_m;
     info[6] = pl.num_xcd;
     info[7] = tg::NTHREADS;
@@ -401,12 +418,12 @@ static void fill_info(const tg::Plan& pl, int64_t* info) {
 extern "C" int tgemm_plan_gemm(int64_t M, int64_t N, int64_t K, int ab_type, const void* A, int64_t lda,
                                const void* B, int64_t ldb, int b_layout, int c_type, void* C, int64_t ldc,
                                float alpha, const float* bias, int act, int force_generic, int group_m,
-                               int num_xcd, int k_step, int stages, int64_t* info) {
-    if (!info) return TGEMM_ERR_INVALID;
+                               int num_xcd, int k_step, int stages, int compute_units, int64_t* info) {
+    if (!info || compute_units < 0 || compute_units > 65536) return TGEMM_ERR_INVALID;
     tg::Plan pl;
     const void* fn = nullptr;
     const int rc = tg::plan_gemm(M, N, K, ab_type, A, lda, B, ldb, b_layout, c_type, C, ldc, alpha, bias, act,
-                                 force_generic, group_m, num_xcd, k_step, stages, &pl, &fn);
+                                 force_generic, group_m, num_xcd, k_step, stages, compute_units, &pl, &fn);
     if (rc != TGEMM_OK) return rc;
     fill_info(pl, info);
     return TGEMM_OK;
@@ -414,9 +431,10 @@ extern "C" int tgemm_plan_gemm(int64_t M, int64_t N, int64_t K, int ab_type, con
 
 extern "C" int tgemm_plan_f16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
                               int64_t ldb, int b_layout, void* C, int64_t ldc, int force_generic,
-                              int group_m, int num_xcd, int k_step, int stages, int64_t* info) {
+                              int group_m, int num_xcd, int k_step, int stages, int compute_units,
+                              int64_t* info) {
     return tgemm_plan_gemm(M, N, K, TGEMM_F16, A, lda, B, ldb, b_layout, TGEMM_F16, C, ldc, 1.0f, nullptr,
-                           TGEMM_ACT_NONE, force_generic, group_m, num_xcd, k_step, stages, info);
+                           TGEMM_ACT_NONE, force_generic, group_m, num_xcd, k_step, stages, compute_units, info);
 }
 
 extern "C" int tgemm_tile_of(int64_t grid_m, int64_t grid_n, int group_m, int num_xcd, int64_t wid,

@@ -234,14 +234,28 @@ const char* tgemm_status_string(int status);
 int tgemm_last_hip_error(void);
 
 /*
- * Host-only planning query (no GPU call): the launch tgemm_f16_config would
- * make for these arguments. Returns TGEMM_OK and fills info[0..9]:
+ * Planning query: the launch tgemm_f16_config would make for these
+ * arguments on a device with `compute_units` compute units (256 on MI355X).
+ * The plan depends on that count in two places: a launch of 64-deep steps
+ * with more tiles than compute units runs one workgroup per compute unit,
+ * and the automatic 32-deep rule for B stored K x N applies to grids of at
+ * most one tile per compute unit.
+ *   compute_units: 1..65536, or 0 for the current device's count, read with
+ *                  one HIP attribute query once the arguments have passed
+ *                  (TGEMM_ERR_HIP when there is no device). With a count
+ *                  given, the query makes no HIP call at all (unless a
+ *                  tuned choice is recorded, whose key names the current
+ *                  device).
+ * Returns TGEMM_OK and fills info[0..9]:
  *   info[0] variant bits: bit0 128-bit A/B loads, bit1 vector C stores
  *           (64-bit runs of a 16-bit C, 128-bit runs of an fp32 C), bit2 B
  *           layout is NxK, bit3 the pipelined kernel (16-bit operands:
  *           streamed directly into LDS; binary32 operands: buffer loads)
  *   info[1] tile rows (BM)   info[2] tile columns (BN)   info[3] K step
- *   info[4] workgroups launched  info[5] group_m  info[6] num_xcd
+ *   info[4] workgroups launched (the tile count ceil(M/BM) * ceil(N/BN), or
+ *           compute_units when each workgroup walks several tiles; 0 when
+ *           M or N is 0)
+ *   info[5] group_m  info[6] num_xcd
  *   info[7] threads per workgroup  info[8] LDS stages  info[9] LDS bytes
  * or the same error tgemm_f16_config would return. `info` must hold 10 values.
  */
@@ -250,13 +264,14 @@ int tgemm_plan_f16(int64_t M, int64_t N, int64_t K,
                    const void* B, int64_t ldb, int b_layout,
                    void* C, int64_t ldc,
                    int force_generic, int group_m, int num_xcd,
-                   int k_step, int stages,
+                   int k_step, int stages, int compute_units,
                    int64_t* info);
 
 /*
- * Host-only planning query for tgemm_gemm_config: the same info[0..9] as
- * tgemm_plan_f16, or the error tgemm_gemm_config would return (including
- * TGEMM_ERR_UNSUPPORTED for a ring depth that is not built for the types).
+ * Planning query for tgemm_gemm_config: the same compute_units and
+ * info[0..9] as tgemm_plan_f16, or the error tgemm_gemm_config would return
+ * (including TGEMM_ERR_UNSUPPORTED for a ring depth that is not built for
+ * the types).
  */
 int tgemm_plan_gemm(int64_t M, int64_t N, int64_t K,
                     int ab_type, const void* A, int64_t lda,
@@ -264,7 +279,7 @@ int tgemm_plan_gemm(int64_t M, int64_t N, int64_t K,
                     int c_type, void* C, int64_t ldc,
                     float alpha, const float* bias, int act,
                     int force_generic, int group_m, int num_xcd,
-                    int k_step, int stages,
+                    int k_step, int stages, int compute_units,
                     int64_t* info);
 
 /*
@@ -275,35 +290,6 @@ int tgemm_plan_gemm(int64_t M, int64_t N, int64_t K,
  */
 int tgemm_tile_of(int64_t grid_m, int64_t grid_n, int group_m, int num_xcd,
                   int64_t wid, int64_t* tile_m, int64_t* tile_n);
-
-/*
- * Measurement aid (not part of the product operation): launches `workgroups`
- * workgroups of 256 threads that run the GEMM kernel's instruction stream
- * without its synchronization, tile changes or C stores: per wave, `iters`
- * rounds of two slices of 64 independent 16x16x32 fp16 MFMAs, with 16
- * 128-bit LDS fragment reads and 8 direct-to-LDS 16-byte loads per slice
- * (operands drawn from `data`). MI355X is power-limited under MFMA load and
- * the operands' switching activity sets the clock, so with the benchmark's
- * inputs as `data` its TFLOP/s is the ceiling the GEMM's instruction mix
- * reaches on this board. `data`: device memory, 16-byte aligned, data_bytes
- * a power of two in [1 MiB, 1 GiB]; `out` must hold workgroups * 256 floats
- * of device memory. Returns TGEMM_OK, TGEMM_ERR_INVALID (bad sizes or
- * pointers) or TGEMM_ERR_HIP.
- */
-int tgemm_mfma_issue_probe(int64_t workgroups, int iters, const void* data, int64_t data_bytes,
-                           float* out, void* stream);
-
-/*
- * Measurement aid (not part of the product operation): launches `workgroups`
- * workgroups of 64 threads; workgroup w writes to out[w] the number (0-15)
- * of the accelerator die (XCD) it ran on, read from the XCC_ID hardware
- * register. The die-aware renumbering in tgemm_tile_of assumes that the
- * workgroups sharing a die are those with equal w mod num_xcd (page 1,
- * section "Swizzle", gives the grouped order this renumbering feeds). `out`: device memory for
- * `workgroups` ints. Returns TGEMM_OK, TGEMM_ERR_INVALID (workgroups outside
- * [1, 2^20] or a null `out`) or TGEMM_ERR_HIP.
- */
-int tgemm_xcd_probe(int64_t workgroups, int* out, void* stream);
 
 #ifdef __cplusplus
 }

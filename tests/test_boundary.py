@@ -16,8 +16,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PA, PB, PC = 1 << 40, 2 << 40, 3 << 40
 
 
-def _declared_functions():
-    src = open(os.path.join(ROOT, "include", "tgemm.h")).read()
+def _declared_functions(header="tgemm.h"):
+    src = open(os.path.join(ROOT, "include", header)).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(tgemm_\w+)\s*\(", src, flags=re.M)))
 
@@ -31,6 +31,22 @@ def test_library_loads_and_exports_every_declared_symbol():
         assert ctypes.cast(getattr(lib, n), ctypes.c_void_p).value
 
 
+def test_measurement_library_is_separate():
+    """The probes live in libtgemm_probe.so (include/tgemm_probe.h), which
+    exports what its header declares; the GEMM library exports none of them."""
+    from dense_tiled_gemm_tgemm_amd import probe
+    plib = probe.load()
+    names = _declared_functions("tgemm_probe.h")
+    assert set(names) == {"tgemm_mfma_issue_probe", "tgemm_xcd_probe"}
+    lib = tg.load()
+    for n in names:
+        assert ctypes.cast(getattr(plib, n), ctypes.c_void_p).value
+        assert not hasattr(lib, n), n
+    # bad sizes are refused before any launch
+    assert plib.tgemm_mfma_issue_probe(0, 4, PA, 1 << 20, PC, None, None) == tg.TGEMM_ERR_INVALID
+    assert plib.tgemm_xcd_probe(0, PC, None) == tg.TGEMM_ERR_INVALID
+
+
 def test_status_strings():
     assert tg.status_string(tg.TGEMM_OK) == "ok"
     assert tg.status_string(tg.TGEMM_ERR_INVALID) == "invalid argument"
@@ -42,6 +58,7 @@ def _plan(M, N, K, A=PA, lda=None, B=PB, ldb=None, lay="KxN", C=PC, ldc=None, **
     lda = K if lda is None else lda
     ldb = (N if lay == "KxN" else K) if ldb is None else ldb
     ldc = N if ldc is None else ldc
+    kw.setdefault("compute_units", 256)          # MI355X; no device query on this host
     return tg.tgemm_plan_f16(M, N, K, A, lda, B, ldb, lay, C, ldc, **kw)
 
 
@@ -91,7 +108,7 @@ def test_bad_layout_rejected():
     lib = tg.load()
     assert lib.tgemm_f16(4, 4, 4, PA, 4, PB, 4, 2, PC, 4, None) == tg.TGEMM_ERR_INVALID
     info = (ctypes.c_int64 * 10)()
-    assert lib.tgemm_plan_f16(4, 4, 4, PA, 4, PB, 4, -1, PC, 4, 0, 0, 0, 0, 0, info) == tg.TGEMM_ERR_INVALID
+    assert lib.tgemm_plan_f16(4, 4, 4, PA, 4, PB, 4, -1, PC, 4, 0, 0, 0, 0, 0, 256, info) == tg.TGEMM_ERR_INVALID
 
 
 def test_empty_outputs_are_noops_without_gpu():
@@ -108,7 +125,16 @@ def test_plan_variants_and_grid():
     rc, info = _plan(8192, 8192, 8192, lay="NxK")
     assert rc == 0
     assert info["variant"] == V | C8 | NXK | DMA
-    assert info["workgroups"] == 32 * 32 and info["group_m"] == 4 and info["num_xcd"] == 8
+    # 1024 tiles on 256 compute units: one persistent workgroup per unit
+    assert info["workgroups"] == 256 and info["group_m"] == 4 and info["num_xcd"] == 8
+    rc, info = _plan(8192, 8192, 8192, lay="NxK", compute_units=304)
+    assert info["workgroups"] == 304
+    rc, info = _plan(8192, 8192, 8192, lay="NxK", compute_units=2048)
+    assert info["workgroups"] == 1024                  # fewer tiles than units: one workgroup per tile
+    # 32-deep steps are not persistent: one workgroup per tile
+    rc, info = _plan(8192, 8192, 8192, lay="NxK", k_step=32)
+    assert info["workgroups"] == 1024
+    rc, info = _plan(8192, 8192, 8192, lay="NxK")
     assert (info["bm"], info["bn"], info["threads"]) == (256, 256, 256)
     assert (info["bk"], info["stages"], info["lds_bytes"]) == (64, 2, 128 * 1024)
     rc, info = _plan(8192, 8192, 8192, lay="NxK", k_step=32)
@@ -136,12 +162,22 @@ def test_plan_variants_and_grid():
     assert rc == 0 and (info["bk"], info["stages"], info["lds_bytes"]) == (64, 2, 128 * 1024)
     rc, info = _plan(4096, 4096, 4099, lda=4104)
     assert info["variant"] == V | C8 | DMA    # K % 8 != 0 is fine: the straddling chunk is cleared
-    # strides past the 32-bit panel-offset limit: register-staged path
+    # strides past the 32-bit panel-offset limit: register-staged path (128-bit loads when aligned)
     rc, info = _plan(512, 512, 512, lay="NxK", lda=4_000_008)
     assert info["variant"] == V | C8 | NXK
-    rc, info = _plan(512, 512, 512, ldb=(1 << 30) // (512 + 64))
-    assert not info["variant"] & DMA
-    rc, info = _plan(512, 512, 512, ldb=((1 << 30) - 512) // (512 + 64) - 1)
+    rc, info = _plan(512, 512, 512, lay="NxK", ldb=4_000_008)
+    assert info["variant"] == V | C8 | NXK
+    rc, info = _plan(512, 512, 512, ldb=4_000_008)
+    assert info["variant"] == V | C8
+    rc, info = _plan(512, 512, 512, lay="NxK", ldb=4_000_000)
+    assert info["variant"] == V | C8 | NXK | DMA
+    # B stored K x N is rebased at every K step: its limit is the row stride alone,
+    # whatever K is (a vocabulary-sized projection, 2.5 GB of B, streams into LDS)
+    rc, info = _plan(8192, 152064, 8192)
+    assert info["variant"] == V | C8 | DMA and (info["bk"], info["workgroups"]) == (64, 256)
+    rc, info = _plan(512, 512, 1000, ldb=1_100_000)
+    assert info["variant"] & DMA
+    rc, info = _plan(512, 512, 512, ldb=4_000_000)
     assert info["variant"] & DMA
     # K <= 64 streams 32-deep steps; K == 0 (zeros only) takes the register-staged kernel
     rc, info = _plan(512, 512, 64, lay="NxK")
@@ -151,6 +187,46 @@ def test_plan_variants_and_grid():
     # group_m larger than the tile rows is clamped (same map)
     rc, info = _plan(512, 4096, 64, group_m=100)
     assert info["group_m"] == 2
+
+
+def test_kxn_one_round_rule_follows_the_compute_unit_count():
+    """Automatic launches with B stored K x N, K > 64 not a multiple of 64 and at
+    most one tile per compute unit take 32-deep steps (default ring depth); more
+    tiles than units, K a multiple of 64, or B stored N x K keep the persistent
+    64-deep ring. The count is an argument of the query, so the rule is checked
+    here without a device."""
+    rc, info = _plan(3001, 5003, 4099)                              # 240 tiles
+    assert rc == 0 and (info["bk"], info["stages"], info["workgroups"]) == (32, 4, 240)
+    rc, info = _plan(3001, 5003, 4099, compute_units=240)
+    assert (info["bk"], info["stages"], info["workgroups"]) == (32, 4, 240)
+    rc, info = _plan(3001, 5003, 4099, compute_units=239)            # one tile more than units
+    assert (info["bk"], info["stages"], info["workgroups"]) == (64, 2, 239)
+    rc, info = _plan(3001, 5003, 4096)                              # K a multiple of 64
+    assert (info["bk"], info["stages"], info["workgroups"]) == (64, 2, 240)
+    rc, info = _plan(3001, 5003, 4099, lay="NxK")                   # B stored N x K
+    assert (info["bk"], info["stages"]) == (64, 2)
+    rc, info = _plan(3001, 5003, 4099, k_step=64)                   # an explicit choice wins
+    assert (info["bk"], info["stages"]) == (64, 2)
+    for ab in ("f16", "bf16"):
+        rc, info = _plan_ex(3001, 5003, 4099, ab=ab, ct="f32", alpha=0.5)
+        assert rc == 0 and (info["bk"], info["stages"]) == (32, 4)
+
+
+def test_plan_query_device_count_needs_a_device():
+    """compute_units = 0 asks the current device; on a host without one the
+    query reports a HIP error once the arguments have passed (argument errors
+    and empty outputs need no device). Negative counts are invalid."""
+    rc, _ = _plan(300, 300, 300, compute_units=0)
+    assert rc in (tg.TGEMM_OK, tg.TGEMM_ERR_HIP)
+    import torch
+    if not torch.cuda.is_available():
+        assert rc == tg.TGEMM_ERR_HIP
+    rc, info = _plan(0, 300, 300, compute_units=0)
+    assert rc == tg.TGEMM_OK and info["workgroups"] == 0
+    rc, _ = _plan(300, 300, 300, lda=5, compute_units=0)
+    assert rc == tg.TGEMM_ERR_INVALID
+    rc, _ = _plan(300, 300, 300, compute_units=-1)
+    assert rc == tg.TGEMM_ERR_INVALID
 
 
 def test_raster_matches_page1_swizzle_without_die_remap():
@@ -205,6 +281,7 @@ def _plan_ex(M, N, K, ab="f16", ct="f16", A=PA, lda=None, B=PB, ldb=None, lay="K
     lda = K if lda is None else lda
     ldb = (N if lay == "KxN" else K) if ldb is None else ldb
     ldc = N if ldc is None else ldc
+    kw.setdefault("compute_units", 256)          # MI355X; no device query on this host
     return tg.tgemm_plan_gemm(M, N, K, ab, A, lda, B, ldb, lay, ct, C, ldc, alpha, bias, act, **kw)
 
 
