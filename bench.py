@@ -9,6 +9,10 @@ Prints ONE JSON line (rank 0):
              achieved = 2*M*N*K / mean per-launch time (HIP events recorded
              on the launch stream between consecutive launches)
   launch_ms  mean, median, min and p90 of the per-launch times
+  roofline.ceiling  the matrix-core ceiling probe in the same process (the
+             GEMM's instruction stream without synchronization, tile changes or
+             C stores, on the workload's A values, and on zeros) with its
+             average clock; roofline.frac_of_ceiling = achieved / ceiling
   cold_cache variant B: up to 50 launches, each after a 512 MiB write that
              evicts the L2s and the Infinity Cache (events around the GEMM only)
   cpu_baseline  the CPU oracle (fp64, all OpenMP threads) timed on a bounded
@@ -132,6 +136,107 @@ def cpu_model() -> str:
     return "unknown"
 
 
+def _read_csv(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _short(name: str) -> str:
+    """Kernel name without its argument list ("void tg::k<...>(tg::Args)" -> "tg::k<...>")."""
+    name = name.strip()
+    if name.startswith("void "):
+        name = name[5:]
+    return name.split("(")[0]
+
+
+def trace_summary(csv_path: str, bench_json: str) -> str:
+    """Markdown summary of a rocprofv3 kernel trace of one bench.py run: the
+    GEMM dispatches of the timed region only (after the run's warm-up
+    launches, as many as its timed steps), against the run's own JSON line."""
+    import numpy as np
+
+    with open(bench_json) as f:
+        rec = json.loads([l for l in f.read().splitlines() if l.startswith("{")][-1])
+    rows = _read_csv(csv_path)
+    if not rows or "Kernel_Name" not in rows[0]:
+        raise SystemExit(f"{csv_path}: not a rocprofv3 kernel trace")
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    by = {}
+    for r in rows:
+        by.setdefault(_short(r["Kernel_Name"]), []).append(r)
+    gemm = max((k for k in by if "tgemm_" in k and "probe" not in k and "ceiling" not in k),
+               key=lambda k: len(by[k]))
+    d = by[gemm]
+    n_warm, steps = rec["warmup_launches"], rec["steps"]
+    timed = d[n_warm:n_warm + steps]
+    if len(timed) != steps:
+        raise SystemExit(f"{len(d)} dispatches of {gemm}, expected at least {n_warm} + {steps}")
+    dur = np.array([(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6 for r in timed])   # ms
+    flops = 2.0 * rec["config"]["M"] * rec["config"]["N"] * rec["config"]["K"]
+    peak = rec["roofline"]["peak"]
+    mean, med = float(dur.mean()), float(np.median(dur))
+    lines = [f"| kernel | dispatches in trace | timed dispatches | mean ms | median ms | min ms | p90 ms |",
+             "|---|---|---|---|---|---|---|",
+             f"| {gemm} | {len(d)} | {len(timed)} (#{n_warm}..#{n_warm + steps - 1}) | {mean:.5f} | {med:.5f} | "
+             f"{dur.min():.5f} | {np.percentile(dur, 90):.5f} |", "",
+             f"2MNK / mean = {flops / mean / 1e9:.1f} TFLOP/s = {flops / mean / 1e9 / peak:.4f} of {peak}; "
+             f"2MNK / median = {flops / med / 1e9:.1f} TFLOP/s = {flops / med / 1e9 / peak:.4f}.",
+             f"Same run's JSON line: value {rec['value']} TFLOP/s, ms_per_step {rec['ms_per_step']}, "
+             f"roofline.frac {rec['roofline']['frac']} (HIP events between consecutive launches, so "
+             f"the dispatch time is at most the per-step time: {mean:.5f} <= {rec['ms_per_step']})."]
+    ceil = rec["roofline"].get("ceiling")
+    if ceil:
+        lines.append(f"Matrix-core ceiling probe, same process: {ceil['tflops']} TFLOP/s at "
+                     f"{ceil['clock_ghz']} GHz (zero operands {ceil['tflops_zero_operands']} at "
+                     f"{ceil['clock_ghz_zero_operands']} GHz); GEMM (trace mean) at "
+                     f"{flops / mean / 1e9 / ceil['tflops']:.3f} of it.")
+    return "\n".join(lines)
+
+
+def counter_summary(csv_paths) -> str:
+    """Markdown table of rocprofv3 --pmc runs (counter_collection CSVs): per
+    kernel, the median over its dispatches of each counter, with the derived
+    clock (GRBM_GUI_ACTIVE per die over the dispatch duration) and matrix-core
+    occupancy (SQ_VALU_MFMA_BUSY_CYCLES over 1024 SIMDs x active cycles per die)."""
+    import numpy as np
+
+    per = {}      # (kernel, dispatch) -> {counter: value, "_ns": duration}
+    for path in csv_paths:
+        for r in _read_csv(path):
+            key = (_short(r["Kernel_Name"]), path, r["Dispatch_Id"])
+            d = per.setdefault(key, {})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            if "Start_Timestamp" in r and "End_Timestamp" in r:
+                d["_ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    kern = {}
+    for (k, _, _), d in per.items():
+        kern.setdefault(k, []).append(d)
+    out = []
+    for k, ds in sorted(kern.items(), key=lambda kv: -len(kv[1])):
+        if "tgemm_" not in k and "copyBuffer" not in k and "Cijk" not in k:
+            continue
+        names = sorted({c for d in ds for c in d if not c.startswith("_")})
+        med = {c: float(np.median([d[c] for d in ds if c in d])) for c in names}
+        row = [f"{c} {med[c]:,.0f}" for c in names]
+        if "GRBM_GUI_ACTIVE" in med:
+            clk = [d["GRBM_GUI_ACTIVE"] / 8 / d["_ns"] for d in ds if "_ns" in d and d["_ns"] > 0
+                   and "GRBM_GUI_ACTIVE" in d]
+            if clk:
+                row.append(f"clock {np.median(clk):.3f} GHz")
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in med:
+                occ = [d["SQ_VALU_MFMA_BUSY_CYCLES"] / (d["GRBM_GUI_ACTIVE"] / 8 * 1024) for d in ds
+                       if "SQ_VALU_MFMA_BUSY_CYCLES" in d and "GRBM_GUI_ACTIVE" in d]
+                row.append(f"MFMA occupancy {100 * np.median(occ):.1f}%")
+        if "SQ_WAIT_ANY" in med and "SQ_WAVE_CYCLES" in med:
+            row.append(f"waiting {100 * med['SQ_WAIT_ANY'] / med['SQ_WAVE_CYCLES']:.1f}% of wave-cycles")
+        if "SQ_LDS_BANK_CONFLICT" in med and "SQ_LDS_IDX_ACTIVE" in med:
+            row.append(f"LDS conflict cycles {100 * med['SQ_LDS_BANK_CONFLICT'] / max(med['SQ_LDS_IDX_ACTIVE'], 1):.2f}% "
+                       f"of LDS active cycles")
+        out.append(f"| {k} | {len(ds)} | " + "; ".join(row) + " |")
+    return "\n".join(["| kernel | dispatches | medians per dispatch |", "|---|---|---|"] + out)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -152,6 +257,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold-cache launches (512 MiB written before each) reported beside the headline")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the matrix-core ceiling probe reported in roofline.ceiling")
     ap.add_argument("--mfma-ceiling", action="store_true",
                     help="instead of the GEMM, time the matrix-core ceiling probe (the GEMM's "
                          "instruction stream on the workload's values, without synchronization, "
@@ -162,7 +269,20 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the GEMM, run device-to-device copies of MIB MiB; used to "
                          "scale the HBM byte counters (FETCH_SIZE / WRITE_SIZE) of a profiler run")
+    ap.add_argument("--trace-summary", metavar="CSV",
+                    help="print a markdown summary of a rocprofv3 kernel trace of a bench.py run (its timed "
+                         "dispatches only) and exit; needs --bench-json")
+    ap.add_argument("--bench-json", metavar="FILE", help="the JSON line printed by the traced run")
+    ap.add_argument("--counter-summary", metavar="CSV", nargs="+",
+                    help="print a markdown table of rocprofv3 --pmc counter CSVs and exit")
     args = ap.parse_args()
+
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary, args.bench_json))
+        return
+    if args.counter_summary:
+        print(counter_summary(args.counter_summary))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -202,39 +322,49 @@ def main():
             torch.cuda.synchronize()
         return n, time.perf_counter() - t_w
 
-    if args.mfma_ceiling:
-        # the GEMM's instruction stream without synchronization, tile changes or
-        # C stores, on the workload's own A values (the operands' switching
-        # activity sets the power-limited clock)
-        tg.load()
-        name = args.workload or inputs.HEADLINE
-        w = inputs.WORKLOADS[name]
-        A, _ = inputs.make_inputs(w)
-        nbytes = 1 << min(26, int(A.nbytes).bit_length() - 1)
-        data = torch.from_numpy(A.reshape(-1)[: nbytes // 2].copy()).to("cuda:0")
+    def mfma_ceiling(A16, name, steps):
+        """The matrix-core ceiling probe (libtgemm_probe.so): the GEMM's
+        instruction stream without synchronization, tile changes or C stores,
+        on the workload's own A values (the operands' switching activity sets
+        the power-limited clock), and on zeros (the same instructions with
+        operands that never toggle). TFLOP/s and the probe's average clock."""
+        from dense_tiled_gemm_tgemm_amd import probe
+        probe.load()
+        a16 = np.ascontiguousarray(A16).view(np.uint16).reshape(-1)
+        nbytes = 1 << min(26, int(a16.nbytes).bit_length() - 1)
+        data = torch.from_numpy(a16[: nbytes // 2].view(np.int16).copy()).to("cuda:0")
         stream = torch.cuda.current_stream()
         wg, iters = 256, 400
         out = torch.empty(wg * 256, dtype=torch.float32, device="cuda:0")
+        clk = torch.zeros(2 * wg, dtype=torch.int64, device="cuda:0")
         flops = wg * 4 * iters * 128 * 2.0 * 16 * 16 * 32
 
         def probe_ms(buf):
-            warm_up(lambda: tg.mfma_issue_probe(wg, iters, buf.data_ptr(), nbytes, out.data_ptr(),
-                                                stream.cuda_stream))
+            def one(c=None):
+                probe.mfma_issue_probe(wg, iters, buf.data_ptr(), nbytes, out.data_ptr(), c, stream.cuda_stream)
+            warm_up(one)
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
             ev[0].record(stream)
-            for _ in range(args.steps):
-                tg.mfma_issue_probe(wg, iters, buf.data_ptr(), nbytes, out.data_ptr(), stream.cuda_stream)
+            for _ in range(steps):
+                one()
             ev[1].record(stream)
+            one(clk.data_ptr())                       # one more launch records the clock
             torch.cuda.synchronize()
-            return ev[0].elapsed_time(ev[1]) / args.steps
+            c = clk.cpu().numpy().reshape(wg, 2).astype(np.float64)
+            return ev[0].elapsed_time(ev[1]) / steps, float(c[:, 0].sum() / c[:, 1].sum() / 10.0)
 
-        ms = probe_ms(data)
-        ms0 = probe_ms(torch.zeros_like(data))      # same instructions, operands that never toggle
-        print(json.dumps({"probe": "mfma_ceiling", "data": f"{name} A, first {nbytes >> 20} MiB",
-                          "workgroups": wg, "iters": iters, "ms": round(ms, 5),
-                          "tflops": round(flops / ms / 1e9, 1),
-                          "tflops_zero_operands": round(flops / ms0 / 1e9, 1),
-                          "peak": PEAK_F16_TFLOPS}), flush=True)
+        ms, ghz = probe_ms(data)
+        ms0, ghz0 = probe_ms(torch.zeros_like(data))
+        return {"data": f"{name} A, first {nbytes >> 20} MiB", "workgroups": wg, "iters": iters,
+                "ms": round(ms, 5), "tflops": round(flops / ms / 1e9, 1), "clock_ghz": round(ghz, 3),
+                "tflops_zero_operands": round(flops / ms0 / 1e9, 1), "clock_ghz_zero_operands": round(ghz0, 3)}
+
+    if args.mfma_ceiling:
+        tg.load()
+        name = args.workload or inputs.HEADLINE
+        A, _ = inputs.make_inputs(inputs.WORKLOADS[name])
+        rec = {"probe": "mfma_ceiling", **mfma_ceiling(A, name, args.steps), "peak": PEAK_F16_TFLOPS}
+        print(json.dumps(rec), flush=True)
         return
 
     name = args.workload or inputs.HEADLINE
@@ -360,6 +490,15 @@ def main():
         log(f"bench: cold-cache launches (512 MiB written before each): median {cs['median']:.4f} ms, "
             f"{cold['tflops_at_median']:.1f} TFLOP/s")
 
+    ceiling = None
+    if not args.no_ceiling and args.ab == "f16":       # the probe runs binary16 MFMAs
+        # same process, same board, after the timed region: the matrix-core
+        # ceiling of this instruction mix on the workload's values
+        ceiling = mfma_ceiling(A, name, min(args.steps, 100))
+        log(f"bench: ceiling probe {ceiling['tflops']} TFLOP/s at {ceiling['clock_ghz']} GHz "
+            f"(zero operands {ceiling['tflops_zero_operands']} at {ceiling['clock_ghz_zero_operands']} GHz); "
+            f"GEMM at {achieved / ceiling['tflops']:.3f} of it")
+
     metric = METRIC if (tag == "" and name == inputs.HEADLINE) else (
         f"GEMM TFLOPS (2MNK/s) at {w.M}x{w.N}x{w.K}, {args.ab} in, {args.out} out"
         f"{', alpha/bias/relu epilogue' if args.epilogue else ''} on 1 MI355X")
@@ -392,6 +531,9 @@ def main():
             "traffic": traffic_from_profiles(name, tag),
         },
     }
+    if ceiling is not None:
+        rec["roofline"]["ceiling"] = ceiling
+        rec["roofline"]["frac_of_ceiling"] = round(achieved / ceiling["tflops"], 4)
     if cold is not None:
         rec["cold_cache"] = cold
     if not args.no_cpu_baseline:

@@ -23,8 +23,6 @@ from ._binding import (  # noqa: F401
     last_hip_error,
     gemm,
     load,
-    mfma_issue_probe,
-    xcd_probe,
     mm,
     status_string,
     tgemm_f16,

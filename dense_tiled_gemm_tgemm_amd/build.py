@@ -1,11 +1,13 @@
 """Compile the HIP library for gfx950 in-tree.
 
 ``python -m dense_tiled_gemm_tgemm_amd.build`` writes
-``dense_tiled_gemm_tgemm_amd/libtgemm.so``. The kernels of each (input type,
-output type, epilogue) combination are instantiated by ``tgemm_inst.hip`` in
-an object of their own; the objects compile in parallel and link with the
-host entry points (``tgemm.hip``) and the measurement probe. All device code
-is built with packed-fp32 instructions disabled (``-packed-fp32-ops``).
+``dense_tiled_gemm_tgemm_amd/libtgemm.so`` (the GEMM, include/tgemm.h) and
+``dense_tiled_gemm_tgemm_amd/libtgemm_probe.so`` (measurement aids,
+include/tgemm_probe.h). The kernels of each (input type, output type,
+epilogue) combination are instantiated by ``tgemm_inst.hip`` in an object of
+their own; the objects compile in parallel and link with the host entry
+points (``tgemm.hip``). All device code is built with packed-fp32
+instructions disabled (``-packed-fp32-ops``).
 """
 import os
 import subprocess
@@ -17,6 +19,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libtgemm.so")
+PROBE_LIB = os.path.join(PKG, "libtgemm_probe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # (input type, output type, epilogue) combinations: 0 binary16, 1 bfloat16, 2 fp32
@@ -53,20 +56,20 @@ def _run(cmd, verbose):
 
 def build(verbose: bool = False, extra=()) -> str:
     with tempfile.TemporaryDirectory(prefix="tgemm_build_") as tmpdir:
-        units = [(os.path.join(CSRC, "tgemm.hip"), [], "tgemm.o"),
-                 (os.path.join(CSRC, "mfma_probe.hip"), [], "mfma_probe.o")]
+        units = [(os.path.join(CSRC, "tgemm.hip"), [], "tgemm.o")]
         for ab, ct, epi in COMBOS:
             units.append((os.path.join(CSRC, "tgemm_inst.hip"),
                           [f"-DTG_AB={ab}", f"-DTG_CT={ct}", f"-DTG_EPI={epi}"], f"inst_{ab}{ct}{epi}.o"))
+        probe = (os.path.join(CSRC, "probe", "tgemm_probe.hip"), [], "tgemm_probe.o")
         cmds = [[HIPCC, *FLAGS, *extra, *defs, "-c", src, "-o", os.path.join(tmpdir, obj)]
-                for src, defs, obj in units]
+                for src, defs, obj in units + [probe]]
         with ThreadPoolExecutor(max_workers=_jobs()) as pool:
             for f in [pool.submit(_run, c, verbose) for c in cmds]:
                 f.result()
-        tmp = LIB + ".tmp"
-        _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC",
-              *[os.path.join(tmpdir, obj) for _, _, obj in units], "-o", tmp], verbose)
-    os.replace(tmp, LIB)
+        for lib, objs in ((LIB, [obj for _, _, obj in units]), (PROBE_LIB, [probe[2]])):
+            _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC",
+                  *[os.path.join(tmpdir, obj) for obj in objs], "-o", lib + ".tmp"], verbose)
+            os.replace(lib + ".tmp", lib)
     return LIB
 
 

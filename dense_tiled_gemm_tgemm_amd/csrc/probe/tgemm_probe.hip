@@ -1,4 +1,5 @@
-// Measurement aids (not part of the product operation).
+// Measurement aids (not part of the product operation), built as a library
+// of their own (libtgemm_probe.so, include/tgemm_probe.h).
 //
 // Matrix-core ceiling probe: the GEMM kernel's instruction stream without its
 // synchronization, tile changes or C stores. Each wave (one per SIMD, as in
@@ -17,6 +18,7 @@
 #include <stdint.h>
 
 #include "tgemm.h"
+#include "tgemm_probe.h"
 
 namespace tg_probe {
 
@@ -29,7 +31,7 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 constexpr int kChunks = 8192;
 
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-mfma_ceiling_kernel(const uint16_t* data, unsigned data_bytes, float* out, int iters) {
+mfma_ceiling_kernel(const uint16_t* data, unsigned data_bytes, float* out, uint64_t* clocks, int iters) {
     __shared__ u32x4 sm[kChunks];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const u32x4* dv = reinterpret_cast<const u32x4*>(data);
@@ -55,6 +57,9 @@ mfma_ceiling_kernel(const uint16_t* data, unsigned data_bytes, float* out, int i
     const unsigned voff = (unsigned)tid * 16u;
     const unsigned smask = data_bytes - 65536u;                     // 64 KiB-aligned windows inside the data
     unsigned soff = (unsigned)blockIdx.x * 65536u;
+    // shader clock and 100 MHz reference time at the start of the rounds
+    const uint64_t t0 = __builtin_amdgcn_s_memtime();
+    const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -84,6 +89,12 @@ mfma_ceiling_kernel(const uint16_t* data, unsigned data_bytes, float* out, int i
         soff += 262144u;
     }
     __builtin_amdgcn_s_waitcnt((0) | (7 << 4) | (15 << 8) | (0 << 14));
+    const uint64_t t1 = __builtin_amdgcn_s_memtime();
+    const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+    if (clocks && tid == 0) {
+        clocks[2 * blockIdx.x] = t1 - t0;
+        clocks[2 * blockIdx.x + 1] = r1 - r0;
+    }
     float s = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -112,14 +123,14 @@ __global__ void __launch_bounds__(64) xcd_id_kernel(int* out, int64_t n) {
 }  // namespace tg_probe
 
 extern "C" int tgemm_mfma_issue_probe(int64_t workgroups, int iters, const void* data, int64_t data_bytes,
-                                      float* out, void* stream) {
+                                      float* out, uint64_t* clocks, void* stream) {
     if (workgroups <= 0 || workgroups > 65536 || iters <= 0 || !out || !data) return TGEMM_ERR_INVALID;
     if (data_bytes < (1 << 20) || data_bytes > (1ll << 30) || (data_bytes & (data_bytes - 1)) != 0)
         return TGEMM_ERR_INVALID;
     if ((uintptr_t)data % 16 != 0) return TGEMM_ERR_INVALID;
     const uint16_t* d = static_cast<const uint16_t*>(data);
     unsigned nb = (unsigned)data_bytes;
-    void* kargs[] = {&d, &nb, &out, &iters};
+    void* kargs[] = {&d, &nb, &out, &clocks, &iters};
     const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&tg_probe::mfma_ceiling_kernel),
                                          dim3((unsigned)workgroups), dim3(256), kargs, 0,
                                          static_cast<hipStream_t>(stream));

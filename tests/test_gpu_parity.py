@@ -13,7 +13,7 @@ pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
 import dense_tiled_gemm_tgemm_amd as tg  # noqa: E402
-from dense_tiled_gemm_tgemm_amd import inputs  # noqa: E402
+from dense_tiled_gemm_tgemm_amd import inputs, probe  # noqa: E402
 
 DEV = "cuda:0"
 NAN16 = 0x7E01          # a quiet-NaN binary16 pattern used as a sentinel
@@ -403,13 +403,20 @@ def test_mfma_issue_probe_runs():
     print("case mfma ceiling probe", flush=True)
     data = _dev(inputs.random_f16((1 << 19,), 7) * np.float16(0.1))     # 1 MiB
     out = torch.empty(8 * 256, dtype=torch.float32, device=DEV)
+    clk = torch.zeros(16, dtype=torch.int64, device=DEV)
     st = torch.cuda.current_stream().cuda_stream
-    tg.mfma_issue_probe(8, 4, data.data_ptr(), 1 << 20, out.data_ptr(), st)
+    probe.mfma_issue_probe(8, 4, data.data_ptr(), 1 << 20, out.data_ptr(), clk.data_ptr(), st)
+    probe.mfma_issue_probe(8, 4, data.data_ptr(), 1 << 20, out.data_ptr(), None, st)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(out).all())
+    # shader cycles and 100 MHz ticks per workgroup: a clock between 0.5 and 3 GHz
+    c = clk.cpu().numpy().reshape(8, 2).astype(np.float64)
+    assert (c > 0).all()
+    ghz = c[:, 0] / c[:, 1] / 10.0
+    assert ((ghz > 0.5) & (ghz < 3.0)).all(), ghz
     for wg, nb in ((0, 1 << 20), (8, (1 << 20) + 2), (8, 1 << 19)):
         with pytest.raises(tg.TgemmError):
-            tg.mfma_issue_probe(wg, 4, data.data_ptr(), nb, out.data_ptr(), st)
+            probe.mfma_issue_probe(wg, 4, data.data_ptr(), nb, out.data_ptr(), None, st)
 
 
 def test_xcd_probe_dispatch_order():
@@ -423,7 +430,7 @@ def test_xcd_probe_dispatch_order():
     st = torch.cuda.current_stream().cuda_stream
     out = torch.full((n,), -1, dtype=torch.int32, device=DEV)
     for launch in range(3):
-        tg.xcd_probe(n - launch, out.data_ptr(), st)     # 8192, 8191, 8190 workgroups
+        probe.xcd_probe(n - launch, out.data_ptr(), st)     # 8192, 8191, 8190 workgroups
         torch.cuda.synchronize()
         got = out.cpu().numpy()[: n - launch]
         c = (got - np.arange(n - launch)) % 8
@@ -432,7 +439,7 @@ def test_xcd_probe_dispatch_order():
         assert got.min() >= 0 and got.max() < 8
         assert (c == c[0]).all()
     with pytest.raises(tg.TgemmError):
-        tg.xcd_probe(0, out.data_ptr(), st)
+        probe.xcd_probe(0, out.data_ptr(), st)
 
 
 def _signed(bits, rng):
