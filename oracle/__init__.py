@@ -36,7 +36,8 @@ import numpy as np
 from . import raster  # noqa: F401  (re-exported submodule)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle_tgemm.so")
+# TGEMM_ORACLE_LIB: another build of tgemm_ref.c (the sanitizer test tier)
+_LIB_PATH = os.environ.get("TGEMM_ORACLE_LIB") or os.path.join(_HERE, "liboracle_tgemm.so")
 _lib = None
 
 _I64 = ctypes.c_int64

@@ -13,16 +13,20 @@ SRC = os.path.join(HERE, "tgemm_ref.c")
 LIB = os.path.join(HERE, "liboracle_tgemm.so")
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
+def build(verbose: bool = False, sanitize: bool = False, out: str = LIB) -> str:
+    """sanitize: AddressSanitizer and UndefinedBehaviorSanitizer instrumentation
+    (for the sanitizer test tier; load the result with libasan preloaded)."""
+    tmp = out + ".tmp"
+    san = ["-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+           "-fno-omit-frame-pointer"] if sanitize else []
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
-           "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra",
+           "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra", *san,
            SRC, "-o", tmp, "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
