@@ -12,9 +12,12 @@ claims to follow it, and the bijection property everywhere.
   the next tile-column. The page uses GROUP_SIZE_M = 8.
 * ``swizzle_2d_p2``: page 2 ("CUDA 13.1 new feature: the Tile programming
   model"), section 7.1 "2D Block Swizzle". The same grouping; the row inside
-  the group is taken from the id modulo (actual group size * grid_n) before
-  the modulo by the group size. The two forms agree on full groups and may
-  order the last, partial group differently.
+  the group follows the id's offset within its group rather than the id
+  itself. The two forms agree on full groups and may order the last,
+  partial group differently.
+  Both are written here as an enumeration of the order the pages describe
+  (bands of tile-rows, each served column by column), not as the pages'
+  per-id formulas; the tests check the product's per-id map against it.
 * ``tile_elements``: page 4 (CUDA programming guide 13.4.2, chapter "Writing
   tile kernels"), section 2.4.6.1 and its Figure 19: a partition view splits
   an array into non-overlapping tiles of a fixed shape; tile index (i, j)
@@ -26,36 +29,48 @@ claims to follow it, and the bijection property everywhere.
 """
 from __future__ import annotations
 
+from functools import lru_cache
+
 
 def cdiv(a: int, b: int) -> int:
     """Ceiling division (page 2, section 5.6: cdiv(7, 4) = 2)."""
     return -(-a // b)
 
 
+@lru_cache(maxsize=None)
+def _grouped_order(rows: int, cols: int, height: int, rotate_by_global_id: bool):
+    """Every tile (row, column) of a rows x cols tile grid, in the order the
+    grouped raster hands them to block ids 0, 1, 2, ...
+
+    Tile-rows are cut into bands of `height` consecutive rows (the last band
+    keeps what is left). Bands are served top to bottom. Inside a band of h
+    rows, each tile-column in turn, left to right, receives h consecutive ids,
+    one per row of the band, so ids run down a column before moving right.
+    The row an id lands on inside its column is its offset in the band modulo
+    h (page 2's wording), or, with rotate_by_global_id, the block id itself
+    modulo h (page 1's wording); on full bands both are the same, because a
+    full band starts at a multiple of h."""
+    order = []
+    for top in range(0, rows, height):
+        h = min(height, rows - top)
+        band_start = len(order)
+        for offset in range(h * cols):
+            col = offset // h
+            r = (band_start + offset if rotate_by_global_id else offset) % h
+            order.append((top + r, col))
+    return tuple(order)
+
+
 def swizzle_2d_from_bid(M: int, N: int, tm: int, tn: int, group_size_m: int, bid: int):
-    """Page 1, section "Swizzle": block id -> (tile row, tile column)."""
-    num_bid_m = cdiv(M, tm)
-    num_bid_n = cdiv(N, tn)
-    num_bid_in_group = group_size_m * num_bid_n
-    group_id = bid // num_bid_in_group
-    first_bid_m = group_id * group_size_m
-    group_size = min(num_bid_m - first_bid_m, group_size_m)
-    bid_m = first_bid_m + (bid % group_size)
-    bid_n = (bid % num_bid_in_group) // group_size
-    return bid_m, bid_n
+    """Page 1, section "Swizzle": block id -> (tile row, tile column) for an
+    M x N output cut into tm x tn tiles, bands of group_size_m tile-rows."""
+    return _grouped_order(cdiv(M, tm), cdiv(N, tn), group_size_m, True)[bid]
 
 
 def swizzle_2d_p2(M: int, N: int, tm: int, tn: int, group_size: int, linear_id: int):
-    """Page 2, section 7.1: block id -> (tile row, tile column)."""
-    grid_m = cdiv(M, tm)
-    grid_n = cdiv(N, tn)
-    group_id = linear_id // (group_size * grid_n)
-    first_row_in_group = group_id * group_size
-    group_size_actual = min(grid_m - first_row_in_group, group_size)
-    within_group = linear_id % (group_size_actual * grid_n)
-    bidx = first_row_in_group + (within_group % group_size_actual)
-    bidy = within_group // group_size_actual
-    return bidx, bidy
+    """Page 2, section 7.1: block id -> (tile row, tile column); the row inside
+    the last, partial band follows the id's offset within that band."""
+    return _grouped_order(cdiv(M, tm), cdiv(N, tn), group_size, False)[linear_id]
 
 
 def linear_2d(N: int, tn: int, bid: int):
