@@ -254,6 +254,10 @@ def main():
     ap.add_argument("--epilogue", action="store_true", help="alpha = 0.5, seeded fp32 bias, rectifier")
     ap.add_argument("--tune", action="store_true",
                     help="run the runtime tuner on the workload first; the timed launches use its choice")
+    ap.add_argument("--k-step", type=int, default=0, help="launch choice (tgemm_gemm_config): K step 32 or 64")
+    ap.add_argument("--stages", type=int, default=0, help="launch choice: LDS ring depth")
+    ap.add_argument("--tile-m", type=int, default=0, help="launch choice: tile rows 256, 128 or 64")
+    ap.add_argument("--producers", type=int, default=0, help="launch choice: 4 = producer/consumer workgroups")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold-cache launches (512 MiB written before each) reported beside the headline")
@@ -413,7 +417,9 @@ def main():
                           "tflops": round(float(w.flops) / ms / 1e9, 1)}), flush=True)
         return
 
-    if tag == "":
+    launch = dict(k_step=args.k_step, stages=args.stages, tile_m=args.tile_m, producers=args.producers)
+    explicit = any(launch.values())
+    if tag == "" and not explicit:
         def step():
             rc = tg.tgemm_f16(w.M, w.N, w.K, Ad.data_ptr(), lda, Bd.data_ptr(), ldb, w.b_layout,
                               Cd.data_ptr(), ldc, sptr)
@@ -423,8 +429,8 @@ def main():
         bptr = bias_d.data_ptr() if bias_d is not None else None
 
         def step():
-            rc = tg.tgemm_gemm(w.M, w.N, w.K, args.ab, Ad.data_ptr(), lda, Bd.data_ptr(), ldb, w.b_layout,
-                               args.out, Cd.data_ptr(), ldc, alpha, bptr, act, sptr)
+            rc = tg.tgemm_gemm_config(w.M, w.N, w.K, args.ab, Ad.data_ptr(), lda, Bd.data_ptr(), ldb, w.b_layout,
+                                      args.out, Cd.data_ptr(), ldc, alpha, bptr, act, sptr, **launch)
             if rc != tg.TGEMM_OK:
                 raise tg.TgemmError(rc)
 
@@ -520,8 +526,9 @@ def main():
         "config": {"workload": name, "M": w.M, "N": w.N, "K": w.K, "b_layout": w.b_layout,
                    "seed": w.seed, "accumulate": "f32", "output": args.out,
                    "epilogue": (f"alpha={EPI_ALPHA}, bias, relu" if args.epilogue else "none"),
-                   "launch": ({k: tuned[k] for k in ("k_step", "stages", "group_m", "num_xcd")} if tuned
-                              else "default")},
+                   "launch": ({k: tuned[k] for k in ("k_step", "stages", "group_m", "num_xcd", "tile_m",
+                                                     "producers")} if tuned
+                              else ({k: v for k, v in launch.items() if v} if explicit else "default"))},
         "roofline": {
             "bound": "mfma",
             "achieved": round(achieved, 2),

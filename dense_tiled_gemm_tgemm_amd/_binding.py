@@ -68,14 +68,14 @@ def load():
     lib.tgemm_f16.restype = _INT
     lib.tgemm_f16.argtypes = gemm_args
     lib.tgemm_f16_config.restype = _INT
-    lib.tgemm_f16_config.argtypes = gemm_args + [_INT, _INT, _INT, _INT, _INT]
+    lib.tgemm_f16_config.argtypes = gemm_args + [_INT, _INT, _INT, _INT, _INT, _INT, _INT]
     ex_args = [_I64, _I64, _I64, _INT, _P, _I64, _P, _I64, _INT, _INT, _P, _I64, ctypes.c_float, _P, _INT]
     lib.tgemm_gemm.restype = _INT
     lib.tgemm_gemm.argtypes = ex_args + [_P]
     lib.tgemm_gemm_config.restype = _INT
-    lib.tgemm_gemm_config.argtypes = ex_args + [_P, _INT, _INT, _INT, _INT, _INT]
+    lib.tgemm_gemm_config.argtypes = ex_args + [_P, _INT, _INT, _INT, _INT, _INT, _INT, _INT]
     lib.tgemm_plan_gemm.restype = _INT
-    lib.tgemm_plan_gemm.argtypes = ex_args + [_INT, _INT, _INT, _INT, _INT, _INT, ctypes.POINTER(_I64)]
+    lib.tgemm_plan_gemm.argtypes = ex_args + [_INT, _INT, _INT, _INT, _INT, _INT, _INT, _INT, ctypes.POINTER(_I64)]
     lib.tgemm_tune_gemm.restype = _INT
     lib.tgemm_tune_gemm.argtypes = ex_args + [_P, _INT, ctypes.POINTER(_I64)]
     lib.tgemm_tuning_entries.restype = _INT
@@ -88,7 +88,7 @@ def load():
     lib.tgemm_last_hip_error.argtypes = []
     lib.tgemm_plan_f16.restype = _INT
     lib.tgemm_plan_f16.argtypes = [_I64, _I64, _I64, _P, _I64, _P, _I64, _INT, _P, _I64,
-                                   _INT, _INT, _INT, _INT, _INT, _INT, ctypes.POINTER(_I64)]
+                                   _INT, _INT, _INT, _INT, _INT, _INT, _INT, _INT, ctypes.POINTER(_I64)]
     lib.tgemm_tile_of.restype = _INT
     lib.tgemm_tile_of.argtypes = [_I64, _I64, _INT, _INT, _I64, ctypes.POINTER(_I64), ctypes.POINTER(_I64)]
     _lib = lib
@@ -109,19 +109,19 @@ def tgemm_f16(M, N, K, A, lda, B, ldb, b_layout, C, ldc, stream=None) -> int:
 
 
 def tgemm_f16_config(M, N, K, A, lda, B, ldb, b_layout, C, ldc, stream=None,
-                     force_generic=0, group_m=0, num_xcd=0, k_step=0, stages=0) -> int:
+                     force_generic=0, group_m=0, num_xcd=0, k_step=0, stages=0, tile_m=0, producers=0) -> int:
     return int(load().tgemm_f16_config(M, N, K, A, lda, B, ldb, _LAYOUT[b_layout], C, ldc, stream,
                                        int(force_generic), int(group_m), int(num_xcd), int(k_step),
-                                       int(stages)))
+                                       int(stages), int(tile_m), int(producers)))
 
 
 def tgemm_plan_f16(M, N, K, A, lda, B, ldb, b_layout, C, ldc, force_generic=0, group_m=0, num_xcd=0,
-                   k_step=0, stages=0, compute_units=0):
+                   k_step=0, stages=0, tile_m=0, producers=0, compute_units=0):
     """Plan query: (status, info dict or None). compute_units=0 asks the current device."""
     info = (_I64 * 10)()
     rc = int(load().tgemm_plan_f16(M, N, K, A, lda, B, ldb, _LAYOUT[b_layout], C, ldc,
                                    int(force_generic), int(group_m), int(num_xcd), int(k_step),
-                                   int(stages), int(compute_units), info))
+                                   int(stages), int(tile_m), int(producers), int(compute_units), info))
     if rc != TGEMM_OK:
         return rc, None
     keys = ("variant", "bm", "bn", "bk", "workgroups", "group_m", "num_xcd", "threads", "stages",
@@ -137,34 +137,38 @@ def tgemm_gemm(M, N, K, ab_type, A, lda, B, ldb, b_layout, c_type, C, ldc, alpha
 
 
 def tgemm_gemm_config(M, N, K, ab_type, A, lda, B, ldb, b_layout, c_type, C, ldc, alpha=1.0, bias=None,
-                      act="none", stream=None, force_generic=0, group_m=0, num_xcd=0, k_step=0, stages=0) -> int:
+                      act="none", stream=None, force_generic=0, group_m=0, num_xcd=0, k_step=0, stages=0,
+                      tile_m=0, producers=0) -> int:
     return int(load().tgemm_gemm_config(M, N, K, _code(_DTYPE, ab_type), A, lda, B, ldb, _LAYOUT[b_layout],
                                         _code(_DTYPE, c_type), C, ldc, float(alpha), bias, _code(_ACT, act), stream,
-                                        int(force_generic), int(group_m), int(num_xcd), int(k_step), int(stages)))
+                                        int(force_generic), int(group_m), int(num_xcd), int(k_step), int(stages),
+                                        int(tile_m), int(producers)))
 
 
 _PLAN_KEYS = ("variant", "bm", "bn", "bk", "workgroups", "group_m", "num_xcd", "threads", "stages", "lds_bytes")
 
 
 def tgemm_plan_gemm(M, N, K, ab_type, A, lda, B, ldb, b_layout, c_type, C, ldc, alpha=1.0, bias=None,
-                    act="none", force_generic=0, group_m=0, num_xcd=0, k_step=0, stages=0, compute_units=0):
+                    act="none", force_generic=0, group_m=0, num_xcd=0, k_step=0, stages=0, tile_m=0, producers=0,
+                    compute_units=0):
     """Plan query of the typed GEMM: (status, info dict or None). compute_units=0 asks the current device."""
     info = (_I64 * 10)()
     rc = int(load().tgemm_plan_gemm(M, N, K, _code(_DTYPE, ab_type), A, lda, B, ldb, _LAYOUT[b_layout], _code(_DTYPE, c_type),
                                     C, ldc, float(alpha), bias, _code(_ACT, act), int(force_generic), int(group_m),
-                                    int(num_xcd), int(k_step), int(stages), int(compute_units), info))
+                                    int(num_xcd), int(k_step), int(stages), int(tile_m), int(producers),
+                                    int(compute_units), info))
     if rc != TGEMM_OK:
         return rc, None
     return rc, dict(zip(_PLAN_KEYS, (int(v) for v in info)))
 
 
-_TUNE_KEYS = ("k_step", "stages", "group_m", "num_xcd", "median_ns", "candidates")
+_TUNE_KEYS = ("k_step", "stages", "group_m", "num_xcd", "median_ns", "candidates", "tile_m", "producers")
 
 
 def tgemm_tune_gemm(M, N, K, ab_type, A, lda, B, ldb, b_layout, c_type, C, ldc, alpha=1.0, bias=None, act="none",
                     stream=None, rounds=5):
     """Raw C call of the runtime tuner: (status, chosen launch dict or None)."""
-    info = (_I64 * 6)()
+    info = (_I64 * 8)()
     rc = int(load().tgemm_tune_gemm(M, N, K, _code(_DTYPE, ab_type), A, lda, B, ldb, _LAYOUT[b_layout],
                                     _code(_DTYPE, c_type), C, ldc, float(alpha), bias, _code(_ACT, act), stream,
                                     int(rounds), info))
@@ -217,7 +221,8 @@ def _same_device(A, *others):
 
 
 def mm(A, B, b_layout: str = "KxN", out=None, stream=None, force_generic: int = 0,
-       group_m: int = 0, num_xcd: int = 0, k_step: int = 0, stages: int = 0):
+       group_m: int = 0, num_xcd: int = 0, k_step: int = 0, stages: int = 0, tile_m: int = 0,
+       producers: int = 0):
     """C = A @ B for fp16 device tensors (fp32 accumulation in the kernel).
 
     A: (M, K). B: (K, N) when b_layout == "KxN", (N, K) when "NxK".
@@ -249,7 +254,7 @@ def mm(A, B, b_layout: str = "KxN", out=None, stream=None, force_generic: int = 
         stream = stream.cuda_stream
     with torch.cuda.device(A.device):
         rc = tgemm_f16_config(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, lay, out.data_ptr(), ldc,
-                              stream, force_generic, group_m, num_xcd, k_step, stages)
+                              stream, force_generic, group_m, num_xcd, k_step, stages, tile_m, producers)
     if rc != TGEMM_OK:
         raise TgemmError(rc, f"M={M} N={N} K={K} layout={b_layout}")
     return out
@@ -273,7 +278,7 @@ def tune(A, B, b_layout: str = "KxN", out=None, out_dtype=None, alpha: float = 1
 
 def gemm(A, B, b_layout: str = "KxN", out=None, out_dtype=None, alpha: float = 1.0, bias=None, act: str = "none",
          stream=None, force_generic: int = 0, group_m: int = 0, num_xcd: int = 0, k_step: int = 0,
-         stages: int = 0, _tune_rounds: int = 0):
+         stages: int = 0, tile_m: int = 0, producers: int = 0, _tune_rounds: int = 0):
     """C = act(alpha * A @ B + bias) for float16, bfloat16 or float32 device
     tensors (fp32 accumulation and epilogue in the kernel).
 
@@ -323,7 +328,7 @@ def gemm(A, B, b_layout: str = "KxN", out=None, out_dtype=None, alpha: float = 1
     with torch.cuda.device(A.device):
         rc = tgemm_gemm_config(M, N, K, _torch_code(A.dtype), A.data_ptr(), lda, B.data_ptr(), ldb, lay,
                                _torch_code(out.dtype), out.data_ptr(), ldc, alpha, bias_ptr, act, stream,
-                               force_generic, group_m, num_xcd, k_step, stages)
+                               force_generic, group_m, num_xcd, k_step, stages, tile_m, producers)
     if rc != TGEMM_OK:
         raise TgemmError(rc, f"M={M} N={N} K={K} layout={b_layout} {A.dtype}->{out.dtype}")
     return out

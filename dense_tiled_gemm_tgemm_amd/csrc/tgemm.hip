@@ -107,7 +107,7 @@ struct TuneKeyHash {
 };
 
 struct TuneChoice {
-    int k_step, stages, group_m, num_xcd;
+    int k_step, stages, group_m, num_xcd, tile_m, producers;
 };
 
 constexpr float kTuneWarmupMs = 100.f;        // GPU time of the clock-settling launches
@@ -143,12 +143,12 @@ static bool tuned_choice(const Plan& pl, TuneChoice* c) {
 // recorded by tgemm_tune_gemm for this problem, if any, is used.
 static int plan_gemm(int64_t M, int64_t N, int64_t K, int ab_type, const void* A, int64_t lda, const void* B,
                      int64_t ldb, int b_layout, int c_type, void* C, int64_t ldc, float alpha, const float* bias,
-                     int act, int force_generic, int group_m, int num_xcd, int k_step, int stages, int ncu,
-                     Plan* pl, const void** fn, bool use_tuned = true) {
+                     int act, int force_generic, int group_m, int num_xcd, int k_step, int stages, int tile_m,
+                     int producers, int ncu, Plan* pl, const void** fn, bool use_tuned = true) {
     if (act != TGEMM_ACT_NONE && act != TGEMM_ACT_RELU) return TGEMM_ERR_INVALID;
     const bool epi = epilogue_requested(alpha, bias, act);
     int rc = make_plan(M, N, K, A, lda, B, ldb, b_layout, C, ldc, force_generic, group_m, num_xcd, k_step, stages,
-                       pl, ab_type, c_type, bias, epi);
+                       pl, ab_type, c_type, bias, epi, tile_m, producers);
     if (rc != TGEMM_OK) return rc;
     if (pl->M == 0 || pl->N == 0) {              // nothing to launch
         *fn = nullptr;
@@ -161,11 +161,11 @@ static int plan_gemm(int64_t M, int64_t N, int64_t K, int ab_type, const void* A
         if (rc != TGEMM_OK) return rc;
     }
     TuneChoice t;
-    const bool automatic = !force_generic && !group_m && !num_xcd && !k_step && !stages;
+    const bool automatic = !force_generic && !group_m && !num_xcd && !k_step && !stages && !tile_m && !producers;
     if (automatic && use_tuned && tuned_choice(*pl, &t)) {
         Plan tp;
         rc = make_plan(M, N, K, A, lda, B, ldb, b_layout, C, ldc, 0, t.group_m, t.num_xcd, t.k_step, t.stages,
-                       &tp, ab_type, c_type, bias, epi);
+                       &tp, ab_type, c_type, bias, epi, t.tile_m, t.producers);
         if (rc == TGEMM_OK) *pl = tp;
     } else if (automatic && (pl->variant & kDma) && !(pl->variant & kLayoutNxK) && ab_type != TGEMM_F32 &&
                K > 64 && K % 64 != 0 && pl->W <= ncu) {
@@ -209,7 +209,7 @@ static int launch(const Plan& pl, const void* fn, const void* A, const void* B, 
                (127 * pl.ldc + (int64_t)pl.N) * c_size + 16 < (int64_t(1) << 31);
     args.c8 = (pl.variant & kVecC) != 0;
     void* kargs[] = {&args};
-    const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)args.grid), dim3(NTHREADS), kargs, 0,
+    const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)args.grid), dim3((unsigned)pl.threads), kargs, 0,
                                          static_cast<hipStream_t>(stream));
     if (e != hipSuccess) {
         g_last_hip_error = (int)e;
@@ -223,11 +223,11 @@ static int launch(const Plan& pl, const void* fn, const void* A, const void* B, 
 extern "C" int tgemm_gemm_config(int64_t M, int64_t N, int64_t K, int ab_type, const void* A, int64_t lda,
                                  const void* B, int64_t ldb, int b_layout, int c_type, void* C, int64_t ldc,
                                  float alpha, const float* bias, int act, void* stream, int force_generic,
-                                 int group_m, int num_xcd, int k_step, int stages) {
+                                 int group_m, int num_xcd, int k_step, int stages, int tile_m, int producers) {
     tg::Plan pl;
     const void* fn = nullptr;
     const int rc = tg::plan_gemm(M, N, K, ab_type, A, lda, B, ldb, b_layout, c_type, C, ldc, alpha, bias, act,
-                                 force_generic, group_m, num_xcd, k_step, stages, 0, &pl, &fn);
+                                 force_generic, group_m, num_xcd, k_step, stages, tile_m, producers, 0, &pl, &fn);
     if (rc != TGEMM_OK) return rc;
     if (pl.M == 0 || pl.N == 0) return TGEMM_OK;
     return tg::launch(pl, fn, A, B, C, c_type, alpha, bias, act, stream);
@@ -237,20 +237,21 @@ extern "C" int tgemm_gemm(int64_t M, int64_t N, int64_t K, int ab_type, const vo
                           int64_t ldb, int b_layout, int c_type, void* C, int64_t ldc, float alpha,
                           const float* bias, int act, void* stream) {
     return tgemm_gemm_config(M, N, K, ab_type, A, lda, B, ldb, b_layout, c_type, C, ldc, alpha, bias, act, stream,
-                             0, 0, 0, 0, 0);
+                             0, 0, 0, 0, 0, 0, 0);
 }
 
 extern "C" int tgemm_f16_config(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                                 const void* B, int64_t ldb, int b_layout, void* C, int64_t ldc,
                                 void* stream, int force_generic, int group_m, int num_xcd, int k_step,
-                                int stages) {
+                                int stages, int tile_m, int producers) {
     return tgemm_gemm_config(M, N, K, TGEMM_F16, A, lda, B, ldb, b_layout, TGEMM_F16, C, ldc, 1.0f, nullptr,
-                             TGEMM_ACT_NONE, stream, force_generic, group_m, num_xcd, k_step, stages);
+                             TGEMM_ACT_NONE, stream, force_generic, group_m, num_xcd, k_step, stages, tile_m,
+                             producers);
 }
 
 extern "C" int tgemm_f16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
                          int64_t ldb, int b_layout, void* C, int64_t ldc, void* stream) {
-    return tgemm_f16_config(M, N, K, A, lda, B, ldb, b_layout, C, ldc, stream, 0, 0, 0, 0, 0);
+    return tgemm_f16_config(M, N, K, A, lda, B, ldb, b_layout, C, ldc, stream, 0, 0, 0, 0, 0, 0, 0);
 }
 
 extern "C" int tgemm_tune_gemm(int64_t M, int64_t N, int64_t K, int ab_type, const void* A, int64_t lda,
@@ -260,38 +261,46 @@ extern "C" int tgemm_tune_gemm(int64_t M, int64_t N, int64_t K, int ab_type, con
     tg::Plan base;
     const void* fn = nullptr;
     int rc = tg::plan_gemm(M, N, K, ab_type, A, lda, B, ldb, b_layout, c_type, C, ldc, alpha, bias, act, 0, 0, 0, 0,
-                           0, 0, &base, &fn, false);
+                           0, 0, 0, 0, &base, &fn, false);
     if (rc != TGEMM_OK) return rc;
     if (info)
-        for (int i = 0; i < 6; ++i) info[i] = 0;
+        for (int i = 0; i < 8; ++i) info[i] = 0;
     if (base.M == 0 || base.N == 0) return TGEMM_OK;
     int ncu = 0;
     rc = tg::device_compute_units(&ncu);
     if (rc != TGEMM_OK) return rc;
 
-    // candidates: K step x ring depth (direct-to-LDS path only) x raster group height
+    // candidates: tile rows x K step x ring depth (direct-to-LDS path only:
+    // 256-row tiles with 64- or 32-deep steps, 128- and 64-row tiles at two
+    // workgroups per compute unit, producer/consumer workgroups) x raster
+    // group height; those not built for the types drop out
     struct Cand {
         tg::TuneChoice c;
         tg::Plan pl;
         const void* fn;
     };
     std::vector<Cand> cands;
-    const int pipes[][2] = {{64, 2}, {32, 4}, {32, 2}, {32, 3}, {32, 5}};
-    const int npipes = (base.variant & tg::kDma) ? 5 : 1;
+    const int pipes[][4] = {{64, 2, 256, 0}, {32, 4, 256, 0}, {32, 2, 256, 0}, {32, 3, 256, 0}, {32, 5, 256, 0},
+                            {32, 3, 128, 0}, {32, 2, 128, 0}, {32, 3, 64, 0},  {32, 3, 128, 4}, {32, 5, 128, 4}};
+    const int npipes = (base.variant & tg::kDma) ? (int)(sizeof(pipes) / sizeof(pipes[0])) : 1;
     const int groups[] = {4, 8, 16};
     for (int ip = 0; ip < npipes; ++ip) {
         for (int g : groups) {
-            const int ks = (base.variant & tg::kDma) ? pipes[ip][0] : 0;
-            const int st = (base.variant & tg::kDma) ? pipes[ip][1] : 0;
+            const bool dma = (base.variant & tg::kDma) != 0;
+            const int ks = dma ? pipes[ip][0] : 0;
+            const int st = dma ? pipes[ip][1] : 0;
+            const int tm = dma ? pipes[ip][2] : 0;
+            const int pr = dma ? pipes[ip][3] : 0;
             Cand cd;
-            cd.c = tg::TuneChoice{ks, st, g, tg::kDefaultNumXcd};
+            cd.c = tg::TuneChoice{ks, st, g, tg::kDefaultNumXcd, tm, pr};
             if (tg::plan_gemm(M, N, K, ab_type, A, lda, B, ldb, b_layout, c_type, C, ldc, alpha, bias, act, 0, g,
-                              tg::kDefaultNumXcd, ks, st, ncu, &cd.pl, &cd.fn, false) != TGEMM_OK)
+                              tg::kDefaultNumXcd, ks, st, tm, pr, ncu, &cd.pl, &cd.fn, false) != TGEMM_OK)
                 continue;                                   // not built for these types, or invalid for this K
             bool dup = false;                               // group heights clamp to the tile rows
             for (const Cand& o : cands)
                 dup = dup || (o.pl.k_step == cd.pl.k_step && o.pl.stages == cd.pl.stages &&
-                              o.pl.group_m == cd.pl.group_m);
+                              o.pl.group_m == cd.pl.group_m && o.pl.bm == cd.pl.bm &&
+                              o.pl.producers == cd.pl.producers);
             if (!dup) cands.push_back(cd);
         }
     }
@@ -302,7 +311,8 @@ extern "C" int tgemm_tune_gemm(int64_t M, int64_t N, int64_t K, int ab_type, con
     int def = 0;
     for (int i = 0; i < nc; ++i)
         if (cands[i].pl.k_step == base.k_step && cands[i].pl.stages == base.stages &&
-            cands[i].pl.group_m == base.group_m)
+            cands[i].pl.group_m == base.group_m && cands[i].pl.bm == base.bm &&
+            cands[i].pl.producers == base.producers)
             def = i;
     // one event between consecutive launches; every round runs every candidate
     // once, round r starting at candidate r (so no candidate always runs first
@@ -367,7 +377,7 @@ extern "C" int tgemm_tune_gemm(int64_t M, int64_t N, int64_t K, int ab_type, con
     const tg::Plan& bp = cands[best].pl;
     {
         std::lock_guard<std::mutex> lock(tg::g_tune_mu);
-        tg::g_tuned[key] = tg::TuneChoice{bp.k_step, bp.stages, bp.group_m, bp.num_xcd};
+        tg::g_tuned[key] = tg::TuneChoice{bp.k_step, bp.stages, bp.group_m, bp.num_xcd, bp.bm, bp.producers};
         tg::g_tuned_count.store((int)tg::g_tuned.size(), std::memory_order_release);
     }
     if (info) {
@@ -377,6 +387,8 @@ extern "C" int tgemm_tune_gemm(int64_t M, int64_t N, int64_t K, int ab_type, con
         info[3] = bp.num_xcd;
         info[4] = (int64_t)(med[best] * 1e6f);   // median launch time, ns
         info[5] = nc;
+        info[6] = bp.bm;
+        info[7] = bp.producers;
     }
     return TGEMM_OK;
 }
@@ -403,27 +415,29 @@ extern "C" int tgemm_last_hip_error(void) { return tg::g_last_hip_error; }
 
 static void fill_info(const tg::Plan& pl, int64_t* info) {
     info[0] = pl.variant;
-    info[1] = tg::BM;
+    info[1] = pl.bm;
     info[2] = pl.bn;
     info[3] = pl.k_step;
     info[4] = (pl.M == 0 || pl.N == 0) ? 0 : pl.grid;
     info[5] = pl.group_m;
     info[6] = pl.num_xcd;
-    info[7] = tg::NTHREADS;
+    info[7] = pl.threads;
     info[8] = pl.stages;
     // LDS bytes per workgroup: stages x (A block + B block rows) x K step x element size
-    info[9] = (int64_t)pl.stages * (tg::BM + pl.bn) * pl.k_step * (pl.ab_type == TGEMM_F32 ? 4 : 2);
+    info[9] = (int64_t)pl.stages * (pl.bm + pl.bn) * pl.k_step * (pl.ab_type == TGEMM_F32 ? 4 : 2);
 }
 
 extern "C" int tgemm_plan_gemm(int64_t M, int64_t N, int64_t K, int ab_type, const void* A, int64_t lda,
                                const void* B, int64_t ldb, int b_layout, int c_type, void* C, int64_t ldc,
                                float alpha, const float* bias, int act, int force_generic, int group_m,
-                               int num_xcd, int k_step, int stages, int compute_units, int64_t* info) {
+                               int num_xcd, int k_step, int stages, int tile_m, int producers, int compute_units,
+                               int64_t* info) {
     if (!info || compute_units < 0 || compute_units > 65536) return TGEMM_ERR_INVALID;
     tg::Plan pl;
     const void* fn = nullptr;
     const int rc = tg::plan_gemm(M, N, K, ab_type, A, lda, B, ldb, b_layout, c_type, C, ldc, alpha, bias, act,
-                                 force_generic, group_m, num_xcd, k_step, stages, compute_units, &pl, &fn);
+                                 force_generic, group_m, num_xcd, k_step, stages, tile_m, producers, compute_units,
+                                 &pl, &fn);
     if (rc != TGEMM_OK) return rc;
     fill_info(pl, info);
     return TGEMM_OK;
@@ -431,10 +445,11 @@ extern "C" int tgemm_plan_gemm(int64_t M, int64_t N, int64_t K, int ab_type, con
 
 extern "C" int tgemm_plan_f16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
                               int64_t ldb, int b_layout, void* C, int64_t ldc, int force_generic,
-                              int group_m, int num_xcd, int k_step, int stages, int compute_units,
-                              int64_t* info) {
+                              int group_m, int num_xcd, int k_step, int stages, int tile_m, int producers,
+                              int compute_units, int64_t* info) {
     return tgemm_plan_gemm(M, N, K, TGEMM_F16, A, lda, B, ldb, b_layout, TGEMM_F16, C, ldc, 1.0f, nullptr,
-                           TGEMM_ACT_NONE, force_generic, group_m, num_xcd, k_step, stages, compute_units, info);
+                           TGEMM_ACT_NONE, force_generic, group_m, num_xcd, k_step, stages, tile_m, producers,
+                           compute_units, info);
 }
 
 extern "C" int tgemm_tile_of(int64_t grid_m, int64_t grid_n, int group_m, int num_xcd, int64_t wid,

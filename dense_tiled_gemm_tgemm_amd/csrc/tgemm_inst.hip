@@ -14,11 +14,34 @@ namespace {
 
 constexpr int kTy = ty_code(TG_AB, TG_CT, TG_EPI != 0);
 // the plain binary16 product instantiates every ring depth of 32-deep
-// steps; the other combinations the default depth only
+// steps, the 2-stage ring of 128 x 256 tiles and the producer/consumer
+// workgroups; the other combinations the default depth of each tile only
 constexpr bool kAllDepths = (kTy == ty_code(0, 0, false));
 
 template <int NXK>
-const void* dma_ptr(int k_step, int stages) {
+const void* dma_ptr(int k_step, int stages, int tile_m, int producers) {
+    if (producers) {
+        // producer/consumer workgroups: 128 x 256 tiles, 32-deep steps
+        if constexpr (kAllDepths) {
+            if (tile_m == 128 && k_step == 32 && stages == 3)
+                return reinterpret_cast<const void*>(&tgemm_dma_kernel<kTy, NXK, 32, 3, 4, true>);
+            if (tile_m == 128 && k_step == 32 && stages == 5)
+                return reinterpret_cast<const void*>(&tgemm_dma_kernel<kTy, NXK, 32, 5, 4, true>);
+        }
+        return nullptr;
+    }
+    if (tile_m == 128) {
+        if (k_step == 32 && stages == kDefaultSmallStages)
+            return reinterpret_cast<const void*>(&tgemm_dma_kernel<kTy, NXK, 32, 3, 4>);
+        if constexpr (kAllDepths)
+            if (k_step == 32 && stages == 2) return reinterpret_cast<const void*>(&tgemm_dma_kernel<kTy, NXK, 32, 2, 4>);
+        return nullptr;
+    }
+    if (tile_m == 64) {
+        if (k_step == 32 && stages == kDefaultSmallStages)
+            return reinterpret_cast<const void*>(&tgemm_dma_kernel<kTy, NXK, 32, 3, 2>);
+        return nullptr;
+    }
     if (k_step == 64) return reinterpret_cast<const void*>(&tgemm_dma_kernel<kTy, NXK, 64, 2>);
     if (stages == kDefaultDmaStages32) return reinterpret_cast<const void*>(&tgemm_dma_kernel<kTy, NXK, 32, 4>);
     if constexpr (kAllDepths) {
@@ -31,7 +54,8 @@ const void* dma_ptr(int k_step, int stages) {
     }
     return nullptr;
 }
-static_assert(kDefaultDmaStages32 == 4, "the default ring depth is instantiated for every combination");
+static_assert(kDefaultDmaStages32 == 4 && kDefaultSmallStages == 3,
+              "the default ring depths are instantiated for every combination");
 
 template <int NXK>
 const void* rs_ptr(bool vec) {
@@ -57,7 +81,9 @@ const void* kernel_for<TG_AB, TG_CT, (TG_EPI != 0)>(const Plan& pl) {
         const bool pipelined = (pl.variant & kDma) != 0;
         return nxk ? f32in_ptr<1>(pipelined, vec) : f32in_ptr<0>(pipelined, vec);
     } else {
-        if (pl.variant & kDma) return nxk ? dma_ptr<1>(pl.k_step, pl.stages) : dma_ptr<0>(pl.k_step, pl.stages);
+        if (pl.variant & kDma)
+            return nxk ? dma_ptr<1>(pl.k_step, pl.stages, pl.bm, pl.producers)
+                       : dma_ptr<0>(pl.k_step, pl.stages, pl.bm, pl.producers);
         return nxk ? rs_ptr<1>(vec) : rs_ptr<0>(vec);
     }
 }

@@ -246,14 +246,16 @@ __device__ __forceinline__ void store16_lanes(const u32x4& v, const BufRsrc& r, 
 // tiles with the next tile's fragments already in registers. Vector stores
 // use the streaming policies (store16_stream above; the 8-byte path is
 // non-temporal).
-template <int TY, int NJ = 8>
-__device__ __forceinline__ void store_c(const f32x4 (&acc)[8][NJ], const Args& a, int m0, int n0, int wm,
+template <int TY, int NJ = 8, int NI = 8>
+__device__ __forceinline__ void store_c(const f32x4 (&acc)[NI][NJ], const Args& a, int m0, int n0, int wm,
                                         int wn, int lane) {
     static_assert(NJ == 8 || NJ == 4, "a wave owns 8 or 4 blocks of 16 columns");
+    static_assert(NI == 8 || NI == 4 || NI == 2 || NI == 1, "a wave owns 8, 4, 2 or 1 blocks of 16 rows");
+    constexpr int kWr = 16 * NI;                      // C rows of a wave
     constexpr int CT = ct_of(TY);
     constexpr bool EPI = epi_of(TY);
     const int r16 = lane & 15, g = lane >> 4;
-    const BufRsrc crs = c_rows_rsrc(a.C, (int64_t)(m0 + wm * 128) * a.ldc * (CT == 2 ? 4 : 2));
+    const BufRsrc crs = c_rows_rsrc(a.C, (int64_t)(m0 + wm * kWr) * a.ldc * (CT == 2 ? 4 : 2));
     float bv[NJ][4];
     float alpha = 1.f;
     bool relu = false;
@@ -263,14 +265,14 @@ __device__ __forceinline__ void store_c(const f32x4 (&acc)[8][NJ], const Args& a
         relu = a.relu != 0;
     }
     const bool whole = __builtin_amdgcn_readfirstlane(
-        (int)(a.c16 && m0 + wm * 128 + 128 <= a.M && n0 + wn * 16 * NJ + 16 * NJ <= a.N)) != 0;
+        (int)(a.c16 && m0 + wm * kWr + kWr <= a.M && n0 + wn * 16 * NJ + 16 * NJ <= a.N)) != 0;
     if constexpr (CT == 2) {
         const int colb = n0 + wn * 16 * NJ + 4 * g;
-        float* base = static_cast<float*>(a.C) + (int64_t)(m0 + wm * 128 + r16) * a.ldc + colb;
+        float* base = static_cast<float*>(a.C) + (int64_t)(m0 + wm * kWr + r16) * a.ldc + colb;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < NI; ++i) {
             __builtin_amdgcn_sched_barrier(0);
-            const bool row_ok = m0 + wm * 128 + i * 16 + r16 < a.M;
+            const bool row_ok = m0 + wm * kWr + i * 16 + r16 < a.M;
             float* row = base + (int64_t)i * 16 * a.ldc;
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
@@ -300,11 +302,11 @@ __device__ __forceinline__ void store_c(const f32x4 (&acc)[8][NJ], const Args& a
         }
     } else {
         const int col0 = n0 + wn * 16 * NJ + (g & 1) * 16 + (g >> 1) * 8;
-        uint16_t* base = static_cast<uint16_t*>(a.C) + (int64_t)(m0 + wm * 128 + r16) * a.ldc + col0;
+        uint16_t* base = static_cast<uint16_t*>(a.C) + (int64_t)(m0 + wm * kWr + r16) * a.ldc + col0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < NI; ++i) {
             __builtin_amdgcn_sched_barrier(0);
-            const bool row_ok = m0 + wm * 128 + i * 16 + r16 < a.M;
+            const bool row_ok = m0 + wm * kWr + i * 16 + r16 < a.M;
             uint16_t* row = base + (int64_t)i * 16 * a.ldc;
             u32x4 vs[NJ / 2];
 #pragma unroll
@@ -364,11 +366,11 @@ __device__ __forceinline__ void zero_acc(f32x4 (&acc)[8][8]) {
 // register allocator keep some of them in vector registers across the K loop
 // and copy them into the accumulator file at every step; starting from a
 // matrix result keeps all of them in the accumulator file.
-template <int AB>
-__device__ __forceinline__ void zero_acc_mma(f32x4 (&acc)[8][8]) {
+template <int AB, int NI = 8>
+__device__ __forceinline__ void zero_acc_mma(f32x4 (&acc)[NI][8]) {
     const half8 z{};
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = mfma16<AB>(z, z, f32x4{});
 }
@@ -661,7 +663,7 @@ struct FragPtrs {
     lds_cchar* tr[8];
 };
 
-template <int KS, int NXK>
+template <int KS, int NXK, int I = 8>
 __device__ __forceinline__ FragPtrs<KS, NXK> frag_ptrs(const u32x4* a_blk, const u32x4* b_blk, int wm, int wn,
                                                         int lane) {
     using L = Lds<KS>;
@@ -669,7 +671,7 @@ __device__ __forceinline__ FragPtrs<KS, NXK> frag_ptrs(const u32x4* a_blk, const
     const int r16 = lane & 15, g = lane >> 4;
 #pragma unroll
     for (int s = 0; s < KS / 32; ++s) {
-        f.a[s] = a_blk + L::slot(wm * 128 + r16, s * 4 + g);
+        f.a[s] = a_blk + L::slot(wm * 16 * I + r16, s * 4 + g);
         f.b[s] = b_blk + L::slot(wn * 128 + r16, s * 4 + g);
     }
     const int krow = 8 * g + (r16 >> 2);
@@ -725,29 +727,33 @@ __device__ __forceinline__ s16x4 frag_b_tr(const FragPtrs<KS, NXK>& f, int so, i
 //    KS * ldb * 2 + 512 bytes for every K.
 // voff[idx] is the row's byte offset plus the chunk's, relative to the
 // tile's resource base; it is the same for every tile.
-template <int KS>
+// An A block of 32 * I rows takes LA = I * CPR / 8 load instructions per
+// step (the first LA of the step), B's 256 rows or columns CPR more.
+template <int KS, int LA = KS / 8>
 struct LaneLoads {
     static constexpr int kCpr = KS / 8;
-    unsigned voff[2 * kCpr];
+    static constexpr int kLa = LA;                    // A loads per step
+    static constexpr int kL = LA + kCpr;              // loads per step
+    unsigned voff[kL];
     unsigned kchunk;      // k offset (elements) of this lane's K-contiguous chunk inside a K step
 };
 
-template <int KS, int NXK>
-__device__ __forceinline__ LaneLoads<KS> lane_loads(const Args& a, int tid) {
+template <int KS, int NXK, int LA = KS / 8>
+__device__ __forceinline__ LaneLoads<KS, LA> lane_loads(const Args& a, int tid) {
     constexpr int kCpr = KS / 8;
-    LaneLoads<KS> p;
+    LaneLoads<KS, LA> p;
     const int r = tid / kCpr;
     const unsigned chunk = (unsigned)((tid % kCpr) ^ Lds<KS>::swz(r));
 #pragma unroll
     for (int j = 0; j < kCpr; ++j) {
         const int row = r + (256 / kCpr) * j;
-        p.voff[j] = (unsigned)row * (unsigned)a.lda * 2u + chunk * 16u;
+        if (j < LA) p.voff[j] = (unsigned)row * (unsigned)a.lda * 2u + chunk * 16u;
         if (NXK) {
-            p.voff[kCpr + j] = (unsigned)row * (unsigned)a.ldb * 2u + chunk * 16u;
+            p.voff[LA + j] = (unsigned)row * (unsigned)a.ldb * 2u + chunk * 16u;
         } else {
             const int krow = 8 * j + (tid >> 5);
             const unsigned c = (unsigned)KnLds::logical(tid & 31, krow);
-            p.voff[kCpr + j] = (unsigned)krow * (unsigned)a.ldb * 2u + c * 16u;
+            p.voff[LA + j] = (unsigned)krow * (unsigned)a.ldb * 2u + c * 16u;
         }
     }
     p.kchunk = chunk * 8u;
@@ -757,14 +763,13 @@ __device__ __forceinline__ LaneLoads<KS> lane_loads(const Args& a, int tid) {
 // Load instruction `idx` (0 .. 2*CPR-1) of a K step into the stage whose A
 // and B blocks are a_blk and b_blk, with the step's scalar offsets (soa for
 // A, sob for B).
-template <int KS, int NXK>
-__device__ __forceinline__ void issue_load(const Rsrc& ra, const Rsrc& rb, const LaneLoads<KS>& p, int idx,
+template <int KS, int NXK, int LA>
+__device__ __forceinline__ void issue_load(const Rsrc& ra, const Rsrc& rb, const LaneLoads<KS, LA>& p, int idx,
                                            unsigned soa, unsigned sob, u32x4* __restrict__ a_blk,
                                            u32x4* __restrict__ b_blk, int wave) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the host pass cannot instantiate these target builtins
-    constexpr int kCpr = KS / 8;
-    const bool isb = idx >= kCpr;
-    const int j = isb ? idx - kCpr : idx;
+    const bool isb = idx >= LA;
+    const int j = isb ? idx - LA : idx;
     const Rsrc& rs = isb ? rb : ra;
     // word 3 = 0x00020000: raw (untyped) access, 32-bit data format
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)rs.base, 0, rs.nrec, 0x00020000);
@@ -799,9 +804,9 @@ __device__ __forceinline__ u32x4 keep_first(const u32x4& v, int nv) {
 // (other rows read the next row past N, which lands in output columns that
 // are never stored). This runs after the lane's loads of the stage have
 // landed and before the barrier that publishes it.
-template <int KS, int NXK>
+template <int KS, int NXK, int LA>
 __device__ __forceinline__ void fix_last_step(u32x4* __restrict__ a_blk, u32x4* __restrict__ b_blk,
-                                              const LaneLoads<KS>& p, const Args& a, int m0, int n0, int k0,
+                                              const LaneLoads<KS, LA>& p, const Args& a, int m0, int n0, int k0,
                                               int tid, int wave, int lane) {
     constexpr int kCpr = KS / 8;
     constexpr int kRowStep = 256 / kCpr;              // rows between a lane's chunks
@@ -815,7 +820,7 @@ __device__ __forceinline__ void fix_last_step(u32x4* __restrict__ a_blk, u32x4* 
         for (int j = 0; j < kCpr; ++j) {
             const int row = r + kRowStep * j;
             const int slot = (j * 4 + wave) * 64 + lane;
-            if (m0 + row < a.M) {
+            if (j < LA && m0 + row < a.M) {
                 if (nv <= 0)
                     a_blk[slot] = u32x4{};
                 else if (m0 + row == a.M - 1)
@@ -850,65 +855,95 @@ __device__ __forceinline__ void fix_last_step(u32x4* __restrict__ a_blk, u32x4* 
 }
 
 // All fragments of slice `s` of stage 0 (used once, before the main loop).
-template <int KS, int NXK>
-__device__ __forceinline__ void read_frags(half8 (&fa)[8], half8 (&fb)[8], const FragPtrs<KS, NXK>& f, int s) {
+template <int KS, int NXK, int I = 8>
+__device__ __forceinline__ void read_frags(half8 (&fa)[I], half8 (&fb)[8], const FragPtrs<KS, NXK>& f, int s) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) fa[i] = frag_a(f, 0, s, i);
+    for (int i = 0; i < I; ++i) fa[i] = frag_a(f, 0, s, i);
 #pragma unroll
     for (int j = 0; j < 8; ++j)
         fb[j] = NXK ? frag_b_kc(f, 0, s, j) : join_halves(frag_b_tr(f, 0, s, j, 0), frag_b_tr(f, 0, s, j, 1));
 }
 
-// One k32 slice: 64 MFMAs (8 x 8 blocks, serpentine by row) on the current
+// One k32 slice: 8 I MFMAs (I x 8 blocks, serpentine by row) on the current
 // fragments, with the next slice's fragment reads (slice next_s of the
-// stage `so` slots from stage 0) and, when LOADS, the 2 * CPR load
-// instructions of one K step placed between them: reads after every
-// even-numbered MFMA, in the order the next slice consumes them (A0, B0..B7,
-// A1..A7; a [k][n] B fragment is two transposing reads), loads spread evenly
-// over the odd-numbered ones. One instruction per MFMA keeps the matrix core
-// fed; with one wave per SIMD every other instruction competes with MFMA
-// issue, so the order is pinned at both the IR and the machine level.
-template <int AB, int KS, int NXK, bool LOADS, bool ZC = false, bool READS = true>
-__device__ __forceinline__ void slice(f32x4 (&acc)[8][8], const half8 (&fa)[8], const half8 (&fb)[8],
-                                      half8 (&na)[8], half8 (&nb)[8], const FragPtrs<KS, NXK>& f, int so,
-                                      int next_s, const Rsrc& ra, const Rsrc& rb, const LaneLoads<KS>& p,
+// stage `so` slots from stage 0) and, when LOADS, the load instructions of
+// one K step placed between them, in the order the next slice consumes them
+// (A0, B0..B7, A1..; a [k][n] B fragment is two transposing reads). With
+// I = 8 (64 MFMAs): reads after every even-numbered MFMA, loads spread evenly
+// over the odd-numbered ones. Other I: the reads and loads together spread
+// evenly over the MFMAs (several after one MFMA when there are more of them
+// than MFMAs), the loads evenly among them. One instruction per MFMA keeps
+// the matrix core fed; with one wave per SIMD every other instruction
+// competes with MFMA issue, so the order is pinned at both the IR and the
+// machine level.
+template <int AB, int KS, int NXK, bool LOADS, bool ZC = false, bool READS = true, int I = 8, int LA = KS / 8>
+__device__ __forceinline__ void slice(f32x4 (&acc)[I][8], const half8 (&fa)[I], const half8 (&fb)[8],
+                                      half8 (&na)[I], half8 (&nb)[8], const FragPtrs<KS, NXK>& f, int so,
+                                      int next_s, const Rsrc& ra, const Rsrc& rb, const LaneLoads<KS, LA>& p,
                                       unsigned soa, unsigned sob, u32x4* __restrict__ ld_a, u32x4* __restrict__ ld_b,
                                       int wave) {
-    constexpr int kLps = KS / 4;
     constexpr int kNb = NXK ? 8 : 16;              // B read instructions
-    constexpr int kReads = 8 + kNb;
-    constexpr int kGap = 64 / kLps;                // MFMAs per load
-    static_assert(2 * kReads <= 64, "reads must fit the even MFMA slots");
+    constexpr int kReads = I + kNb;
     s16x4 lo[8];
-#pragma unroll
-    for (int q = 0; q < 64; ++q) {
-        // serpentine over the 8 x 8 blocks: a row change keeps the B fragment,
-        // so one operand changes per MFMA throughout (less switching power)
-        const int i = q >> 3, j = (i & 1) ? 7 - (q & 7) : (q & 7);
-        // ZC: a tile's first slice starts the sums from zero (inline constant C)
-        acc[i][j] = mfma16<AB>(fb[j], fa[i], ZC ? f32x4{} : acc[i][j]);
-        if (READS && (q & 1) == 0 && q / 2 < kReads) {
-            const int rq = q / 2;
-            if (rq >= 1 && rq <= kNb) {
-                if (NXK) {
-                    nb[rq - 1] = frag_b_kc(f, so, next_s, rq - 1);
-                } else {
-                    const int blk = (rq - 1) >> 1, hh = (rq - 1) & 1;
-                    const s16x4 v = frag_b_tr(f, so, next_s, blk, hh);
-                    if (hh == 0)
-                        lo[blk] = v;
-                    else
-                        nb[blk] = join_halves(lo[blk], v);
-                }
+    // read number rq of the next slice's fragments (consumption order)
+    auto read = [&](int rq) {
+        if (rq >= 1 && rq <= kNb) {
+            if (NXK) {
+                nb[rq - 1] = frag_b_kc(f, so, next_s, rq - 1);
             } else {
-                const int ai = rq == 0 ? 0 : rq - kNb;
-                na[ai] = frag_a(f, so, next_s, ai);
+                const int blk = (rq - 1) >> 1, hh = (rq - 1) & 1;
+                const s16x4 v = frag_b_tr(f, so, next_s, blk, hh);
+                if (hh == 0)
+                    lo[blk] = v;
+                else
+                    nb[blk] = join_halves(lo[blk], v);
             }
-        } else if (LOADS && q % kGap == kGap - 1) {
-            issue_load<KS, NXK>(ra, rb, p, q / kGap, soa, sob, ld_a, ld_b, wave);
+        } else {
+            const int ai = rq == 0 ? 0 : rq - kNb;
+            na[ai] = frag_a(f, so, next_s, ai);
         }
-        TG_COMPILER_FENCE();
-        __builtin_amdgcn_sched_barrier(0);
+    };
+    if constexpr (I == 8) {
+        constexpr int kLps = KS / 4;
+        constexpr int kGap = 64 / kLps;                // MFMAs per load
+        static_assert(2 * kReads <= 64, "reads must fit the even MFMA slots");
+        static_assert(LA == KS / 8, "a 256-row A block takes CPR loads");
+#pragma unroll
+        for (int q = 0; q < 64; ++q) {
+            // serpentine over the 8 x 8 blocks: a row change keeps the B fragment,
+            // so one operand changes per MFMA throughout (less switching power)
+            const int i = q >> 3, j = (i & 1) ? 7 - (q & 7) : (q & 7);
+            // ZC: a tile's first slice starts the sums from zero (inline constant C)
+            acc[i][j] = mfma16<AB>(fb[j], fa[i], ZC ? f32x4{} : acc[i][j]);
+            if (READS && (q & 1) == 0 && q / 2 < kReads) {
+                read(q / 2);
+            } else if (LOADS && q % kGap == kGap - 1) {
+                issue_load<KS, NXK>(ra, rb, p, q / kGap, soa, sob, ld_a, ld_b, wave);
+            }
+            TG_COMPILER_FENCE();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    } else {
+        constexpr int kQ = 8 * I;                      // MFMAs
+        constexpr int kR = READS ? kReads : 0;
+        constexpr int kLd = LOADS ? LaneLoads<KS, LA>::kL : 0;
+        constexpr int kT = kR + kLd;                   // instructions placed between them
+#pragma unroll
+        for (int q = 0; q < kQ; ++q) {
+            const int i = q >> 3, j = (i & 1) ? 7 - (q & 7) : (q & 7);
+            acc[i][j] = mfma16<AB>(fb[j], fa[i], ZC ? f32x4{} : acc[i][j]);
+#pragma unroll
+            for (int e = q * kT / kQ; e < (q + 1) * kT / kQ; ++e) {
+                const int before = kT ? e * kLd / kT : 0;       // loads among events 0 .. e-1
+                if (kT && (e + 1) * kLd / kT > before)
+                    issue_load<KS, NXK>(ra, rb, p, before, soa, sob, ld_a, ld_b, wave);
+                else
+                    read(e - before);
+                TG_COMPILER_FENCE();
+            }
+            TG_COMPILER_FENCE();
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
 }
 
@@ -922,12 +957,12 @@ struct Tile {
     int m0, n0;
 };
 
-template <int NXK>
+template <int NXK, int TBM = BM>
 __device__ __forceinline__ Tile make_tile(const Args& a, int wid) {
     int tm, tn;
     tile_of(wid, a.W, a.grid_m, a.grid_n, a.group_m, a.num_xcd, &tm, &tn);
     Tile t;
-    t.m0 = tm * BM;
+    t.m0 = tm * TBM;
     t.n0 = tn * BN;
     t.ra = operand_rsrc(a.A, a.lda, a.M, a.K, t.m0);
     // B: N x K rows n0.. ; K x N columns n0.. of all K rows
@@ -956,20 +991,29 @@ __device__ __forceinline__ Rsrc b_step_rsrc(const Tile& t, int d, int64_t ldb) {
     return Rsrc{t.rb.base + rows * ldb, (int)span};
 }
 
-// Per-workgroup constants of the direct-to-LDS kernel. LDS holds the S
-// stages' A blocks, then their B blocks.
-template <int KS, int NXK, int S>
+// Per-workgroup constants of the direct-to-LDS kernel. With 256-row A
+// blocks (I = 8) LDS holds the S stages' A blocks, then their B blocks; with
+// smaller A blocks each stage holds its A block then its B block. Either way
+// stage st's blocks sit st * kShift slots after stage 0's.
+template <int KS, int NXK, int S, int I = 8>
 struct DmaCtx {
-    LaneLoads<KS> p;
+    static constexpr int kLa = I * (KS / 8) / 8;                    // A loads per step
+    static constexpr int kABlk = 32 * I * (KS / 8);                 // slots of an A block
+    static constexpr int kBBlk = Lds<KS>::kBlock;                   // slots of a B block (256 rows / columns)
+    static constexpr int kShift = I == 8 ? kBBlk : kABlk + kBBlk;   // slots between stages
+    static constexpr int kSlots = S * (kABlk + kBBlk);
+    LaneLoads<KS, kLa> p;
     unsigned bstep;       // scalar-offset advance of B per K step (B stored N x K; K x N rebases instead)
     int nk, klast;        // K steps per tile; first k of a tile's last step
     int lead;             // leading empty steps (0 or 1): data step of step t is t - lead
     bool fixup;           // a tile's last step needs fix_last_step
-    int tid, wave, lane;
+    int tid, wave, lane;  // of the loading waves (the producers' own numbering with PC)
     u32x4* smem;
     FragPtrs<KS, NXK> fp; // read positions in stage 0
-    __device__ __forceinline__ u32x4* a_blk(int st) const { return smem + st * Lds<KS>::kBlock; }
-    __device__ __forceinline__ u32x4* b_blk(int st) const { return smem + (S + st) * Lds<KS>::kBlock; }
+    __device__ __forceinline__ u32x4* a_blk(int st) const { return smem + st * kShift; }
+    __device__ __forceinline__ u32x4* b_blk(int st) const {
+        return I == 8 ? smem + (S + st) * kBBlk : smem + st * kShift + kABlk;
+    }
 };
 
 // K step t of tile tc, in stage st (FIRST: the tile's first step, whose
@@ -986,50 +1030,87 @@ struct DmaCtx {
 // stage on return; they are derived once per step, before the barrier wait,
 // into registers no matrix instruction reads (a vector ALU write into a
 // just-read MFMA operand register stalls the matrix cores).
-template <int AB, int NXK, int KS, int S, int F0, bool FIRST = false, bool LAST = false>
-__device__ __forceinline__ void dma_step(f32x4 (&acc)[8][8], half8 (&fa)[2][8], half8 (&fb)[2][8], int st, int t,
-                                         const Args& a, const DmaCtx<KS, NXK, S>& c, FragPtrs<KS, NXK>& cur,
+// CONSUMER (producer/consumer workgroups): the step without its loads, wait
+// counts or fix-up, which the producer waves do (producer_step).
+template <int AB, int NXK, int KS, int S, int F0, bool FIRST = false, bool LAST = false, int I = 8,
+          bool CONSUMER = false>
+__device__ __forceinline__ void dma_step(f32x4 (&acc)[I][8], half8 (&fa)[2][I], half8 (&fb)[2][8], int st, int t,
+                                         const Args& a, const DmaCtx<KS, NXK, S, I>& c, FragPtrs<KS, NXK>& cur,
                                          const Tile& tc, const Tile& tn, bool has_next) {
-    using L = Lds<KS>;
+    using Ctx = DmaCtx<KS, NXK, S, I>;
     constexpr int kSlices = KS / 32;
-    constexpr int kLps = KS / 4;
+    constexpr int kL = Ctx::kLa + KS / 8;             // loads per step
     constexpr int FL = (F0 + kSlices - 1) & 1;       // buffer of the last slice
     const int nst = (st + 1 == S) ? 0 : st + 1;
     static_assert(!FIRST || kSlices > 1, "the zero-start slice is the first of a 2-slice step");
 #pragma unroll
     for (int s = 0; s + 1 < kSlices; ++s) {
         if (FIRST && s == 0)
-            slice<AB, KS, NXK, false, true>(acc, fa[F0 & 1], fb[F0 & 1], fa[(F0 + 1) & 1], fb[(F0 + 1) & 1], cur, 0,
-                                        1, tc.ra, tc.rb, c.p, 0u, 0u, c.smem, c.smem, c.wave);
+            slice<AB, KS, NXK, false, true, true, I>(acc, fa[F0 & 1], fb[F0 & 1], fa[(F0 + 1) & 1], fb[(F0 + 1) & 1],
+                                                    cur, 0, 1, tc.ra, tc.rb, c.p, 0u, 0u, c.smem, c.smem, c.wave);
         else
-            slice<AB, KS, NXK, false>(acc, fa[(F0 + s) & 1], fb[(F0 + s) & 1], fa[(F0 + s + 1) & 1],
-                                  fb[(F0 + s + 1) & 1], cur, 0, s + 1, tc.ra, tc.rb, c.p, 0u, 0u, c.smem, c.smem,
-                                  c.wave);
+            slice<AB, KS, NXK, false, false, true, I>(acc, fa[(F0 + s) & 1], fb[(F0 + s) & 1], fa[(F0 + s + 1) & 1],
+                                                     fb[(F0 + s + 1) & 1], cur, 0, s + 1, tc.ra, tc.rb, c.p, 0u, 0u,
+                                                     c.smem, c.smem, c.wave);
     }
-    cur = shifted(c.fp, nst * L::kBlock);
-    // the step these loads are for (uniform: scalar selects)
+    cur = shifted(c.fp, nst * Ctx::kShift);
+    if constexpr (CONSUMER) {
+        TG_COMPILER_FENCE();
+        __builtin_amdgcn_sched_barrier(0);
+        wait_lgkmcnt0();                              // this wave's reads of stage st returned
+        block_barrier();                              // the producers published step t + 1
+        slice<AB, KS, NXK, false, false, !LAST, I>(acc, fa[FL], fb[FL], fa[FL ^ 1], fb[FL ^ 1], cur, 0, 0, tc.ra,
+                                                  tc.rb, c.p, 0u, 0u, c.smem, c.smem, c.wave);
+    } else {
+        // the step these loads are for (uniform: scalar selects)
+        const int tl = t + S;
+        const bool in_next = tl >= c.nk;
+        const int ls = in_next ? tl - c.nk : tl;
+        const bool live = !in_next || has_next;
+        const int ld = KS == 32 ? ls - c.lead : ls;      // >= 0: tl >= S > lead
+        const unsigned soa = live ? (unsigned)ld * (unsigned)(KS * 2) : kOob;
+        const unsigned sob = live ? (NXK ? (unsigned)ld * c.bstep : 0u) : kOob;
+        const Rsrc lra = in_next ? tn.ra : tc.ra;
+        const Rsrc lrb = b_step_rsrc<KS, NXK>(in_next ? tn : tc, live ? ld : 0, a.ldb);
+        TG_COMPILER_FENCE();
+        __builtin_amdgcn_sched_barrier(0);
+        wait_lgkmcnt0();                                  // this wave's reads of stage st returned
+        wait_vmcnt<(S - 2) * kL>();                       // step t + 1 landed
+        // rare (once per tile at most): laid out of line, so that an ordinary step
+        // falls through to its last slice and the step loop takes one branch per
+        // step, its back edge (+0.9% at 8192^3)
+        if (__builtin_expect(c.fixup && t + 2 == c.nk, 0))
+            fix_last_step<KS, NXK>(c.a_blk(nst), c.b_blk(nst), c.p, a, tc.m0, tc.n0, c.klast, c.tid, c.wave, c.lane);
+        block_barrier();
+        // the loads go into the stage just released
+        slice<AB, KS, NXK, true, false, !LAST, I>(acc, fa[FL], fb[FL], fa[FL ^ 1], fb[FL ^ 1], cur, 0, 0, lra, lrb,
+                                                 c.p, soa, sob, c.a_blk(st), c.b_blk(st), c.wave);
+    }
+}
+
+// A producer wave's part of K step t (producer/consumer workgroups, one tile
+// per workgroup): wait for its own loads of step t + 1, fix up a partial last
+// step, meet the consumers at the step's barrier (which publishes step t + 1
+// and releases stage st), then load step t + S into stage st.
+template <int NXK, int KS, int S, int I>
+__device__ __forceinline__ void producer_step(int st, int t, const Args& a, const DmaCtx<KS, NXK, S, I>& c,
+                                              const Tile& tc) {
+    using Ctx = DmaCtx<KS, NXK, S, I>;
+    constexpr int kL = Ctx::kLa + KS / 8;
+    const int nst = (st + 1 == S) ? 0 : st + 1;
     const int tl = t + S;
-    const bool in_next = tl >= c.nk;
-    const int ls = in_next ? tl - c.nk : tl;
-    const bool live = !in_next || has_next;
-    const int ld = KS == 32 ? ls - c.lead : ls;      // >= 0: tl >= S > lead
+    const bool live = tl < c.nk;
+    const int ld = KS == 32 ? tl - c.lead : tl;
     const unsigned soa = live ? (unsigned)ld * (unsigned)(KS * 2) : kOob;
     const unsigned sob = live ? (NXK ? (unsigned)ld * c.bstep : 0u) : kOob;
-    const Rsrc lra = in_next ? tn.ra : tc.ra;
-    const Rsrc lrb = b_step_rsrc<KS, NXK>(in_next ? tn : tc, live ? ld : 0, a.ldb);
-    TG_COMPILER_FENCE();
-    __builtin_amdgcn_sched_barrier(0);
-    wait_lgkmcnt0();                                  // this wave's reads of stage st returned
-    wait_vmcnt<(S - 2) * kLps>();                     // step t + 1 landed
-    // rare (once per tile at most): laid out of line, so that an ordinary step
-    // falls through to its last slice and the step loop takes one branch per
-    // step, its back edge (+0.9% at 8192^3)
+    const Rsrc lrb = b_step_rsrc<KS, NXK>(tc, live ? ld : 0, a.ldb);
+    wait_vmcnt<(S - 2) * kL>();                       // step t + 1 landed
     if (__builtin_expect(c.fixup && t + 2 == c.nk, 0))
         fix_last_step<KS, NXK>(c.a_blk(nst), c.b_blk(nst), c.p, a, tc.m0, tc.n0, c.klast, c.tid, c.wave, c.lane);
     block_barrier();
-    // the loads go into the stage just released
-    slice<AB, KS, NXK, true, false, !LAST>(acc, fa[FL], fb[FL], fa[FL ^ 1], fb[FL ^ 1], cur, 0, 0, lra, lrb, c.p,
-                                       soa, sob, c.a_blk(st), c.b_blk(st), c.wave);
+#pragma unroll
+    for (int idx = 0; idx < kL; ++idx)
+        issue_load<KS, NXK>(tc.ra, lrb, c.p, idx, soa, sob, c.a_blk(st), c.b_blk(st), c.wave);
 }
 
 // The steps 0 .. nk-1 (an even count) of a one-slice ring, in pairs: such
@@ -1038,15 +1119,15 @@ __device__ __forceinline__ void dma_step(f32x4 (&acc)[8][8], half8 (&fa)[2][8], 
 // path into store_c (an odd step taken apart from the pairs) made the register
 // allocator split the accumulators between the two register files and move
 // them every step.
-template <int AB, int NXK, int S>
-__device__ __forceinline__ void step_pairs(f32x4 (&acc)[8][8], half8 (&fa)[2][8], half8 (&fb)[2][8],
-                                           const Args& a, const DmaCtx<32, NXK, S>& c, FragPtrs<32, NXK>& cur,
+template <int AB, int NXK, int S, int I = 8, bool CONSUMER = false>
+__device__ __forceinline__ void step_pairs(f32x4 (&acc)[I][8], half8 (&fa)[2][I], half8 (&fb)[2][8],
+                                           const Args& a, const DmaCtx<32, NXK, S, I>& c, FragPtrs<32, NXK>& cur,
                                            const Tile& tc) {
     int st = 0;
     for (int t = 0; t < c.nk; t += 2) {
-        dma_step<AB, NXK, 32, S, 0>(acc, fa, fb, st, t, a, c, cur, tc, tc, false);
+        dma_step<AB, NXK, 32, S, 0, false, false, I, CONSUMER>(acc, fa, fb, st, t, a, c, cur, tc, tc, false);
         st = (st + 1 == S) ? 0 : st + 1;
-        dma_step<AB, NXK, 32, S, 1>(acc, fa, fb, st, t + 1, a, c, cur, tc, tc, false);
+        dma_step<AB, NXK, 32, S, 1, false, false, I, CONSUMER>(acc, fa, fb, st, t + 1, a, c, cur, tc, tc, false);
         st = (st + 1 == S) ? 0 : st + 1;
     }
 }
@@ -1054,7 +1135,10 @@ __device__ __forceinline__ void step_pairs(f32x4 (&acc)[8][8], half8 (&fa)[2][8]
 // Tile kernel with both operands streamed straight into an S-stage LDS ring
 // of KS-deep K steps (KS / 32 slices each): A K-contiguous, B either
 // K-contiguous (stored N x K, NXK = 1) or kept [k][n] and transposed on read
-// (stored K x N). Workgroup b computes tiles b, b + grid, ... (grid = the
+// (stored K x N). The tile is 32 I x 256 (I = 8: 256 x 256, one workgroup
+// per compute unit; I = 4 or 2: 128 x 256 or 64 x 256, two per compute unit),
+// four waves in a 2 x 2 grid, each 16 I x 128 as I x 8 blocks of 16 x 16.
+// Workgroup b computes tiles b, b + grid, ... (grid = the
 // workgroups launched: one per compute unit for 64-deep steps, else one per
 // tile). Its K steps form one stream across those tiles; step g lives in
 // stage g mod S. The barrier of a step sits before its last slice: it
@@ -1067,22 +1151,33 @@ __device__ __forceinline__ void step_pairs(f32x4 (&acc)[8][8], half8 (&fa)[2][8]
 // same number of loads (steps past the last tile, and the leading step of an
 // odd 32-deep step count, read nothing and write zeros), so all wait counts
 // are constants.
-template <int TY, int NXK, int KS, int S>
-__global__ void __launch_bounds__(NTHREADS)
-__attribute__((amdgpu_waves_per_eu(1, 1)))
+// PC (producer/consumer, page 5's warp specialisation: one tile per
+// workgroup, 32-deep steps, I = 4): eight waves, two per SIMD; waves 0-3
+// compute as above but issue no loads and wait on nothing but their own LDS
+// reads and the step barrier; waves 4-7 issue every load, wait for them, fix
+// up a partial last step and meet the consumers at the same barriers.
+template <int TY, int NXK, int KS, int S, int I = 8, bool PC = false>
+__global__ void __launch_bounds__(PC ? 2 * NTHREADS : NTHREADS)
+__attribute__((amdgpu_waves_per_eu((I == 8 && !PC) ? 1 : 2, (I == 8 && !PC) ? 1 : 2)))
 tgemm_dma_kernel(Args a) {
     constexpr int AB = ab_of(TY);
-    using L = Lds<KS>;
+    using Ctx = DmaCtx<KS, NXK, S, I>;
     static_assert(KS == 64 || KS == 32, "K step");
     static_assert(KS == 32 || S == 2, "64-deep steps use a 2-stage ring");
-    static_assert(S >= 2 && S <= 5 && 2 * S * L::kBlock * 16 <= 160 * 1024, "LDS ring must fit 160 KiB");
-    constexpr int kLps = KS / 4;                      // load instructions per step per wave
-    __shared__ u32x4 smem[2 * S * L::kBlock];
+    static_assert(I == 8 || I == 4 || I == 2, "A blocks of 256, 128 or 64 rows");
+    static_assert(Ctx::kLa >= 1, "the A block takes at least one load per step");
+    static_assert(!PC || (KS == 32 && I == 4), "producer/consumer workgroups: 32-deep steps, 128 x 256 tiles");
+    static_assert(S >= 2 && S <= 6 && Ctx::kSlots * 16 <= 160 * 1024, "LDS ring must fit 160 KiB");
+    static_assert(I == 8 || PC || Ctx::kSlots * 16 <= 80 * 1024, "two workgroups per compute unit");
+    constexpr int kL = Ctx::kLa + KS / 8;             // load instructions per step per loading wave
+    constexpr int kBm = 32 * I;                       // tile rows
+    __shared__ u32x4 smem[Ctx::kSlots];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const bool producer = PC && wave >= 4;
+    const int wm = PC ? (wave & 3) >> 1 : wave >> 1, wn = wave & 1;
     const int nkd = (a.K + KS - 1) / KS;              // K steps holding data
     // 32-deep steps go in pairs: an odd count gets one leading step whose
     // loads all fall out of range (zeros), so that every tile runs one loop
@@ -1090,42 +1185,70 @@ tgemm_dma_kernel(Args a) {
     const int nk = nkd + lead;
 
     int wid = (int)blockIdx.x;
-    Tile tc = make_tile<NXK>(a, wid);
+    Tile tc = make_tile<NXK, kBm>(a, wid);
     bool has_next = wid + a.grid < a.W;              // K == 0: one tile per workgroup
-    Tile tn = has_next ? make_tile<NXK>(a, wid + a.grid) : tc;
-    f32x4 acc[8][8];
-    if (KS == 32) zero_acc_mma<AB>(acc);
+    Tile tn = has_next ? make_tile<NXK, kBm>(a, wid + a.grid) : tc;
+    f32x4 acc[I][8];
+    if (KS == 32) zero_acc_mma<AB, I>(acc);
 
-    DmaCtx<KS, NXK, S> c;
-    c.p = lane_loads<KS, NXK>(a, tid);
+    Ctx c;
+    const int ltid = PC ? tid - NTHREADS : tid;       // numbering of the loading waves
+    const int lwave = PC ? wave - 4 : wave;
+    c.p = lane_loads<KS, NXK, Ctx::kLa>(a, ltid);
     c.bstep = (unsigned)(KS * 2);
     c.nk = nk;
     c.lead = lead;
     c.klast = (nkd - 1) * KS;
     c.fixup = (a.K % KS) != 0 || (!NXK && (a.N % 8) != 0);
-    c.tid = tid;
-    c.wave = wave;
+    c.tid = ltid;
+    c.wave = lwave;
     c.lane = lane;
     c.smem = smem;
-    c.fp = frag_ptrs<KS, NXK>(c.a_blk(0), c.b_blk(0), wm, wn, lane);
-    half8 fa[2][8], fb[2][8];
-    if (nk > 0) {
-        // prologue: steps 0 .. S-1 of the first tile (a workgroup with more
-        // than one tile has nk >= S); step t holds data step t - lead
-        for (int t = 0; t < S; ++t) {
-            const int d = t - lead;                   // data step
-            const bool live = d >= 0 && t < nk;
-            for (int idx = 0; idx < kLps; ++idx)
-                issue_load<KS, NXK>(tc.ra, b_step_rsrc<KS, NXK>(tc, live ? d : 0, a.ldb), c.p, idx,
-                                    live ? (unsigned)d * (unsigned)(KS * 2) : kOob,
-                                    live ? (NXK ? (unsigned)d * c.bstep : 0u) : kOob, c.a_blk(t), c.b_blk(t),
-                                    wave);
+    c.fp = frag_ptrs<KS, NXK, I>(c.a_blk(0), c.b_blk(0), wm, wn, lane);
+    if (producer) {
+        if (nk > 0) {
+            for (int t = 0; t < S; ++t) {
+                const int d = t - lead;
+                const bool live = d >= 0 && t < nk;
+                for (int idx = 0; idx < kL; ++idx)
+                    issue_load<KS, NXK>(tc.ra, b_step_rsrc<KS, NXK>(tc, live ? d : 0, a.ldb), c.p, idx,
+                                        live ? (unsigned)d * (unsigned)(KS * 2) : kOob,
+                                        live ? (NXK ? (unsigned)d * c.bstep : 0u) : kOob, c.a_blk(t), c.b_blk(t),
+                                        lwave);
+            }
+            wait_vmcnt<(S - 1) * kL>();               // step 0 landed
+            if (c.fixup && nk == 1)
+                fix_last_step<KS, NXK>(c.a_blk(0), c.b_blk(0), c.p, a, tc.m0, tc.n0, c.klast, ltid, lwave, lane);
+            block_barrier();
+            int st = 0;
+            for (int t = 0; t < nk; ++t) {
+                producer_step<NXK, KS, S, I>(st, t, a, c, tc);
+                st = (st + 1 == S) ? 0 : st + 1;
+            }
         }
-        wait_vmcnt<(S - 1) * kLps>();                 // step 0 landed
-        if (c.fixup && nk == 1)
-            fix_last_step<KS, NXK>(c.a_blk(0), c.b_blk(0), c.p, a, tc.m0, tc.n0, c.klast, tid, wave, lane);
+        wait_vmcnt<0>();                              // no load may still be writing LDS at exit
+        return;
+    }
+    half8 fa[2][I], fb[2][8];
+    if (nk > 0) {
+        if constexpr (!PC) {
+            // prologue: steps 0 .. S-1 of the first tile (a workgroup with more
+            // than one tile has nk >= S); step t holds data step t - lead
+            for (int t = 0; t < S; ++t) {
+                const int d = t - lead;                   // data step
+                const bool live = d >= 0 && t < nk;
+                for (int idx = 0; idx < kL; ++idx)
+                    issue_load<KS, NXK>(tc.ra, b_step_rsrc<KS, NXK>(tc, live ? d : 0, a.ldb), c.p, idx,
+                                        live ? (unsigned)d * (unsigned)(KS * 2) : kOob,
+                                        live ? (NXK ? (unsigned)d * c.bstep : 0u) : kOob, c.a_blk(t), c.b_blk(t),
+                                        wave);
+            }
+            wait_vmcnt<(S - 1) * kL>();                   // step 0 landed
+            if (c.fixup && nk == 1)
+                fix_last_step<KS, NXK>(c.a_blk(0), c.b_blk(0), c.p, a, tc.m0, tc.n0, c.klast, tid, wave, lane);
+        }
         block_barrier();
-        read_frags<KS, NXK>(fa[0], fb[0], c.fp, 0);
+        read_frags<KS, NXK, I>(fa[0], fb[0], c.fp, 0);
     }
     FragPtrs<KS, NXK> cur = c.fp;                     // read positions of the current stage
     if constexpr (KS == 64) {
@@ -1137,26 +1260,26 @@ tgemm_dma_kernel(Args a) {
         // (64-deep steps are used with nk >= 2)
         int st = 0;
         for (;;) {
-            dma_step<AB, NXK, KS, S, 0, true>(acc, fa, fb, st, 0, a, c, cur, tc, tn, has_next);
+            dma_step<AB, NXK, KS, S, 0, true, false, I>(acc, fa, fb, st, 0, a, c, cur, tc, tn, has_next);
             st ^= 1;
             for (int t = 1; t + 1 < nk; ++t) {
-                dma_step<AB, NXK, KS, S, 0>(acc, fa, fb, st, t, a, c, cur, tc, tn, has_next);
+                dma_step<AB, NXK, KS, S, 0, false, false, I>(acc, fa, fb, st, t, a, c, cur, tc, tn, has_next);
                 st ^= 1;
             }
-            dma_step<AB, NXK, KS, S, 0, false, true>(acc, fa, fb, st, nk - 1, a, c, cur, tc, tn, has_next);
+            dma_step<AB, NXK, KS, S, 0, false, true, I>(acc, fa, fb, st, nk - 1, a, c, cur, tc, tn, has_next);
             st ^= 1;
-            store_c<TY>(acc, a, tc.m0, tc.n0, wm, wn, lane);
+            store_c<TY, 8, I>(acc, a, tc.m0, tc.n0, wm, wn, lane);
             if (!has_next) break;
-            read_frags<KS, NXK>(fa[0], fb[0], cur, 0);   // the next tile's first fragments
+            read_frags<KS, NXK, I>(fa[0], fb[0], cur, 0);   // the next tile's first fragments
             wid += a.grid;
             tc = tn;
             has_next = wid + a.grid < a.W;
-            if (has_next) tn = make_tile<NXK>(a, wid + a.grid);
+            if (has_next) tn = make_tile<NXK, kBm>(a, wid + a.grid);
         }
     } else {
         // one tile per workgroup, its steps (an even count) in pairs
-        step_pairs<AB, NXK, S>(acc, fa, fb, a, c, cur, tc);
-        store_c<TY>(acc, a, tc.m0, tc.n0, wm, wn, lane);
+        step_pairs<AB, NXK, S, I, PC>(acc, fa, fb, a, c, cur, tc);
+        store_c<TY, 8, I>(acc, a, tc.m0, tc.n0, wm, wn, lane);
     }
     // no load may still be writing this workgroup's LDS when it exits
     wait_vmcnt<0>();

@@ -32,6 +32,10 @@ constexpr int kDefaultNumXcd = 8;        // MI355X: 8 accelerator dies of 32 CUs
 // K step 64, 32 KiB at K step 32). 64-deep steps take a 2-stage ring.
 constexpr int kDefaultDmaKStep = 64;
 constexpr int kDefaultDmaStages32 = 4;     // ring depth when the K step is 32
+// Tiles of 128 or 64 rows (x 256 columns) run two workgroups per compute
+// unit: 32-deep steps in a ring of at most 80 KiB (3 stages by default).
+constexpr int kDefaultSmallStages = 3;
+constexpr int kProducerWaves = 4;          // producer/consumer workgroups: 4 + 4 waves
 // Automatic launches of 16-bit operands with B stored K x N, K not a multiple
 // of 64 and no more tiles than compute units take 32-deep steps (default ring
 // depth, built for every type combination): measured 2-4% ahead of the
@@ -81,7 +85,10 @@ struct Plan {
     int c_type;        // TGEMM_F16, TGEMM_BF16 or TGEMM_F32
     bool epi;          // scale, bias or activation requested (else C = A * B as it is)
     int variant;       // kVecAB | kVecC | kLayoutNxK | kDma bits
+    int bm;            // tile rows of the launched kernel (BM, or 128 / 64 for the small tiles)
     int bn;            // tile columns of the launched kernel (BN, or kF32PipeBn)
+    int producers;     // producer waves per workgroup (0, or kProducerWaves)
+    int threads;       // threads per workgroup
     int grid_m, grid_n, W;
     int group_m, num_xcd;
     int k_step, stages;   // K step per LDS stage and ring depth of the launched kernel
@@ -110,11 +117,13 @@ inline bool overlaps(const void* p, uint64_t pn, const void* q, uint64_t qn) {
 
 // ab_type / c_type: element types; bias: N floats or null; alpha and act as
 // in tgemm_gemm (epi: alpha != 1, a bias or an activation).
+// tile_m: 0 (automatic: 256), 256, 128 or 64 tile rows; producers: 0, or 4
+// (producer/consumer workgroups, 128-row tiles).
 inline int make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
                      int64_t ldb, int b_layout, void* C, int64_t ldc, int force_generic,
                      int group_m, int num_xcd, int k_step, int stages, Plan* pl,
                      int ab_type = TGEMM_F16, int c_type = TGEMM_F16, const void* bias = nullptr,
-                     bool epi = false) {
+                     bool epi = false, int tile_m = 0, int producers = 0) {
     const int64_t kMaxDim = 2147483647;
     if (M < 0 || N < 0 || K < 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim)
         return TGEMM_ERR_INVALID;
@@ -128,6 +137,15 @@ inline int make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
     if (k_step != 0 && k_step != 32 && k_step != 64) return TGEMM_ERR_INVALID;
     if (stages != 0 && (stages < 2 || stages > 5)) return TGEMM_ERR_INVALID;
     if (k_step == 64 && stages != 0 && stages != 2) return TGEMM_ERR_INVALID;  // 2 x 64 KiB fills LDS
+    if (tile_m != 0 && tile_m != 256 && tile_m != 128 && tile_m != 64) return TGEMM_ERR_INVALID;
+    if (producers != 0 && producers != kProducerWaves) return TGEMM_ERR_INVALID;
+    if (producers && tile_m != 0 && tile_m != 128) return TGEMM_ERR_INVALID;
+    const int bm = producers ? 128 : (tile_m ? tile_m : BM);
+    // smaller tiles and producer/consumer workgroups: 32-deep steps, and a
+    // ring of at most 80 KiB per workgroup (two per compute unit) for the
+    // small tiles
+    if (bm != BM && k_step == 64) return TGEMM_ERR_INVALID;
+    if (bm != BM && !producers && stages > 3) return TGEMM_ERR_INVALID;
     const int64_t one = 1;
     if (lda < (K > one ? K : one)) return TGEMM_ERR_INVALID;
     const int64_t bmin = (b_layout == TGEMM_B_KxN) ? N : K;
@@ -151,7 +169,7 @@ inline int make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
     if (overlaps(C, nc, bias, nbias)) return TGEMM_ERR_INVALID;
 
     // tile grid: fixed below once the kernel (and its tile width) is known
-    const int64_t gm = (M + BM - 1) / BM;
+    const int64_t gm = (M + bm - 1) / bm;
 
     pl->M = (int)M;
     pl->N = (int)N;
@@ -199,13 +217,19 @@ inline int make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
     } else if (dma) {
         // a ring deeper than 2 stages implies 32-deep steps; 64-deep steps
         // need at least two steps
-        pl->k_step = k_step ? k_step : ((stages > 2 || K <= 64) ? 32 : kDefaultDmaKStep);
+        pl->k_step = k_step ? k_step : ((stages > 2 || K <= 64 || bm != BM) ? 32 : kDefaultDmaKStep);
         if (pl->k_step == 64 && K <= 64) return TGEMM_ERR_INVALID;
-        pl->stages = pl->k_step == 64 ? 2 : (stages ? stages : kDefaultDmaStages32);
+        pl->stages = pl->k_step == 64 ? 2 : (stages ? stages : (bm != BM ? kDefaultSmallStages : kDefaultDmaStages32));
     } else {
         pl->k_step = BK;
         pl->stages = 2;
     }
+    // the small tiles and producer/consumer workgroups exist on the
+    // direct-to-LDS path only (16-bit operands)
+    if (bm != BM && !(dma && ab_type != TGEMM_F32)) return TGEMM_ERR_UNSUPPORTED;
+    pl->bm = bm;
+    pl->producers = producers;
+    pl->threads = NTHREADS + producers * 64;
     pl->bn = (ab_type == TGEMM_F32 && dma) ? kF32PipeBn : BN;
     const int64_t gn = (N + pl->bn - 1) / pl->bn;
     if (gm * gn > kMaxDim) return TGEMM_ERR_UNSUPPORTED;

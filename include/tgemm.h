@@ -108,11 +108,23 @@ int tgemm_f16(int64_t M, int64_t N, int64_t K,
  *                  0 = default (64, or 32 when stages > 2 or K <= 64),
  *                  32 or 64 (64 needs K > 64).
  *   stages:        LDS ring depth of that path: 0 = default (2 at k_step 64,
- *                  4 at k_step 32), 2..5 (k_step 64 allows only 2). Other
- *                  paths ignore k_step and stages. With every launch choice
- *                  0 and no tuned choice recorded, 16-bit operands with B
- *                  stored K x N, K > 64 not a multiple of 64 and at most one
- *                  tile per compute unit run at k_step 32 (default depth).
+ *                  4 at k_step 32, 3 for the smaller tiles), 2..5 (k_step
+ *                  64 allows only 2; the smaller tiles 2..3, producer/
+ *                  consumer workgroups 3..6). Other paths ignore k_step and
+ *                  stages. With every launch choice 0 and no tuned choice
+ *                  recorded, 16-bit operands with B stored K x N, K > 64
+ *                  not a multiple of 64 and at most one tile per compute
+ *                  unit run at k_step 32 (default depth).
+ *   tile_m:        output tile rows of that path (page 2, section 7.4 tunes
+ *                  the tile shape): 0 = default (256), 256, 128 or 64. Tiles
+ *                  of 128 or 64 rows (x 256 columns) run two workgroups per
+ *                  compute unit with 32-deep steps. Other paths accept only
+ *                  0 and 256 (else TGEMM_ERR_UNSUPPORTED).
+ *   producers:     0, or 4: producer/consumer workgroups (page 5, Croqtile
+ *                  tutorial "dense GEMM fp16 from naive", section "Kernel 3:
+ *                  warp specialization"): 8 waves, 4 of which only load
+ *                  operands into LDS and 4 only compute, on 128 x 256 tiles
+ *                  with 32-deep steps (tile_m 0 or 128).
  * Out-of-range choices return TGEMM_ERR_INVALID. Every choice computes the
  * same C bit for bit (each output's k order is fixed by its tile position).
  */
@@ -122,7 +134,7 @@ int tgemm_f16_config(int64_t M, int64_t N, int64_t K,
                      void* C, int64_t ldc,
                      void* stream,
                      int force_generic, int group_m, int num_xcd,
-                     int k_step, int stages);
+                     int k_step, int stages, int tile_m, int producers);
 
 /*
  * C = act(alpha * A * B + bias) with a choice of element types, on `stream`.
@@ -170,9 +182,11 @@ int tgemm_gemm(int64_t M, int64_t N, int64_t K,
 /*
  * tgemm_gemm with the launch choices of tgemm_f16_config (same meaning and
  * ranges). The binary16-in, binary16-out product without epilogue is built
- * for every K step and ring depth; every other combination for the default
- * ring depth of each K step (2 stages at 64, 4 at 32): other depths return
- * TGEMM_ERR_UNSUPPORTED for it, with nothing enqueued.
+ * for every K step, ring depth and tile choice listed there (producer/
+ * consumer workgroups with 3 or 5 stages); every other 16-bit combination
+ * for the default ring depth of each K step (2 stages at 64, 4 at 32) and of
+ * the 128- and 64-row tiles (3), without producer/consumer workgroups: other
+ * choices return TGEMM_ERR_UNSUPPORTED for it, with nothing enqueued.
  */
 int tgemm_gemm_config(int64_t M, int64_t N, int64_t K,
                       int ab_type, const void* A, int64_t lda,
@@ -181,7 +195,7 @@ int tgemm_gemm_config(int64_t M, int64_t N, int64_t K,
                       float alpha, const float* bias, int act,
                       void* stream,
                       int force_generic, int group_m, int num_xcd,
-                      int k_step, int stages);
+                      int k_step, int stages, int tile_m, int producers);
 
 /*
  * Runtime tuning, per problem shape (page 2, "CUDA 13.1 new feature: the Tile
@@ -191,9 +205,9 @@ int tgemm_gemm_config(int64_t M, int64_t N, int64_t K,
  *
  * tgemm_tune_gemm takes the arguments of tgemm_gemm and runs the problem on
  * the caller's buffers under each launch choice that leaves the result
- * unchanged bit for bit: the K step and LDS ring depth of the direct-to-LDS
- * pipeline (those built for the types) and a raster group height of 4, 8 or
- * 16 tile rows. Each choice runs once; then the untuned launch runs for about
+ * unchanged bit for bit: the tile rows, K step, LDS ring depth and
+ * producer/consumer choice of the direct-to-LDS pipeline (those built for
+ * the types) and a raster group height of 4, 8 or 16 tile rows. Each choice runs once; then the untuned launch runs for about
  * 100 ms of GPU time (at most 4096 launches) so that the power-limited clock
  * settles; then every choice runs `rounds` times (1..100), interleaved with the
  * others (round r starts at a different choice), timed with HIP events on
@@ -208,8 +222,9 @@ int tgemm_gemm_config(int64_t M, int64_t N, int64_t K,
  * Synchronizes `stream` (not for use under graph capture). C holds the
  * product on return, as after tgemm_gemm (every choice computes the same
  * bits). Creates and destroys HIP events; allocates no device memory.
- * info: NULL or 6 values: the chosen k_step, stages, group_m, num_xcd, its
- * median launch time in ns, and the number of choices tried.
+ * info: NULL or 8 values: the chosen k_step, stages, group_m, num_xcd, its
+ * median launch time in ns, the number of choices tried, and the chosen
+ * tile rows and producer waves.
  * Returns the argument errors of tgemm_gemm (nothing run), TGEMM_ERR_INVALID
  * for rounds outside 1..100, or TGEMM_ERR_HIP. M == 0 or N == 0: nothing is
  * run or recorded (info all 0). The table is shared by all threads.
@@ -251,7 +266,7 @@ int tgemm_last_hip_error(void);
  *           (64-bit runs of a 16-bit C, 128-bit runs of an fp32 C), bit2 B
  *           layout is NxK, bit3 the pipelined kernel (16-bit operands:
  *           streamed directly into LDS; binary32 operands: buffer loads)
- *   info[1] tile rows (BM)   info[2] tile columns (BN)   info[3] K step
+ *   info[1] tile rows        info[2] tile columns      info[3] K step
  *   info[4] workgroups launched (the tile count ceil(M/BM) * ceil(N/BN), or
  *           compute_units when each workgroup walks several tiles; 0 when
  *           M or N is 0)
@@ -264,8 +279,8 @@ int tgemm_plan_f16(int64_t M, int64_t N, int64_t K,
                    const void* B, int64_t ldb, int b_layout,
                    void* C, int64_t ldc,
                    int force_generic, int group_m, int num_xcd,
-                   int k_step, int stages, int compute_units,
-                   int64_t* info);
+                   int k_step, int stages, int tile_m, int producers,
+                   int compute_units, int64_t* info);
 
 /*
  * Planning query for tgemm_gemm_config: the same compute_units and
@@ -279,8 +294,8 @@ int tgemm_plan_gemm(int64_t M, int64_t N, int64_t K,
                     int c_type, void* C, int64_t ldc,
                     float alpha, const float* bias, int act,
                     int force_generic, int group_m, int num_xcd,
-                    int k_step, int stages, int compute_units,
-                    int64_t* info);
+                    int k_step, int stages, int tile_m, int producers,
+                    int compute_units, int64_t* info);
 
 /*
  * Host-only: the output tile that workgroup `wid` of a grid_m x grid_n tile

@@ -87,13 +87,21 @@ def _plan(M, N, K, A=PA, lda=None, B=PB, ldb=None, lay="KxN", C=PC, ldc=None, **
     dict(M=4, N=4, K=4, stages=6),
     dict(M=4, N=4, K=4, k_step=64, stages=3),
     dict(M=4, N=16, K=64, k_step=64),            # 64-deep steps need K > 64
+    dict(M=4, N=4, K=4, tile_m=96),
+    dict(M=4, N=4, K=4, tile_m=32),
+    dict(M=4, N=4, K=4, producers=2),
+    dict(M=4, N=4, K=4, producers=4, tile_m=64),  # producer/consumer workgroups have 128-row tiles
+    dict(M=4, N=4, K=4, producers=4, tile_m=256),
+    dict(M=300, N=300, K=300, tile_m=128, k_step=64),  # the smaller tiles take 32-deep steps
+    dict(M=300, N=300, K=300, tile_m=128, stages=4),   # two workgroups per unit: at most 80 KiB of ring
 ])
 def test_invalid_arguments_rejected(args):
     rc, info = _plan(**args)
     assert rc == tg.TGEMM_ERR_INVALID and info is None
     # the launching entry point returns the same code without touching the GPU
     a = dict(args)
-    kw = {k: a.pop(k) for k in ("force_generic", "group_m", "num_xcd", "k_step", "stages") if k in a}
+    kw = {k: a.pop(k) for k in ("force_generic", "group_m", "num_xcd", "k_step", "stages", "tile_m", "producers")
+          if k in a}
     M, N, K = a["M"], a["N"], a["K"]
     lay = a.get("lay", "KxN")
     lda = a.get("lda", K)
@@ -108,7 +116,8 @@ def test_bad_layout_rejected():
     lib = tg.load()
     assert lib.tgemm_f16(4, 4, 4, PA, 4, PB, 4, 2, PC, 4, None) == tg.TGEMM_ERR_INVALID
     info = (ctypes.c_int64 * 10)()
-    assert lib.tgemm_plan_f16(4, 4, 4, PA, 4, PB, 4, -1, PC, 4, 0, 0, 0, 0, 0, 256, info) == tg.TGEMM_ERR_INVALID
+    assert lib.tgemm_plan_f16(4, 4, 4, PA, 4, PB, 4, -1, PC, 4, 0, 0, 0, 0, 0, 0, 0, 256, info) == \
+        tg.TGEMM_ERR_INVALID
 
 
 def test_empty_outputs_are_noops_without_gpu():
@@ -187,6 +196,41 @@ def test_plan_variants_and_grid():
     # group_m larger than the tile rows is clamped (same map)
     rc, info = _plan(512, 4096, 64, group_m=100)
     assert info["group_m"] == 2
+
+
+def test_tile_choices_plan():
+    """Smaller tiles (128 or 64 rows x 256 columns, two workgroups per compute
+    unit, 32-deep steps, 3 stages by default) and producer/consumer workgroups
+    (512 threads, 128-row tiles): grid, threads and LDS bytes follow."""
+    DMA = 8
+    rc, info = _plan(4096, 4096, 4096, tile_m=128)
+    assert rc == 0 and info["variant"] & DMA
+    assert (info["bm"], info["bn"], info["bk"], info["stages"]) == (128, 256, 32, 3)
+    assert (info["workgroups"], info["threads"], info["lds_bytes"]) == (32 * 16, 256, 3 * 384 * 32 * 2)
+    rc, info = _plan(4096, 4096, 4096, tile_m=128, stages=2)
+    assert (info["stages"], info["lds_bytes"]) == (2, 2 * 384 * 32 * 2)
+    rc, info = _plan(256, 256, 256, tile_m=64)
+    assert (info["bm"], info["workgroups"], info["lds_bytes"]) == (64, 4, 3 * 320 * 32 * 2)
+    rc, info = _plan(3001, 5003, 4099, tile_m=128)                 # ragged: 24 x 20 tiles
+    assert (info["bm"], info["workgroups"]) == (128, 24 * 20)
+    rc, info = _plan(8192, 8192, 8192, lay="NxK", producers=4)
+    assert rc == 0 and (info["bm"], info["threads"], info["bk"], info["stages"]) == (128, 512, 32, 3)
+    assert info["workgroups"] == 64 * 32
+    rc, info = _plan(8192, 8192, 8192, lay="NxK", producers=4, stages=5)
+    assert (info["stages"], info["lds_bytes"]) == (5, 5 * 384 * 32 * 2)
+    assert _plan(8192, 8192, 8192, lay="NxK", producers=4, stages=4)[0] == tg.TGEMM_ERR_UNSUPPORTED
+    # only the direct-to-LDS path has the smaller tiles
+    assert _plan(512, 512, 512, tile_m=128, force_generic=1)[0] == tg.TGEMM_ERR_UNSUPPORTED
+    assert _plan(512, 512, 512, lay="NxK", lda=4_000_008, tile_m=128)[0] == tg.TGEMM_ERR_UNSUPPORTED
+    assert _plan(512, 512, 512, tile_m=256, force_generic=1)[0] == tg.TGEMM_OK
+    # every 16-bit type combination has the default depth of the smaller tiles;
+    # producer/consumer workgroups only the plain binary16 product
+    for ab, ct, kw in (("bf16", "bf16", {}), ("f16", "f32", {}), ("f16", "f16", dict(alpha=2.0))):
+        for tm in (128, 64):
+            assert _plan_ex(1024, 1024, 1024, ab=ab, ct=ct, tile_m=tm, **kw)[0] == tg.TGEMM_OK
+        assert _plan_ex(1024, 1024, 1024, ab=ab, ct=ct, tile_m=128, stages=2, **kw)[0] == tg.TGEMM_ERR_UNSUPPORTED
+        assert _plan_ex(1024, 1024, 1024, ab=ab, ct=ct, producers=4, **kw)[0] == tg.TGEMM_ERR_UNSUPPORTED
+    assert _plan_ex(1024, 1024, 1024, ab="f32", ct="f32", tile_m=128)[0] == tg.TGEMM_ERR_UNSUPPORTED
 
 
 def test_kxn_one_round_rule_follows_the_compute_unit_count():
@@ -348,7 +392,7 @@ def test_typed_ring_depths_other_than_default_are_unsupported():
             lib = tg.load()
             rc = lib.tgemm_gemm_config(1024, 1024, 1024, tg._binding._DTYPE[ab], PA, 1024, PB, 1024, 0,
                                        tg._binding._DTYPE[ct], PC, 1024, kw.get("alpha", 1.0), None, 0, None,
-                                       0, 0, 0, 32, st)
+                                       0, 0, 0, 32, st, 0, 0)
             assert rc == tg.TGEMM_ERR_UNSUPPORTED
 
 

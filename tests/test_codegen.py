@@ -81,7 +81,8 @@ def _innermost_mfma_loop(body):
         d = re.search(r"Depth=(\d+)", comment)
         return int(d.group(1)) if d else 0
 
-    mfma_depths = [depth(c) for c, ins in blocks if sum(i.startswith("v_mfma") for i in ins) >= 64]
+    # a block of the K loop holds at least one slice: 16 MFMAs for the 64-row tiles
+    mfma_depths = [depth(c) for c, ins in blocks if sum(i.startswith("v_mfma") for i in ins) >= 16]
     deepest = max(mfma_depths, default=0)
     assert deepest > 0, "no K loop found"
     return [i for c, ins in blocks if depth(c) == deepest for i in ins]

@@ -241,16 +241,21 @@ def test_runs_on_a_side_stream(oracle_mod):
     _full_check(oracle_mod, A, B, "KxN", C.cpu().numpy(), "side stream")
 
 
-PIPES = [(64, 2), (32, 2), (32, 3), (32, 4), (32, 5)]
+# (K step, ring depth, tile rows, producer waves)
+PIPES = [(64, 2, 0, 0), (32, 2, 0, 0), (32, 3, 0, 0), (32, 4, 0, 0), (32, 5, 0, 0),
+         (32, 3, 128, 0), (32, 2, 128, 0), (32, 3, 64, 0), (32, 3, 128, 4), (32, 5, 128, 4)]
 
 
 @pytest.mark.parametrize("lay", ["NxK", "KxN"])
-@pytest.mark.parametrize("M,N,K", [(512, 512, 512), (700, 600, 264), (1000, 1300, 8), (256, 256, 4096 + 32)])
+@pytest.mark.parametrize("M,N,K", [(512, 512, 512), (700, 600, 264), (1000, 1300, 8), (256, 256, 4096 + 32),
+                                   (3001, 1030, 1000)])
 def test_pipeline_choices_are_bit_identical(oracle_mod, M, N, K, lay):
-    """Every direct-to-LDS pipeline (K step x ring depth) and the register-staged
-    path produce the same bits: each output's 32-deep K slices are summed in the
-    same order. Odd step counts (K = 8, 264, 4128 at K step 32) cover the leading
-    all-zero step that makes a 32-deep ring's step count even."""
+    """Every direct-to-LDS pipeline (K step x ring depth x tile rows x
+    producer/consumer workgroups) and the register-staged path produce the same
+    bits: each output's 32-deep K slices are summed in the same order. Odd step
+    counts (K = 8, 264, 4128 at K step 32) cover the leading all-zero step that
+    makes a 32-deep ring's step count even; M = 3001 leaves partial 128- and
+    64-row tiles."""
     print(f"case pipelines {M}x{N}x{K} {lay}", flush=True)
     A = inputs.random_f16((M, K), M + K)
     B = inputs.random_f16((N, K) if lay == "NxK" else (K, N), N + K)
@@ -258,14 +263,15 @@ def test_pipeline_choices_are_bit_identical(oracle_mod, M, N, K, lay):
     base = tg.mm(Ad, Bd, lay, force_generic=1)
     got = _host(base)
     _full_check(oracle_mod, A, B, lay, got, f"pipelines {M}x{N}x{K} {lay}")
-    for ks, st in PIPES:
+    for ks, st, tm, pr in PIPES:
+        kw = dict(k_step=ks, stages=st, tile_m=tm, producers=pr)
         if ks == 64 and K <= 64:                     # 64-deep steps need two steps or more
             with pytest.raises(tg.TgemmError, match="invalid"):
-                tg.mm(Ad, Bd, lay, k_step=ks, stages=st)
+                tg.mm(Ad, Bd, lay, **kw)
             continue
-        C = tg.mm(Ad, Bd, lay, k_step=ks, stages=st)
+        C = tg.mm(Ad, Bd, lay, **kw)
         torch.cuda.synchronize()
-        assert torch.equal(C.view(torch.int16), base.view(torch.int16)), (ks, st)
+        assert torch.equal(C.view(torch.int16), base.view(torch.int16)), kw
 
 
 @pytest.mark.parametrize("lay", ["NxK", "KxN"])

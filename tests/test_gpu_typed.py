@@ -213,7 +213,8 @@ def test_epilogue_workload_parity(oracle_mod, ab, ct):
 def test_persistent_grid_and_pipelines_agree(oracle_mod, ab, ct, lay):
     """More tiles than compute units (the persistent kernel), with the
     epilogue: bit-identical to the register-staged kernel, to 32-deep steps,
-    and under another raster; sampled outputs within tolerance."""
+    to the 128- and 64-row tiles (two workgroups per compute unit) and under
+    another raster; sampled outputs within tolerance."""
     M, N, K = 4300, 4300, 1000
     print(f"case typed persistent {ab}->{ct} {lay}", flush=True)
     A = _bits((M, K), 41, ab)
@@ -222,7 +223,8 @@ def test_persistent_grid_and_pipelines_agree(oracle_mod, ab, ct, lay):
     Ad, Bd = _dev(A, ab), _dev(B, ab)
     kw = dict(out_dtype=TORCH_DT[ct], alpha=-0.75, bias=b_dev, act="relu")
     outs = [tg.gemm(Ad, Bd, lay, **kw), tg.gemm(Ad, Bd, lay, force_generic=1, **kw),
-            tg.gemm(Ad, Bd, lay, k_step=32, **kw), tg.gemm(Ad, Bd, lay, group_m=3, num_xcd=1, **kw)]
+            tg.gemm(Ad, Bd, lay, k_step=32, **kw), tg.gemm(Ad, Bd, lay, group_m=3, num_xcd=1, **kw),
+            tg.gemm(Ad, Bd, lay, tile_m=128, **kw), tg.gemm(Ad, Bd, lay, tile_m=64, **kw)]
     torch.cuda.synchronize()
     base = outs[0] if ct == "f32" else outs[0].view(torch.int16)
     for o in outs[1:]:
@@ -258,8 +260,9 @@ def test_tile_changes_with_epilogue_bit_identical(oracle_mod, ab, ct, lay):
 def test_odd_step_count_32_deep_ring_agrees(oracle_mod, ab, ct, lay):
     """K = 1040: 33 steps of 32 (an odd count, so the ring runs one leading
     all-zero step) with a partial last step (K mod 32 = 16). The 32-deep ring,
-    the default 64-deep pipeline and the register-staged kernel give the same
-    bits, with the epilogue; every output within tolerance of the oracle."""
+    the default 64-deep pipeline, the 128- and 64-row tiles and the
+    register-staged kernel give the same bits, with the epilogue; every
+    output within tolerance of the oracle."""
     M, N, K = 520, 777, 1040
     print(f"case typed odd steps {ab}->{ct} {lay}", flush=True)
     A = _bits((M, K), 61, ab)
@@ -268,7 +271,8 @@ def test_odd_step_count_32_deep_ring_agrees(oracle_mod, ab, ct, lay):
     Ad, Bd = _dev(A, ab), _dev(B, ab)
     kw = dict(out_dtype=TORCH_DT[ct], alpha=1.25, bias=b_dev, act="relu")
     outs = [tg.gemm(Ad, Bd, lay, k_step=32, **kw), tg.gemm(Ad, Bd, lay, **kw),
-            tg.gemm(Ad, Bd, lay, force_generic=1, **kw)]
+            tg.gemm(Ad, Bd, lay, force_generic=1, **kw), tg.gemm(Ad, Bd, lay, tile_m=128, **kw),
+            tg.gemm(Ad, Bd, lay, tile_m=64, **kw)]
     torch.cuda.synchronize()
     base = outs[0] if ct == "f32" else outs[0].view(torch.int16)
     for o in outs[1:]:
