@@ -167,6 +167,14 @@ static int plan_gemm(int64_t M, int64_t N, int64_t K, int ab_type, const void* A
         rc = make_plan(M, N, K, A, lda, B, ldb, b_layout, C, ldc, 0, t.group_m, t.num_xcd, t.k_step, t.stages,
                        &tp, ab_type, c_type, bias, epi, t.tile_m, t.producers);
         if (rc == TGEMM_OK) *pl = tp;
+    } else if (automatic && (pl->variant & kDma) && ab_type != TGEMM_F32 && (int64_t)pl->W * kSmallGridDiv <= ncu) {
+        // a grid of 256-row tiles filling at most a quarter of the compute
+        // units: 64-row tiles spread the same work over four times the
+        // workgroups (256^3: 3.0 -> 5.9 TFLOP/s)
+        Plan rp;
+        rc = make_plan(M, N, K, A, lda, B, ldb, b_layout, C, ldc, 0, 0, 0, 0, 0, &rp, ab_type, c_type, bias, epi,
+                       kSmallGridTileM, 0);
+        if (rc == TGEMM_OK) *pl = rp;
     } else if (automatic && (pl->variant & kDma) && !(pl->variant & kLayoutNxK) && ab_type != TGEMM_F32 &&
                K > 64 && K % 64 != 0 && pl->W <= ncu) {
         Plan rp;

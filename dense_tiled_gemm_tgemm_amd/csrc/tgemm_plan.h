@@ -36,6 +36,10 @@ constexpr int kDefaultDmaStages32 = 4;     // ring depth when the K step is 32
 // unit: 32-deep steps in a ring of at most 80 KiB (3 stages by default).
 constexpr int kDefaultSmallStages = 3;
 constexpr int kProducerWaves = 4;          // producer/consumer workgroups: 4 + 4 waves
+// Automatic launches whose grid of 256-row tiles fills at most 1 / kSmallGridDiv
+// of the compute units take tiles of kSmallGridTileM rows.
+constexpr int kSmallGridDiv = 4;
+constexpr int kSmallGridTileM = 64;
 // Automatic launches of 16-bit operands with B stored K x N, K not a multiple
 // of 64 and no more tiles than compute units take 32-deep steps (default ring
 // depth, built for every type combination): measured 2-4% ahead of the

@@ -189,7 +189,7 @@ def test_plan_variants_and_grid():
     rc, info = _plan(512, 512, 512, ldb=4_000_000)
     assert info["variant"] & DMA
     # K <= 64 streams 32-deep steps; K == 0 (zeros only) takes the register-staged kernel
-    rc, info = _plan(512, 512, 64, lay="NxK")
+    rc, info = _plan(512, 512, 64, lay="NxK", tile_m=256)
     assert info["variant"] & DMA and (info["bk"], info["stages"]) == (32, 4)
     rc, info = _plan(512, 512, 0, lay="NxK", lda=1, ldb=1)
     assert rc == 0 and not info["variant"] & DMA
@@ -231,6 +231,27 @@ def test_tile_choices_plan():
         assert _plan_ex(1024, 1024, 1024, ab=ab, ct=ct, tile_m=128, stages=2, **kw)[0] == tg.TGEMM_ERR_UNSUPPORTED
         assert _plan_ex(1024, 1024, 1024, ab=ab, ct=ct, producers=4, **kw)[0] == tg.TGEMM_ERR_UNSUPPORTED
     assert _plan_ex(1024, 1024, 1024, ab="f32", ct="f32", tile_m=128)[0] == tg.TGEMM_ERR_UNSUPPORTED
+
+
+def test_small_grids_take_64_row_tiles():
+    """Automatic launches whose grid of 256-row tiles fills at most a quarter of
+    the compute units take 64-row tiles (four times the workgroups); explicit
+    choices, the register-staged path and larger grids keep 256 rows."""
+    rc, info = _plan(256, 256, 256)
+    assert rc == 0 and (info["bm"], info["workgroups"], info["bk"], info["stages"]) == (64, 4, 32, 3)
+    rc, info = _plan(2048, 2048, 2048, lay="NxK")                  # 64 tiles of 256 rows: a quarter of 256
+    assert (info["bm"], info["workgroups"]) == (64, 256)
+    rc, info = _plan(2304, 2048, 2048)                             # 72 tiles
+    assert (info["bm"], info["workgroups"]) == (256, 72)
+    rc, info = _plan(2048, 2048, 2048, compute_units=255)
+    assert info["bm"] == 256
+    rc, info = _plan(256, 256, 256, tile_m=256)
+    assert (info["bm"], info["workgroups"]) == (256, 1)
+    rc, info = _plan(256, 256, 256, force_generic=1)
+    assert info["bm"] == 256
+    for ab, ct in (("bf16", "f32"), ("f16", "bf16")):
+        assert _plan_ex(256, 256, 256, ab=ab, ct=ct, alpha=0.5)[1]["bm"] == 64
+    assert _plan_ex(256, 256, 256, ab="f32", ct="f32")[1]["bm"] == 256
 
 
 def test_kxn_one_round_rule_follows_the_compute_unit_count():
@@ -371,7 +392,7 @@ def test_typed_plans_match_f16_plans():
                 rc, info = _plan_ex(8192, 8192, 8192, ab=ab, ct=ct, lay="NxK", **kw)
                 rc0, info0 = _plan(8192, 8192, 8192, lay="NxK")
                 assert rc == rc0 == 0 and info == info0, (ab, ct, kw)
-                rc, info = _plan_ex(512, 512, 64, ab=ab, ct=ct, **kw)
+                rc, info = _plan_ex(512, 512, 64, ab=ab, ct=ct, tile_m=256, **kw)
                 assert rc == 0 and (info["bk"], info["stages"]) == (32, 4)
                 rc, info = _plan_ex(300, 200, 100, ab=ab, ct=ct, force_generic=1, **kw)
                 assert rc == 0 and not info["variant"] & 8

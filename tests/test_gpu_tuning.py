@@ -49,7 +49,7 @@ def test_tuned_choice_is_recorded_used_and_changes_no_bits():
     print(f"  chosen {chosen}", flush=True)
     assert torch.equal(C.view(torch.int16), base.view(torch.int16))
     assert tg.tuning_entries() == 1
-    assert chosen["candidates"] == 15 and chosen["median_ns"] > 0
+    assert chosen["candidates"] == 30 and chosen["median_ns"] > 0     # 10 pipelines x 3 group heights
     assert (chosen["k_step"], chosen["stages"]) in {(64, 2), (32, 2), (32, 3), (32, 4), (32, 5)}
     # raster groups 4, 8 and 16 tile rows, each capped at the 9 tile rows of M
     assert chosen["group_m"] in (4, 8, 9) and chosen["num_xcd"] == 8
@@ -81,8 +81,12 @@ def test_tuning_with_epilogue_and_bf16(oracle_mod):
     C, chosen = tg.tune(Ad, Bd, "KxN", out_dtype=torch.float32, alpha=0.25, bias=bd, act="relu", rounds=3)
     torch.cuda.synchronize()
     print(f"  chosen {chosen}", flush=True)
-    # bfloat16 -> fp32 with an epilogue builds the default ring depth of each K step
-    assert chosen["candidates"] == 6 and (chosen["k_step"], chosen["stages"]) in {(64, 2), (32, 4)}
+    # bfloat16 -> fp32 with an epilogue builds the default ring depth of each K
+    # step and of the 128- and 64-row tiles: 4 pipelines x 3 group heights
+    assert chosen["candidates"] == 12
+    assert (chosen["k_step"], chosen["stages"], chosen["tile_m"]) in {(64, 2, 256), (32, 4, 256), (32, 3, 128),
+                                                                      (32, 3, 64)}
+    assert chosen["producers"] == 0
     assert torch.equal(C, base)
     got = tg.gemm(Ad, Bd, "KxN", out_dtype=torch.float32, alpha=0.25, bias=bd, act="relu").cpu().numpy()
     I, J = inputs.sample_points(M, N, 4096, 6)
@@ -104,7 +108,7 @@ def test_automatic_pipeline_choice(lay, K, tiles_m, ab, want):
     64-deep step on a grid of one round or less runs 32-deep steps; the other
     cases keep the 64-deep ring. Same bits either way."""
     print(f"case automatic pipeline {lay} K={K} tiles_m={tiles_m} {ab}", flush=True)
-    M, N = 256 * tiles_m, 2048
+    M, N = 256 * tiles_m, 8192       # 32 tile columns: more than a quarter of the compute units
     dt = torch.float16 if ab == "f16" else torch.bfloat16
     gen = inputs.random_f16 if ab == "f16" else inputs.random_bf16
     A = _dev16(gen((M, K), 7).view(np.uint16), dt)
