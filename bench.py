@@ -335,6 +335,8 @@ def main():
         from dense_tiled_gemm_tgemm_amd import probe
         probe.load()
         a16 = np.ascontiguousarray(A16).view(np.uint16).reshape(-1)
+        if a16.nbytes < (1 << 20):                    # the probe reads at least 1 MiB: repeat the values
+            a16 = np.resize(a16, (1 << 20) // 2)
         nbytes = 1 << min(26, int(a16.nbytes).bit_length() - 1)
         data = torch.from_numpy(a16[: nbytes // 2].view(np.int16).copy()).to("cuda:0")
         stream = torch.cuda.current_stream()

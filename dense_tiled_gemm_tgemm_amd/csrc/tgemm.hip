@@ -162,18 +162,22 @@ static int plan_gemm(int64_t M, int64_t N, int64_t K, int ab_type, const void* A
     }
     TuneChoice t;
     const bool automatic = !force_generic && !group_m && !num_xcd && !k_step && !stages && !tile_m && !producers;
-    if (automatic && use_tuned && tuned_choice(*pl, &t)) {
+    const bool tuned = automatic && use_tuned && tuned_choice(*pl, &t);
+    if (tuned) {
         Plan tp;
         rc = make_plan(M, N, K, A, lda, B, ldb, b_layout, C, ldc, 0, t.group_m, t.num_xcd, t.k_step, t.stages,
                        &tp, ab_type, c_type, bias, epi, t.tile_m, t.producers);
         if (rc == TGEMM_OK) *pl = tp;
-    } else if (automatic && (pl->variant & kDma) && ab_type != TGEMM_F32 && (int64_t)pl->W * kSmallGridDiv <= ncu) {
-        // a grid of 256-row tiles filling at most a quarter of the compute
-        // units: 64-row tiles spread the same work over four times the
-        // workgroups (256^3: 3.0 -> 5.9 TFLOP/s)
+    } else if (automatic && (pl->variant & kDma) && ab_type != TGEMM_F32 && (int64_t)pl->W * 2 <= ncu) {
+        // a grid of 256-row tiles filling at most half of the compute units:
+        // smaller tiles spread the same work over more workgroups; 64-row
+        // tiles when it fills a quarter or less (256^3: 3.0 -> 5.9 TFLOP/s,
+        // 2048^3: 441 -> 613), 128-row tiles up to half (2560 x 2048 x 2048:
+        // 545 -> 718, 4096 x 2048 x 2048: 872 -> 963); above half the
+        // 256-row tile is ahead (2560 x 4096 x 2048: 1058 against 773)
         Plan rp;
-        rc = make_plan(M, N, K, A, lda, B, ldb, b_layout, C, ldc, 0, 0, 0, 0, 0, &rp, ab_type, c_type, bias, epi,
-                       kSmallGridTileM, 0);
+        const int tm = (int64_t)pl->W * 4 <= ncu ? 64 : 128;
+        rc = make_plan(M, N, K, A, lda, B, ldb, b_layout, C, ldc, 0, 0, 0, 0, 0, &rp, ab_type, c_type, bias, epi, tm, 0);
         if (rc == TGEMM_OK) *pl = rp;
     } else if (automatic && (pl->variant & kDma) && !(pl->variant & kLayoutNxK) && ab_type != TGEMM_F32 &&
                K > 64 && K % 64 != 0 && pl->W <= ncu) {
@@ -184,6 +188,7 @@ static int plan_gemm(int64_t M, int64_t N, int64_t K, int ab_type, const void* A
     }
     // one workgroup per compute unit, each walking several tiles
     if (persistent(*pl) && ncu < pl->W) pl->grid = ncu;
+    if (!num_xcd && !tuned) pl->num_xcd = num_xcd_for(ncu);    // the tuned choice names its own
     *fn = pick_kernel(*pl);
     return *fn ? TGEMM_OK : TGEMM_ERR_UNSUPPORTED;
 }
@@ -211,10 +216,12 @@ static int launch(const Plan& pl, const void* fn, const void* A, const void* B, 
     args.group_m = pl.group_m;
     args.num_xcd = pl.num_xcd;
     args.grid = pl.grid;
-    // 16-byte C stores: rows 16-byte aligned, and every byte offset inside a
-    // wave's 128 rows below 2^31 (they go through a 32-bit buffer offset)
-    args.c16 = ((uintptr_t)C % 16 == 0) && ((pl.ldc * c_size) % 16 == 0) &&
-               (127 * pl.ldc + (int64_t)pl.N) * c_size + 16 < (int64_t(1) << 31);
+    // 16-byte C stores at any alignment of the rows (gfx950 buffer stores
+    // accept unaligned addresses, as its buffer loads do: on the 3001 x 5003
+    // x 4099 workload, whose C rows are 2-byte aligned, 140.2 -> 130.8 us
+    // against element stores), wherever every byte offset inside a wave's
+    // 128 rows stays below 2^31 (they go through a 32-bit buffer offset)
+    args.c16 = (127 * pl.ldc + (int64_t)pl.N) * c_size + 16 < (int64_t(1) << 31);
     args.c8 = (pl.variant & kVecC) != 0;
     void* kargs[] = {&args};
     const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)args.grid), dim3((unsigned)pl.threads), kargs, 0,
@@ -300,9 +307,9 @@ extern "C" int tgemm_tune_gemm(int64_t M, int64_t N, int64_t K, int ab_type, con
             const int tm = dma ? pipes[ip][2] : 0;
             const int pr = dma ? pipes[ip][3] : 0;
             Cand cd;
-            cd.c = tg::TuneChoice{ks, st, g, tg::kDefaultNumXcd, tm, pr};
+            cd.c = tg::TuneChoice{ks, st, g, tg::num_xcd_for(ncu), tm, pr};
             if (tg::plan_gemm(M, N, K, ab_type, A, lda, B, ldb, b_layout, c_type, C, ldc, alpha, bias, act, 0, g,
-                              tg::kDefaultNumXcd, ks, st, tm, pr, ncu, &cd.pl, &cd.fn, false) != TGEMM_OK)
+                              tg::num_xcd_for(ncu), ks, st, tm, pr, ncu, &cd.pl, &cd.fn, false) != TGEMM_OK)
                 continue;                                   // not built for these types, or invalid for this K
             bool dup = false;                               // group heights clamp to the tile rows
             for (const Cand& o : cands)

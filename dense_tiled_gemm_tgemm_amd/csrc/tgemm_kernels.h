@@ -75,7 +75,7 @@ struct Args {
     int M, N, K;
     int grid_m, grid_n, W, group_m, num_xcd;
     int grid;             // workgroups launched; workgroup b computes tiles b, b + grid, ...
-    int c16;              // C base 16-byte aligned and each row a multiple of 16 bytes
+    int c16;              // 16-byte C stores (any alignment): every offset in a wave's rows below 2^31
     int c8;               // the same for 8 bytes
 };
 
@@ -221,25 +221,28 @@ __device__ __forceinline__ void store16_lanes(const u32x4& v, const BufRsrc& r, 
     store16_stream(v, r, (int)o);
 }
 
-// Lane l of wave (wm, wn) holds, in acc[i][j], C row m0 + 128 wm + 16 i + (l mod 16)
-// at columns n0 + 16 NJ wn + 16 j + 4 (l / 16) + 0..3 (NJ = 8 column blocks per
-// wave, 4 in the two-workgroups-per-unit binary32 kernel).
+// Lane l of wave (wm, wn) holds, in acc[i][j], C row m0 + 16 NI wm + 16 i + (l mod 16)
+// at columns n0 + 16 NJ wn + 16 j + 4 (l / 16) + 0..3 (NI = 8 row blocks and
+// NJ = 8 column blocks per wave; NI = 4 or 2 in the smaller tiles, NJ = 4 in
+// the two-workgroups-per-unit binary32 kernel).
 //  * 16-bit outputs: for each pair of 16-column blocks (j, j+1),
 //    v_permlane16_swap exchanges the converted words between 16-lane rows so
 //    that a lane in row g then holds the 8 consecutive columns
-//    16 (j + (g & 1)) + 8 (g >> 1) .. +7 of its C row: one 16-byte store when
-//    every C row starts 16-byte aligned (each store instruction writes 16 rows
-//    x 64 bytes), two 8-byte stores when 8-byte aligned, element stores
-//    otherwise and where the 8 columns straddle N.
+//    16 (j + (g & 1)) + 8 (g >> 1) .. +7 of its C row: one 16-byte store
+//    (each store instruction writes 16 rows x 64 bytes) at whatever alignment
+//    the row has (gfx950 buffer stores accept unaligned addresses; against
+//    element stores for 2-byte-aligned rows, 140.2 -> 130.8 us on the 3001 x
+//    5003 x 4099 workload); element stores where the 8 columns straddle N,
+//    and 8-byte or element stores when C's offsets exceed 31 bits.
 //  * fp32 output: each block's four columns are 16 contiguous bytes of the
-//    lane's row, stored as they are (16 rows x 64 bytes per instruction) when
-//    every C row starts 16-byte aligned, element stores otherwise (an 8-byte
-//    path here made the register allocator move the accumulators around in
-//    the main loop of the binary32-operand kernel).
+//    lane's row, stored as they are (16 rows x 64 bytes per instruction),
+//    element stores where they straddle N (an 8-byte path here made the
+//    register allocator move the accumulators around in the main loop of the
+//    binary32-operand kernel).
 // All lanes run the exchange; only the stores are predicated: the 16-byte store
 // on its own condition, the 8-byte and element stores behind one uniform test
-// (`whole`: the wave's 128 rows lie inside C and its columns end at or before
-// N, with 16-byte rows), so an interior wave skips them with one scalar branch
+// (`whole`: the wave's rows lie inside C and its columns end at or before
+// N, with 16-byte stores available), so an interior wave skips them with one scalar branch
 // per store instead of a chain of exec-mask branches, which took longer than
 // the conversions themselves. One 16-row block
 // at a time (pinned), so the temporaries stay few when this runs between two

@@ -28,6 +28,15 @@ constexpr int NTHREADS = 256;            // 4 waves of 64 lanes, 2 x 2 over the 
 // the same within noise at 8192^3 and on the projection shape).
 constexpr int kDefaultGroupM = 4;
 constexpr int kDefaultNumXcd = 8;        // MI355X: 8 accelerator dies of 32 CUs
+constexpr int kCusPerXcd = 32;           // gfx950: compute units per accelerator die
+
+// Dies the dispatcher deals workgroups over, for a device of `ncu` compute
+// units: a whole MI355X has 8 dies of 32 compute units; a partitioned one
+// exposes a whole number of dies per device (4, 2 or 1).
+inline int num_xcd_for(int ncu) {
+    const int x = ncu / kCusPerXcd;
+    return x < 1 ? 1 : (x > kDefaultNumXcd ? kDefaultNumXcd : x);
+}
 // Direct-to-LDS pipeline: K step and LDS ring depth (a stage holds 64 KiB at
 // K step 64, 32 KiB at K step 32). 64-deep steps take a 2-stage ring.
 constexpr int kDefaultDmaKStep = 64;
@@ -36,10 +45,7 @@ constexpr int kDefaultDmaStages32 = 4;     // ring depth when the K step is 32
 // unit: 32-deep steps in a ring of at most 80 KiB (3 stages by default).
 constexpr int kDefaultSmallStages = 3;
 constexpr int kProducerWaves = 4;          // producer/consumer workgroups: 4 + 4 waves
-// Automatic launches whose grid of 256-row tiles fills at most 1 / kSmallGridDiv
-// of the compute units take tiles of kSmallGridTileM rows.
-constexpr int kSmallGridDiv = 4;
-constexpr int kSmallGridTileM = 64;
+
 // Automatic launches of 16-bit operands with B stored K x N, K not a multiple
 // of 64 and no more tiles than compute units take 32-deep steps (default ring
 // depth, built for every type combination): measured 2-4% ahead of the

@@ -80,8 +80,9 @@ enum {
  * start 16-byte aligned run faster, and rows that start 128-byte aligned,
  * a stride that is a multiple of 64 elements, fastest); otherwise they are
  * staged through registers with 128-bit or element loads. C is written with
- * 16-byte stores where every row starts 16-byte aligned, 8-byte stores where
- * 8-byte aligned, and element stores otherwise and at its right edge.
+ * 16-byte stores at any 2-byte alignment (element stores at its right edge;
+ * 8-byte or element stores when a byte offset within 128 rows of C would
+ * exceed 2^31).
  * C must not alias A or B (page 4, section 2.4.12.1: restrict-qualified
  * operands must not overlap).
  */
@@ -100,8 +101,10 @@ int tgemm_f16(int64_t M, int64_t N, int64_t K,
  *                  (4 of these 256-row tiles: the same 1024 rows as the
  *                  page's 8); 1..1024 otherwise.
  *   num_xcd:       number of dies the workgroups are spread over for the
- *                  die-aware renumbering; 0 = default (8 on MI355X);
- *                  1 disables the renumbering; 1..64 otherwise.
+ *                  die-aware renumbering; 0 = default (the device's compute
+ *                  units / 32, from 1 to 8: 8 on a whole MI355X, fewer on
+ *                  a partitioned one); 1 disables the renumbering; 1..64
+ *                  otherwise.
  *   k_step:        K depth of one LDS stage of the direct-to-LDS path
  *                  (used whenever K > 0 and both row strides are at least
  *                  8 elements and small enough for 32-bit offsets):
@@ -116,10 +119,14 @@ int tgemm_f16(int64_t M, int64_t N, int64_t K,
  *                  not a multiple of 64 and at most one tile per compute
  *                  unit run at k_step 32 (default depth).
  *   tile_m:        output tile rows of that path (page 2, section 7.4 tunes
- *                  the tile shape): 0 = default (256), 256, 128 or 64. Tiles
- *                  of 128 or 64 rows (x 256 columns) run two workgroups per
- *                  compute unit with 32-deep steps. Other paths accept only
- *                  0 and 256 (else TGEMM_ERR_UNSUPPORTED).
+ *                  the tile shape): 0 = automatic, 256, 128 or 64. Tiles of
+ *                  128 or 64 rows (x 256 columns) run two workgroups per
+ *                  compute unit with 32-deep steps. Automatic (with every
+ *                  other launch choice 0 and no tuned choice): 256 rows,
+ *                  except where a grid of 256-row tiles would fill at most
+ *                  half of the compute units (128 rows) or at most a
+ *                  quarter (64 rows). Other paths accept only 0 and 256
+ *                  (else TGEMM_ERR_UNSUPPORTED).
  *   producers:     0, or 4: producer/consumer workgroups (page 5, Croqtile
  *                  tutorial "dense GEMM fp16 from naive", section "Kernel 3:
  *                  warp specialization"): 8 waves, 4 of which only load
@@ -251,10 +258,11 @@ int tgemm_last_hip_error(void);
 /*
  * Planning query: the launch tgemm_f16_config would make for these
  * arguments on a device with `compute_units` compute units (256 on MI355X).
- * The plan depends on that count in two places: a launch of 64-deep steps
+ * The plan depends on that count in three places: a launch of 64-deep steps
  * with more tiles than compute units runs one workgroup per compute unit,
- * and the automatic 32-deep rule for B stored K x N applies to grids of at
- * most one tile per compute unit.
+ * the automatic tile rows depend on how much of the device a 256-row grid
+ * fills, and the automatic 32-deep rule for B stored K x N applies to grids
+ * of at most one tile per compute unit.
  *   compute_units: 1..65536, or 0 for the current device's count, read with
  *                  one HIP attribute query once the arguments have passed
  *                  (TGEMM_ERR_HIP when there is no device). With a count

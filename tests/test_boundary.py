@@ -138,7 +138,7 @@ def test_plan_variants_and_grid():
     assert info["workgroups"] == 256 and info["group_m"] == 4 and info["num_xcd"] == 8
     rc, info = _plan(8192, 8192, 8192, lay="NxK", compute_units=304)
     assert info["workgroups"] == 304
-    rc, info = _plan(8192, 8192, 8192, lay="NxK", compute_units=2048)
+    rc, info = _plan(8192, 8192, 8192, lay="NxK", compute_units=1536)
     assert info["workgroups"] == 1024                  # fewer tiles than units: one workgroup per tile
     # 32-deep steps are not persistent: one workgroup per tile
     rc, info = _plan(8192, 8192, 8192, lay="NxK", k_step=32)
@@ -233,17 +233,24 @@ def test_tile_choices_plan():
     assert _plan_ex(1024, 1024, 1024, ab="f32", ct="f32", tile_m=128)[0] == tg.TGEMM_ERR_UNSUPPORTED
 
 
-def test_small_grids_take_64_row_tiles():
+def test_small_grids_take_smaller_tiles():
     """Automatic launches whose grid of 256-row tiles fills at most a quarter of
-    the compute units take 64-row tiles (four times the workgroups); explicit
-    choices, the register-staged path and larger grids keep 256 rows."""
+    the compute units take 64-row tiles (four times the workgroups), at most
+    half 128-row tiles; explicit choices, the register-staged path and larger
+    grids keep 256 rows."""
     rc, info = _plan(256, 256, 256)
     assert rc == 0 and (info["bm"], info["workgroups"], info["bk"], info["stages"]) == (64, 4, 32, 3)
     rc, info = _plan(2048, 2048, 2048, lay="NxK")                  # 64 tiles of 256 rows: a quarter of 256
     assert (info["bm"], info["workgroups"]) == (64, 256)
     rc, info = _plan(2304, 2048, 2048)                             # 72 tiles
-    assert (info["bm"], info["workgroups"]) == (256, 72)
+    assert (info["bm"], info["workgroups"], info["stages"]) == (128, 144, 3)
+    rc, info = _plan(4096, 2048, 2048)                             # 128 tiles: half of 256
+    assert (info["bm"], info["workgroups"]) == (128, 256)
+    rc, info = _plan(4352, 2048, 2048)                             # 136 tiles
+    assert (info["bm"], info["workgroups"]) == (256, 136)
     rc, info = _plan(2048, 2048, 2048, compute_units=255)
+    assert info["bm"] == 128
+    rc, info = _plan(2048, 2048, 2048, compute_units=127)
     assert info["bm"] == 256
     rc, info = _plan(256, 256, 256, tile_m=256)
     assert (info["bm"], info["workgroups"]) == (256, 1)
@@ -252,6 +259,17 @@ def test_small_grids_take_64_row_tiles():
     for ab, ct in (("bf16", "f32"), ("f16", "bf16")):
         assert _plan_ex(256, 256, 256, ab=ab, ct=ct, alpha=0.5)[1]["bm"] == 64
     assert _plan_ex(256, 256, 256, ab="f32", ct="f32")[1]["bm"] == 256
+
+
+def test_default_die_count_follows_the_compute_units():
+    """The die-aware renumbering spreads over compute units / 32 dies (gfx950:
+    32 compute units per die), 1 to 8: a whole MI355X has 8, a partitioned
+    one 4, 2 or 1. An explicit num_xcd is kept."""
+    for cu, x in ((256, 8), (128, 4), (64, 2), (32, 1), (16, 1), (304, 8)):
+        rc, info = _plan(8192, 8192, 8192, lay="NxK", compute_units=cu)
+        assert rc == 0 and info["num_xcd"] == x, (cu, info)
+    rc, info = _plan(8192, 8192, 8192, lay="NxK", compute_units=64, num_xcd=8)
+    assert info["num_xcd"] == 8
 
 
 def test_kxn_one_round_rule_follows_the_compute_unit_count():

@@ -37,7 +37,7 @@ def _plan(A, B, C, lay, ab, ct, **kw):
 
 def test_tuned_choice_is_recorded_used_and_changes_no_bits():
     print("case tuning f16 NxK", flush=True)
-    M, N, K = 2304, 2560, 1000
+    M, N, K = 2304, 5120, 1000          # 180 tiles of 256 rows: more than half the compute units
     A = _dev16(inputs.random_f16((M, K), 1).view(np.uint16), torch.float16)
     B = _dev16(inputs.random_f16((N, K), 2).view(np.uint16), torch.float16)
     base = tg.mm(A, B, "NxK")
@@ -51,11 +51,12 @@ def test_tuned_choice_is_recorded_used_and_changes_no_bits():
     assert tg.tuning_entries() == 1
     assert chosen["candidates"] == 30 and chosen["median_ns"] > 0     # 10 pipelines x 3 group heights
     assert (chosen["k_step"], chosen["stages"]) in {(64, 2), (32, 2), (32, 3), (32, 4), (32, 5)}
-    # raster groups 4, 8 and 16 tile rows, each capped at the 9 tile rows of M
-    assert chosen["group_m"] in (4, 8, 9) and chosen["num_xcd"] == 8
+    # raster groups 4, 8 and 16 tile rows, each capped at the tile rows of M
+    # (9 of 256 rows, 18 of 128, 36 of 64)
+    assert chosen["group_m"] in (4, 8, 9, 16) and chosen["num_xcd"] == 8
     rc, plan = _plan(A, B, C, "NxK", "f16", "f16")
-    assert (plan["bk"], plan["stages"], plan["group_m"], plan["num_xcd"]) == \
-        (chosen["k_step"], chosen["stages"], chosen["group_m"], chosen["num_xcd"])
+    assert (plan["bk"], plan["stages"], plan["group_m"], plan["num_xcd"], plan["bm"]) == \
+        (chosen["k_step"], chosen["stages"], chosen["group_m"], chosen["num_xcd"], chosen["tile_m"])
     # another key (other types) is not affected
     C32 = torch.empty((M, N), dtype=torch.float32, device=DEV)
     rc, plan32 = _plan(A, B, C32, "NxK", "f16", "f32")
@@ -108,7 +109,7 @@ def test_automatic_pipeline_choice(lay, K, tiles_m, ab, want):
     64-deep step on a grid of one round or less runs 32-deep steps; the other
     cases keep the 64-deep ring. Same bits either way."""
     print(f"case automatic pipeline {lay} K={K} tiles_m={tiles_m} {ab}", flush=True)
-    M, N = 256 * tiles_m, 8192       # 32 tile columns: more than a quarter of the compute units
+    M, N = 256 * tiles_m, 16384      # 64 tile columns: more than half of the compute units
     dt = torch.float16 if ab == "f16" else torch.bfloat16
     gen = inputs.random_f16 if ab == "f16" else inputs.random_bf16
     A = _dev16(gen((M, K), 7).view(np.uint16), dt)
