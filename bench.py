@@ -237,6 +237,46 @@ def counter_summary(csv_paths) -> str:
     return "\n".join(["| kernel | dispatches | medians per dispatch |", "|---|---|---|"] + out)
 
 
+def traffic_summary(fetch_csv, write_csv, fetch_copy_csv, write_copy_csv, workload: str, copy_mib: int) -> dict:
+    """HBM-side bytes per GEMM launch from rocprofv3 --pmc FETCH_SIZE and
+    WRITE_SIZE runs (KiB per dispatch, medians over the GEMM kernel's
+    dispatches), each scaled by what the same counter reads for device copies
+    of copy_mib MiB (bench.py --copy-calibration): the record bench.py reports
+    as roofline.traffic while the kernel sources hash to the stored value."""
+    import numpy as np
+    from dense_tiled_gemm_tgemm_amd import inputs
+
+    def med(path, counter, pick):
+        by = {}
+        for r in _read_csv(path):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (_short(r["Kernel_Name"]), r["Dispatch_Id"])
+            by[key] = by.get(key, 0.0) + float(r["Counter_Value"])
+        names = {k for k, _ in by}
+        kern = [n for n in names if pick(n)]
+        if len(kern) != 1:
+            raise SystemExit(f"{path}: expected one {counter} kernel to pick, found {sorted(names)}")
+        vals = [v for (k, _), v in by.items() if k == kern[0]]
+        return kern[0], float(np.median(vals)), len(vals)
+
+    gemm = lambda n: "tgemm_" in n and "probe" not in n and "ceiling" not in n
+    copy = lambda n: "copyBuffer" in n or "copy" in n.lower()
+    kern, fetch, nf = med(fetch_csv, "FETCH_SIZE", gemm)
+    _, write, nw = med(write_csv, "WRITE_SIZE", gemm)
+    _, cfetch, _ = med(fetch_copy_csv, "FETCH_SIZE", copy)
+    _, cwrite, _ = med(write_copy_csv, "WRITE_SIZE", copy)
+    nbytes = copy_mib << 20
+    fs, ws = nbytes / (cfetch * 1024), nbytes / (cwrite * 1024)
+    w = inputs.WORKLOADS[workload]
+    return {"workload": workload, "kernel": kern, "kernel_source_hash": kernel_source_hash(),
+            "fetch_size_kib_per_launch": fetch, "write_size_kib_per_launch": write, "dispatches": [nf, nw],
+            "copy_calibration": {"bytes_copied": nbytes, "fetch_size_kib": cfetch, "write_size_kib": cwrite,
+                                 "fetch_scale": fs, "write_scale": ws},
+            "hbm_bytes_per_launch": int(round(fetch * 1024 * fs + write * 1024 * ws)),
+            "compulsory_bytes": int(2 * (w.M * w.K + w.N * w.K + w.M * w.N))}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -279,8 +319,16 @@ def main():
     ap.add_argument("--bench-json", metavar="FILE", help="the JSON line printed by the traced run")
     ap.add_argument("--counter-summary", metavar="CSV", nargs="+",
                     help="print a markdown table of rocprofv3 --pmc counter CSVs and exit")
+    ap.add_argument("--traffic-summary", metavar="CSV", nargs=4,
+                    help="FETCH_SIZE and WRITE_SIZE counter CSVs of the GEMM, then of --copy-calibration runs: "
+                         "print the HBM traffic record (JSON) for --workload and exit")
+    ap.add_argument("--copy-mib", type=int, default=1024, help="MiB per copy of the calibration runs")
     args = ap.parse_args()
 
+    if args.traffic_summary:
+        print(json.dumps(traffic_summary(*args.traffic_summary, args.workload or "sq8192_nt", args.copy_mib),
+                         indent=1))
+        return
     if args.trace_summary:
         print(trace_summary(args.trace_summary, args.bench_json))
         return

@@ -1457,15 +1457,27 @@ __device__ __forceinline__ F32Lanes f32_lanes(const Args& a, int tid) {
     return L;
 }
 
+// B stored K x N goes through a resource based at the step's first k row
+// (record count to B's last element, bspan bytes from k row 0 of the
+// tile's columns), so the lane offsets stay below 16 rows of B whatever K is;
+// a step at or past K gets an empty range and reads zeros.
 template <int NXK>
 __device__ __forceinline__ void f32_buf_load(u32x4 (&ra)[4], u32x4 (&rb)[2], const Rsrc& rsa, const Rsrc& rsb,
-                                             const F32Lanes& L, const Args& a, int t) {
+                                             int64_t bspan, const F32Lanes& L, const Args& a, int t) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the host pass cannot instantiate these target builtins
     const int k0 = t * kF32Ks;
     const __amdgpu_buffer_rsrc_t xa = __builtin_amdgcn_make_buffer_rsrc((void*)rsa.base, 0, rsa.nrec, 0x00020000);
-    const __amdgpu_buffer_rsrc_t xb = __builtin_amdgcn_make_buffer_rsrc((void*)rsb.base, 0, rsb.nrec, 0x00020000);
     const unsigned soa = (unsigned)k0 * 4u;
-    const unsigned sob = NXK ? (unsigned)k0 * 4u : (unsigned)k0 * (unsigned)a.ldb * 4u;
+    const uint16_t* bbase = rsb.base;
+    int brec = rsb.nrec;
+    if (!NXK) {
+        int64_t span = bspan - (int64_t)k0 * a.ldb * 4;
+        span = span < 0 ? 0 : (span > (int64_t)kOob - 1 ? (int64_t)kOob - 1 : span);
+        bbase += (int64_t)k0 * a.ldb * 2;                   // 16-bit units: two per float
+        brec = (int)span;
+    }
+    const __amdgpu_buffer_rsrc_t xb = __builtin_amdgcn_make_buffer_rsrc((void*)bbase, 0, brec, 0x00020000);
+    const unsigned sob = NXK ? (unsigned)k0 * 4u : 0u;
 #pragma unroll
     for (int p = 0; p < 4; ++p)
         ra[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xa, (int)L.va[p], (int)soa, 0));
@@ -1473,7 +1485,7 @@ __device__ __forceinline__ void f32_buf_load(u32x4 (&ra)[4], u32x4 (&rb)[2], con
     for (int p = 0; p < 2; ++p)
         rb[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xb, (int)L.vb[p], (int)sob, 0));
 #else
-    (void)ra; (void)rb; (void)rsa; (void)rsb; (void)L; (void)a; (void)t;
+    (void)ra; (void)rb; (void)rsa; (void)rsb; (void)bspan; (void)L; (void)a; (void)t;
 #endif
 }
 
@@ -1569,7 +1581,8 @@ tgemm_f32in_kernel(Args a) {
     const F32Lanes L = f32_lanes<NXK>(a, tid);
     const Rsrc rsa = f32_rsrc(a.A, a.lda, a.M, a.K, m0);
     // B: N x K rows n0.. ; K x N columns n0.. of all K rows
-    const Rsrc rsb = NXK ? f32_rsrc(a.B, a.ldb, a.N, a.K, n0) : f32_rsrc(a.B + 2 * n0, a.ldb, a.K, a.N - n0, 0);
+    const Rsrc rsb = NXK ? f32_rsrc(a.B, a.ldb, a.N, a.K, n0) : Rsrc{a.B + 2 * n0, 0};
+    const int64_t bspan = NXK ? 0 : ((int64_t)(a.K - 1) * a.ldb + (a.N - n0)) * 4;
 
     // stage-0 read positions (8-byte units) of 16-row block 0; block i lies
     // 128 further, stage 1 2 * kF32StageSlots further, the hi half 1 further
@@ -1586,14 +1599,14 @@ tgemm_f32in_kernel(Args a) {
     F32Frags f;
     u32x4 ra[4], rb[2];
     if (nk > 0) {
-        f32_buf_load<NXK>(ra, rb, rsa, rsb, L, a, 0);
+        f32_buf_load<NXK>(ra, rb, rsa, rsb, bspan, L, a, 0);
         f32_store_step<NXK>(smem, ra, rb, L, a, n0, 0, tid);
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < 8; ++i) f.alo[i] = pa0[i * 128];
 #pragma unroll
         for (int j = 0; j < 4; ++j) f.blo[j] = pb0[j * 128];
-        f32_buf_load<NXK>(ra, rb, rsa, rsb, L, a, 1);   // past the last step: zeros
+        f32_buf_load<NXK>(ra, rb, rsa, rsb, bspan, L, a, 1);   // past the last step: zeros
     }
     for (int t = 0; t < nk; ++t) {
         const int st = t & 1;
@@ -1603,7 +1616,7 @@ tgemm_f32in_kernel(Args a) {
         __builtin_amdgcn_sched_barrier(0);
         wait_vmcnt<0>();                              // step t + 1 in the staging registers
         f32_store_step<NXK>(smem + (st ^ 1) * kF32StageSlots, ra, rb, L, a, n0, t + 1, tid);
-        f32_buf_load<NXK>(ra, rb, rsa, rsb, L, a, t + 2);
+        f32_buf_load<NXK>(ra, rb, rsa, rsb, bspan, L, a, t + 2);
         TG_COMPILER_FENCE();
         __builtin_amdgcn_sched_barrier(0);
         f32_half<0, 48, 64>(acc, f, pa0 + so, pb0 + so);

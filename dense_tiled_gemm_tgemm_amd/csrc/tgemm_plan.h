@@ -211,13 +211,12 @@ inline int make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
     // element by element; narrower operands take the register-staged kernel)
     // (binary32 operands have kernels of their own: the kDma bit then marks the
     // pipelined one, whose buffer loads need K (and, for B stored K x N, N) a
-    // multiple of 4 and every byte offset of a tile below 2^31)
+    // multiple of 4 and every byte offset of a tile below 2^31; a K x N B is
+    // rebased at every K step there too)
     const bool dma =
         ab_type == TGEMM_F32
-            ? (!force_generic && K > 0 && K % 4 == 0 && lda <= kMaxDmaLd / 2 &&
-               (b_layout == TGEMM_B_NxK ? ldb <= kMaxDmaLd / 2
-                                        : N % 4 == 0 && ldb < (int64_t(1) << 29) &&
-                                              (K + 64) * ldb < (int64_t(1) << 29) - 256))
+            ? (!force_generic && K > 0 && K % 4 == 0 && lda <= kMaxDmaLd / 2 && ldb <= kMaxDmaLd / 2 &&
+               (b_layout == TGEMM_B_NxK || N % 4 == 0))
             : (!force_generic && K > 0 && lda >= 8 && ldb >= 8 && lda <= kMaxDmaLd && ldb <= kMaxDmaLd);
     pl->variant = (vec_ab ? kVecAB : 0) | (vec_c ? kVecC : 0) |
                   (b_layout == TGEMM_B_NxK ? kLayoutNxK : 0) | (dma ? kDma : 0);

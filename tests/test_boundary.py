@@ -509,6 +509,11 @@ def test_fp32_operand_plans():
     # strides past the 32-bit offset limits: the general kernel
     rc, info = _plan_ex(300, 200, 100, ab="f32", ct="f32", lay="NxK", lda=2_000_004)
     assert rc == 0 and not info["variant"] & PIPE
+    rc, info = _plan_ex(300, 200, 100, ab="f32", ct="f32", ldb=2_000_004)
+    assert rc == 0 and not info["variant"] & PIPE
+    # B stored K x N is rebased at every step: a wide B stays on the pipelined kernel
+    rc, info = _plan_ex(300, 200, 8192, ab="f32", ct="f32", ldb=2_000_000)
+    assert rc == 0 and info["variant"] & PIPE
 
 
 @pytest.mark.parametrize("lay,M,N,K,lda,ldb,dma", [

@@ -175,3 +175,37 @@ def test_vocabulary_projection_kxn_streams_into_lds(oracle_mod):
     ref, absum = oracle_mod.gemm(np.ascontiguousarray(A[rows]), np.ascontiguousarray(B[:, cols]), "KxN")
     res = oracle_mod.check(np.ascontiguousarray(got[np.ix_(rows, cols)]), ref, absum)
     assert res["nfail"] == 0, res
+
+
+def test_binary32_operands_padded_kxn_stride(oracle_mod):
+    """Binary32 operands, B stored K x N with a stride whose K-step offsets
+    from the first k row exceed 2^31 bytes: the pipelined buffer-load kernel
+    (each 16-deep step has its own B resource), rows past K and the padding
+    NaN. Bit-identical to the general register-staged kernel; full parity
+    with the oracle, plain and with the epilogue into fp32."""
+    M, N, K, ldb = 300, 520, 1000, 600_000
+    print(f"case binary32 padded K x N stride {M}x{N}x{K} ldb={ldb}", flush=True)
+    assert (K + 64) * ldb * 4 > 2 ** 31
+    A = inputs.random_f32((M, K), 541)
+    B = inputs.random_f32((K, N), 542)
+    Ad = torch.from_numpy(A).to(DEV)
+    Bd = torch.full((K * ldb + 64,), float("nan"), dtype=torch.float32, device=DEV)
+    Bd.as_strided((K, N), (ldb, 1)).copy_(torch.from_numpy(B).to(DEV))
+    bias = inputs.random_bias(N, 543)
+    bd = torch.from_numpy(bias).to(DEV)
+    for alpha, bptr, act in ((1.0, None, "none"), (0.5, bd.data_ptr(), "relu")):
+        C = torch.empty((M, N), dtype=torch.float32, device=DEV)
+        rc, plan = tg.tgemm_plan_gemm(M, N, K, "f32", Ad.data_ptr(), K, Bd.data_ptr(), ldb, "KxN", "f32",
+                                      C.data_ptr(), N, alpha, bptr, act)
+        assert rc == tg.TGEMM_OK and plan["variant"] & DMA, plan
+        assert tg.tgemm_gemm(M, N, K, "f32", Ad.data_ptr(), K, Bd.data_ptr(), ldb, "KxN", "f32", C.data_ptr(), N,
+                             alpha, bptr, act, _st()) == tg.TGEMM_OK
+        Cg = torch.empty_like(C)
+        assert tg.tgemm_gemm_config(M, N, K, "f32", Ad.data_ptr(), K, Bd.data_ptr(), ldb, "KxN", "f32",
+                                    Cg.data_ptr(), N, alpha, bptr, act, _st(), 1) == tg.TGEMM_OK
+        torch.cuda.synchronize()
+        got = C.cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), Cg.cpu().numpy().view(np.uint32))
+        ref, tol = oracle_mod.gemm_ex(A, B, "KxN", "f32", alpha, bias if bptr else None, act)
+        res = oracle_mod.check_ex(got, "f32", ref, tol)
+        assert res["nfail"] == 0, res
