@@ -53,16 +53,19 @@ SMALL = [(1, 1, 1), (1, 300, 7), (31, 17, 65), (64, 64, 64), (255, 257, 63), (25
          (257, 255, 129), (300, 520, 200), (513, 300, 8), (96, 1100, 1000), (512, 512, 512)]
 
 
-@pytest.mark.parametrize("generic", [0, 1])
+@pytest.mark.parametrize("mode", ["auto", "tile256", "generic"])
 @pytest.mark.parametrize("lay", ["KxN", "NxK"])
 @pytest.mark.parametrize("M,N,K", SMALL)
-def test_small_shapes_full_parity(oracle_mod, M, N, K, lay, generic):
-    print(f"case small M={M} N={N} K={K} {lay} generic={generic}", flush=True)
+def test_small_shapes_full_parity(oracle_mod, M, N, K, lay, mode):
+    """The automatic launch (at these sizes mostly 64-row tiles), the 256-row
+    direct-to-LDS tile and the register-staged kernel, each in full parity."""
+    print(f"case small M={M} N={N} K={K} {lay} {mode}", flush=True)
     seed = (M * 7 + N * 13 + K * 17) % 100003
     A = inputs.random_f16((M, K), seed)
     B = inputs.random_f16((K, N) if lay == "KxN" else (N, K), seed + 1)
-    got = _run(A, B, lay, force_generic=generic)
-    _full_check(oracle_mod, A, B, lay, got, f"{M}x{N}x{K} {lay} generic={generic}")
+    kw = {"auto": {}, "tile256": dict(tile_m=256), "generic": dict(force_generic=1)}[mode]
+    got = _run(A, B, lay, **kw)
+    _full_check(oracle_mod, A, B, lay, got, f"{M}x{N}x{K} {lay} {mode}")
 
 
 @pytest.mark.parametrize("lay,offset,M,N,K,pad", [
@@ -87,17 +90,19 @@ def test_strided_offset_operands_and_guard_band(oracle_mod, lay, offset, M, N, K
     A = np.lib.stride_tricks.as_strided(Abuf[offset:], (M, K), (2 * lda, 2))
     B = np.lib.stride_tricks.as_strided(Bbuf[offset:], (rows_b, K if lay == "NxK" else N), (2 * ldb, 2))
     Ad, Bd = _dev(Abuf), _dev(Bbuf)
-    Cd = torch.full(((M + 1) * ldc + 5,), NAN16, dtype=torch.int32).to(torch.int16).view(torch.float16).to(DEV)
-    rc = tg.tgemm_f16(M, N, K, Ad.data_ptr() + 2 * offset, lda, Bd.data_ptr() + 2 * offset, ldb, lay,
-                      Cd.data_ptr() + 2 * offset, ldc, torch.cuda.current_stream().cuda_stream)
-    assert rc == tg.TGEMM_OK
-    Cbits = _host(Cd).view(np.uint16)
-    inside = np.zeros(Cbits.shape, dtype=bool)
-    idx = offset + (np.arange(M)[:, None] * ldc + np.arange(N)[None, :])
-    inside[idx.ravel()] = True
-    assert np.all(Cbits[~inside] == NAN16), "write outside M x N"
-    got = Cbits[idx]
-    _full_check(oracle_mod, np.ascontiguousarray(A), np.ascontiguousarray(B), lay, got, "strided")
+    for tile_m in (0, 256):                          # automatic (small grid: 64-row tiles) and 256-row tiles
+        Cd = torch.full(((M + 1) * ldc + 5,), NAN16, dtype=torch.int32).to(torch.int16).view(torch.float16).to(DEV)
+        rc = tg.tgemm_f16_config(M, N, K, Ad.data_ptr() + 2 * offset, lda, Bd.data_ptr() + 2 * offset, ldb, lay,
+                                 Cd.data_ptr() + 2 * offset, ldc, torch.cuda.current_stream().cuda_stream,
+                                 tile_m=tile_m)
+        assert rc == tg.TGEMM_OK
+        Cbits = _host(Cd).view(np.uint16)
+        inside = np.zeros(Cbits.shape, dtype=bool)
+        idx = offset + (np.arange(M)[:, None] * ldc + np.arange(N)[None, :])
+        inside[idx.ravel()] = True
+        assert np.all(Cbits[~inside] == NAN16), f"write outside M x N (tile_m {tile_m})"
+        got = Cbits[idx]
+        _full_check(oracle_mod, np.ascontiguousarray(A), np.ascontiguousarray(B), lay, got, f"strided {tile_m}")
     # inputs were not modified
     assert np.array_equal(_host(Ad).view(np.uint16), Abuf.view(np.uint16))
     assert np.array_equal(_host(Bd).view(np.uint16), Bbuf.view(np.uint16))
@@ -333,14 +338,14 @@ def _nan_padded(rows, cols, ld, seed, offset):
     return buf, np.ascontiguousarray(view)
 
 
-@pytest.mark.parametrize("generic", [0, 1])
+@pytest.mark.parametrize("mode", ["auto", "tile256", "generic"])
 @pytest.mark.parametrize("lay", ["NxK", "KxN"])
 @pytest.mark.parametrize("K", [5, 37, 261, 264, 512 + 24, 1000])
-def test_nan_beyond_k_and_edges_never_leaks(oracle_mod, lay, K, generic):
+def test_nan_beyond_k_and_edges_never_leaks(oracle_mod, lay, K, mode):
     """Padding past K, past N (row stride slack) and after the last element is NaN;
     odd strides and an odd element offset leave the rows only 2-byte aligned. Every
     output must still match the oracle, so no padded element reaches the sums."""
-    print(f"case nan-padding {lay} K={K} generic={generic}", flush=True)
+    print(f"case nan-padding {lay} K={K} {mode}", flush=True)
     M, N, off = 300, 270, 3
     lda = K + 5
     Abuf, A = _nan_padded(M, K, lda, K, off)
@@ -353,11 +358,12 @@ def test_nan_beyond_k_and_edges_never_leaks(oracle_mod, lay, K, generic):
     Ad, Bd = _dev(Abuf), _dev(Bbuf)
     C = torch.empty((M, N), dtype=torch.float16, device=DEV)
     rc = tg.tgemm_f16_config(M, N, K, Ad.data_ptr() + 2 * off, lda, Bd.data_ptr() + 2 * off, ldb, lay,
-                             C.data_ptr(), N, torch.cuda.current_stream().cuda_stream, generic)
+                             C.data_ptr(), N, torch.cuda.current_stream().cuda_stream, int(mode == "generic"),
+                             tile_m=256 if mode == "tile256" else 0)
     assert rc == tg.TGEMM_OK
     got = _host(C)
     assert np.isfinite(got.astype(np.float32)).all(), "a padded NaN reached an output"
-    _full_check(oracle_mod, A, B, lay, got, f"nan padding {lay} K={K}")
+    _full_check(oracle_mod, A, B, lay, got, f"nan padding {lay} K={K} {mode}")
 
 
 @pytest.mark.parametrize("lay,M,N,K,ldb", [
@@ -379,11 +385,12 @@ def test_narrow_operands(oracle_mod, lay, M, N, K, ldb):
     Bbuf = np.zeros((rows, ldb), dtype=np.float16)
     Bbuf[:, :cols] = B
     Ad, Bd = _dev(Abuf), _dev(Bbuf)
-    C = torch.empty((M, N), dtype=torch.float16, device=DEV)
-    rc = tg.tgemm_f16_config(M, N, K, Ad.data_ptr(), lda, Bd.data_ptr(), ldb, lay, C.data_ptr(), N,
-                             torch.cuda.current_stream().cuda_stream, 0)
-    assert rc == tg.TGEMM_OK
-    _full_check(oracle_mod, A, B, lay, _host(C), f"narrow {lay} {M}x{N}x{K} ldb={ldb}")
+    for tile_m in (0, 256):                          # automatic (small grid: 64-row tiles) and 256-row tiles
+        C = torch.empty((M, N), dtype=torch.float16, device=DEV)
+        rc = tg.tgemm_f16_config(M, N, K, Ad.data_ptr(), lda, Bd.data_ptr(), ldb, lay, C.data_ptr(), N,
+                                 torch.cuda.current_stream().cuda_stream, 0, tile_m=tile_m)
+        assert rc == tg.TGEMM_OK
+        _full_check(oracle_mod, A, B, lay, _host(C), f"narrow {lay} {M}x{N}x{K} ldb={ldb} tile_m={tile_m}")
 
 
 @pytest.mark.parametrize("lay", ["NxK", "KxN"])

@@ -3,7 +3,9 @@ full against the oracle: sizes from 1 to several tiles in every dimension,
 both B layouts, all input and output types, row strides with slack, base
 addresses off by a few elements, and the epilogue on or off. Everything
 outside the operands is NaN and a guard band surrounds C, so any read past an
-operand or write past C shows up.
+operand or write past C shows up. Each problem runs with the automatic launch
+(at these sizes mostly 64-row tiles) and again with 256-row tiles, whose
+bits must be the same.
 
 Tolerance per element (the extended oracle's check):
   |g - ref| <= 1e-3 * (|alpha| * sum_k |a*b| + |bias[j]|) + ulp_out(ref)
@@ -81,22 +83,28 @@ def test_random_case_full_parity(oracle_mod, case):
     dA, dB, dC = dev(bufA), dev(bufB), dev(bufC)
     dbias = torch.from_numpy(bias).to(DEV) if bias is not None else None
     es_in, es_out = ESIZE[ab], ESIZE[ct]
-    rc = tg.tgemm_gemm(M, N, K, ab, dA.data_ptr() + es_in * oa, lda, dB.data_ptr() + es_in * ob, ldb, lay,
-                       ct, dC.data_ptr() + es_out * oc, ldc, alpha,
-                       dbias.data_ptr() if dbias is not None else None, act,
-                       torch.cuda.current_stream().cuda_stream)
-    assert rc == tg.TGEMM_OK, tg.status_string(rc)
-    torch.cuda.synchronize()
-    out = dC.cpu().numpy()
-    out = out.view(np.uint16) if ct != "f32" else out
-    got = out[oc:oc + M * ldc].reshape(M, ldc)[:, :N]
-    # the guard band and the row slack of C are untouched
-    mask = np.ones(out.shape, dtype=bool)
-    mask[oc:oc + M * ldc].reshape(M, ldc)[:, :N] = False
-    if ct == "f32":
-        assert np.isnan(out[mask]).all(), "a store landed outside C"
-    else:
-        assert (out[mask] == NAN_BITS[ct]).all(), "a store landed outside C"
+    dC256 = dev(bufC.copy())
+    outs = []
+    for C, tile_m in ((dC, 0), (dC256, 256)):
+        rc = tg.tgemm_gemm_config(M, N, K, ab, dA.data_ptr() + es_in * oa, lda, dB.data_ptr() + es_in * ob, ldb,
+                                  lay, ct, C.data_ptr() + es_out * oc, ldc, alpha,
+                                  dbias.data_ptr() if dbias is not None else None, act,
+                                  torch.cuda.current_stream().cuda_stream, tile_m=tile_m)
+        assert rc == tg.TGEMM_OK, (tile_m, tg.status_string(rc))
+        torch.cuda.synchronize()
+        out = C.cpu().numpy()
+        out = out.view(np.uint16) if ct != "f32" else out
+        # the guard band and the row slack of C are untouched
+        mask = np.ones(out.shape, dtype=bool)
+        mask[oc:oc + M * ldc].reshape(M, ldc)[:, :N] = False
+        if ct == "f32":
+            assert np.isnan(out[mask]).all(), f"a store landed outside C (tile_m {tile_m})"
+        else:
+            assert (out[mask] == NAN_BITS[ct]).all(), f"a store landed outside C (tile_m {tile_m})"
+        outs.append(out[oc:oc + M * ldc].reshape(M, ldc)[:, :N])
+    got = outs[0]
+    assert np.array_equal(got.view(np.uint32 if ct == "f32" else np.uint16),
+                          outs[1].view(np.uint32 if ct == "f32" else np.uint16)), "tile rows changed the bits"
     ref, tol = oracle_mod.gemm_ex(A, B, lay, ab, alpha, bias, act)
     res = oracle_mod.check_ex(np.ascontiguousarray(got), ct, ref, tol)
     assert res["nfail"] == 0, f"case {i}: {res}"

@@ -82,8 +82,13 @@ def test_small_shapes_full_parity(oracle_mod, M, N, K, ab, ct, lay, epi):
     B = _bits((K, N) if lay == "KxN" else (N, K), seed + 1, ab)
     e = EPI[epi]
     b_np, b_dev = _bias(N, seed + 2, e["bias"])
-    C = tg.gemm(_dev(A, ab), _dev(B, ab), lay, out_dtype=TORCH_DT[ct], alpha=e["alpha"], bias=b_dev, act=e["act"])
+    Ad, Bd = _dev(A, ab), _dev(B, ab)
+    C = tg.gemm(Ad, Bd, lay, out_dtype=TORCH_DT[ct], alpha=e["alpha"], bias=b_dev, act=e["act"])
     _check(oracle_mod, A, B, lay, ab, ct, _out_np(C), e["alpha"], b_np, e["act"], f"{M}x{N}x{K} {ab}->{ct} {lay}")
+    # 256-row tiles (the automatic launch takes smaller ones on these grids): the same bits
+    C256 = tg.gemm(Ad, Bd, lay, out_dtype=TORCH_DT[ct], alpha=e["alpha"], bias=b_dev, act=e["act"], tile_m=256)
+    torch.cuda.synchronize()
+    assert torch.equal(C.view(torch.int16), C256.view(torch.int16))
 
 
 @pytest.mark.parametrize("lay", ["KxN", "NxK"])
@@ -293,17 +298,18 @@ def test_k_zero_stores_rectified_bias(ct):
 
 
 @pytest.mark.parametrize("ct,offset,pad", [
-    ("f32", 0, 2),      # rows start 16-byte aligned: 16-byte stores
-    ("f32", 2, 6),      # 8-byte aligned rows: 8-byte stores
-    ("f32", 1, 3),      # element stores
-    ("bf16", 0, 2),     # 16-byte stores
-    ("f16", 4, 2),      # 8-byte stores
-    ("bf16", 1, 3),     # element stores
+    ("f32", 0, 2),      # rows 16-byte aligned
+    ("f32", 2, 6),      # rows 8-byte aligned: 16-byte stores at 8-byte alignment
+    ("f32", 1, 3),      # rows 4-byte aligned
+    ("bf16", 0, 2),     # rows 16-byte aligned
+    ("f16", 4, 2),      # rows 8-byte aligned
+    ("bf16", 1, 3),     # rows 2-byte aligned: 16-byte stores at 2-byte alignment
 ])
 def test_output_alignment_paths_and_guard_band(oracle_mod, ct, offset, pad):
     """C inside a larger NaN-filled buffer (row stride N + pad, start `offset`
-    elements in): 16-byte, 8-byte and element stores, edge tiles; nothing
-    outside the M x N window changes."""
+    elements in): 16-byte stores at every row alignment, element stores at the
+    right edge, edge tiles, with the automatic launch (64-row tiles here) and
+    with 256-row tiles; nothing outside the M x N window changes."""
     M, N, K = 300, 270, 130
     print(f"case typed guard {ct} offset={offset} pad={pad}", flush=True)
     A = _bits((M, K), 61, "bf16")
@@ -317,18 +323,22 @@ def test_output_alignment_paths_and_guard_band(oracle_mod, ct, offset, pad):
         buf = torch.full((total,), 0x7FC1 if ct == "bf16" else 0x7E01, dtype=torch.int16, device=DEV)
         buf = buf.view(TORCH_DT[ct])
     Ad, Bd = _dev(A, "bf16"), _dev(B, "bf16")
-    rc = tg.tgemm_gemm(M, N, K, "bf16", Ad.data_ptr(), K, Bd.data_ptr(), N, "KxN", ct,
-                       buf.data_ptr() + offset * buf.element_size(), ldc, 1.5, b_dev.data_ptr(), "none",
-                       torch.cuda.current_stream().cuda_stream)
-    assert rc == tg.TGEMM_OK
-    host = _out_np(buf)
-    win = host[offset:offset + M * ldc].reshape(M, ldc)
-    _check(oracle_mod, A, B, "KxN", "bf16", ct, np.ascontiguousarray(win[:, :N]), 1.5, b_np, "none", "guard")
-    outside = np.concatenate([host[:offset], win[:, N:].ravel(), host[offset + M * ldc:]])
-    if ct == "f32":
-        assert np.isnan(outside).all()
-    else:
-        assert (outside == (0x7FC1 if ct == "bf16" else 0x7E01)).all()
+    fresh = buf.clone()
+    for tile_m in (0, 256):
+        buf = fresh.clone()
+        rc = tg.tgemm_gemm_config(M, N, K, "bf16", Ad.data_ptr(), K, Bd.data_ptr(), N, "KxN", ct,
+                                  buf.data_ptr() + offset * buf.element_size(), ldc, 1.5, b_dev.data_ptr(), "none",
+                                  torch.cuda.current_stream().cuda_stream, tile_m=tile_m)
+        assert rc == tg.TGEMM_OK
+        host = _out_np(buf)
+        win = host[offset:offset + M * ldc].reshape(M, ldc)
+        _check(oracle_mod, A, B, "KxN", "bf16", ct, np.ascontiguousarray(win[:, :N]), 1.5, b_np, "none",
+               f"guard {tile_m}")
+        outside = np.concatenate([host[:offset], win[:, N:].ravel(), host[offset + M * ldc:]])
+        if ct == "f32":
+            assert np.isnan(outside).all()
+        else:
+            assert (outside == (0x7FC1 if ct == "bf16" else 0x7E01)).all()
 
 
 def test_bias_nan_and_inf_propagate(oracle_mod):
