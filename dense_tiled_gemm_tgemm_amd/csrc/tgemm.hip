@@ -168,6 +168,21 @@ static int plan_gemm(int64_t M, int64_t N, int64_t K, int ab_type, const void* A
         rc = make_plan(M, N, K, A, lda, B, ldb, b_layout, C, ldc, 0, t.group_m, t.num_xcd, t.k_step, t.stages,
                        &tp, ab_type, c_type, bias, epi, t.tile_m, t.producers);
         if (rc == TGEMM_OK) *pl = tp;
+    } else if (automatic && f32_on_dma(*pl)) {
+        // binary32 operands: a 64-row tile keeps 96-98% of the 256-row tile's
+        // rate (the matrix work per staged byte is 8 times that of 16-bit
+        // operands), and its finer grid balances better, so it is taken
+        // unless the 256-row tiles fill at least 7/8 of their rounds over the
+        // compute units (measured at 256 units: 64 rows ahead by 23-54% with
+        // 160, 192, 320 and 384 tiles and by 1.9-3.6x below half a round;
+        // even at 224; 256-row tiles 2-4% ahead with 256, 1024 and 1536)
+        const int64_t rounds = ((int64_t)pl->W + ncu - 1) / ncu;
+        if ((int64_t)pl->W * 8 < rounds * ncu * 7) {
+            Plan rp;
+            rc = make_plan(M, N, K, A, lda, B, ldb, b_layout, C, ldc, 0, 0, 0, 0, 0, &rp, ab_type, c_type, bias, epi,
+                           64, 0);
+            if (rc == TGEMM_OK) *pl = rp;
+        }
     } else if (automatic && (pl->variant & kDma) && ab_type != TGEMM_F32 && (int64_t)pl->W * 2 <= ncu) {
         // a grid of 256-row tiles filling at most half of the compute units:
         // smaller tiles spread the same work over more workgroups; 64-row
@@ -204,12 +219,16 @@ static int launch(const Plan& pl, const void* fn, const void* A, const void* B, 
     args.bias = bias;
     args.alpha = alpha;
     args.relu = act == TGEMM_ACT_RELU;
-    args.lda = pl.lda;
-    args.ldb = pl.ldb;
+    // binary32 operands on the direct-to-LDS kernel: K and the operand
+    // strides in 16-bit units (the kernel moves bytes; its matrix
+    // instructions read the 4-byte values)
+    const int units = f32_on_dma(pl) ? 2 : 1;
+    args.lda = pl.lda * units;
+    args.ldb = pl.ldb * units;
     args.ldc = pl.ldc;
     args.M = pl.M;
     args.N = pl.N;
-    args.K = pl.K;
+    args.K = pl.K * units;
     args.grid_m = pl.grid_m;
     args.grid_n = pl.grid_n;
     args.W = pl.W;
@@ -295,9 +314,13 @@ extern "C" int tgemm_tune_gemm(int64_t M, int64_t N, int64_t K, int ab_type, con
         const void* fn;
     };
     std::vector<Cand> cands;
-    const int pipes[][4] = {{64, 2, 256, 0}, {32, 4, 256, 0}, {32, 2, 256, 0}, {32, 3, 256, 0}, {32, 5, 256, 0},
-                            {32, 3, 128, 0}, {32, 2, 128, 0}, {32, 3, 64, 0},  {32, 3, 128, 4}, {32, 5, 128, 4}};
-    const int npipes = (base.variant & tg::kDma) ? (int)(sizeof(pipes) / sizeof(pipes[0])) : 1;
+    const int pipes16[][4] = {{64, 2, 256, 0}, {32, 4, 256, 0}, {32, 2, 256, 0}, {32, 3, 256, 0}, {32, 5, 256, 0},
+                              {32, 3, 128, 0}, {32, 2, 128, 0}, {32, 3, 64, 0},  {32, 3, 128, 4}, {32, 5, 128, 4}};
+    // binary32 operands: 16-deep steps only (the K step choice does not apply)
+    const int pipes32[][4] = {{16, 2, 256, 0}, {16, 3, 256, 0}, {16, 3, 128, 0}, {16, 3, 64, 0}};
+    const bool f32 = ab_type == TGEMM_F32;
+    const int(*pipes)[4] = f32 ? pipes32 : pipes16;
+    const int npipes = (base.variant & tg::kDma) ? (f32 ? 4 : (int)(sizeof(pipes16) / sizeof(pipes16[0]))) : 1;
     const int groups[] = {4, 8, 16};
     for (int ip = 0; ip < npipes; ++ip) {
         for (int g : groups) {

@@ -1,8 +1,8 @@
 // Device code of the dense tiled GEMM for MI355X (gfx950):
-// C = act(alpha * A * B + bias), binary16 or bfloat16 in, fp32 accumulate,
-// binary16, bfloat16 or fp32 out (the plain product is alpha = 1, no bias,
-// no activation). Included by the translation units that instantiate the
-// kernels, one per (input type, output type).
+// C = act(alpha * A * B + bias), binary16, bfloat16 or binary32 in, fp32
+// accumulate, binary16, bfloat16 or fp32 out (the plain product is alpha = 1,
+// no bias, no activation). Included by the translation units that
+// instantiate the kernels, one per (input type, output type).
 //
 // One workgroup owns one BM x BN output tile and walks K in steps (page 1,
 // "Using NVIDIA CUDA Tile to write a high-performance matrix multiply",
@@ -31,6 +31,12 @@
 //    cycles per instruction but issues less evenly.)
 //  * Every path multiplies the same operand values in the same 32-deep K
 //    slices in ascending order, so all of them produce the same bits.
+//  * Binary32 operands with B stored N x K run on the direct-to-LDS kernel
+//    as pairs of 16-bit units (K and the strides doubled): a 32-unit step is
+//    16 floats, a 128-bit fragment 4 consecutive-k floats, and each block
+//    takes four v_mfma_f32_16x16x4_f32 (slice()). The k each instruction
+//    and lane sums are those of the binary32 register-staged kernels below,
+//    so all binary32 paths produce the same bits too.
 //  * Workgroup -> tile: die-aware renumbering, then the grouped order of
 //    page 1, section "Swizzle" (tile_of in tgemm_plan.h).
 #pragma once
@@ -125,9 +131,11 @@ __device__ __forceinline__ u32x4 load8_elems(const uint16_t* __restrict__ p, int
 }
 
 // Fragments are carried as 8 x 16-bit bit patterns; AB selects how the
-// matrix core reads them.
+// matrix core reads them (16-bit types; slice() takes binary32 fragments
+// apart into four v_mfma_f32_16x16x4_f32).
 template <int AB>
 __device__ __forceinline__ f32x4 mfma16(const half8& b, const half8& a, const f32x4& c) {
+    static_assert(AB == 0 || AB == 1, "16-bit operand types");
     if constexpr (AB == 0)
         return __builtin_amdgcn_mfma_f32_16x16x32_f16(b, a, c, 0, 0, 0);
     else
@@ -375,7 +383,12 @@ __device__ __forceinline__ void zero_acc_mma(f32x4 (&acc)[NI][8]) {
 #pragma unroll
     for (int i = 0; i < NI; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = mfma16<AB>(z, z, f32x4{});
+        for (int j = 0; j < 8; ++j) {
+            if constexpr (AB == 2)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(0.0f, 0.0f, f32x4{}, 0, 0, 0);
+            else
+                acc[i][j] = mfma16<AB>(z, z, f32x4{});
+        }
 }
 
 // ---------------------------------------------------------------------------
@@ -906,7 +919,46 @@ __device__ __forceinline__ void slice(f32x4 (&acc)[I][8], const half8 (&fa)[I], 
             na[ai] = frag_a(f, so, next_s, ai);
         }
     };
-    if constexpr (I == 8) {
+    if constexpr (AB == 2) {
+        // binary32 operands: a 16-byte fragment holds 4 floats of one row,
+        // k = 4 (l / 16) + e within the 16-deep step, and v_mfma_f32_16x16x4_f32
+        // e (e = 0..3) takes float e of every lane, so it sums the products of
+        // k = e, 4 + e, 8 + e, 12 + e. A block's four instructions run back to
+        // back on its accumulator (the matrix core chains them; spread over
+        // the slice instead, the register allocator moves the accumulators
+        // between register files at every step), so each accumulator takes
+        // e = 0..3, step after step. A slice is 32 I instructions of 32
+        // cycles: the step's loads go first, one after every fourth
+        // instruction, so they have most of the slice to land, and the next
+        // slice's fragment reads spread evenly over the rest.
+        static_assert(KS == 32, "binary32 operands: 16-deep steps (32 16-bit units)");
+        constexpr int kQ = 8 * I;                      // blocks
+        constexpr int kM = 4 * kQ;                     // matrix instructions
+        constexpr int kR = READS ? kReads : 0;
+        constexpr int kLd = LOADS ? LaneLoads<KS, LA>::kL : 0;
+        constexpr int kLoadEnd = 4 * kLd;              // instructions that carry the loads
+        static_assert(kLoadEnd + kR <= kM, "at most one read or load after each matrix instruction");
+#pragma unroll
+        for (int q = 0; q < kQ; ++q) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int m = q * 4 + e;
+                const int i = q >> 3, j = (i & 1) ? 7 - (q & 7) : (q & 7);
+                const f32x4 av = __builtin_bit_cast(f32x4, fa[i]);
+                const f32x4 bv = __builtin_bit_cast(f32x4, fb[j]);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(bv[e], av[e],
+                                                                (ZC && e == 0) ? f32x4{} : acc[i][j], 0, 0, 0);
+                if (m < kLoadEnd) {
+                    if ((m & 3) == 3) issue_load<KS, NXK>(ra, rb, p, m >> 2, soa, sob, ld_a, ld_b, wave);
+                } else if (kR) {
+                    const int u = m - kLoadEnd, span = kM - kLoadEnd;
+                    if ((u + 1) * kR / span > u * kR / span) read(u * kR / span);
+                }
+                TG_COMPILER_FENCE();
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    } else if constexpr (I == 8) {
         constexpr int kLps = KS / 4;
         constexpr int kGap = 64 / kLps;                // MFMAs per load
         static_assert(2 * kReads <= 64, "reads must fit the even MFMA slots");
@@ -1170,6 +1222,7 @@ tgemm_dma_kernel(Args a) {
     static_assert(I == 8 || I == 4 || I == 2, "A blocks of 256, 128 or 64 rows");
     static_assert(Ctx::kLa >= 1, "the A block takes at least one load per step");
     static_assert(!PC || (KS == 32 && I == 4), "producer/consumer workgroups: 32-deep steps, 128 x 256 tiles");
+    static_assert(AB != 2 || (KS == 32 && NXK && !PC), "binary32 operands: 16-deep steps, B stored N x K");
     static_assert(S >= 2 && S <= 6 && Ctx::kSlots * 16 <= 160 * 1024, "LDS ring must fit 160 KiB");
     static_assert(I == 8 || PC || Ctx::kSlots * 16 <= 80 * 1024, "two workgroups per compute unit");
     constexpr int kL = Ctx::kLa + KS / 8;             // load instructions per step per loading wave
@@ -1406,15 +1459,16 @@ __device__ __forceinline__ f32x4 read_f32_frag(const u32x4* __restrict__ s_blk, 
     return __builtin_bit_cast(f32x4, s_blk[LdsF::slot(half * 128 + blk * 16 + (lane & 15), lane >> 4)]);
 }
 
-// Pipelined kernel (K a multiple of 4, and N too for B stored K x N, so that
-// no 4-float chunk straddles the end of a row): tile 256 x 128, 4 waves of
+// Pipelined kernel for B stored K x N (K and N multiples of 4, so that no
+// 4-float chunk straddles the end of a row; B stored N x K takes the
+// direct-to-LDS kernel above): tile 256 x 128, 4 waves of
 // 128 x 64 (8 x 4 blocks, 128 accumulators), two workgroups per compute unit
 // (two waves per SIMD from independent workgroups, so one workgroup's barrier
 // and staging gaps are covered by the other's matrix instructions). LDS per
 // workgroup: 2 stages of A (256 rows) and B (128 rows) blocks of 4 chunks,
 // 48 KiB. Staging: 16-byte buffer loads through per-tile resources that
-// return zeros past each operand's last element (rows past M or N, and for B
-// stored K x N rows past K); chunks at or past K (columns at or past N) are
+// return zeros past each operand's last element (rows past M, and B's rows
+// past K); chunks at or past K (columns at or past N) are
 // cleared with selects when the staged step is written to LDS. No branches,
 // so the accumulators stay in place across a step.
 constexpr int kF32Bn = kF32PipeBn;              // tile columns of the pipelined kernel
@@ -1429,15 +1483,13 @@ __device__ __forceinline__ Rsrc f32_rsrc(const uint16_t* X, int64_t ld, int nrow
 }
 
 // This lane's loads of a step: A chunks (t & 3) of rows (t >> 2) + 64 p,
-// p = 0..3; B stored N x K chunks (t & 3) of rows (t >> 2) + 64 p, p = 0..1;
-// B stored K x N the 2 x 4 block k = 2 (t >> 5) + 0..1, n = 4 (t & 31) + 0..3.
+// p = 0..3; B the 2 x 4 block k = 2 (t >> 5) + 0..1, n = 4 (t & 31) + 0..3.
 struct F32Lanes {
     unsigned va[4], vb[2];   // byte offsets from the tile's resource bases
-    int kc;                  // k offset (floats) of this lane's K-contiguous chunk within a step
-    int nc;                  // column offset (floats) of this lane's K x N chunk within the tile
+    int kc;                  // k offset (floats) of this lane's A chunk within a step
+    int nc;                  // column offset (floats) of this lane's B chunk within the tile
 };
 
-template <int NXK>
 __device__ __forceinline__ F32Lanes f32_lanes(const Args& a, int tid) {
     F32Lanes L;
     const unsigned c = (unsigned)(tid & 3);
@@ -1445,74 +1497,57 @@ __device__ __forceinline__ F32Lanes f32_lanes(const Args& a, int tid) {
     for (int p = 0; p < 4; ++p) {
         const unsigned row = (unsigned)((tid >> 2) + 64 * p);
         L.va[p] = (row * (unsigned)a.lda + 4u * c) * 4u;
-        if (NXK && p < 2) L.vb[p] = (row * (unsigned)a.ldb + 4u * c) * 4u;
     }
-    if (!NXK) {
-        const unsigned kr = (unsigned)(2 * (tid >> 5)), nb = (unsigned)(tid & 31);
+    const unsigned kr = (unsigned)(2 * (tid >> 5)), nb = (unsigned)(tid & 31);
 #pragma unroll
-        for (int q = 0; q < 2; ++q) L.vb[q] = ((kr + (unsigned)q) * (unsigned)a.ldb + 4u * nb) * 4u;
-    }
+    for (int q = 0; q < 2; ++q) L.vb[q] = ((kr + (unsigned)q) * (unsigned)a.ldb + 4u * nb) * 4u;
     L.kc = 4 * (tid & 3);
     L.nc = 4 * (tid & 31);
     return L;
 }
 
-// B stored K x N goes through a resource based at the step's first k row
-// (record count to B's last element, bspan bytes from k row 0 of the
-// tile's columns), so the lane offsets stay below 16 rows of B whatever K is;
-// a step at or past K gets an empty range and reads zeros.
-template <int NXK>
+// B goes through a resource based at the step's first k row (record count
+// to B's last element, bspan bytes from k row 0 of the tile's columns), so
+// the lane offsets stay below 16 rows of B whatever K is; a step at or past
+// K gets an empty range and reads zeros.
 __device__ __forceinline__ void f32_buf_load(u32x4 (&ra)[4], u32x4 (&rb)[2], const Rsrc& rsa, const Rsrc& rsb,
                                              int64_t bspan, const F32Lanes& L, const Args& a, int t) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the host pass cannot instantiate these target builtins
     const int k0 = t * kF32Ks;
     const __amdgpu_buffer_rsrc_t xa = __builtin_amdgcn_make_buffer_rsrc((void*)rsa.base, 0, rsa.nrec, 0x00020000);
     const unsigned soa = (unsigned)k0 * 4u;
-    const uint16_t* bbase = rsb.base;
-    int brec = rsb.nrec;
-    if (!NXK) {
-        int64_t span = bspan - (int64_t)k0 * a.ldb * 4;
-        span = span < 0 ? 0 : (span > (int64_t)kOob - 1 ? (int64_t)kOob - 1 : span);
-        bbase += (int64_t)k0 * a.ldb * 2;                   // 16-bit units: two per float
-        brec = (int)span;
-    }
-    const __amdgpu_buffer_rsrc_t xb = __builtin_amdgcn_make_buffer_rsrc((void*)bbase, 0, brec, 0x00020000);
-    const unsigned sob = NXK ? (unsigned)k0 * 4u : 0u;
+    int64_t span = bspan - (int64_t)k0 * a.ldb * 4;
+    span = span < 0 ? 0 : (span > (int64_t)kOob - 1 ? (int64_t)kOob - 1 : span);
+    const uint16_t* bbase = rsb.base + (int64_t)k0 * a.ldb * 2;   // 16-bit units: two per float
+    const __amdgpu_buffer_rsrc_t xb = __builtin_amdgcn_make_buffer_rsrc((void*)bbase, 0, (int)span, 0x00020000);
 #pragma unroll
     for (int p = 0; p < 4; ++p)
         ra[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xa, (int)L.va[p], (int)soa, 0));
 #pragma unroll
     for (int p = 0; p < 2; ++p)
-        rb[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xb, (int)L.vb[p], (int)sob, 0));
+        rb[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xb, (int)L.vb[p], 0, 0));
 #else
     (void)ra; (void)rb; (void)rsa; (void)rsb; (void)bspan; (void)L; (void)a; (void)t;
 #endif
 }
 
 // Write step t's staged operands into an LDS stage (A block at `s`, B block
-// kF32ABlk slots later), clearing chunks at or past K (columns at or past N
-// for B stored K x N). The selects sit here, a half step after the loads were
-// issued, so they never wait on memory inside the matrix-instruction stream.
-template <int NXK>
+// kF32ABlk slots later), clearing A chunks at or past K and B columns at or
+// past N. The selects sit here, a half step after the loads were issued, so
+// they never wait on memory inside the matrix-instruction stream.
 __device__ __forceinline__ void f32_store_step(u32x4* __restrict__ s, u32x4 (&ra)[4], u32x4 (&rb)[2],
                                                const F32Lanes& L, const Args& a, int n0, int t, int tid) {
     const bool k_ok = t * kF32Ks + L.kc < a.K;
 #pragma unroll
     for (int p = 0; p < 4; ++p) s[LdsF::slot((tid >> 2) + 64 * p, tid & 3)] = k_ok ? ra[p] : u32x4{};
-    u32x4* sb = s + kF32ABlk;
-    if (NXK) {
+    // B's 2 x 4 block -> 4 rows (columns n) x 2 floats (k = 2 (t >> 5) + 0..1):
+    // 8-byte half (t >> 5) & 1 of chunk (t >> 6) of row 4 (t & 31) + v
+    const bool n_ok = n0 + L.nc < a.N;
+    u32x2* sb2 = reinterpret_cast<u32x2*>(s + kF32ABlk);
+    const int kp = tid >> 5, nb = tid & 31;
 #pragma unroll
-        for (int p = 0; p < 2; ++p) sb[LdsF::slot((tid >> 2) + 64 * p, tid & 3)] = k_ok ? rb[p] : u32x4{};
-    } else {
-        // 2 x 4 block -> 4 rows (columns n) x 2 floats (k = 2 (t >> 5) + 0..1):
-        // 8-byte half (t >> 5) & 1 of chunk (t >> 6) of row 4 (t & 31) + v
-        const bool n_ok = n0 + L.nc < a.N;
-        u32x2* sb2 = reinterpret_cast<u32x2*>(sb);
-        const int kp = tid >> 5, nb = tid & 31;
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-            sb2[2 * LdsF::slot(4 * nb + v, kp >> 1) + (kp & 1)] = n_ok ? u32x2{rb[0][v], rb[1][v]} : u32x2{};
-    }
+    for (int v = 0; v < 4; ++v)
+        sb2[2 * LdsF::slot(4 * nb + v, kp >> 1) + (kp & 1)] = n_ok ? u32x2{rb[0][v], rb[1][v]} : u32x2{};
 }
 
 // The wave's fragments as 8-byte halves of its 16-byte chunks: lo = k0 + 4g +
@@ -1562,7 +1597,7 @@ __device__ __forceinline__ void f32_half(f32x4 (&acc)[8][4], F32Frags& f, const 
 // read. The section boundaries are pinned: otherwise the compiler moves
 // matrix instructions across the staging block and leaves the next step's
 // reads exposed.
-template <int TY, int NXK>
+template <int TY>
 __global__ void __launch_bounds__(NTHREADS)
 __attribute__((amdgpu_waves_per_eu(2, 2)))
 tgemm_f32in_kernel(Args a) {
@@ -1578,11 +1613,11 @@ tgemm_f32in_kernel(Args a) {
     tile_of((int)blockIdx.x, a.W, a.grid_m, a.grid_n, a.group_m, a.num_xcd, &tm, &tn);
     const int m0 = tm * BM, n0 = tn * kF32Bn;
     const int nk = (a.K + kF32Ks - 1) / kF32Ks;
-    const F32Lanes L = f32_lanes<NXK>(a, tid);
+    const F32Lanes L = f32_lanes(a, tid);
     const Rsrc rsa = f32_rsrc(a.A, a.lda, a.M, a.K, m0);
-    // B: N x K rows n0.. ; K x N columns n0.. of all K rows
-    const Rsrc rsb = NXK ? f32_rsrc(a.B, a.ldb, a.N, a.K, n0) : Rsrc{a.B + 2 * n0, 0};
-    const int64_t bspan = NXK ? 0 : ((int64_t)(a.K - 1) * a.ldb + (a.N - n0)) * 4;
+    // B: columns n0.. of all K rows (rebased at every step)
+    const Rsrc rsb = Rsrc{a.B + 2 * n0, 0};
+    const int64_t bspan = ((int64_t)(a.K - 1) * a.ldb + (a.N - n0)) * 4;
 
     // stage-0 read positions (8-byte units) of 16-row block 0; block i lies
     // 128 further, stage 1 2 * kF32StageSlots further, the hi half 1 further
@@ -1599,14 +1634,14 @@ tgemm_f32in_kernel(Args a) {
     F32Frags f;
     u32x4 ra[4], rb[2];
     if (nk > 0) {
-        f32_buf_load<NXK>(ra, rb, rsa, rsb, bspan, L, a, 0);
-        f32_store_step<NXK>(smem, ra, rb, L, a, n0, 0, tid);
+        f32_buf_load(ra, rb, rsa, rsb, bspan, L, a, 0);
+        f32_store_step(smem, ra, rb, L, a, n0, 0, tid);
         __syncthreads();
 #pragma unroll
         for (int i = 0; i < 8; ++i) f.alo[i] = pa0[i * 128];
 #pragma unroll
         for (int j = 0; j < 4; ++j) f.blo[j] = pb0[j * 128];
-        f32_buf_load<NXK>(ra, rb, rsa, rsb, bspan, L, a, 1);   // past the last step: zeros
+        f32_buf_load(ra, rb, rsa, rsb, bspan, L, a, 1);   // past the last step: zeros
     }
     for (int t = 0; t < nk; ++t) {
         const int st = t & 1;
@@ -1615,8 +1650,8 @@ tgemm_f32in_kernel(Args a) {
         TG_COMPILER_FENCE();
         __builtin_amdgcn_sched_barrier(0);
         wait_vmcnt<0>();                              // step t + 1 in the staging registers
-        f32_store_step<NXK>(smem + (st ^ 1) * kF32StageSlots, ra, rb, L, a, n0, t + 1, tid);
-        f32_buf_load<NXK>(ra, rb, rsa, rsb, bspan, L, a, t + 2);
+        f32_store_step(smem + (st ^ 1) * kF32StageSlots, ra, rb, L, a, n0, t + 1, tid);
+        f32_buf_load(ra, rb, rsa, rsb, bspan, L, a, t + 2);
         TG_COMPILER_FENCE();
         __builtin_amdgcn_sched_barrier(0);
         f32_half<0, 48, 64>(acc, f, pa0 + so, pb0 + so);

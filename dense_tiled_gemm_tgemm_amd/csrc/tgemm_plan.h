@@ -105,6 +105,12 @@ struct Plan {
     int grid;             // workgroups launched (W, or the compute units for a persistent launch)
 };
 
+// Binary32 operands (B stored N x K) planned onto the direct-to-LDS kernel:
+// it is launched with K and both row strides counted in 16-bit units.
+inline bool f32_on_dma(const Plan& pl) {
+    return pl.ab_type == TGEMM_F32 && (pl.variant & kDma) && pl.layout == TGEMM_B_NxK;
+}
+
 inline bool span_bytes(int64_t rows, int64_t cols, int64_t ld, uint64_t* bytes, int esize = 2) {
     // bytes covered by a row-major rows x cols array of esize-byte elements
     if (rows <= 0 || cols <= 0) {
@@ -144,7 +150,9 @@ inline int make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
     const int c_size = c_type == TGEMM_F32 ? 4 : 2;
     if (force_generic != 0 && force_generic != 1) return TGEMM_ERR_INVALID;
     if (group_m < 0 || group_m > 1024 || num_xcd < 0 || num_xcd > 64) return TGEMM_ERR_INVALID;
-    if (k_step != 0 && k_step != 32 && k_step != 64) return TGEMM_ERR_INVALID;
+    // (binary32 operands always step 16 floats: 0 or 16, the value a plan reports)
+    if (k_step != 0 && k_step != 32 && k_step != 64 && !(ab_type == TGEMM_F32 && k_step == kF32KStep))
+        return TGEMM_ERR_INVALID;
     if (stages != 0 && (stages < 2 || stages > 5)) return TGEMM_ERR_INVALID;
     if (k_step == 64 && stages != 0 && stages != 2) return TGEMM_ERR_INVALID;  // 2 x 64 KiB fills LDS
     if (tile_m != 0 && tile_m != 256 && tile_m != 128 && tile_m != 64) return TGEMM_ERR_INVALID;
@@ -209,18 +217,29 @@ inline int make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
     // (row strides of at least 8 elements: then a 16-byte access can run past
     // the end of an operand only in its last row, which the kernel reloads
     // element by element; narrower operands take the register-staged kernel)
-    // (binary32 operands have kernels of their own: the kDma bit then marks the
-    // pipelined one, whose buffer loads need K (and, for B stored K x N, N) a
-    // multiple of 4 and every byte offset of a tile below 2^31; a K x N B is
-    // rebased at every K step there too)
+    // (binary32 operands with B stored N x K run on the same kernel as pairs
+    // of 16-bit units: row strides of at least 4 floats and at most half the
+    // 16-bit limit. With B stored K x N the kDma bit marks the pipelined
+    // register-staged binary32 kernel, whose buffer loads need K and N
+    // multiples of 4 and every byte offset of a tile below 2^31; its B is
+    // rebased at every K step too)
     const bool dma =
         ab_type == TGEMM_F32
-            ? (!force_generic && K > 0 && K % 4 == 0 && lda <= kMaxDmaLd / 2 && ldb <= kMaxDmaLd / 2 &&
-               (b_layout == TGEMM_B_NxK || N % 4 == 0))
+            ? (b_layout == TGEMM_B_NxK
+                   ? (!force_generic && K > 0 && lda >= 4 && ldb >= 4 && lda <= kMaxDmaLd / 2 &&
+                      ldb <= kMaxDmaLd / 2)
+                   : (!force_generic && K > 0 && K % 4 == 0 && N % 4 == 0 && lda <= kMaxDmaLd / 2 &&
+                      ldb <= kMaxDmaLd / 2))
             : (!force_generic && K > 0 && lda >= 8 && ldb >= 8 && lda <= kMaxDmaLd && ldb <= kMaxDmaLd);
+    // binary32 operands on the direct-to-LDS kernel (B stored N x K)
+    const bool f32_dma = ab_type == TGEMM_F32 && dma && b_layout == TGEMM_B_NxK;
     pl->variant = (vec_ab ? kVecAB : 0) | (vec_c ? kVecC : 0) |
                   (b_layout == TGEMM_B_NxK ? kLayoutNxK : 0) | (dma ? kDma : 0);
-    if (ab_type == TGEMM_F32) {
+    if (f32_dma) {
+        // 16 floats per step whatever k_step asks; 2 stages (256-row tiles) or 3
+        pl->k_step = kF32KStep;
+        pl->stages = stages ? stages : (bm != BM ? kDefaultSmallStages : 2);
+    } else if (ab_type == TGEMM_F32) {
         pl->k_step = kF32KStep;
         pl->stages = 2;
     } else if (dma) {
@@ -234,12 +253,12 @@ inline int make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
         pl->stages = 2;
     }
     // the small tiles and producer/consumer workgroups exist on the
-    // direct-to-LDS path only (16-bit operands)
-    if (bm != BM && !(dma && ab_type != TGEMM_F32)) return TGEMM_ERR_UNSUPPORTED;
+    // direct-to-LDS path only
+    if (bm != BM && !(dma && (ab_type != TGEMM_F32 || f32_dma))) return TGEMM_ERR_UNSUPPORTED;
     pl->bm = bm;
     pl->producers = producers;
     pl->threads = NTHREADS + producers * 64;
-    pl->bn = (ab_type == TGEMM_F32 && dma) ? kF32PipeBn : BN;
+    pl->bn = (ab_type == TGEMM_F32 && dma && !f32_dma) ? kF32PipeBn : BN;
     const int64_t gn = (N + pl->bn - 1) / pl->bn;
     if (gm * gn > kMaxDim) return TGEMM_ERR_UNSUPPORTED;
     pl->grid_m = (int)gm;

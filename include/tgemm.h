@@ -125,7 +125,8 @@ int tgemm_f16(int64_t M, int64_t N, int64_t K,
  *                  other launch choice 0 and no tuned choice): 256 rows,
  *                  except where a grid of 256-row tiles would fill at most
  *                  half of the compute units (128 rows) or at most a
- *                  quarter (64 rows). Other paths accept only 0 and 256
+ *                  quarter (64 rows); binary32 operands follow their own
+ *                  rule (tgemm_gemm). Other paths accept only 0 and 256
  *                  (else TGEMM_ERR_UNSUPPORTED).
  *   producers:     0, or 4: producer/consumer workgroups (page 5, Croqtile
  *                  tutorial "dense GEMM fp16 from naive", section "Kernel 3:
@@ -164,10 +165,17 @@ int tgemm_f16_config(int64_t M, int64_t N, int64_t K,
  *   ab_type: TGEMM_F16, TGEMM_BF16 or TGEMM_F32, the type of both A and B
  *            (lda and ldb count elements of that type; binary32 operands
  *            must be 4-byte aligned). Binary32 operands run on
- *            v_mfma_f32_16x16x4_f32 with fp32 accumulation, one kernel
- *            family staged through registers (16-deep K steps, 2 LDS stages:
- *            the k_step and stages choices of tgemm_gemm_config do not apply
- *            to it).
+ *            v_mfma_f32_16x16x4_f32 with fp32 accumulation in 16-deep K
+ *            steps. With B stored N x K (and K > 0, row strides of 4 to
+ *            2,000,000 floats) they take the direct-to-LDS kernel of the
+ *            16-bit types on their bytes: tiles of 256, 128 or 64 rows, an
+ *            LDS ring of 2 (default), 3 or 4 stages at 256 rows and 3 for the
+ *            smaller tiles; automatic launches take 64-row tiles unless
+ *            256-row tiles fill at least 7/8 of their rounds over the compute
+ *            units. With B stored K x N a kernel staged through registers
+ *            (256 x 128 tiles, 2 stages). The k_step choice of
+ *            tgemm_gemm_config does not apply to binary32 operands (a plan
+ *            reports 16), nor stages and tile_m to B stored K x N.
  *   c_type:  TGEMM_F16, TGEMM_BF16 or TGEMM_F32; ldc counts elements of
  *            that type (C[i*ldc + j]).
  *   bias:    NULL, or N fp32 values in device memory (4-byte aligned),
@@ -192,8 +200,9 @@ int tgemm_gemm(int64_t M, int64_t N, int64_t K,
  * for every K step, ring depth and tile choice listed there (producer/
  * consumer workgroups with 3 or 5 stages); every other 16-bit combination
  * for the default ring depth of each K step (2 stages at 64, 4 at 32) and of
- * the 128- and 64-row tiles (3), without producer/consumer workgroups: other
- * choices return TGEMM_ERR_UNSUPPORTED for it, with nothing enqueued.
+ * the 128- and 64-row tiles (3), without producer/consumer workgroups;
+ * binary32 operands as listed under tgemm_gemm. Other choices return
+ * TGEMM_ERR_UNSUPPORTED for the combination, with nothing enqueued.
  */
 int tgemm_gemm_config(int64_t M, int64_t N, int64_t K,
                       int ab_type, const void* A, int64_t lda,
@@ -272,8 +281,9 @@ int tgemm_last_hip_error(void);
  * Returns TGEMM_OK and fills info[0..9]:
  *   info[0] variant bits: bit0 128-bit A/B loads, bit1 vector C stores
  *           (64-bit runs of a 16-bit C, 128-bit runs of an fp32 C), bit2 B
- *           layout is NxK, bit3 the pipelined kernel (16-bit operands:
- *           streamed directly into LDS; binary32 operands: buffer loads)
+ *           layout is NxK, bit3 the pipelined kernel (streamed directly
+ *           into LDS; binary32 operands with B stored K x N: buffer loads
+ *           into registers)
  *   info[1] tile rows        info[2] tile columns      info[3] K step
  *   info[4] workgroups launched (the tile count ceil(M/BM) * ceil(N/BN), or
  *           compute_units when each workgroup walks several tiles; 0 when

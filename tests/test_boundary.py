@@ -230,6 +230,12 @@ def test_tile_choices_plan():
             assert _plan_ex(1024, 1024, 1024, ab=ab, ct=ct, tile_m=tm, **kw)[0] == tg.TGEMM_OK
         assert _plan_ex(1024, 1024, 1024, ab=ab, ct=ct, tile_m=128, stages=2, **kw)[0] == tg.TGEMM_ERR_UNSUPPORTED
         assert _plan_ex(1024, 1024, 1024, ab=ab, ct=ct, producers=4, **kw)[0] == tg.TGEMM_ERR_UNSUPPORTED
+    # binary32 operands: the smaller tiles with B stored N x K (direct-to-LDS), not K x N
+    for tm in (128, 64):
+        rc, info = _plan_ex(1024, 1024, 1024, ab="f32", ct="f32", lay="NxK", tile_m=tm)
+        assert rc == 0 and (info["bm"], info["bk"], info["stages"]) == (tm, 16, 3)
+    assert _plan_ex(1024, 1024, 1024, ab="f32", ct="f32", lay="NxK", tile_m=128, stages=2)[0] == \
+        tg.TGEMM_ERR_UNSUPPORTED
     assert _plan_ex(1024, 1024, 1024, ab="f32", ct="f32", tile_m=128)[0] == tg.TGEMM_ERR_UNSUPPORTED
 
 
@@ -258,7 +264,28 @@ def test_small_grids_take_smaller_tiles():
     assert info["bm"] == 256
     for ab, ct in (("bf16", "f32"), ("f16", "bf16")):
         assert _plan_ex(256, 256, 256, ab=ab, ct=ct, alpha=0.5)[1]["bm"] == 64
-    assert _plan_ex(256, 256, 256, ab="f32", ct="f32")[1]["bm"] == 256
+    assert _plan_ex(256, 256, 256, ab="f32", ct="f32")[1]["bm"] == 256      # B stored K x N
+
+
+@pytest.mark.parametrize("M,N,cu,bm", [
+    (256, 256, 256, 64), (4096, 2048, 256, 64),          # a tile, half a round
+    (2560, 4096, 256, 64), (3072, 4096, 256, 64),        # 160 and 192 tiles on 256 units
+    (3584, 4096, 256, 256), (4096, 4096, 256, 256),      # 224 (7/8) and 256 tiles
+    (5120, 4096, 256, 64), (6144, 4096, 256, 64),        # 320 and 384: rounds 5/8 and 3/4 full
+    (8192, 8192, 256, 256), (8192, 12288, 256, 256),     # 1024 and 1536: whole rounds
+    (4096, 4096, 255, 64), (3584, 4096, 224, 256),       # the fill is counted on the device's units
+])
+def test_binary32_tile_rows_follow_round_fill(M, N, cu, bm):
+    """Binary32 operands (B stored N x K): 64-row tiles unless 256-row tiles
+    fill at least 7/8 of their rounds over the compute units; explicit tile
+    rows and B stored K x N are left alone."""
+    rc, info = _plan_ex(M, N, 2048, ab="f32", ct="f32", lay="NxK", compute_units=cu)
+    assert rc == 0 and info["bm"] == bm
+    assert info["stages"] == (2 if bm == 256 else 3)
+    rc, info = _plan_ex(M, N, 2048, ab="f32", ct="f32", lay="NxK", compute_units=cu, tile_m=256)
+    assert rc == 0 and info["bm"] == 256
+    rc, info = _plan_ex(M, N, 2048, ab="f32", ct="f32", compute_units=cu)
+    assert rc == 0 and info["bm"] == 256
 
 
 def test_default_die_count_follows_the_compute_units():
@@ -483,31 +510,57 @@ def test_tuning_rejects_bad_arguments_without_gpu():
 
 def test_fp32_operand_plans():
     V, CV, NXK, PIPE = 1, 2, 4, 8
-    # binary32 operands: 16-deep steps, 2 stages of 2 x 256 x 16 floats; the
-    # pipelined kernel when K is a multiple of 4 (and N too for B stored K x N)
+    # binary32 operands with B stored N x K: the direct-to-LDS kernel on the
+    # operands' bytes, 256 x 256 tiles, 16-deep steps, 2 stages of
+    # 2 x 256 x 16 floats, one tile per workgroup
     rc, info = _plan_ex(8192, 8192, 8192, ab="f32", ct="f32", lay="NxK")
     assert rc == 0 and info["variant"] == V | CV | NXK | PIPE
-    # the pipelined kernel's tile is 256 x 128 (two workgroups per compute unit)
+    assert (info["bm"], info["bn"]) == (256, 256)
+    assert (info["bk"], info["stages"], info["lds_bytes"], info["workgroups"]) == (16, 2, 64 * 1024, 1024)
+    # the K step choice does not apply; rings of 2 or 3 stages are built
+    rc2, info2 = _plan_ex(8192, 8192, 8192, ab="f32", ct="f32", lay="NxK", k_step=32)
+    assert rc2 == 0 and info2 == info
+    rc3, info3 = _plan_ex(8192, 8192, 8192, ab="f32", ct="f32", lay="NxK", stages=3)
+    assert rc3 == 0 and (info3["stages"], info3["lds_bytes"]) == (3, 96 * 1024)
+    assert _plan_ex(8192, 8192, 8192, ab="f32", ct="f32", lay="NxK", stages=5)[0] == tg.TGEMM_ERR_UNSUPPORTED
+    assert _plan_ex(8192, 8192, 8192, ab="f32", ct="f32", lay="NxK", producers=4)[0] == tg.TGEMM_ERR_UNSUPPORTED
+    # any K, and row strides of at least 4 floats (8 16-bit units)
+    rc, info = _plan_ex(300, 200, 101, ab="f32", ct="f16", lay="NxK")
+    assert rc == 0 and info["variant"] == CV | NXK | PIPE
+    rc, info = _plan_ex(300, 200, 4, ab="f32", ct="f32", lay="NxK")
+    assert rc == 0 and info["variant"] & PIPE
+    rc, info = _plan_ex(300, 200, 3, ab="f32", ct="f32", lay="NxK")
+    assert rc == 0 and not info["variant"] & PIPE
+    rc, info = _plan_ex(300, 202, 100, ab="f32", ct="f16", lay="NxK", ldc=208)
+    assert rc == 0 and info["variant"] == V | CV | NXK | PIPE
+    # B stored K x N: the pipelined register-staged kernel when K and N are
+    # multiples of 4; its tile is 256 x 128 (two workgroups per compute unit)
+    rc, info = _plan_ex(8192, 8192, 8192, ab="f32", ct="f32")
+    assert rc == 0 and info["variant"] == V | CV | PIPE
     assert (info["bm"], info["bn"]) == (256, 128)
     assert (info["bk"], info["stages"], info["lds_bytes"], info["workgroups"]) == (16, 2, 48 * 1024, 2048)
-    # launch choices for the 16-bit pipelines do not apply
-    rc2, info2 = _plan_ex(8192, 8192, 8192, ab="f32", ct="f32", lay="NxK", k_step=32, stages=5)
+    # launch choices for the direct-to-LDS pipelines do not apply to it
+    rc2, info2 = _plan_ex(8192, 8192, 8192, ab="f32", ct="f32", k_step=32, stages=5)
     assert rc2 == 0 and info2 == info
     # K not a multiple of 4, or N for B stored K x N, or forced: the general kernel
     rc, info = _plan_ex(300, 200, 101, ab="f32", ct="f16", lda=101)
     assert rc == 0 and info["variant"] == CV
     rc, info = _plan_ex(300, 202, 100, ab="f32", ct="f16", lda=100, ldb=202, ldc=208)
     assert rc == 0 and info["variant"] == CV
-    rc, info = _plan_ex(300, 202, 100, ab="f32", ct="f16", lay="NxK", ldc=208)
-    assert rc == 0 and info["variant"] == V | CV | NXK | PIPE
     rc, info = _plan_ex(300, 200, 100, ab="f32", ct="f16", lda=100, ldb=200, force_generic=1)
     assert rc == 0 and info["variant"] == CV
     assert (info["bn"], info["lds_bytes"], info["workgroups"]) == (256, 64 * 1024, 2)
-    # 4-byte-aligned bases are fine for the pipelined kernel (buffer loads)
+    rc, info = _plan_ex(300, 200, 100, ab="f32", ct="f16", lay="NxK", force_generic=1)
+    assert rc == 0 and info["variant"] == CV | NXK
+    # 4-byte-aligned bases are fine for both (buffer loads)
     rc, info = _plan_ex(300, 200, 100, ab="f32", ct="bf16", A=PA + 4)
     assert rc == 0 and info["variant"] == CV | PIPE
+    rc, info = _plan_ex(300, 200, 100, ab="f32", ct="bf16", lay="NxK", A=PA + 4)
+    assert rc == 0 and info["variant"] == CV | NXK | PIPE
     # strides past the 32-bit offset limits: the general kernel
     rc, info = _plan_ex(300, 200, 100, ab="f32", ct="f32", lay="NxK", lda=2_000_004)
+    assert rc == 0 and not info["variant"] & PIPE
+    rc, info = _plan_ex(300, 200, 100, ab="f32", ct="f32", lay="NxK", ldb=2_000_004)
     assert rc == 0 and not info["variant"] & PIPE
     rc, info = _plan_ex(300, 200, 100, ab="f32", ct="f32", ldb=2_000_004)
     assert rc == 0 and not info["variant"] & PIPE

@@ -122,3 +122,40 @@ def test_automatic_pipeline_choice(lay, K, tiles_m, ab, want):
     other = tg.gemm(A, B, lay, k_step=64 if want[0] == 32 else 32)
     torch.cuda.synchronize()
     assert torch.equal(auto.view(torch.int16), other.view(torch.int16))
+
+
+@pytest.mark.parametrize("lay,cands", [("NxK", 12), ("KxN", 3)])
+def test_tuning_binary32_operands(oracle_mod, lay, cands):
+    """Binary32 operands: with B stored N x K the tuner tries the direct-to-LDS
+    kernel's ring depths (2, 3 at 256 rows) and its 128- and 64-row tiles
+    (4 pipelines x 3 group heights); with B stored K x N only the group height
+    of the register-staged kernel. The recorded choice (K step 16 floats) is
+    used by later automatic calls and changes no bits."""
+    print(f"case tuning f32 {lay}", flush=True)
+    M, N, K = 3584, 4096, 1000          # 14 x 16 tiles of 256 x 256
+    A = inputs.random_f32((M, K), 11)
+    B = inputs.random_f32((N, K) if lay == "NxK" else (K, N), 12)
+    Ad = torch.from_numpy(A).to(DEV)
+    Bd = torch.from_numpy(B).to(DEV)
+    base = tg.gemm(Ad, Bd, lay, out_dtype=torch.float32)
+    C, chosen = tg.tune(Ad, Bd, lay, out_dtype=torch.float32, rounds=3)
+    torch.cuda.synchronize()
+    print(f"  chosen {chosen}", flush=True)
+    assert chosen["candidates"] == cands and chosen["k_step"] == 16
+    if lay == "NxK":
+        assert (chosen["stages"], chosen["tile_m"]) in {(2, 256), (3, 256), (3, 128), (3, 64)}
+    else:
+        assert (chosen["stages"], chosen["tile_m"]) == (2, 256)
+    assert torch.equal(C, base)
+    rc, plan = _plan(Ad, Bd, C, lay, "f32", "f32")
+    assert rc == 0
+    assert (plan["bk"], plan["stages"], plan["group_m"], plan["bm"]) == \
+        (chosen["k_step"], chosen["stages"], chosen["group_m"], chosen["tile_m"])
+    again = tg.gemm(Ad, Bd, lay, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(again, base)
+    got = again.cpu().numpy()
+    I, J = inputs.sample_points(M, N, 4096, 13)
+    ref, tol = oracle_mod.gemm_ex(A, B, lay, "f32", I=I, J=J)
+    res = oracle_mod.check_ex(got[I, J], "f32", ref, tol)
+    assert res["nfail"] == 0, res
