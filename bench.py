@@ -307,6 +307,10 @@ def main():
                     help="instead of the GEMM, time the matrix-core ceiling probe (the GEMM's "
                          "instruction stream on the workload's values, without synchronization, "
                          "tile changes or C stores) and print its TFLOP/s")
+    ap.add_argument("--stream-probes", metavar="KINDS",
+                    help="instead of the GEMM, time the instruction-stream probes (comma-separated kinds of "
+                         "include/tgemm_probe.h in lower case without the TGEMM_STREAM_ prefix, or 'all') on "
+                         "the workload's A values and on zeros; one JSON line each")
     ap.add_argument("--torch-matmul", action="store_true",
                     help="instead of this library's GEMM, time torch.matmul (the vendor BLAS) on "
                          "the same inputs and print its TFLOP/s (context, not the headline)")
@@ -374,6 +378,32 @@ def main():
             torch.cuda.synchronize()
         return n, time.perf_counter() - t_w
 
+    def probe_data(A16):
+        """The workload's A as probe operands: its first 64 MiB (a power of two
+        of at least 1 MiB, the values repeated for a smaller A)."""
+        a16 = np.ascontiguousarray(A16).view(np.uint16).reshape(-1)
+        if a16.nbytes < (1 << 20):                    # the probes read at least 1 MiB: repeat the values
+            a16 = np.resize(a16, (1 << 20) // 2)
+        nbytes = 1 << min(26, int(a16.nbytes).bit_length() - 1)
+        return torch.from_numpy(a16[: nbytes // 2].view(np.int16).copy()).to("cuda:0"), nbytes
+
+    def probe_time(launch, wg, steps):
+        """Mean ms per launch of a probe (after the warm-up) and its average
+        clock in GHz (one more launch records each workgroup's shader cycles
+        and 100 MHz reference ticks)."""
+        stream = torch.cuda.current_stream()
+        clk = torch.zeros(2 * wg, dtype=torch.int64, device="cuda:0")
+        warm_up(launch)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(steps):
+            launch()
+        ev[1].record(stream)
+        launch(clk.data_ptr())
+        torch.cuda.synchronize()
+        c = clk.cpu().numpy().reshape(wg, 2).astype(np.float64)
+        return ev[0].elapsed_time(ev[1]) / steps, float(c[:, 0].sum() / c[:, 1].sum() / 10.0)
+
     def mfma_ceiling(A16, name, steps):
         """The matrix-core ceiling probe (libtgemm_probe.so): the GEMM's
         instruction stream without synchronization, tile changes or C stores,
@@ -382,36 +412,50 @@ def main():
         operands that never toggle). TFLOP/s and the probe's average clock."""
         from dense_tiled_gemm_tgemm_amd import probe
         probe.load()
-        a16 = np.ascontiguousarray(A16).view(np.uint16).reshape(-1)
-        if a16.nbytes < (1 << 20):                    # the probe reads at least 1 MiB: repeat the values
-            a16 = np.resize(a16, (1 << 20) // 2)
-        nbytes = 1 << min(26, int(a16.nbytes).bit_length() - 1)
-        data = torch.from_numpy(a16[: nbytes // 2].view(np.int16).copy()).to("cuda:0")
+        data, nbytes = probe_data(A16)
         stream = torch.cuda.current_stream()
         wg, iters = 256, 400
         out = torch.empty(wg * 256, dtype=torch.float32, device="cuda:0")
-        clk = torch.zeros(2 * wg, dtype=torch.int64, device="cuda:0")
         flops = wg * 4 * iters * 128 * 2.0 * 16 * 16 * 32
 
         def probe_ms(buf):
             def one(c=None):
                 probe.mfma_issue_probe(wg, iters, buf.data_ptr(), nbytes, out.data_ptr(), c, stream.cuda_stream)
-            warm_up(one)
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-            ev[0].record(stream)
-            for _ in range(steps):
-                one()
-            ev[1].record(stream)
-            one(clk.data_ptr())                       # one more launch records the clock
-            torch.cuda.synchronize()
-            c = clk.cpu().numpy().reshape(wg, 2).astype(np.float64)
-            return ev[0].elapsed_time(ev[1]) / steps, float(c[:, 0].sum() / c[:, 1].sum() / 10.0)
+            return probe_time(one, wg, steps)
 
         ms, ghz = probe_ms(data)
         ms0, ghz0 = probe_ms(torch.zeros_like(data))
         return {"data": f"{name} A, first {nbytes >> 20} MiB", "workgroups": wg, "iters": iters,
                 "ms": round(ms, 5), "tflops": round(flops / ms / 1e9, 1), "clock_ghz": round(ghz, 3),
                 "tflops_zero_operands": round(flops / ms0 / 1e9, 1), "clock_ghz_zero_operands": round(ghz0, 3)}
+
+    if args.stream_probes:
+        # the GEMM's instruction stream taken apart (libtgemm_probe.so): per
+        # kind and operand set, TFLOP/s, average clock, and matrix-core issue
+        # efficiency = TFLOP/s over the dense peak scaled to that clock
+        from dense_tiled_gemm_tgemm_amd import probe
+        probe.load()
+        name = args.workload or inputs.HEADLINE
+        A, _ = inputs.make_inputs(inputs.WORKLOADS[name])
+        data, nbytes = probe_data(A)
+        zeros = torch.zeros_like(data)
+        stream = torch.cuda.current_stream()
+        wg, iters = 256, 200
+        out = torch.empty(wg * 512, dtype=torch.float32, device="cuda:0")
+        kinds = args.stream_probes.split(",") if args.stream_probes != "all" else list(probe.STREAM_KINDS)
+        for kind in kinds:
+            _, _, fpr = probe.STREAM_KINDS[kind]
+            peak = PEAK_F32_TFLOPS if kind.startswith("f32") else PEAK_F16_TFLOPS
+            for tag, buf in (("workload", data), ("zeros", zeros)):
+                def one(c=None, buf=buf, kind=kind):
+                    probe.mfma_stream_probe(kind, wg, iters, buf.data_ptr(), nbytes, out.data_ptr(), c,
+                                            stream.cuda_stream)
+                ms, ghz = probe_time(one, wg, args.steps)
+                tf = wg * iters * float(fpr) / ms / 1e9
+                print(json.dumps({"probe": "stream", "kind": kind, "operands": tag, "data": f"{name} A",
+                                  "ms": round(ms, 5), "tflops": round(tf, 1), "clock_ghz": round(ghz, 3),
+                                  "issue_efficiency": round(tf / (peak * ghz / 2.4), 4)}), flush=True)
+        return
 
     if args.mfma_ceiling:
         tg.load()

@@ -31,6 +31,8 @@ def load():
     lib = ctypes.CDLL(PROBE_LIB_PATH)
     lib.tgemm_mfma_issue_probe.restype = _INT
     lib.tgemm_mfma_issue_probe.argtypes = [_I64, _INT, _P, _I64, _P, _P, _P]
+    lib.tgemm_mfma_stream_probe.restype = _INT
+    lib.tgemm_mfma_stream_probe.argtypes = [_INT, _I64, _INT, _P, _I64, _P, _P, _P]
     lib.tgemm_xcd_probe.restype = _INT
     lib.tgemm_xcd_probe.argtypes = [_I64, _P, _P]
     _lib = lib
@@ -44,6 +46,34 @@ def mfma_issue_probe(workgroups: int, iters: int, data_ptr: int, data_bytes: int
                                            clocks_ptr, stream))
     if rc != TGEMM_OK:
         raise TgemmError(rc, "mfma_issue_probe")
+
+
+# instruction-stream probe kinds (include/tgemm_probe.h): name -> (code,
+# threads per workgroup, flops per workgroup and round)
+STREAM_KINDS = {
+    "f16_mfma": (0, 256, 1 << 23),
+    "f16_reads": (1, 256, 1 << 23),
+    "f16_gemm": (2, 256, 1 << 23),
+    "f16_gemm_no_barrier": (3, 256, 1 << 23),
+    "f16_half_loads": (4, 256, 1 << 23),
+    "f16_vgpr_loads": (5, 256, 1 << 23),
+    "f16_lds_writes": (6, 256, 1 << 23),
+    "f16_32x32": (7, 256, 1 << 23),
+    "f16_32x32_gemm": (8, 256, 1 << 23),
+    "f16_8w_mfma": (9, 512, 1 << 23),
+    "f16_8w_gemm": (10, 512, 1 << 23),
+    "f32_gemm": (11, 256, 1 << 22),
+}
+
+
+def mfma_stream_probe(kind: str, workgroups: int, iters: int, data_ptr: int, data_bytes: int, out_ptr: int,
+                      clocks_ptr=None, stream=None) -> None:
+    """Launch one instruction-stream probe (include/tgemm_probe.h); `kind` is
+    a key of STREAM_KINDS, `out` holds workgroups x its threads floats."""
+    rc = int(load().tgemm_mfma_stream_probe(STREAM_KINDS[kind][0], int(workgroups), int(iters), data_ptr,
+                                            int(data_bytes), out_ptr, clocks_ptr, stream))
+    if rc != TGEMM_OK:
+        raise TgemmError(rc, "mfma_stream_probe")
 
 
 def xcd_probe(workgroups: int, out_ptr: int, stream=None) -> None:

@@ -37,7 +37,7 @@ def test_measurement_library_is_separate():
     from dense_tiled_gemm_tgemm_amd import probe
     plib = probe.load()
     names = _declared_functions("tgemm_probe.h")
-    assert set(names) == {"tgemm_mfma_issue_probe", "tgemm_xcd_probe"}
+    assert set(names) == {"tgemm_mfma_issue_probe", "tgemm_mfma_stream_probe", "tgemm_xcd_probe"}
     lib = tg.load()
     for n in names:
         assert ctypes.cast(getattr(plib, n), ctypes.c_void_p).value
@@ -45,6 +45,21 @@ def test_measurement_library_is_separate():
     # bad sizes are refused before any launch
     assert plib.tgemm_mfma_issue_probe(0, 4, PA, 1 << 20, PC, None, None) == tg.TGEMM_ERR_INVALID
     assert plib.tgemm_xcd_probe(0, PC, None) == tg.TGEMM_ERR_INVALID
+    # unknown stream kinds, and the sizes the ceiling probe refuses, too
+    for kind in (-1, 12):
+        assert plib.tgemm_mfma_stream_probe(kind, 8, 4, PA, 1 << 20, PC, None, None) == tg.TGEMM_ERR_INVALID
+    assert plib.tgemm_mfma_stream_probe(0, 0, 4, PA, 1 << 20, PC, None, None) == tg.TGEMM_ERR_INVALID
+    assert plib.tgemm_mfma_stream_probe(0, 8, 4, PA, (1 << 20) + 2, PC, None, None) == tg.TGEMM_ERR_INVALID
+
+
+def test_stream_probe_kinds_match_the_header():
+    """The binding's kind table holds exactly the kinds include/tgemm_probe.h
+    enumerates, with the same codes."""
+    from dense_tiled_gemm_tgemm_amd import probe
+    src = open(os.path.join(ROOT, "include", "tgemm_probe.h")).read()
+    enum = {m.group(1).lower(): int(m.group(2)) for m in re.finditer(r"TGEMM_STREAM_(\w+) = (\d+)", src)}
+    assert enum == {k: v[0] for k, v in probe.STREAM_KINDS.items()}
+    assert all(v[1] == (512 if "8w" in k else 256) for k, v in probe.STREAM_KINDS.items())
 
 
 def test_status_strings():

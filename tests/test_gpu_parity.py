@@ -432,6 +432,25 @@ def test_mfma_issue_probe_runs():
             probe.mfma_issue_probe(wg, 4, data.data_ptr(), nb, out.data_ptr(), None, st)
 
 
+@pytest.mark.parametrize("kind", list(probe.STREAM_KINDS))
+def test_mfma_stream_probe_runs(kind):
+    """Each instruction-stream probe (measurement aid) launches on binary16 data,
+    produces finite sums in every thread's slot and records a plausible clock."""
+    print(f"case stream probe {kind}", flush=True)
+    _, threads, _ = probe.STREAM_KINDS[kind]
+    data = _dev(inputs.random_f16((1 << 19,), 8) * np.float16(0.1))     # 1 MiB
+    out = torch.full((8 * threads,), float("nan"), dtype=torch.float32, device=DEV)
+    clk = torch.zeros(16, dtype=torch.int64, device=DEV)
+    st = torch.cuda.current_stream().cuda_stream
+    probe.mfma_stream_probe(kind, 8, 4, data.data_ptr(), 1 << 20, out.data_ptr(), clk.data_ptr(), st)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all())
+    c = clk.cpu().numpy().reshape(8, 2).astype(np.float64)
+    assert (c > 0).all()
+    ghz = c[:, 0] / c[:, 1] / 10.0
+    assert ((ghz > 0.5) & (ghz < 3.0)).all(), ghz
+
+
 def test_xcd_probe_dispatch_order():
     """The die probe (measurement aid for the die-aware raster): over launches of
     8192 workgroups every recorded die number lies in [0, 8) and workgroup w ran
