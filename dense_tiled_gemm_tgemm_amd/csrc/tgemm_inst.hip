@@ -63,32 +63,28 @@ const void* rs_ptr(bool vec) {
                : reinterpret_cast<const void*>(&tgemm_rs_kernel<kTy, NXK, false>);
 }
 
-// binary32 operands with B stored N x K: the direct-to-LDS kernel on the
-// operands' bytes, 16-deep steps (32 16-bit units); 256-row tiles with a
-// 2- or 3-stage ring, the smaller tiles with 3 stages
+// binary32 operands: the direct-to-LDS kernel on the operands' bytes,
+// 16-deep steps (32 16-bit units); 256-row tiles with a 2-, 3- or 4-stage
+// ring, the smaller tiles with 3 stages
+template <int NXK>
 const void* f32_dma_ptr(int stages, int tile_m) {
     if constexpr (TG_AB == 2) {
-        if (tile_m == 256 && stages == 2) return reinterpret_cast<const void*>(&tgemm_dma_kernel<kTy, 1, 32, 2>);
-        if (tile_m == 256 && stages == 3) return reinterpret_cast<const void*>(&tgemm_dma_kernel<kTy, 1, 32, 3>);
-        if (tile_m == 256 && stages == 4) return reinterpret_cast<const void*>(&tgemm_dma_kernel<kTy, 1, 32, 4>);
+        if (tile_m == 256 && stages == 2) return reinterpret_cast<const void*>(&tgemm_dma_kernel<kTy, NXK, 32, 2>);
+        if (tile_m == 256 && stages == 3) return reinterpret_cast<const void*>(&tgemm_dma_kernel<kTy, NXK, 32, 3>);
+        if (tile_m == 256 && stages == 4) return reinterpret_cast<const void*>(&tgemm_dma_kernel<kTy, NXK, 32, 4>);
         if (tile_m == 128 && stages == kDefaultSmallStages)
-            return reinterpret_cast<const void*>(&tgemm_dma_kernel<kTy, 1, 32, 3, 4>);
+            return reinterpret_cast<const void*>(&tgemm_dma_kernel<kTy, NXK, 32, 3, 4>);
         if (tile_m == 64 && stages == kDefaultSmallStages)
-            return reinterpret_cast<const void*>(&tgemm_dma_kernel<kTy, 1, 32, 3, 2>);
+            return reinterpret_cast<const void*>(&tgemm_dma_kernel<kTy, NXK, 32, 3, 2>);
     }
     (void)stages;
     (void)tile_m;
     return nullptr;
 }
 
-// binary32 operands: the pipelined register-staged kernel (B stored K x N
-// only), or the general one
+// binary32 operands, general kernel
 template <int NXK>
-const void* f32in_ptr(bool pipelined, bool vec) {
-    if (pipelined) {
-        if constexpr (NXK == 0) return reinterpret_cast<const void*>(&tgemm_f32in_kernel<kTy>);
-        return nullptr;                                 // B stored N x K: f32_dma_ptr
-    }
+const void* f32in_ptr(bool vec) {
     return vec ? reinterpret_cast<const void*>(&tgemm_f32in_rs_kernel<kTy, NXK, true>)
                : reinterpret_cast<const void*>(&tgemm_f32in_rs_kernel<kTy, NXK, false>);
 }
@@ -100,11 +96,10 @@ const void* kernel_for<TG_AB, TG_CT, (TG_EPI != 0)>(const Plan& pl) {
     const bool nxk = (pl.variant & kLayoutNxK) != 0;
     const bool vec = (pl.variant & kVecAB) != 0;
     if constexpr (TG_AB == 2) {
-        // binary32 operands: B stored N x K on the direct-to-LDS kernel, K x N
-        // on the pipelined register-staged one; otherwise the general kernel
-        const bool pipelined = (pl.variant & kDma) != 0;
-        if (pipelined && nxk) return pl.producers ? nullptr : f32_dma_ptr(pl.stages, pl.bm);
-        return nxk ? f32in_ptr<1>(pipelined, vec) : f32in_ptr<0>(pipelined, vec);
+        // binary32 operands: the direct-to-LDS kernel, or the general one
+        if (pl.variant & kDma)
+            return pl.producers ? nullptr : (nxk ? f32_dma_ptr<1>(pl.stages, pl.bm) : f32_dma_ptr<0>(pl.stages, pl.bm));
+        return nxk ? f32in_ptr<1>(vec) : f32in_ptr<0>(vec);
     } else {
         if (pl.variant & kDma)
             return nxk ? dma_ptr<1>(pl.k_step, pl.stages, pl.bm, pl.producers)

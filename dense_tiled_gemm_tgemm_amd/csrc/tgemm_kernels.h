@@ -31,12 +31,13 @@
 //    cycles per instruction but issues less evenly.)
 //  * Every path multiplies the same operand values in the same 32-deep K
 //    slices in ascending order, so all of them produce the same bits.
-//  * Binary32 operands with B stored N x K run on the direct-to-LDS kernel
-//    as pairs of 16-bit units (K and the strides doubled): a 32-unit step is
-//    16 floats, a 128-bit fragment 4 consecutive-k floats, and each block
-//    takes four v_mfma_f32_16x16x4_f32 (slice()). The k each instruction
-//    and lane sums are those of the binary32 register-staged kernels below,
-//    so all binary32 paths produce the same bits too.
+//  * Binary32 operands run on the direct-to-LDS kernel as pairs of 16-bit
+//    units (K and the strides doubled): a 32-unit step is 16 floats, a
+//    128-bit A (and N x K B) fragment 4 consecutive-k floats, a K x N B kept
+//    [k][n] (F32KnLds) and read as four floats, and each block takes four
+//    v_mfma_f32_16x16x4_f32 (slice()). The k each instruction and lane sums
+//    are those of the binary32 general kernel below, so both binary32 paths
+//    produce the same bits too.
 //  * Workgroup -> tile: die-aware renumbering, then the grouped order of
 //    page 1, section "Swizzle" (tile_of in tgemm_plan.h).
 #pragma once
@@ -644,6 +645,21 @@ struct KnLds {
     __device__ static __forceinline__ int logical(int p, int k) { return p ^ h(k); }
 };
 
+// Binary32 B stored K x N, [k][n] in LDS: a 16-deep step is 16 k rows of 256
+// floats (1 KiB, 64 chunks of 4 floats); chunk c of k row k sits at physical
+// chunk c ^ 4 ((k >> 2) & 3). A 16x16x4 fragment takes float e of block j
+// for lane l from k row 4 (l / 16) + e, column 128 wn + 16 j + (l mod 16):
+// four 32-bit reads whose 16-lane groups (k rows 4 apart) fall in four
+// distinct 16-bank windows. Load instruction j of wave w fills k row 4j + w
+// linearly, lane t taking logical chunk t ^ 4j.
+struct F32KnLds {
+    // byte offset in the B block of block jl (0..3; jl + 4 is 256 bytes on),
+    // float e = 0 (e adds 1024 bytes), for lane group g, wave column wn, lane r16
+    __device__ static __forceinline__ int frag_byte(int g, int wn, int jl, int r16) {
+        return 4096 * g + 512 * wn + 64 * (jl ^ g) + 4 * r16;
+    }
+};
+
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 // Four k values (4 consecutive k rows) of one n column of B stored [k][n],
@@ -679,7 +695,7 @@ struct FragPtrs {
     lds_cchar* tr[8];
 };
 
-template <int KS, int NXK, int I = 8>
+template <int KS, int NXK, int I = 8, int AB = 0>
 __device__ __forceinline__ FragPtrs<KS, NXK> frag_ptrs(const u32x4* a_blk, const u32x4* b_blk, int wm, int wn,
                                                         int lane) {
     using L = Lds<KS>;
@@ -690,12 +706,20 @@ __device__ __forceinline__ FragPtrs<KS, NXK> frag_ptrs(const u32x4* a_blk, const
         f.a[s] = a_blk + L::slot(wm * 16 * I + r16, s * 4 + g);
         f.b[s] = b_blk + L::slot(wn * 128 + r16, s * 4 + g);
     }
-    const int krow = 8 * g + (r16 >> 2);
+    if constexpr (AB == 2 && !NXK) {
+        // binary32 B stored K x N (F32KnLds): block j's float e of this lane
+        // sits at tr[j & 3] + 256 (j >> 2) + 1024 e bytes
 #pragma unroll
-    for (int blk = 0; blk < 8; ++blk) {
-        const int ncol = wn * 128 + blk * 16 + 4 * (r16 & 3);
-        const int byte = krow * 512 + KnLds::phys(ncol >> 3, krow) * 16 + (ncol & 7) * 2;
-        f.tr[blk] = NXK ? nullptr : (lds_cchar*)b_blk + byte;
+        for (int jl = 0; jl < 8; ++jl)
+            f.tr[jl] = jl < 4 ? (lds_cchar*)b_blk + F32KnLds::frag_byte(g, wn, jl, r16) : nullptr;
+    } else {
+        const int krow = 8 * g + (r16 >> 2);
+#pragma unroll
+        for (int blk = 0; blk < 8; ++blk) {
+            const int ncol = wn * 128 + blk * 16 + 4 * (r16 & 3);
+            const int byte = krow * 512 + KnLds::phys(ncol >> 3, krow) * 16 + (ncol & 7) * 2;
+            f.tr[blk] = NXK ? nullptr : (lds_cchar*)b_blk + byte;
+        }
     }
     return f;
 }
@@ -730,6 +754,13 @@ __device__ __forceinline__ s16x4 frag_b_tr(const FragPtrs<KS, NXK>& f, int so, i
     return read_tr(f.tr[blk] + so * 16 + s * 16384 + hh * 2048);
 }
 
+// Binary32 B stored K x N: float e of block j's fragment (F32KnLds).
+template <int KS, int NXK>
+__device__ __forceinline__ unsigned frag_b_f32kn(const FragPtrs<KS, NXK>& f, int so, int j, int e) {
+    return *reinterpret_cast<const __attribute__((address_space(3))) unsigned*>(f.tr[j & 3] + so * 16 +
+                                                                                (j >> 2) * 256 + e * 1024);
+}
+
 // Per-lane source offsets of the 2 * CPR load instructions of a K step (A's
 // CPR, then B's). A wave instruction j fills LDS slots (4j + w) * 64 + L.
 //  * K-contiguous operand (A; B stored N x K): slot -> row (256 / CPR) * j +
@@ -754,7 +785,7 @@ struct LaneLoads {
     unsigned kchunk;      // k offset (elements) of this lane's K-contiguous chunk inside a K step
 };
 
-template <int KS, int NXK, int LA = KS / 8>
+template <int KS, int NXK, int LA = KS / 8, int AB = 0>
 __device__ __forceinline__ LaneLoads<KS, LA> lane_loads(const Args& a, int tid) {
     constexpr int kCpr = KS / 8;
     LaneLoads<KS, LA> p;
@@ -766,6 +797,11 @@ __device__ __forceinline__ LaneLoads<KS, LA> lane_loads(const Args& a, int tid) 
         if (j < LA) p.voff[j] = (unsigned)row * (unsigned)a.lda * 2u + chunk * 16u;
         if (NXK) {
             p.voff[LA + j] = (unsigned)row * (unsigned)a.ldb * 2u + chunk * 16u;
+        } else if (AB == 2) {
+            // binary32 [k][n] (F32KnLds): k row 4j + wave, logical chunk lane ^ 4j
+            const unsigned krow = (unsigned)(4 * j + (tid >> 6));
+            const unsigned c = (unsigned)((tid & 63) ^ (4 * j));
+            p.voff[LA + j] = krow * (unsigned)a.ldb * 2u + c * 16u;
         } else {
             const int krow = 8 * j + (tid >> 5);
             const unsigned c = (unsigned)KnLds::logical(tid & 31, krow);
@@ -820,7 +856,7 @@ __device__ __forceinline__ u32x4 keep_first(const u32x4& v, int nv) {
 // (other rows read the next row past N, which lands in output columns that
 // are never stored). This runs after the lane's loads of the stage have
 // landed and before the barrier that publishes it.
-template <int KS, int NXK, int LA>
+template <int KS, int NXK, int LA, int AB = 0>
 __device__ __forceinline__ void fix_last_step(u32x4* __restrict__ a_blk, u32x4* __restrict__ b_blk,
                                               const LaneLoads<KS, LA>& p, const Args& a, int m0, int n0, int k0,
                                               int tid, int wave, int lane) {
@@ -854,7 +890,7 @@ __device__ __forceinline__ void fix_last_step(u32x4* __restrict__ a_blk, u32x4* 
             }
         }
     }
-    if (!NXK) {
+    if (!NXK && AB != 2) {       // (binary32 K x N rows are whole chunks: N % 4 == 0)
 #pragma unroll 1
         for (int j = 0; j < kCpr; ++j) {
             const int krow = 8 * j + (tid >> 5);
@@ -871,13 +907,18 @@ __device__ __forceinline__ void fix_last_step(u32x4* __restrict__ a_blk, u32x4* 
 }
 
 // All fragments of slice `s` of stage 0 (used once, before the main loop).
-template <int KS, int NXK, int I = 8>
+template <int KS, int NXK, int I = 8, int AB = 0>
 __device__ __forceinline__ void read_frags(half8 (&fa)[I], half8 (&fb)[8], const FragPtrs<KS, NXK>& f, int s) {
 #pragma unroll
     for (int i = 0; i < I; ++i) fa[i] = frag_a(f, 0, s, i);
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-        fb[j] = NXK ? frag_b_kc(f, 0, s, j) : join_halves(frag_b_tr(f, 0, s, j, 0), frag_b_tr(f, 0, s, j, 1));
+    for (int j = 0; j < 8; ++j) {
+        if constexpr (AB == 2 && !NXK)
+            fb[j] = __builtin_bit_cast(half8, u32x4{frag_b_f32kn(f, 0, j, 0), frag_b_f32kn(f, 0, j, 1),
+                                                    frag_b_f32kn(f, 0, j, 2), frag_b_f32kn(f, 0, j, 3)});
+        else
+            fb[j] = NXK ? frag_b_kc(f, 0, s, j) : join_halves(frag_b_tr(f, 0, s, j, 0), frag_b_tr(f, 0, s, j, 1));
+    }
 }
 
 // One k32 slice: 8 I MFMAs (I x 8 blocks, serpentine by row) on the current
@@ -898,13 +939,19 @@ __device__ __forceinline__ void slice(f32x4 (&acc)[I][8], const half8 (&fa)[I], 
                                       int next_s, const Rsrc& ra, const Rsrc& rb, const LaneLoads<KS, LA>& p,
                                       unsigned soa, unsigned sob, u32x4* __restrict__ ld_a, u32x4* __restrict__ ld_b,
                                       int wave) {
-    constexpr int kNb = NXK ? 8 : 16;              // B read instructions
+    constexpr bool kF32Kn = AB == 2 && !NXK;
+    constexpr int kNb = NXK ? 8 : (kF32Kn ? 32 : 16);   // B read instructions
     constexpr int kReads = I + kNb;
     s16x4 lo[8];
     // read number rq of the next slice's fragments (consumption order)
     auto read = [&](int rq) {
         if (rq >= 1 && rq <= kNb) {
-            if (NXK) {
+            if (kF32Kn) {
+                const int blk = (rq - 1) >> 2, e = (rq - 1) & 3;
+                u32x4 v = __builtin_bit_cast(u32x4, nb[blk]);
+                v[e] = frag_b_f32kn(f, so, blk, e);
+                nb[blk] = __builtin_bit_cast(half8, v);
+            } else if (NXK) {
                 nb[rq - 1] = frag_b_kc(f, so, next_s, rq - 1);
             } else {
                 const int blk = (rq - 1) >> 1, hh = (rq - 1) & 1;
@@ -1012,7 +1059,7 @@ struct Tile {
     int m0, n0;
 };
 
-template <int NXK, int TBM = BM>
+template <int NXK, int TBM = BM, int AB = 0>
 __device__ __forceinline__ Tile make_tile(const Args& a, int wid) {
     int tm, tn;
     tile_of(wid, a.W, a.grid_m, a.grid_n, a.group_m, a.num_xcd, &tm, &tn);
@@ -1024,6 +1071,10 @@ __device__ __forceinline__ Tile make_tile(const Args& a, int wid) {
     if (NXK) {
         t.rb = operand_rsrc(a.B, a.ldb, a.N, a.K, t.n0);
         t.bspan = 0;
+    } else if (AB == 2) {
+        // binary32 (K, lda and ldb in 16-bit units, N in floats): K / 2 rows of B
+        t.rb = Rsrc{a.B + 2 * t.n0, 0};
+        t.bspan = ((int64_t)(a.K / 2 - 1) * a.ldb + 2 * (int64_t)(a.N - t.n0)) * 2;
     } else {
         t.rb = Rsrc{a.B + t.n0, 0};
         t.bspan = ((int64_t)(a.K - 1) * a.ldb + (a.N - t.n0)) * 2;
@@ -1037,10 +1088,10 @@ __device__ __forceinline__ Tile make_tile(const Args& a, int wid) {
 // capped below kOob; the lane offsets then stay below KS rows of B, so any
 // K works with a row stride up to the K-contiguous limit. Scalar arithmetic
 // only (d is uniform); a step that loads nothing passes d = 0.
-template <int KS, int NXK>
+template <int KS, int NXK, int AB = 0>
 __device__ __forceinline__ Rsrc b_step_rsrc(const Tile& t, int d, int64_t ldb) {
     if (NXK) return t.rb;
-    const int64_t rows = (int64_t)d * KS;
+    const int64_t rows = (int64_t)d * (AB == 2 ? KS / 2 : KS);   // binary32: two 16-bit units per k
     int64_t span = t.bspan - rows * ldb * 2;
     span = span < 0 ? 0 : (span > (int64_t)kOob - 1 ? (int64_t)kOob - 1 : span);
     return Rsrc{t.rb.base + rows * ldb, (int)span};
@@ -1126,7 +1177,7 @@ __device__ __forceinline__ void dma_step(f32x4 (&acc)[I][8], half8 (&fa)[2][I], 
         const unsigned soa = live ? (unsigned)ld * (unsigned)(KS * 2) : kOob;
         const unsigned sob = live ? (NXK ? (unsigned)ld * c.bstep : 0u) : kOob;
         const Rsrc lra = in_next ? tn.ra : tc.ra;
-        const Rsrc lrb = b_step_rsrc<KS, NXK>(in_next ? tn : tc, live ? ld : 0, a.ldb);
+        const Rsrc lrb = b_step_rsrc<KS, NXK, AB>(in_next ? tn : tc, live ? ld : 0, a.ldb);
         TG_COMPILER_FENCE();
         __builtin_amdgcn_sched_barrier(0);
         wait_lgkmcnt0();                                  // this wave's reads of stage st returned
@@ -1135,7 +1186,8 @@ __device__ __forceinline__ void dma_step(f32x4 (&acc)[I][8], half8 (&fa)[2][I], 
         // falls through to its last slice and the step loop takes one branch per
         // step, its back edge (+0.9% at 8192^3)
         if (__builtin_expect(c.fixup && t + 2 == c.nk, 0))
-            fix_last_step<KS, NXK>(c.a_blk(nst), c.b_blk(nst), c.p, a, tc.m0, tc.n0, c.klast, c.tid, c.wave, c.lane);
+            fix_last_step<KS, NXK, Ctx::kLa, AB>(c.a_blk(nst), c.b_blk(nst), c.p, a, tc.m0, tc.n0, c.klast, c.tid,
+                                                 c.wave, c.lane);
         block_barrier();
         // the loads go into the stage just released
         slice<AB, KS, NXK, true, false, !LAST, I>(acc, fa[FL], fb[FL], fa[FL ^ 1], fb[FL ^ 1], cur, 0, 0, lra, lrb,
@@ -1222,7 +1274,7 @@ tgemm_dma_kernel(Args a) {
     static_assert(I == 8 || I == 4 || I == 2, "A blocks of 256, 128 or 64 rows");
     static_assert(Ctx::kLa >= 1, "the A block takes at least one load per step");
     static_assert(!PC || (KS == 32 && I == 4), "producer/consumer workgroups: 32-deep steps, 128 x 256 tiles");
-    static_assert(AB != 2 || (KS == 32 && NXK && !PC), "binary32 operands: 16-deep steps, B stored N x K");
+    static_assert(AB != 2 || (KS == 32 && !PC), "binary32 operands: 16-deep steps (32 16-bit units)");
     static_assert(S >= 2 && S <= 6 && Ctx::kSlots * 16 <= 160 * 1024, "LDS ring must fit 160 KiB");
     static_assert(I == 8 || PC || Ctx::kSlots * 16 <= 80 * 1024, "two workgroups per compute unit");
     constexpr int kL = Ctx::kLa + KS / 8;             // load instructions per step per loading wave
@@ -1241,40 +1293,41 @@ tgemm_dma_kernel(Args a) {
     const int nk = nkd + lead;
 
     int wid = (int)blockIdx.x;
-    Tile tc = make_tile<NXK, kBm>(a, wid);
+    Tile tc = make_tile<NXK, kBm, AB>(a, wid);
     bool has_next = wid + a.grid < a.W;              // K == 0: one tile per workgroup
-    Tile tn = has_next ? make_tile<NXK, kBm>(a, wid + a.grid) : tc;
+    Tile tn = has_next ? make_tile<NXK, kBm, AB>(a, wid + a.grid) : tc;
     f32x4 acc[I][8];
     if (KS == 32) zero_acc_mma<AB, I>(acc);
 
     Ctx c;
     const int ltid = PC ? tid - NTHREADS : tid;       // numbering of the loading waves
     const int lwave = PC ? wave - 4 : wave;
-    c.p = lane_loads<KS, NXK, Ctx::kLa>(a, ltid);
+    c.p = lane_loads<KS, NXK, Ctx::kLa, AB>(a, ltid);
     c.bstep = (unsigned)(KS * 2);
     c.nk = nk;
     c.lead = lead;
     c.klast = (nkd - 1) * KS;
-    c.fixup = (a.K % KS) != 0 || (!NXK && (a.N % 8) != 0);
+    c.fixup = (a.K % KS) != 0 || (!NXK && AB != 2 && (a.N % 8) != 0);
     c.tid = ltid;
     c.wave = lwave;
     c.lane = lane;
     c.smem = smem;
-    c.fp = frag_ptrs<KS, NXK, I>(c.a_blk(0), c.b_blk(0), wm, wn, lane);
+    c.fp = frag_ptrs<KS, NXK, I, AB>(c.a_blk(0), c.b_blk(0), wm, wn, lane);
     if (producer) {
         if (nk > 0) {
             for (int t = 0; t < S; ++t) {
                 const int d = t - lead;
                 const bool live = d >= 0 && t < nk;
                 for (int idx = 0; idx < kL; ++idx)
-                    issue_load<KS, NXK>(tc.ra, b_step_rsrc<KS, NXK>(tc, live ? d : 0, a.ldb), c.p, idx,
+                    issue_load<KS, NXK>(tc.ra, b_step_rsrc<KS, NXK, AB>(tc, live ? d : 0, a.ldb), c.p, idx,
                                         live ? (unsigned)d * (unsigned)(KS * 2) : kOob,
                                         live ? (NXK ? (unsigned)d * c.bstep : 0u) : kOob, c.a_blk(t), c.b_blk(t),
                                         lwave);
             }
             wait_vmcnt<(S - 1) * kL>();               // step 0 landed
             if (c.fixup && nk == 1)
-                fix_last_step<KS, NXK>(c.a_blk(0), c.b_blk(0), c.p, a, tc.m0, tc.n0, c.klast, ltid, lwave, lane);
+                fix_last_step<KS, NXK, Ctx::kLa, AB>(c.a_blk(0), c.b_blk(0), c.p, a, tc.m0, tc.n0, c.klast, ltid, lwave,
+                                                     lane);
             block_barrier();
             int st = 0;
             for (int t = 0; t < nk; ++t) {
@@ -1294,17 +1347,18 @@ tgemm_dma_kernel(Args a) {
                 const int d = t - lead;                   // data step
                 const bool live = d >= 0 && t < nk;
                 for (int idx = 0; idx < kL; ++idx)
-                    issue_load<KS, NXK>(tc.ra, b_step_rsrc<KS, NXK>(tc, live ? d : 0, a.ldb), c.p, idx,
+                    issue_load<KS, NXK>(tc.ra, b_step_rsrc<KS, NXK, AB>(tc, live ? d : 0, a.ldb), c.p, idx,
                                         live ? (unsigned)d * (unsigned)(KS * 2) : kOob,
                                         live ? (NXK ? (unsigned)d * c.bstep : 0u) : kOob, c.a_blk(t), c.b_blk(t),
                                         wave);
             }
             wait_vmcnt<(S - 1) * kL>();                   // step 0 landed
             if (c.fixup && nk == 1)
-                fix_last_step<KS, NXK>(c.a_blk(0), c.b_blk(0), c.p, a, tc.m0, tc.n0, c.klast, tid, wave, lane);
+                fix_last_step<KS, NXK, Ctx::kLa, AB>(c.a_blk(0), c.b_blk(0), c.p, a, tc.m0, tc.n0, c.klast, tid, wave,
+                                                     lane);
         }
         block_barrier();
-        read_frags<KS, NXK, I>(fa[0], fb[0], c.fp, 0);
+        read_frags<KS, NXK, I, AB>(fa[0], fb[0], c.fp, 0);
     }
     FragPtrs<KS, NXK> cur = c.fp;                     // read positions of the current stage
     if constexpr (KS == 64) {
@@ -1326,11 +1380,11 @@ tgemm_dma_kernel(Args a) {
             st ^= 1;
             store_c<TY, 8, I>(acc, a, tc.m0, tc.n0, wm, wn, lane);
             if (!has_next) break;
-            read_frags<KS, NXK, I>(fa[0], fb[0], cur, 0);   // the next tile's first fragments
+            read_frags<KS, NXK, I, AB>(fa[0], fb[0], cur, 0);   // the next tile's first fragments
             wid += a.grid;
             tc = tn;
             has_next = wid + a.grid < a.W;
-            if (has_next) tn = make_tile<NXK, kBm>(a, wid + a.grid);
+            if (has_next) tn = make_tile<NXK, kBm, AB>(a, wid + a.grid);
         }
     } else {
         // one tile per workgroup, its steps (an even count) in pairs
@@ -1342,16 +1396,16 @@ tgemm_dma_kernel(Args a) {
 }
 
 // ---------------------------------------------------------------------------
-// binary32 operands. Page 1's launcher gives 4-byte inputs a tile
-// configuration of their own; here the output tile and the wave grid stay
-// those of the 16-bit kernels (256 x 256, 2 x 2 waves of 128 x 128 as 8 x 8
-// blocks of 16 x 16 fp32 accumulators, so store_c is shared) and the K step
-// is 16 floats. The inner product is v_mfma_f32_16x16x4_f32 (one float of
-// each operand per lane, 32 cycles): at 1/16 of the 16-bit rate per
-// instruction, the operand traffic per MFMA is small, so operands are staged
-// through registers (any stride and alignment of 4 bytes) into a 2-stage LDS
-// ring; fragments are read one step ahead so that the matrix cores do not
-// wait for LDS after each barrier.
+// binary32 operands, general kernel (for strides, alignments and a K x N B
+// with N not a multiple of 4 that the direct-to-LDS kernel does not take; it
+// runs binary32 operands on the same tiles with the fragment layout below).
+// Page 1's launcher gives 4-byte inputs a tile configuration of their own;
+// here the output tile and the wave grid stay those of the 16-bit kernels
+// (256 x 256, 2 x 2 waves of 128 x 128 as 8 x 8 blocks of 16 x 16 fp32
+// accumulators, so store_c is shared) and the K step is 16 floats. The inner
+// product is v_mfma_f32_16x16x4_f32 (one float of each operand per lane, 32
+// cycles): operands are staged through registers (any stride and alignment
+// of 4 bytes) into a 2-stage LDS ring.
 //
 // LDS: per stage an A block and a B block of 256 rows x 4 chunks of 4 floats
 // (k 4c .. 4c+3 in chunk c), chunk c of row r at slot r * 4 + (c ^ f(r)),
@@ -1457,213 +1511,6 @@ __device__ __forceinline__ void f32_store_stage(u32x4* __restrict__ sA, u32x4* _
 
 __device__ __forceinline__ f32x4 read_f32_frag(const u32x4* __restrict__ s_blk, int half, int blk, int lane) {
     return __builtin_bit_cast(f32x4, s_blk[LdsF::slot(half * 128 + blk * 16 + (lane & 15), lane >> 4)]);
-}
-
-// Pipelined kernel for B stored K x N (K and N multiples of 4, so that no
-// 4-float chunk straddles the end of a row; B stored N x K takes the
-// direct-to-LDS kernel above): tile 256 x 128, 4 waves of
-// 128 x 64 (8 x 4 blocks, 128 accumulators), two workgroups per compute unit
-// (two waves per SIMD from independent workgroups, so one workgroup's barrier
-// and staging gaps are covered by the other's matrix instructions). LDS per
-// workgroup: 2 stages of A (256 rows) and B (128 rows) blocks of 4 chunks,
-// 48 KiB. Staging: 16-byte buffer loads through per-tile resources that
-// return zeros past each operand's last element (rows past M, and B's rows
-// past K); chunks at or past K (columns at or past N) are
-// cleared with selects when the staged step is written to LDS. No branches,
-// so the accumulators stay in place across a step.
-constexpr int kF32Bn = kF32PipeBn;              // tile columns of the pipelined kernel
-constexpr int kF32ABlk = 256 * 4;               // slots of an A block
-constexpr int kF32BBlk = kF32Bn * 4;            // slots of a B block
-constexpr int kF32StageSlots = kF32ABlk + kF32BBlk;
-
-__device__ __forceinline__ Rsrc f32_rsrc(const uint16_t* X, int64_t ld, int nrows, int ncols, int row0) {
-    int64_t span = ((int64_t)(nrows - row0 - 1) * ld + ncols) * 4;
-    if (span > (int64_t)kOob - 1) span = (int64_t)kOob - 1;
-    return Rsrc{X + (int64_t)row0 * ld * 2, (int)span};
-}
-
-// This lane's loads of a step: A chunks (t & 3) of rows (t >> 2) + 64 p,
-// p = 0..3; B the 2 x 4 block k = 2 (t >> 5) + 0..1, n = 4 (t & 31) + 0..3.
-struct F32Lanes {
-    unsigned va[4], vb[2];   // byte offsets from the tile's resource bases
-    int kc;                  // k offset (floats) of this lane's A chunk within a step
-    int nc;                  // column offset (floats) of this lane's B chunk within the tile
-};
-
-__device__ __forceinline__ F32Lanes f32_lanes(const Args& a, int tid) {
-    F32Lanes L;
-    const unsigned c = (unsigned)(tid & 3);
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        const unsigned row = (unsigned)((tid >> 2) + 64 * p);
-        L.va[p] = (row * (unsigned)a.lda + 4u * c) * 4u;
-    }
-    const unsigned kr = (unsigned)(2 * (tid >> 5)), nb = (unsigned)(tid & 31);
-#pragma unroll
-    for (int q = 0; q < 2; ++q) L.vb[q] = ((kr + (unsigned)q) * (unsigned)a.ldb + 4u * nb) * 4u;
-    L.kc = 4 * (tid & 3);
-    L.nc = 4 * (tid & 31);
-    return L;
-}
-
-// B goes through a resource based at the step's first k row (record count
-// to B's last element, bspan bytes from k row 0 of the tile's columns), so
-// the lane offsets stay below 16 rows of B whatever K is; a step at or past
-// K gets an empty range and reads zeros.
-__device__ __forceinline__ void f32_buf_load(u32x4 (&ra)[4], u32x4 (&rb)[2], const Rsrc& rsa, const Rsrc& rsb,
-                                             int64_t bspan, const F32Lanes& L, const Args& a, int t) {
-#if defined(__HIP_DEVICE_COMPILE__)   // the host pass cannot instantiate these target builtins
-    const int k0 = t * kF32Ks;
-    const __amdgpu_buffer_rsrc_t xa = __builtin_amdgcn_make_buffer_rsrc((void*)rsa.base, 0, rsa.nrec, 0x00020000);
-    const unsigned soa = (unsigned)k0 * 4u;
-    int64_t span = bspan - (int64_t)k0 * a.ldb * 4;
-    span = span < 0 ? 0 : (span > (int64_t)kOob - 1 ? (int64_t)kOob - 1 : span);
-    const uint16_t* bbase = rsb.base + (int64_t)k0 * a.ldb * 2;   // 16-bit units: two per float
-    const __amdgpu_buffer_rsrc_t xb = __builtin_amdgcn_make_buffer_rsrc((void*)bbase, 0, (int)span, 0x00020000);
-#pragma unroll
-    for (int p = 0; p < 4; ++p)
-        ra[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xa, (int)L.va[p], (int)soa, 0));
-#pragma unroll
-    for (int p = 0; p < 2; ++p)
-        rb[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xb, (int)L.vb[p], 0, 0));
-#else
-    (void)ra; (void)rb; (void)rsa; (void)rsb; (void)bspan; (void)L; (void)a; (void)t;
-#endif
-}
-
-// Write step t's staged operands into an LDS stage (A block at `s`, B block
-// kF32ABlk slots later), clearing A chunks at or past K and B columns at or
-// past N. The selects sit here, a half step after the loads were issued, so
-// they never wait on memory inside the matrix-instruction stream.
-__device__ __forceinline__ void f32_store_step(u32x4* __restrict__ s, u32x4 (&ra)[4], u32x4 (&rb)[2],
-                                               const F32Lanes& L, const Args& a, int n0, int t, int tid) {
-    const bool k_ok = t * kF32Ks + L.kc < a.K;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) s[LdsF::slot((tid >> 2) + 64 * p, tid & 3)] = k_ok ? ra[p] : u32x4{};
-    // B's 2 x 4 block -> 4 rows (columns n) x 2 floats (k = 2 (t >> 5) + 0..1):
-    // 8-byte half (t >> 5) & 1 of chunk (t >> 6) of row 4 (t & 31) + v
-    const bool n_ok = n0 + L.nc < a.N;
-    u32x2* sb2 = reinterpret_cast<u32x2*>(s + kF32ABlk);
-    const int kp = tid >> 5, nb = tid & 31;
-#pragma unroll
-    for (int v = 0; v < 4; ++v)
-        sb2[2 * LdsF::slot(4 * nb + v, kp >> 1) + (kp & 1)] = n_ok ? u32x2{rb[0][v], rb[1][v]} : u32x2{};
-}
-
-// The wave's fragments as 8-byte halves of its 16-byte chunks: lo = k0 + 4g +
-// 0..1 (MFMAs e = 0, 1), hi = k0 + 4g + 2..3 (e = 2, 3).
-struct F32Frags {
-    f32x2 alo[8], ahi[8], blo[4], bhi[4];
-};
-
-// Half of a step's MFMAs, [Q0, Q1) of 64 (EH = 0: e = 0, 1 on the lo halves;
-// EH = 1: e = 2, 3 on the hi halves), walking the 8 x 4 blocks in serpentine
-// order twice, with the 12 reads of the other halves placed after every fifth
-// MFMA: EH = 0 reads this step's hi halves, EH = 1 the next step's lo halves
-// (from `pa` / `pb`, in the order the next half consumes them: A0, B0..B3,
-// A1..A7). The compiler schedules inside a section; pinning it instruction
-// by instruction, as in the 16-bit kernels, makes the register allocator
-// rotate the accumulators at every step here.
-template <int EH, int Q0 = 0, int Q1 = 64>
-__device__ __forceinline__ void f32_half(f32x4 (&acc)[8][4], F32Frags& f, const f32x2* __restrict__ pa,
-                                         const f32x2* __restrict__ pb) {
-    constexpr int kHalf = EH ? 0 : 1;                 // which half the reads fill
-#pragma unroll
-    for (int q = Q0; q < Q1; ++q) {
-        const int e = q >> 5, x = q & 31;
-        const int i = x >> 2, j = (i & 1) ? 3 - (x & 3) : (x & 3);
-        const f32x2& av = EH ? f.ahi[i] : f.alo[i];
-        const f32x2& bv = EH ? f.bhi[j] : f.blo[j];
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(bv[e], av[e], acc[i][j], 0, 0, 0);
-        if (q % 5 == 4 && q / 5 < 12) {
-            const int r = q / 5;                      // 0 .. 11
-            if (r >= 1 && r <= 4) {
-                f32x2& d = EH ? f.blo[r - 1] : f.bhi[r - 1];
-                d = pb[(r - 1) * 128 + kHalf];
-            } else {
-                const int ai = r == 0 ? 0 : r - 4;
-                f32x2& d = EH ? f.alo[ai] : f.ahi[ai];
-                d = pa[ai * 128 + kHalf];
-            }
-        }
-    }
-}
-
-// Per 16-deep step t (LDS stage t mod 2): the first 48 MFMAs of the lo half
-// while the hi halves are read; the step t + 1 operands (staged since step
-// t - 1) are written to the other stage and the loads of step t + 2 issued;
-// the last 16 MFMAs of the lo half cover the LDS writes; one barrier
-// publishes the stage; the hi half runs while the next step's lo halves are
-// read. The section boundaries are pinned: otherwise the compiler moves
-// matrix instructions across the staging block and leaves the next step's
-// reads exposed.
-template <int TY>
-__global__ void __launch_bounds__(NTHREADS)
-__attribute__((amdgpu_waves_per_eu(2, 2)))
-tgemm_f32in_kernel(Args a) {
-    static_assert(ab_of(TY) == 2, "binary32 operands");
-    __shared__ u32x4 smem[2 * kF32StageSlots];   // [stage][A block | B block], 48 KiB
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-
-    int tm, tn;
-    tile_of((int)blockIdx.x, a.W, a.grid_m, a.grid_n, a.group_m, a.num_xcd, &tm, &tn);
-    const int m0 = tm * BM, n0 = tn * kF32Bn;
-    const int nk = (a.K + kF32Ks - 1) / kF32Ks;
-    const F32Lanes L = f32_lanes(a, tid);
-    const Rsrc rsa = f32_rsrc(a.A, a.lda, a.M, a.K, m0);
-    // B: columns n0.. of all K rows (rebased at every step)
-    const Rsrc rsb = Rsrc{a.B + 2 * n0, 0};
-    const int64_t bspan = ((int64_t)(a.K - 1) * a.ldb + (a.N - n0)) * 4;
-
-    // stage-0 read positions (8-byte units) of 16-row block 0; block i lies
-    // 128 further, stage 1 2 * kF32StageSlots further, the hi half 1 further
-    const int r16 = lane & 15, g = lane >> 4;
-    const f32x2* pa0 = reinterpret_cast<const f32x2*>(smem) + 2 * LdsF::slot(wm * 128 + r16, g);
-    const f32x2* pb0 = reinterpret_cast<const f32x2*>(smem + kF32ABlk) + 2 * LdsF::slot(wn * 64 + r16, g);
-    constexpr int kStage2 = 2 * kF32StageSlots;
-
-    f32x4 acc[8][4];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{};
-    F32Frags f;
-    u32x4 ra[4], rb[2];
-    if (nk > 0) {
-        f32_buf_load(ra, rb, rsa, rsb, bspan, L, a, 0);
-        f32_store_step(smem, ra, rb, L, a, n0, 0, tid);
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < 8; ++i) f.alo[i] = pa0[i * 128];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) f.blo[j] = pb0[j * 128];
-        f32_buf_load(ra, rb, rsa, rsb, bspan, L, a, 1);   // past the last step: zeros
-    }
-    for (int t = 0; t < nk; ++t) {
-        const int st = t & 1;
-        const int so = st * kStage2, sn = (st ^ 1) * kStage2;
-        f32_half<0, 0, 48>(acc, f, pa0 + so, pb0 + so);
-        TG_COMPILER_FENCE();
-        __builtin_amdgcn_sched_barrier(0);
-        wait_vmcnt<0>();                              // step t + 1 in the staging registers
-        f32_store_step(smem + (st ^ 1) * kF32StageSlots, ra, rb, L, a, n0, t + 1, tid);
-        f32_buf_load(ra, rb, rsa, rsb, bspan, L, a, t + 2);
-        TG_COMPILER_FENCE();
-        __builtin_amdgcn_sched_barrier(0);
-        f32_half<0, 48, 64>(acc, f, pa0 + so, pb0 + so);
-        TG_COMPILER_FENCE();
-        __builtin_amdgcn_sched_barrier(0);
-        __syncthreads();
-        __builtin_amdgcn_sched_barrier(0);
-        f32_half<1>(acc, f, pa0 + sn, pb0 + sn);
-        TG_COMPILER_FENCE();
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    store_c<TY, 4>(acc, a, m0, n0, wm, wn, lane);
 }
 
 // One 16-deep K step of the wave's 128 x 128 sub-tile from LDS: 4 x 8 x 8 MFMAs.

@@ -54,7 +54,6 @@ constexpr int kProducerWaves = 4;          // producer/consumer workgroups: 4 + 
 // grid of one round or less measured.
 constexpr int kPartialKxNKStep = 32;
 constexpr int kF32KStep = 16;              // K step (floats) of the binary32-operand kernels
-constexpr int kF32PipeBn = 128;            // tile columns of the pipelined binary32-operand kernel
 
 enum : int { kVecAB = 1, kVecC = 2, kLayoutNxK = 4, kDma = 8 };
 
@@ -96,7 +95,7 @@ struct Plan {
     bool epi;          // scale, bias or activation requested (else C = A * B as it is)
     int variant;       // kVecAB | kVecC | kLayoutNxK | kDma bits
     int bm;            // tile rows of the launched kernel (BM, or 128 / 64 for the small tiles)
-    int bn;            // tile columns of the launched kernel (BN, or kF32PipeBn)
+    int bn;            // tile columns of the launched kernel (BN)
     int producers;     // producer waves per workgroup (0, or kProducerWaves)
     int threads;       // threads per workgroup
     int grid_m, grid_n, W;
@@ -105,11 +104,9 @@ struct Plan {
     int grid;             // workgroups launched (W, or the compute units for a persistent launch)
 };
 
-// Binary32 operands (B stored N x K) planned onto the direct-to-LDS kernel:
-// it is launched with K and both row strides counted in 16-bit units.
-inline bool f32_on_dma(const Plan& pl) {
-    return pl.ab_type == TGEMM_F32 && (pl.variant & kDma) && pl.layout == TGEMM_B_NxK;
-}
+// Binary32 operands planned onto the direct-to-LDS kernel: it is launched
+// with K and both row strides counted in 16-bit units.
+inline bool f32_on_dma(const Plan& pl) { return pl.ab_type == TGEMM_F32 && (pl.variant & kDma); }
 
 inline bool span_bytes(int64_t rows, int64_t cols, int64_t ld, uint64_t* bytes, int esize = 2) {
     // bytes covered by a row-major rows x cols array of esize-byte elements
@@ -217,22 +214,18 @@ inline int make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
     // (row strides of at least 8 elements: then a 16-byte access can run past
     // the end of an operand only in its last row, which the kernel reloads
     // element by element; narrower operands take the register-staged kernel)
-    // (binary32 operands with B stored N x K run on the same kernel as pairs
-    // of 16-bit units: row strides of at least 4 floats and at most half the
-    // 16-bit limit. With B stored K x N the kDma bit marks the pipelined
-    // register-staged binary32 kernel, whose buffer loads need K and N
-    // multiples of 4 and every byte offset of a tile below 2^31; its B is
-    // rebased at every K step too)
+    // (binary32 operands run on the same kernel as pairs of 16-bit units: row
+    // strides of at least 4 floats and at most half the 16-bit limit; with B
+    // stored K x N, N a multiple of 4, so that no 4-float chunk of B's last
+    // row straddles the end of the operand, where the range check would zero
+    // it whole)
     const bool dma =
         ab_type == TGEMM_F32
-            ? (b_layout == TGEMM_B_NxK
-                   ? (!force_generic && K > 0 && lda >= 4 && ldb >= 4 && lda <= kMaxDmaLd / 2 &&
-                      ldb <= kMaxDmaLd / 2)
-                   : (!force_generic && K > 0 && K % 4 == 0 && N % 4 == 0 && lda <= kMaxDmaLd / 2 &&
-                      ldb <= kMaxDmaLd / 2))
+            ? (!force_generic && K > 0 && lda >= 4 && ldb >= 4 && lda <= kMaxDmaLd / 2 && ldb <= kMaxDmaLd / 2 &&
+               (b_layout == TGEMM_B_NxK || N % 4 == 0))
             : (!force_generic && K > 0 && lda >= 8 && ldb >= 8 && lda <= kMaxDmaLd && ldb <= kMaxDmaLd);
-    // binary32 operands on the direct-to-LDS kernel (B stored N x K)
-    const bool f32_dma = ab_type == TGEMM_F32 && dma && b_layout == TGEMM_B_NxK;
+    // binary32 operands on the direct-to-LDS kernel
+    const bool f32_dma = ab_type == TGEMM_F32 && dma;
     pl->variant = (vec_ab ? kVecAB : 0) | (vec_c ? kVecC : 0) |
                   (b_layout == TGEMM_B_NxK ? kLayoutNxK : 0) | (dma ? kDma : 0);
     if (f32_dma) {
@@ -258,7 +251,7 @@ inline int make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
     pl->bm = bm;
     pl->producers = producers;
     pl->threads = NTHREADS + producers * 64;
-    pl->bn = (ab_type == TGEMM_F32 && dma && !f32_dma) ? kF32PipeBn : BN;
+    pl->bn = BN;
     const int64_t gn = (N + pl->bn - 1) / pl->bn;
     if (gm * gn > kMaxDim) return TGEMM_ERR_UNSUPPORTED;
     pl->grid_m = (int)gm;

@@ -166,16 +166,16 @@ int tgemm_f16_config(int64_t M, int64_t N, int64_t K,
  *            (lda and ldb count elements of that type; binary32 operands
  *            must be 4-byte aligned). Binary32 operands run on
  *            v_mfma_f32_16x16x4_f32 with fp32 accumulation in 16-deep K
- *            steps. With B stored N x K (and K > 0, row strides of 4 to
- *            2,000,000 floats) they take the direct-to-LDS kernel of the
- *            16-bit types on their bytes: tiles of 256, 128 or 64 rows, an
- *            LDS ring of 2 (default), 3 or 4 stages at 256 rows and 3 for the
- *            smaller tiles; automatic launches take 64-row tiles unless
- *            256-row tiles fill at least 7/8 of their rounds over the compute
- *            units. With B stored K x N a kernel staged through registers
- *            (256 x 128 tiles, 2 stages). The k_step choice of
- *            tgemm_gemm_config does not apply to binary32 operands (a plan
- *            reports 16), nor stages and tile_m to B stored K x N.
+ *            steps. With K > 0, row strides of 4 to 2,000,000 floats and,
+ *            for B stored K x N, N a multiple of 4, they take the
+ *            direct-to-LDS kernel of the 16-bit types on their bytes: tiles
+ *            of 256, 128 or 64 rows, an LDS ring of 2 (default), 3 or 4
+ *            stages at 256 rows and 3 for the smaller tiles; automatic
+ *            launches take 64-row tiles unless 256-row tiles fill at least
+ *            7/8 of their rounds over the compute units. Otherwise a general
+ *            kernel staged through registers (256 x 256 tiles, 2 stages). The
+ *            k_step choice of tgemm_gemm_config does not apply to binary32
+ *            operands (a plan reports 16).
  *   c_type:  TGEMM_F16, TGEMM_BF16 or TGEMM_F32; ldc counts elements of
  *            that type (C[i*ldc + j]).
  *   bias:    NULL, or N fp32 values in device memory (4-byte aligned),
@@ -281,9 +281,8 @@ int tgemm_last_hip_error(void);
  * Returns TGEMM_OK and fills info[0..9]:
  *   info[0] variant bits: bit0 128-bit A/B loads, bit1 vector C stores
  *           (64-bit runs of a 16-bit C, 128-bit runs of an fp32 C), bit2 B
- *           layout is NxK, bit3 the pipelined kernel (streamed directly
- *           into LDS; binary32 operands with B stored K x N: buffer loads
- *           into registers)
+ *           layout is NxK, bit3 the pipelined kernel (operands streamed
+ *           directly into LDS)
  *   info[1] tile rows        info[2] tile columns      info[3] K step
  *   info[4] workgroups launched (the tile count ceil(M/BM) * ceil(N/BN), or
  *           compute_units when each workgroup walks several tiles; 0 when

@@ -245,13 +245,15 @@ def test_tile_choices_plan():
             assert _plan_ex(1024, 1024, 1024, ab=ab, ct=ct, tile_m=tm, **kw)[0] == tg.TGEMM_OK
         assert _plan_ex(1024, 1024, 1024, ab=ab, ct=ct, tile_m=128, stages=2, **kw)[0] == tg.TGEMM_ERR_UNSUPPORTED
         assert _plan_ex(1024, 1024, 1024, ab=ab, ct=ct, producers=4, **kw)[0] == tg.TGEMM_ERR_UNSUPPORTED
-    # binary32 operands: the smaller tiles with B stored N x K (direct-to-LDS), not K x N
-    for tm in (128, 64):
-        rc, info = _plan_ex(1024, 1024, 1024, ab="f32", ct="f32", lay="NxK", tile_m=tm)
-        assert rc == 0 and (info["bm"], info["bk"], info["stages"]) == (tm, 16, 3)
-    assert _plan_ex(1024, 1024, 1024, ab="f32", ct="f32", lay="NxK", tile_m=128, stages=2)[0] == \
-        tg.TGEMM_ERR_UNSUPPORTED
-    assert _plan_ex(1024, 1024, 1024, ab="f32", ct="f32", tile_m=128)[0] == tg.TGEMM_ERR_UNSUPPORTED
+    # binary32 operands: the smaller tiles on the direct-to-LDS kernel (3 stages),
+    # not on the general kernel
+    for lay in ("NxK", "KxN"):
+        for tm in (128, 64):
+            rc, info = _plan_ex(1024, 1024, 1024, ab="f32", ct="f32", lay=lay, tile_m=tm)
+            assert rc == 0 and (info["bm"], info["bk"], info["stages"]) == (tm, 16, 3)
+        assert _plan_ex(1024, 1024, 1024, ab="f32", ct="f32", lay=lay, tile_m=128, stages=2)[0] == \
+            tg.TGEMM_ERR_UNSUPPORTED
+    assert _plan_ex(1024, 1022, 1024, ab="f32", ct="f32", tile_m=128)[0] == tg.TGEMM_ERR_UNSUPPORTED
 
 
 def test_small_grids_take_smaller_tiles():
@@ -279,7 +281,8 @@ def test_small_grids_take_smaller_tiles():
     assert info["bm"] == 256
     for ab, ct in (("bf16", "f32"), ("f16", "bf16")):
         assert _plan_ex(256, 256, 256, ab=ab, ct=ct, alpha=0.5)[1]["bm"] == 64
-    assert _plan_ex(256, 256, 256, ab="f32", ct="f32")[1]["bm"] == 256      # B stored K x N
+    assert _plan_ex(256, 256, 256, ab="f32", ct="f32")[1]["bm"] == 64
+    assert _plan_ex(256, 254, 256, ab="f32", ct="f32", ldb=256, ldc=256)[1]["bm"] == 256   # general kernel
 
 
 @pytest.mark.parametrize("M,N,cu,bm", [
@@ -291,16 +294,15 @@ def test_small_grids_take_smaller_tiles():
     (4096, 4096, 255, 64), (3584, 4096, 224, 256),       # the fill is counted on the device's units
 ])
 def test_binary32_tile_rows_follow_round_fill(M, N, cu, bm):
-    """Binary32 operands (B stored N x K): 64-row tiles unless 256-row tiles
+    """Binary32 operands (either B layout): 64-row tiles unless 256-row tiles
     fill at least 7/8 of their rounds over the compute units; explicit tile
-    rows and B stored K x N are left alone."""
-    rc, info = _plan_ex(M, N, 2048, ab="f32", ct="f32", lay="NxK", compute_units=cu)
-    assert rc == 0 and info["bm"] == bm
-    assert info["stages"] == (2 if bm == 256 else 3)
-    rc, info = _plan_ex(M, N, 2048, ab="f32", ct="f32", lay="NxK", compute_units=cu, tile_m=256)
-    assert rc == 0 and info["bm"] == 256
-    rc, info = _plan_ex(M, N, 2048, ab="f32", ct="f32", compute_units=cu)
-    assert rc == 0 and info["bm"] == 256
+    rows are left alone."""
+    for lay in ("NxK", "KxN"):
+        rc, info = _plan_ex(M, N, 2048, ab="f32", ct="f32", lay=lay, compute_units=cu)
+        assert rc == 0 and info["bm"] == bm
+        assert info["stages"] == (2 if bm == 256 else 3)
+        rc, info = _plan_ex(M, N, 2048, ab="f32", ct="f32", lay=lay, compute_units=cu, tile_m=256)
+        assert rc == 0 and info["bm"] == 256
 
 
 def test_default_die_count_follows_the_compute_units():
@@ -548,18 +550,16 @@ def test_fp32_operand_plans():
     assert rc == 0 and not info["variant"] & PIPE
     rc, info = _plan_ex(300, 202, 100, ab="f32", ct="f16", lay="NxK", ldc=208)
     assert rc == 0 and info["variant"] == V | CV | NXK | PIPE
-    # B stored K x N: the pipelined register-staged kernel when K and N are
-    # multiples of 4; its tile is 256 x 128 (two workgroups per compute unit)
+    # B stored K x N: the same kernel when N is a multiple of 4 (any K)
     rc, info = _plan_ex(8192, 8192, 8192, ab="f32", ct="f32")
     assert rc == 0 and info["variant"] == V | CV | PIPE
-    assert (info["bm"], info["bn"]) == (256, 128)
-    assert (info["bk"], info["stages"], info["lds_bytes"], info["workgroups"]) == (16, 2, 48 * 1024, 2048)
-    # launch choices for the direct-to-LDS pipelines do not apply to it
-    rc2, info2 = _plan_ex(8192, 8192, 8192, ab="f32", ct="f32", k_step=32, stages=5)
-    assert rc2 == 0 and info2 == info
-    # K not a multiple of 4, or N for B stored K x N, or forced: the general kernel
+    assert (info["bm"], info["bn"]) == (256, 256)
+    assert (info["bk"], info["stages"], info["lds_bytes"], info["workgroups"]) == (16, 2, 64 * 1024, 1024)
     rc, info = _plan_ex(300, 200, 101, ab="f32", ct="f16", lda=101)
-    assert rc == 0 and info["variant"] == CV
+    assert rc == 0 and info["variant"] == CV | PIPE
+    rc3, info3 = _plan_ex(8192, 8192, 8192, ab="f32", ct="f32", stages=4)
+    assert rc3 == 0 and (info3["stages"], info3["lds_bytes"]) == (4, 128 * 1024)
+    # N not a multiple of 4, or forced: the general kernel
     rc, info = _plan_ex(300, 202, 100, ab="f32", ct="f16", lda=100, ldb=202, ldc=208)
     assert rc == 0 and info["variant"] == CV
     rc, info = _plan_ex(300, 200, 100, ab="f32", ct="f16", lda=100, ldb=200, force_generic=1)
@@ -567,7 +567,7 @@ def test_fp32_operand_plans():
     assert (info["bn"], info["lds_bytes"], info["workgroups"]) == (256, 64 * 1024, 2)
     rc, info = _plan_ex(300, 200, 100, ab="f32", ct="f16", lay="NxK", force_generic=1)
     assert rc == 0 and info["variant"] == CV | NXK
-    # 4-byte-aligned bases are fine for both (buffer loads)
+    # 4-byte-aligned bases are fine (buffer loads)
     rc, info = _plan_ex(300, 200, 100, ab="f32", ct="bf16", A=PA + 4)
     assert rc == 0 and info["variant"] == CV | PIPE
     rc, info = _plan_ex(300, 200, 100, ab="f32", ct="bf16", lay="NxK", A=PA + 4)
@@ -579,7 +579,7 @@ def test_fp32_operand_plans():
     assert rc == 0 and not info["variant"] & PIPE
     rc, info = _plan_ex(300, 200, 100, ab="f32", ct="f32", ldb=2_000_004)
     assert rc == 0 and not info["variant"] & PIPE
-    # B stored K x N is rebased at every step: a wide B stays on the pipelined kernel
+    # B stored K x N is rebased at every step: a wide B stays on the direct-to-LDS kernel
     rc, info = _plan_ex(300, 200, 8192, ab="f32", ct="f32", ldb=2_000_000)
     assert rc == 0 and info["variant"] & PIPE
 

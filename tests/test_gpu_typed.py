@@ -442,6 +442,30 @@ def test_f32_operands_strided_and_offset(oracle_mod, lay, offset, pad, N, K):
     _check(oracle_mod, A, B, lay, "f32", "f32", _out_np(C), 1.0, None, "none", "f32 strided")
 
 
+@pytest.mark.parametrize("M,N,K", [(300, 260, 133), (257, 512, 29), (64, 4, 5), (33, 300, 16), (1000, 1028, 1000),
+                                   (520, 768, 4096)])
+def test_f32_operands_kxn_direct_to_lds(oracle_mod, M, N, K):
+    """Binary32 operands with B stored K x N (N a multiple of 4) take the
+    direct-to-LDS kernel: full parity with the oracle (partial tiles in both
+    directions, K tails, a 4-column B), and the same bits from every tile
+    shape and ring depth and from the general kernel."""
+    print(f"case f32-in KxN direct-to-LDS {M}x{N}x{K}", flush=True)
+    seed = (M * 7 + N * 3 + K) % 1009
+    A = _f32((M, K), seed)
+    B = _f32((K, N), seed + 1)
+    Ad, Bd = _d32(A), _d32(B)
+    C = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    rc, info = tg.tgemm_plan_gemm(M, N, K, "f32", Ad.data_ptr(), K, Bd.data_ptr(), N, "KxN", "f32", C.data_ptr(), N)
+    assert rc == 0 and info["variant"] & 8 and info["bn"] == 256, info
+    C = tg.gemm(Ad, Bd, "KxN", out_dtype=torch.float32)
+    _check(oracle_mod, A, B, "KxN", "f32", "f32", _out_np(C), 1.0, None, "none", f"f32 KxN {M}x{N}x{K}")
+    for kw in (dict(tile_m=256), dict(tile_m=128), dict(tile_m=64), dict(tile_m=256, stages=3),
+               dict(tile_m=256, stages=4), dict(force_generic=1)):
+        C2 = tg.gemm(Ad, Bd, "KxN", out_dtype=torch.float32, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(C, C2), kw
+
+
 @pytest.mark.parametrize("name", ["sq256", "sq4096", "ragged", "sq8192_nt", "qkv_proj"])
 def test_f32_operands_ternary_bit_exact(oracle_mod, name):
     """Entries in {-1, 0, 1}: every product and partial sum is an integer below
