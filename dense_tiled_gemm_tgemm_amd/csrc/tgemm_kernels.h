@@ -651,7 +651,11 @@ struct KnLds {
 // for lane l from k row 4 (l / 16) + e, column 128 wn + 16 j + (l mod 16):
 // four 32-bit reads whose 16-lane groups (k rows 4 apart) fall in four
 // distinct 16-bank windows. Load instruction j of wave w fills k row 4j + w
-// linearly, lane t taking logical chunk t ^ 4j.
+// linearly, lane t taking logical chunk t ^ 4j. B's rows past K read zeros
+// (they lie past the per-step range); a chunk straddling column N reads the
+// next row's first floats, which reach only output columns that are never
+// stored, except in B's last row, where the range check zeroes the whole
+// chunk and fix_last_step reloads its valid floats.
 struct F32KnLds {
     // byte offset in the B block of block jl (0..3; jl + 4 is 256 bytes on),
     // float e = 0 (e adds 1024 bytes), for lane group g, wave column wn, lane r16
@@ -890,7 +894,20 @@ __device__ __forceinline__ void fix_last_step(u32x4* __restrict__ a_blk, u32x4* 
             }
         }
     }
-    if (!NXK && AB != 2) {       // (binary32 K x N rows are whole chunks: N % 4 == 0)
+    if (!NXK && AB == 2) {
+        // binary32 [k][n] (F32KnLds): load j of this wave holds k row 4j + wave,
+        // logical chunk lane ^ 4j; B's last row is k0 / 2 + krow == K / 2 - 1
+        // (k0 and K in 16-bit units)
+#pragma unroll 1
+        for (int j = 0; j < kCpr; ++j) {
+            const int krow = 4 * j + wave;
+            const int nc = n0 + 4 * (lane ^ (4 * j));
+            const int nvn = a.N - nc;                   // valid floats of the chunk
+            if (k0 / 2 + krow == a.K / 2 - 1 && nvn > 0 && nvn < 4)
+                b_blk[(j * 4 + wave) * 64 + lane] =
+                    load8_elems(a.B + (int64_t)(a.K / 2 - 1) * a.ldb + 2 * (int64_t)nc, 2 * nvn);
+        }
+    } else if (!NXK) {
 #pragma unroll 1
         for (int j = 0; j < kCpr; ++j) {
             const int krow = 8 * j + (tid >> 5);
@@ -1307,7 +1324,7 @@ tgemm_dma_kernel(Args a) {
     c.nk = nk;
     c.lead = lead;
     c.klast = (nkd - 1) * KS;
-    c.fixup = (a.K % KS) != 0 || (!NXK && AB != 2 && (a.N % 8) != 0);
+    c.fixup = (a.K % KS) != 0 || (!NXK && (a.N % (AB == 2 ? 4 : 8)) != 0);
     c.tid = ltid;
     c.wave = lwave;
     c.lane = lane;

@@ -215,14 +215,10 @@ inline int make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
     // the end of an operand only in its last row, which the kernel reloads
     // element by element; narrower operands take the register-staged kernel)
     // (binary32 operands run on the same kernel as pairs of 16-bit units: row
-    // strides of at least 4 floats and at most half the 16-bit limit; with B
-    // stored K x N, N a multiple of 4, so that no 4-float chunk of B's last
-    // row straddles the end of the operand, where the range check would zero
-    // it whole)
+    // strides of at least 4 floats and at most half the 16-bit limit)
     const bool dma =
         ab_type == TGEMM_F32
-            ? (!force_generic && K > 0 && lda >= 4 && ldb >= 4 && lda <= kMaxDmaLd / 2 && ldb <= kMaxDmaLd / 2 &&
-               (b_layout == TGEMM_B_NxK || N % 4 == 0))
+            ? (!force_generic && K > 0 && lda >= 4 && ldb >= 4 && lda <= kMaxDmaLd / 2 && ldb <= kMaxDmaLd / 2)
             : (!force_generic && K > 0 && lda >= 8 && ldb >= 8 && lda <= kMaxDmaLd && ldb <= kMaxDmaLd);
     // binary32 operands on the direct-to-LDS kernel
     const bool f32_dma = ab_type == TGEMM_F32 && dma;

@@ -166,9 +166,9 @@ int tgemm_f16_config(int64_t M, int64_t N, int64_t K,
  *            (lda and ldb count elements of that type; binary32 operands
  *            must be 4-byte aligned). Binary32 operands run on
  *            v_mfma_f32_16x16x4_f32 with fp32 accumulation in 16-deep K
- *            steps. With K > 0, row strides of 4 to 2,000,000 floats and,
- *            for B stored K x N, N a multiple of 4, they take the
- *            direct-to-LDS kernel of the 16-bit types on their bytes: tiles
+ *            steps. With K > 0 and row strides of 4 to 2,000,000 floats
+ *            they take the direct-to-LDS kernel of the 16-bit types on their
+ *            bytes (both B layouts): tiles
  *            of 256, 128 or 64 rows, an LDS ring of 2 (default), 3 or 4
  *            stages at 256 rows and 3 for the smaller tiles; automatic
  *            launches take 64-row tiles unless 256-row tiles fill at least

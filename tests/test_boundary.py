@@ -253,7 +253,8 @@ def test_tile_choices_plan():
             assert rc == 0 and (info["bm"], info["bk"], info["stages"]) == (tm, 16, 3)
         assert _plan_ex(1024, 1024, 1024, ab="f32", ct="f32", lay=lay, tile_m=128, stages=2)[0] == \
             tg.TGEMM_ERR_UNSUPPORTED
-    assert _plan_ex(1024, 1022, 1024, ab="f32", ct="f32", tile_m=128)[0] == tg.TGEMM_ERR_UNSUPPORTED
+    assert _plan_ex(1024, 1022, 1024, ab="f32", ct="f32", tile_m=128, force_generic=1)[0] == \
+        tg.TGEMM_ERR_UNSUPPORTED
 
 
 def test_small_grids_take_smaller_tiles():
@@ -282,7 +283,7 @@ def test_small_grids_take_smaller_tiles():
     for ab, ct in (("bf16", "f32"), ("f16", "bf16")):
         assert _plan_ex(256, 256, 256, ab=ab, ct=ct, alpha=0.5)[1]["bm"] == 64
     assert _plan_ex(256, 256, 256, ab="f32", ct="f32")[1]["bm"] == 64
-    assert _plan_ex(256, 254, 256, ab="f32", ct="f32", ldb=256, ldc=256)[1]["bm"] == 256   # general kernel
+    assert _plan_ex(256, 254, 256, ab="f32", ct="f32", force_generic=1)[1]["bm"] == 256   # general kernel
 
 
 @pytest.mark.parametrize("M,N,cu,bm", [
@@ -550,7 +551,7 @@ def test_fp32_operand_plans():
     assert rc == 0 and not info["variant"] & PIPE
     rc, info = _plan_ex(300, 202, 100, ab="f32", ct="f16", lay="NxK", ldc=208)
     assert rc == 0 and info["variant"] == V | CV | NXK | PIPE
-    # B stored K x N: the same kernel when N is a multiple of 4 (any K)
+    # B stored K x N: the same kernel (any K, any N)
     rc, info = _plan_ex(8192, 8192, 8192, ab="f32", ct="f32")
     assert rc == 0 and info["variant"] == V | CV | PIPE
     assert (info["bm"], info["bn"]) == (256, 256)
@@ -559,8 +560,10 @@ def test_fp32_operand_plans():
     assert rc == 0 and info["variant"] == CV | PIPE
     rc3, info3 = _plan_ex(8192, 8192, 8192, ab="f32", ct="f32", stages=4)
     assert rc3 == 0 and (info3["stages"], info3["lds_bytes"]) == (4, 128 * 1024)
-    # N not a multiple of 4, or forced: the general kernel
     rc, info = _plan_ex(300, 202, 100, ab="f32", ct="f16", lda=100, ldb=202, ldc=208)
+    assert rc == 0 and info["variant"] == CV | PIPE
+    # row strides under 4 floats, or forced: the general kernel
+    rc, info = _plan_ex(300, 3, 100, ab="f32", ct="f16", lda=100, ldb=3, ldc=8)
     assert rc == 0 and info["variant"] == CV
     rc, info = _plan_ex(300, 200, 100, ab="f32", ct="f16", lda=100, ldb=200, force_generic=1)
     assert rc == 0 and info["variant"] == CV

@@ -443,12 +443,14 @@ def test_f32_operands_strided_and_offset(oracle_mod, lay, offset, pad, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(300, 260, 133), (257, 512, 29), (64, 4, 5), (33, 300, 16), (1000, 1028, 1000),
-                                   (520, 768, 4096)])
+                                   (520, 768, 4096), (300, 259, 133), (64, 5, 5), (33, 301, 16), (129, 1023, 64),
+                                   (70, 6, 4)])
 def test_f32_operands_kxn_direct_to_lds(oracle_mod, M, N, K):
-    """Binary32 operands with B stored K x N (N a multiple of 4) take the
-    direct-to-LDS kernel: full parity with the oracle (partial tiles in both
-    directions, K tails, a 4-column B), and the same bits from every tile
-    shape and ring depth and from the general kernel."""
+    """Binary32 operands with B stored K x N take the direct-to-LDS kernel:
+    full parity with the oracle (partial tiles in both directions, K tails,
+    N not a multiple of 4 so that B's last row ends inside a 16-byte chunk,
+    narrow B), and the same bits from every tile shape and ring depth and
+    from the general kernel."""
     print(f"case f32-in KxN direct-to-LDS {M}x{N}x{K}", flush=True)
     seed = (M * 7 + N * 3 + K) % 1009
     A = _f32((M, K), seed)
