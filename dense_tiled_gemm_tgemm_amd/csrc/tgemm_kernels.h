@@ -237,12 +237,16 @@ __device__ __forceinline__ void store16_lanes(const u32x4& v, const BufRsrc& r, 
 //  * 16-bit outputs: for each pair of 16-column blocks (j, j+1),
 //    v_permlane16_swap exchanges the converted words between 16-lane rows so
 //    that a lane in row g then holds the 8 consecutive columns
-//    16 (j + (g & 1)) + 8 (g >> 1) .. +7 of its C row: one 16-byte store
-//    (each store instruction writes 16 rows x 64 bytes) at whatever alignment
-//    the row has (gfx950 buffer stores accept unaligned addresses; against
-//    element stores for 2-byte-aligned rows, 140.2 -> 130.8 us on the 3001 x
-//    5003 x 4099 workload); element stores where the 8 columns straddle N,
-//    and 8-byte or element stores when C's offsets exceed 31 bits.
+//    16 (j + (g & 1)) + 8 (g >> 1) .. +7 of its C row; a DPP rotation then
+//    trades such 16-byte pieces between lanes l and l + 8 of each 16-lane row,
+//    so that each store instruction writes 8 rows x 128 contiguous bytes
+//    rather than 16 rows x 64 (3001 x 5003 x 4099, rows 2-byte aligned:
+//    132.9 -> 125.1 us; no change at the aligned workloads). One 16-byte
+//    store per lane at whatever alignment the row has (gfx950 buffer stores
+//    accept unaligned addresses; against element stores for 2-byte-aligned
+//    rows, 140.2 -> 130.8 us on the same workload); element stores where the
+//    8 columns straddle N, and 8-byte or element stores when C's offsets
+//    exceed 31 bits.
 //  * fp32 output: each block's four columns are 16 contiguous bytes of the
 //    lane's row, stored as they are (16 rows x 64 bytes per instruction),
 //    element stores where they straddle N (an 8-byte path here made the
@@ -313,52 +317,71 @@ __device__ __forceinline__ void store_c(const f32x4 (&acc)[NI][NJ], const Args& 
             }
         }
     } else {
-        const int col0 = n0 + wn * 16 * NJ + (g & 1) * 16 + (g >> 1) * 8;
-        uint16_t* base = static_cast<uint16_t*>(a.C) + (int64_t)(m0 + wm * kWr + r16) * a.ldc + col0;
+        // pairs (2q, 2q + 1) of 32-column groups: after the conversion,
+        // lanes 8-15 of each 16-lane row trade group 2q of their C row for
+        // group 2q + 1 of the row 8 above (DPP rotation by 8 inside the row),
+        // so that one store writes rows 0-7 and the next rows 8-15 of the
+        // block, each row 64 contiguous columns (128 bytes). A lane stores
+        // row rl (+ 8 h + 16 i) at columns colq (+ 64 q); the row parts of
+        // the byte offsets are uniform (scalar registers).
+        const bool hi = r16 >= 8;
+        const int rl = r16 & 7;
+        const int colq = n0 + wn * 16 * NJ + (g & 1) * 16 + (g >> 1) * 8 + (hi ? 32 : 0);
+        const int rowl = m0 + wm * kWr + rl;
+        const int64_t lane_off = ((int64_t)rl * a.ldc + colq) * 2;
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             __builtin_amdgcn_sched_barrier(0);
-            const bool row_ok = m0 + wm * kWr + i * 16 + r16 < a.M;
-            uint16_t* row = base + (int64_t)i * 16 * a.ldc;
-            u32x4 vs[NJ / 2];
 #pragma unroll
-            for (int pr = 0; pr < NJ / 2; ++pr) {
-                const f32x4& x = acc[i][2 * pr];
-                const f32x4& y = acc[i][2 * pr + 1];
-                const float* bx = bv[2 * pr];
-                const float* by = bv[2 * pr + 1];
-                const unsigned x01 = pack2<CT>(epi<EPI>(x[0], alpha, EPI ? bx[0] : 0.f, relu),
-                                               epi<EPI>(x[1], alpha, EPI ? bx[1] : 0.f, relu));
-                const unsigned x23 = pack2<CT>(epi<EPI>(x[2], alpha, EPI ? bx[2] : 0.f, relu),
-                                               epi<EPI>(x[3], alpha, EPI ? bx[3] : 0.f, relu));
-                const unsigned y01 = pack2<CT>(epi<EPI>(y[0], alpha, EPI ? by[0] : 0.f, relu),
-                                               epi<EPI>(y[1], alpha, EPI ? by[1] : 0.f, relu));
-                const unsigned y23 = pack2<CT>(epi<EPI>(y[2], alpha, EPI ? by[2] : 0.f, relu),
-                                               epi<EPI>(y[3], alpha, EPI ? by[3] : 0.f, relu));
-                const auto s0 = __builtin_amdgcn_permlane16_swap(x01, y01, false, false);
-                const auto s1 = __builtin_amdgcn_permlane16_swap(x23, y23, false, false);
-                const u32x4 v = u32x4{s0[0], s1[0], s0[1], s1[1]};
-                const int col = col0 + 32 * pr;
-                const bool ok16 = row_ok & (col + 8 <= a.N) & (a.c16 != 0);
-                store16_lanes(v, crs, ok16, ((int64_t)(i * 16 + r16) * a.ldc + col0 + 32 * pr) * 2);
-                vs[pr] = v;
-            }
-            if (__builtin_expect(!whole, 0)) {
-                asm volatile("");                     // a scalar branch of its own, not merged into the lane mask
+            for (int q = 0; q < NJ / 4; ++q) {
+                u32x4 vs[2];
 #pragma unroll
-                for (int pr = 0; pr < NJ / 2; ++pr) {
-                    const u32x4& v = vs[pr];
-                    const int col = col0 + 32 * pr;
-                    uint16_t* dst = row + 32 * pr;
-                    const bool ok16 = row_ok & (col + 8 <= a.N) & (a.c16 != 0);
-                    if (ok16 || !row_ok) {
-                    } else if (col + 8 <= a.N && a.c8) {
-                        __builtin_nontemporal_store(u32x2{v[0], v[1]}, (u32x2*)dst);
-                        __builtin_nontemporal_store(u32x2{v[2], v[3]}, (u32x2*)(dst + 4));
-                    } else if (col < a.N) {
+                for (int h = 0; h < 2; ++h) {
+                    const int pr = 2 * q + h;
+                    const f32x4& x = acc[i][2 * pr];
+                    const f32x4& y = acc[i][2 * pr + 1];
+                    const float* bx = bv[2 * pr];
+                    const float* by = bv[2 * pr + 1];
+                    const unsigned x01 = pack2<CT>(epi<EPI>(x[0], alpha, EPI ? bx[0] : 0.f, relu),
+                                                   epi<EPI>(x[1], alpha, EPI ? bx[1] : 0.f, relu));
+                    const unsigned x23 = pack2<CT>(epi<EPI>(x[2], alpha, EPI ? bx[2] : 0.f, relu),
+                                                   epi<EPI>(x[3], alpha, EPI ? bx[3] : 0.f, relu));
+                    const unsigned y01 = pack2<CT>(epi<EPI>(y[0], alpha, EPI ? by[0] : 0.f, relu),
+                                                   epi<EPI>(y[1], alpha, EPI ? by[1] : 0.f, relu));
+                    const unsigned y23 = pack2<CT>(epi<EPI>(y[2], alpha, EPI ? by[2] : 0.f, relu),
+                                                   epi<EPI>(y[3], alpha, EPI ? by[3] : 0.f, relu));
+                    const auto s0 = __builtin_amdgcn_permlane16_swap(x01, y01, false, false);
+                    const auto s1 = __builtin_amdgcn_permlane16_swap(x23, y23, false, false);
+                    vs[h] = u32x4{s0[0], s1[0], s0[1], s1[1]};
+                }
+                u32x4 d[2];
 #pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            if (col + e < a.N) dst[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+                for (int e = 0; e < 4; ++e) {
+                    const unsigned u = hi ? vs[0][e] : vs[1][e];
+                    const unsigned w = (unsigned)__builtin_amdgcn_mov_dpp((int)u, 0x128, 0xf, 0xf, false);
+                    d[0][e] = hi ? w : vs[0][e];
+                    d[1][e] = hi ? vs[1][e] : w;
+                }
+                const int col = colq + 64 * q;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int ru = i * 16 + 8 * h;                 // uniform part of the row
+                    const bool rok = rowl + ru < a.M;
+                    const bool ok16 = rok & (col + 8 <= a.N) & (a.c16 != 0);
+                    store16_lanes(d[h], crs, ok16, lane_off + 128 * q + (int64_t)ru * a.ldc * 2);
+                    if (__builtin_expect(!whole, 0)) {
+                        asm volatile("");             // a scalar branch of its own, not merged into the lane mask
+                        uint16_t* dst = static_cast<uint16_t*>(a.C) + (int64_t)(rowl + ru) * a.ldc + col;
+                        const u32x4& v = d[h];
+                        if (ok16 || !rok) {
+                        } else if (col + 8 <= a.N && a.c8) {
+                            __builtin_nontemporal_store(u32x2{v[0], v[1]}, (u32x2*)dst);
+                            __builtin_nontemporal_store(u32x2{v[2], v[3]}, (u32x2*)(dst + 4));
+                        } else if (col < a.N) {
+#pragma unroll
+                            for (int e = 0; e < 8; ++e)
+                                if (col + e < a.N) dst[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+                        }
                     }
                 }
             }
