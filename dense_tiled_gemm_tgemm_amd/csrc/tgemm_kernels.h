@@ -248,8 +248,9 @@ __device__ __forceinline__ void store16_lanes(const u32x4& v, const BufRsrc& r, 
 //    8 columns straddle N, and 8-byte or element stores when C's offsets
 //    exceed 31 bits.
 //  * fp32 output: each block's four columns are 16 contiguous bytes of the
-//    lane's row, stored as they are (16 rows x 64 bytes per instruction),
-//    element stores where they straddle N (an 8-byte path here made the
+//    lane's row; the same DPP trade between lanes l and l + 8 over pairs of
+//    blocks makes each store instruction write 8 rows x 128 bytes, element
+//    stores where the four columns straddle N (an 8-byte path here made the
 //    register allocator move the accumulators around in the main loop of the
 //    binary32-operand kernel).
 // All lanes run the exchange; only the stores are predicated: the 16-byte store
@@ -283,35 +284,61 @@ __device__ __forceinline__ void store_c(const f32x4 (&acc)[NI][NJ], const Args& 
     const bool whole = __builtin_amdgcn_readfirstlane(
         (int)(a.c16 && m0 + wm * kWr + kWr <= a.M && n0 + wn * 16 * NJ + 16 * NJ <= a.N)) != 0;
     if constexpr (CT == 2) {
-        const int colb = n0 + wn * 16 * NJ + 4 * g;
-        float* base = static_cast<float*>(a.C) + (int64_t)(m0 + wm * kWr + r16) * a.ldc + colb;
+        // pairs (2q, 2q + 1) of 16-column blocks: lanes 8-15 of each 16-lane
+        // row trade block 2q of their C row for block 2q + 1 of the row 8
+        // above (DPP rotation by 8 inside the row), so that one store writes
+        // rows 0-7 and the next rows 8-15 of the block, each row 32 contiguous
+        // floats (128 bytes). A lane stores row rl (+ 8 h + 16 i) at columns
+        // colq (+ 32 q); the row parts of the byte offsets are uniform.
+        const bool hi = r16 >= 8;
+        const int rl = r16 & 7;
+        const int colq = n0 + wn * 16 * NJ + 4 * g + (hi ? 16 : 0);
+        const int rowl = m0 + wm * kWr + rl;
+        const int64_t lane_off = ((int64_t)rl * a.ldc + colq) * 4;
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             __builtin_amdgcn_sched_barrier(0);
-            const bool row_ok = m0 + wm * kWr + i * 16 + r16 < a.M;
-            float* row = base + (int64_t)i * 16 * a.ldc;
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                // the block's values enter vector registers here and not
-                // earlier: left to itself the compiler copied all 256
-                // accumulators out at the top of the store (ahead of the
-                // per-block branches), ran out of registers, and its spill
-                // code then stored one lane value from the wrong register
-                f32x4 x = acc[i][j];
-                asm volatile("" : "+v"(x));
-                f32x4 v;
+            for (int q = 0; q < NJ / 2; ++q) {
+                u32x4 vs[2];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = epi<EPI>(x[e], alpha, EPI ? bv[j][e] : 0.f, relu);
-                const int col = colb + 16 * j;
-                float* dst = row + 16 * j;
-                const bool ok16 = row_ok & (col + 4 <= a.N) & (a.c16 != 0);
-                store16_lanes(__builtin_bit_cast(u32x4, v), crs, ok16, ((int64_t)(i * 16 + r16) * a.ldc + colb + 16 * j) * 4);
-                if (__builtin_expect(!whole, 0)) {
-                    asm volatile("");                 // a scalar branch of its own, not merged into the lane mask
-                    if (!ok16 && row_ok && col < a.N) {
+                for (int h = 0; h < 2; ++h) {
+                    // the block's values enter vector registers here and not
+                    // earlier: left to itself the compiler copied all 256
+                    // accumulators out at the top of the store (ahead of the
+                    // per-block branches), ran out of registers, and its spill
+                    // code then stored one lane value from the wrong register
+                    f32x4 x = acc[i][2 * q + h];
+                    asm volatile("" : "+v"(x));
+                    f32x4 v;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (col + e < a.N) dst[e] = v[e];
+                    for (int e = 0; e < 4; ++e) v[e] = epi<EPI>(x[e], alpha, EPI ? bv[2 * q + h][e] : 0.f, relu);
+                    vs[h] = __builtin_bit_cast(u32x4, v);
+                }
+                u32x4 d[2];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const unsigned u = hi ? vs[0][e] : vs[1][e];
+                    const unsigned w = (unsigned)__builtin_amdgcn_mov_dpp((int)u, 0x128, 0xf, 0xf, false);
+                    d[0][e] = hi ? w : vs[0][e];
+                    d[1][e] = hi ? vs[1][e] : w;
+                }
+                const int col = colq + 32 * q;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int ru = i * 16 + 8 * h;                 // uniform part of the row
+                    const bool rok = rowl + ru < a.M;
+                    const bool ok16 = rok & (col + 4 <= a.N) & (a.c16 != 0);
+                    store16_lanes(d[h], crs, ok16, lane_off + 128 * q + (int64_t)ru * a.ldc * 4);
+                    if (__builtin_expect(!whole, 0)) {
+                        asm volatile("");             // a scalar branch of its own, not merged into the lane mask
+                        if (!ok16 && rok && col < a.N) {
+                            float* dst = static_cast<float*>(a.C) + (int64_t)(rowl + ru) * a.ldc + col;
+                            const f32x4 v = __builtin_bit_cast(f32x4, d[h]);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                if (col + e < a.N) dst[e] = v[e];
+                        }
                     }
                 }
             }
