@@ -55,9 +55,9 @@ mfma_ceiling_kernel(const uint16_t* data, unsigned data_bytes, float* out, uint6
 #if defined(__HIP_DEVICE_COMPILE__)
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)data, 0, (int)data_bytes, 0x00020000);
 #endif
-    const unsigned voff = (unsigned)tid * 16u;
-    const unsigned smask = data_bytes - 65536u;                     // 64 KiB-aligned windows inside the data
-    unsigned soff = (unsigned)blockIdx.x * 65536u;
+    [[maybe_unused]] const unsigned voff = (unsigned)tid * 16u;
+    [[maybe_unused]] const unsigned smask = data_bytes - 65536u;                     // 64 KiB-aligned windows inside the data
+    [[maybe_unused]] unsigned soff = (unsigned)blockIdx.x * 65536u;
     // shader clock and 100 MHz reference time at the start of the rounds
     const uint64_t t0 = __builtin_amdgcn_s_memtime();
     const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
@@ -194,9 +194,9 @@ stream16_kernel(const uint16_t* data, unsigned data_bytes, float* out, uint64_t*
 #if defined(__HIP_DEVICE_COMPILE__)
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)data, 0, (int)data_bytes, 0x00020000);
 #endif
-    const unsigned voff = (unsigned)tid * 16u;
-    const unsigned wmask = data_bytes - 4096u;
-    unsigned soff = window0();
+    [[maybe_unused]] const unsigned voff = (unsigned)tid * 16u;
+    [[maybe_unused]] const unsigned wmask = data_bytes - 4096u;
+    [[maybe_unused]] unsigned soff = window0();
     const uint64_t t0 = __builtin_amdgcn_s_memtime();
     const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
     for (int it = 0; it < iters; ++it) {
@@ -219,7 +219,7 @@ stream16_kernel(const uint16_t* data, unsigned data_bytes, float* out, uint64_t*
                     d = __builtin_bit_cast(half8, sm[lane + 64 * r + 1024 * wave + 16 * (it & 3)]);
                 } else if (LOADS && h == 1 && (q & 3) == 3 && (LOADS != 2 || (q & 7) == 7)) {
                     const int l = q >> 2;
-                    const unsigned so = (soff + (unsigned)l * 4096u) & wmask;
+                    [[maybe_unused]] const unsigned so = (soff + (unsigned)l * 4096u) & wmask;
                     if (LOADS == 1 || LOADS == 2) {
 #if defined(__HIP_DEVICE_COMPILE__)
                         u32x4* dst = sm + 4096 + (l * 4 + wave) * 64;
@@ -281,9 +281,9 @@ stream32x32_kernel(const uint16_t* data, unsigned data_bytes, float* out, uint64
 #if defined(__HIP_DEVICE_COMPILE__)
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)data, 0, (int)data_bytes, 0x00020000);
 #endif
-    const unsigned voff = (unsigned)tid * 16u;
-    const unsigned wmask = data_bytes - 4096u;
-    unsigned soff = window0();
+    [[maybe_unused]] const unsigned voff = (unsigned)tid * 16u;
+    [[maybe_unused]] const unsigned wmask = data_bytes - 4096u;
+    [[maybe_unused]] unsigned soff = window0();
     const uint64_t t0 = __builtin_amdgcn_s_memtime();
     const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
     for (int it = 0; it < iters; ++it) {
@@ -359,9 +359,9 @@ stream8w_kernel(const uint16_t* data, unsigned data_bytes, float* out, uint64_t*
 #if defined(__HIP_DEVICE_COMPILE__)
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)data, 0, (int)data_bytes, 0x00020000);
 #endif
-    const unsigned voff = (unsigned)tid * 16u;
-    const unsigned wmask = data_bytes - 8192u;          // 8 KiB windows: 512 threads x 16 bytes
-    unsigned soff = window0();
+    [[maybe_unused]] const unsigned voff = (unsigned)tid * 16u;
+    [[maybe_unused]] const unsigned wmask = data_bytes - 8192u;          // 8 KiB windows: 512 threads x 16 bytes
+    [[maybe_unused]] unsigned soff = window0();
     const uint64_t t0 = __builtin_amdgcn_s_memtime();
     const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
     for (int it = 0; it < iters; ++it) {
