@@ -242,6 +242,8 @@ static int launch(const Plan& pl, const void* fn, const void* A, const void* B, 
     // 128 rows stays below 2^31 (they go through a 32-bit buffer offset)
     args.c16 = (127 * pl.ldc + (int64_t)pl.N) * c_size + 16 < (int64_t(1) << 31);
     args.c8 = (pl.variant & kVecC) != 0;
+    // streamed 16-byte C stores where whole 128-byte lines are written
+    args.c_stream = ((uintptr_t)C % 128 == 0) && ((pl.ldc * c_size) % 128 == 0);
     void* kargs[] = {&args};
     const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)args.grid), dim3((unsigned)pl.threads), kargs, 0,
                                          static_cast<hipStream_t>(stream));

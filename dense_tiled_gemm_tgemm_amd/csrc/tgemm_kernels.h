@@ -84,6 +84,7 @@ struct Args {
     int grid;             // workgroups launched; workgroup b computes tiles b, b + grid, ...
     int c16;              // 16-byte C stores (any alignment): every offset in a wave's rows below 2^31
     int c8;               // the same for 8 bytes
+    int c_stream;         // 1: C rows 128-byte aligned, 16-byte stores streamed (nt sc1); 0: default policy
 };
 
 // LDS layout of one staged K-contiguous operand block (256 rows x KS halves)
@@ -188,11 +189,18 @@ __device__ __forceinline__ void load_bias(float (&bv)[NJ][4], const Args& a, int
 
 // 16-byte C stores go through a buffer resource over the wave's 128 C rows
 // (the host keeps this path only where every byte offset in those rows fits
-// in 31 bits) with the streaming policy nt sc1: C is written once and never
-// read back, and every workgroup stores its tile at about the same time, so
-// the burst drains faster when the lines bypass the caches' normal
-// replacement (measured at 8192^3: +2.3% with an fp32 C against nt alone,
-// and 3-4% against plain stores).
+// in 31 bits). Where C's rows are 128-byte aligned (base and row pitch) they
+// use the streaming policy nt sc1: C is written once and never read back,
+// every workgroup stores its tile at about the same time, and whole lines
+// drain faster when they bypass the caches' normal replacement (8192^3:
+// 1.8% against the default policy with a 16-bit C, 2.8% with an fp32 C).
+// Rows at any other alignment split their 128-byte pieces over two lines,
+// which streamed stores then write as partial lines; there the default
+// (write-back) policy is faster, as the L2 merges the halves: 3001 x 5003 x
+// 4099 (2-byte-aligned rows) 121.9 -> 116.8 us with a 16-bit C and 142.2 ->
+// 118.3 with an fp32 C; 8192 x 12288 x 4096 with ldc 12289 648.7 -> 636.4
+// and 728.8 -> 628.9. The choice is a uniform flag (Args::c_stream), one
+// scalar branch per store.
 #if defined(__HIP_DEVICE_COMPILE__)
 typedef __amdgpu_buffer_rsrc_t BufRsrc;
 #else
@@ -209,11 +217,14 @@ __device__ __forceinline__ BufRsrc c_rows_rsrc(void* C, int64_t byte_offset) {
 #endif
 }
 
-__device__ __forceinline__ void store16_stream(const u32x4& v, const BufRsrc& r, int64_t byte_offset) {
+__device__ __forceinline__ void store16_c(const u32x4& v, const BufRsrc& r, int64_t byte_offset, bool stream) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)byte_offset, 0, kCStorePolicy);
+    if (stream)
+        __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)byte_offset, 0, kCStorePolicy);
+    else
+        __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)byte_offset, 0, 0);
 #else
-    (void)v; (void)r; (void)byte_offset;
+    (void)v; (void)r; (void)byte_offset; (void)stream;
 #endif
 }
 
@@ -224,10 +235,11 @@ __device__ __forceinline__ void store16_stream(const u32x4& v, const BufRsrc& r,
 // instruction's immediate offset (which would shift the dropped lanes' offset
 // back into range).
 constexpr unsigned kCOob = 0x80000000u;
-__device__ __forceinline__ void store16_lanes(const u32x4& v, const BufRsrc& r, bool ok, int64_t byte_offset) {
+__device__ __forceinline__ void store16_lanes(const u32x4& v, const BufRsrc& r, bool ok, int64_t byte_offset,
+                                              bool stream) {
     unsigned o = ok ? (unsigned)byte_offset : kCOob;
     asm volatile("" : "+v"(o));
-    store16_stream(v, r, (int)o);
+    store16_c(v, r, (int)o, stream);
 }
 
 // Lane l of wave (wm, wn) holds, in acc[i][j], C row m0 + 16 NI wm + 16 i + (l mod 16)
@@ -260,9 +272,9 @@ __device__ __forceinline__ void store16_lanes(const u32x4& v, const BufRsrc& r, 
 // per store instead of a chain of exec-mask branches, which took longer than
 // the conversions themselves. One 16-row block
 // at a time (pinned), so the temporaries stay few when this runs between two
-// tiles with the next tile's fragments already in registers. Vector stores
-// use the streaming policies (store16_stream above; the 8-byte path is
-// non-temporal).
+// tiles with the next tile's fragments already in registers. The 16-byte
+// stores take the policy store16_c chooses from C's alignment; the 8-byte
+// path is non-temporal.
 template <int TY, int NJ = 8, int NI = 8>
 __device__ __forceinline__ void store_c(const f32x4 (&acc)[NI][NJ], const Args& a, int m0, int n0, int wm,
                                         int wn, int lane) {
@@ -283,6 +295,7 @@ __device__ __forceinline__ void store_c(const f32x4 (&acc)[NI][NJ], const Args& 
     }
     const bool whole = __builtin_amdgcn_readfirstlane(
         (int)(a.c16 && m0 + wm * kWr + kWr <= a.M && n0 + wn * 16 * NJ + 16 * NJ <= a.N)) != 0;
+    const bool stream = __builtin_amdgcn_readfirstlane(a.c_stream) != 0;
     if constexpr (CT == 2) {
         // pairs (2q, 2q + 1) of 16-column blocks: lanes 8-15 of each 16-lane
         // row trade block 2q of their C row for block 2q + 1 of the row 8
@@ -329,7 +342,7 @@ __device__ __forceinline__ void store_c(const f32x4 (&acc)[NI][NJ], const Args& 
                     const int ru = i * 16 + 8 * h;                 // uniform part of the row
                     const bool rok = rowl + ru < a.M;
                     const bool ok16 = rok & (col + 4 <= a.N) & (a.c16 != 0);
-                    store16_lanes(d[h], crs, ok16, lane_off + 128 * q + (int64_t)ru * a.ldc * 4);
+                    store16_lanes(d[h], crs, ok16, lane_off + 128 * q + (int64_t)ru * a.ldc * 4, stream);
                     if (__builtin_expect(!whole, 0)) {
                         asm volatile("");             // a scalar branch of its own, not merged into the lane mask
                         if (!ok16 && rok && col < a.N) {
@@ -395,7 +408,7 @@ __device__ __forceinline__ void store_c(const f32x4 (&acc)[NI][NJ], const Args& 
                     const int ru = i * 16 + 8 * h;                 // uniform part of the row
                     const bool rok = rowl + ru < a.M;
                     const bool ok16 = rok & (col + 8 <= a.N) & (a.c16 != 0);
-                    store16_lanes(d[h], crs, ok16, lane_off + 128 * q + (int64_t)ru * a.ldc * 2);
+                    store16_lanes(d[h], crs, ok16, lane_off + 128 * q + (int64_t)ru * a.ldc * 2, stream);
                     if (__builtin_expect(!whole, 0)) {
                         asm volatile("");             // a scalar branch of its own, not merged into the lane mask
                         uint16_t* dst = static_cast<uint16_t*>(a.C) + (int64_t)(rowl + ru) * a.ldc + col;
