@@ -610,3 +610,48 @@ def test_concurrent_streams():
     for c1, c2 in outs:
         assert torch.equal(c1.view(torch.int16), ref1.view(torch.int16))
         assert torch.equal(c2, ref2)
+
+
+@pytest.mark.parametrize("ct", ["f16", "f32"])
+@pytest.mark.parametrize("lay", ["NxK", "KxN"])
+def test_c_placement_selects_store_policy_same_bits(oracle_mod, lay, ct):
+    """The 16-byte C stores are streamed where C's base and row pitch are
+    multiples of 128 bytes and use the default policy elsewhere: the same
+    product stored at 128-byte-aligned rows, at 16-byte-aligned rows, at
+    2-byte-aligned rows and at a base 64 bytes past a 128-byte boundary gives
+    the same bits, matches the oracle, and leaves the NaN guard around C
+    intact. The 256-row-tile launch and the automatic one both run."""
+    M, N, K = 520, 1000, 200
+    print(f"case store policy {lay} {ct}", flush=True)
+    A = _bits((M, K), 91, "f16")
+    B = _bits((K, N) if lay == "KxN" else (N, K), 92, "f16")
+    Ad, Bd = _dev(A, "f16"), _dev(B, "f16")
+    esz = 4 if ct == "f32" else 2
+    ref, tol = oracle_mod.gemm_ex(A, B, lay, "f16")
+    outs = []
+    for ldc, off_bytes in ((1024, 0), (1000, 0), (1001, 0), (1024, 64)):
+        for tile_m in (0, 256):
+            n_el = (M + 1) * ldc + 64
+            if ct == "f32":
+                buf = torch.full((n_el,), float("nan"), dtype=torch.float32, device=DEV)
+            else:
+                buf = torch.full((n_el,), 0x7E01, dtype=torch.int32).to(torch.int16).to(DEV)
+            off = off_bytes // esz
+            rc = tg.tgemm_gemm_config(M, N, K, "f16", Ad.data_ptr(), K, Bd.data_ptr(), B.shape[1], lay, ct,
+                                      buf.data_ptr() + off_bytes, ldc, 1.0, None, "none",
+                                      torch.cuda.current_stream().cuda_stream, tile_m=tile_m)
+            assert rc == tg.TGEMM_OK, (ldc, off_bytes, tile_m)
+            host = _out_np(buf)
+            idx = off + (np.arange(M)[:, None] * ldc + np.arange(N)[None, :])
+            inside = np.zeros(host.shape, dtype=bool)
+            inside[idx.ravel()] = True
+            if ct == "f32":
+                assert np.isnan(host[~inside]).all(), (ldc, off_bytes, tile_m)
+            else:
+                assert (host[~inside] == 0x7E01).all(), (ldc, off_bytes, tile_m)
+            got = np.ascontiguousarray(host[idx])
+            res = oracle_mod.check_ex(got, ct, ref, tol)
+            assert res["nfail"] == 0, (ldc, off_bytes, tile_m, res)
+            outs.append(got.view(np.uint32 if ct == "f32" else np.uint16))
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
