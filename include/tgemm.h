@@ -82,7 +82,8 @@ enum {
  * staged through registers with 128-bit or element loads. C is written with
  * 16-byte stores at any 2-byte alignment (element stores at its right edge;
  * 8-byte or element stores when a byte offset within 128 rows of C would
- * exceed 2^31).
+ * exceed 2^31), streamed past the caches where C's base and row pitch are
+ * multiples of 128 bytes and through the L2 otherwise.
  * C must not alias A or B (page 4, section 2.4.12.1: restrict-qualified
  * operands must not overlap).
  */
