@@ -84,23 +84,25 @@ static bool epilogue_requested(float alpha, const float* bias, int act) {
 // launch parameters that leave the result unchanged bit for bit: K step and
 // LDS ring depth of the direct-to-LDS pipeline, and the raster group height.
 // The table is per device, keyed by everything that selects a kernel: sizes,
-// strides, layout, types, epilogue on/off and the variant bits (alignment
-// classes, load path).
+// strides, layout, types, epilogue on/off, the variant bits (alignment
+// classes, load path) and the C store policy.
 // ---------------------------------------------------------------------------
 struct TuneKey {
     int dev;
     int64_t M, N, K, lda, ldb, ldc;
-    int layout, ab, ct, epi, variant;
+    int layout, ab, ct, epi, variant, c_stream;
     bool operator==(const TuneKey& o) const {
         return dev == o.dev && M == o.M && N == o.N && K == o.K && lda == o.lda && ldb == o.ldb && ldc == o.ldc &&
-               layout == o.layout && ab == o.ab && ct == o.ct && epi == o.epi && variant == o.variant;
+               layout == o.layout && ab == o.ab && ct == o.ct && epi == o.epi && variant == o.variant &&
+               c_stream == o.c_stream;
     }
 };
 
 struct TuneKeyHash {
     size_t operator()(const TuneKey& k) const {
         uint64_t h = 1469598103934665603ull;
-        const int64_t v[] = {k.dev, k.M, k.N, k.K, k.lda, k.ldb, k.ldc, k.layout, k.ab, k.ct, k.epi, k.variant};
+        const int64_t v[] = {k.dev, k.M,      k.N,  k.K,  k.lda,   k.ldb,    k.ldc,
+                             k.layout, k.ab, k.ct, k.epi, k.variant, k.c_stream};
         for (int64_t x : v) h = (h ^ (uint64_t)x) * 1099511628211ull;    // FNV-1a over the fields
         return (size_t)h;
     }
@@ -121,8 +123,9 @@ static std::atomic<int> g_tuned_count{0};
 static bool tune_key(const Plan& pl, TuneKey* k) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return false;
-    *k = TuneKey{dev, pl.M, pl.N, pl.K, pl.lda, pl.ldb, pl.ldc, pl.layout, pl.ab_type, pl.c_type, pl.epi ? 1 : 0,
-                 pl.variant};
+    *k = TuneKey{dev,        pl.M,       pl.N,        pl.K,      pl.lda,     pl.ldb,
+                 pl.ldc,     pl.layout,  pl.ab_type,  pl.c_type, pl.epi ? 1 : 0, pl.variant,
+                 pl.c_stream ? 1 : 0};
     return true;
 }
 
@@ -243,7 +246,7 @@ static int launch(const Plan& pl, const void* fn, const void* A, const void* B, 
     args.c16 = (127 * pl.ldc + (int64_t)pl.N) * c_size + 16 < (int64_t(1) << 31);
     args.c8 = (pl.variant & kVecC) != 0;
     // streamed 16-byte C stores where whole 128-byte lines are written
-    args.c_stream = ((uintptr_t)C % 128 == 0) && ((pl.ldc * c_size) % 128 == 0);
+    args.c_stream = pl.c_stream;
     void* kargs[] = {&args};
     const hipError_t e = hipLaunchKernel(fn, dim3((unsigned)args.grid), dim3((unsigned)pl.threads), kargs, 0,
                                          static_cast<hipStream_t>(stream));

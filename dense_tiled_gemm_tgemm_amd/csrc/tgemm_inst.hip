@@ -19,7 +19,7 @@ constexpr int kTy = ty_code(TG_AB, TG_CT, TG_EPI != 0);
 constexpr bool kAllDepths = (kTy == ty_code(0, 0, false));
 
 template <int NXK>
-const void* dma_ptr(int k_step, int stages, int tile_m, int producers) {
+const void* dma_ptr(int k_step, int stages, int tile_m, int producers, bool c_stream) {
     if (producers) {
         // producer/consumer workgroups: 128 x 256 tiles, 32-deep steps
         if constexpr (kAllDepths) {
@@ -42,7 +42,10 @@ const void* dma_ptr(int k_step, int stages, int tile_m, int producers) {
             return reinterpret_cast<const void*>(&tgemm_dma_kernel<kTy, NXK, 32, 3, 2>);
         return nullptr;
     }
-    if (k_step == 64) return reinterpret_cast<const void*>(&tgemm_dma_kernel<kTy, NXK, 64, 2>);
+    // 64-deep steps: one build per C store policy
+    if (k_step == 64)
+        return c_stream ? reinterpret_cast<const void*>(&tgemm_dma_kernel<kTy, NXK, 64, 2, 8, false, 1>)
+                        : reinterpret_cast<const void*>(&tgemm_dma_kernel<kTy, NXK, 64, 2, 8, false, 0>);
     if (stages == kDefaultDmaStages32) return reinterpret_cast<const void*>(&tgemm_dma_kernel<kTy, NXK, 32, 4>);
     if constexpr (kAllDepths) {
         switch (stages) {
@@ -102,8 +105,8 @@ const void* kernel_for<TG_AB, TG_CT, (TG_EPI != 0)>(const Plan& pl) {
         return nxk ? f32in_ptr<1>(vec) : f32in_ptr<0>(vec);
     } else {
         if (pl.variant & kDma)
-            return nxk ? dma_ptr<1>(pl.k_step, pl.stages, pl.bm, pl.producers)
-                       : dma_ptr<0>(pl.k_step, pl.stages, pl.bm, pl.producers);
+            return nxk ? dma_ptr<1>(pl.k_step, pl.stages, pl.bm, pl.producers, pl.c_stream)
+                       : dma_ptr<0>(pl.k_step, pl.stages, pl.bm, pl.producers, pl.c_stream);
         return nxk ? rs_ptr<1>(vec) : rs_ptr<0>(vec);
     }
 }

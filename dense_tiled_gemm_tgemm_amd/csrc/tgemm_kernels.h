@@ -199,8 +199,9 @@ __device__ __forceinline__ void load_bias(float (&bv)[NJ][4], const Args& a, int
 // (write-back) policy is faster, as the L2 merges the halves: 3001 x 5003 x
 // 4099 (2-byte-aligned rows) 121.9 -> 116.8 us with a 16-bit C and 142.2 ->
 // 118.3 with an fp32 C; 8192 x 12288 x 4096 with ldc 12289 648.7 -> 636.4
-// and 728.8 -> 628.9. The choice is a uniform flag (Args::c_stream), one
-// scalar branch per store.
+// and 728.8 -> 628.9. The persistent 64-deep kernel is built once per policy
+// (the host picks by C's alignment); elsewhere the choice is a uniform flag
+// (Args::c_stream), one scalar branch per store.
 #if defined(__HIP_DEVICE_COMPILE__)
 typedef __amdgpu_buffer_rsrc_t BufRsrc;
 #else
@@ -275,7 +276,8 @@ __device__ __forceinline__ void store16_lanes(const u32x4& v, const BufRsrc& r, 
 // tiles with the next tile's fragments already in registers. The 16-byte
 // stores take the policy store16_c chooses from C's alignment; the 8-byte
 // path is non-temporal.
-template <int TY, int NJ = 8, int NI = 8>
+// POL: 1 streamed stores, 0 default policy, -1 chosen at run time by a.c_stream.
+template <int TY, int NJ = 8, int NI = 8, int POL = -1>
 __device__ __forceinline__ void store_c(const f32x4 (&acc)[NI][NJ], const Args& a, int m0, int n0, int wm,
                                         int wn, int lane) {
     static_assert(NJ == 8 || NJ == 4, "a wave owns 8 or 4 blocks of 16 columns");
@@ -295,7 +297,7 @@ __device__ __forceinline__ void store_c(const f32x4 (&acc)[NI][NJ], const Args& 
     }
     const bool whole = __builtin_amdgcn_readfirstlane(
         (int)(a.c16 && m0 + wm * kWr + kWr <= a.M && n0 + wn * 16 * NJ + 16 * NJ <= a.N)) != 0;
-    const bool stream = __builtin_amdgcn_readfirstlane(a.c_stream) != 0;
+    const bool stream = POL < 0 ? __builtin_amdgcn_readfirstlane(a.c_stream) != 0 : POL == 1;
     if constexpr (CT == 2) {
         // pairs (2q, 2q + 1) of 16-column blocks: lanes 8-15 of each 16-lane
         // row trade block 2q of their C row for block 2q + 1 of the row 8
@@ -1343,7 +1345,8 @@ __device__ __forceinline__ void step_pairs(f32x4 (&acc)[I][8], half8 (&fa)[2][I]
 // compute as above but issue no loads and wait on nothing but their own LDS
 // reads and the step barrier; waves 4-7 issue every load, wait for them, fix
 // up a partial last step and meet the consumers at the same barriers.
-template <int TY, int NXK, int KS, int S, int I = 8, bool PC = false>
+// POL (64-deep steps): the C store policy fixed at compile time (store_c).
+template <int TY, int NXK, int KS, int S, int I = 8, bool PC = false, int POL = -1>
 __global__ void __launch_bounds__(PC ? 2 * NTHREADS : NTHREADS)
 __attribute__((amdgpu_waves_per_eu((I == 8 && !PC) ? 1 : 2, (I == 8 && !PC) ? 1 : 2)))
 tgemm_dma_kernel(Args a) {
@@ -1355,6 +1358,7 @@ tgemm_dma_kernel(Args a) {
     static_assert(Ctx::kLa >= 1, "the A block takes at least one load per step");
     static_assert(!PC || (KS == 32 && I == 4), "producer/consumer workgroups: 32-deep steps, 128 x 256 tiles");
     static_assert(AB != 2 || (KS == 32 && !PC), "binary32 operands: 16-deep steps (32 16-bit units)");
+    static_assert(POL < 0 || KS == 64, "a fixed store policy for the persistent kernel only");
     static_assert(S >= 2 && S <= 6 && Ctx::kSlots * 16 <= 160 * 1024, "LDS ring must fit 160 KiB");
     static_assert(I == 8 || PC || Ctx::kSlots * 16 <= 80 * 1024, "two workgroups per compute unit");
     constexpr int kL = Ctx::kLa + KS / 8;             // load instructions per step per loading wave
@@ -1458,7 +1462,7 @@ tgemm_dma_kernel(Args a) {
             }
             dma_step<AB, NXK, KS, S, 0, false, true, I>(acc, fa, fb, st, nk - 1, a, c, cur, tc, tn, has_next);
             st ^= 1;
-            store_c<TY, 8, I>(acc, a, tc.m0, tc.n0, wm, wn, lane);
+            store_c<TY, 8, I, POL>(acc, a, tc.m0, tc.n0, wm, wn, lane);
             if (!has_next) break;
             read_frags<KS, NXK, I, AB>(fa[0], fb[0], cur, 0);   // the next tile's first fragments
             wid += a.grid;

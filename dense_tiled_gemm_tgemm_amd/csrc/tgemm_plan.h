@@ -102,6 +102,7 @@ struct Plan {
     int group_m, num_xcd;
     int k_step, stages;   // K step per LDS stage and ring depth of the launched kernel
     int grid;             // workgroups launched (W, or the compute units for a persistent launch)
+    bool c_stream;        // C's base and row pitch multiples of 128 bytes: its 16-byte stores are streamed
 };
 
 // Binary32 operands planned onto the direct-to-LDS kernel: it is launched
@@ -192,6 +193,7 @@ inline int make_plan(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda
     pl->lda = lda;
     pl->ldb = ldb;
     pl->ldc = ldc;
+    pl->c_stream = ((uintptr_t)C % 128 == 0) && ((ldc * c_size) % 128 == 0);
     pl->layout = b_layout;
     pl->ab_type = ab_type;
     pl->c_type = c_type;

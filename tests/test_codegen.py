@@ -170,8 +170,30 @@ def test_c_store_offsets_drop_masked_lanes(asm, case):
         ins = [l.strip() for l in body if l.strip() and not l.strip().startswith((";", "."))]
         k, bad = _unguarded_c_stores(ins)
         assert not bad, (name, bad[:3])
-        # the policy follows C's alignment at run time: both forms of every store
         streamed = sum(1 for l in ins if l.startswith("buffer_store_dwordx4") and l.endswith("nt sc1"))
-        assert 2 * streamed == k, (name, streamed, k)
+        pol = _store_policy(name)
+        if pol is None:
+            # the policy follows C's alignment at run time: both forms of every store
+            assert 2 * streamed == k, (name, streamed, k)
+        else:
+            # built for one policy (the persistent 64-deep kernel): that form only
+            assert k > 0 and streamed == (k if pol == 1 else 0), (name, streamed, k)
         n += k
     assert n >= 64, n
+
+
+def _store_policy(name):
+    """The C store policy a direct-to-LDS kernel was built for (its last
+    template argument: 1 streamed, 0 default), or None where it is chosen at
+    run time (-1, mangled n1) and for the other kernel families."""
+    m = re.match(r"_ZN2tg16tgemm_dma_kernelI\w*?Lb[01]ELi(n1|0|1)EEEvNS_4ArgsE$", name)
+    if not m or m.group(1) == "n1":
+        return None
+    return int(m.group(1))
+
+
+def test_store_policy_parse():
+    assert _store_policy("_ZN2tg16tgemm_dma_kernelILi0ELi1ELi64ELi2ELi8ELb0ELi1EEEvNS_4ArgsE") == 1
+    assert _store_policy("_ZN2tg16tgemm_dma_kernelILi0ELi1ELi64ELi2ELi8ELb0ELi0EEEvNS_4ArgsE") == 0
+    assert _store_policy("_ZN2tg16tgemm_dma_kernelILi0ELi1ELi32ELi3ELi4ELb1ELin1EEEvNS_4ArgsE") is None
+    assert _store_policy("_ZN2tg15tgemm_rs_kernelILi0ELi0ELb1EEEvNS_4ArgsE") is None
